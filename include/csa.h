@@ -1,0 +1,281 @@
+/*
+ * csa.h -- C ABI of libcsa.so: Compressed Sparse Attention (CSA) and Heavily
+ * Compressed Attention (HCA) of DeepSeek-V4 on AMD Instinct MI355X (gfx950).
+ *
+ * The method, as the public pages describe it:
+ *  - "DeepSeek v4" (Korean summary page), section "Compressed Sparse Attention":
+ *    compressed KV entries (two token-level series C_a, C_b with weights Z_a, Z_b
+ *    and positional biases, a row-wise softmax over 2m elements, the first block
+ *    padded), the lightning indexer (score = sum over indexer heads of a per-head
+ *    weight times ReLU(q . K) for each preceding compressed block), the top-k
+ *    selector, and the sliding-window entries appended to the selected ones;
+ *    section on the hybrid CSA/HCA attention (HCA compresses m' >> m tokens per
+ *    entry and stays dense).
+ *  - "DeepSeek-AI (2026) - ARXIV-2606.19348" anthology record, Key takeaways: two
+ *    latent KV streams pooled over overlapping 2m-token windows; an RMSNorm on each
+ *    query head and on the single compressed-KV head before the core attention.
+ *  - "DeepSeek-V4-Pro" techniques map: one KV head shared by all query heads
+ *    (multi-query attention), sliding window of 128 (the window keeps w-1 past
+ *    tokens plus the current one), index_topk with invalid slots set to -1, QK
+ *    normalisation, FP4 precision for the attention indexer.
+ *
+ * Conventions common to every call
+ *  - Tensor pointers are DEVICE pointers (HIP device memory, e.g. from torch).
+ *    Descriptors and scalar arguments live in host memory and are read before the
+ *    call returns.  The caller owns every buffer, including the workspace.
+ *  - Layouts are row-major with the innermost dimension contiguous.  Per-sequence
+ *    caches are [batch, capacity, width]: sequence b's row r starts at element
+ *    (b * capacity + r) * width.  Token positions are absolute int32.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and
+ *    the call returns without synchronising.  The library allocates no device
+ *    memory and keeps no state between calls.
+ *  - Errors: every argument is validated on the host before anything is launched;
+ *    on failure nothing is enqueued, a csa_status code is returned and
+ *    csa_last_error() describes it.  A failed launch returns CSA_ERR_HIP.  Values
+ *    that live in device memory (positions, counts, indices) cannot be checked on
+ *    the host: kernels never access memory outside the described buffers, and an
+ *    index or window row outside its buffer is skipped (contributes nothing).
+ *  - Workspaces: sized by the matching *_workspace_size call.  A workspace must be
+ *    zero-filled before its first use; any counters the library keeps in it are back
+ *    at zero when the enqueued work completes.  Two calls in flight at once must not
+ *    share one workspace.
+ */
+#ifndef CSA_H_
+#define CSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA_ABI_VERSION 1
+
+typedef enum {
+  CSA_OK = 0,
+  CSA_ERR_NULL = 1,        /* a required pointer is NULL */
+  CSA_ERR_SHAPE = 2,       /* sizes inconsistent or outside the supported range */
+  CSA_ERR_DTYPE = 3,       /* unsupported dtype or dtype combination */
+  CSA_ERR_ALIGN = 4,       /* a pointer is not aligned as the kernel requires */
+  CSA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than *_workspace_size */
+  CSA_ERR_UNSUPPORTED = 6, /* valid request this build does not implement */
+  CSA_ERR_HIP = 7          /* the HIP runtime reported an error */
+} csa_status;
+
+typedef enum {
+  CSA_F32 = 0,   /* IEEE binary32 */
+  CSA_BF16 = 1,  /* bfloat16 stored as uint16 bit patterns */
+  CSA_MXFP4 = 2  /* OCP MX v1.0 MXFP4: 4-bit e2m1 codes, two per byte (even element in
+                    the low nibble), plus one e8m0 scale byte per 32 elements */
+} csa_dtype;
+
+/* Returns CSA_ABI_VERSION. */
+int csa_abi_version(void);
+/* Static description of a status code. */
+const char* csa_status_string(int status);
+/* Detail of the last failure on the calling thread (thread-local storage; valid until
+   the next call on that thread). */
+const char* csa_last_error(void);
+
+/* ------------------------------------------------------------------------------
+ * csa_compress -- overlapping two-stream softmax pooling of token rows into
+ * compressed entries ("DeepSeek v4" summary, "Compressed Sparse Attention",
+ * compressed KV entries; anthology record, Key takeaways).  Also builds the
+ * indexer keys, which use the same operation on their own streams.
+ *
+ * Entry j pools the A stream over tokens [m*j, m*j+m) and the B stream over the
+ * previous block [m*(j-1), m*j): logits l = z + positional bias over those 2m
+ * slots, weights = softmax(l) (per channel when zc == channels, shared when
+ * zc == 1), entry = sum of weight * row.  Entry 0 has no B half (logits -inf,
+ * rows 0).  Arithmetic in fp32.
+ *
+ *   a, b     [batch, n_rows, channels]  in_dtype; row r = absolute token tok_base + r
+ *   za, zb   [batch, n_rows, zc]        fp32 pooling logits of the A and B streams
+ *   bias_a, bias_b  [m, zc] fp32 positional biases, or NULL for zero
+ *   out      [batch, out_cap, channels] out_dtype; entry j is written to row j
+ * Entries [entry_begin, entry_end) are produced.  Requires the rows they need to be
+ * present: m*entry_begin - (entry_begin > 0 ? m : 0) >= tok_base and
+ * m*entry_end <= tok_base + n_rows; entry_end <= out_cap; 1 <= m <= 256.
+ * ---------------------------------------------------------------------------- */
+typedef struct {
+  int32_t batch;
+  int32_t channels;
+  int32_t m;
+  int32_t zc;            /* 1 or channels */
+  int32_t n_rows;
+  int32_t tok_base;
+  int32_t entry_begin;
+  int32_t entry_end;
+  int32_t out_cap;
+  int32_t in_dtype;      /* CSA_F32 or CSA_BF16 */
+  int32_t out_dtype;     /* CSA_F32 or CSA_BF16 */
+} csa_compress_desc;
+
+csa_status csa_compress(const csa_compress_desc* desc, const void* a, const void* b,
+                        const float* za, const float* zb, const float* bias_a,
+                        const float* bias_b, void* out, void* stream);
+
+/* ------------------------------------------------------------------------------
+ * csa_mxfp4_quantize -- OCP MX v1.0 MXFP4 encoding of n_blocks blocks of 32
+ * consecutive values (the pages' FP4 indexer QK path: forum post on the DeepSeek
+ * V4 paper; techniques map, "FP4 precision for the attention indexer").
+ * Shared exponent E = floor(log2(max|x|)) - 2 clamped to [-127, 127] (E = -127 for
+ * an all-zero block), scale byte = E + 127; element code = x / 2^E rounded to the
+ * nearest e2m1 value (ties to the even code), saturating at 6, sign bit = sign of x.
+ *   x       [n_blocks * 32]  dtype CSA_F32 or CSA_BF16
+ *   codes   [n_blocks * 16]  bytes
+ *   scales  [n_blocks]       bytes
+ * ---------------------------------------------------------------------------- */
+csa_status csa_mxfp4_quantize(int32_t dtype, const void* x, int64_t n_blocks, uint8_t* codes,
+                              uint8_t* scales, void* stream);
+
+/* ------------------------------------------------------------------------------
+ * Lightning indexer and top-k ("DeepSeek v4" summary, "Compressed Sparse
+ * Attention", lightning indexer; techniques map, "Indexer-selected sparse
+ * attention").  For each query (sequence b, query i at absolute position
+ * t = q_pos[b*n_q+i]) only complete, preceding blocks are visible:
+ * V = min(n_entries[b], floor((t+1)/m)).  For s < V:
+ *     score[s] = sum_h w[h] * max(0, q_idx[h] . k_idx[s])        (no scale)
+ * csa_index_topk keeps the `topk` largest scores (ties by lower index) and writes
+ * their entry indices in ascending index order, then -1 for the remaining slots
+ * when V < topk.  The indexer does not normalise q or k.
+ *
+ *   q_idx  [batch, n_q, idx_heads, idx_dim]  dtype (MXFP4: codes [.., idx_dim/2] bytes)
+ *   q_scale  MXFP4 only: [batch, n_q, idx_heads, idx_dim/32] bytes, else NULL
+ *   w      [batch, n_q, idx_heads] fp32 head weights
+ *   k_idx  [batch, k_cap, idx_dim] dtype (MXFP4: codes [batch, k_cap, idx_dim/2])
+ *   k_scale  MXFP4 only: [batch, k_cap, idx_dim/32] bytes, else NULL
+ *   n_entries [batch] int32 (<= n_max);  q_pos [batch, n_q] int32
+ *   out_idx   [batch, n_q, topk] int32
+ *   out_score [batch, n_q, topk] fp32 score of each selected entry (-inf for -1), or NULL
+ * Supported: CSA_F32 any idx_dim <= 256 and idx_heads <= 128; CSA_BF16 and CSA_MXFP4
+ * with idx_dim == 128 and idx_heads in {32, 64, 96, 128}.  1 <= topk <= 4096,
+ * n_max <= k_cap.
+ * ---------------------------------------------------------------------------- */
+typedef struct {
+  int32_t batch;
+  int32_t n_q;
+  int32_t idx_heads;
+  int32_t idx_dim;
+  int32_t m;
+  int32_t topk;
+  int32_t n_max;      /* upper bound of n_entries[b] over the batch */
+  int32_t k_cap;      /* rows per sequence in k_idx */
+  int32_t dtype;      /* CSA_F32, CSA_BF16 or CSA_MXFP4 (q_idx and k_idx) */
+} csa_index_desc;
+
+size_t csa_index_workspace_size(const csa_index_desc* desc);
+
+/* Scores only: writes score rows [batch, n_q, n_max] fp32 (-inf at s >= V). */
+csa_status csa_index_scores(const csa_index_desc* desc, const void* q_idx, const uint8_t* q_scale,
+                            const float* w, const void* k_idx, const uint8_t* k_scale,
+                            const int32_t* n_entries, const int32_t* q_pos, float* scores,
+                            void* stream);
+
+csa_status csa_index_topk(const csa_index_desc* desc, const void* q_idx, const uint8_t* q_scale,
+                          const float* w, const void* k_idx, const uint8_t* k_scale,
+                          const int32_t* n_entries, const int32_t* q_pos, int32_t* out_idx,
+                          float* out_score, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------
+ * Core multi-query attention ("DeepSeek-V4-Pro" techniques map, "Grouped-query
+ * attention", "Sliding-window attention", "QK normalization"; anthology record,
+ * Key takeaways: RMSNorm on every query head and on the compressed KV head).
+ * All `heads` query heads share one KV head; each KV row is both key and value.
+ * Every query head and every attended row is RMS-normalised:
+ *     x_hat = x * g / sqrt(mean(x^2) + eps),  g = rms_weight (NULL = ones).
+ * The attended set of the query at position t is its compressed entries (sparse:
+ * idx, -1 skipped; dense: every s < V(t)) plus the raw tokens
+ * u in [max(0, t-window+1), t], read from kv_raw row u - raw_base[b].  One softmax
+ * over the whole set with logits scale * q_hat . k_hat (scale <= 0 selects
+ * 1/sqrt(head_dim)); out = sum softmax * k_hat.  An empty set gives out = 0 and
+ * lse = -inf.
+ *
+ *   q      [batch, n_q, heads, head_dim] dtype
+ *   kv     [batch, kv_cap, head_dim]     dtype (compressed entries)
+ *   idx    [batch, n_q, topk] int32 (sparse only)
+ *   n_entries [batch] int32 (dense only, <= n_max)
+ *   kv_raw [batch, raw_cap, head_dim] dtype;  raw_base [batch] int32
+ *   q_pos  [batch, n_q] int32
+ *   out    [batch, n_q, heads, head_dim] dtype
+ *   lse    [batch, n_q, heads] fp32 natural-log softmax denominator, or NULL
+ * Supported: CSA_F32 with head_dim <= 512; CSA_BF16 with head_dim == 512 and heads a
+ * multiple of 16.  q, kv, kv_raw, out 16-byte aligned.
+ * ---------------------------------------------------------------------------- */
+typedef struct {
+  int32_t batch;
+  int32_t n_q;
+  int32_t heads;
+  int32_t head_dim;
+  int32_t topk;       /* sparse: idx slots per query */
+  int32_t m;          /* dense: compression ratio for V(t) */
+  int32_t n_max;      /* dense: upper bound of n_entries[b] */
+  int32_t window;     /* >= 0 */
+  int32_t kv_cap;
+  int32_t raw_cap;
+  float scale;
+  float eps;
+  int32_t dtype;      /* CSA_F32 or CSA_BF16 */
+} csa_mqa_desc;
+
+size_t csa_mqa_workspace_size(const csa_mqa_desc* desc, int32_t dense);
+
+csa_status csa_sparse_mqa(const csa_mqa_desc* desc, const void* q, const void* kv,
+                          const int32_t* idx, const void* kv_raw, const int32_t* raw_base,
+                          const int32_t* q_pos, const float* rms_weight, void* out, float* lse,
+                          void* ws, size_t ws_bytes, void* stream);
+
+csa_status hca_dense_mqa(const csa_mqa_desc* desc, const void* q, const void* kv,
+                         const int32_t* n_entries, const void* kv_raw, const int32_t* raw_base,
+                         const int32_t* q_pos, const float* rms_weight, void* out, float* lse,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------
+ * csa_decode -- one fused CSA step for n_q queries per sequence, stream-ordered:
+ * optional compression of newly completed blocks (kv_job / key_job, as
+ * csa_compress), then the indexer and top-k (as csa_index_topk, writing out_idx),
+ * then sparse MQA over the selected entries plus the window (as csa_sparse_mqa).
+ * index.batch/n_q must equal attn.batch/n_q and index.topk == attn.topk.
+ * ---------------------------------------------------------------------------- */
+typedef struct {
+  csa_compress_desc desc;
+  const void* a;
+  const void* b;
+  const float* za;
+  const float* zb;
+  const float* bias_a;
+  const float* bias_b;
+  void* out;
+} csa_compress_job;
+
+typedef struct {
+  csa_index_desc index;
+  csa_mqa_desc attn;
+  const csa_compress_job* kv_job;   /* NULL = none */
+  const csa_compress_job* key_job;  /* NULL = none */
+  const void* q;
+  const void* kv;
+  const void* kv_raw;
+  const int32_t* raw_base;
+  const int32_t* q_pos;
+  const float* rms_weight;
+  const void* q_idx;
+  const uint8_t* q_idx_scale;
+  const float* w;
+  const void* k_idx;
+  const uint8_t* k_idx_scale;
+  const int32_t* n_entries;
+  int32_t* out_idx;                 /* required: the selected entries */
+  float* out_score;                 /* nullable */
+  void* out;
+  float* lse;                       /* nullable */
+} csa_decode_args;
+
+size_t csa_decode_workspace_size(const csa_decode_args* args);
+csa_status csa_decode(const csa_decode_args* args, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA_H_ */

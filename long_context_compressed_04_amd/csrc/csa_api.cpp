@@ -1,0 +1,295 @@
+// C ABI of libcsa.so: host-side validation and dispatch (declarations and the
+// contract of every entry point are in include/csa.h).
+//
+// Validation runs entirely on the host and makes no HIP call, so a rejected
+// request enqueues nothing and touches no device.
+#include "csa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "csa_kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+csa_status fail(csa_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+csa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return CSA_OK;
+  return fail(CSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// ----------------------------------------------------------------- compress
+csa_status check_compress(const csa_compress_desc* d, const void* a, const void* b, const float* za,
+                          const float* zb, const void* out) {
+  if (!d) return fail(CSA_ERR_NULL, "csa_compress: desc is NULL");
+  if (!a || !b || !za || !zb || !out) return fail(CSA_ERR_NULL, "csa_compress: a, b, za, zb and out are required");
+  if ((d->in_dtype != CSA_F32 && d->in_dtype != CSA_BF16) || (d->out_dtype != CSA_F32 && d->out_dtype != CSA_BF16))
+    return fail(CSA_ERR_DTYPE, "csa_compress: in_dtype/out_dtype must be CSA_F32 or CSA_BF16");
+  if (d->batch < 0 || d->channels < 1 || d->m < 1 || d->m > 256 || d->n_rows < 0 || d->out_cap < 0)
+    return fail(CSA_ERR_SHAPE, "csa_compress: need batch >= 0, channels >= 1, 1 <= m <= 256");
+  if (!(d->zc == 1 || d->zc == d->channels)) return fail(CSA_ERR_SHAPE, "csa_compress: zc must be 1 or channels");
+  if (d->entry_begin < 0 || d->entry_end < d->entry_begin || d->entry_end > d->out_cap)
+    return fail(CSA_ERR_SHAPE, "csa_compress: need 0 <= entry_begin <= entry_end <= out_cap");
+  if (d->entry_end > d->entry_begin) {
+    long first = (long)d->m * d->entry_begin - (d->entry_begin > 0 ? d->m : 0);
+    long last = (long)d->m * d->entry_end;
+    if (first < d->tok_base || last > (long)d->tok_base + d->n_rows)
+      return fail(CSA_ERR_SHAPE, "csa_compress: token rows [%d, %d) do not cover tokens [%ld, %ld)", d->tok_base,
+                  d->tok_base + d->n_rows, first, last);
+  }
+  return CSA_OK;
+}
+
+// ------------------------------------------------------------------- index
+csa_status check_index(const char* fn, const csa_index_desc* d, const void* q, const uint8_t* qs, const float* w,
+                       const void* k, const uint8_t* kscale, const int32_t* ne, const int32_t* qpos) {
+  if (!d) return fail(CSA_ERR_NULL, "%s: desc is NULL", fn);
+  if (!q || !w || !k || !ne || !qpos) return fail(CSA_ERR_NULL, "%s: q_idx, w, k_idx, n_entries, q_pos are required", fn);
+  if (d->batch < 0 || d->n_q < 0 || d->n_max < 0 || d->k_cap < d->n_max || d->m < 1 || d->topk < 1 || d->topk > 4096)
+    return fail(CSA_ERR_SHAPE, "%s: need batch, n_q >= 0, 0 <= n_max <= k_cap, m >= 1, 1 <= topk <= 4096", fn);
+  if (d->dtype == CSA_F32) {
+    if (d->idx_heads < 1 || d->idx_heads > 128 || d->idx_dim < 1 || d->idx_dim > 256)
+      return fail(CSA_ERR_SHAPE, "%s: fp32 indexer needs 1 <= idx_heads <= 128, 1 <= idx_dim <= 256", fn);
+    if ((long)d->idx_heads * d->idx_dim > 16384) return fail(CSA_ERR_SHAPE, "%s: idx_heads * idx_dim > 16384", fn);
+  } else if (d->dtype == CSA_BF16 || d->dtype == CSA_MXFP4) {
+    if (d->idx_dim != 128 || d->idx_heads % 32 != 0 || d->idx_heads < 32 || d->idx_heads > 128)
+      return fail(CSA_ERR_UNSUPPORTED, "%s: bf16/MXFP4 indexer needs idx_dim == 128 and idx_heads in {32,64,96,128}", fn);
+    if (!aligned16(q) || !aligned16(k)) return fail(CSA_ERR_ALIGN, "%s: q_idx and k_idx must be 16-byte aligned", fn);
+    if (d->dtype == CSA_MXFP4) {
+      if (!qs || !kscale) return fail(CSA_ERR_NULL, "%s: MXFP4 needs q_scale and k_scale", fn);
+      if (((uintptr_t)qs & 3u) || ((uintptr_t)kscale & 3u))
+        return fail(CSA_ERR_ALIGN, "%s: q_scale and k_scale must be 4-byte aligned", fn);
+    }
+  } else {
+    return fail(CSA_ERR_DTYPE, "%s: dtype must be CSA_F32, CSA_BF16 or CSA_MXFP4", fn);
+  }
+  return CSA_OK;
+}
+
+csa::IndexArgs index_args(const csa_index_desc* d, const void* q, const uint8_t* qs, const float* w, const void* k,
+                          const uint8_t* ks, const int32_t* ne, const int32_t* qpos) {
+  csa::IndexArgs A;
+  A.batch = d->batch; A.n_q = d->n_q; A.heads = d->idx_heads; A.dim = d->idx_dim; A.m = d->m; A.topk = d->topk;
+  A.n_max = d->n_max; A.k_cap = d->k_cap; A.dtype = d->dtype;
+  A.q = q; A.q_scale = qs; A.w = w; A.k = k; A.k_scale = ks; A.n_entries = ne; A.q_pos = qpos;
+  return A;
+}
+
+size_t index_ws(const csa_index_desc* d) {
+  return round256(sizeof(float) * (size_t)d->batch * d->n_q * (size_t)d->n_max);
+}
+
+// --------------------------------------------------------------------- MQA
+csa_status check_mqa(const char* fn, const csa_mqa_desc* d, int dense, const void* q, const void* kv,
+                     const void* sel, const void* kv_raw, const int32_t* raw_base, const int32_t* qpos,
+                     const void* out) {
+  if (!d) return fail(CSA_ERR_NULL, "%s: desc is NULL", fn);
+  if (!q || !kv || !sel || !kv_raw || !raw_base || !qpos || !out)
+    return fail(CSA_ERR_NULL, "%s: q, kv, %s, kv_raw, raw_base, q_pos and out are required", fn,
+                dense ? "n_entries" : "idx");
+  if (d->batch < 0 || d->n_q < 0 || d->heads < 1 || d->window < 0 || d->kv_cap < 0 || d->raw_cap < 1)
+    return fail(CSA_ERR_SHAPE, "%s: need batch, n_q >= 0, heads >= 1, window >= 0, raw_cap >= 1", fn);
+  if (dense) {
+    if (d->m < 1 || d->n_max < 0 || d->n_max > d->kv_cap) return fail(CSA_ERR_SHAPE, "%s: need m >= 1, 0 <= n_max <= kv_cap", fn);
+  } else if (d->topk < 0 || d->topk > 65536) {
+    return fail(CSA_ERR_SHAPE, "%s: need 0 <= topk <= 65536", fn);
+  }
+  if (!(d->eps >= 0.f) || !std::isfinite(d->scale)) return fail(CSA_ERR_SHAPE, "%s: eps must be >= 0, scale finite", fn);
+  if (d->dtype == CSA_F32) {
+    if (d->head_dim < 1 || d->head_dim > 512) return fail(CSA_ERR_SHAPE, "%s: fp32 path needs 1 <= head_dim <= 512", fn);
+  } else if (d->dtype == CSA_BF16) {
+    if (d->head_dim != 512 || d->heads % 16 != 0)
+      return fail(CSA_ERR_UNSUPPORTED, "%s: bf16 path needs head_dim == 512 and heads a multiple of 16", fn);
+    if (!aligned16(q) || !aligned16(kv) || !aligned16(kv_raw) || !aligned16(out))
+      return fail(CSA_ERR_ALIGN, "%s: q, kv, kv_raw and out must be 16-byte aligned", fn);
+  } else {
+    return fail(CSA_ERR_DTYPE, "%s: dtype must be CSA_F32 or CSA_BF16", fn);
+  }
+  return CSA_OK;
+}
+
+csa::MqaArgs mqa_args(const csa_mqa_desc* d, int dense) {
+  csa::MqaArgs A{};
+  A.batch = d->batch; A.n_q = d->n_q; A.heads = d->heads; A.dim = d->head_dim; A.topk = dense ? 0 : d->topk;
+  A.m = d->m; A.n_max = d->n_max; A.window = d->window; A.kv_cap = d->kv_cap; A.raw_cap = d->raw_cap;
+  A.dense = dense; A.bf16 = d->dtype == CSA_BF16;
+  A.scale = d->scale > 0.f ? d->scale : 1.f / std::sqrt((float)d->head_dim);
+  A.eps = d->eps;
+  return A;
+}
+
+}  // namespace
+
+extern "C" {
+
+int csa_abi_version(void) { return CSA_ABI_VERSION; }
+
+const char* csa_status_string(int s) {
+  switch (s) {
+    case CSA_OK: return "ok";
+    case CSA_ERR_NULL: return "required pointer is NULL";
+    case CSA_ERR_SHAPE: return "inconsistent or unsupported sizes";
+    case CSA_ERR_DTYPE: return "unsupported dtype";
+    case CSA_ERR_ALIGN: return "misaligned pointer";
+    case CSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case CSA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case CSA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* csa_last_error(void) { return g_last_error.c_str(); }
+
+csa_status csa_compress(const csa_compress_desc* d, const void* a, const void* b, const float* za, const float* zb,
+                        const float* bias_a, const float* bias_b, void* out, void* stream) {
+  csa_status st = check_compress(d, a, b, za, zb, out);
+  if (st != CSA_OK) return st;
+  csa::CompressArgs A;
+  A.batch = d->batch; A.channels = d->channels; A.m = d->m; A.zc = d->zc; A.n_rows = d->n_rows;
+  A.tok_base = d->tok_base; A.entry_begin = d->entry_begin; A.entry_end = d->entry_end; A.out_cap = d->out_cap;
+  A.in_bf16 = d->in_dtype == CSA_BF16; A.out_bf16 = d->out_dtype == CSA_BF16;
+  A.a = a; A.b = b; A.za = za; A.zb = zb; A.bias_a = bias_a; A.bias_b = bias_b; A.out = out;
+  return hip_status(csa::launch_compress(A, (hipStream_t)stream), "csa_compress");
+}
+
+csa_status csa_mxfp4_quantize(int32_t dtype, const void* x, int64_t n_blocks, uint8_t* codes, uint8_t* scales,
+                              void* stream) {
+  if (!x || !codes || !scales) return fail(CSA_ERR_NULL, "csa_mxfp4_quantize: x, codes and scales are required");
+  if (dtype != CSA_F32 && dtype != CSA_BF16) return fail(CSA_ERR_DTYPE, "csa_mxfp4_quantize: dtype must be CSA_F32 or CSA_BF16");
+  if (n_blocks < 0) return fail(CSA_ERR_SHAPE, "csa_mxfp4_quantize: n_blocks < 0");
+  if (!aligned16(x) || !aligned16(codes)) return fail(CSA_ERR_ALIGN, "csa_mxfp4_quantize: x and codes must be 16-byte aligned");
+  return hip_status(csa::launch_mxfp4_quantize(dtype == CSA_BF16, x, n_blocks, codes, scales, (hipStream_t)stream),
+                    "csa_mxfp4_quantize");
+}
+
+size_t csa_index_workspace_size(const csa_index_desc* d) { return d ? index_ws(d) : 0; }
+
+csa_status csa_index_scores(const csa_index_desc* d, const void* q, const uint8_t* qs, const float* w, const void* k,
+                            const uint8_t* ks, const int32_t* ne, const int32_t* qpos, float* scores, void* stream) {
+  csa_status st = check_index("csa_index_scores", d, q, qs, w, k, ks, ne, qpos);
+  if (st != CSA_OK) return st;
+  if (!scores) return fail(CSA_ERR_NULL, "csa_index_scores: scores is required");
+  csa::IndexArgs A = index_args(d, q, qs, w, k, ks, ne, qpos);
+  return hip_status(csa::launch_index_scores(A, scores, (hipStream_t)stream), "csa_index_scores");
+}
+
+csa_status csa_index_topk(const csa_index_desc* d, const void* q, const uint8_t* qs, const float* w, const void* k,
+                          const uint8_t* ks, const int32_t* ne, const int32_t* qpos, int32_t* out_idx, float* out_score,
+                          void* ws, size_t ws_bytes, void* stream) {
+  csa_status st = check_index("csa_index_topk", d, q, qs, w, k, ks, ne, qpos);
+  if (st != CSA_OK) return st;
+  if (!out_idx) return fail(CSA_ERR_NULL, "csa_index_topk: out_idx is required");
+  const size_t need = index_ws(d);
+  if (need && (!ws || ws_bytes < need))
+    return fail(CSA_ERR_WORKSPACE, "csa_index_topk: workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : 0);
+  csa::IndexArgs A = index_args(d, q, qs, w, k, ks, ne, qpos);
+  hipStream_t s = (hipStream_t)stream;
+  float* scores = (float*)ws;
+  st = hip_status(csa::launch_index_scores(A, scores, s), "csa_index_topk (scores)");
+  if (st != CSA_OK) return st;
+  return hip_status(csa::launch_topk_rows(A, scores, out_idx, out_score, s), "csa_index_topk (select)");
+}
+
+size_t csa_mqa_workspace_size(const csa_mqa_desc* d, int32_t dense) {
+  if (!d) return 0;
+  csa::MqaArgs A = mqa_args(d, dense);
+  return round256(csa::mqa_workspace_bytes(A));
+}
+
+static csa_status run_mqa(const char* fn, const csa_mqa_desc* d, int dense, const void* q, const void* kv,
+                          const int32_t* idx, const int32_t* ne, const void* kv_raw, const int32_t* raw_base,
+                          const int32_t* qpos, const float* g, void* out, float* lse, void* ws, size_t ws_bytes,
+                          hipStream_t s) {
+  csa::MqaArgs A = mqa_args(d, dense);
+  const size_t need = round256(csa::mqa_workspace_bytes(A));
+  if (need && (!ws || ws_bytes < need))
+    return fail(CSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws ? ws_bytes : 0);
+  A.q = q; A.kv = kv; A.idx = idx; A.n_entries = ne; A.kv_raw = kv_raw; A.raw_base = raw_base; A.q_pos = qpos;
+  A.gamma = g; A.out = out; A.lse = lse;
+  return hip_status(csa::launch_mqa(A, ws, ws_bytes, s), fn);
+}
+
+csa_status csa_sparse_mqa(const csa_mqa_desc* d, const void* q, const void* kv, const int32_t* idx, const void* kv_raw,
+                          const int32_t* raw_base, const int32_t* qpos, const float* g, void* out, float* lse, void* ws,
+                          size_t ws_bytes, void* stream) {
+  csa_status st = check_mqa("csa_sparse_mqa", d, 0, q, kv, idx, kv_raw, raw_base, qpos, out);
+  if (st != CSA_OK) return st;
+  return run_mqa("csa_sparse_mqa", d, 0, q, kv, idx, nullptr, kv_raw, raw_base, qpos, g, out, lse, ws, ws_bytes,
+                 (hipStream_t)stream);
+}
+
+csa_status hca_dense_mqa(const csa_mqa_desc* d, const void* q, const void* kv, const int32_t* ne, const void* kv_raw,
+                         const int32_t* raw_base, const int32_t* qpos, const float* g, void* out, float* lse, void* ws,
+                         size_t ws_bytes, void* stream) {
+  csa_status st = check_mqa("hca_dense_mqa", d, 1, q, kv, ne, kv_raw, raw_base, qpos, out);
+  if (st != CSA_OK) return st;
+  return run_mqa("hca_dense_mqa", d, 1, q, kv, nullptr, ne, kv_raw, raw_base, qpos, g, out, lse, ws, ws_bytes,
+                 (hipStream_t)stream);
+}
+
+static csa_status check_decode(const csa_decode_args* a) {
+  if (!a) return fail(CSA_ERR_NULL, "csa_decode: args is NULL");
+  if (!a->out_idx) return fail(CSA_ERR_NULL, "csa_decode: out_idx is required");
+  if (a->index.batch != a->attn.batch || a->index.n_q != a->attn.n_q || a->index.topk != a->attn.topk)
+    return fail(CSA_ERR_SHAPE, "csa_decode: index and attn must agree on batch, n_q and topk");
+  csa_status st = check_index("csa_decode", &a->index, a->q_idx, a->q_idx_scale, a->w, a->k_idx, a->k_idx_scale,
+                              a->n_entries, a->q_pos);
+  if (st != CSA_OK) return st;
+  st = check_mqa("csa_decode", &a->attn, 0, a->q, a->kv, a->out_idx, a->kv_raw, a->raw_base, a->q_pos, a->out);
+  if (st != CSA_OK) return st;
+  const csa_compress_job* jobs[2] = {a->kv_job, a->key_job};
+  for (const csa_compress_job* j : jobs) {
+    if (!j) continue;
+    st = check_compress(&j->desc, j->a, j->b, j->za, j->zb, j->out);
+    if (st != CSA_OK) return st;
+  }
+  return CSA_OK;
+}
+
+size_t csa_decode_workspace_size(const csa_decode_args* a) {
+  if (!a) return 0;
+  csa::MqaArgs M = mqa_args(&a->attn, 0);
+  return index_ws(&a->index) + round256(csa::mqa_workspace_bytes(M));
+}
+
+csa_status csa_decode(const csa_decode_args* a, void* ws, size_t ws_bytes, void* stream) {
+  csa_status st = check_decode(a);
+  if (st != CSA_OK) return st;
+  const size_t iws = index_ws(&a->index);
+  const size_t need = csa_decode_workspace_size(a);
+  if (need && (!ws || ws_bytes < need))
+    return fail(CSA_ERR_WORKSPACE, "csa_decode: workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : 0);
+  hipStream_t s = (hipStream_t)stream;
+  const csa_compress_job* jobs[2] = {a->kv_job, a->key_job};
+  for (const csa_compress_job* j : jobs) {
+    if (!j) continue;
+    st = csa_compress(&j->desc, j->a, j->b, j->za, j->zb, j->bias_a, j->bias_b, j->out, stream);
+    if (st != CSA_OK) return st;
+  }
+  st = csa_index_topk(&a->index, a->q_idx, a->q_idx_scale, a->w, a->k_idx, a->k_idx_scale, a->n_entries, a->q_pos,
+                      a->out_idx, a->out_score, ws, iws, stream);
+  if (st != CSA_OK) return st;
+  return run_mqa("csa_decode", &a->attn, 0, a->q, a->kv, a->out_idx, nullptr, a->kv_raw, a->raw_base, a->q_pos,
+                 a->rms_weight, a->out, a->lse, (uint8_t*)ws + iws, ws_bytes - iws, s);
+}
+
+}  // extern "C"

@@ -1,0 +1,45 @@
+// Internal launcher interface between the C ABI (csa_api.cpp) and the HIP kernels.
+// All sizes were validated by the caller; launchers only enqueue work.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa {
+
+struct CompressArgs {
+  int batch, channels, m, zc, n_rows, tok_base, entry_begin, entry_end, out_cap;
+  int in_bf16, out_bf16;
+  const void* a; const void* b; const float* za; const float* zb;
+  const float* bias_a; const float* bias_b; void* out;
+};
+hipError_t launch_compress(const CompressArgs& A, hipStream_t s);
+
+hipError_t launch_mxfp4_quantize(int in_bf16, const void* x, int64_t n_blocks, uint8_t* codes,
+                                 uint8_t* scales, hipStream_t s);
+
+// dtype: 0 = fp32, 1 = bf16, 2 = mxfp4
+struct IndexArgs {
+  int batch, n_q, heads, dim, m, topk, n_max, k_cap, dtype;
+  const void* q; const uint8_t* q_scale; const float* w;
+  const void* k; const uint8_t* k_scale;
+  const int32_t* n_entries; const int32_t* q_pos;
+};
+// Score rows [batch*n_q, n_max] (-inf past the visible count).
+hipError_t launch_index_scores(const IndexArgs& A, float* scores, hipStream_t s);
+// Top-k per score row.
+hipError_t launch_topk_rows(const IndexArgs& A, const float* scores, int32_t* out_idx,
+                            float* out_score, hipStream_t s);
+
+struct MqaArgs {
+  int batch, n_q, heads, dim, topk, m, n_max, window, kv_cap, raw_cap, dense, bf16;
+  float scale, eps;
+  const void* q; const void* kv; const int32_t* idx; const int32_t* n_entries;
+  const void* kv_raw; const int32_t* raw_base; const int32_t* q_pos; const float* gamma;
+  void* out; float* lse;
+};
+// Workspace bytes the MQA path needs for these sizes (split partials).
+size_t mqa_workspace_bytes(const MqaArgs& A);
+hipError_t launch_mqa(const MqaArgs& A, void* ws, size_t ws_bytes, hipStream_t s);
+
+}  // namespace csa

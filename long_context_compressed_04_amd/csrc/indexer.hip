@@ -1,0 +1,199 @@
+// Lightning-indexer scores.
+//
+// "DeepSeek v4" summary page, section "Compressed Sparse Attention", lightning
+// indexer: several indexer query heads per query token; the score of each
+// preceding compressed block s is the sum over heads of a per-head weight times
+// ReLU(q_h . K_s).  Techniques map "DeepSeek-V4-Pro", "Indexer-selected sparse
+// attention": 64 indexer heads x 128 dims, entries at or past the causal threshold
+// are invalid.  FP4 activations on this QK path: forum post on the DeepSeek V4
+// paper; techniques map, "FP4 precision for the attention indexer".
+//
+// Kernels
+//  * index_scores_f32: VALU, one thread per entry (fp32 workloads, any shape).
+//  * index_scores_mfma<HB, FP4>: heads on the MFMA M axis (HB blocks of 32 heads),
+//    entries on N (32 per tile).  Each wave keeps TPW key tiles in registers
+//    (B operands loaded straight from HBM, 16 B per lane), then loops over the
+//    workgroup's queries with q staged through LDS, so keys are read once per
+//    query tile.  bf16 uses v_mfma_f32_32x32x16_bf16; MXFP4 uses the block-scaled
+//    v_mfma_scale_f32_32x32x64_f8f6f4 (e2m1 operands, e8m0 scale per 32 k-values).
+//    Epilogue: ReLU, per-head weight, reduction over the 32 rows of each block
+//    (16 in-lane, then the partner lane l^32), one fp32 score per entry.
+#include "csa_device.hpp"
+#include "csa_kernels.hpp"
+
+namespace csa {
+
+// ------------------------------------------------------------------ fp32 (VALU)
+constexpr int kIdxF32Threads = 256;
+
+__global__ __launch_bounds__(kIdxF32Threads) void index_scores_f32(IndexArgs A, float* scores) {
+  extern __shared__ float smem[];
+  const int b = blockIdx.z, qi = blockIdx.y;
+  const int H = A.heads, D = A.dim;
+  float* qs = smem;            // [H * D]
+  float* ws = smem + H * D;    // [H]
+  const long row = (long)b * A.n_q + qi;
+  const float* q = (const float*)A.q + row * H * D;
+  for (int i = threadIdx.x; i < H * D; i += blockDim.x) qs[i] = q[i];
+  for (int i = threadIdx.x; i < H; i += blockDim.x) ws[i] = A.w[row * H + i];
+  __syncthreads();
+  const int ne = min(A.n_entries[b], A.n_max);
+  const int V = visible_entries(A.q_pos[row], ne, A.m);
+  const int s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (s >= A.n_max) return;
+  float total = -INFINITY;
+  if (s < V) {
+    const float* k = (const float*)A.k + ((long)b * A.k_cap + s) * D;
+    total = 0.f;
+    for (int h = 0; h < H; ++h) {
+      float dot = 0.f;
+      for (int i = 0; i < D; ++i) dot = fmaf(qs[h * D + i], k[i], dot);
+      total = fmaf(ws[h], fmaxf(dot, 0.f), total);
+    }
+  }
+  scores[row * A.n_max + s] = total;
+}
+
+// ------------------------------------------------------------ MFMA (bf16 / MXFP4)
+constexpr int kIdxWaves = 4;
+constexpr int kIdxDim = 128;                 // indexer head dim on the MFMA paths
+constexpr int kQRowBf16 = kIdxDim * 2 + 16;  // LDS row stride (bytes), padded
+constexpr int kQRowFp4 = kIdxDim / 2 + 16;
+
+template <int HB, bool FP4, int TPW>
+__global__ __launch_bounds__(kIdxWaves * 64) void index_scores_mfma(IndexArgs A, float* scores, int q_tile) {
+  constexpr int H = HB * 32;
+  constexpr int KS = FP4 ? 2 : 8;           // k-steps over the 128 dims
+  constexpr int QROW = FP4 ? kQRowFp4 : kQRowBf16;
+  __shared__ __attribute__((aligned(16))) uint8_t q_lds[H * QROW];
+  __shared__ uint32_t qs_lds[H];            // FP4: 4 scale bytes per head
+  __shared__ float w_lds[H];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int half = lane >> 5, col = lane & 31;
+  const int b = blockIdx.z;
+  const int chunk0 = blockIdx.x * (kIdxWaves * TPW * 32);
+  const int wave0 = chunk0 + wave * TPW * 32;
+  const int ne = min(A.n_entries[b], A.n_max);
+
+  // ---- keys for this wave's TPW tiles (registers, B operands)
+  uint4 kb[TPW][KS];
+  uint32_t ksc[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int e = wave0 + t * 32 + col;
+    const bool ok = e < ne;
+    if (FP4) {
+      const uint8_t* kr = (const uint8_t*)A.k + ((long)b * A.k_cap + (ok ? e : 0)) * (kIdxDim / 2);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kb[t][ks] = ok ? *(const uint4*)(kr + 32 * ks + 16 * half) : make_uint4(0, 0, 0, 0);
+      ksc[t] = ok ? *(const uint32_t*)(A.k_scale + ((long)b * A.k_cap + e) * (kIdxDim / 32)) : 0x7f7f7f7fu;
+    } else {
+      const uint16_t* kr = (const uint16_t*)A.k + ((long)b * A.k_cap + (ok ? e : 0)) * kIdxDim;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kb[t][ks] = ok ? *(const uint4*)(kr + 16 * ks + 8 * half) : make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  const int q_begin = blockIdx.y * q_tile;
+  const int q_end = min(A.n_q, q_begin + q_tile);
+  for (int qi = q_begin; qi < q_end; ++qi) {
+    const long row = (long)b * A.n_q + qi;
+    // ---- stage q (and its scales) and w for this query in LDS
+    __syncthreads();
+    if (FP4) {
+      const uint8_t* qg = (const uint8_t*)A.q + row * H * (kIdxDim / 2);
+      for (int i = threadIdx.x; i < H * 4; i += blockDim.x) {   // 16 B pieces: 4 per head
+        int h = i >> 2, p = i & 3;
+        *(uint4*)(q_lds + h * QROW + 16 * p) = *(const uint4*)(qg + h * 64 + 16 * p);
+      }
+      for (int h = threadIdx.x; h < H; h += blockDim.x)
+        qs_lds[h] = *(const uint32_t*)(A.q_scale + (row * H + h) * 4);
+    } else {
+      const uint16_t* qg = (const uint16_t*)A.q + row * H * kIdxDim;
+      for (int i = threadIdx.x; i < H * 16; i += blockDim.x) {  // 16 B pieces: 16 per head
+        int h = i >> 4, p = i & 15;
+        *(uint4*)(q_lds + h * QROW + 16 * p) = *(const uint4*)(qg + h * kIdxDim + 8 * p);
+      }
+    }
+    for (int h = threadIdx.x; h < H; h += blockDim.x) w_lds[h] = A.w[row * H + h];
+    __syncthreads();
+
+    const int V = visible_entries(A.q_pos[row], ne, A.m);
+    // weights of the 16 heads this lane's accumulator rows hold, per head block
+    float wl[HB][16];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) wl[hb][r] = w_lds[hb * 32 + 8 * (r / 4) + 4 * half + (r % 4)];
+
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int tile0 = wave0 + t * 32;
+      if (tile0 >= V) break;                 // whole tile masked (uniform per wave)
+      float part = 0.f;
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        const int head = hb * 32 + col;      // A-operand row of this lane
+        f32x16_t acc = {};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          if (FP4) {
+            uint4 a4 = *(const uint4*)(q_lds + head * QROW + 32 * ks + 16 * half);
+            i32x8_t av = {(int)a4.x, (int)a4.y, (int)a4.z, (int)a4.w, 0, 0, 0, 0};
+            i32x8_t bv = {(int)kb[t][ks].x, (int)kb[t][ks].y, (int)kb[t][ks].z, (int)kb[t][ks].w, 0, 0, 0, 0};
+            const int sa = (int)((qs_lds[head] >> (8 * (2 * ks + half))) & 0xff);
+            const int sb = (int)((ksc[t] >> (8 * (2 * ks + half))) & 0xff);
+            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 4, 4, 0, sa, 0, sb);
+          } else {
+            uint4 a4 = *(const uint4*)(q_lds + head * QROW + (16 * ks + 8 * half) * 2);
+            acc = mfma32x32x16(as_bf16x8(a4), as_bf16x8(kb[t][ks]), acc);
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) part = fmaf(wl[hb][r], fmaxf(acc[r], 0.f), part);
+      }
+      part += __shfl_xor(part, 32, 64);
+      const int e = tile0 + col;
+      if (half == 0 && e < A.n_max) scores[row * A.n_max + e] = (e < V) ? part : -INFINITY;
+    }
+    // tiles skipped above still need their masked scores
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int e = wave0 + t * 32 + col;
+      if (wave0 + t * 32 >= V && half == 0 && e < A.n_max) scores[row * A.n_max + e] = -INFINITY;
+    }
+  }
+}
+
+template <int HB, bool FP4>
+static void launch_mfma_hb(const IndexArgs& A, float* scores, hipStream_t s) {
+  constexpr int TPW = 2;
+  const int chunk = kIdxWaves * TPW * 32;
+  const int q_tile = A.n_q >= 64 ? 16 : 1;
+  dim3 grid((A.n_max + chunk - 1) / chunk, (A.n_q + q_tile - 1) / q_tile, A.batch);
+  index_scores_mfma<HB, FP4, TPW><<<grid, kIdxWaves * 64, 0, s>>>(A, scores, q_tile);
+}
+
+hipError_t launch_index_scores(const IndexArgs& A, float* scores, hipStream_t s) {
+  if (A.batch <= 0 || A.n_q <= 0 || A.n_max <= 0) return hipSuccess;
+  if (A.dtype == 0) {
+    dim3 grid((A.n_max + kIdxF32Threads - 1) / kIdxF32Threads, A.n_q, A.batch);
+    size_t lds = sizeof(float) * ((size_t)A.heads * A.dim + A.heads);
+    index_scores_f32<<<grid, kIdxF32Threads, lds, s>>>(A, scores);
+    return hipGetLastError();
+  }
+  const bool fp4 = A.dtype == 2;
+  switch (A.heads / 32) {
+    case 1: fp4 ? launch_mfma_hb<1, true>(A, scores, s) : launch_mfma_hb<1, false>(A, scores, s); break;
+    case 2: fp4 ? launch_mfma_hb<2, true>(A, scores, s) : launch_mfma_hb<2, false>(A, scores, s); break;
+    case 3: fp4 ? launch_mfma_hb<3, true>(A, scores, s) : launch_mfma_hb<3, false>(A, scores, s); break;
+    case 4: fp4 ? launch_mfma_hb<4, true>(A, scores, s) : launch_mfma_hb<4, false>(A, scores, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace csa

@@ -1,0 +1,311 @@
+"""GPU parity: every C-ABI call against the CPU oracle on the same seeded inputs,
+at sizes the oracle finishes in seconds that still span several tiles and a ragged
+tail, plus edge cases.  Full workload sizes are in test_gpu_workloads.py."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from long_context_compressed_04_amd import csa
+from long_context_compressed_04_amd import workloads as W
+
+from _helpers import (assert_bf16_close, assert_f32_close, check_topk_row, dev, host)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    csa.lib()
+
+
+def _i32(x):
+    return torch.as_tensor(np.asarray(x, dtype=np.int32)).cuda()
+
+
+# ------------------------------------------------------------------- compress
+@pytest.mark.parametrize("dtype,m,c,zc,rows,tok_base,e0,e1", [
+    ("f32", 4, 64, 1, 2048, 0, 0, 512),          # the fp32 decode workload's compression
+    ("bf16", 4, 512, 1, 68, 60, 16, 32),          # new-token block with a B-stream lag
+    ("bf16", 4, 128, 1, 40, 0, 0, 10),
+    ("f32", 128, 64, 1, 640, 0, 0, 5),            # HCA ratio
+    ("f32", 1, 32, 1, 9, 0, 0, 9),
+    ("f32", 4, 48, 48, 64, 0, 0, 16),             # per-channel logits
+    ("bf16", 3, 40, 1, 33, 0, 0, 11),             # ragged channels / rows
+])
+def test_compress(dtype, m, c, zc, rows, tok_base, e0, e1):
+    rng = np.random.default_rng(100 + m + c)
+    B = 2
+    A = W.store(rng.standard_normal((B, rows, c)).astype(np.float32), dtype)
+    Bs = W.store(rng.standard_normal((B, rows, c)).astype(np.float32), dtype)
+    zshape = (B, rows) if zc == 1 else (B, rows, c)
+    za = rng.standard_normal(zshape).astype(np.float32)
+    zb = rng.standard_normal(zshape).astype(np.float32)
+    bias_a = rng.standard_normal((m, zc)).astype(np.float32) * 0.5
+    bias_b = rng.standard_normal((m, zc)).astype(np.float32) * 0.5
+    cap = e1 + 3
+    out = torch.zeros((B, cap, c), dtype=torch.float32 if dtype == "f32" else torch.bfloat16, device="cuda")
+    csa.compress(dev(A), dev(Bs), dev(za), dev(zb), m, out, tok_base=tok_base, entry_begin=e0, entry_end=e1,
+                 bias_a=dev(bias_a), bias_b=dev(bias_b))
+    got = host(out)
+    for b in range(B):
+        want = oracle.compress(W.value(A[b]), W.value(Bs[b]), za[b], zb[b], m, bias_a=bias_a, bias_b=bias_b,
+                               tok_base=tok_base, entry_begin=e0, entry_end=e1)
+        if dtype == "f32":
+            assert_f32_close(got[b, e0:e1], want, "compress")
+        else:
+            assert_bf16_close(got[b, e0:e1], want, "compress")
+        assert np.all(got[b, :e0] == 0) and np.all(got[b, e1:] == 0), "wrote outside [e0, e1)"
+
+
+# ---------------------------------------------------------------------- MXFP4
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_mxfp4_quantize_bit_exact(dtype):
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal((97, 128)) * np.exp(rng.uniform(-3, 3, (97, 1)))).astype(np.float32)
+    x[0, :32] = 0.0                                              # all-zero block
+    x[1, :8] = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -1.5]     # exact ties at E = 0
+    x[1, 8] = -0.0
+    x[2, :32] = 1e-41                                            # subnormal block
+    x[3, 0] = 7.9                                                # saturation
+    xs = W.store(x, dtype)
+    codes, scales = csa.mxfp4_quantize(dev(xs))
+    oc, os_ = oracle.mxfp4_quantize(W.value(xs))
+    np.testing.assert_array_equal(scales.cpu().numpy(), os_)
+    np.testing.assert_array_equal(codes.cpu().numpy(), oc)
+
+
+# ----------------------------------------------------------------- indexer
+def _index_case(dtype, B, n_q, HI, dI, N, cap, m, seed, t_list=None):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, n_q, HI, dI)).astype(np.float32)
+    k = rng.standard_normal((B, cap, dI)).astype(np.float32)
+    w = rng.random((B, n_q, HI)).astype(np.float32)
+    n_entries = np.array([N - 7 * b for b in range(B)], dtype=np.int32)
+    if t_list is None:
+        t_list = [[m * N + 5 - 3 * i - 11 * b for i in range(n_q)] for b in range(B)]
+    q_pos = np.array(t_list, dtype=np.int32)
+    return q, k, w, n_entries, q_pos
+
+
+def _oracle_scores(qv, kv, w, n_entries, q_pos, m, b, i):
+    V = oracle.visible(q_pos[b, i], n_entries[b], m)
+    return oracle.index_scores(qv[b, i], w[b, i], kv[b, :V]), V
+
+
+@pytest.mark.parametrize("dtype,B,n_q,HI,dI,N,m,k", [
+    ("f32", 1, 1, 4, 32, 512, 4, 64),            # the fp32 decode workload's indexer
+    ("f32", 2, 3, 5, 24, 300, 4, 32),
+    ("bf16", 2, 1, 64, 128, 3000, 4, 256),        # several tiles + ragged tail
+    ("bf16", 1, 5, 64, 128, 700, 4, 64),
+    ("bf16", 2, 2, 32, 128, 333, 4, 16),
+    ("bf16", 1, 2, 128, 128, 257, 4, 300),        # V < k for some rows
+    ("mxfp4", 2, 1, 64, 128, 2500, 4, 128),
+])
+def test_index_scores_and_topk(dtype, B, n_q, HI, dI, N, m, k):
+    q, kk, w, n_entries, q_pos = _index_case(dtype, B, n_q, HI, dI, N, N + 40, m, seed=HI + N)
+    if dtype == "mxfp4":
+        qc, qsc = csa.mxfp4_quantize(dev(q))
+        kc, ksc = csa.mxfp4_quantize(dev(kk))
+        qv = oracle.mxfp4_dequantize(*oracle.mxfp4_quantize(q))
+        kv = oracle.mxfp4_dequantize(*oracle.mxfp4_quantize(kk))
+        args = dict(q_scale=qsc, k_scale=ksc)
+        qd, kd = qc, kc
+    else:
+        qs, ks = W.store(q, dtype), W.store(kk, dtype)
+        qv, kv = W.value(qs), W.value(ks)
+        args = {}
+        qd, kd = dev(qs), dev(ks)
+    ne_d, qp_d, w_d = _i32(n_entries), _i32(q_pos), dev(w)
+    scores = host(csa.index_scores(qd, w_d, kd, ne_d, qp_d, m=m, n_max=N, **args))
+    idx, sc = csa.index_topk(qd, w_d, kd, ne_d, qp_d, m=m, topk=k, n_max=N, **args)
+    idx = idx.cpu().numpy()
+    for b in range(B):
+        for i in range(n_q):
+            want, V = _oracle_scores(qv, kv, w, n_entries, q_pos, m, b, i)
+            assert np.all(np.isneginf(scores[b, i, V:])), "masked scores must be -inf"
+            assert_f32_close(scores[b, i, :V], want, "scores")
+            check_topk_row(idx[b, i], want, V, k, "topk")
+            # the selection kernel alone: on the GPU's own scores it must be exact
+            exact = oracle.topk(scores[b, i, :V], V, k)
+            np.testing.assert_array_equal(idx[b, i], np.sort(exact[:min(k, V)]).tolist() + [-1] * (k - min(k, V)))
+
+
+def test_topk_ties_and_degenerate_rows():
+    """All-zero weights (every score 0), duplicated keys (exact ties), V == k, V == 0."""
+    B, HI, dI, N, m = 4, 64, 128, 600, 4
+    rng = np.random.default_rng(5)
+    q = W.store(rng.standard_normal((B, 1, HI, dI)).astype(np.float32), "bf16")
+    kk = rng.standard_normal((B, N, dI)).astype(np.float32)
+    kk[1, 100:400] = kk[1, 50]                        # many identical keys in sequence 1
+    kk = W.store(kk, "bf16")
+    w = rng.random((B, 1, HI)).astype(np.float32)
+    w[0] = 0.0                                          # sequence 0: every score is 0
+    n_entries = np.array([N, N, 64, N], dtype=np.int32)
+    q_pos = np.array([[m * N - 1], [m * N - 1], [m * N - 1], [2]], dtype=np.int32)   # seq 3: nothing visible
+    k = 64
+    idx, _ = csa.index_topk(dev(q), dev(w), dev(kk), _i32(n_entries), _i32(q_pos), m=m, topk=k, n_max=N)
+    idx = idx.cpu().numpy()
+    scores = host(csa.index_scores(dev(q), dev(w), dev(kk), _i32(n_entries), _i32(q_pos), m=m, n_max=N))
+    for b in range(B):
+        V = oracle.visible(q_pos[b, 0], n_entries[b], m)
+        exact = oracle.topk(scores[b, 0, :V], V, k)
+        np.testing.assert_array_equal(idx[b, 0], np.sort(exact[:min(k, V)]).tolist() + [-1] * (k - min(k, V)))
+    np.testing.assert_array_equal(idx[0, 0], np.arange(k))      # all ties -> lowest indices
+    np.testing.assert_array_equal(idx[3, 0], -np.ones(k))
+
+
+# ------------------------------------------------------------------------ MQA
+def _mqa_case(dtype, B, n_q, H, d, N, k, window, seed):
+    rng = np.random.default_rng(seed)
+    q = W.store(rng.standard_normal((B, n_q, H, d)).astype(np.float32), dtype)
+    kv = W.store(rng.standard_normal((B, N, d)).astype(np.float32), dtype)
+    raw_cap = window + n_q + 5
+    kv_raw = W.store(rng.standard_normal((B, raw_cap, d)).astype(np.float32), dtype)
+    return q, kv, kv_raw, rng
+
+
+@pytest.mark.parametrize("dtype,B,n_q,H,d,N,k,window", [
+    ("f32", 1, 1, 8, 64, 512, 64, 128),           # the fp32 decode workload's attention
+    ("f32", 2, 2, 3, 40, 100, 17, 5),
+    ("bf16", 2, 1, 128, 512, 2000, 1024, 128),     # many splits
+    ("bf16", 1, 3, 64, 512, 500, 100, 128),
+    ("bf16", 2, 1, 16, 512, 300, 50, 7),
+    ("bf16", 1, 40, 32, 512, 400, 64, 128),        # many queries (one split each)
+])
+def test_sparse_mqa(dtype, B, n_q, H, d, N, k, window):
+    q, kv, kv_raw, rng = _mqa_case(dtype, B, n_q, H, d, N, k, window, seed=H + N + k)
+    idx = np.stack([np.stack([np.sort(rng.choice(N, size=k, replace=False)) for _ in range(n_q)])
+                    for _ in range(B)]).astype(np.int32)
+    idx[:, :, -3:] = -1                                     # some invalid slots
+    if B > 1:
+        idx[1, 0, : k // 2] = -1
+    raw_base = np.array([1000 + 10 * b for b in range(B)], dtype=np.int32)
+    q_pos = np.array([[raw_base[b] + window + 2 + i for i in range(n_q)] for b in range(B)], dtype=np.int32)
+    gamma = (0.5 + rng.random(d)).astype(np.float32)
+    for g in (None, gamma):
+        out, lse = csa.sparse_mqa(dev(q), dev(kv), _i32(idx), dev(kv_raw), _i32(raw_base), _i32(q_pos),
+                                  window=window, rms_weight=None if g is None else dev(g))
+        out, lse = host(out), host(lse)
+        for b in range(B):
+            for i in range(n_q):
+                want, wl = oracle.sparse_mqa(W.value(q[b, i]), W.value(kv[b]), idx[b, i], W.value(kv_raw[b]),
+                                             raw_base[b], q_pos[b, i], window, 1 / np.sqrt(d), 1e-6, g)
+                if dtype == "f32":
+                    assert_f32_close(out[b, i], want, "sparse out")
+                    assert_f32_close(lse[b, i], wl, "sparse lse")
+                else:
+                    assert_bf16_close(out[b, i], want, "sparse out")
+                    np.testing.assert_allclose(lse[b, i], wl, atol=2e-2)
+
+
+@pytest.mark.parametrize("dtype,B,n_q,H,d,N,m,window,t_off", [
+    ("f32", 1, 1, 8, 64, 300, 128, 128, 0),
+    ("f32", 2, 2, 4, 32, 50, 4, 9, -30),           # causal: V < N
+    ("bf16", 2, 1, 128, 512, 1500, 128, 128, 0),
+    ("bf16", 1, 2, 64, 512, 333, 4, 128, -100),
+    ("bf16", 1, 1, 16, 512, 40, 4, 128, -150),       # t < m*N: few entries visible
+])
+def test_dense_mqa(dtype, B, n_q, H, d, N, m, window, t_off):
+    q, kv, kv_raw, rng = _mqa_case(dtype, B, n_q, H, d, N, 0, window, seed=H + N + m)
+    n_entries = np.array([N - 3 * b for b in range(B)], dtype=np.int32)
+    q_pos = np.array([[m * N - 1 + t_off - i for i in range(n_q)] for b in range(B)], dtype=np.int32)
+    raw_base = np.array([max(0, q_pos[b].min() - window + 1) for b in range(B)], dtype=np.int32)
+    out, lse = csa.hca_dense_mqa(dev(q), dev(kv), _i32(n_entries), dev(kv_raw), _i32(raw_base), _i32(q_pos), m=m,
+                                 window=window)
+    out, lse = host(out), host(lse)
+    for b in range(B):
+        for i in range(n_q):
+            want, wl = oracle.dense_mqa(W.value(q[b, i]), W.value(kv[b]), n_entries[b], m, W.value(kv_raw[b]),
+                                        raw_base[b], q_pos[b, i], window, 1 / np.sqrt(d), 1e-6)
+            if dtype == "f32":
+                assert_f32_close(out[b, i], want, "dense out")
+                assert_f32_close(lse[b, i], wl, "dense lse")
+            else:
+                assert_bf16_close(out[b, i], want, "dense out")
+                np.testing.assert_allclose(lse[b, i], wl, atol=2e-2)
+
+
+def test_sparse_topk_covering_everything_equals_dense():
+    """k >= N: CSA over all entries equals HCA on the same cache (GPU vs GPU and oracle)."""
+    B, H, d, N, m, window = 1, 64, 512, 200, 4, 128
+    q, kv, kv_raw, rng = _mqa_case("bf16", B, 1, H, d, N, 0, window, seed=3)
+    t = m * N - 1
+    raw_base = np.array([t - window + 1], dtype=np.int32)
+    q_pos = np.array([[t]], dtype=np.int32)
+    idx = np.concatenate([np.arange(N), -np.ones(56)]).astype(np.int32)[None, None]
+    o1, _ = csa.sparse_mqa(dev(q), dev(kv), _i32(idx), dev(kv_raw), _i32(raw_base), _i32(q_pos), window=window)
+    o2, _ = csa.hca_dense_mqa(dev(q), dev(kv), _i32([N]), dev(kv_raw), _i32(raw_base), _i32(q_pos), m=m,
+                              window=window)
+    assert_bf16_close(host(o1), host(o2), "sparse vs dense")
+
+
+def test_mqa_empty_set_gives_zero():
+    B, H, d = 1, 16, 512
+    q, kv, kv_raw, rng = _mqa_case("bf16", B, 1, H, d, 10, 0, 0, seed=9)
+    idx = -np.ones((1, 1, 8), dtype=np.int32)
+    out, lse = csa.sparse_mqa(dev(q), dev(kv), _i32(idx), dev(kv_raw), _i32([0]), _i32([[5]]), window=0)
+    assert np.all(host(out) == 0) and np.all(np.isneginf(host(lse)))
+
+
+# --------------------------------------------------------------------- decode
+def _run_decode(c, k, window, m):
+    """csa_decode on a workload dict (bf16 caches); returns out, idx."""
+    dt = c["idx_dtype"]
+    if dt == "mxfp4":
+        qd, qsc = csa.mxfp4_quantize(dev(c["qI"][:, None]))
+        kd, ksc = csa.mxfp4_quantize(dev(c["kI"]))
+    else:
+        qd, kd, qsc, ksc = dev(c["qI"][:, None]), dev(c["kI"]), None, None
+    dec = csa.Decoder(dev(c["q"][:, None]), dev(c["kv"]), dev(c["kv_raw"]), _i32(c["raw_base"]),
+                      _i32(c["q_pos"][:, None]), qd, dev(c["w"][:, None]), kd, _i32(c["n_entries"]), m=m, topk=k,
+                      window=window, q_scale=qsc, k_scale=ksc)
+    out, idx = dec()
+    return host(out)[:, 0], idx.cpu().numpy()[:, 0]
+
+
+@pytest.mark.parametrize("B,T,k", [(2, 12000, 256), (3, 4000, 1024)])
+def test_decode_bf16_small(B, T, k):
+    c = W.csa_decode(1, B=B, T=T, H=64, k=k)
+    out, idx = _run_decode(c, k, 128, 4)
+    for b in range(B):
+        t = int(c["q_pos"][b])
+        scores = oracle.index_scores(W.value(c["qI"][b]), c["w"][b], W.value(c["kI"][b]))
+        V = oracle.visible(t, c["N"], 4)
+        check_topk_row(idx[b], scores, V, k, "decode topk")
+        want, _ = oracle.sparse_mqa(W.value(c["q"][b]), W.value(c["kv"][b]), idx[b], W.value(c["kv_raw"][b]),
+                                    c["raw_base"][b], t, 128, c["scale"], c["eps"])
+        assert_bf16_close(out[b], want, "decode out")
+
+
+def test_decode_fp32_workload_end_to_end():
+    """The fp32 single-layer decode: compression of 2048 tokens -> 512 entries on the GPU,
+    then indexer, top-64, window-128 sparse MQA, all against the oracle at 1e-5."""
+    c = W.cfg1()
+    A, Bs, z = c["A"], c["Bs"], c["z"]
+    kv = torch.zeros((1, 512, 64), dtype=torch.float32, device="cuda")
+    csa.compress(dev(A), dev(Bs), dev(z), dev(z), 4, kv)
+    kv_o = oracle.compress(A[0], Bs[0], z[0], z[0], 4)
+    assert_f32_close(host(kv)[0], kv_o, "cfg1 compress")
+    dec = csa.Decoder(dev(c["q"][:, None]), kv, dev(c["kv_raw"]), _i32(c["raw_base"]), _i32(c["q_pos"][:, None]),
+                      dev(c["qI"][:, None]), dev(c["w"][:, None]), dev(c["kI"]), _i32(c["n_entries"]), m=4, topk=64,
+                      window=128)
+    out, idx = dec()
+    out, idx = host(out)[0, 0], idx.cpu().numpy()[0, 0]
+    res = oracle.csa_decode_query(c["q"][0], kv_o, 512, 4, c["qI"][0], c["w"][0], c["kI"][0], 64, c["kv_raw"][0],
+                                  int(c["raw_base"][0]), int(c["q_pos"][0]), 128, c["scale"], c["eps"])
+    check_topk_row(idx, res["scores"], res["visible"], 64, "cfg1 topk")
+    want, _ = oracle.sparse_mqa(c["q"][0], kv_o, idx, c["kv_raw"][0], int(c["raw_base"][0]), int(c["q_pos"][0]), 128,
+                                c["scale"], c["eps"])
+    assert_f32_close(out, want, "cfg1 out")
+
+
+def test_determinism():
+    """Same inputs, same outputs, bit for bit (fixed split boundaries and merge order)."""
+    c = W.csa_decode(2, B=2, T=8000, H=128, k=512)
+    o1, i1 = _run_decode(c, 512, 128, 4)
+    o2, i2 = _run_decode(c, 512, 128, 4)
+    np.testing.assert_array_equal(i1, i2)
+    np.testing.assert_array_equal(o1, o2)
