@@ -42,9 +42,10 @@ struct ItemSource {
   int win_lo;             // first window token
   int raw_base, raw_cap;
   int row_bytes;
+  int idx_off;            // idx[i - idx_off] holds slot i
   __device__ __forceinline__ const uint8_t* row(int i) const {
     if (i < n_first) {
-      int e = idx ? idx[i] : i;
+      int e = idx ? idx[i - idx_off] : i;
       if (e < 0 || e >= kv_rows) return nullptr;
       return kv + (long)e * row_bytes;
     }
@@ -65,6 +66,7 @@ __device__ __forceinline__ void query_items(const MqaArgs& A, int b, long row, i
   src.win_lo = win_lo;
   src.raw_base = A.raw_base[b];
   src.raw_cap = A.raw_cap;
+  src.idx_off = 0;
   if (A.dense) {
     const int ne = min(min(A.n_entries[b], A.n_max), A.kv_cap);
     src.idx = nullptr;
@@ -169,6 +171,7 @@ constexpr int kRowB = kD * 2 + 16;      // LDS row stride in bytes (padded)
 
 struct MqaLaunch {
   int nsplit, ips, n_hg, units, nw;   // nw: waves per workgroup (16 heads each)
+  int slots;                          // index slots of a split copied to LDS
 };
 
 __device__ __forceinline__ i16x4_t lds_read_tr16(const uint8_t* p) {
@@ -178,8 +181,9 @@ __device__ __forceinline__ i16x4_t lds_read_tr16(const uint8_t* p) {
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void mqa_bf16_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  uint8_t* tile = lds;                                   // [kTile][kRowB]
-  float* inv_rms = (float*)(lds + kTile * kRowB);        // [kTile]
+  uint8_t* const tiles = lds;                                    // [2][kTile][kRowB]
+  float* const inv_rms = (float*)(lds + 2 * kTile * kRowB);      // [2][kTile]
+  int32_t* const slot_idx = (int32_t*)(inv_rms + 2 * kTile);     // [L.ips] (sparse)
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, c16 = lane & 15;
@@ -200,6 +204,16 @@ __global__ __launch_bounds__(NW * 64) void mqa_bf16_kernel(MqaArgs A, MqaLaunch 
   query_items(A, b, row, 2, src, total);
   const int it0 = split * L.ips;
   const int it1 = min(total, it0 + L.ips);
+  // index slots of this split, copied once so that row addresses need no global load
+  if (src.idx && L.slots) {
+    for (int i = threadIdx.x; i < L.ips; i += NW * 64) {
+      const int it = it0 + i;
+      slot_idx[i] = (it < min(it1, src.n_first)) ? src.idx[it] : -1;
+    }
+    src.idx = slot_idx;           // item i < n_first reads slot_idx[i - it0]
+    src.idx_off = it0;
+  }
+  __syncthreads();
 
   // ---- normalised q (times g^2) as B operands: dims 32*ks + 8*g + [0, 8)
   bf16x8_t qf[16];
@@ -242,15 +256,29 @@ __global__ __launch_bounds__(NW * 64) void mqa_bf16_kernel(MqaArgs A, MqaLaunch 
 #pragma unroll
   for (int db = 0; db < 32; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int tb = it0; tb < it1; tb += kTile) {
-    // ---- stage 32 rows (each wave loads whole rows: 64 lanes x 16 B) + 1/rms
-    __syncthreads();
+  // Tile pipeline: rows of tile i+1 are fetched into registers while tile i is
+  // computed from LDS; two LDS buffers, one barrier per tile.
+  constexpr int RPW = kTile / NW;   // rows each wave fetches per tile
+  uint4 stage[RPW];
+  bool stage_ok[RPW];
+  auto fetch = [&](int tb) {
 #pragma unroll
-    for (int rr = 0; rr < kTile / NW; ++rr) {
-      const int r = wave + NW * rr;
-      const int item = tb + r;
+    for (int rr = 0; rr < RPW; ++rr) {
+      const int item = tb + wave + NW * rr;
       const uint8_t* p = (item < it1) ? src.row(item) : nullptr;
-      uint4 v = p ? *(const uint4*)(p + 16 * lane) : make_uint4(0, 0, 0, 0);
+      stage_ok[rr] = p != nullptr;
+      stage[rr] = p ? *(const uint4*)(p + 16 * lane) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  if (it0 < it1) fetch(it0);
+  int buf = 0;
+  for (int tb = it0; tb < it1; tb += kTile, buf ^= 1) {
+    uint8_t* const tile = tiles + buf * (kTile * kRowB);
+    float* const irms = inv_rms + buf * kTile;
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr) {
+      const int r = wave + NW * rr;
+      const uint4 v = stage[rr];
       *(uint4*)(tile + r * kRowB + 16 * lane) = v;
       uint32_t w4[4] = {v.x, v.y, v.z, v.w};
       float ss = 0.f;
@@ -260,9 +288,10 @@ __global__ __launch_bounds__(NW * 64) void mqa_bf16_kernel(MqaArgs A, MqaLaunch 
         ss = fmaf(lo, lo, fmaf(hi, hi, ss));
       }
       ss = wave_sum(ss);
-      if (lane == 0) inv_rms[r] = p ? 1.f / sqrtf(ss * (1.f / kD) + A.eps) : 0.f;
+      if (lane == 0) irms[r] = stage_ok[rr] ? 1.f / sqrtf(ss * (1.f / kD) + A.eps) : 0.f;
     }
     __syncthreads();
+    if (tb + kTile < it1) fetch(tb + kTile);
 
     // ---- S^T = K . q^T for items [0,16) and [16,32)
     f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -279,8 +308,8 @@ __global__ __launch_bounds__(NW * 64) void mqa_bf16_kernel(MqaArgs A, MqaLaunch 
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i0 = 4 * g + r, i1 = 16 + 4 * g + r;
-      ir[r] = inv_rms[i0];
-      ir[4 + r] = inv_rms[i1];
+      ir[r] = irms[i0];
+      ir[4 + r] = irms[i1];
       lg[r] = (ir[r] > 0.f) ? s0[r] * sl2 * ir[r] : -INFINITY;
       lg[4 + r] = (ir[4 + r] > 0.f) ? s1[r] * sl2 * ir[4 + r] : -INFINITY;
     }
@@ -349,35 +378,48 @@ __global__ __launch_bounds__(NW * 64) void mqa_bf16_kernel(MqaArgs A, MqaLaunch 
 }
 
 // Fixed-order merge of split partials: out = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
+constexpr int kMaxSplit = 128;
+
 __global__ __launch_bounds__(128) void mqa_combine_kernel(MqaArgs A, MqaLaunch L, const float* part_o,
                                                           const float* part_ml) {
   const int head = blockIdx.x;
   const long row = blockIdx.y;
   const int S = L.nsplit;
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, part_ml[((row * S + s) * A.heads + head) * 2]);
-  float Lsum = 0.f;
-  for (int s = 0; s < S; ++s) {
+  __shared__ float ms[kMaxSplit], ls[kMaxSplit], wts[kMaxSplit];
+  __shared__ float s_M, s_L;
+  for (int s = threadIdx.x; s < S; s += blockDim.x) {
     const float* pm = part_ml + ((row * S + s) * A.heads + head) * 2;
-    Lsum += (pm[0] == -INFINITY) ? 0.f : pm[1] * exp2f(pm[0] - M);
+    ms[s] = pm[0];
+    ls[s] = pm[1];
   }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float M = -INFINITY;
+    for (int s = 0; s < S; ++s) M = fmaxf(M, ms[s]);
+    float Ls = 0.f;
+    for (int s = 0; s < S; ++s) {
+      const float w = (ms[s] == -INFINITY) ? 0.f : exp2f(ms[s] - M);
+      wts[s] = w;
+      Ls += ls[s] * w;
+    }
+    s_M = M;
+    s_L = Ls;
+  }
+  __syncthreads();
+  const float Lsum = s_L;
   const float inv_l = Lsum > 0.f ? 1.f / Lsum : 0.f;
   const int d0 = threadIdx.x * 4;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < S; ++s) {
-    const float ms = part_ml[((row * S + s) * A.heads + head) * 2];
-    if (ms == -INFINITY) continue;
-    const float wgt = exp2f(ms - M);
-    f32x4_t v = *(const f32x4_t*)(part_o + ((row * S + s) * A.heads + head) * kD + d0);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] = fmaf(v[r], wgt, acc[r]);
-  }
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  const float* po = part_o + ((row * S) * A.heads + head) * kD + d0;
+  const long sstride = (long)A.heads * kD;
+#pragma unroll 8
+  for (int s = 0; s < S; ++s) acc += *(const f32x4_t*)(po + s * sstride) * wts[s];
   float v[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) v[r] = acc[r] * inv_l * (A.gamma ? A.gamma[d0 + r] : 1.f);
   uint16_t* orow = (uint16_t*)A.out + (row * A.heads + head) * kD;
   *(uint2*)(orow + d0) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-  if (A.lse && threadIdx.x == 0) A.lse[row * A.heads + head] = Lsum > 0.f ? M * kLn2 + logf(Lsum) : -INFINITY;
+  if (A.lse && threadIdx.x == 0) A.lse[row * A.heads + head] = Lsum > 0.f ? s_M * kLn2 + logf(Lsum) : -INFINITY;
 }
 
 static MqaLaunch plan_mqa(const MqaArgs& A) {
@@ -386,18 +428,27 @@ static MqaLaunch plan_mqa(const MqaArgs& A) {
   L.n_hg = A.heads / (L.nw * 16);
   const long rows = (long)A.batch * A.n_q;
   const int total_max = (A.dense ? A.n_max : A.topk) + A.window;
-  const long target = 512;                        // workgroups to fill 256 CUs twice
-  long want = (target + rows * L.n_hg - 1) / (rows * L.n_hg);
-  int ips = (int)((total_max + want - 1) / (want > 0 ? want : 1));
-  ips = ((ips + kTile - 1) / kTile) * kTile;
-  if (ips < 2 * kTile) ips = 2 * kTile;
-  if (ips > total_max) ips = ((total_max + kTile - 1) / kTile) * kTile;
-  if (ips < kTile) ips = kTile;
-  L.ips = ips;
-  L.nsplit = (total_max + ips - 1) / ips;
-  if (L.nsplit < 1) L.nsplit = 1;
+  const int tiles_max = (total_max + kTile - 1) / kTile;
+  // One workgroup per CU fits (about 370 registers per lane): aim at one round of
+  // at most 256 workgroups, splitting each query's items when there are few queries.
+  long want = 256 / (rows * L.n_hg);
+  if (want < 1) want = 1;
+  int tps = (int)((tiles_max + want - 1) / want);      // tiles per split
+  if (tps < 1) tps = 1;
+  int nsplit = (tiles_max + tps - 1) / tps;
+  if (nsplit > kMaxSplit) {
+    tps = (tiles_max + kMaxSplit - 1) / kMaxSplit;
+    nsplit = (tiles_max + tps - 1) / tps;
+  }
+  L.ips = tps * kTile;
+  L.nsplit = nsplit < 1 ? 1 : nsplit;
   L.units = (int)(rows * L.nsplit);
+  L.slots = (!A.dense && L.ips <= 16384) ? 1 : 0;
   return L;
+}
+
+static size_t mqa_lds_bytes(const MqaLaunch& L) {
+  return (size_t)2 * kTile * kRowB + 2 * kTile * sizeof(float) + (L.slots ? (size_t)L.ips * sizeof(int32_t) : 0);
 }
 
 size_t mqa_workspace_bytes(const MqaArgs& A) {
@@ -424,7 +475,19 @@ hipError_t launch_mqa(const MqaArgs& A, void* ws, size_t ws_bytes, hipStream_t s
     part_o = (float*)ws;
     part_ml = part_o + parts * kD;
   }
-  const size_t lds = (size_t)kTile * kRowB + kTile * sizeof(float);
+  const size_t lds = mqa_lds_bytes(L);
+  static hipError_t attr = [] {
+    hipError_t e = hipSuccess;
+    const void* fns[3] = {(const void*)mqa_bf16_kernel<1>, (const void*)mqa_bf16_kernel<2>,
+                          (const void*)mqa_bf16_kernel<4>};
+    for (const void* fn : fns) {
+      hipError_t r = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+      if (r != hipSuccess) e = r;
+    }
+    return e;
+  }();
+  if (attr != hipSuccess) return attr;
+  if (lds > 160 * 1024) return hipErrorInvalidValue;
   const long groups = ((long)L.units + 7) / 8;
   dim3 grid((unsigned)(groups * 8 * L.n_hg));
   if (L.nw == 4) mqa_bf16_kernel<4><<<grid, 4 * 64, lds, s>>>(A, L, part_o, part_ml);

@@ -7,21 +7,34 @@
 // marked -1.
 //
 // One workgroup (1024 threads) per score row.  Scores map to order-preserving
-// uint32 keys.  A min/max pass finds the bits all visible keys share; MSB-first
-// radix passes (<= 8 bits each, LDS histogram) then narrow the prefix of the k-th
-// largest key, stopping early once the remaining bucket is taken whole.  The final
-// compaction is in index order (two block scans): every key above the threshold
-// prefix, then the lowest-index keys equal to it, so the output is the exact set
-// "score descending, ties to the lower index", sorted by index, -1 padded.
+// uint32 keys; rows of up to kLdsKeys keys are held in LDS (one pass over HBM/L2
+// with every load in flight), longer rows are re-read from global memory.  A
+// min/max pass finds the bits all visible keys share; MSB-first radix passes of up
+// to 11 bits (2048-bin LDS histogram, the threshold digit found with one block
+// scan) narrow the prefix of the k-th largest key, stopping early once the
+// remaining bucket is taken whole.  The final compaction is in index order (two
+// block scans): every key above the threshold prefix, then the lowest-index keys
+// equal to it -- the exact set "score descending, ties to the lower index", sorted
+// by index, -1 padded.
 #include "csa_device.hpp"
 #include "csa_kernels.hpp"
 
 namespace csa {
 
 constexpr int kTopkThreads = 1024;
+constexpr int kBins = 2048;
+constexpr int kDigit = 11;
+constexpr int kLdsKeys = 32768;
 
+template <bool IN_LDS>
 __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(IndexArgs A, const float* scores,
                                                                  int32_t* out_idx, float* out_score) {
+  extern __shared__ uint32_t keys[];   // IN_LDS: [V]
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t tmp[kTopkThreads / 64 + 1];
+  __shared__ uint32_t red_min[kTopkThreads / 64], red_max[kTopkThreads / 64];
+  __shared__ uint32_t s_prefix, s_need, s_cnt;
+
   const long row = blockIdx.x;
   const int b = (int)(row / A.n_q);
   const int k = A.topk;
@@ -31,11 +44,6 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(IndexArgs A, co
   int32_t* oi = out_idx + row * k;
   float* os = out_score ? out_score + row * k : nullptr;
 
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t tmp[kTopkThreads / 64 + 1];
-  __shared__ uint32_t red_min[kTopkThreads / 64], red_max[kTopkThreads / 64];
-  __shared__ uint32_t s_prefix, s_need, s_cnt;
-
   if (V <= k) {  // everything visible is selected
     for (int i = threadIdx.x; i < k; i += blockDim.x) {
       oi[i] = i < V ? i : -1;
@@ -44,11 +52,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(IndexArgs A, co
     return;
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  auto key_at = [&](int i) -> uint32_t { return IN_LDS ? keys[i] : order_key(src[i]); };
 
-  // ---- bits shared by every visible key
+  // ---- load (LDS rows) and the bits every visible key shares
   uint32_t kmin = 0xffffffffu, kmax = 0u;
-  for (int i = threadIdx.x; i < V; i += blockDim.x) {
+#pragma unroll 8
+  for (int i = threadIdx.x; i < V; i += kTopkThreads) {
     uint32_t key = order_key(src[i]);
+    if (IN_LDS) keys[i] = key;
     kmin = min(kmin, key);
     kmax = max(kmax, key);
   }
@@ -69,37 +80,32 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(IndexArgs A, co
 
   // ---- MSB-first radix narrowing of the k-th largest key's prefix
   while (hi > 0) {
-    const int width = hi < 8 ? hi : 8;
+    const int width = hi < kDigit ? hi : kDigit;
     const int shift = hi - width;
     const uint32_t dmask = (1u << width) - 1u;
+    for (int i = threadIdx.x; i < kBins; i += kTopkThreads) hist[i] = 0;
     __syncthreads();
-    for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0;
-    __syncthreads();
-    for (int i = threadIdx.x; i < V; i += blockDim.x) {
-      uint32_t key = order_key(src[i]);
+#pragma unroll 8
+    for (int i = threadIdx.x; i < V; i += kTopkThreads) {
+      uint32_t key = key_at(i);
       if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
     }
     __syncthreads();
-    if (wave == 0) {
-      uint32_t c[4] = {hist[4 * lane], hist[4 * lane + 1], hist[4 * lane + 2], hist[4 * lane + 3]};
-      uint32_t tot = c[0] + c[1] + c[2] + c[3];
-      uint32_t suf = tot;  // inclusive suffix sum over lanes (higher lane = higher bins)
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        uint32_t y = (uint32_t)__shfl_down((int)suf, o, 64);
-        if (lane + o < 64) suf += y;
-      }
-      uint32_t above = suf - tot;
-      if (above < need && need <= suf) {
-        uint32_t cum = above;
-        int d = 3;
-        for (; d > 0; --d) {
-          if (cum + c[d] >= need) break;
-          cum += c[d];
-        }
-        s_prefix = prefix | ((uint32_t)(4 * lane + d) << shift);
-        s_need = need - cum;
-        s_cnt = c[d];
+    // thread t owns bins 2047-2t (upper) and 2046-2t: a scan in thread order counts
+    // every key in higher bins
+    const int bu = kBins - 1 - 2 * threadIdx.x, bl = bu - 1;
+    const uint32_t cu = hist[bu], cl = hist[bl];
+    uint32_t total;
+    const uint32_t above = block_exclusive_scan<kTopkThreads>(cu + cl, tmp, &total);
+    if (above < need && need <= above + cu + cl) {
+      if (above + cu >= need) {
+        s_prefix = prefix | ((uint32_t)bu << shift);
+        s_need = need - above;
+        s_cnt = cu;
+      } else {
+        s_prefix = prefix | ((uint32_t)bl << shift);
+        s_need = need - above - cu;
+        s_cnt = cl;
       }
     }
     __syncthreads();
@@ -107,7 +113,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(IndexArgs A, co
     need = s_need;
     mask |= dmask << shift;
     hi = shift;
-    if (s_cnt == need) break;   // the whole bucket is selected
+    const bool whole = s_cnt == need;
+    __syncthreads();
+    if (whole) break;   // the whole bucket is selected
   }
 
   // ---- index-ordered compaction: keys whose prefix is above, then the first `need`
@@ -117,7 +125,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(IndexArgs A, co
   const int hi_i = min(V, lo + seg);
   uint32_t n_gt = 0, n_eq = 0;
   for (int i = lo; i < hi_i; ++i) {
-    uint32_t kp = order_key(src[i]) & mask;
+    uint32_t kp = key_at(i) & mask;
     n_gt += kp > prefix;
     n_eq += kp == prefix;
   }
@@ -127,8 +135,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(IndexArgs A, co
   uint32_t pos = block_exclusive_scan<kTopkThreads>(n_gt + take_eq, tmp, &tot);
   uint32_t eq_seen = eq_before;
   for (int i = lo; i < hi_i; ++i) {
-    const float sv = src[i];
-    const uint32_t kp = order_key(sv) & mask;
+    const uint32_t kp = key_at(i) & mask;
     bool sel = kp > prefix;
     if (kp == prefix) {
       sel = eq_seen < need;
@@ -136,7 +143,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(IndexArgs A, co
     }
     if (sel && pos < (uint32_t)k) {
       oi[pos] = i;
-      if (os) os[pos] = sv;
+      if (os) os[pos] = src[i];
       ++pos;
     }
   }
@@ -146,7 +153,16 @@ hipError_t launch_topk_rows(const IndexArgs& A, const float* scores, int32_t* ou
                             hipStream_t s) {
   const long rows = (long)A.batch * A.n_q;
   if (rows <= 0) return hipSuccess;
-  topk_rows_kernel<<<dim3((unsigned)rows), kTopkThreads, 0, s>>>(A, scores, out_idx, out_score);
+  if (A.n_max <= kLdsKeys) {
+    const size_t lds = sizeof(uint32_t) * (size_t)A.n_max;
+    static hipError_t attr = hipFuncSetAttribute((const void*)topk_rows_kernel<true>,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 (int)(sizeof(uint32_t) * kLdsKeys));
+    if (attr != hipSuccess) return attr;
+    topk_rows_kernel<true><<<dim3((unsigned)rows), kTopkThreads, lds, s>>>(A, scores, out_idx, out_score);
+  } else {
+    topk_rows_kernel<false><<<dim3((unsigned)rows), kTopkThreads, 0, s>>>(A, scores, out_idx, out_score);
+  }
   return hipGetLastError();
 }
 
