@@ -27,6 +27,8 @@
 // row scales its logit and its softmax weight, and g multiplies the output.
 // Splits write fp32 partials (unnormalised O, running max, sum) that a second
 // kernel combines in fixed split order (deterministic).
+#include <type_traits>
+
 #include "csa_device.hpp"
 #include "csa_kernels.hpp"
 
@@ -732,6 +734,310 @@ __global__ __launch_bounds__(256) void mqa32_kernel(MqaArgs A, MqaLaunch L, floa
   }
 }
 
+// ------------------------- bf16, 32 heads x 256 dims per wave (MFMA 32x32x16, dim-split)
+// A workgroup = 8 waves = 4 head groups of 32 heads x 2 halves of the head dim.  Both
+// waves of a pair take the logits of their half of the dims, swap them through LDS
+// and add them, so each holds the same full S^T; each then accumulates O^T for its
+// own 256 dims only.  This halves the registers a wave needs (O^T 128, q 64), which
+// lets two waves share each SIMD and hide each other's LDS and VALU latency.
+//
+// Gathered rows land in LDS by direct-to-LDS loads, two tiles ahead.  The three tile
+// buffers are separate static LDS objects and the pipeline is unrolled by three, so
+// the compiler can see that reads of one buffer never alias the loads still landing
+// in another (one shared array would force a wait for every load before any LDS
+// read); the barriers are plain s_barrier with explicit LDS waits for the same reason.
+constexpr int kXS = 16;             // logits per lane exchanged within a wave pair
+constexpr int kSlotsLds = 2048;     // index slots of a split held in LDS
+
+__device__ __forceinline__ float rows_total4(const float (&p)[4], int lane) {
+  bool up = (lane & 32) != 0;
+  float a[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float send = up ? p[j] : p[2 + j];
+    const float keep = up ? p[2 + j] : p[j];
+    a[j] = keep + __shfl_xor(send, 32, 64);
+  }
+  up = (lane & 16) != 0;
+  float s = (up ? a[1] : a[0]) + __shfl_xor(up ? a[0] : a[1], 16, 64);
+  s += __shfl_xor(s, 8, 64);
+  s += __shfl_xor(s, 4, 64);
+  s += __shfl_xor(s, 2, 64);
+  s += __shfl_xor(s, 1, 64);
+  return s;   // total of row 2*(lane>>5 & 1) + (lane>>4 & 1)
+}
+
+// Barrier without a memory fence: waits only for this wave's LDS operations, so
+// direct-to-LDS loads of later tiles stay in flight across it (a workgroup fence
+// would wait for them).  The signal fences keep the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+struct RowSrc {
+  const uint8_t* kv;
+  const uint8_t* raw;
+  const int32_t* gidx;   // global index slots (sparse, when not copied to LDS)
+  int it0, it1, n_first, kv_rows, win_lo, raw_base, raw_cap, use_slots, dense;
+};
+
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void mqa32d_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml) {
+  __shared__ __attribute__((aligned(16))) uint8_t tb0[kTile * kRowB2];
+  __shared__ __attribute__((aligned(16))) uint8_t tb1[kTile * kRowB2];
+  __shared__ __attribute__((aligned(16))) uint8_t tb2[kTile * kRowB2];
+  __shared__ float irms[kNB][kTile];
+  __shared__ float xbuf[8][kXS][64];
+  __shared__ int32_t slot[kSlotsLds];
+  __shared__ float qss[8][64];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane >> 5, c32 = lane & 31, dh = wave & 1;
+
+  const int f = blockIdx.x;
+  const int xcd = f & 7, r8 = f >> 3;
+  const int hg = r8 % L.n_hg, ug = r8 / L.n_hg;
+  const int unit = ug * 8 + xcd;
+  if (unit >= L.units) return;
+  const long row = unit / L.nsplit;
+  const int split = unit % L.nsplit;
+  const int b = (int)(row / A.n_q);
+  const int head = hg * 128 + (wave >> 1) * 32 + c32;
+
+  // ---- this wave's half of the query row first (it depends on nothing else)
+  const uint16_t* qrow = (const uint16_t*)A.q + (row * A.heads + head) * kD + 256 * dh;
+  uint4 qraw[16];
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks) qraw[ks] = *(const uint4*)(qrow + 16 * ks + 8 * h);
+
+  // ---- the items of this (query, split)
+  RowSrc R;
+  {
+    ItemSource src;
+    int total;
+    query_items(A, b, row, 2, src, total);
+    R.kv = src.kv; R.raw = src.raw; R.n_first = src.n_first; R.kv_rows = src.kv_rows; R.win_lo = src.win_lo;
+    R.raw_base = src.raw_base; R.raw_cap = src.raw_cap; R.dense = A.dense;
+    R.it0 = split * L.ips;
+    R.it1 = min(total, R.it0 + L.ips);
+    R.gidx = src.idx;
+    R.use_slots = !A.dense;   // the host routes splits longer than kSlotsLds elsewhere
+    if (R.use_slots)
+      for (int i = threadIdx.x; i < L.ips; i += 512) {
+        const int it = R.it0 + i;
+        slot[i] = (it < min(R.it1, R.n_first)) ? src.idx[it] : -1;
+      }
+  }
+  auto resolve = [&](int item) -> const uint8_t* {
+    if (item >= R.it1) return nullptr;
+    if (item < R.n_first) {
+      const int e = R.dense ? item : slot[item - R.it0];
+      return (e >= 0 && e < R.kv_rows) ? R.kv + (long)e * (kD * 2) : nullptr;
+    }
+    const int r = R.win_lo + (item - R.n_first) - R.raw_base;
+    return (r >= 0 && r < R.raw_cap) ? R.raw + (long)r * (kD * 2) : nullptr;
+  };
+
+  // ---- u = q / rms(q) for this wave's dims 256*dh + 16*ks + 8*h + [0, 8); the pair
+  // swaps half-row sums of squares
+  bf16x8_t qf[16];
+  {
+    float ss = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) {
+      const uint32_t w4[4] = {qraw[ks].x, qraw[ks].y, qraw[ks].z, qraw[ks].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float lo = __uint_as_float(w4[k] << 16), hi = __uint_as_float(w4[k] & 0xffff0000u);
+        ss = fmaf(lo, lo, fmaf(hi, hi, ss));
+      }
+    }
+    ss += __shfl_xor(ss, 32, 64);
+    qss[wave][lane] = ss;
+    __syncthreads();   // also publishes the index slots
+    ss += qss[wave ^ 1][lane];
+    const float qinv = 1.f / sqrtf(ss * (1.f / kD) + A.eps);
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) {
+      const uint32_t w4[4] = {qraw[ks].x, qraw[ks].y, qraw[ks].z, qraw[ks].w};
+      uint32_t o4[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        o4[k] = pack_bf16x2(__uint_as_float(w4[k] << 16) * qinv, __uint_as_float(w4[k] & 0xffff0000u) * qinv);
+      qf[ks] = as_bf16x8(make_uint4(o4[0], o4[1], o4[2], o4[3]));
+    }
+  }
+  const float sl2 = A.scale * kLog2e;
+  const float eps = A.eps;
+  float l_run = 0.f;
+  f32x16_t o[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) o[db] = f32x16_t{};
+
+  constexpr int RPW = kTile / 8;   // rows each wave loads per tile
+  const int n_tiles = (R.it1 - R.it0 + kTile - 1) / kTile;
+  uint32_t okm[kNB] = {0, 0, 0};
+  auto buf_ptr = [&](int bi) -> uint8_t* { return bi == 0 ? tb0 : (bi == 1 ? tb1 : tb2); };
+  // Few distinct load instructions (the rows are a rolled loop): the compiler can
+  // track only a handful of in-flight direct-to-LDS loads individually before it
+  // falls back to waiting for all of them at every LDS access.
+  auto issue = [&](int ti, uint8_t* dst) -> uint32_t {
+    uint32_t ok = 0;
+#pragma unroll 1
+    for (int rr = 0; rr < RPW; ++rr) {
+      const uint8_t* p = resolve(R.it0 + ti * kTile + wave + 8 * rr);
+      ok |= (p != nullptr ? 1u : 0u) << rr;
+      load_row_to_lds((p ? p : g_zero_row) + 16 * lane, dst + (wave + 8 * rr) * kRowB2);
+    }
+    return ok;
+  };
+  if (n_tiles > 0) okm[0] = issue(0, tb0);
+  if (n_tiles > 1) okm[1] = issue(1, tb1);
+
+  const int G = lane >> 4, sl = lane & 15;
+  const int vb_off = (4 * h + (sl >> 2)) * kRowB2 + 512 * dh + (16 * (G & 1) + 4 * (sl & 3)) * 2;
+  const int ka_off = c32 * kRowB2 + 512 * dh + 16 * h;
+
+  auto step = [&](auto BUFC, int ti) {
+    constexpr int BUF = decltype(BUFC)::value;
+    uint8_t* const tile = BUF == 0 ? tb0 : (BUF == 1 ? tb1 : tb2);
+    // this wave's rows of tile ti have landed (tile ti+1's loads may still be in
+    // flight; loads complete in issue order)
+    if (ti + 1 < n_tiles) __builtin_amdgcn_s_waitcnt(0x0F70 | RPW);
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
+    {
+      float part[RPW];
+#pragma unroll
+      for (int rr = 0; rr < RPW; ++rr) {
+        const uint4 v = *(const uint4*)(tile + (wave + 8 * rr) * kRowB2 + 16 * lane);
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+        float ss = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float lo = __uint_as_float(w4[k] << 16), hi = __uint_as_float(w4[k] & 0xffff0000u);
+          ss = fmaf(lo, lo, fmaf(hi, hi, ss));
+        }
+        part[rr] = ss;
+      }
+      const float tot = rows_total4(part, lane);
+      const int rr = 2 * ((lane >> 5) & 1) + ((lane >> 4) & 1);
+      if ((lane & 15) == 0)
+        irms[BUF][wave + 8 * rr] = ((okm[BUF] >> rr) & 1u) ? 1.f / sqrtf(tot * (1.f / kD) + eps) : 0.f;
+    }
+    lds_barrier();
+    if (ti + 2 < n_tiles) okm[(BUF + 2) % kNB] = issue(ti + 2, buf_ptr((BUF + 2) % kNB));
+
+    // ---- partial S^T over this wave's 256 dims: 16 k-steps of 16
+    f32x16_t s;
+    {
+      const uint8_t* ka = tile + ka_off;
+      constexpr int PF = 2;
+      uint4 a[PF];
+#pragma unroll
+      for (int j = 0; j < PF; ++j) a[j] = *(const uint4*)(ka + 32 * j);
+      f32x16_t s2[2] = {f32x16_t{}, f32x16_t{}};   // two chains of dependent MFMAs
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) {
+        const uint4 c = a[ks % PF];
+        if (ks + PF < 16) a[ks % PF] = *(const uint4*)(ka + 32 * (ks + PF));
+        s2[ks & 1] = mfma32x32x16(as_bf16x8(c), qf[ks], s2[ks & 1]);
+      }
+      s = s2[0] + s2[1];
+    }
+    // ---- full S^T = own half + partner's half (the same sum in both waves)
+#pragma unroll
+    for (int r = 0; r < kXS; ++r) xbuf[wave][r][lane] = s[r];
+    lds_barrier();
+    // ---- softmax weights: this lane's head over items 8*(r/4) + 4*h + r%4.  LDS
+    // operands first, then branch-free weights (a masked row has inv_rms 0 and
+    // weight 0).  Exponents lie in [-100, 100]: the hardware exp2 is never denormal.
+    float ir[16], xp[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      ir[r] = irms[BUF][8 * (r / 4) + 4 * h + (r % 4)];
+      xp[r] = xbuf[wave ^ 1][r][lane];
+    }
+    float psum = 0.f;
+    uint32_t pk[8];
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      float p2[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const float full = s[r + u] + xp[r + u];
+        const float e = __builtin_amdgcn_exp2f(full * sl2 * ir[r + u]);
+        const float p = ir[r + u] > 0.f ? e : 0.f;
+        psum += p;
+        p2[u] = p * ir[r + u];   // weight on the raw row (its 1/rms folded in)
+      }
+      pk[r / 2] = pack_bf16x2(p2[0], p2[1]);
+    }
+    l_run += psum;
+    const bf16x8_t pb0 = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
+    const bf16x8_t pb1 = as_bf16x8(make_uint4(pk[4], pk[5], pk[6], pk[7]));
+    // ---- O^T += V^T . P^T over this wave's 8 dim blocks (V^T by transposing reads)
+    const uint8_t* vb = tile + vb_off;
+    constexpr int PF = 2;
+    i16x4_t v0[PF], v1[PF];
+    auto vaddr = [&](int k) { return vb + (16 * (k & 1)) * kRowB2 + 64 * (k >> 1); };   // k = 2*db + t
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      v0[j] = lds_read_tr16(vaddr(j));
+      v1[j] = lds_read_tr16(vaddr(j) + 8 * kRowB2);
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const i16x4_t c0 = v0[k % PF], c1 = v1[k % PF];
+      if (k + PF < 16) {
+        v0[k % PF] = lds_read_tr16(vaddr(k + PF));
+        v1[k % PF] = lds_read_tr16(vaddr(k + PF) + 8 * kRowB2);
+      }
+      typedef short i16x8_t __attribute__((ext_vector_type(8)));
+      const i16x8_t vv = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+      o[k >> 1] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, vv), (k & 1) ? pb1 : pb0, o[k >> 1]);
+    }
+  };
+  for (int ti = 0; ti < n_tiles; ti += kNB) {
+    step(std::integral_constant<int, 0>{}, ti);
+    if (ti + 1 < n_tiles) step(std::integral_constant<int, 1>{}, ti + 1);
+    if (ti + 2 < n_tiles) step(std::integral_constant<int, 2>{}, ti + 2);
+  }
+
+  l_run += __shfl_xor(l_run, 32, 64);
+  // o[db][r] holds dim 256*dh + 32*db + 8*(r/4) + 4*h + r%4 of this lane's head
+  if (L.nsplit == 1) {
+    const float inv_l = l_run > 0.f ? 1.f / l_run : 0.f;
+    uint16_t* orow = (uint16_t*)A.out + (row * A.heads + head) * kD + 256 * dh;
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d0 = 32 * db + 8 * j + 4 * h;
+        *(uint2*)(orow + d0) = make_uint2(pack_bf16x2(o[db][4 * j] * inv_l, o[db][4 * j + 1] * inv_l),
+                                          pack_bf16x2(o[db][4 * j + 2] * inv_l, o[db][4 * j + 3] * inv_l));
+      }
+    if (A.lse && h == 0 && dh == 0) A.lse[row * A.heads + head] = l_run > 0.f ? logf(l_run) : -INFINITY;
+  } else {
+    float* po = part_o + (((long)row * L.nsplit + split) * A.heads + head) * kD + 256 * dh;
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *(f32x4_t*)(po + 32 * db + 8 * j + 4 * h) =
+            f32x4_t{o[db][4 * j], o[db][4 * j + 1], o[db][4 * j + 2], o[db][4 * j + 3]};
+    if (h == 0 && dh == 0) {
+      float* pm = part_ml + (((long)row * L.nsplit + split) * A.heads + head) * 2;
+      pm[0] = l_run > 0.f ? 0.f : -INFINITY;
+      pm[1] = l_run;
+    }
+  }
+}
+
 // Fixed-order merge of split partials: out = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
 constexpr int kMaxSplit = 128;
 
@@ -786,11 +1092,11 @@ static MqaLaunch plan_mqa(const MqaArgs& A) {
   // every exp2(logit) normal without a running maximum.
   L.heads32 = A.heads % 128 == 0 && A.gamma == nullptr && A.scale * kLog2e * kD * 1.01f <= 100.f;
   if (L.heads32) {
-    // 32-head waves, all of a 128-head group per workgroup, one workgroup per CU.
-    // Pick the split count from a cost model: waves of <= 256 workgroups times the
-    // tiles each works through (~0.9 us a tile), plus writing and re-reading the
-    // fp32 partials (512 KiB per query and split at ~4 TB/s).
-    L.nw = 4;
+    // One workgroup (8 waves: 4 x 32 heads x 2 dim halves) per CU.  Split count
+    // from a cost model measured on MI355X: ~2.9 us per 32-row tile a workgroup
+    // works through, rounds of <= 256 workgroups, ~0.06 us per (query, split) of
+    // fp32 partials written and merged, ~6 us for the merge kernel itself.
+    L.nw = 8;
     L.n_hg = A.heads / 128;
     double best = 1e30;
     int best_s = 1;
@@ -798,14 +1104,16 @@ static MqaLaunch plan_mqa(const MqaArgs& A) {
       const int tps = (tiles_max + sp - 1) / sp;
       const int s_eff = (tiles_max + tps - 1) / tps;
       const double wgs = (double)rows * L.n_hg * s_eff;
-      const double rounds = (wgs + 255) / 256;
-      const double cost = (int)rounds * tps * 0.9 + (s_eff > 1 ? rows * s_eff * 0.5 / 4.0 * (A.heads / 128) : 0.0);
+      const int rounds = (int)((wgs + 255) / 256);
+      const double cost = rounds * tps * 2.9 + (s_eff > 1 ? 6.0 + 0.06 * rows * L.n_hg * s_eff : 0.0);
       if (cost < best - 1e-9) { best = cost; best_s = s_eff; }
     }
     const int tps = (tiles_max + best_s - 1) / best_s;
     L.ips = tps * kTile;
     L.nsplit = (tiles_max + tps - 1) / tps;
-  } else {
+    if (!A.dense && L.ips > kSlotsLds) L.heads32 = 0;   // index slots must fit in LDS
+  }
+  if (!L.heads32) {
     L.nw = (A.heads % 64 == 0) ? 4 : ((A.heads % 32 == 0) ? 2 : 1);
     L.n_hg = A.heads / (L.nw * 16);
     // One workgroup per CU fits (about 380 registers per lane): aim at one round of
@@ -833,7 +1141,7 @@ constexpr int kMaxDynLds = 152 * 1024;
 
 static size_t mqa_lds_bytes(const MqaLaunch& L) {
   const size_t slots = L.slots ? (size_t)L.ips * sizeof(int32_t) : 0;
-  if (L.heads32) return (size_t)kNB * kTile * kRowB2 + kNB * kTile * sizeof(float) + slots;
+  if (L.heads32) return 0;   // static LDS only
   return (size_t)2 * kTile * kRowB + 2 * kTile * sizeof(float) + kD * sizeof(float) + slots;
 }
 
@@ -875,8 +1183,8 @@ hipError_t launch_mqa(const MqaArgs& A, void* ws, size_t ws_bytes, hipStream_t s
   const size_t lds = mqa_lds_bytes(L);
   static hipError_t attr = [] {
     hipError_t e = hipSuccess;
-    const void* fns[4] = {(const void*)mqa_bf16_kernel<1>, (const void*)mqa_bf16_kernel<2>,
-                          (const void*)mqa_bf16_kernel<4>, (const void*)mqa32_kernel};
+    const void* fns[3] = {(const void*)mqa_bf16_kernel<1>, (const void*)mqa_bf16_kernel<2>,
+                          (const void*)mqa_bf16_kernel<4>};
     for (const void* fn : fns) {
       hipError_t r = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxDynLds);
       if (r != hipSuccess) e = r;
@@ -887,7 +1195,7 @@ hipError_t launch_mqa(const MqaArgs& A, void* ws, size_t ws_bytes, hipStream_t s
   if (lds > (size_t)kMaxDynLds) return hipErrorInvalidValue;
   const long groups = ((long)L.units + 7) / 8;
   dim3 grid((unsigned)(groups * 8 * L.n_hg));
-  if (L.heads32) mqa32_kernel<<<grid, 256, lds, s>>>(A, L, part_o, part_ml);
+  if (L.heads32) mqa32d_kernel<<<grid, 512, lds, s>>>(A, L, part_o, part_ml);
   else if (L.nw == 4) mqa_bf16_kernel<4><<<grid, 4 * 64, lds, s>>>(A, L, part_o, part_ml);
   else if (L.nw == 2) mqa_bf16_kernel<2><<<grid, 2 * 64, lds, s>>>(A, L, part_o, part_ml);
   else mqa_bf16_kernel<1><<<grid, 64, lds, s>>>(A, L, part_o, part_ml);
