@@ -1,19 +1,31 @@
 #!/usr/bin/env python3
-"""Benchmark: CSA decode at 64K context (8 sequences x 16,384 compressed entries,
-128 query heads x 512, indexer 64 x 128, top-1024, 128-token window) on one MI355X.
+"""Benchmark of the CSA / HCA attention step on one MI355X.
 
-One step = one fused csa_decode call: lightning indexer over every visible index
-key, causal top-1024, sparse MQA over the selected entries plus the window (RMSNorm
-folded in).  Inputs are resident in HBM before timing starts.  Each step reads a
-different replica of the caches, so that the 256 MB Infinity Cache cannot serve a
-step from the previous one (cold-cache HBM numbers; a warm figure is reported too).
+Default workload (csa_decode_64k): 8 sequences at 64K context, m = 4 (16,384
+compressed entries each), 128 query heads x 512, indexer 64 heads x 128, top-1024,
+128-token window.  One step = one fused csa_decode call: lightning indexer over
+every visible index key, causal top-1024, sparse MQA over the selected entries plus
+the window (RMSNorm folded in).  Other workloads (--workload):
+  hca_decode_1m      4 sequences at 1M context, m = 128 (8,192 entries), dense MQA
+  csa_decode_1m_fp4  1 sequence at 1M context (262,144 entries), MXFP4 indexer
+                     (the per-step query quantisation included), top-1024, MQA
+  csa_prefill_4k     4,096 new queries on 61,440 prior tokens: compression of the new
+                     blocks (KV and index keys), indexer + top-1024 per query, MQA
 
-Prints ONE JSON line.  Also reports the dominant kernel (the indexer) against the
-HBM roofline, timed live with HIP events on its own stream, and the CPU oracle's
-throughput on a bounded sample of the same workload.
+Inputs are seeded synthetic data resident in HBM before timing starts.  Decode
+steps cycle through replicas of every cache so that the 256 MB Infinity Cache
+cannot serve one step from the previous (cold-cache numbers; a warm-cache figure
+with a single replica is reported too).  The timed steps are replayed from a HIP
+graph.
+
+Prints ONE JSON line.  `roofline` is for the kernel that takes the largest share of
+the step, timed live with HIP events that the library records on the kernel's own
+stream (eager launches); `kernels` lists every kernel of the step.  `traffic` comes
+from the committed FETCH_SIZE / WRITE_SIZE counter summary when the kernel's sources
+are unchanged since it was taken.  `cpu_baseline` times the CPU oracle on a bounded
+sample of the same workload.
 """
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -25,7 +37,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-MFMA_BF16_PEAK_TFLOPS = 2500.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "mxfp4": 10100.0}
+WORKLOADS = ["csa_decode_64k", "hca_decode_1m", "csa_decode_1m_fp4", "csa_prefill_4k"]
+CALIB_BYTES = 256 << 20
 
 
 def parse():
@@ -33,153 +47,468 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--replicas", type=int, default=16)
+    p.add_argument("--workload", default="csa_decode_64k", choices=WORKLOADS)
+    p.add_argument("--replicas", type=int, default=16, help="cache replicas cycled by decode steps")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--graph", type=int, default=1, help="replay the step from a HIP graph")
+    p.add_argument("--graph", type=int, default=1, help="replay the timed steps from a HIP graph")
+    p.add_argument("--pmc-pass", action="store_true",
+                   help="counter-collection pass: a few eager steps plus one calibration copy of "
+                        "%d MiB, no timing output" % (CALIB_BYTES >> 20))
     return p.parse_args()
 
 
-def file_hash(*paths):
-    h = hashlib.sha256()
-    for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+# ------------------------------------------------------------------------------------
+class Step:
+    """One workload: its inputs on the GPU, a step launcher, and per-kernel algorithmic
+    work (bytes for HBM-bound kernels, flops for MFMA-bound ones) per launch."""
+    name = ""
+    metric = ""
+    tokens = 1
+    replicas = 1
+
+    def launch(self, i):
+        raise NotImplementedError
+
+    def algorithmic(self, kernel):
+        return None
 
 
+def _torch():
+    import torch
+    return torch
+
+
+def to_dev(x, dev):
+    torch = _torch()
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(x).to(dev)
+
+
+def i32(x, dev):
+    torch = _torch()
+    return torch.as_tensor(np.asarray(x, dtype=np.int32)).to(dev)
+
+
+class CsaDecode64k(Step):
+    name = "csa_decode_64k"
+    metric = "CSA decode tokens/s at 64K context (one layer, 8 sequences)"
+
+    def __init__(self, dev, R):
+        from long_context_compressed_04_amd import csa
+        from long_context_compressed_04_amd import workloads as W
+        self.B, self.T, self.m, self.H, self.d, self.HI, self.dI, self.k, self.w = 8, 65536, 4, 128, 512, 64, 128, \
+            1024, 128
+        self.N = self.T // self.m
+        self.tokens = self.B
+        self.replicas = R
+        c = W.csa_decode(0, B=self.B, T=self.T, m=self.m, H=self.H, d=self.d, HI=self.HI, dI=self.dI, k=self.k,
+                         window=self.w)
+        base = dict(q=to_dev(c["q"][:, None], dev), kv=to_dev(c["kv"], dev), kv_raw=to_dev(c["kv_raw"], dev),
+                    qI=to_dev(c["qI"][:, None], dev), w=to_dev(c["w"][:, None], dev), kI=to_dev(c["kI"], dev))
+        rb, qp, ne = i32(c["raw_base"], dev), i32(c["q_pos"][:, None], dev), i32(c["n_entries"], dev)
+        reps = [base] + [{key: t.clone() for key, t in base.items()} for _ in range(R - 1)]
+        self.decs = [csa.Decoder(r["q"], r["kv"], r["kv_raw"], rb, qp, r["qI"], r["w"], r["kI"], ne, m=self.m,
+                                 topk=self.k, window=self.w) for r in reps]
+        self.config = {"workload": self.name, "batch": self.B, "context": self.T, "compress_ratio": self.m,
+                       "entries": self.N, "heads": self.H, "head_dim": self.d, "idx_heads": self.HI,
+                       "idx_dim": self.dI, "topk": self.k, "window": self.w, "cache_replicas": R}
+        B, N, k, w, d, H, HI, dI = self.B, self.N, self.k, self.w, self.d, self.H, self.HI, self.dI
+        self.step_bytes = B * N * dI * 2 + B * (k + w) * d * 2 + 2 * B * H * d * 2 + B * HI * dI * 2 + B * HI * 4 \
+            + B * k * 4
+        self.step_flops = 2.0 * B * N * HI * dI + 4.0 * B * H * d * (k + w)
+
+    def launch(self, i):
+        self.decs[i % self.replicas]()
+
+    def algorithmic(self, kernel):
+        B, N, k, w, d, H, HI, dI = self.B, self.N, self.k, self.w, self.d, self.H, self.HI, self.dI
+        if kernel == "index_scores_bf16":
+            return "hbm", B * N * dI * 2 + B * HI * dI * 2 + B * HI * 4 + B * N * 4
+        if kernel == "topk":
+            return "hbm", B * N * 4 + B * k * 4
+        if kernel.startswith("mqa_bf16"):
+            return "hbm", B * (k + w) * d * 2 + 2 * B * H * d * 2 + B * k * 4
+        return None
+
+    def cpu_baseline(self):
+        import oracle
+        from long_context_compressed_04_amd import workloads as W
+        c = W.csa_decode(0, B=self.B, T=self.T, m=self.m, H=self.H, d=self.d, HI=self.HI, dI=self.dI, k=self.k,
+                         window=self.w)
+        vals = [(W.value(c["q"][b]), W.value(c["kv"][b]), W.value(c["qI"][b]), c["w"][b], W.value(c["kI"][b]),
+                 W.value(c["kv_raw"][b]), int(c["raw_base"][b]), int(c["q_pos"][b])) for b in range(self.B)]
+        n, t0 = 0, time.perf_counter()
+        while True:     # sequences in turn until at least 10 s of work
+            q, kv, qI, w, kI, raw, rb, t = vals[n % len(vals)]
+            oracle.csa_decode_query(q, kv, c["N"], self.m, qI, w, kI, self.k, raw, rb, t, self.w, c["scale"],
+                                    c["eps"])
+            n += 1
+            secs = time.perf_counter() - t0
+            if secs >= 10.0:
+                break
+        return {"value": round(n / secs, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                "sample": "%d whole decode steps of one sequence each (indexer over 16,384 keys, top-1024, MQA over "
+                          "1,152 rows x 128 heads), fp64, single thread, %.1f s" % (n, secs)}
+
+
+class HcaDecode1m(Step):
+    name = "hca_decode_1m"
+    metric = "HCA decode tokens/s at 1M context (one layer, 4 sequences)"
+
+    def __init__(self, dev, R):
+        torch = _torch()
+        from long_context_compressed_04_amd import csa
+        from long_context_compressed_04_amd import workloads as W
+        c = W.cfg3()
+        self.c = c
+        self.B, self.N, self.m, self.H, self.d, self.w = 4, c["N"], 128, 128, 512, 128
+        self.tokens = self.B
+        self.replicas = R
+        base = dict(q=to_dev(c["q"][:, None], dev), kv=to_dev(c["kv"], dev), kv_raw=to_dev(c["kv_raw"], dev))
+        self.rb, self.qp, self.ne = i32(c["raw_base"], dev), i32(c["q_pos"][:, None], dev), i32(c["n_entries"], dev)
+        self.reps = [base] + [{key: t.clone() for key, t in base.items()} for _ in range(R - 1)]
+        self.out = torch.empty_like(base["q"])
+        self.lse = torch.empty(base["q"].shape[:3], dtype=torch.float32, device=dev)
+        d = csa._mqa_desc(base["q"], base["kv"], base["kv_raw"], m=self.m, n_max=self.N, window=self.w)
+        import ctypes
+        self.ws = torch.zeros(max(1, csa.lib().csa_mqa_workspace_size(ctypes.byref(d), 1)), dtype=torch.uint8,
+                              device=dev)
+        self.csa = csa
+        self.config = {"workload": self.name, "batch": self.B, "context": 1 << 20, "compress_ratio": self.m,
+                       "entries": self.N, "heads": self.H, "head_dim": self.d, "window": self.w,
+                       "cache_replicas": R}
+        B, N, w, d, H = self.B, self.N, self.w, self.d, self.H
+        self.step_bytes = B * (N + w) * d * 2 + 2 * B * H * d * 2
+        self.step_flops = 4.0 * B * H * d * (N + w)
+
+    def launch(self, i):
+        r = self.reps[i % self.replicas]
+        self.csa.hca_dense_mqa(r["q"], r["kv"], self.ne, r["kv_raw"], self.rb, self.qp, m=self.m, window=self.w,
+                               workspace=self.ws, out=self.out, lse=self.lse)
+
+    def algorithmic(self, kernel):
+        if kernel.startswith("mqa_bf16"):
+            return "hbm", self.step_bytes
+        return None
+
+    def cpu_baseline(self):
+        import oracle
+        from long_context_compressed_04_amd import workloads as W
+        c = self.c
+        vals = [(W.value(c["q"][b]), W.value(c["kv"][b]), W.value(c["kv_raw"][b]), int(c["raw_base"][b]),
+                 int(c["q_pos"][b])) for b in range(self.B)]
+        n, t0 = 0, time.perf_counter()
+        while True:     # sequences in turn until at least 10 s of work
+            q, kv, raw, rb, t = vals[n % len(vals)]
+            oracle.dense_mqa(q, kv, self.N, self.m, raw, rb, t, self.w, c["scale"], c["eps"])
+            n += 1
+            secs = time.perf_counter() - t0
+            if secs >= 10.0:
+                break
+        return {"value": round(n / secs, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                "sample": "%d decode steps of one sequence each (dense MQA over 8,320 rows x 128 heads), fp64, "
+                          "single thread, %.1f s" % (n, secs)}
+
+
+class CsaDecode1mFp4(Step):
+    name = "csa_decode_1m_fp4"
+    metric = "CSA decode tokens/s at 1M context with the MXFP4 indexer (one layer, 1 sequence)"
+
+    def __init__(self, dev, R):
+        torch = _torch()
+        from long_context_compressed_04_amd import csa
+        from long_context_compressed_04_amd import workloads as W
+        c = W.cfg4()
+        self.c = c
+        self.N, self.m, self.H, self.d, self.HI, self.dI, self.k, self.w = c["N"], 4, 128, 512, 64, 128, 1024, 128
+        self.tokens = 1
+        self.replicas = R
+        self.csa = csa
+        qI = to_dev(c["qI"][:, None], dev)
+        kI = to_dev(c["kI"], dev)
+        base = dict(q=to_dev(c["q"][:, None], dev), kv=to_dev(c["kv"], dev), kv_raw=to_dev(c["kv_raw"], dev), qI=qI)
+        # index keys are quantised once, when the cache is written
+        kc, ks = csa.mxfp4_quantize(kI)
+        base["kc"], base["ks"] = kc, ks
+        del kI
+        rb, qp, ne = i32(c["raw_base"], dev), i32(c["q_pos"][:, None], dev), i32(c["n_entries"], dev)
+        w = to_dev(c["w"][:, None], dev)
+        reps = [base] + [{key: t.clone() for key, t in base.items()} for _ in range(R - 1)]
+        self.reps = reps
+        for r in reps:
+            r["qc"], r["qs"] = csa.mxfp4_quantize(r["qI"])
+        self.decs = [csa.Decoder(r["q"], r["kv"], r["kv_raw"], rb, qp, r["qc"], w, r["kc"], ne, m=self.m,
+                                 topk=self.k, window=self.w, q_scale=r["qs"], k_scale=r["ks"]) for r in reps]
+        self.config = {"workload": self.name, "batch": 1, "context": 1 << 20, "compress_ratio": self.m,
+                       "entries": self.N, "heads": self.H, "head_dim": self.d, "idx_heads": self.HI,
+                       "idx_dim": self.dI, "idx_dtype": "mxfp4", "topk": self.k, "window": self.w,
+                       "cache_replicas": R}
+        N, k, w, d, H, HI, dI = self.N, self.k, self.w, self.d, self.H, self.HI, self.dI
+        self.key_bytes = N * (dI // 2 + dI // 32)
+        self.step_bytes = self.key_bytes + (k + w) * d * 2 + 2 * H * d * 2 + HI * dI * 2 + HI * 4 + k * 4
+        self.step_flops = 2.0 * N * HI * dI + 4.0 * H * d * (k + w)
+
+    def launch(self, i):
+        r = self.reps[i % self.replicas]
+        self.csa.mxfp4_quantize(r["qI"], r["qc"], r["qs"])
+        self.decs[i % self.replicas]()
+
+    def algorithmic(self, kernel):
+        N, k, w, d, H, HI, dI = self.N, self.k, self.w, self.d, self.H, self.HI, self.dI
+        if kernel == "index_scores_mxfp4":
+            return "hbm", self.key_bytes + HI * (dI // 2 + dI // 32) + HI * 4 + N * 4
+        if kernel == "topk":
+            return "hbm", N * 4 + k * 4
+        if kernel == "mxfp4_quantize":
+            return "hbm", HI * dI * 2 + HI * (dI // 2 + dI // 32)
+        if kernel.startswith("mqa_bf16"):
+            return "hbm", (k + w) * d * 2 + 2 * H * d * 2 + k * 4
+        return None
+
+    def cpu_baseline(self):
+        import oracle
+        from long_context_compressed_04_amd import workloads as W
+        c = self.c
+        q, kv, raw = W.value(c["q"][0]), W.value(c["kv"][0]), W.value(c["kv_raw"][0])
+        kc, ksc = oracle.mxfp4_quantize(c["kI"][0])
+        k_deq = oracle.mxfp4_dequantize(kc, ksc)      # at cache write, not per step
+        n, t0 = 0, time.perf_counter()
+        while True:
+            q_deq = oracle.mxfp4_dequantize(*oracle.mxfp4_quantize(c["qI"][0]))
+            oracle.csa_decode_query(q, kv, self.N, self.m, q_deq, c["w"][0], k_deq, self.k, raw,
+                                    int(c["raw_base"][0]), int(c["q_pos"][0]), self.w, c["scale"], c["eps"])
+            n += 1
+            secs = time.perf_counter() - t0
+            if secs >= 10.0:
+                break
+        return {"value": round(n / secs, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                "sample": "%d whole decode steps (query quantisation, indexer over 262,144 dequantised keys, "
+                          "top-1024, MQA over 1,152 rows x 128 heads), fp64, single thread, %.1f s" % (n, secs)}
+
+
+class CsaPrefill4k(Step):
+    name = "csa_prefill_4k"
+    metric = "CSA prefill tokens/s (4,096 new queries on 61,440 prior tokens, one layer)"
+
+    def __init__(self, dev, R):
+        torch = _torch()
+        from long_context_compressed_04_amd import csa
+        from long_context_compressed_04_amd import workloads as W
+        c = W.cfg5()
+        self.c = c
+        self.csa = csa
+        self.replicas = 1
+        N, P, d, dI = c["N"], c["P"], c["d"], c["dI"]
+        self.N, self.P, self.Q, self.H, self.d, self.HI, self.dI, self.k, self.w, self.m = \
+            N, P, c["n_new"], c["H"], d, c["HI"], dI, c["k"], c["window"], c["m"]
+        self.tokens = self.Q
+        self.kv = torch.zeros((1, N, d), dtype=torch.bfloat16, device=dev)
+        self.kI = torch.zeros((1, N, dI), dtype=torch.bfloat16, device=dev)
+        self.kv[0, :P] = to_dev(c["kv_prior"], dev)
+        self.kI[0, :P] = to_dev(c["kI_prior"], dev)
+        self.A, self.Bs, self.z = to_dev(c["A"][None], dev), to_dev(c["Bs"][None], dev), to_dev(c["z"][None], dev)
+        self.AI, self.BI, self.zI = to_dev(c["AI"][None], dev), to_dev(c["BI"][None], dev), to_dev(c["zI"][None], dev)
+        self.q, self.qI, self.wt = to_dev(c["q"][None], dev), to_dev(c["qI"][None], dev), to_dev(c["w"][None], dev)
+        self.raw = to_dev(c["kv_raw"][None], dev)
+        self.q_pos = i32(c["q_pos"][None], dev)
+        self.rb = i32([c["raw_base"]], dev)
+        self.ne = i32([N], dev)
+        self.tb = c["tok_base"]
+        import ctypes
+        di = csa._index_desc(self.qI, self.kI, self.m, self.k, None, csa.BF16)
+        self.idx_ws = torch.zeros(csa.lib().csa_index_workspace_size(ctypes.byref(di)), dtype=torch.uint8,
+                                  device=dev)
+        dm = csa._mqa_desc(self.q, self.kv, self.raw, topk=self.k, window=self.w)
+        self.mqa_ws = torch.zeros(max(1, csa.lib().csa_mqa_workspace_size(ctypes.byref(dm), 0)), dtype=torch.uint8,
+                                  device=dev)
+        self.idx = torch.empty((1, self.Q, self.k), dtype=torch.int32, device=dev)
+        self.score = torch.empty((1, self.Q, self.k), dtype=torch.float32, device=dev)
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty(self.q.shape[:3], dtype=torch.float32, device=dev)
+        self.config = {"workload": self.name, "batch": 1, "new_tokens": self.Q, "prior_tokens": c["T_prior"],
+                       "compress_ratio": self.m, "entries": N, "heads": self.H, "head_dim": d,
+                       "idx_heads": self.HI, "idx_dim": dI, "topk": self.k, "window": self.w}
+        vis = np.minimum(N, (c["q_pos"].astype(np.int64) + 1) // self.m)
+        self.pairs = int(vis.sum())
+        sel = np.minimum(vis, self.k) + np.minimum(c["q_pos"].astype(np.int64) + 1, self.w)
+        self.mqa_rows = int(sel.sum())
+        R_tok = self.Q + self.m
+        self.compress_bytes = {d: R_tok * d * 2 * 2 + R_tok * 4 * 2 + (N - P) * d * 2 for d in (d, dI)}
+        self.step_flops = 2.0 * self.pairs * self.HI * dI + 4.0 * self.H * d * self.mqa_rows
+        # compulsory: the compression's token rows, logits and new entries; every index
+        # key once; q, out, q_idx, w and the selection of every query; every compressed
+        # entry and raw window row at most once
+        self.step_bytes = sum(self.compress_bytes.values()) + N * dI * 2 + \
+            self.Q * (self.H * d * 2 * 2 + self.HI * dI * 2 + self.HI * 4 + self.k * 4) + \
+            N * d * 2 + (self.Q + self.w - 1) * d * 2
+
+    def launch(self, i):
+        csa = self.csa
+        csa.compress(self.A, self.Bs, self.z, self.z, self.m, self.kv, tok_base=self.tb, entry_begin=self.P,
+                     entry_end=self.N)
+        csa.compress(self.AI, self.BI, self.zI, self.zI, self.m, self.kI, tok_base=self.tb, entry_begin=self.P,
+                     entry_end=self.N)
+        csa.index_topk(self.qI, self.wt, self.kI, self.ne, self.q_pos, m=self.m, topk=self.k,
+                       workspace=self.idx_ws, out_idx=self.idx, out_score=self.score)
+        csa.sparse_mqa(self.q, self.kv, self.idx, self.raw, self.rb, self.q_pos, window=self.w,
+                       workspace=self.mqa_ws, out=self.out, lse=self.lse)
+
+    def algorithmic(self, kernel):
+        if kernel == "index_scores_bf16":
+            return "mfma", 2.0 * self.pairs * self.HI * self.dI
+        if kernel.startswith("mqa_bf16"):
+            return "mfma", 4.0 * self.H * self.d * self.mqa_rows
+        if kernel == "topk":
+            return "hbm", self.pairs * 4 + self.Q * self.k * 4
+        return None
+
+    def cpu_baseline(self):
+        import oracle
+        from long_context_compressed_04_amd import workloads as W
+        c = self.c
+        t0 = time.perf_counter()
+        new_kv = oracle.compress(W.value(c["A"]), W.value(c["Bs"]), c["z"], c["z"], self.m, tok_base=self.tb,
+                                 entry_begin=self.P, entry_end=self.N)
+        new_kI = oracle.compress(W.value(c["AI"]), W.value(c["BI"]), c["zI"], c["zI"], self.m, tok_base=self.tb,
+                                 entry_begin=self.P, entry_end=self.N)
+        t_compress = time.perf_counter() - t0
+        keys = np.concatenate([W.value(c["kI_prior"]), new_kI])
+        kv_all = np.concatenate([W.value(c["kv_prior"]), new_kv])
+        raw = W.value(c["kv_raw"])
+        sample = list(range(0, self.Q, 128))
+        t0 = time.perf_counter()
+        for i in sample:
+            t = int(c["q_pos"][i])
+            V = oracle.visible(t, self.N, self.m)
+            scores = oracle.index_scores(W.value(c["qI"][i]), c["w"][i], keys[:V])
+            idx = oracle.topk(scores, V, self.k)
+            sel = idx[idx >= 0]
+            oracle.sparse_mqa(W.value(c["q"][i]), kv_all, idx, raw, c["raw_base"], t, self.w, c["scale"],
+                              c["eps"])
+        t_q = time.perf_counter() - t0
+        secs = t_compress + t_q * self.Q / len(sample)
+        return {"value": round(self.Q / secs, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                "sample": "compression of the 1,024 new entries (KV and index keys) in full (%.1f s) plus %d of the "
+                          "4,096 queries (indexer, top-1024, MQA; %.1f s) scaled to all 4,096; fp64, single thread"
+                          % (t_compress, len(sample), t_q)}
+
+
+def make(name, dev, R):
+    return {"csa_decode_64k": CsaDecode64k, "hca_decode_1m": HcaDecode1m, "csa_decode_1m_fp4": CsaDecode1mFp4,
+            "csa_prefill_4k": CsaPrefill4k}[name](dev, R)
+
+
+# ------------------------------------------------------------------------------------
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build runs on a single MI355X and has no multi-GPU path "
-              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        print("bench.py measures one GPU: this implementation runs on a single MI355X and has no multi-GPU "
+              "path (--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     import torch
     from long_context_compressed_04_amd import csa
-    from long_context_compressed_04_amd import workloads as W
+    from long_context_compressed_04_amd import profiling
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     csa.lib()
-
-    B, T, m, H, d, HI, dI, k, window = 8, 65536, 4, 128, 512, 64, 128, 1024, 128
-    N = T // m
-    c = W.csa_decode(0, B=B, T=T, m=m, H=H, d=d, HI=HI, dI=dI, k=k, window=window)
-
-    def to_dev(x):
-        x = np.ascontiguousarray(x)
-        if x.dtype == np.uint16:
-            return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
-        return torch.from_numpy(x).to(dev)
-
-    def i32(x):
-        return torch.as_tensor(np.asarray(x, dtype=np.int32)).to(dev)
-
-    base = dict(q=to_dev(c["q"][:, None]), kv=to_dev(c["kv"]), kv_raw=to_dev(c["kv_raw"]),
-                qI=to_dev(c["qI"][:, None]), w=to_dev(c["w"][:, None]), kI=to_dev(c["kI"]))
-    raw_base, q_pos, n_entries = i32(c["raw_base"]), i32(c["q_pos"][:, None]), i32(c["n_entries"])
-    del c
-    R = max(1, args.replicas)
-    reps = [base] + [{key: t.clone() for key, t in base.items()} for _ in range(R - 1)]
-    decs = [csa.Decoder(r["q"], r["kv"], r["kv_raw"], raw_base, q_pos, r["qI"], r["w"], r["kI"], n_entries,
-                        m=m, topk=k, window=window) for r in reps]
+    wl = make(args.workload, dev, max(1, args.replicas))
+    R = wl.replicas
     torch.cuda.synchronize()
-
     stream = torch.cuda.current_stream(dev)
 
-    def run_steps(n, replica_cycle=True):
-        for i in range(n):
-            decs[i % R if replica_cycle else 0]()
-
-    # ---- graph capture of R consecutive steps (one per replica)
-    graph = None
-    if args.graph:
-        run_steps(R)
+    if args.pmc_pass:
+        for i in range(2 * R):
+            wl.launch(i)
         torch.cuda.synchronize()
+        src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print("pmc pass done: %s, %d steps, calibration copy %d bytes" % (wl.name, 2 * R, CALIB_BYTES), flush=True)
+        return
+
+    # ---- graph of R consecutive steps (one per replica)
+    graph = None
+    for i in range(R):
+        wl.launch(i)
+    torch.cuda.synchronize()
+    if args.graph:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=torch.cuda.Stream(dev)):
-            run_steps(R)
+            for i in range(R):
+                wl.launch(i)
         torch.cuda.synchronize()
 
-    def timed(n_steps, replica_cycle=True):
-        if graph is not None and replica_cycle:
+    def timed(n_steps, cycle=True):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        if graph is not None and cycle:
             reps_n = max(1, n_steps // R)
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             for _ in range(reps_n):
                 graph.replay()
             e1.record(stream)
             torch.cuda.synchronize()
             return e0.elapsed_time(e1) / 1e3, reps_n * R
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        run_steps(n_steps, replica_cycle)
+        for i in range(n_steps):
+            wl.launch(i if cycle else 0)
         e1.record(stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / 1e3, n_steps
 
-    # warmup, then the timed region
     if graph is not None:
         for _ in range(max(1, args.warmup // R)):
             graph.replay()
     else:
-        run_steps(args.warmup)
+        for i in range(args.warmup):
+            wl.launch(i)
     torch.cuda.synchronize()
     secs, steps = timed(args.steps)
     ms_per_step = secs * 1e3 / steps
-    tok_s = B * steps / secs
+    warm_secs, warm_steps = timed(min(args.steps, 50), cycle=False)
 
-    # warm-cache figure (same replica every step, eager launches)
-    warm_secs, warm_steps = timed(min(args.steps, 100), replica_cycle=False)
-    warm_ms = warm_secs * 1e3 / warm_steps
-
-    # ---- compulsory bytes of one step (cold): every visible index key, the selected
-    # entries and window rows, q, q_idx, w, the output
-    kv_row, key_row = d * 2, dI * 2
-    step_bytes = (B * N * key_row + B * (k + window) * kv_row + B * H * d * 2 * 2 + B * HI * dI * 2 + B * HI * 4
-                  + B * k * 4)
-    step_flops = 2.0 * B * N * HI * dI + 4.0 * B * H * d * (k + window)
-
-    # ---- dominant kernel: the indexer, timed per launch with HIP events on its stream
-    ne_bytes = B * N * key_row + B * HI * dI * 2 + B * HI * 4 + B * N * 4
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(R * 4)]
-    scores_out = [torch.empty((B, 1, N), dtype=torch.float32, device=dev) for _ in range(2)]
-    for i in range(R):
-        r = reps[i]
-        csa.index_scores(r["qI"], r["w"], r["kI"], n_entries, q_pos, m=m, n_max=N)
-    torch.cuda.synchronize()
-    durs = []
-    lib = csa.lib()
-    import ctypes
-    desc = csa.IndexDesc(B, 1, HI, dI, m, k, N, N, csa.BF16)
-    for j, (a, b_) in enumerate(ev):
-        r = reps[j % R]
-        a.record(stream)
-        st = lib.csa_index_scores(ctypes.byref(desc), r["qI"].data_ptr(), None, r["w"].data_ptr(),
-                                  r["kI"].data_ptr(), None, n_entries.data_ptr(), q_pos.data_ptr(),
-                                  scores_out[j % 2].data_ptr(), stream.cuda_stream)
-        assert st == 0
-        b_.record(stream)
-    torch.cuda.synchronize()
-    durs = [a.elapsed_time(b_) * 1e-3 for a, b_ in ev]
-    idx_s = float(np.mean(durs))
-    achieved = ne_bytes / idx_s / 1e9
-
-    traffic = None
-    prof = os.path.join(ROOT, "profiles", "index_scores_bf16_csa_decode_64k_traffic.json")
+    # ---- every kernel of the step, timed live (HIP events on the launch stream)
+    csa.timing_enable(True)
+    n_t = max(2 * R, 4)
+    for i in range(n_t):
+        wl.launch(i)
+    kt = csa.timing_collect()
+    csa.timing_enable(False)
+    per_step = {k: v["avg_us"] * v["launches"] / n_t for k, v in kt.items()}
+    dom = max(per_step, key=per_step.get)
+    kernels = {k: {"avg_us": round(v["avg_us"], 3), "launches_per_step": round(v["launches"] / n_t, 2),
+                   "us_per_step": round(per_step[k], 3)} for k, v in kt.items()}
+    alg = wl.algorithmic(dom)
+    dom_us = kt[dom]["avg_us"]
+    roof = {"bound": None, "kernel": dom, "achieved": None, "peak": None, "unit": None, "frac": None,
+            "traffic": None, "avg_launch_us": round(dom_us, 3)}
+    if alg is not None:
+        bound, amount = alg
+        if bound == "hbm":
+            achieved, peak, unit = amount / (dom_us * 1e-6) / 1e9, HBM_PEAK_GBS, "GB/s"
+            roof["bytes_per_launch"] = amount
+        else:
+            peak = MFMA_PEAK_TFLOPS["mxfp4" if "mxfp4" in dom else "bf16"]
+            achieved, unit = amount / (dom_us * 1e-6) / 1e12, "TFLOP/s"
+            roof["flops_per_launch"] = amount
+        roof.update(bound=bound, achieved=round(achieved, 1), peak=peak, unit=unit, frac=round(achieved / peak, 4))
+    prof = os.path.join(ROOT, "profiles", "traffic_%s.json" % wl.name)
     if os.path.exists(prof):
         with open(prof) as f:
             pj = json.load(f)
-        if pj.get("source_hash") == file_hash("long_context_compressed_04_amd/csrc/indexer.hip"):
-            traffic = pj.get("bytes_per_launch")
+        ent = pj.get("kernels", {}).get(dom)
+        if ent and ent.get("source_hash") == profiling.source_hash(dom):
+            roof["traffic"] = ent["bytes_per_launch"]
 
     result = {
-        "metric": "CSA decode tokens/s at 64K context (one layer, 8 sequences)",
-        "value": round(tok_s, 1),
+        "metric": wl.metric,
+        "value": round(wl.tokens * steps / secs, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": steps,
@@ -189,40 +518,19 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) caches and queries, U[0,1) indexer head weights)",
-        "config": {"workload": "csa_decode_64k", "batch": B, "context": T, "compress_ratio": m,
-                   "entries": N, "heads": H, "head_dim": d, "idx_heads": HI, "idx_dim": dI, "topk": k,
-                   "window": window, "cache_replicas": R, "graph": bool(graph is not None)},
-        "step_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "step_bytes": step_bytes,
-        "step_flops": step_flops,
-        "warm_ms_per_step": round(warm_ms, 5),
-        "roofline": {"bound": "hbm", "kernel": "index_scores_mfma (bf16)", "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "bytes_per_launch": ne_bytes, "avg_launch_us": round(idx_s * 1e6, 3)},
+        "data": "synthetic (seeded N(0,1) caches, token streams and queries; U[0,1) indexer head weights)",
+        "config": dict(wl.config, graph=graph is not None),
+        "step_bytes": wl.step_bytes,
+        "step_flops": wl.step_flops,
+        "step_hbm_frac": round(wl.step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "step_mfma_frac": round(wl.step_flops / (ms_per_step * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
+        "warm_ms_per_step": round(warm_secs * 1e3 / warm_steps, 5),
+        "kernels": kernels,
+        "roofline": roof,
     }
-
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(B, T, m, H, d, HI, dI, k, window)
+        result["cpu_baseline"] = wl.cpu_baseline()
     print(json.dumps(result), flush=True)
-
-
-def cpu_baseline(B, T, m, H, d, HI, dI, k, window):
-    """The oracle (single thread, fp64) on the same workload: all sequences of one step."""
-    import oracle
-    from long_context_compressed_04_amd import workloads as W
-    c = W.csa_decode(0, B=B, T=T, m=m, H=H, d=d, HI=HI, dI=dI, k=k, window=window)
-    seqs = list(range(B))
-    vals = [(W.value(c["q"][b]), W.value(c["kv"][b]), W.value(c["qI"][b]), c["w"][b], W.value(c["kI"][b]),
-             W.value(c["kv_raw"][b])) for b in seqs]
-    t0 = time.perf_counter()
-    for b, (q, kv, qI, w, kI, raw) in zip(seqs, vals):
-        oracle.csa_decode_query(q, kv, c["N"], m, qI, w, kI, k, raw, int(c["raw_base"][b]), int(c["q_pos"][b]),
-                                window, c["scale"], c["eps"])
-    secs = time.perf_counter() - t0
-    return {"value": round(len(seqs) / secs, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": "one full decode step of all %d sequences (indexer over 16,384 keys, top-1024, "
-                      "MQA over 1,152 rows x 128 heads), fp64, single thread, %.1f s" % (len(seqs), secs)}
 
 
 if __name__ == "__main__":

@@ -28,7 +28,8 @@
  *    (b * capacity + r) * width.  Token positions are absolute int32.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and
  *    the call returns without synchronising.  The library allocates no device
- *    memory and keeps no state between calls.
+ *    memory and keeps no state between calls (launch timing, at the end of this
+ *    file, aside).
  *  - Errors: every argument is validated on the host before anything is launched;
  *    on failure nothing is enqueued, a csa_status code is returned and
  *    csa_last_error() describes it.  A failed launch returns CSA_ERR_HIP.  Values
@@ -274,6 +275,28 @@ typedef struct {
 
 size_t csa_decode_workspace_size(const csa_decode_args* args);
 csa_status csa_decode(const csa_decode_args* args, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------
+ * Launch timing (diagnostics; not part of the method).  csa_timing_enable(1)
+ * makes the library bracket every later kernel launch with a pair of HIP events
+ * recorded on the launch stream (launches on a stream that is being captured into
+ * a graph are not timed); csa_timing_enable(0) stops it.  This is the one piece of
+ * state the library keeps across calls: the events, created on first use and
+ * reused.  csa_timing_collect waits for every recorded launch to finish, writes
+ * up to `cap` per-kernel aggregates (in order of first launch) to `out` and forgets
+ * the records; it returns the number of entries written, or with out == NULL the
+ * number of distinct kernels without writing anything.  Thread-safe.
+ * ---------------------------------------------------------------------------- */
+typedef struct {
+  char name[40];      /* kernel name, NUL-terminated */
+  int32_t launches;
+  double total_us;
+  double min_us;
+  double max_us;
+} csa_kernel_time;
+
+csa_status csa_timing_enable(int32_t on);
+int32_t csa_timing_collect(csa_kernel_time* out, int32_t cap);
 
 #ifdef __cplusplus
 }

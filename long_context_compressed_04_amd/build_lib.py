@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libcsa.so")
 BUILD = os.path.join(PKG, "_build")
 
-SOURCES = ["compress.hip", "indexer.hip", "topk.hip", "mqa.hip", "csa_api.cpp"]
+SOURCES = ["compress.hip", "indexer.hip", "topk.hip", "mqa.hip", "csa_api.cpp", "launch_timer.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

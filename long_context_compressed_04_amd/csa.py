@@ -57,6 +57,11 @@ class DecodeArgs(ctypes.Structure):
                     "k_idx_scale", "n_entries", "out_idx", "out_score", "out", "lse")]
 
 
+class KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 40), ("launches", ctypes.c_int32), ("total_us", ctypes.c_double),
+                ("min_us", ctypes.c_double), ("max_us", ctypes.c_double)]
+
+
 def lib():
     """Load libcsa.so (built in-tree by build_lib / __graft_entry__.build())."""
     global _lib
@@ -89,6 +94,10 @@ def lib():
         L.csa_decode_workspace_size.restype = Z
         L.csa_decode.argtypes = [ctypes.POINTER(DecodeArgs), V, Z, V]
         L.csa_decode.restype = S
+        L.csa_timing_enable.argtypes = [ctypes.c_int32]
+        L.csa_timing_enable.restype = S
+        L.csa_timing_collect.argtypes = [ctypes.POINTER(KernelTime), ctypes.c_int32]
+        L.csa_timing_collect.restype = ctypes.c_int32
         _lib = L
     return _lib
 
@@ -148,12 +157,16 @@ def compress(a, b, za, zb, m, out, *, tok_base=0, entry_begin=0, entry_end=None,
     return out
 
 
-def mxfp4_quantize(x):
+def mxfp4_quantize(x, codes=None, scales=None):
     """MXFP4 along the last axis (multiple of 32): returns (codes uint8 [..., n/2],
-    scales uint8 [..., n/32])."""
+    scales uint8 [..., n/32]), written into `codes` / `scales` when given."""
     n = x.shape[-1]
-    codes = torch.empty(x.shape[:-1] + (n // 2,), dtype=torch.uint8, device=x.device)
-    scales = torch.empty(x.shape[:-1] + (n // 32,), dtype=torch.uint8, device=x.device)
+    if codes is None:
+        codes = torch.empty(x.shape[:-1] + (n // 2,), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(x.shape[:-1] + (n // 32,), dtype=torch.uint8, device=x.device)
+    if codes.numel() * 2 != x.numel() or scales.numel() * 32 != x.numel():
+        raise ValueError("codes / scales do not match x")
     _check(lib().csa_mxfp4_quantize(_dtype_code(x), _p(x), x.numel() // 32, _p(codes), _p(scales), _stream(x)))
     return codes, scales
 
@@ -252,3 +265,20 @@ class Decoder:
     def __call__(self):
         _check(lib().csa_decode(ctypes.byref(self.args), _p(self.ws), self.nb, _stream(self.stream_of)))
         return self.out, self.out_idx
+
+
+def timing_enable(on=True):
+    """Bracket every later library launch (outside graph capture) with HIP events."""
+    _check(lib().csa_timing_enable(1 if on else 0))
+
+
+def timing_collect():
+    """Wait for the timed launches; return {kernel: {launches, avg_us, min_us, max_us}}."""
+    L = lib()
+    buf = (KernelTime * 64)()
+    n = L.csa_timing_collect(buf, 64)
+    res = {}
+    for t in buf[:n]:
+        res[t.name.decode()] = {"launches": t.launches, "avg_us": t.total_us / max(1, t.launches),
+                                "min_us": t.min_us, "max_us": t.max_us}
+    return res

@@ -13,6 +13,7 @@
 // streams channels with coalesced row reads.  fp32 arithmetic throughout.
 #include "csa_device.hpp"
 #include "csa_kernels.hpp"
+#include "launch_timer.hpp"
 
 namespace csa {
 
@@ -112,6 +113,7 @@ hipError_t launch_compress(const CompressArgs& A, hipStream_t s) {
   int n = A.entry_end - A.entry_begin;
   if (n <= 0 || A.batch <= 0) return hipSuccess;
   dim3 grid(n, A.batch), block(kCompressThreads);
+  LaunchTimer timer("compress", s);
   if (A.in_bf16 && A.out_bf16) compress_kernel<true, true><<<grid, block, 0, s>>>(A);
   else if (A.in_bf16) compress_kernel<true, false><<<grid, block, 0, s>>>(A);
   else if (A.out_bf16) compress_kernel<false, true><<<grid, block, 0, s>>>(A);
@@ -190,6 +192,7 @@ hipError_t launch_mxfp4_quantize(int in_bf16, const void* x, int64_t n_blocks, u
                                  hipStream_t s) {
   if (n_blocks <= 0) return hipSuccess;
   dim3 grid((unsigned)((n_blocks + 255) / 256)), block(256);
+  LaunchTimer timer("mxfp4_quantize", s);
   if (in_bf16) mxfp4_quantize_kernel<true><<<grid, block, 0, s>>>(x, n_blocks, codes, scales);
   else mxfp4_quantize_kernel<false><<<grid, block, 0, s>>>(x, n_blocks, codes, scales);
   return hipGetLastError();

@@ -20,6 +20,7 @@
 //    (16 in-lane, then the partner lane l^32), one fp32 score per entry.
 #include "csa_device.hpp"
 #include "csa_kernels.hpp"
+#include "launch_timer.hpp"
 
 namespace csa {
 
@@ -174,6 +175,7 @@ static void launch_mfma_hb(const IndexArgs& A, float* scores, hipStream_t s) {
   const int chunk = kIdxWaves * TPW * 32;
   const int q_tile = A.n_q >= 64 ? 16 : 1;
   dim3 grid((A.n_max + chunk - 1) / chunk, (A.n_q + q_tile - 1) / q_tile, A.batch);
+  LaunchTimer timer(FP4 ? "index_scores_mxfp4" : "index_scores_bf16", s);
   index_scores_mfma<HB, FP4, TPW><<<grid, kIdxWaves * 64, 0, s>>>(A, scores, q_tile);
 }
 
@@ -182,6 +184,7 @@ hipError_t launch_index_scores(const IndexArgs& A, float* scores, hipStream_t s)
   if (A.dtype == 0) {
     dim3 grid((A.n_max + kIdxF32Threads - 1) / kIdxF32Threads, A.n_q, A.batch);
     size_t lds = sizeof(float) * ((size_t)A.heads * A.dim + A.heads);
+    LaunchTimer timer("index_scores_f32", s);
     index_scores_f32<<<grid, kIdxF32Threads, lds, s>>>(A, scores);
     return hipGetLastError();
   }

@@ -31,6 +31,7 @@
 
 #include "csa_device.hpp"
 #include "csa_kernels.hpp"
+#include "launch_timer.hpp"
 
 namespace csa {
 
@@ -1168,6 +1169,7 @@ hipError_t launch_mqa(const MqaArgs& A, void* ws, size_t ws_bytes, hipStream_t s
   if (A.batch <= 0 || A.n_q <= 0) return hipSuccess;
   if (!A.bf16) {
     dim3 grid(A.heads, A.n_q, A.batch);
+    LaunchTimer timer("mqa_f32", s);
     mqa_f32_kernel<<<grid, kF32Waves * 64, 0, s>>>(A);
     return hipGetLastError();
   }
@@ -1195,13 +1197,17 @@ hipError_t launch_mqa(const MqaArgs& A, void* ws, size_t ws_bytes, hipStream_t s
   if (lds > (size_t)kMaxDynLds) return hipErrorInvalidValue;
   const long groups = ((long)L.units + 7) / 8;
   dim3 grid((unsigned)(groups * 8 * L.n_hg));
-  if (L.heads32) mqa32d_kernel<<<grid, 512, lds, s>>>(A, L, part_o, part_ml);
-  else if (L.nw == 4) mqa_bf16_kernel<4><<<grid, 4 * 64, lds, s>>>(A, L, part_o, part_ml);
-  else if (L.nw == 2) mqa_bf16_kernel<2><<<grid, 2 * 64, lds, s>>>(A, L, part_o, part_ml);
-  else mqa_bf16_kernel<1><<<grid, 64, lds, s>>>(A, L, part_o, part_ml);
+  {
+    LaunchTimer timer(L.heads32 ? "mqa_bf16_h32" : "mqa_bf16_h16", s);
+    if (L.heads32) mqa32d_kernel<<<grid, 512, lds, s>>>(A, L, part_o, part_ml);
+    else if (L.nw == 4) mqa_bf16_kernel<4><<<grid, 4 * 64, lds, s>>>(A, L, part_o, part_ml);
+    else if (L.nw == 2) mqa_bf16_kernel<2><<<grid, 2 * 64, lds, s>>>(A, L, part_o, part_ml);
+    else mqa_bf16_kernel<1><<<grid, 64, lds, s>>>(A, L, part_o, part_ml);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || L.nsplit == 1) return e;
   dim3 cgrid(A.heads, (unsigned)((long)A.batch * A.n_q));
+  LaunchTimer timer("mqa_combine", s);
   mqa_combine_kernel<<<cgrid, kD / 4, 0, s>>>(A, L, part_o, part_ml);
   return hipGetLastError();
 }

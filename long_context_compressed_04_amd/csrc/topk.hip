@@ -18,6 +18,7 @@
 // by index, -1 padded.
 #include "csa_device.hpp"
 #include "csa_kernels.hpp"
+#include "launch_timer.hpp"
 
 namespace csa {
 
@@ -153,6 +154,7 @@ hipError_t launch_topk_rows(const IndexArgs& A, const float* scores, int32_t* ou
                             hipStream_t s) {
   const long rows = (long)A.batch * A.n_q;
   if (rows <= 0) return hipSuccess;
+  LaunchTimer timer("topk", s);
   if (A.n_max <= kLdsKeys) {
     const size_t lds = sizeof(uint32_t) * (size_t)A.n_max;
     static hipError_t attr = hipFuncSetAttribute((const void*)topk_rows_kernel<true>,

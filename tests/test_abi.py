@@ -124,3 +124,12 @@ def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(ValueError):
         csa._p(torch.zeros(4))
+
+
+def test_launch_timing_without_launches():
+    """Timing on and off with nothing launched: nothing to collect, no HIP call made."""
+    L = csa.lib()
+    assert L.csa_timing_enable(1) == 0
+    assert L.csa_timing_collect(None, 0) == 0
+    assert csa.timing_collect() == {}
+    assert L.csa_timing_enable(0) == 0
