@@ -94,8 +94,13 @@ csa::IndexArgs index_args(const csa_index_desc* d, const void* q, const uint8_t*
   return A;
 }
 
-size_t index_ws(const csa_index_desc* d) {
+size_t scores_ws(const csa_index_desc* d) {
   return round256(sizeof(float) * (size_t)d->batch * d->n_q * (size_t)d->n_max);
+}
+size_t index_ws(const csa_index_desc* d) {
+  csa::IndexArgs A{};
+  A.batch = d->batch; A.n_q = d->n_q; A.n_max = d->n_max; A.topk = d->topk;
+  return scores_ws(d) + round256(csa::topk_workspace_bytes(A));
 }
 
 // --------------------------------------------------------------------- MQA
@@ -206,7 +211,9 @@ csa_status csa_index_topk(const csa_index_desc* d, const void* q, const uint8_t*
   float* scores = (float*)ws;
   st = hip_status(csa::launch_index_scores(A, scores, s), "csa_index_topk (scores)");
   if (st != CSA_OK) return st;
-  return hip_status(csa::launch_topk_rows(A, scores, out_idx, out_score, s), "csa_index_topk (select)");
+  const size_t sws = scores_ws(d);
+  return hip_status(csa::launch_topk_rows(A, scores, out_idx, out_score, (char*)ws + sws, ws_bytes - sws, s),
+                    "csa_index_topk (select)");
 }
 
 size_t csa_mqa_workspace_size(const csa_mqa_desc* d, int32_t dense) {

@@ -28,8 +28,10 @@ struct IndexArgs {
 // Score rows [batch*n_q, n_max] (-inf past the visible count).
 hipError_t launch_index_scores(const IndexArgs& A, float* scores, hipStream_t s);
 // Top-k per score row.
+// Rows longer than the LDS-resident limit use `ws` (topk_workspace_bytes).
+size_t topk_workspace_bytes(const IndexArgs& A);
 hipError_t launch_topk_rows(const IndexArgs& A, const float* scores, int32_t* out_idx,
-                            float* out_score, hipStream_t s);
+                            float* out_score, void* ws, size_t ws_bytes, hipStream_t s);
 
 struct MqaArgs {
   int batch, n_q, heads, dim, topk, m, n_max, window, kv_cap, raw_cap, dense, bf16;

@@ -6,16 +6,26 @@
 // selected sparse attention": index_topk entries, slots past the causal threshold
 // marked -1.
 //
-// One workgroup (1024 threads) per score row.  Scores map to order-preserving
-// uint32 keys; rows of up to kLdsKeys keys are held in LDS (one pass over HBM/L2
-// with every load in flight), longer rows are re-read from global memory.  A
-// min/max pass finds the bits all visible keys share; MSB-first radix passes of up
-// to 11 bits (2048-bin LDS histogram, the threshold digit found with one block
-// scan) narrow the prefix of the k-th largest key, stopping early once the
-// remaining bucket is taken whole.  The final compaction is in index order (two
-// block scans): every key above the threshold prefix, then the lowest-index keys
-// equal to it -- the exact set "score descending, ties to the lower index", sorted
-// by index, -1 padded.
+// The selected set is exact: "score descending, ties to the lower index", written
+// in ascending index order and -1 padded.  Scores map to order-preserving uint32
+// keys.  One 1024-thread workgroup selects one row:
+//  - the keys stay in registers (thread t holds positions 1024 j + t, loaded
+//    coalesced with raw buffer loads that return 0 past the row);
+//  - threshold: below the bits every key shares, an 11-bit radix digit is counted
+//    in a 2048-bin LDS histogram (padded so that one wave reads it without bank
+//    conflicts) and one wave finds the bin of the k-th largest key with two
+//    cross-lane scans.  A bin of at most 64 keys is then resolved exactly by one
+//    wave, bit by bit with ballots; larger bins take further 11-bit passes;
+//  - compaction: two ballots per (round, wave) cell record which keys lie above the
+//    threshold and which equal it; one wave scans the cells in position order; each
+//    thread then writes its selected keys to their output slots (keys above before
+//    it plus the equal keys before it, capped at the number still needed).
+// Rows longer than kRegKeys take three launches: a sample of kSample keys gives a
+// threshold expected to pass about 3k keys; many workgroups filter the row against
+// it into per-chunk candidate lists (index order kept); one workgroup per row
+// selects among the candidates.  If the sample's threshold passes fewer than k keys
+// or more than kCandCap, that row is selected straight from its scores in global
+// memory (exact, slower).
 #include "csa_device.hpp"
 #include "csa_kernels.hpp"
 #include "launch_timer.hpp"
@@ -23,148 +33,588 @@
 namespace csa {
 
 constexpr int kTopkThreads = 1024;
-constexpr int kBins = 2048;
-constexpr int kDigit = 11;
-constexpr int kLdsKeys = 32768;
+constexpr int kTW = kTopkThreads / 64;
+constexpr int kRegKeys = 16384;       // direct path: the whole row in registers (16 keys per thread)
+constexpr int kMaxKpt = kRegKeys / kTopkThreads;
+constexpr int kCandCap = 16384;       // long rows: candidates kept for the exact selection
+constexpr int kSample = 8192;         // long rows: keys in the threshold sample
+constexpr int kChunk = 4096;          // long rows: keys per filter workgroup
+constexpr int kFilterThreads = 256;
+constexpr int kMaxChunks = 2048;
+constexpr int kBins = 2048;           // 11-bit radix digit
+constexpr int kHistWords = kBins + kBins / 32;
+constexpr int kBucketMax = 64;
 
-template <bool IN_LDS>
-__global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(IndexArgs A, const float* scores,
-                                                                 int32_t* out_idx, float* out_score) {
-  extern __shared__ uint32_t keys[];   // IN_LDS: [V]
-  __shared__ uint32_t hist[kBins];
-  __shared__ uint32_t tmp[kTopkThreads / 64 + 1];
-  __shared__ uint32_t red_min[kTopkThreads / 64], red_max[kTopkThreads / 64];
-  __shared__ uint32_t s_prefix, s_need, s_cnt;
+struct SelShared {
+  uint32_t hist[kHistWords];          // bin b at b + b / 32
+  uint32_t red[2 * kTW];
+  uint32_t wcnt[2 * kTW];
+  uint64_t gmask[kMaxKpt * kTW];      // per (round, wave) cell: keys above the threshold
+  uint64_t emask[kMaxKpt * kTW];      // ... and keys equal to it
+  uint32_t gbase[kMaxKpt * kTW];      // ... and how many of each come before the cell
+  uint32_t ebase[kMaxKpt * kTW];
+  uint32_t bkey[kBucketMax];
+  uint32_t bcount;
+  uint32_t s_prefix, s_need, s_cnt;
+};
 
-  const long row = blockIdx.x;
-  const int b = (int)(row / A.n_q);
-  const int k = A.topk;
-  const int ne = min(A.n_entries[b], A.n_max);
-  const int V = visible_entries(A.q_pos[row], ne, A.m);
-  const float* src = scores + row * A.n_max;
-  int32_t* oi = out_idx + row * k;
-  float* os = out_score ? out_score + row * k : nullptr;
+__device__ __forceinline__ int hslot(int b) { return b + (b >> 5); }
 
-  if (V <= k) {  // everything visible is selected
-    for (int i = threadIdx.x; i < k; i += blockDim.x) {
-      oi[i] = i < V ? i : -1;
-      if (os) os[i] = i < V ? src[i] : -INFINITY;
-    }
-    return;
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = (uint32_t)__shfl_up((int)v, o, 64);
+    if (lane >= o) v += y;
   }
+  return v;
+}
+
+// Block-wide min and max of one key pair per thread (barriers inside).
+__device__ __forceinline__ void block_minmax(uint32_t& kmin, uint32_t& kmax, SelShared& sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  auto key_at = [&](int i) -> uint32_t { return IN_LDS ? keys[i] : order_key(src[i]); };
-
-  // ---- load (LDS rows) and the bits every visible key shares
-  uint32_t kmin = 0xffffffffu, kmax = 0u;
-#pragma unroll 8
-  for (int i = threadIdx.x; i < V; i += kTopkThreads) {
-    uint32_t key = order_key(src[i]);
-    if (IN_LDS) keys[i] = key;
-    kmin = min(kmin, key);
-    kmax = max(kmax, key);
-  }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
     kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
   }
-  if (lane == 0) { red_min[wave] = kmin; red_max[wave] = kmax; }
+  if (lane == 0) {
+    sh.red[wave] = kmin;
+    sh.red[kTW + wave] = kmax;
+  }
   __syncthreads();
-  kmin = red_min[0]; kmax = red_max[0];
-  for (int w = 1; w < kTopkThreads / 64; ++w) { kmin = min(kmin, red_min[w]); kmax = max(kmax, red_max[w]); }
-
-  int hi = (kmin == kmax) ? 0 : 32 - __clz((int)(kmin ^ kmax));   // low bits still undecided
-  uint32_t mask = hi >= 32 ? 0u : ~((1u << hi) - 1u);
-  uint32_t prefix = kmin & mask;
-  uint32_t need = (uint32_t)k;
-
-  // ---- MSB-first radix narrowing of the k-th largest key's prefix
-  while (hi > 0) {
-    const int width = hi < kDigit ? hi : kDigit;
-    const int shift = hi - width;
-    const uint32_t dmask = (1u << width) - 1u;
-    for (int i = threadIdx.x; i < kBins; i += kTopkThreads) hist[i] = 0;
-    __syncthreads();
-#pragma unroll 8
-    for (int i = threadIdx.x; i < V; i += kTopkThreads) {
-      uint32_t key = key_at(i);
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
-    }
-    __syncthreads();
-    // thread t owns bins 2047-2t (upper) and 2046-2t: a scan in thread order counts
-    // every key in higher bins
-    const int bu = kBins - 1 - 2 * threadIdx.x, bl = bu - 1;
-    const uint32_t cu = hist[bu], cl = hist[bl];
-    uint32_t total;
-    const uint32_t above = block_exclusive_scan<kTopkThreads>(cu + cl, tmp, &total);
-    if (above < need && need <= above + cu + cl) {
-      if (above + cu >= need) {
-        s_prefix = prefix | ((uint32_t)bu << shift);
-        s_need = need - above;
-        s_cnt = cu;
-      } else {
-        s_prefix = prefix | ((uint32_t)bl << shift);
-        s_need = need - above - cu;
-        s_cnt = cl;
-      }
-    }
-    __syncthreads();
-    prefix = s_prefix;
-    need = s_need;
-    mask |= dmask << shift;
-    hi = shift;
-    const bool whole = s_cnt == need;
-    __syncthreads();
-    if (whole) break;   // the whole bucket is selected
+  kmin = lane < kTW ? sh.red[lane] : 0xffffffffu;
+  kmax = lane < kTW ? sh.red[kTW + lane] : 0u;
+#pragma unroll
+  for (int o = kTW / 2; o >= 1; o >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
   }
+  kmin = (uint32_t)__builtin_amdgcn_readfirstlane((int)kmin);
+  kmax = (uint32_t)__builtin_amdgcn_readfirstlane((int)kmax);
+  __syncthreads();
+}
 
-  // ---- index-ordered compaction: keys whose prefix is above, then the first `need`
-  // keys equal to the prefix
-  const int seg = (V + kTopkThreads - 1) / kTopkThreads;
-  const int lo = threadIdx.x * seg;
-  const int hi_i = min(V, lo + seg);
-  uint32_t n_gt = 0, n_eq = 0;
-  for (int i = lo; i < hi_i; ++i) {
-    uint32_t kp = key_at(i) & mask;
-    n_gt += kp > prefix;
-    n_eq += kp == prefix;
-  }
-  uint32_t tot;
-  const uint32_t eq_before = block_exclusive_scan<kTopkThreads>(n_eq, tmp, &tot);
-  const uint32_t take_eq = eq_before >= need ? 0u : min(n_eq, need - eq_before);
-  uint32_t pos = block_exclusive_scan<kTopkThreads>(n_gt + take_eq, tmp, &tot);
-  uint32_t eq_seen = eq_before;
-  for (int i = lo; i < hi_i; ++i) {
-    const uint32_t kp = key_at(i) & mask;
-    bool sel = kp > prefix;
-    if (kp == prefix) {
-      sel = eq_seen < need;
-      ++eq_seen;
+// One radix pass's threshold digit.  Wave 0 scans the 2048-bin histogram from the
+// top: lane l first sums bins 2047-32l ... 2016-32l; the lane whose range holds the
+// need-th largest key is found by a scan over lanes, then its 32 bins are scanned
+// across lanes 0..31.  Records the bin's prefix, the count still needed inside it,
+// and its size.  Call from every thread after the histogram barrier.
+__device__ __forceinline__ void pick_digit(SelShared& sh, uint32_t prefix, int shift, uint32_t need) {
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x < 64) {
+    // the 32 bins of lane l sit in consecutive padded slots, 33 words apart per lane
+    const uint32_t* hp = sh.hist + hslot(kBins - 32 - 32 * lane);
+    uint32_t s = 0;
+#pragma unroll 1
+    for (int g = 0; g < 4; ++g) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s += hp[8 * g + i];
     }
-    if (sel && pos < (uint32_t)k) {
-      oi[pos] = i;
-      if (os) os[pos] = src[i];
-      ++pos;
+    const uint32_t inc = wave_inclusive_sum(s);
+    const uint64_t hit = __ballot(inc - s < need && need <= inc);
+    const int L = hit ? (int)__builtin_ctzll(hit) : 0;
+    const uint32_t aboveL = (uint32_t)__shfl((int)(inc - s), L, 64);
+    const int b = kBins - 1 - 32 * L - lane;
+    const uint32_t c = lane < 32 ? sh.hist[hslot(b)] : 0u;
+    const uint32_t inc2 = aboveL + wave_inclusive_sum(c);
+    if (lane < 32 && inc2 - c < need && need <= inc2) {
+      sh.s_prefix = prefix | ((uint32_t)b << shift);
+      sh.s_need = need - (inc2 - c);
+      sh.s_cnt = c;
     }
   }
 }
 
-hipError_t launch_topk_rows(const IndexArgs& A, const float* scores, int32_t* out_idx, float* out_score,
-                            hipStream_t s) {
+// 11-bit radix passes narrowing (prefix, mask, need) until the remaining bucket is
+// taken whole or the bits run out (hi = number of undecided low bits).
+// `hist_keys(mask, prefix, shift, dmask)` adds every key matching the prefix to the
+// histogram under its digit.  `bucket(prefix, mask, need, cnt)` may resolve a small
+// bucket itself and return true.
+template <class HistKeys, class Bucket>
+__device__ __forceinline__ void radix_passes(HistKeys hist_keys, Bucket bucket, SelShared& sh, int hi,
+                                             uint32_t& prefix, uint32_t& mask, uint32_t& need) {
+  while (hi > 0) {
+    const int width = hi < 11 ? hi : 11;
+    const int shift = hi - width;
+    const uint32_t dmask = (1u << width) - 1u;
+    for (int i = threadIdx.x; i < kHistWords; i += kTopkThreads) sh.hist[i] = 0u;
+    if (threadIdx.x == 0) sh.bcount = 0u;
+    __syncthreads();
+    hist_keys(mask, prefix, shift, dmask);
+    __syncthreads();
+    pick_digit(sh, prefix, shift, need);
+    __syncthreads();
+    prefix = sh.s_prefix;
+    need = sh.s_need;
+    const uint32_t cnt = sh.s_cnt;
+    mask |= dmask << shift;
+    hi = shift;
+    if (cnt == need || hi == 0) break;   // uniform across the block
+    if (cnt <= (uint32_t)kBucketMax && bucket(prefix, mask, need, cnt)) break;
+  }
+}
+
+// ---- keys held in registers: key[j] is position 1024 j + t; positions >= n are
+// never counted
+__device__ __forceinline__ bool valid_pos(int j, int n) { return kTopkThreads * j + (int)threadIdx.x < n; }
+
+// Finds (prefix, mask, need): the k largest of the n keys are every key with
+// (key & mask) > prefix plus the first `need` keys (in position order) with
+// (key & mask) == prefix.  Requires 1 <= k <= n.
+template <int KPT>
+__device__ __forceinline__ void reg_threshold(const uint32_t (&key)[KPT], int n, uint32_t k, SelShared& sh,
+                                              uint32_t& prefix, uint32_t& mask, uint32_t& need) {
+  const int lane = threadIdx.x & 63;
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    if (valid_pos(j, n)) {
+      kmin = min(kmin, key[j]);
+      kmax = max(kmax, key[j]);
+    }
+  }
+  block_minmax(kmin, kmax, sh);
+  const int hi = (kmin == kmax) ? 0 : 32 - __clz((int)(kmin ^ kmax));
+  mask = hi >= 32 ? 0u : ~((1u << hi) - 1u);
+  prefix = kmin & mask;
+  need = k;
+  auto hist = [&](uint32_t msk, uint32_t pre, int shift, uint32_t dmask) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      if (valid_pos(j, n) && (key[j] & msk) == pre) atomicAdd(&sh.hist[hslot((key[j] >> shift) & dmask)], 1u);
+    }
+  };
+  // a bucket of <= 64 keys: gather it, and let one wave find the need-th largest
+  // key exactly, bit by bit; ties with it are taken in position order later
+  bool resolved = false;
+  auto bucket = [&](uint32_t pre, uint32_t msk, uint32_t nd, uint32_t cnt) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const bool in = valid_pos(j, n) && (key[j] & msk) == pre;
+      const uint64_t bm = __ballot(in);
+      if (bm) {   // uniform: one slot reservation per wave and round
+        uint32_t base = 0;
+        if (lane == (int)__builtin_ctzll(bm)) base = atomicAdd(&sh.bcount, (uint32_t)__popcll(bm));
+        base = (uint32_t)__builtin_amdgcn_readlane((int)base, (int)__builtin_ctzll(bm));
+        if (in) {
+          const uint32_t p = base + lanes_below(bm);
+          sh.bkey[p] = key[j];
+        }
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      // bitwise MSB-first selection over the undecided low bits, with ballots
+      const uint32_t kl = (uint32_t)lane < cnt ? sh.bkey[lane] : 0u;
+      bool cand = (uint32_t)lane < cnt;
+      uint32_t rem = nd;
+      for (int bit = 31 - __clz((int)~msk); bit >= 0; --bit) {
+        const uint64_t ones = __ballot(cand && ((kl >> bit) & 1u));
+        const uint32_t c1 = (uint32_t)__popcll(ones);
+        const bool take_ones = rem <= c1;
+        if (!take_ones) rem -= c1;
+        cand = cand && (((kl >> bit) & 1u) == (take_ones ? 1u : 0u));
+      }
+      const uint64_t left = __ballot(cand);
+      if (lane == (int)__builtin_ctzll(left)) {
+        sh.s_prefix = kl;
+        sh.s_need = rem;
+      }
+    }
+    __syncthreads();
+    resolved = true;
+    return true;
+  };
+  radix_passes(hist, bucket, sh, hi, prefix, mask, need);
+  if (resolved) {   // uniform: the exact threshold key and the count of its ties to take
+    prefix = sh.s_prefix;
+    need = sh.s_need;
+    mask = ~0u;
+  }
+}
+
+// Writes the selection in position order: out_idx[p] = idx_of(j) for this thread's
+// key[j] when it is the p-th selected position, out_score[p] its score.  Exactly k
+// slots are written.
+template <int KPT, class IdxOf>
+__device__ __forceinline__ void reg_compact(const uint32_t (&key)[KPT], int n, uint32_t prefix, uint32_t mask,
+                                            uint32_t need, int k, IdxOf idx_of, int32_t* oi, float* os,
+                                            SelShared& sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // ballots per round; lane j of the wave keeps round j's two masks
+  uint32_t glo = 0, ghi = 0, elo = 0, ehi = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const bool v = valid_pos(j, n);
+    const uint32_t kp = key[j] & mask;
+    const uint64_t g = __ballot(v && kp > prefix);
+    const uint64_t e = __ballot(v && kp == prefix);
+    if (lane == j) {
+      glo = (uint32_t)g;
+      ghi = (uint32_t)(g >> 32);
+      elo = (uint32_t)e;
+      ehi = (uint32_t)(e >> 32);
+    }
+  }
+  if (lane < KPT) {
+    sh.gmask[lane * kTW + wave] = ((uint64_t)ghi << 32) | glo;
+    sh.emask[lane * kTW + wave] = ((uint64_t)ehi << 32) | elo;
+  }
+  __syncthreads();
+  // cells c = round * kTW + wave are in position order: one wave scans them (lane l
+  // takes C consecutive cells) into per-cell bases
+  if (wave == 0) {
+    constexpr int C = KPT * kTW / 64;
+    uint32_t cg[C], ce[C], sg = 0, se = 0;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      cg[c] = (uint32_t)__popcll(sh.gmask[lane * C + c]);
+      ce[c] = (uint32_t)__popcll(sh.emask[lane * C + c]);
+      sg += cg[c];
+      se += ce[c];
+    }
+    uint32_t gb = wave_inclusive_sum(sg) - sg;
+    uint32_t eb = wave_inclusive_sum(se) - se;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      sh.gbase[lane * C + c] = gb;
+      sh.ebase[lane * C + c] = eb;
+      gb += cg[c];
+      eb += ce[c];
+    }
+  }
+  __syncthreads();
+  const uint32_t bgl = lane < KPT ? sh.gbase[lane * kTW + wave] : 0u;
+  const uint32_t bel = lane < KPT ? sh.ebase[lane * kTW + wave] : 0u;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const uint64_t G = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)ghi, j) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((int)glo, j);
+    const uint64_t E = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)ehi, j) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((int)elo, j);
+    const uint32_t gb = (uint32_t)__builtin_amdgcn_readlane((int)bgl, j);
+    const uint32_t eb = (uint32_t)__builtin_amdgcn_readlane((int)bel, j);
+    const uint64_t bit = 1ull << lane;
+    const uint32_t eq_before = eb + lanes_below(E);
+    const bool sel = (G & bit) || ((E & bit) && eq_before < need);
+    const uint32_t p = gb + lanes_below(G) + min(eq_before, need);
+    if (sel && p < (uint32_t)k) {
+      oi[p] = idx_of(j);
+      if (os) os[p] = key_to_float(key[j]);
+    }
+  }
+}
+
+// ---- keys read from global memory on every pass (long rows whose sampled
+// threshold missed): the same selection, slower.
+template <class KeyAt>
+__device__ __forceinline__ void global_select(KeyAt key_at, int n, int k, int32_t* oi, float* os, SelShared& sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  for (int i = threadIdx.x; i < n; i += kTopkThreads) {
+    const uint32_t key = key_at(i);
+    kmin = min(kmin, key);
+    kmax = max(kmax, key);
+  }
+  block_minmax(kmin, kmax, sh);
+  const int hi0 = (kmin == kmax) ? 0 : 32 - __clz((int)(kmin ^ kmax));
+  uint32_t mask = hi0 >= 32 ? 0u : ~((1u << hi0) - 1u);
+  uint32_t prefix = kmin & mask, need = (uint32_t)k;
+  auto hist = [&](uint32_t msk, uint32_t pre, int shift, uint32_t dmask) {
+#pragma unroll 4
+    for (int i = threadIdx.x; i < n; i += kTopkThreads) {
+      const uint32_t key = key_at(i);
+      if ((key & msk) == pre) atomicAdd(&sh.hist[hslot((key >> shift) & dmask)], 1u);
+    }
+  };
+  auto no_bucket = [](uint32_t, uint32_t, uint32_t, uint32_t) { return false; };
+  radix_passes(hist, no_bucket, sh, hi0, prefix, mask, need);
+  // each wave owns a contiguous range of positions; ballots place the selection in order
+  const int per = (n + kTopkThreads - 1) / kTopkThreads * 64;
+  const int lo = wave * per;
+  const int hi = min(n, lo + per);
+  uint32_t gt = 0, eq = 0;
+  for (int base = lo; base < hi; base += 64) {
+    const int i = base + lane;
+    const bool v = i < hi;
+    const uint32_t kp = v ? (key_at(i) & mask) : 0u;
+    gt += __popcll(__ballot(v && kp > prefix));
+    eq += __popcll(__ballot(v && kp == prefix));
+  }
+  if (lane == 0) {
+    sh.wcnt[wave] = gt;
+    sh.wcnt[kTW + wave] = eq;
+  }
+  __syncthreads();
+  uint32_t gt_before = 0, eq_before = 0;
+  for (int w = 0; w < wave; ++w) {
+    gt_before += sh.wcnt[w];
+    eq_before += sh.wcnt[kTW + w];
+  }
+  uint32_t pos = gt_before + min(eq_before, need);
+  uint32_t eq_seen = eq_before;
+  for (int base = lo; base < hi; base += 64) {
+    const int i = base + lane;
+    const bool v = i < hi;
+    const uint32_t key = v ? key_at(i) : 0u;
+    const uint32_t kp = key & mask;
+    const bool g = v && kp > prefix;
+    const bool e = v && kp == prefix;
+    const uint64_t be = __ballot(e);
+    const bool sel = g || (e && eq_seen + lanes_below(be) < need);
+    const uint64_t bs = __ballot(sel);
+    const uint32_t p = pos + lanes_below(bs);
+    if (sel && p < (uint32_t)k) {
+      oi[p] = i;
+      if (os) os[p] = key_to_float(key);
+    }
+    pos += __popcll(bs);
+    eq_seen += __popcll(be);
+  }
+}
+
+__device__ __forceinline__ int row_visible(const IndexArgs& A, long row) {
+  const int b = (int)(row / A.n_q);
+  const int ne = min(A.n_entries[b], A.n_max);
+  return visible_entries(A.q_pos[row], ne, A.m);
+}
+
+// V <= k: every visible entry in order, then -1.
+__device__ __forceinline__ void take_all(const float* src, int V, int k, int32_t* oi, float* os) {
+  for (int i = threadIdx.x; i < k; i += blockDim.x) {
+    oi[i] = i < V ? i : -1;
+    if (os) os[i] = i < V ? src[i] : -INFINITY;
+  }
+}
+
+// Raw buffer loads over exactly `n_valid` floats: one address register, and
+// positions past the end read as 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t float_rsrc(const float* p, int n_valid) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, n_valid * 4, 0x00020000);
+}
+
+// One row of V <= KPT * 1024 scores, held in registers.
+template <int KPT>
+__device__ __forceinline__ void select_reg_row(const float* src, int V, int k, int32_t* oi, float* os,
+                                               SelShared& sh) {
+  const __amdgpu_buffer_rsrc_t rs = float_rsrc(src, V);
+  uint32_t key[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j)
+    key[j] = order_key(
+        __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (int)threadIdx.x * 4, j * kTopkThreads * 4, 0)));
+  uint32_t prefix, mask, need;
+  reg_threshold<KPT>(key, V, (uint32_t)k, sh, prefix, mask, need);
+  auto idx_of = [](int j) { return kTopkThreads * j + (int)threadIdx.x; };
+  reg_compact<KPT>(key, V, prefix, mask, need, k, idx_of, oi, os, sh);
+}
+
+// ---- rows of up to KPT * 1024 entries: one workgroup per row
+template <int KPT>
+__global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(IndexArgs A, const float* scores, int32_t* out_idx,
+                                                                 float* out_score) {
+  __shared__ SelShared sh;
+  const long row = blockIdx.x;
+  const int V = row_visible(A, row);
+  const int k = A.topk;
+  const float* src = scores + row * A.n_max;
+  int32_t* oi = out_idx + row * k;
+  float* os = out_score ? out_score + row * k : nullptr;
+  if (V <= k) {
+    take_all(src, V, k, oi, os);
+    return;
+  }
+  select_reg_row<KPT>(src, V, k, oi, os, sh);
+}
+
+// ---- long rows, launch 1: the threshold from a fixed sample of the row
+struct LongWs {
+  uint32_t* tau;      // [rows]
+  uint32_t* counts;   // [rows, chunks]
+  uint32_t* ckey;     // [rows, n_max]
+  int32_t* cidx;      // [rows, n_max]
+  int chunks;
+};
+
+__global__ __launch_bounds__(kTopkThreads) void topk_sample_kernel(IndexArgs A, const float* scores, LongWs L) {
+  __shared__ SelShared sh;
+  constexpr int KPT = kSample / kTopkThreads;
+  const long row = blockIdx.x;
+  const int V = row_visible(A, row);
+  if (V <= kRegKeys || V <= A.topk) return;
+  const float* src = scores + row * A.n_max;
+  uint32_t key[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) key[j] = order_key(src[(long)(kTopkThreads * j + threadIdx.x) * V / kSample]);
+  // rank in the sample expected to leave ~3k keys of the row at or above it
+  long r = ((long)3 * A.topk * kSample + V - 1) / V;
+  r = r < 1 ? 1 : (r > kSample ? kSample : r);
+  uint32_t prefix, mask, need;
+  reg_threshold<KPT>(key, kSample, (uint32_t)r, sh, prefix, mask, need);
+  if (threadIdx.x == 0) L.tau[row] = prefix;   // key >= prefix  <=>  (key & mask) >= prefix
+}
+
+// ---- long rows, launch 2: keys at or above the threshold, per chunk, index order
+__global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(IndexArgs A, const float* scores, LongWs L) {
+  __shared__ uint32_t wtot[kFilterThreads / 64];
+  const long row = blockIdx.y;
+  const int c = blockIdx.x;
+  const int V = row_visible(A, row);
+  if (V <= kRegKeys || V <= A.topk) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c0 = c * kChunk;
+  const uint32_t tau = L.tau[row];
+  const float* src = scores + row * A.n_max;
+  constexpr int kIt = kChunk / kFilterThreads;            // 16 keys per lane
+  constexpr int kPerWave = kChunk / (kFilterThreads / 64);
+  const int w0 = c0 + wave * kPerWave;
+  uint32_t key[kIt];
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int r = 0; r < kIt; ++r) {
+    const int i = w0 + r * 64 + lane;
+    key[r] = i < V ? order_key(src[i]) : 0u;
+    cnt += __popcll(__ballot(i < V && key[r] >= tau));
+  }
+  if (lane == 0) wtot[wave] = cnt;
+  __syncthreads();
+  uint32_t pos = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kFilterThreads / 64; ++w) {
+    pos += w < wave ? wtot[w] : 0u;
+    total += wtot[w];
+  }
+  uint32_t* ck = L.ckey + row * A.n_max + c0;
+  int32_t* ci = L.cidx + row * A.n_max + c0;
+#pragma unroll
+  for (int r = 0; r < kIt; ++r) {
+    const int i = w0 + r * 64 + lane;
+    const bool sel = i < V && key[r] >= tau;
+    const uint64_t bs = __ballot(sel);
+    if (sel) {
+      const uint32_t p = pos + lanes_below(bs);
+      ck[p] = key[r];
+      ci[p] = i;
+    }
+    pos += __popcll(bs);
+  }
+  if (threadIdx.x == 0) L.counts[row * L.chunks + c] = total;
+}
+
+// ---- long rows, launch 3: exact selection among the candidates (or the whole row)
+__global__ __launch_bounds__(kTopkThreads) void topk_candidates_kernel(IndexArgs A, const float* scores, LongWs L,
+                                                                       int32_t* out_idx, float* out_score) {
+  __shared__ SelShared sh;
+  __shared__ uint32_t coff[kMaxChunks + 1];
+  __shared__ int32_t cand_idx[kCandCap];
+  constexpr int KPT = kCandCap / kTopkThreads;
+  const long row = blockIdx.x;
+  const int V = row_visible(A, row);
+  const int k = A.topk;
+  const float* src = scores + row * A.n_max;
+  int32_t* oi = out_idx + row * k;
+  float* os = out_score ? out_score + row * k : nullptr;
+  if (V <= k) {
+    take_all(src, V, k, oi, os);
+    return;
+  }
+  if (V <= kRegKeys) {
+    select_reg_row<kMaxKpt>(src, V, k, oi, os, sh);
+    return;
+  }
+  // chunk offsets (exclusive scan of the per-chunk counts, one wave)
+  const int nch = (V + kChunk - 1) / kChunk;
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x < 64) {
+    uint32_t run = 0;
+    for (int base = 0; base < nch; base += 64) {
+      const int c = base + lane;
+      const uint32_t v = c < nch ? L.counts[row * L.chunks + c] : 0u;
+      const uint32_t inc = wave_inclusive_sum(v);
+      if (c < nch) coff[c] = run + inc - v;
+      run += (uint32_t)__shfl((int)inc, 63, 64);
+    }
+    if (lane == 0) coff[nch] = run;
+  }
+  __syncthreads();
+  const int M = (int)coff[nch];
+  if (M < k || M > kCandCap) {   // the sample's threshold missed: select from the row itself
+    auto key_at = [&](int i) { return order_key(src[i]); };
+    global_select(key_at, V, k, oi, os, sh);
+    return;
+  }
+  const uint32_t* gk = L.ckey + row * A.n_max;
+  const int32_t* gi = L.cidx + row * A.n_max;
+  uint32_t key[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int c = kTopkThreads * j + (int)threadIdx.x;
+    key[j] = 0u;
+    if (c < M) {
+      int lo = 0, hi = nch - 1;   // chunk holding candidate c: last chunk whose offset is <= c
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (coff[mid] <= (uint32_t)c) lo = mid;
+        else hi = mid - 1;
+      }
+      const long src_pos = (long)lo * kChunk + (c - (int)coff[lo]);
+      key[j] = gk[src_pos];
+      cand_idx[c] = gi[src_pos];
+    }
+  }
+  uint32_t prefix, mask, need;
+  reg_threshold<KPT>(key, M, (uint32_t)k, sh, prefix, mask, need);   // (its barriers publish cand_idx)
+  auto idx_of = [&](int j) { return cand_idx[kTopkThreads * j + threadIdx.x]; };
+  reg_compact<KPT>(key, M, prefix, mask, need, k, idx_of, oi, os, sh);
+}
+
+static int long_chunks(const IndexArgs& A) { return (A.n_max + kChunk - 1) / kChunk; }
+
+size_t topk_workspace_bytes(const IndexArgs& A) {
+  if (A.n_max <= kRegKeys) return 0;
+  const size_t rows = (size_t)A.batch * A.n_q;
+  const size_t chunks = (size_t)long_chunks(A);
+  auto r256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  return r256(rows * 4) + r256(rows * chunks * 4) + 2 * r256(rows * (size_t)A.n_max * 4);
+}
+
+hipError_t launch_topk_rows(const IndexArgs& A, const float* scores, int32_t* out_idx, float* out_score, void* ws,
+                            size_t ws_bytes, hipStream_t s) {
   const long rows = (long)A.batch * A.n_q;
   if (rows <= 0) return hipSuccess;
   LaunchTimer timer("topk", s);
-  if (A.n_max <= kLdsKeys) {
-    const size_t lds = sizeof(uint32_t) * (size_t)A.n_max;
-    static hipError_t attr = hipFuncSetAttribute((const void*)topk_rows_kernel<true>,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 (int)(sizeof(uint32_t) * kLdsKeys));
-    if (attr != hipSuccess) return attr;
-    topk_rows_kernel<true><<<dim3((unsigned)rows), kTopkThreads, lds, s>>>(A, scores, out_idx, out_score);
-  } else {
-    topk_rows_kernel<false><<<dim3((unsigned)rows), kTopkThreads, 0, s>>>(A, scores, out_idx, out_score);
+  const dim3 grid((unsigned)rows);
+  if (A.n_max <= kRegKeys) {
+    if (A.n_max <= 4096) topk_rows_kernel<4><<<grid, kTopkThreads, 0, s>>>(A, scores, out_idx, out_score);
+    else if (A.n_max <= 8192) topk_rows_kernel<8><<<grid, kTopkThreads, 0, s>>>(A, scores, out_idx, out_score);
+    else topk_rows_kernel<16><<<grid, kTopkThreads, 0, s>>>(A, scores, out_idx, out_score);
+    return hipGetLastError();
   }
+  const int chunks = long_chunks(A);
+  if (chunks > kMaxChunks || ws_bytes < topk_workspace_bytes(A) || !ws) return hipErrorInvalidValue;
+  auto r256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  char* p = (char*)ws;
+  LongWs L;
+  L.tau = (uint32_t*)p;
+  p += r256((size_t)rows * 4);
+  L.counts = (uint32_t*)p;
+  p += r256((size_t)rows * chunks * 4);
+  L.ckey = (uint32_t*)p;
+  p += r256((size_t)rows * A.n_max * 4);
+  L.cidx = (int32_t*)p;
+  L.chunks = chunks;
+  topk_sample_kernel<<<grid, kTopkThreads, 0, s>>>(A, scores, L);
+  topk_filter_kernel<<<dim3((unsigned)chunks, (unsigned)rows), kFilterThreads, 0, s>>>(A, scores, L);
+  topk_candidates_kernel<<<grid, kTopkThreads, 0, s>>>(A, scores, L, out_idx, out_score);
   return hipGetLastError();
 }
 

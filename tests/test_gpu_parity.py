@@ -157,6 +157,39 @@ def test_topk_ties_and_degenerate_rows():
     np.testing.assert_array_equal(idx[3, 0], -np.ones(k))
 
 
+def test_topk_long_rows():
+    """Rows longer than the LDS-resident limit (40,000 entries): the sampled-threshold
+    filter path (also with exact ties at the boundary), its fallback (the threshold
+    passes too many keys: half the scores tie; every score 0), and shorter rows in the
+    same launch.  Exact against the oracle's selection on the GPU's own scores."""
+    B, n_q, HI, dI, N, m, k = 5, 2, 2, 32, 40000, 4, 1000
+    rng = np.random.default_rng(11)
+    q = rng.standard_normal((B, n_q, HI, dI)).astype(np.float32)
+    kk = rng.standard_normal((B, N, dI)).astype(np.float32)
+    for b, (lo, hi) in ((1, (-3, 6)), (4, (0, 2))):      # score = (w0 + w1) * relu(k0): few values
+        q[b] = 0.0
+        q[b, :, :, 0] = 1.0
+        kk[b, :, 0] = rng.integers(lo, hi, N).astype(np.float32)
+    w = rng.random((B, n_q, HI)).astype(np.float32)
+    w[3] = 0.0                                             # seq 3: every score 0
+    n_entries = np.array([N, N, 20000, N, N], dtype=np.int32)   # seq 2: rows within the LDS limit
+    q_pos = np.array([[m * N - 1, m * 33000], [m * N - 1, m * N - 9], [m * N - 1, 100], [m * N - 1, m * N - 1],
+                      [m * N - 1, m * 35000]], dtype=np.int32)
+    args = (dev(q), dev(w), dev(kk), _i32(n_entries), _i32(q_pos))
+    idx, sc = csa.index_topk(*args, m=m, topk=k, n_max=N)
+    idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+    scores = host(csa.index_scores(*args, m=m, n_max=N))
+    for b in range(B):
+        for i in range(n_q):
+            V = oracle.visible(q_pos[b, i], n_entries[b], m)
+            exact = oracle.topk(scores[b, i, :V], V, k)
+            want = np.sort(exact[:min(k, V)]).tolist() + [-1] * (k - min(k, V))
+            np.testing.assert_array_equal(idx[b, i], want, "seq %d query %d (V=%d)" % (b, i, V))
+            sel = idx[b, i] >= 0
+            np.testing.assert_array_equal(sc[b, i][sel], scores[b, i][idx[b, i][sel]])
+    np.testing.assert_array_equal(idx[3, 0], np.arange(k))     # all ties -> lowest indices
+
+
 # ------------------------------------------------------------------------ MQA
 def _mqa_case(dtype, B, n_q, H, d, N, k, window, seed):
     rng = np.random.default_rng(seed)
