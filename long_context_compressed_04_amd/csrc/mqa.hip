@@ -175,7 +175,7 @@ constexpr int kRowB = kD * 2 + 16;      // LDS row stride in bytes (padded)
 struct MqaLaunch {
   int nsplit, ips, n_hg, units, nw;   // nw: waves per workgroup
   int slots;                          // index slots of a split copied to LDS
-  int heads32;                        // 32-head waves (heads % 128 == 0)
+  int kind;                           // 0: 16-head waves, 1: 128-head workgroups, 2: 32-head workgroups
 };
 
 // Masked items are loaded from this all-zero row, so that no lane ever reads
@@ -748,6 +748,7 @@ __global__ __launch_bounds__(256) void mqa32_kernel(MqaArgs A, MqaLaunch L, floa
 // in another (one shared array would force a wait for every load before any LDS
 // read); the barriers are plain s_barrier with explicit LDS waits for the same reason.
 constexpr int kXS = 16;             // logits per lane exchanged within a wave pair
+constexpr int kStageRow = 128 + 4;  // fp32 words per head row of the output staging (padded)
 constexpr int kSlotsLds = 2048;     // index slots of a split held in LDS
 
 __device__ __forceinline__ float rows_total4(const float (&p)[4], int lane) {
@@ -779,6 +780,38 @@ __device__ __forceinline__ void lds_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Sum of squares of 8 bf16 values added to acc (four v_dot2_f32_bf16).
+__device__ __forceinline__ float sumsq_bf16x8(uint4 v, float acc) {
+  typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+  const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const bf16x2_v b = __builtin_bit_cast(bf16x2_v, w4[k]);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(b, b, acc, false);
+  }
+  return acc;
+}
+
+// Gathers RPW rows (items item0 + STRIDE * rr) of one wave into LDS rows
+// dst + STRIDE * rr * kRowB2, 16 bytes per lane.  Lane rr resolves row rr (all
+// lookups at once); the loop reads the addresses back as scalars.  A masked row is
+// loaded from the zero row.  Returns the mask of rows that exist.
+template <int RPW, int STRIDE, class Resolve>
+__device__ __forceinline__ uint32_t issue_rows(Resolve resolve, int item0, int lane, uint8_t* dst) {
+  const uint8_t* pl = resolve(item0 + STRIDE * (lane % RPW));
+  const uint64_t pv = (uint64_t)(pl ? pl : g_zero_row);
+  const uint32_t lo = (uint32_t)pv, hi = (uint32_t)(pv >> 32);
+  const uint32_t ok = (uint32_t)__ballot(pl != nullptr) & ((1u << RPW) - 1u);
+  // a rolled loop: few distinct direct-to-LDS instructions for the compiler to track
+#pragma unroll 1
+  for (int rr = 0; rr < RPW; ++rr) {
+    const uint64_t p = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, rr) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((int)lo, rr);
+    load_row_to_lds((const uint8_t*)p + 16 * lane, dst + STRIDE * rr * kRowB2);
+  }
+  return ok;
+}
+
 struct RowSrc {
   const uint8_t* kv;
   const uint8_t* raw;
@@ -791,8 +824,8 @@ void mqa32d_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml) {
   __shared__ __attribute__((aligned(16))) uint8_t tb0[kTile * kRowB2];
   __shared__ __attribute__((aligned(16))) uint8_t tb1[kTile * kRowB2];
   __shared__ __attribute__((aligned(16))) uint8_t tb2[kTile * kRowB2];
-  __shared__ float irms[kNB][kTile];
-  __shared__ float xbuf[8][kXS][64];
+  __shared__ uint32_t okw[kNB][8];        // per buffer: which of each wave's rows exist
+  __shared__ float xbuf[8][kXS + 1][64];  // partial S^T, then the partial row sum of squares
   __shared__ int32_t slot[kSlotsLds];
   __shared__ float qss[8][64];
 
@@ -888,14 +921,7 @@ void mqa32d_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml) {
   // track only a handful of in-flight direct-to-LDS loads individually before it
   // falls back to waiting for all of them at every LDS access.
   auto issue = [&](int ti, uint8_t* dst) -> uint32_t {
-    uint32_t ok = 0;
-#pragma unroll 1
-    for (int rr = 0; rr < RPW; ++rr) {
-      const uint8_t* p = resolve(R.it0 + ti * kTile + wave + 8 * rr);
-      ok |= (p != nullptr ? 1u : 0u) << rr;
-      load_row_to_lds((p ? p : g_zero_row) + 16 * lane, dst + (wave + 8 * rr) * kRowB2);
-    }
-    return ok;
+    return issue_rows<RPW, 8>(resolve, R.it0 + ti * kTile + wave, lane, dst + wave * kRowB2);
   };
   if (n_tiles > 0) okm[0] = issue(0, tb0);
   if (n_tiles > 1) okm[1] = issue(1, tb1);
@@ -911,30 +937,13 @@ void mqa32d_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml) {
     // flight; loads complete in issue order)
     if (ti + 1 < n_tiles) __builtin_amdgcn_s_waitcnt(0x0F70 | RPW);
     else __builtin_amdgcn_s_waitcnt(0x0F70);
-    {
-      float part[RPW];
-#pragma unroll
-      for (int rr = 0; rr < RPW; ++rr) {
-        const uint4 v = *(const uint4*)(tile + (wave + 8 * rr) * kRowB2 + 16 * lane);
-        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-        float ss = 0.f;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float lo = __uint_as_float(w4[k] << 16), hi = __uint_as_float(w4[k] & 0xffff0000u);
-          ss = fmaf(lo, lo, fmaf(hi, hi, ss));
-        }
-        part[rr] = ss;
-      }
-      const float tot = rows_total4(part, lane);
-      const int rr = 2 * ((lane >> 5) & 1) + ((lane >> 4) & 1);
-      if ((lane & 15) == 0)
-        irms[BUF][wave + 8 * rr] = ((okm[BUF] >> rr) & 1u) ? 1.f / sqrtf(tot * (1.f / kD) + eps) : 0.f;
-    }
+    if (lane == 0) okw[BUF][wave] = okm[BUF];
     lds_barrier();
     if (ti + 2 < n_tiles) okm[(BUF + 2) % kNB] = issue(ti + 2, buf_ptr((BUF + 2) % kNB));
 
     // ---- partial S^T over this wave's 256 dims: 16 k-steps of 16
     f32x16_t s;
+    float ssr = 0.f;
     {
       const uint8_t* ka = tile + ka_off;
       constexpr int PF = 2;
@@ -947,22 +956,30 @@ void mqa32d_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml) {
         const uint4 c = a[ks % PF];
         if (ks + PF < 16) a[ks % PF] = *(const uint4*)(ka + 32 * (ks + PF));
         s2[ks & 1] = mfma32x32x16(as_bf16x8(c), qf[ks], s2[ks & 1]);
+        // row c32's sum of squares over the same operand (dims 16 ks + 8 h + [0, 8))
+        ssr = sumsq_bf16x8(c, ssr);
+        // keep this order: consuming the operand loaded PF steps ago, not the one
+        // just requested, keeps PF LDS reads in flight
+        __builtin_amdgcn_sched_barrier(0);
       }
       s = s2[0] + s2[1];
     }
     // ---- full S^T = own half + partner's half (the same sum in both waves)
+    ssr += __shfl_xor(ssr, 32, 64);   // this wave's 256 dims of row c32
 #pragma unroll
     for (int r = 0; r < kXS; ++r) xbuf[wave][r][lane] = s[r];
+    xbuf[wave][kXS][lane] = ssr;
     lds_barrier();
     // ---- softmax weights: this lane's head over items 8*(r/4) + 4*h + r%4.  LDS
     // operands first, then branch-free weights (a masked row has inv_rms 0 and
     // weight 0).  Exponents lie in [-100, 100]: the hardware exp2 is never denormal.
-    float ir[16], xp[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      ir[r] = irms[BUF][8 * (r / 4) + 4 * h + (r % 4)];
-      xp[r] = xbuf[wave ^ 1][r][lane];
-    }
+    for (int r = 0; r < 16; ++r) s[r] += xbuf[wave ^ 1][r][lane];
+    // 1/rms of row c32 (0 for a row that does not exist); the rows of this lane's
+    // logits, 8 (r/4) + 4 h + r%4, are read from the lanes holding them
+    const float ss = ssr + xbuf[wave ^ 1][kXS][lane];
+    const bool row_ok = (okw[BUF][c32 & 7] >> (c32 >> 3)) & 1u;
+    const float inv = row_ok ? 1.f / sqrtf(ss * (1.f / kD) + eps) : 0.f;
     float psum = 0.f;
     uint32_t pk[8];
 #pragma unroll
@@ -970,11 +987,11 @@ void mqa32d_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml) {
       float p2[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const float full = s[r + u] + xp[r + u];
-        const float e = __builtin_amdgcn_exp2f(full * sl2 * ir[r + u]);
-        const float p = ir[r + u] > 0.f ? e : 0.f;
+        const float ir = __shfl(inv, 8 * ((r + u) / 4) + 4 * h + ((r + u) % 4), 64);
+        const float e = __builtin_amdgcn_exp2f(s[r + u] * sl2 * ir);
+        const float p = ir > 0.f ? e : 0.f;
         psum += p;
-        p2[u] = p * ir[r + u];   // weight on the raw row (its 1/rms folded in)
+        p2[u] = p * ir;   // weight on the raw row (its 1/rms folded in)
       }
       pk[r / 2] = pack_bf16x2(p2[0], p2[1]);
     }
@@ -1010,28 +1027,296 @@ void mqa32d_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml) {
   }
 
   l_run += __shfl_xor(l_run, 32, 64);
-  // o[db][r] holds dim 256*dh + 32*db + 8*(r/4) + 4*h + r%4 of this lane's head
-  if (L.nsplit == 1) {
-    const float inv_l = l_run > 0.f ? 1.f / l_run : 0.f;
-    uint16_t* orow = (uint16_t*)A.out + (row * A.heads + head) * kD + 256 * dh;
+  // o[db][r] holds dim 256 dh + 32 db + 8 (r/4) + 4 h + r%4 of this lane's head.  The
+  // 32 x 256 block leaves through LDS in two 128-dim halves (the tile buffers and the
+  // exchange buffer are free once every wave is past its last tile), so that each
+  // store instruction writes two whole head rows.
+  lds_barrier();
+  float* stage = (float*)((wave < 2 ? tb0 : (wave < 4 ? tb1 : (wave < 6 ? tb2 : (uint8_t*)&xbuf[0][0][0]))) +
+                          (wave & 1) * (32 * kStageRow * 4));
+  const int hl = lane >> 5, d4 = lane & 31;
+  const float inv_l = l_run > 0.f ? 1.f / l_run : 0.f;   // l of lane c32's head
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
+  for (int half = 0; half < 2; ++half) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int d0 = 32 * db + 8 * j + 4 * h;
-        *(uint2*)(orow + d0) = make_uint2(pack_bf16x2(o[db][4 * j] * inv_l, o[db][4 * j + 1] * inv_l),
-                                          pack_bf16x2(o[db][4 * j + 2] * inv_l, o[db][4 * j + 3] * inv_l));
+        const f32x16_t& od = o[4 * half + db];
+        *(f32x4_t*)(stage + c32 * kStageRow + 32 * db + 8 * j + 4 * h) =
+            f32x4_t{od[4 * j], od[4 * j + 1], od[4 * j + 2], od[4 * j + 3]};
       }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // (a wave-private region: no barrier)
+    const int dim0 = 256 * dh + 128 * half + 4 * d4;
+    if (L.nsplit == 1) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int hh = 2 * k + hl;
+        const float il = __shfl(inv_l, hh, 64);
+        const f32x4_t v = *(const f32x4_t*)(stage + hh * kStageRow + 4 * d4);
+        uint16_t* orow = (uint16_t*)A.out + (row * A.heads + hg * 128 + (wave >> 1) * 32 + hh) * kD + dim0;
+        *(uint2*)orow = make_uint2(pack_bf16x2(v[0] * il, v[1] * il), pack_bf16x2(v[2] * il, v[3] * il));
+      }
+    } else {
+      float* po = part_o + (((long)row * L.nsplit + split) * A.heads + hg * 128 + (wave >> 1) * 32) * kD + dim0;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int hh = 2 * k + hl;
+        *(f32x4_t*)(po + (long)hh * kD) = *(const f32x4_t*)(stage + hh * kStageRow + 4 * d4);
+      }
+    }
+  }
+  if (L.nsplit == 1) {
     if (A.lse && h == 0 && dh == 0) A.lse[row * A.heads + head] = l_run > 0.f ? logf(l_run) : -INFINITY;
+  } else if (h == 0 && dh == 0) {
+    float* pm = part_ml + (((long)row * L.nsplit + split) * A.heads + head) * 2;
+    pm[0] = l_run > 0.f ? 0.f : -INFINITY;
+    pm[1] = l_run;
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Head-group kernel for few queries (decode): a workgroup = 4 waves = one group of
+// 32 heads of one (query, split) unit, wave w owning dims 128 w .. 128 w + 127.  The
+// four head groups of a unit run on one XCD, so three of the four gathers of a row
+// hit that XCD's L2.  Per 32-row tile each wave forms S^T over its 128 dims, the
+// four partial S^T meet in LDS (one barrier), and each wave accumulates O^T for its
+// own dims.  Splitting heads as well as items keeps the fp32 partials of a
+// decode-sized batch 4x smaller than splitting items alone.
+constexpr int kHgWaves = 4;
+constexpr int kHgRpw = kTile / kHgWaves;   // rows each wave stages per tile
+
+__global__ __launch_bounds__(kHgWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mqa_hg_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml) {
+  __shared__ __attribute__((aligned(16))) uint8_t tb0[kTile * kRowB2];
+  __shared__ __attribute__((aligned(16))) uint8_t tb1[kTile * kRowB2];
+  __shared__ __attribute__((aligned(16))) uint8_t tb2[kTile * kRowB2];
+  __shared__ float irms[kNB][kTile];
+  __shared__ float xbuf[2][kHgWaves][kXS][64];   // by tile parity: one barrier per tile
+  __shared__ int32_t slot[kSlotsLds];
+  __shared__ float qss[kHgWaves][64];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane >> 5, c32 = lane & 31;
+
+  const int f = blockIdx.x;
+  const int xcd = f & 7, r8 = f >> 3;
+  const int hg = r8 % L.n_hg, ug = r8 / L.n_hg;
+  const int unit = ug * 8 + xcd;
+  if (unit >= L.units) return;
+  const long row = unit / L.nsplit;
+  const int split = unit % L.nsplit;
+  const int b = (int)(row / A.n_q);
+  const int head = hg * 32 + c32;
+
+  // ---- the items of this (query, split): index slots first, then the query
+  RowSrc R;
+  {
+    ItemSource src;
+    int total;
+    query_items(A, b, row, 2, src, total);
+    R.kv = src.kv; R.raw = src.raw; R.n_first = src.n_first; R.kv_rows = src.kv_rows; R.win_lo = src.win_lo;
+    R.raw_base = src.raw_base; R.raw_cap = src.raw_cap; R.dense = A.dense;
+    R.it0 = split * L.ips;
+    R.it1 = min(total, R.it0 + L.ips);
+    R.gidx = src.idx;
+    R.use_slots = !A.dense;
+    if (R.use_slots)
+      for (int i = threadIdx.x; i < L.ips; i += kHgWaves * 64) {
+        const int it = R.it0 + i;
+        slot[i] = (it < min(R.it1, R.n_first)) ? src.idx[it] : -1;
+      }
+  }
+  // this wave's dims of the query row: 128 w + 16 ks + 8 h + [0, 8)
+  const uint16_t* qrow = (const uint16_t*)A.q + (row * A.heads + head) * kD + 128 * wave;
+  uint4 qraw[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) qraw[ks] = *(const uint4*)(qrow + 16 * ks + 8 * h);
+  lds_barrier();   // the slots are in LDS (each store waited for its load)
+
+  auto resolve = [&](int item) -> const uint8_t* {
+    if (item >= R.it1) return nullptr;
+    if (item < R.n_first) {
+      const int e = R.dense ? item : slot[item - R.it0];
+      return (e >= 0 && e < R.kv_rows) ? R.kv + (long)e * (kD * 2) : nullptr;
+    }
+    const int r = R.win_lo + (item - R.n_first) - R.raw_base;
+    return (r >= 0 && r < R.raw_cap) ? R.raw + (long)r * (kD * 2) : nullptr;
+  };
+  const int n_tiles = (R.it1 - R.it0 + kTile - 1) / kTile;
+  uint32_t okm[kNB] = {0, 0, 0};
+  auto buf_ptr = [&](int bi) -> uint8_t* { return bi == 0 ? tb0 : (bi == 1 ? tb1 : tb2); };
+  auto issue = [&](int ti, uint8_t* dst) -> uint32_t {
+    return issue_rows<kHgRpw, kHgWaves>(resolve, R.it0 + ti * kTile + wave, lane, dst + wave * kRowB2);
+  };
+  // the first two tiles' gathers go out before the query is normalised
+  if (n_tiles > 0) okm[0] = issue(0, tb0);
+  if (n_tiles > 1) okm[1] = issue(1, tb1);
+
+  // ---- u = q / rms(q): the four waves swap their partial sums of squares
+  bf16x8_t qf[8];
+  {
+    float ss = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const uint32_t w4[4] = {qraw[ks].x, qraw[ks].y, qraw[ks].z, qraw[ks].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float lo = __uint_as_float(w4[k] << 16), hi = __uint_as_float(w4[k] & 0xffff0000u);
+        ss = fmaf(lo, lo, fmaf(hi, hi, ss));
+      }
+    }
+    ss += __shfl_xor(ss, 32, 64);
+    qss[wave][lane] = ss;
+    lds_barrier();
+    ss = qss[0][lane] + qss[1][lane] + qss[2][lane] + qss[3][lane];
+    const float qinv = 1.f / sqrtf(ss * (1.f / kD) + A.eps);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const uint32_t w4[4] = {qraw[ks].x, qraw[ks].y, qraw[ks].z, qraw[ks].w};
+      uint32_t o4[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        o4[k] = pack_bf16x2(__uint_as_float(w4[k] << 16) * qinv, __uint_as_float(w4[k] & 0xffff0000u) * qinv);
+      qf[ks] = as_bf16x8(make_uint4(o4[0], o4[1], o4[2], o4[3]));
+    }
+  }
+  const float sl2 = A.scale * kLog2e;
+  const float eps = A.eps;
+  float l_run = 0.f;
+  f32x16_t o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) o[db] = f32x16_t{};
+
+  const int G = lane >> 4, sl = lane & 15;
+  const int vb_off = (4 * h + (sl >> 2)) * kRowB2 + 256 * wave + (16 * (G & 1) + 4 * (sl & 3)) * 2;
+  const int ka_off = c32 * kRowB2 + 256 * wave + 16 * h;
+
+  auto step = [&](auto BUFC, int ti) {
+    constexpr int BUF = decltype(BUFC)::value;
+    uint8_t* const tile = BUF == 0 ? tb0 : (BUF == 1 ? tb1 : tb2);
+    // this wave's rows of tile ti have landed (tile ti+1's may still be in flight)
+    if (ti + 1 < n_tiles) __builtin_amdgcn_s_waitcnt(0x0F70 | kHgRpw);
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
+    // ---- 1/rms of the rows this wave staged (written for the other waves)
+    {
+      float part[kHgRpw];
+#pragma unroll
+      for (int rr = 0; rr < kHgRpw; ++rr) {
+        const uint4 v = *(const uint4*)(tile + (wave + kHgWaves * rr) * kRowB2 + 16 * lane);
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+        float ss = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float lo = __uint_as_float(w4[k] << 16), hi = __uint_as_float(w4[k] & 0xffff0000u);
+          ss = fmaf(lo, lo, fmaf(hi, hi, ss));
+        }
+        part[rr] = ss;
+      }
+      row_totals<kHgRpw>(part, lane, irms[BUF], wave, kHgWaves, okm[BUF], eps);
+    }
+    // ---- partial S^T over this wave's 128 dims: 8 k-steps of 16
+    f32x16_t s;
+    {
+      const uint8_t* ka = tile + ka_off;
+      uint4 a[8];
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) a[ks] = *(const uint4*)(ka + 32 * ks);
+      f32x16_t s2[2] = {f32x16_t{}, f32x16_t{}};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) s2[ks & 1] = mfma32x32x16(as_bf16x8(a[ks]), qf[ks], s2[ks & 1]);
+      s = s2[0] + s2[1];
+    }
+    float (*const xb)[kXS][64] = xbuf[ti & 1];
+#pragma unroll
+    for (int r = 0; r < kXS; ++r) xb[wave][r][lane] = s[r];
+    // every wave is past the previous tile (its buffer is free) and this tile's
+    // partial S^T and row norms are in LDS
+    lds_barrier();
+    if (ti + 2 < n_tiles) okm[(BUF + 2) % kNB] = issue(ti + 2, buf_ptr((BUF + 2) % kNB));
+    float ir[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ir[r] = irms[BUF][8 * (r / 4) + 4 * h + (r % 4)];
+#pragma unroll
+    for (int w = 0; w < kHgWaves; ++w) {
+      if (w == wave) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] += xb[w][r][lane];
+    }
+    // ---- softmax weights (exponents within [-100, 100]; a masked row has weight 0)
+    float psum = 0.f;
+    uint32_t pk[8];
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      float p2[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const float e = __builtin_amdgcn_exp2f(s[r + u] * sl2 * ir[r + u]);
+        const float p = ir[r + u] > 0.f ? e : 0.f;
+        psum += p;
+        p2[u] = p * ir[r + u];
+      }
+      pk[r / 2] = pack_bf16x2(p2[0], p2[1]);
+    }
+    l_run += psum;
+    const bf16x8_t pb0 = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
+    const bf16x8_t pb1 = as_bf16x8(make_uint4(pk[4], pk[5], pk[6], pk[7]));
+    // ---- O^T += V^T . P^T over this wave's 4 dim blocks
+    const uint8_t* vb = tile + vb_off;
+    i16x4_t v0[8], v1[8];
+    auto vaddr = [&](int k) { return vb + (16 * (k & 1)) * kRowB2 + 64 * (k >> 1); };   // k = 2*db + t
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      v0[k] = lds_read_tr16(vaddr(k));
+      v1[k] = lds_read_tr16(vaddr(k) + 8 * kRowB2);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      typedef short i16x8_t __attribute__((ext_vector_type(8)));
+      const i16x8_t vv = {v0[k][0], v0[k][1], v0[k][2], v0[k][3], v1[k][0], v1[k][1], v1[k][2], v1[k][3]};
+      o[k >> 1] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, vv), (k & 1) ? pb1 : pb0, o[k >> 1]);
+    }
+  };
+  for (int ti = 0; ti < n_tiles; ti += kNB) {
+    step(std::integral_constant<int, 0>{}, ti);
+    if (ti + 1 < n_tiles) step(std::integral_constant<int, 1>{}, ti + 1);
+    if (ti + 2 < n_tiles) step(std::integral_constant<int, 2>{}, ti + 2);
+  }
+
+  l_run += __shfl_xor(l_run, 32, 64);
+  // o[db][r] holds dim 128 w + 32 db + 8 (r/4) + 4 h + r%4 of this lane's head.  The
+  // 32 x 128 block goes through LDS (the tile buffers are free once every wave is
+  // past its last tile) so that each store instruction writes two whole head rows.
+  lds_barrier();
+  float* stage = (float*)((wave < 2 ? tb0 : tb1) + (wave & 1) * (32 * kStageRow * 4));
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *(f32x4_t*)(stage + c32 * kStageRow + 32 * db + 8 * j + 4 * h) =
+          f32x4_t{o[db][4 * j], o[db][4 * j + 1], o[db][4 * j + 2], o[db][4 * j + 3]};
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // this wave's LDS writes are done (wave-private region)
+  const int hl = lane >> 5, d4 = lane & 31;
+  if (L.nsplit == 1) {
+    const float inv_l = l_run > 0.f ? 1.f / l_run : 0.f;   // l is per head: lane c32's head
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int hh = 2 * k + hl;
+      const float il = __shfl(inv_l, hh, 64);
+      const f32x4_t v = *(const f32x4_t*)(stage + hh * kStageRow + 4 * d4);
+      uint16_t* orow = (uint16_t*)A.out + (row * A.heads + hg * 32 + hh) * kD + 128 * wave + 4 * d4;
+      *(uint2*)orow = make_uint2(pack_bf16x2(v[0] * il, v[1] * il), pack_bf16x2(v[2] * il, v[3] * il));
+    }
+    if (A.lse && h == 0 && wave == 0) A.lse[row * A.heads + head] = l_run > 0.f ? logf(l_run) : -INFINITY;
   } else {
-    float* po = part_o + (((long)row * L.nsplit + split) * A.heads + head) * kD + 256 * dh;
+    float* po = part_o + (((long)row * L.nsplit + split) * A.heads + hg * 32) * kD + 128 * wave + 4 * d4;
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *(f32x4_t*)(po + 32 * db + 8 * j + 4 * h) =
-            f32x4_t{o[db][4 * j], o[db][4 * j + 1], o[db][4 * j + 2], o[db][4 * j + 3]};
-    if (h == 0 && dh == 0) {
+    for (int k = 0; k < 16; ++k) {
+      const int hh = 2 * k + hl;
+      *(f32x4_t*)(po + (long)hh * kD) = *(const f32x4_t*)(stage + hh * kStageRow + 4 * d4);
+    }
+    if (h == 0 && wave == 0) {
       float* pm = part_ml + (((long)row * L.nsplit + split) * A.heads + head) * 2;
       pm[0] = l_run > 0.f ? 0.f : -INFINITY;
       pm[1] = l_run;
@@ -1089,32 +1374,38 @@ static MqaLaunch plan_mqa(const MqaArgs& A) {
   const long rows = (long)A.batch * A.n_q;
   const int total_max = (A.dense ? A.n_max : A.topk) + A.window;
   const int tiles_max = (total_max + kTile - 1) / kTile;
-  // 32-head path: heads in groups of 128, unit RMSNorm weight, and a scale that keeps
-  // every exp2(logit) normal without a running maximum.
-  L.heads32 = A.heads % 128 == 0 && A.gamma == nullptr && A.scale * kLog2e * kD * 1.01f <= 100.f;
-  if (L.heads32) {
-    // One workgroup (8 waves: 4 x 32 heads x 2 dim halves) per CU.  Split count
-    // from a cost model measured on MI355X: ~2.9 us per 32-row tile a workgroup
-    // works through, rounds of <= 256 workgroups, ~0.06 us per (query, split) of
-    // fp32 partials written and merged, ~6 us for the merge kernel itself.
-    L.nw = 8;
-    L.n_hg = A.heads / 128;
+  // 32-head MFMA paths need the unit RMSNorm weight and a scale that keeps every
+  // exp2(logit) normal without a running maximum.  Few queries (decode): 32-head
+  // workgroups, splitting heads and items; many queries: 128-head workgroups.
+  const bool fixed = A.gamma == nullptr && A.scale * kLog2e * kD * 1.01f <= 100.f;
+  L.kind = 0;
+  if (fixed && A.heads % 32 == 0 && rows <= 32) L.kind = 2;
+  else if (fixed && A.heads % 128 == 0) L.kind = 1;
+  if (L.kind != 0) {
+    // Split count from a cost model measured on MI355X: per 32-row tile a workgroup
+    // works through, rounds of <= 256 workgroups (one per CU), the fp32 partials each
+    // (query, head group, split) writes and the merge reads, and the merge launch.
+    const bool hg = L.kind == 2;
+    L.nw = hg ? kHgWaves : 8;
+    L.n_hg = A.heads / (hg ? 32 : 128);
+    const double t_tile = hg ? 0.6 : 2.9, t_part = hg ? 0.03 : 0.06, t_merge = hg ? 4.0 : 6.0;
     double best = 1e30;
     int best_s = 1;
     for (int sp = 1; sp <= kMaxSplit && sp <= tiles_max; ++sp) {
       const int tps = (tiles_max + sp - 1) / sp;
       const int s_eff = (tiles_max + tps - 1) / tps;
+      if (!A.dense && tps * kTile > kSlotsLds) continue;   // index slots must fit in LDS
       const double wgs = (double)rows * L.n_hg * s_eff;
       const int rounds = (int)((wgs + 255) / 256);
-      const double cost = rounds * tps * 2.9 + (s_eff > 1 ? 6.0 + 0.06 * rows * L.n_hg * s_eff : 0.0);
+      const double cost = rounds * tps * t_tile + (s_eff > 1 ? t_merge + t_part * rows * L.n_hg * s_eff : 0.0);
       if (cost < best - 1e-9) { best = cost; best_s = s_eff; }
     }
     const int tps = (tiles_max + best_s - 1) / best_s;
     L.ips = tps * kTile;
     L.nsplit = (tiles_max + tps - 1) / tps;
-    if (!A.dense && L.ips > kSlotsLds) L.heads32 = 0;   // index slots must fit in LDS
+    if (!A.dense && L.ips > kSlotsLds) L.kind = 0;
   }
-  if (!L.heads32) {
+  if (L.kind == 0) {
     L.nw = (A.heads % 64 == 0) ? 4 : ((A.heads % 32 == 0) ? 2 : 1);
     L.n_hg = A.heads / (L.nw * 16);
     // One workgroup per CU fits (about 380 registers per lane): aim at one round of
@@ -1142,7 +1433,7 @@ constexpr int kMaxDynLds = 152 * 1024;
 
 static size_t mqa_lds_bytes(const MqaLaunch& L) {
   const size_t slots = L.slots ? (size_t)L.ips * sizeof(int32_t) : 0;
-  if (L.heads32) return 0;   // static LDS only
+  if (L.kind != 0) return 0;   // static LDS only
   return (size_t)2 * kTile * kRowB + 2 * kTile * sizeof(float) + kD * sizeof(float) + slots;
 }
 
@@ -1198,8 +1489,9 @@ hipError_t launch_mqa(const MqaArgs& A, void* ws, size_t ws_bytes, hipStream_t s
   const long groups = ((long)L.units + 7) / 8;
   dim3 grid((unsigned)(groups * 8 * L.n_hg));
   {
-    LaunchTimer timer(L.heads32 ? "mqa_bf16_h32" : "mqa_bf16_h16", s);
-    if (L.heads32) mqa32d_kernel<<<grid, 512, lds, s>>>(A, L, part_o, part_ml);
+    LaunchTimer timer(L.kind == 2 ? "mqa_bf16_hg" : (L.kind == 1 ? "mqa_bf16_h32" : "mqa_bf16_h16"), s);
+    if (L.kind == 2) mqa_hg_kernel<<<grid, kHgWaves * 64, lds, s>>>(A, L, part_o, part_ml);
+    else if (L.kind == 1) mqa32d_kernel<<<grid, 512, lds, s>>>(A, L, part_o, part_ml);
     else if (L.nw == 4) mqa_bf16_kernel<4><<<grid, 4 * 64, lds, s>>>(A, L, part_o, part_ml);
     else if (L.nw == 2) mqa_bf16_kernel<2><<<grid, 2 * 64, lds, s>>>(A, L, part_o, part_ml);
     else mqa_bf16_kernel<1><<<grid, 64, lds, s>>>(A, L, part_o, part_ml);

@@ -207,6 +207,9 @@ def _mqa_case(dtype, B, n_q, H, d, N, k, window, seed):
     ("bf16", 1, 3, 64, 512, 500, 100, 128),
     ("bf16", 2, 1, 16, 512, 300, 50, 7),
     ("bf16", 1, 40, 32, 512, 400, 64, 128),        # many queries (one split each)
+    ("bf16", 1, 40, 128, 512, 700, 300, 128),      # many queries, 128-head workgroups
+    ("bf16", 3, 2, 96, 512, 1500, 700, 128),       # few queries, 32-head workgroups, 3 head groups
+    ("bf16", 1, 1, 128, 512, 300, 40, 0),          # no window, one tile
 ])
 def test_sparse_mqa(dtype, B, n_q, H, d, N, k, window):
     q, kv, kv_raw, rng = _mqa_case(dtype, B, n_q, H, d, N, k, window, seed=H + N + k)
@@ -240,6 +243,7 @@ def test_sparse_mqa(dtype, B, n_q, H, d, N, k, window):
     ("bf16", 2, 1, 128, 512, 1500, 128, 128, 0),
     ("bf16", 1, 2, 64, 512, 333, 4, 128, -100),
     ("bf16", 1, 1, 16, 512, 40, 4, 128, -150),       # t < m*N: few entries visible
+    ("bf16", 1, 40, 128, 512, 600, 4, 128, -50),     # many queries, 128-head workgroups
 ])
 def test_dense_mqa(dtype, B, n_q, H, d, N, m, window, t_off):
     q, kv, kv_raw, rng = _mqa_case(dtype, B, n_q, H, d, N, 0, window, seed=H + N + m)
