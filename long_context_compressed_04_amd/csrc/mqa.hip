@@ -13,20 +13,18 @@
 // Attended items of a query (sparse): its `topk` index slots (-1 masked), then the
 // window tokens max(0, t-w+1) .. t.  Dense: entries 0 .. V(t)-1, then the window.
 //
-// bf16 kernel (head_dim 512): a workgroup = NW waves x 16 heads, one (query, split)
-// unit.  Item tiles of 32 rows are staged in LDS (row-major, padded); each row's
-// 1/rms comes from the same load.  Per wave and tile:
-//   S^T[32 items x 16 heads] = K . q^T   (v_mfma_f32_16x16x32_bf16; A = K rows from
-//                                         LDS, B = normalised q^T held in registers)
-//   online softmax per head column (exp2, fp32)
-//   O^T[512 x 16] += V^T . P^T           (A = V^T via ds_read_b64_tr_b16 from the same
-//                                         row-major tile, B = P^T straight from the
-//                                         S^T registers: the MFMA's k order is chosen
-//                                         to match the rows each lane already holds)
-// RMSNorm is folded: q is normalised (times g^2) before the product, 1/rms of each
-// row scales its logit and its softmax weight, and g multiplies the output.
-// Splits write fp32 partials (unnormalised O, running max, sum) that a second
-// kernel combines in fixed split order (deterministic).
+// bf16 kernels (head_dim 512), chosen by the host:
+//  - mqa_fd_kernel (many queries, unit RMSNorm weight): 4 waves = the 128 heads of a
+//    (query, split) unit, 32 heads x all 512 dims per wave;
+//  - mqa_hg_kernel (few queries, unit weight): 4 waves = one group of 32 heads of a
+//    (query, split) unit, 128 dims per wave, partial logits summed through LDS;
+//  - mqa_bf16_kernel (any RMSNorm weight): NW waves x 16 heads with an online
+//    (running maximum) softmax.
+// All stage 32-row item tiles in LDS (row-major, padded) and form S^T = K . u^T and
+// O^T += V^T . P^T on MFMA.  RMSNorm is folded: q is normalised (times g^2) before
+// the product, 1/rms of each row scales its logit and its softmax weight, and g
+// multiplies the output.  Splits write fp32 partials (unnormalised O, maximum, sum)
+// that a second kernel combines in fixed split order (deterministic).
 #include <type_traits>
 
 #include "csa_device.hpp"
@@ -502,272 +500,26 @@ __global__ __launch_bounds__(NW * 64) void mqa_bf16_kernel(MqaArgs A, MqaLaunch 
 }
 
 // ------------------------------------------------ bf16, 32 heads per wave (MFMA 32x32x16)
-// A workgroup = 4 waves x 32 heads = 128 heads, so every staged row feeds all heads
-// of a 128-head group.  S^T[32 items x 32 heads] and O^T[512 x 32] use
-// v_mfma_f32_32x32x16_bf16, which halves the LDS bytes per flop of the 16-head
-// layout.  Three LDS tile buffers keep two tiles of gathered rows in flight.
+// Per wave and 32-row tile, with the heads as the N side of v_mfma_f32_32x32x16_bf16:
+//   S^T[32 rows x 32 heads] = K . u^T        (A = K rows from LDS, B = normalised q)
+//   O^T[dims x 32 heads]   += V^T . P^T      (A = V^T by ds_read_b64_tr_b16 from the
+//                                             same row-major tile, B = P^T straight
+//                                             from the S^T registers)
 // Softmax without a running maximum: with unit RMSNorm weight every logit obeys
-// |l| <= scale * d (|q_hat|, |k_hat| <= sqrt(d)), so for scale * d * log2(e) <= 100
+// |l| <= scale * d (|u|, |k_hat| <= sqrt(d)), so for scale * d * log2(e) <= 100
 // exp2(l * log2 e) stays a normal float with no overflow (host-checked); weights are
 // exp2 of the logit itself, sums need no rescaling and splits merge by addition.
-constexpr int kRowB2 = kD * 2 + 48;   // LDS row stride: conflict-free b128 and tr16 reads
-constexpr int kNB = 3;                // LDS tile buffers
-
-struct TileCtx32 {
-  uint8_t* tiles;      // [kNB][kTile][kRowB2] LDS
-  float* inv_rms;      // [kNB][kTile] LDS
-  ItemSource src;
-  int it0, it1, wave, lane, h, c32;
-  float sl2, eps;
-};
-
-__device__ __forceinline__ void mqa32_tiles(const TileCtx32& C, const bf16x8_t (&qf)[32], float& l_run,
-                                            f32x16_t (&o)[16]) {
-  constexpr int RPW = kTile / 4;   // rows each wave loads per tile
-  const int lane = C.lane, wave = C.wave, h = C.h, c32 = C.c32;
-  uint32_t okm[kNB] = {0, 0, 0};   // validity of this wave's rows per buffer
-  auto issue = [&](int tb, int buf) {
-    uint32_t ok = 0;
-#pragma unroll
-    for (int rr = 0; rr < RPW; ++rr) {
-      const int r = wave + 4 * rr;
-      const int item = tb + r;
-      const uint8_t* p = (item < C.it1) ? C.src.row(item) : nullptr;
-      ok |= (p != nullptr ? 1u : 0u) << rr;
-      load_row_to_lds((p ? p : g_zero_row) + 16 * lane, C.tiles + buf * (kTile * kRowB2) + r * kRowB2);
-    }
-    return ok;
-  };
-  const int n_tiles = (C.it1 - C.it0 + kTile - 1) / kTile;
-  if (n_tiles > 0) okm[0] = issue(C.it0, 0);
-  if (n_tiles > 1) okm[1] = issue(C.it0 + kTile, 1);
-  for (int ti = 0; ti < n_tiles; ++ti) {
-    const int buf = ti % kNB;
-    uint8_t* const tile = C.tiles + buf * (kTile * kRowB2);
-    float* const irms = C.inv_rms + buf * kTile;
-    // this wave's rows of tile ti have landed (tile ti+1's RPW loads may be in flight;
-    // loads complete in issue order)
-    if (ti + 1 < n_tiles) __builtin_amdgcn_s_waitcnt(0x0F70 | RPW);
-    else __builtin_amdgcn_s_waitcnt(0x0F70);
-    {
-      float part[RPW];
-#pragma unroll
-      for (int rr = 0; rr < RPW; ++rr) {
-        const uint4 v = *(const uint4*)(tile + (wave + 4 * rr) * kRowB2 + 16 * lane);
-        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-        float ss = 0.f;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float lo = __uint_as_float(w4[k] << 16), hi = __uint_as_float(w4[k] & 0xffff0000u);
-          ss = fmaf(lo, lo, fmaf(hi, hi, ss));
-        }
-        part[rr] = ss;
-      }
-      row_totals<RPW>(part, lane, irms, wave, 4, okm[buf], C.eps);
-    }
-    __syncthreads();
-    if (ti + 2 < n_tiles) okm[(ti + 2) % kNB] = issue(C.it0 + (ti + 2) * kTile, (ti + 2) % kNB);
-
-    // ---- S^T = K . u^T: 32 items x 32 heads, 32 k-steps of 16 dims
-    f32x16_t s = {};
-    {
-      const uint8_t* ka = tile + c32 * kRowB2 + 16 * h;
-      constexpr int PF = 4;
-      uint4 a[PF];
-#pragma unroll
-      for (int j = 0; j < PF; ++j) a[j] = *(const uint4*)(ka + 32 * j);
-#pragma unroll
-      for (int ks = 0; ks < 32; ++ks) {
-        const uint4 c = a[ks % PF];
-        if (ks + PF < 32) a[ks % PF] = *(const uint4*)(ka + 32 * (ks + PF));
-        s = mfma32x32x16(as_bf16x8(c), qf[ks], s);
-      }
-    }
-    // ---- softmax weights: this lane's head over items 8*(r/4) + 4*h + r%4
-    float pw[16], psum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float ir = irms[8 * (r / 4) + 4 * h + (r % 4)];
-      const float p = (ir > 0.f) ? exp2f(s[r] * C.sl2 * ir) : 0.f;
-      psum += p;
-      pw[r] = p * ir;   // weight on the raw row (its 1/rms folded in)
-    }
-    l_run += psum;
-    bf16x8_t pb[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-      pb[t] = as_bf16x8(make_uint4(pack_bf16x2(pw[8 * t], pw[8 * t + 1]), pack_bf16x2(pw[8 * t + 2], pw[8 * t + 3]),
-                                   pack_bf16x2(pw[8 * t + 4], pw[8 * t + 5]), pack_bf16x2(pw[8 * t + 6], pw[8 * t + 7])));
-    // ---- O^T += V^T . P^T: 16 dim blocks x 2 k-steps of 16 items.  A lane's V^T
-    // fragment is items 16t + 4h + [0,4) and 16t + 8 + 4h + [0,4) of dim
-    // 32*db + (lane % 32), read with two transposing LDS reads.
-    const int G = lane >> 4, sl = lane & 15;
-    const uint8_t* vb = tile + (4 * h + (sl >> 2)) * kRowB2 + (16 * (G & 1) + 4 * (sl & 3)) * 2;
-    {
-      constexpr int PF = 4;
-      i16x4_t v0[PF], v1[PF];
-      auto vaddr = [&](int k) { return vb + (16 * (k & 1)) * kRowB2 + 64 * (k >> 1); };   // k = 2*db + t
-#pragma unroll
-      for (int j = 0; j < PF; ++j) {
-        v0[j] = lds_read_tr16(vaddr(j));
-        v1[j] = lds_read_tr16(vaddr(j) + 8 * kRowB2);
-      }
-#pragma unroll
-      for (int k = 0; k < 32; ++k) {
-        const i16x4_t c0 = v0[k % PF], c1 = v1[k % PF];
-        if (k + PF < 32) {
-          v0[k % PF] = lds_read_tr16(vaddr(k + PF));
-          v1[k % PF] = lds_read_tr16(vaddr(k + PF) + 8 * kRowB2);
-        }
-        typedef short i16x8_t __attribute__((ext_vector_type(8)));
-        const i16x8_t vv = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-        o[k >> 1] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, vv), pb[k & 1], o[k >> 1]);
-      }
-    }
-  }
-}
-
-__global__ __launch_bounds__(256) void mqa32_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  int32_t* const slot_idx = (int32_t*)(lds + kNB * kTile * kRowB2 + kNB * kTile * sizeof(float));   // [L.ips]
-
-  TileCtx32 C;
-  C.tiles = lds;
-  C.inv_rms = (float*)(lds + kNB * kTile * kRowB2);
-  C.lane = threadIdx.x & 63;
-  C.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  C.h = C.lane >> 5;
-  C.c32 = C.lane & 31;
-  const int h = C.h;
-
-  const int f = blockIdx.x;
-  const int xcd = f & 7, r8 = f >> 3;
-  const int hg = r8 % L.n_hg, ug = r8 / L.n_hg;
-  const int unit = ug * 8 + xcd;
-  if (unit >= L.units) return;
-  const long row = unit / L.nsplit;
-  const int split = unit % L.nsplit;
-  const int b = (int)(row / A.n_q);
-  const int head = hg * 128 + C.wave * 32 + C.c32;
-
-  int total;
-  query_items(A, b, row, 2, C.src, total);
-  C.it0 = split * L.ips;
-  C.it1 = min(total, C.it0 + L.ips);
-  if (C.src.idx && L.slots) {
-    for (int i = threadIdx.x; i < L.ips; i += 256) {
-      const int it = C.it0 + i;
-      slot_idx[i] = (it < min(C.it1, C.src.n_first)) ? C.src.idx[it] : -1;
-    }
-    C.src.idx = slot_idx;
-    C.src.idx_off = C.it0;
-  }
-  __syncthreads();
-
-  // ---- u = q * g^2 / rms(q): B operands, dims 16*ks + 8*h + [0, 8)
-  bf16x8_t qf[32];
-  {
-    const uint16_t* qrow = (const uint16_t*)A.q + (row * A.heads + head) * kD;
-    // two passes over the (L2-resident) query row keep register use low: the sum of
-    // squares first, then the scaled bf16 operands
-    float ss = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < 32; ++ks) {
-      const uint4 v = *(const uint4*)(qrow + 16 * ks + 8 * h);
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float lo = __uint_as_float(w4[k] << 16), hi = __uint_as_float(w4[k] & 0xffff0000u);
-        ss = fmaf(lo, lo, fmaf(hi, hi, ss));
-      }
-    }
-    ss += __shfl_xor(ss, 32, 64);
-    const float qinv = 1.f / sqrtf(ss * (1.f / kD) + A.eps);
-#pragma unroll
-    for (int ks = 0; ks < 32; ++ks) {
-      const uint4 v = *(const uint4*)(qrow + 16 * ks + 8 * h);
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-      uint32_t o4[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        o4[k] = pack_bf16x2(__uint_as_float(w4[k] << 16) * qinv, __uint_as_float(w4[k] & 0xffff0000u) * qinv);
-      qf[ks] = as_bf16x8(make_uint4(o4[0], o4[1], o4[2], o4[3]));
-    }
-  }
-  C.sl2 = A.scale * kLog2e;
-  C.eps = A.eps;
-  float l_run = 0.f;
-  const float m_run = 0.f;
-  f32x16_t o[16];
-#pragma unroll
-  for (int db = 0; db < 16; ++db) o[db] = f32x16_t{};
-  mqa32_tiles(C, qf, l_run, o);
-
-  l_run += __shfl_xor(l_run, 32, 64);
-  // o[db][r] holds dim 32*db + 8*(r/4) + 4*h + r%4 of this lane's head
-  if (L.nsplit == 1) {
-    const float inv_l = l_run > 0.f ? 1.f / l_run : 0.f;
-    uint16_t* orow = (uint16_t*)A.out + (row * A.heads + head) * kD;
-#pragma unroll
-    for (int db = 0; db < 16; ++db)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d0 = 32 * db + 8 * j + 4 * h;
-        float v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = o[db][4 * j + r] * inv_l;
-        *(uint2*)(orow + d0) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-      }
-    if (A.lse && h == 0) A.lse[row * A.heads + head] = l_run > 0.f ? m_run * kLn2 + logf(l_run) : -INFINITY;
-  } else {
-    float* po = part_o + (((long)row * L.nsplit + split) * A.heads + head) * kD;
-#pragma unroll
-    for (int db = 0; db < 16; ++db)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *(f32x4_t*)(po + 32 * db + 8 * j + 4 * h) =
-            f32x4_t{o[db][4 * j], o[db][4 * j + 1], o[db][4 * j + 2], o[db][4 * j + 3]};
-    if (h == 0) {
-      float* pm = part_ml + (((long)row * L.nsplit + split) * A.heads + head) * 2;
-      pm[0] = l_run > 0.f ? m_run : -INFINITY;
-      pm[1] = l_run;
-    }
-  }
-}
-
-// ------------------------- bf16, 32 heads x 256 dims per wave (MFMA 32x32x16, dim-split)
-// A workgroup = 8 waves = 4 head groups of 32 heads x 2 halves of the head dim.  Both
-// waves of a pair take the logits of their half of the dims, swap them through LDS
-// and add them, so each holds the same full S^T; each then accumulates O^T for its
-// own 256 dims only.  This halves the registers a wave needs (O^T 128, q 64), which
-// lets two waves share each SIMD and hide each other's LDS and VALU latency.
 //
 // Gathered rows land in LDS by direct-to-LDS loads, two tiles ahead.  The three tile
-// buffers are separate static LDS objects and the pipeline is unrolled by three, so
+// buffers are separate static LDS objects and each tile loop is unrolled by three, so
 // the compiler can see that reads of one buffer never alias the loads still landing
 // in another (one shared array would force a wait for every load before any LDS
 // read); the barriers are plain s_barrier with explicit LDS waits for the same reason.
-constexpr int kXS = 16;             // logits per lane exchanged within a wave pair
+constexpr int kRowB2 = kD * 2 + 48;   // LDS row stride: conflict-free b128 and tr16 reads
+constexpr int kNB = 3;                // LDS tile buffers
+constexpr int kXS = 16;             // logits per lane exchanged between waves
 constexpr int kStageRow = 128 + 4;  // fp32 words per head row of the output staging (padded)
 constexpr int kSlotsLds = 2048;     // index slots of a split held in LDS
-
-__device__ __forceinline__ float rows_total4(const float (&p)[4], int lane) {
-  bool up = (lane & 32) != 0;
-  float a[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const float send = up ? p[j] : p[2 + j];
-    const float keep = up ? p[2 + j] : p[j];
-    a[j] = keep + __shfl_xor(send, 32, 64);
-  }
-  up = (lane & 16) != 0;
-  float s = (up ? a[1] : a[0]) + __shfl_xor(up ? a[0] : a[1], 16, 64);
-  s += __shfl_xor(s, 8, 64);
-  s += __shfl_xor(s, 4, 64);
-  s += __shfl_xor(s, 2, 64);
-  s += __shfl_xor(s, 1, 64);
-  return s;   // total of row 2*(lane>>5 & 1) + (lane>>4 & 1)
-}
 
 // Barrier without a memory fence: waits only for this wave's LDS operations, so
 // direct-to-LDS loads of later tiles stay in flight across it (a workgroup fence
@@ -780,14 +532,13 @@ __device__ __forceinline__ void lds_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// Sum of squares of 8 bf16 values added to acc (four v_dot2_f32_bf16).
+// Sum of squares of 8 bf16 values added to acc (exact fp32 widening, full-rate FMAs).
 __device__ __forceinline__ float sumsq_bf16x8(uint4 v, float acc) {
-  typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
   const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const bf16x2_v b = __builtin_bit_cast(bf16x2_v, w4[k]);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(b, b, acc, false);
+    const float lo = __uint_as_float(w4[k] << 16), hi = __uint_as_float(w4[k] & 0xffff0000u);
+    acc = fmaf(lo, lo, fmaf(hi, hi, acc));
   }
   return acc;
 }
@@ -818,262 +569,6 @@ struct RowSrc {
   const int32_t* gidx;   // global index slots (sparse, when not copied to LDS)
   int it0, it1, n_first, kv_rows, win_lo, raw_base, raw_cap, use_slots, dense;
 };
-
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void mqa32d_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml) {
-  __shared__ __attribute__((aligned(16))) uint8_t tb0[kTile * kRowB2];
-  __shared__ __attribute__((aligned(16))) uint8_t tb1[kTile * kRowB2];
-  __shared__ __attribute__((aligned(16))) uint8_t tb2[kTile * kRowB2];
-  __shared__ uint32_t okw[kNB][8];        // per buffer: which of each wave's rows exist
-  __shared__ float xbuf[8][kXS + 1][64];  // partial S^T, then the partial row sum of squares
-  __shared__ int32_t slot[kSlotsLds];
-  __shared__ float qss[8][64];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int h = lane >> 5, c32 = lane & 31, dh = wave & 1;
-
-  const int f = blockIdx.x;
-  const int xcd = f & 7, r8 = f >> 3;
-  const int hg = r8 % L.n_hg, ug = r8 / L.n_hg;
-  const int unit = ug * 8 + xcd;
-  if (unit >= L.units) return;
-  const long row = unit / L.nsplit;
-  const int split = unit % L.nsplit;
-  const int b = (int)(row / A.n_q);
-  const int head = hg * 128 + (wave >> 1) * 32 + c32;
-
-  // ---- this wave's half of the query row first (it depends on nothing else)
-  const uint16_t* qrow = (const uint16_t*)A.q + (row * A.heads + head) * kD + 256 * dh;
-  uint4 qraw[16];
-#pragma unroll
-  for (int ks = 0; ks < 16; ++ks) qraw[ks] = *(const uint4*)(qrow + 16 * ks + 8 * h);
-
-  // ---- the items of this (query, split)
-  RowSrc R;
-  {
-    ItemSource src;
-    int total;
-    query_items(A, b, row, 2, src, total);
-    R.kv = src.kv; R.raw = src.raw; R.n_first = src.n_first; R.kv_rows = src.kv_rows; R.win_lo = src.win_lo;
-    R.raw_base = src.raw_base; R.raw_cap = src.raw_cap; R.dense = A.dense;
-    R.it0 = split * L.ips;
-    R.it1 = min(total, R.it0 + L.ips);
-    R.gidx = src.idx;
-    R.use_slots = !A.dense;   // the host routes splits longer than kSlotsLds elsewhere
-    if (R.use_slots)
-      for (int i = threadIdx.x; i < L.ips; i += 512) {
-        const int it = R.it0 + i;
-        slot[i] = (it < min(R.it1, R.n_first)) ? src.idx[it] : -1;
-      }
-  }
-  auto resolve = [&](int item) -> const uint8_t* {
-    if (item >= R.it1) return nullptr;
-    if (item < R.n_first) {
-      const int e = R.dense ? item : slot[item - R.it0];
-      return (e >= 0 && e < R.kv_rows) ? R.kv + (long)e * (kD * 2) : nullptr;
-    }
-    const int r = R.win_lo + (item - R.n_first) - R.raw_base;
-    return (r >= 0 && r < R.raw_cap) ? R.raw + (long)r * (kD * 2) : nullptr;
-  };
-
-  // ---- u = q / rms(q) for this wave's dims 256*dh + 16*ks + 8*h + [0, 8); the pair
-  // swaps half-row sums of squares
-  bf16x8_t qf[16];
-  {
-    float ss = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      const uint32_t w4[4] = {qraw[ks].x, qraw[ks].y, qraw[ks].z, qraw[ks].w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float lo = __uint_as_float(w4[k] << 16), hi = __uint_as_float(w4[k] & 0xffff0000u);
-        ss = fmaf(lo, lo, fmaf(hi, hi, ss));
-      }
-    }
-    ss += __shfl_xor(ss, 32, 64);
-    qss[wave][lane] = ss;
-    __syncthreads();   // also publishes the index slots
-    ss += qss[wave ^ 1][lane];
-    const float qinv = 1.f / sqrtf(ss * (1.f / kD) + A.eps);
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      const uint32_t w4[4] = {qraw[ks].x, qraw[ks].y, qraw[ks].z, qraw[ks].w};
-      uint32_t o4[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        o4[k] = pack_bf16x2(__uint_as_float(w4[k] << 16) * qinv, __uint_as_float(w4[k] & 0xffff0000u) * qinv);
-      qf[ks] = as_bf16x8(make_uint4(o4[0], o4[1], o4[2], o4[3]));
-    }
-  }
-  const float sl2 = A.scale * kLog2e;
-  const float eps = A.eps;
-  float l_run = 0.f;
-  f32x16_t o[8];
-#pragma unroll
-  for (int db = 0; db < 8; ++db) o[db] = f32x16_t{};
-
-  constexpr int RPW = kTile / 8;   // rows each wave loads per tile
-  const int n_tiles = (R.it1 - R.it0 + kTile - 1) / kTile;
-  uint32_t okm[kNB] = {0, 0, 0};
-  auto buf_ptr = [&](int bi) -> uint8_t* { return bi == 0 ? tb0 : (bi == 1 ? tb1 : tb2); };
-  // Few distinct load instructions (the rows are a rolled loop): the compiler can
-  // track only a handful of in-flight direct-to-LDS loads individually before it
-  // falls back to waiting for all of them at every LDS access.
-  auto issue = [&](int ti, uint8_t* dst) -> uint32_t {
-    return issue_rows<RPW, 8>(resolve, R.it0 + ti * kTile + wave, lane, dst + wave * kRowB2);
-  };
-  if (n_tiles > 0) okm[0] = issue(0, tb0);
-  if (n_tiles > 1) okm[1] = issue(1, tb1);
-
-  const int G = lane >> 4, sl = lane & 15;
-  const int vb_off = (4 * h + (sl >> 2)) * kRowB2 + 512 * dh + (16 * (G & 1) + 4 * (sl & 3)) * 2;
-  const int ka_off = c32 * kRowB2 + 512 * dh + 16 * h;
-
-  auto step = [&](auto BUFC, int ti) {
-    constexpr int BUF = decltype(BUFC)::value;
-    uint8_t* const tile = BUF == 0 ? tb0 : (BUF == 1 ? tb1 : tb2);
-    // this wave's rows of tile ti have landed (tile ti+1's loads may still be in
-    // flight; loads complete in issue order)
-    if (ti + 1 < n_tiles) __builtin_amdgcn_s_waitcnt(0x0F70 | RPW);
-    else __builtin_amdgcn_s_waitcnt(0x0F70);
-    if (lane == 0) okw[BUF][wave] = okm[BUF];
-    lds_barrier();
-    if (ti + 2 < n_tiles) okm[(BUF + 2) % kNB] = issue(ti + 2, buf_ptr((BUF + 2) % kNB));
-
-    // ---- partial S^T over this wave's 256 dims: 16 k-steps of 16
-    f32x16_t s;
-    float ssr = 0.f;
-    {
-      const uint8_t* ka = tile + ka_off;
-      constexpr int PF = 2;
-      uint4 a[PF];
-#pragma unroll
-      for (int j = 0; j < PF; ++j) a[j] = *(const uint4*)(ka + 32 * j);
-      f32x16_t s2[2] = {f32x16_t{}, f32x16_t{}};   // two chains of dependent MFMAs
-#pragma unroll
-      for (int ks = 0; ks < 16; ++ks) {
-        const uint4 c = a[ks % PF];
-        if (ks + PF < 16) a[ks % PF] = *(const uint4*)(ka + 32 * (ks + PF));
-        s2[ks & 1] = mfma32x32x16(as_bf16x8(c), qf[ks], s2[ks & 1]);
-        // row c32's sum of squares over the same operand (dims 16 ks + 8 h + [0, 8))
-        ssr = sumsq_bf16x8(c, ssr);
-        // keep this order: consuming the operand loaded PF steps ago, not the one
-        // just requested, keeps PF LDS reads in flight
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      s = s2[0] + s2[1];
-    }
-    // ---- full S^T = own half + partner's half (the same sum in both waves)
-    ssr += __shfl_xor(ssr, 32, 64);   // this wave's 256 dims of row c32
-#pragma unroll
-    for (int r = 0; r < kXS; ++r) xbuf[wave][r][lane] = s[r];
-    xbuf[wave][kXS][lane] = ssr;
-    lds_barrier();
-    // ---- softmax weights: this lane's head over items 8*(r/4) + 4*h + r%4.  LDS
-    // operands first, then branch-free weights (a masked row has inv_rms 0 and
-    // weight 0).  Exponents lie in [-100, 100]: the hardware exp2 is never denormal.
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] += xbuf[wave ^ 1][r][lane];
-    // 1/rms of row c32 (0 for a row that does not exist); the rows of this lane's
-    // logits, 8 (r/4) + 4 h + r%4, are read from the lanes holding them
-    const float ss = ssr + xbuf[wave ^ 1][kXS][lane];
-    const bool row_ok = (okw[BUF][c32 & 7] >> (c32 >> 3)) & 1u;
-    const float inv = row_ok ? 1.f / sqrtf(ss * (1.f / kD) + eps) : 0.f;
-    float psum = 0.f;
-    uint32_t pk[8];
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      float p2[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const float ir = __shfl(inv, 8 * ((r + u) / 4) + 4 * h + ((r + u) % 4), 64);
-        const float e = __builtin_amdgcn_exp2f(s[r + u] * sl2 * ir);
-        const float p = ir > 0.f ? e : 0.f;
-        psum += p;
-        p2[u] = p * ir;   // weight on the raw row (its 1/rms folded in)
-      }
-      pk[r / 2] = pack_bf16x2(p2[0], p2[1]);
-    }
-    l_run += psum;
-    const bf16x8_t pb0 = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
-    const bf16x8_t pb1 = as_bf16x8(make_uint4(pk[4], pk[5], pk[6], pk[7]));
-    // ---- O^T += V^T . P^T over this wave's 8 dim blocks (V^T by transposing reads)
-    const uint8_t* vb = tile + vb_off;
-    constexpr int PF = 2;
-    i16x4_t v0[PF], v1[PF];
-    auto vaddr = [&](int k) { return vb + (16 * (k & 1)) * kRowB2 + 64 * (k >> 1); };   // k = 2*db + t
-#pragma unroll
-    for (int j = 0; j < PF; ++j) {
-      v0[j] = lds_read_tr16(vaddr(j));
-      v1[j] = lds_read_tr16(vaddr(j) + 8 * kRowB2);
-    }
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const i16x4_t c0 = v0[k % PF], c1 = v1[k % PF];
-      if (k + PF < 16) {
-        v0[k % PF] = lds_read_tr16(vaddr(k + PF));
-        v1[k % PF] = lds_read_tr16(vaddr(k + PF) + 8 * kRowB2);
-      }
-      typedef short i16x8_t __attribute__((ext_vector_type(8)));
-      const i16x8_t vv = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-      o[k >> 1] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, vv), (k & 1) ? pb1 : pb0, o[k >> 1]);
-    }
-  };
-  for (int ti = 0; ti < n_tiles; ti += kNB) {
-    step(std::integral_constant<int, 0>{}, ti);
-    if (ti + 1 < n_tiles) step(std::integral_constant<int, 1>{}, ti + 1);
-    if (ti + 2 < n_tiles) step(std::integral_constant<int, 2>{}, ti + 2);
-  }
-
-  l_run += __shfl_xor(l_run, 32, 64);
-  // o[db][r] holds dim 256 dh + 32 db + 8 (r/4) + 4 h + r%4 of this lane's head.  The
-  // 32 x 256 block leaves through LDS in two 128-dim halves (the tile buffers and the
-  // exchange buffer are free once every wave is past its last tile), so that each
-  // store instruction writes two whole head rows.
-  lds_barrier();
-  float* stage = (float*)((wave < 2 ? tb0 : (wave < 4 ? tb1 : (wave < 6 ? tb2 : (uint8_t*)&xbuf[0][0][0]))) +
-                          (wave & 1) * (32 * kStageRow * 4));
-  const int hl = lane >> 5, d4 = lane & 31;
-  const float inv_l = l_run > 0.f ? 1.f / l_run : 0.f;   // l of lane c32's head
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x16_t& od = o[4 * half + db];
-        *(f32x4_t*)(stage + c32 * kStageRow + 32 * db + 8 * j + 4 * h) =
-            f32x4_t{od[4 * j], od[4 * j + 1], od[4 * j + 2], od[4 * j + 3]};
-      }
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // (a wave-private region: no barrier)
-    const int dim0 = 256 * dh + 128 * half + 4 * d4;
-    if (L.nsplit == 1) {
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int hh = 2 * k + hl;
-        const float il = __shfl(inv_l, hh, 64);
-        const f32x4_t v = *(const f32x4_t*)(stage + hh * kStageRow + 4 * d4);
-        uint16_t* orow = (uint16_t*)A.out + (row * A.heads + hg * 128 + (wave >> 1) * 32 + hh) * kD + dim0;
-        *(uint2*)orow = make_uint2(pack_bf16x2(v[0] * il, v[1] * il), pack_bf16x2(v[2] * il, v[3] * il));
-      }
-    } else {
-      float* po = part_o + (((long)row * L.nsplit + split) * A.heads + hg * 128 + (wave >> 1) * 32) * kD + dim0;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int hh = 2 * k + hl;
-        *(f32x4_t*)(po + (long)hh * kD) = *(const f32x4_t*)(stage + hh * kStageRow + 4 * d4);
-      }
-    }
-  }
-  if (L.nsplit == 1) {
-    if (A.lse && h == 0 && dh == 0) A.lse[row * A.heads + head] = l_run > 0.f ? logf(l_run) : -INFINITY;
-  } else if (h == 0 && dh == 0) {
-    float* pm = part_ml + (((long)row * L.nsplit + split) * A.heads + head) * 2;
-    pm[0] = l_run > 0.f ? 0.f : -INFINITY;
-    pm[1] = l_run;
-  }
-}
 
 // ---------------------------------------------------------------------------------
 // Head-group kernel for few queries (decode): a workgroup = 4 waves = one group of
@@ -1324,6 +819,292 @@ void mqa_hg_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml) {
   }
 }
 
+// ---------------------------------------------------------------------------------
+// Full-dim kernel for many queries (prefill): a workgroup = 4 waves = the 128 heads
+// of one (query, split) unit, wave w owning heads 32 w .. 32 w + 31 over all 512
+// dims (one wave per SIMD: q in 128 registers, O^T in 256 accumulators).  No
+// partial-logit exchange between waves: one barrier per tile (the rows every wave
+// gathered have landed, and the buffer two tiles ahead is free).
+//
+// Gathered rows are row-major in LDS (kRowB2 bytes apart); each wave gathers 8 rows
+// of the tile two ahead right after the tile barrier.  The 1/rms of every row comes
+// from a pre-pass
+// over the whole cache (row_inv_rms_kernel): a compressed entry is normalised once,
+// not once per query that selects it.
+constexpr int kFdWaves = 4;
+constexpr int kFdRpw = kTile / kFdWaves;
+
+__device__ float g_zero_f32;   // 1/rms of a missing row: weight 0
+
+// One wave per row: 1/rms of every row of kv (all kv_cap rows of every sequence) and
+// kv_raw, written to inv_kv [batch, kv_cap] and inv_raw [batch, raw_cap].
+__global__ __launch_bounds__(256) void row_inv_rms_kernel(MqaArgs A, float* inv_kv, float* inv_raw) {
+  const long gw = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const long n_kv = (long)A.batch * A.kv_cap, n_raw = (long)A.batch * A.raw_cap;
+  if (gw >= n_kv + n_raw) return;
+  const uint8_t* rowp = gw < n_kv ? (const uint8_t*)A.kv + gw * (kD * 2)
+                                  : (const uint8_t*)A.kv_raw + (gw - n_kv) * (kD * 2);
+  const float ss = wave_sum(sumsq_bf16x8(*(const uint4*)(rowp + 16 * lane), 0.f));
+  if (lane == 0) {
+    const float r = 1.f / sqrtf(ss * (1.f / kD) + A.eps);
+    if (gw < n_kv) inv_kv[gw] = r;
+    else inv_raw[gw - n_kv] = r;
+  }
+}
+
+__global__ __launch_bounds__(kFdWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mqa_fd_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml, const float* inv_kv,
+                   const float* inv_raw) {
+  __shared__ __attribute__((aligned(16))) uint8_t tb0[kTile * kRowB2];
+  __shared__ __attribute__((aligned(16))) uint8_t tb1[kTile * kRowB2];
+  __shared__ __attribute__((aligned(16))) uint8_t tb2[kTile * kRowB2];
+  __shared__ __attribute__((aligned(16))) float irms[kNB][kTile];
+  __shared__ int32_t slot[kSlotsLds];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane >> 5, c32 = lane & 31;
+
+  const int f = blockIdx.x;
+  const int xcd = f & 7, r8 = f >> 3;
+  const int hg = r8 % L.n_hg, ug = r8 / L.n_hg;
+  const int unit = ug * 8 + xcd;
+  if (unit >= L.units) return;
+  const long row = unit / L.nsplit;
+  const int split = unit % L.nsplit;
+  const int b = (int)(row / A.n_q);
+  const int head = hg * 128 + wave * 32 + c32;
+
+  RowSrc R;
+  {
+    ItemSource src;
+    int total;
+    query_items(A, b, row, 2, src, total);
+    R.kv = src.kv; R.raw = src.raw; R.n_first = src.n_first; R.kv_rows = src.kv_rows; R.win_lo = src.win_lo;
+    R.raw_base = src.raw_base; R.raw_cap = src.raw_cap; R.dense = A.dense;
+    R.it0 = split * L.ips;
+    R.it1 = min(total, R.it0 + L.ips);
+    R.gidx = src.idx;
+    R.use_slots = !A.dense;
+    if (R.use_slots)
+      for (int i = threadIdx.x; i < L.ips; i += kFdWaves * 64) {
+        const int it = R.it0 + i;
+        slot[i] = (it < min(R.it1, R.n_first)) ? src.idx[it] : -1;
+      }
+  }
+  const float* inv_kv_b = inv_kv + (long)b * A.kv_cap;
+  const float* inv_raw_b = inv_raw + (long)b * A.raw_cap;
+  // the query row of this lane's head: dims 16 ks + 8 h + [0, 8), ks = 0..31
+  const uint16_t* qrow = (const uint16_t*)A.q + (row * A.heads + head) * kD;
+  uint4 qraw[32];
+#pragma unroll
+  for (int ks = 0; ks < 32; ++ks) qraw[ks] = *(const uint4*)(qrow + 16 * ks + 8 * h);
+  lds_barrier();   // the slots are in LDS (each store waited for its load)
+
+  const int n_tiles = (R.it1 - R.it0 + kTile - 1) / kTile;
+  // Tile row item -> source row (nullptr: masked) and its 1/rms (the zero float for a
+  // masked row, whose weight is then 0).
+  auto resolve = [&](int item, const float*& ip) -> const uint8_t* {
+    ip = &g_zero_f32;
+    if (item >= R.it1) return nullptr;
+    if (item < R.n_first) {
+      const int e = R.dense ? item : slot[item - R.it0];
+      if (e < 0 || e >= R.kv_rows) return nullptr;
+      ip = inv_kv_b + e;
+      return R.kv + (long)e * (kD * 2);
+    }
+    const int r = R.win_lo + (item - R.n_first) - R.raw_base;
+    if (r < 0 || r >= R.raw_cap) return nullptr;
+    ip = inv_raw_b + r;
+    return R.raw + (long)r * (kD * 2);
+  };
+  // Gathers tile ti: wave 0 first brings the 32 rows' 1/rms into LDS (lane l: row l),
+  // then every wave its 8 rows (lane rr resolves row wave + 4 rr; a rolled loop of one
+  // direct-to-LDS instruction, which the compiler tracks without extra waits).  Wave 0
+  // issues 9 loads per tile, the others 8.
+  auto issue = [&](int ti, uint8_t* dst, float* irms_dst) {
+    const int item0 = R.it0 + ti * kTile;
+    const float* ip;
+    if (wave == 0) {
+      resolve(item0 + c32, ip);
+      if (h == 0)
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)ip,
+                                         (__attribute__((address_space(3))) void*)irms_dst, 4, 0, 0);
+    }
+    const uint8_t* pl = resolve(item0 + wave + kFdWaves * (lane & (kFdRpw - 1)), ip);
+    const uint64_t pv = (uint64_t)(pl ? pl : g_zero_row);
+    const uint32_t lo = (uint32_t)pv, hi = (uint32_t)(pv >> 32);
+#pragma unroll 1
+    for (int rr = 0; rr < kFdRpw; ++rr) {
+      const uint64_t p = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, rr) << 32) |
+                         (uint32_t)__builtin_amdgcn_readlane((int)lo, rr);
+      load_row_to_lds((const uint8_t*)p + 16 * lane, dst + (wave + kFdWaves * rr) * kRowB2);
+    }
+  };
+  auto buf_ptr = [&](int bi) -> uint8_t* { return bi == 0 ? tb0 : (bi == 1 ? tb1 : tb2); };
+  if (n_tiles > 0) issue(0, tb0, irms[0]);
+  if (n_tiles > 1) issue(1, tb1, irms[1]);
+
+  // ---- u = q / rms(q), all within the wave (the two lanes of a head hold its halves)
+  bf16x8_t qf[32];
+  {
+    float ss = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 32; ++ks) ss = sumsq_bf16x8(qraw[ks], ss);
+    ss += __shfl_xor(ss, 32, 64);
+    const float qinv = 1.f / sqrtf(ss * (1.f / kD) + A.eps);
+#pragma unroll
+    for (int ks = 0; ks < 32; ++ks) {
+      const uint32_t w4[4] = {qraw[ks].x, qraw[ks].y, qraw[ks].z, qraw[ks].w};
+      uint32_t o4[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        o4[k] = pack_bf16x2(__uint_as_float(w4[k] << 16) * qinv, __uint_as_float(w4[k] & 0xffff0000u) * qinv);
+      qf[ks] = as_bf16x8(make_uint4(o4[0], o4[1], o4[2], o4[3]));
+    }
+  }
+  const float sl2 = A.scale * kLog2e;
+  float l_run = 0.f;
+  f32x16_t o[16];
+#pragma unroll
+  for (int db = 0; db < 16; ++db) o[db] = f32x16_t{};
+
+  const int G = lane >> 4, sl = lane & 15;
+  const int ka_base = c32 * kRowB2 + 16 * h;   // K: row c32, dims 16 ks + 8 h
+  const int vb_base = (4 * h + (sl >> 2)) * kRowB2 + (16 * (G & 1) + 4 * (sl & 3)) * 2;
+  auto ka_off = [](int ks) { return 32 * ks; };
+  auto vb_off = [](int k) { return (16 * (k & 1)) * kRowB2 + 64 * (k >> 1); };   // k = 2 db + t
+
+  auto step = [&](auto BUFC, int ti) {
+    constexpr int BUF = decltype(BUFC)::value;
+    uint8_t* const tile = BUF == 0 ? tb0 : (BUF == 1 ? tb1 : tb2);
+    // this wave's loads of tile ti are done (tile ti+1's may still be in flight)
+    if (ti + 1 < n_tiles) {
+      if (wave == 0) __builtin_amdgcn_s_waitcnt(0x0F70 | (kFdRpw + 1));
+      else __builtin_amdgcn_s_waitcnt(0x0F70 | kFdRpw);
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+    }
+    // every wave's rows (and the row norms) of tile ti have landed; every wave is
+    // past tile ti-1
+    lds_barrier();
+    if (ti + 2 < n_tiles) issue(ti + 2, buf_ptr((BUF + 2) % kNB), irms[(BUF + 2) % kNB]);
+    // rows of this lane's logits: 8 (r/4) + 4 h + [0, 4), four aligned quads
+    f32x4_t irq[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) irq[g] = *(const f32x4_t*)&irms[BUF][8 * g + 4 * h];
+    // ---- S^T over all 512 dims: 32 k-steps of 16
+    f32x16_t s;
+    {
+      const uint8_t* ka = tile + ka_base;
+      constexpr int PF = 8;
+      uint4 a[PF];
+#pragma unroll
+      for (int j = 0; j < PF; ++j) a[j] = *(const uint4*)(ka + ka_off(j));
+      f32x16_t s2[2] = {f32x16_t{}, f32x16_t{}};
+#pragma unroll
+      for (int ks = 0; ks < 32; ++ks) {
+        const uint4 c = a[ks % PF];
+        if (ks + PF < 32) a[ks % PF] = *(const uint4*)(ka + ka_off(ks + PF));
+        s2[ks & 1] = mfma32x32x16(as_bf16x8(c), qf[ks], s2[ks & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      s = s2[0] + s2[1];
+    }
+    // ---- softmax weights (exponents within [-100, 100]; a missing row has weight 0)
+    float psum = 0.f;
+    uint32_t pk[8];
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      float p2[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const float ir = irq[(r + u) / 4][(r + u) % 4];
+        const float e = __builtin_amdgcn_exp2f(s[r + u] * sl2 * ir);
+        const float p = ir > 0.f ? e : 0.f;
+        psum += p;
+        p2[u] = p * ir;
+      }
+      pk[r / 2] = pack_bf16x2(p2[0], p2[1]);
+    }
+    l_run += psum;
+    const bf16x8_t pb0 = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
+    const bf16x8_t pb1 = as_bf16x8(make_uint4(pk[4], pk[5], pk[6], pk[7]));
+    // ---- O^T += V^T . P^T over the 16 dim blocks
+    const uint8_t* vb = tile + vb_base;
+    constexpr int PV = 4;
+    i16x4_t v0[PV], v1[PV];
+#pragma unroll
+    for (int j = 0; j < PV; ++j) {
+      v0[j] = lds_read_tr16(vb + vb_off(j));
+      v1[j] = lds_read_tr16(vb + vb_off(j) + 8 * kRowB2);
+    }
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const i16x4_t c0 = v0[k % PV], c1 = v1[k % PV];
+      if (k + PV < 32) {
+        v0[k % PV] = lds_read_tr16(vb + vb_off(k + PV));
+        v1[k % PV] = lds_read_tr16(vb + vb_off(k + PV) + 8 * kRowB2);
+      }
+      typedef short i16x8_t __attribute__((ext_vector_type(8)));
+      const i16x8_t vv = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+      o[k >> 1] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, vv), (k & 1) ? pb1 : pb0, o[k >> 1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  for (int ti = 0; ti < n_tiles; ti += kNB) {
+    step(std::integral_constant<int, 0>{}, ti);
+    if (ti + 1 < n_tiles) step(std::integral_constant<int, 1>{}, ti + 1);
+    if (ti + 2 < n_tiles) step(std::integral_constant<int, 2>{}, ti + 2);
+  }
+
+  l_run += __shfl_xor(l_run, 32, 64);
+  // o[db][r] holds dim 32 db + 8 (r/4) + 4 h + r%4 of this lane's head; out through
+  // LDS in four 128-dim quarters (each wave its own region of the free tile buffers)
+  lds_barrier();
+  float* stage = (float*)((wave < 2 ? tb0 : tb1) + (wave & 1) * (32 * kStageRow * 4));
+  const int hl = lane >> 5, d4 = lane & 31;
+  const float inv_l = l_run > 0.f ? 1.f / l_run : 0.f;
+#pragma unroll
+  for (int qtr = 0; qtr < 4; ++qtr) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x16_t& od = o[4 * qtr + db];
+        *(f32x4_t*)(stage + c32 * kStageRow + 32 * db + 8 * j + 4 * h) =
+            f32x4_t{od[4 * j], od[4 * j + 1], od[4 * j + 2], od[4 * j + 3]};
+      }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    const int dim0 = 128 * qtr + 4 * d4;
+    if (L.nsplit == 1) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int hh = 2 * k + hl;
+        const float il = __shfl(inv_l, hh, 64);
+        const f32x4_t v = *(const f32x4_t*)(stage + hh * kStageRow + 4 * d4);
+        uint16_t* orow = (uint16_t*)A.out + (row * A.heads + hg * 128 + wave * 32 + hh) * kD + dim0;
+        *(uint2*)orow = make_uint2(pack_bf16x2(v[0] * il, v[1] * il), pack_bf16x2(v[2] * il, v[3] * il));
+      }
+    } else {
+      float* po = part_o + (((long)row * L.nsplit + split) * A.heads + hg * 128 + wave * 32) * kD + dim0;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int hh = 2 * k + hl;
+        *(f32x4_t*)(po + (long)hh * kD) = *(const f32x4_t*)(stage + hh * kStageRow + 4 * d4);
+      }
+    }
+  }
+  if (L.nsplit == 1) {
+    if (A.lse && h == 0) A.lse[row * A.heads + head] = l_run > 0.f ? logf(l_run) : -INFINITY;
+  } else if (h == 0) {
+    float* pm = part_ml + (((long)row * L.nsplit + split) * A.heads + head) * 2;
+    pm[0] = l_run > 0.f ? 0.f : -INFINITY;
+    pm[1] = l_run;
+  }
+}
+
 // Fixed-order merge of split partials: out = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
 constexpr int kMaxSplit = 128;
 
@@ -1386,9 +1167,9 @@ static MqaLaunch plan_mqa(const MqaArgs& A) {
     // works through, rounds of <= 256 workgroups (one per CU), the fp32 partials each
     // (query, head group, split) writes and the merge reads, and the merge launch.
     const bool hg = L.kind == 2;
-    L.nw = hg ? kHgWaves : 8;
+    L.nw = hg ? kHgWaves : kFdWaves;
     L.n_hg = A.heads / (hg ? 32 : 128);
-    const double t_tile = hg ? 0.6 : 2.9, t_part = hg ? 0.03 : 0.06, t_merge = hg ? 4.0 : 6.0;
+    const double t_tile = hg ? 2.6 : 1.5, t_part = hg ? 0.033 : 0.06, t_merge = 5.0;
     double best = 1e30;
     int best_s = 1;
     for (int sp = 1; sp <= kMaxSplit && sp <= tiles_max; ++sp) {
@@ -1437,10 +1218,18 @@ static size_t mqa_lds_bytes(const MqaLaunch& L) {
   return (size_t)2 * kTile * kRowB + 2 * kTile * sizeof(float) + kD * sizeof(float) + slots;
 }
 
+static size_t r256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 static size_t partial_bytes(const MqaArgs& A, const MqaLaunch& L) {
   if (L.nsplit == 1) return 0;
   const size_t parts = (size_t)A.batch * A.n_q * L.nsplit * A.heads;
-  return parts * kD * sizeof(float) + parts * 2 * sizeof(float);
+  return r256(parts * kD * sizeof(float) + parts * 2 * sizeof(float));
+}
+
+// Row norms of the full-dim kernel: [batch, kv_cap] then [batch, raw_cap] fp32.
+static size_t norm_bytes(const MqaArgs& A, const MqaLaunch& L) {
+  if (L.kind != 1) return 0;
+  return r256((size_t)A.batch * A.kv_cap * sizeof(float)) + r256((size_t)A.batch * A.raw_cap * sizeof(float));
 }
 
 // The plan depends on whether a norm weight is given, which the size query does not
@@ -1449,10 +1238,12 @@ size_t mqa_workspace_bytes(const MqaArgs& A) {
   if (!A.bf16) return 0;
   MqaArgs B = A;
   B.gamma = nullptr;
-  const size_t a = partial_bytes(B, plan_mqa(B));
+  const MqaLaunch La = plan_mqa(B);
+  const size_t a = partial_bytes(B, La) + norm_bytes(B, La);
   static const float one = 1.f;
   B.gamma = &one;
-  const size_t b = partial_bytes(B, plan_mqa(B));
+  const MqaLaunch Lb = plan_mqa(B);
+  const size_t b = partial_bytes(B, Lb) + norm_bytes(B, Lb);
   return a > b ? a : b;
 }
 
@@ -1467,11 +1258,23 @@ hipError_t launch_mqa(const MqaArgs& A, void* ws, size_t ws_bytes, hipStream_t s
   MqaLaunch L = plan_mqa(A);
   float* part_o = nullptr;
   float* part_ml = nullptr;
+  const size_t pb = partial_bytes(A, L), nb = norm_bytes(A, L);
+  if (pb + nb > 0 && (ws_bytes < pb + nb || !ws)) return hipErrorInvalidValue;
   if (L.nsplit > 1) {
     const size_t parts = (size_t)A.batch * A.n_q * L.nsplit * A.heads;
-    if (ws_bytes < parts * (kD + 2) * sizeof(float) || !ws) return hipErrorInvalidValue;
     part_o = (float*)ws;
     part_ml = part_o + parts * kD;
+  }
+  float* inv_kv = nullptr;
+  float* inv_raw = nullptr;
+  if (nb > 0) {
+    inv_kv = (float*)((char*)ws + pb);
+    inv_raw = (float*)((char*)ws + pb + r256((size_t)A.batch * A.kv_cap * sizeof(float)));
+    const long n_rows = (long)A.batch * ((long)A.kv_cap + A.raw_cap);
+    LaunchTimer timer("mqa_row_norms", s);
+    row_inv_rms_kernel<<<dim3((unsigned)((n_rows + 3) / 4)), 256, 0, s>>>(A, inv_kv, inv_raw);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
   const size_t lds = mqa_lds_bytes(L);
   static hipError_t attr = [] {
@@ -1491,7 +1294,7 @@ hipError_t launch_mqa(const MqaArgs& A, void* ws, size_t ws_bytes, hipStream_t s
   {
     LaunchTimer timer(L.kind == 2 ? "mqa_bf16_hg" : (L.kind == 1 ? "mqa_bf16_h32" : "mqa_bf16_h16"), s);
     if (L.kind == 2) mqa_hg_kernel<<<grid, kHgWaves * 64, lds, s>>>(A, L, part_o, part_ml);
-    else if (L.kind == 1) mqa32d_kernel<<<grid, 512, lds, s>>>(A, L, part_o, part_ml);
+    else if (L.kind == 1) mqa_fd_kernel<<<grid, kFdWaves * 64, lds, s>>>(A, L, part_o, part_ml, inv_kv, inv_raw);
     else if (L.nw == 4) mqa_bf16_kernel<4><<<grid, 4 * 64, lds, s>>>(A, L, part_o, part_ml);
     else if (L.nw == 2) mqa_bf16_kernel<2><<<grid, 2 * 64, lds, s>>>(A, L, part_o, part_ml);
     else mqa_bf16_kernel<1><<<grid, 64, lds, s>>>(A, L, part_o, part_ml);

@@ -32,11 +32,12 @@ KERNELS = {
     "index_scores_mxfp4": (r"index_scores_mfma<\d+, true", "indexer.hip"),
     "index_scores_f32": (r"index_scores_f32", "indexer.hip"),
     "topk": (r"topk_", "topk.hip"),
-    "mqa_bf16_h32": (r"mqa32d_kernel", "mqa.hip"),
+    "mqa_bf16_h32": (r"mqa_fd_kernel", "mqa.hip"),
     "mqa_bf16_hg": (r"mqa_hg_kernel", "mqa.hip"),
     "mqa_bf16_h16": (r"mqa_bf16_kernel<", "mqa.hip"),
     "mqa_f32": (r"mqa_f32_kernel", "mqa.hip"),
     "mqa_combine": (r"mqa_combine_kernel", "mqa.hip"),
+    "mqa_row_norms": (r"row_inv_rms_kernel", "mqa.hip"),
     "compress": (r"compress_kernel<", "compress.hip"),
     "mxfp4_quantize": (r"mxfp4_quantize_kernel", "compress.hip"),
 }
