@@ -14,10 +14,11 @@
 // window tokens max(0, t-w+1) .. t.  Dense: entries 0 .. V(t)-1, then the window.
 //
 // bf16 kernels (head_dim 512), chosen by the host:
-//  - mqa_fd_kernel (many queries, unit RMSNorm weight): 4 waves = the 128 heads of a
-//    (query, split) unit, 32 heads x all 512 dims per wave;
+//  - mqa_w8_kernel (unit RMSNorm weight): 8 waves = the 128 heads of a (query,
+//    split) unit, two waves per SIMD; prefill, dense HCA decode;
 //  - mqa_hg_kernel (few queries, unit weight): 4 waves = one group of 32 heads of a
 //    (query, split) unit, 128 dims per wave, partial logits summed through LDS;
+//    sparse decode;
 //  - mqa_bf16_kernel (any RMSNorm weight): NW waves x 16 heads with an online
 //    (running maximum) softmax.
 // All stage 32-row item tiles in LDS (row-major, padded) and form S^T = K . u^T and
@@ -25,6 +26,7 @@
 // the product, 1/rms of each row scales its logit and its softmax weight, and g
 // multiplies the output.  Splits write fp32 partials (unnormalised O, maximum, sum)
 // that a second kernel combines in fixed split order (deterministic).
+#include <cmath>
 #include <type_traits>
 
 #include "csa_device.hpp"
@@ -173,7 +175,8 @@ constexpr int kRowB = kD * 2 + 16;      // LDS row stride in bytes (padded)
 struct MqaLaunch {
   int nsplit, ips, n_hg, units, nw;   // nw: waves per workgroup
   int slots;                          // index slots of a split copied to LDS
-  int kind;                           // 0: 16-head waves, 1: 128-head workgroups, 2: 32-head workgroups
+  int kind;   // 0: 16-head waves, 2: 32-head workgroups, 3: 128-head 8-wave workgroups
+  int pre;    // kind 3: row 1/rms from the per-cache pre-pass
 };
 
 // Masked items are loaded from this all-zero row, so that no lane ever reads
@@ -820,20 +823,8 @@ void mqa_hg_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml) {
 }
 
 // ---------------------------------------------------------------------------------
-// Full-dim kernel for many queries (prefill): a workgroup = 4 waves = the 128 heads
-// of one (query, split) unit, wave w owning heads 32 w .. 32 w + 31 over all 512
-// dims (one wave per SIMD: q in 128 registers, O^T in 256 accumulators).  No
-// partial-logit exchange between waves: one barrier per tile (the rows every wave
-// gathered have landed, and the buffer two tiles ahead is free).
-//
-// Gathered rows are row-major in LDS (kRowB2 bytes apart); each wave gathers 8 rows
-// of the tile two ahead right after the tile barrier.  The 1/rms of every row comes
-// from a pre-pass
-// over the whole cache (row_inv_rms_kernel): a compressed entry is normalised once,
-// not once per query that selects it.
-constexpr int kFdWaves = 4;
-constexpr int kFdRpw = kTile / kFdWaves;
-
+// Row 1/rms pre-pass for many queries (prefill): a compressed entry is normalised
+// once, not once per query that selects it.
 __device__ float g_zero_f32;   // 1/rms of a missing row: weight 0
 
 // One wave per row: 1/rms of every row of kv (all kv_cap rows of every sequence) and
@@ -853,28 +844,76 @@ __global__ __launch_bounds__(256) void row_inv_rms_kernel(MqaArgs A, float* inv_
   }
 }
 
-__global__ __launch_bounds__(kFdWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void mqa_fd_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml, const float* inv_kv,
+// ---------------------------------------------------------------------------------
+// Eight-wave kernel: a workgroup = one (query, split) unit x 128 heads, two waves per
+// SIMD so that one wave's MFMAs run while the other waits on LDS (on MI355X a wave
+// alone on its SIMD keeps an LDS-fed MFMA stream roughly half busy; two reach about
+// four fifths).  Per 32-row tile:
+//   QK: wave w = (head block hb = w & 3, dim half dh = w >> 2) forms the partial
+//       S^T[32 rows x 32 heads] over its 256 dims.  The pair (hb, 0), (hb, 1) swaps
+//       halves through LDS and each finishes 16 rows: their softmax weights, packed
+//       to bf16, are exactly the B operand of k-step dh of the P V product.
+//   PV: wave w = (head pair hp = w & 1, dim quarter dq = w >> 1) accumulates
+//       O^T[128 dims x 64 heads]; each V^T fragment (ds_read_b64_tr_b16, the slow
+//       LDS read) feeds two MFMAs.
+// Row 1/rms: from the per-cache pre-pass (PRE, many queries: each row normalised
+// once), or from the gathered tile itself, each wave summing the 4 rows it loaded
+// (few queries: a pre-pass would read the whole cache for a few hundred rows).
+constexpr int kW8Waves = 8;
+constexpr int kW8Rpw = kTile / kW8Waves;   // rows each wave gathers per tile
+constexpr int kW8Stage = 64 + 4;           // fp32 words per head row of the output staging
+
+// Row sums of squares of the 4 rows a wave loaded (part[rr]: this lane's share of
+// row rr): a row-splitting butterfly; the lane ends with the total of row
+// 2 * bit5(lane) + bit4(lane).
+__device__ __forceinline__ float rows_total4(const float (&p)[4], int lane) {
+  bool up = (lane & 32) != 0;
+  float a[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float send = up ? p[j] : p[2 + j];
+    const float keep = up ? p[2 + j] : p[j];
+    a[j] = keep + __shfl_xor(send, 32, 64);
+  }
+  up = (lane & 16) != 0;
+  float s = (up ? a[1] : a[0]) + __shfl_xor(up ? a[0] : a[1], 16, 64);
+  s += __shfl_xor(s, 8, 64);
+  s += __shfl_xor(s, 4, 64);
+  s += __shfl_xor(s, 2, 64);
+  s += __shfl_xor(s, 1, 64);
+  return s;
+}
+
+template <bool PRE>
+__global__ __launch_bounds__(kW8Waves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void mqa_w8_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml, const float* inv_kv,
                    const float* inv_raw) {
   __shared__ __attribute__((aligned(16))) uint8_t tb0[kTile * kRowB2];
   __shared__ __attribute__((aligned(16))) uint8_t tb1[kTile * kRowB2];
   __shared__ __attribute__((aligned(16))) uint8_t tb2[kTile * kRowB2];
   __shared__ __attribute__((aligned(16))) float irms[kNB][kTile];
+  __shared__ __attribute__((aligned(16))) f32x4_t xs[kW8Waves][2][64];   // partial S^T halves
+  __shared__ __attribute__((aligned(16))) uint4 pbuf[4][2][64];          // P^T B operands
+  __shared__ float red[kW8Waves][64];                                    // q norms, then l
   __shared__ int32_t slot[kSlotsLds];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5, c32 = lane & 31;
+  const int hb = wave & 3, dh = wave >> 2;   // QK role
+  const int hp = wave & 1, dq = wave >> 1;   // PV role
 
-  const int f = blockIdx.x;
-  const int xcd = f & 7, r8 = f >> 3;
-  const int hg = r8 % L.n_hg, ug = r8 / L.n_hg;
-  const int unit = ug * 8 + xcd;
-  if (unit >= L.units) return;
-  const long row = unit / L.nsplit;
-  const int split = unit % L.nsplit;
+  // The units of one XCD are consecutive, so neighbouring queries (which share their
+  // window rows and many selected entries) meet in one L2.
+  const int total_units = L.units * L.n_hg;
+  const int upx = (total_units + 7) / 8;
+  const int unit = (blockIdx.x & 7) * upx + (blockIdx.x >> 3);
+  if (unit >= total_units) return;
+  const int hg = unit % L.n_hg;
+  const long rs = unit / L.n_hg;
+  const long row = rs / L.nsplit;
+  const int split = (int)(rs % L.nsplit);
   const int b = (int)(row / A.n_q);
-  const int head = hg * 128 + wave * 32 + c32;
 
   RowSrc R;
   {
@@ -888,74 +927,92 @@ void mqa_fd_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml, const 
     R.gidx = src.idx;
     R.use_slots = !A.dense;
     if (R.use_slots)
-      for (int i = threadIdx.x; i < L.ips; i += kFdWaves * 64) {
+      for (int i = threadIdx.x; i < L.ips; i += kW8Waves * 64) {
         const int it = R.it0 + i;
         slot[i] = (it < min(R.it1, R.n_first)) ? src.idx[it] : -1;
       }
   }
-  const float* inv_kv_b = inv_kv + (long)b * A.kv_cap;
-  const float* inv_raw_b = inv_raw + (long)b * A.raw_cap;
-  // the query row of this lane's head: dims 16 ks + 8 h + [0, 8), ks = 0..31
-  const uint16_t* qrow = (const uint16_t*)A.q + (row * A.heads + head) * kD;
-  uint4 qraw[32];
+  const float* inv_kv_b = PRE ? inv_kv + (long)b * A.kv_cap : nullptr;
+  const float* inv_raw_b = PRE ? inv_raw + (long)b * A.raw_cap : nullptr;
+  // this lane's query head (QK role) and its dims 256 dh + 16 ks + 8 h + [0, 8)
+  const uint16_t* qrow = (const uint16_t*)A.q + (row * A.heads + hg * 128 + 32 * hb + c32) * kD + 256 * dh + 8 * h;
+  uint4 qraw[16];
 #pragma unroll
-  for (int ks = 0; ks < 32; ++ks) qraw[ks] = *(const uint4*)(qrow + 16 * ks + 8 * h);
-  lds_barrier();   // the slots are in LDS (each store waited for its load)
+  for (int ks = 0; ks < 16; ++ks) qraw[ks] = *(const uint4*)(qrow + 16 * ks);
+  lds_barrier();   // the slots are in LDS
 
   const int n_tiles = (R.it1 - R.it0 + kTile - 1) / kTile;
-  // Tile row item -> source row (nullptr: masked) and its 1/rms (the zero float for a
-  // masked row, whose weight is then 0).
+  // tile row item -> source row (nullptr: masked) and, with PRE, its 1/rms (the zero
+  // float for a masked row, whose weight is then 0)
   auto resolve = [&](int item, const float*& ip) -> const uint8_t* {
     ip = &g_zero_f32;
     if (item >= R.it1) return nullptr;
     if (item < R.n_first) {
       const int e = R.dense ? item : slot[item - R.it0];
       if (e < 0 || e >= R.kv_rows) return nullptr;
-      ip = inv_kv_b + e;
+      if (PRE) ip = inv_kv_b + e;
       return R.kv + (long)e * (kD * 2);
     }
     const int r = R.win_lo + (item - R.n_first) - R.raw_base;
     if (r < 0 || r >= R.raw_cap) return nullptr;
-    ip = inv_raw_b + r;
+    if (PRE) ip = inv_raw_b + r;
     return R.raw + (long)r * (kD * 2);
   };
-  // Gathers tile ti: wave 0 first brings the 32 rows' 1/rms into LDS (lane l: row l),
-  // then every wave its 8 rows (lane rr resolves row wave + 4 rr; a rolled loop of one
-  // direct-to-LDS instruction, which the compiler tracks without extra waits).  Wave 0
-  // issues 9 loads per tile, the others 8.
-  auto issue = [&](int ti, uint8_t* dst, float* irms_dst) {
+  // Gathering tile ti: lane rr of every wave resolves the wave's row wave + 8 rr (a
+  // masked row reads the zero row), with PRE wave 0's lane l also the 1/rms of row l.
+  struct Gather {
+    uint32_t lo, hi;   // row address of lane rr
+    const float* ip;   // PRE: 1/rms address of row c32
+    uint32_t ok;       // rows that exist
+  };
+  auto resolve_tile = [&](int ti) -> Gather {
+    Gather g;
     const int item0 = R.it0 + ti * kTile;
-    const float* ip;
-    if (wave == 0) {
-      resolve(item0 + c32, ip);
-      if (h == 0)
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)ip,
-                                         (__attribute__((address_space(3))) void*)irms_dst, 4, 0, 0);
-    }
-    const uint8_t* pl = resolve(item0 + wave + kFdWaves * (lane & (kFdRpw - 1)), ip);
+    g.ip = &g_zero_f32;
+    if (PRE && wave == 0) resolve(item0 + c32, g.ip);
+    const float* unused;
+    const uint8_t* pl = resolve(item0 + wave + kW8Waves * (lane & (kW8Rpw - 1)), unused);
+    g.ok = (uint32_t)__ballot(pl != nullptr) & ((1u << kW8Rpw) - 1u);
     const uint64_t pv = (uint64_t)(pl ? pl : g_zero_row);
-    const uint32_t lo = (uint32_t)pv, hi = (uint32_t)(pv >> 32);
+    g.lo = (uint32_t)pv;
+    g.hi = (uint32_t)(pv >> 32);
+    return g;
+  };
+  // the 1/rms of the tile's rows (PRE, wave 0, lanes 0..31: row = lane)
+  auto load_norms = [&](const Gather& g, float* irms_dst) {
+    if (PRE && wave == 0 && h == 0)
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g.ip,
+                                       (__attribute__((address_space(3))) void*)irms_dst, 4, 0, 0);
+  };
+  auto load_row = [&](const Gather& g, int rr, uint8_t* dst) {
+    const uint64_t p = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)g.hi, rr) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((int)g.lo, rr);
+    load_row_to_lds((const uint8_t*)p + 16 * lane, dst + (wave + kW8Waves * rr) * kRowB2);
+  };
+  auto issue = [&](int ti, uint8_t* dst, float* irms_dst) -> uint32_t {
+    const Gather g = resolve_tile(ti);
+    load_norms(g, irms_dst);
 #pragma unroll 1
-    for (int rr = 0; rr < kFdRpw; ++rr) {
-      const uint64_t p = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, rr) << 32) |
-                         (uint32_t)__builtin_amdgcn_readlane((int)lo, rr);
-      load_row_to_lds((const uint8_t*)p + 16 * lane, dst + (wave + kFdWaves * rr) * kRowB2);
-    }
+    for (int rr = 0; rr < kW8Rpw; ++rr) load_row(g, rr, dst);
+    return g.ok;
   };
   auto buf_ptr = [&](int bi) -> uint8_t* { return bi == 0 ? tb0 : (bi == 1 ? tb1 : tb2); };
-  if (n_tiles > 0) issue(0, tb0, irms[0]);
-  if (n_tiles > 1) issue(1, tb1, irms[1]);
+  uint32_t okm[kNB] = {0, 0, 0};
+  if (n_tiles > 0) okm[0] = issue(0, tb0, irms[0]);
+  if (n_tiles > 1) okm[1] = issue(1, tb1, irms[1]);
 
-  // ---- u = q / rms(q), all within the wave (the two lanes of a head hold its halves)
-  bf16x8_t qf[32];
+  // ---- u = q / rms(q): the pair (hb, 0), (hb, 1) holds the two dim halves of a head
+  bf16x8_t qf[16];
   {
     float ss = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < 32; ++ks) ss = sumsq_bf16x8(qraw[ks], ss);
+    for (int ks = 0; ks < 16; ++ks) ss = sumsq_bf16x8(qraw[ks], ss);
     ss += __shfl_xor(ss, 32, 64);
-    const float qinv = 1.f / sqrtf(ss * (1.f / kD) + A.eps);
+    red[wave][lane] = ss;
+    lds_barrier();
+    const float qinv = 1.f / sqrtf((ss + red[wave ^ 4][lane]) * (1.f / kD) + A.eps);
 #pragma unroll
-    for (int ks = 0; ks < 32; ++ks) {
+    for (int ks = 0; ks < 16; ++ks) {
       const uint32_t w4[4] = {qraw[ks].x, qraw[ks].y, qraw[ks].z, qraw[ks].w};
       uint32_t o4[4];
 #pragma unroll
@@ -966,142 +1023,209 @@ void mqa_fd_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml, const 
   }
   const float sl2 = A.scale * kLog2e;
   float l_run = 0.f;
-  f32x16_t o[16];
+  f32x16_t o[2][4];
 #pragma unroll
-  for (int db = 0; db < 16; ++db) o[db] = f32x16_t{};
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[j][db] = f32x16_t{};
 
   const int G = lane >> 4, sl = lane & 15;
-  const int ka_base = c32 * kRowB2 + 16 * h;   // K: row c32, dims 16 ks + 8 h
-  const int vb_base = (4 * h + (sl >> 2)) * kRowB2 + (16 * (G & 1) + 4 * (sl & 3)) * 2;
-  auto ka_off = [](int ks) { return 32 * ks; };
-  auto vb_off = [](int k) { return (16 * (k & 1)) * kRowB2 + 64 * (k >> 1); };   // k = 2 db + t
+  const int ka_base = c32 * kRowB2 + 16 * h;   // K: row c32, dims 256 dh + 16 ks + 8 h
+  const int vb_base = (4 * h + (sl >> 2)) * kRowB2 + (16 * (G & 1) + 4 * (sl & 3)) * 2 + 256 * dq;
+  // V^T fragment f = 2 db + t: dims 128 dq + 32 db + [0, 32), rows of k-step t
+  auto vb_off = [](int f) { return (16 * (f & 1)) * kRowB2 + 64 * (f >> 1); };
 
-  auto step = [&](auto BUFC, int ti) {
+  // DH: this wave's dim half as a compile-time constant (register indices must be static)
+  auto step = [&](auto BUFC, auto DHC, int ti) {
     constexpr int BUF = decltype(BUFC)::value;
+    constexpr int DH = decltype(DHC)::value;
     uint8_t* const tile = BUF == 0 ? tb0 : (BUF == 1 ? tb1 : tb2);
-    // this wave's loads of tile ti are done (tile ti+1's may still be in flight)
-    if (ti + 1 < n_tiles) {
-      if (wave == 0) __builtin_amdgcn_s_waitcnt(0x0F70 | (kFdRpw + 1));
-      else __builtin_amdgcn_s_waitcnt(0x0F70 | kFdRpw);
+    // tile ti is in LDS (waited before the previous barrier)
+    if (!PRE) {
+      // 1/rms of the 4 rows this wave loaded (read before the barrier: they are its own)
+      float part[kW8Rpw];
+#pragma unroll
+      for (int rr = 0; rr < kW8Rpw; ++rr) {   // one row at a time: few live registers
+        part[rr] = sumsq_bf16x8(*(const uint4*)(tile + (wave + kW8Waves * rr) * kRowB2 + 16 * lane), 0.f);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const float s = rows_total4(part, lane);
+      const int rr = 2 * ((lane >> 5) & 1) + ((lane >> 4) & 1);
+      if ((lane & 15) == 0)
+        irms[BUF][wave + kW8Waves * rr] = ((okm[BUF] >> rr) & 1u) ? 1.f / sqrtf(s * (1.f / kD) + A.eps) : 0.f;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // ---- partial S^T over this wave's 256 dims: 16 k-steps
+    f32x16_t s = f32x16_t{};
+    {
+      const uint8_t* ka = tile + ka_base + 512 * DH;
+      constexpr int PF = 2;
+      uint4 a[PF];
+#pragma unroll
+      for (int j = 0; j < PF; ++j) a[j] = *(const uint4*)(ka + 32 * j);
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) {
+        const uint4 c = a[ks % PF];
+        if (ks + PF < 16) a[ks % PF] = *(const uint4*)(ka + 32 * (ks + PF));
+        s = mfma32x32x16(as_bf16x8(c), qf[ks], s);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // ---- the partner finishes the rows of k-step 1 - dh: hand it those 8 partials
+    {
+      constexpr int g = 8 * (1 - DH);
+      xs[wave][0][lane] = f32x4_t{s[g], s[g + 1], s[g + 2], s[g + 3]};
+      xs[wave][1][lane] = f32x4_t{s[g + 4], s[g + 5], s[g + 6], s[g + 7]};
+    }
+    // every wave is past tile ti - 1 (its P V): its buffer takes tile ti + 2
+    lds_barrier();
+    if (ti + 2 < n_tiles) okm[(BUF + 2) % kNB] = issue(ti + 2, buf_ptr((BUF + 2) % kNB), irms[(BUF + 2) % kNB]);
+    // rows of k-step dh: s[8 dh + k] is row 16 dh + 8 (k / 4) + 4 h + k % 4
+    {
+      const f32x4_t x0 = xs[wave ^ 4][0][lane], x1 = xs[wave ^ 4][1][lane];
+      const f32x4_t ir0 = *(const f32x4_t*)&irms[BUF][16 * DH + 4 * h];
+      const f32x4_t ir1 = *(const f32x4_t*)&irms[BUF][16 * DH + 8 + 4 * h];
+      float sf[8], ir[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        sf[k] = s[8 * DH + k] + x0[k];
+        sf[4 + k] = s[8 * DH + 4 + k] + x1[k];
+        ir[k] = ir0[k];
+        ir[4 + k] = ir1[k];
+      }
+      float psum = 0.f;
+      uint32_t pk[4];
+#pragma unroll
+      for (int k = 0; k < 8; k += 2) {
+        float p2[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const float e = __builtin_amdgcn_exp2f(sf[k + u] * sl2 * ir[k + u]);
+          const float p = ir[k + u] > 0.f ? e : 0.f;
+          psum += p;
+          p2[u] = p * ir[k + u];
+        }
+        pk[k / 2] = pack_bf16x2(p2[0], p2[1]);
+      }
+      l_run += psum;
+      pbuf[hb][DH][lane] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    }
+    // this wave's loads of tile ti + 1 are done (those of tile ti + 2 may be in flight);
+    // after the barrier every wave's are, and every wave's P of tile ti is in LDS
+    if (ti + 2 < n_tiles) {
+      if (PRE && wave == 0) __builtin_amdgcn_s_waitcnt(0x0F70 | (kW8Rpw + 1));
+      else __builtin_amdgcn_s_waitcnt(0x0F70 | kW8Rpw);
     } else {
       __builtin_amdgcn_s_waitcnt(0x0F70);
     }
-    // every wave's rows (and the row norms) of tile ti have landed; every wave is
-    // past tile ti-1
     lds_barrier();
-    if (ti + 2 < n_tiles) issue(ti + 2, buf_ptr((BUF + 2) % kNB), irms[(BUF + 2) % kNB]);
-    // rows of this lane's logits: 8 (r/4) + 4 h + [0, 4), four aligned quads
-    f32x4_t irq[4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) irq[g] = *(const f32x4_t*)&irms[BUF][8 * g + 4 * h];
-    // ---- S^T over all 512 dims: 32 k-steps of 16
-    f32x16_t s;
+    // ---- O^T[128 dq .. + 128 dims x 64 heads] += V^T . P^T
     {
-      const uint8_t* ka = tile + ka_base;
-      constexpr int PF = 8;
-      uint4 a[PF];
+      const bf16x8_t p00 = as_bf16x8(pbuf[2 * hp][0][lane]), p01 = as_bf16x8(pbuf[2 * hp][1][lane]);
+      const bf16x8_t p10 = as_bf16x8(pbuf[2 * hp + 1][0][lane]), p11 = as_bf16x8(pbuf[2 * hp + 1][1][lane]);
+      const uint8_t* vb = tile + vb_base;
+      constexpr int PV = 2;
+      i16x4_t v0[PV], v1[PV];
 #pragma unroll
-      for (int j = 0; j < PF; ++j) a[j] = *(const uint4*)(ka + ka_off(j));
-      f32x16_t s2[2] = {f32x16_t{}, f32x16_t{}};
+      for (int j = 0; j < PV; ++j) {
+        v0[j] = lds_read_tr16(vb + vb_off(j));
+        v1[j] = lds_read_tr16(vb + vb_off(j) + 8 * kRowB2);
+      }
 #pragma unroll
-      for (int ks = 0; ks < 32; ++ks) {
-        const uint4 c = a[ks % PF];
-        if (ks + PF < 32) a[ks % PF] = *(const uint4*)(ka + ka_off(ks + PF));
-        s2[ks & 1] = mfma32x32x16(as_bf16x8(c), qf[ks], s2[ks & 1]);
+      for (int f = 0; f < 8; ++f) {
+        const i16x4_t c0 = v0[f % PV], c1 = v1[f % PV];
+        if (f + PV < 8) {
+          v0[f % PV] = lds_read_tr16(vb + vb_off(f + PV));
+          v1[f % PV] = lds_read_tr16(vb + vb_off(f + PV) + 8 * kRowB2);
+        }
+        typedef short i16x8_t __attribute__((ext_vector_type(8)));
+        const bf16x8_t va = __builtin_bit_cast(bf16x8_t, i16x8_t{c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]});
+        o[0][f >> 1] = mfma32x32x16(va, (f & 1) ? p01 : p00, o[0][f >> 1]);
+        o[1][f >> 1] = mfma32x32x16(va, (f & 1) ? p11 : p10, o[1][f >> 1]);
         __builtin_amdgcn_sched_barrier(0);
       }
-      s = s2[0] + s2[1];
-    }
-    // ---- softmax weights (exponents within [-100, 100]; a missing row has weight 0)
-    float psum = 0.f;
-    uint32_t pk[8];
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      float p2[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const float ir = irq[(r + u) / 4][(r + u) % 4];
-        const float e = __builtin_amdgcn_exp2f(s[r + u] * sl2 * ir);
-        const float p = ir > 0.f ? e : 0.f;
-        psum += p;
-        p2[u] = p * ir;
-      }
-      pk[r / 2] = pack_bf16x2(p2[0], p2[1]);
-    }
-    l_run += psum;
-    const bf16x8_t pb0 = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
-    const bf16x8_t pb1 = as_bf16x8(make_uint4(pk[4], pk[5], pk[6], pk[7]));
-    // ---- O^T += V^T . P^T over the 16 dim blocks
-    const uint8_t* vb = tile + vb_base;
-    constexpr int PV = 4;
-    i16x4_t v0[PV], v1[PV];
-#pragma unroll
-    for (int j = 0; j < PV; ++j) {
-      v0[j] = lds_read_tr16(vb + vb_off(j));
-      v1[j] = lds_read_tr16(vb + vb_off(j) + 8 * kRowB2);
-    }
-#pragma unroll
-    for (int k = 0; k < 32; ++k) {
-      const i16x4_t c0 = v0[k % PV], c1 = v1[k % PV];
-      if (k + PV < 32) {
-        v0[k % PV] = lds_read_tr16(vb + vb_off(k + PV));
-        v1[k % PV] = lds_read_tr16(vb + vb_off(k + PV) + 8 * kRowB2);
-      }
-      typedef short i16x8_t __attribute__((ext_vector_type(8)));
-      const i16x8_t vv = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-      o[k >> 1] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, vv), (k & 1) ? pb1 : pb0, o[k >> 1]);
-      __builtin_amdgcn_sched_barrier(0);
     }
   };
-  for (int ti = 0; ti < n_tiles; ti += kNB) {
-    step(std::integral_constant<int, 0>{}, ti);
-    if (ti + 1 < n_tiles) step(std::integral_constant<int, 1>{}, ti + 1);
-    if (ti + 2 < n_tiles) step(std::integral_constant<int, 2>{}, ti + 2);
+  // tile 0 in LDS (tile 1 may be in flight)
+  if (n_tiles > 1) {
+    if (PRE && wave == 0) __builtin_amdgcn_s_waitcnt(0x0F70 | (kW8Rpw + 1));
+    else __builtin_amdgcn_s_waitcnt(0x0F70 | kW8Rpw);
+  } else {
+    __builtin_amdgcn_s_waitcnt(0x0F70);
   }
-
-  l_run += __shfl_xor(l_run, 32, 64);
-  // o[db][r] holds dim 32 db + 8 (r/4) + 4 h + r%4 of this lane's head; out through
-  // LDS in four 128-dim quarters (each wave its own region of the free tile buffers)
   lds_barrier();
-  float* stage = (float*)((wave < 2 ? tb0 : tb1) + (wave & 1) * (32 * kStageRow * 4));
-  const int hl = lane >> 5, d4 = lane & 31;
-  const float inv_l = l_run > 0.f ? 1.f / l_run : 0.f;
+  auto run = [&](auto DHC) {
+    for (int ti = 0; ti < n_tiles; ti += kNB) {
+      step(std::integral_constant<int, 0>{}, DHC, ti);
+      if (ti + 1 < n_tiles) step(std::integral_constant<int, 1>{}, DHC, ti + 1);
+      if (ti + 2 < n_tiles) step(std::integral_constant<int, 2>{}, DHC, ti + 2);
+    }
+  };
+  if (dh) run(std::integral_constant<int, 1>{});
+  else run(std::integral_constant<int, 0>{});
+
+  // ---- softmax denominators: head 32 hb + c32 summed over the two lane halves here,
+  // then over the pair (hb, 0), (hb, 1) through LDS
+  l_run += __shfl_xor(l_run, 32, 64);
+  lds_barrier();   // every wave is past its last tile: the tile buffers and red are free
+  red[wave][lane] = l_run;
+  lds_barrier();
+  float inv_l[2], l_tot[2];
 #pragma unroll
-  for (int qtr = 0; qtr < 4; ++qtr) {
+  for (int j = 0; j < 2; ++j) {
+    const int hbj = 2 * hp + j;
+    l_tot[j] = red[hbj][c32] + red[hbj + 4][c32];
+    inv_l[j] = l_tot[j] > 0.f ? 1.f / l_tot[j] : 0.f;
+  }
+  // ---- O^T -> rows of 64 dims through a wave-private LDS region, four chunks
+  // (head block j of the pair, dim half of the quarter)
+  float* stage = (float*)(buf_ptr(wave / 3) + (wave % 3) * (32 * kW8Stage * 4));
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x16_t& od = o[4 * qtr + db];
-        *(f32x4_t*)(stage + c32 * kStageRow + 32 * db + 8 * j + 4 * h) =
-            f32x4_t{od[4 * j], od[4 * j + 1], od[4 * j + 2], od[4 * j + 3]};
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int dbl = 0; dbl < 2; ++dbl)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x16_t& od = o[j][2 * half + dbl];
+          *(f32x4_t*)(stage + c32 * kW8Stage + 32 * dbl + 8 * q + 4 * h) =
+              f32x4_t{od[4 * q], od[4 * q + 1], od[4 * q + 2], od[4 * q + 3]};
+        }
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      const int dim0 = 128 * dq + 64 * half + 4 * (lane & 15);
+      const int head0 = hg * 128 + 64 * hp + 32 * j;
+      if (L.nsplit == 1) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int hh = 4 * k + (lane >> 4);
+          const float il = __shfl(inv_l[j], hh, 64);
+          const f32x4_t v = *(const f32x4_t*)(stage + hh * kW8Stage + 4 * (lane & 15));
+          uint16_t* orow = (uint16_t*)A.out + (row * A.heads + head0 + hh) * kD + dim0;
+          *(uint2*)orow = make_uint2(pack_bf16x2(v[0] * il, v[1] * il), pack_bf16x2(v[2] * il, v[3] * il));
+        }
+      } else {
+        float* po = part_o + (((long)row * L.nsplit + split) * A.heads + head0) * kD + dim0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int hh = 4 * k + (lane >> 4);
+          *(f32x4_t*)(po + (long)hh * kD) = *(const f32x4_t*)(stage + hh * kW8Stage + 4 * (lane & 15));
+        }
       }
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    const int dim0 = 128 * qtr + 4 * d4;
-    if (L.nsplit == 1) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // reads done before the next chunk overwrites
+    }
+  if (dq == 0 && h == 0) {
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int hh = 2 * k + hl;
-        const float il = __shfl(inv_l, hh, 64);
-        const f32x4_t v = *(const f32x4_t*)(stage + hh * kStageRow + 4 * d4);
-        uint16_t* orow = (uint16_t*)A.out + (row * A.heads + hg * 128 + wave * 32 + hh) * kD + dim0;
-        *(uint2*)orow = make_uint2(pack_bf16x2(v[0] * il, v[1] * il), pack_bf16x2(v[2] * il, v[3] * il));
-      }
-    } else {
-      float* po = part_o + (((long)row * L.nsplit + split) * A.heads + hg * 128 + wave * 32) * kD + dim0;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int hh = 2 * k + hl;
-        *(f32x4_t*)(po + (long)hh * kD) = *(const f32x4_t*)(stage + hh * kStageRow + 4 * d4);
+    for (int j = 0; j < 2; ++j) {
+      const int head = hg * 128 + 64 * hp + 32 * j + c32;
+      if (L.nsplit == 1) {
+        if (A.lse) A.lse[row * A.heads + head] = l_tot[j] > 0.f ? logf(l_tot[j]) : -INFINITY;
+      } else {
+        float* pm = part_ml + (((long)row * L.nsplit + split) * A.heads + head) * 2;
+        pm[0] = l_tot[j] > 0.f ? 0.f : -INFINITY;
+        pm[1] = l_tot[j];
       }
     }
-  }
-  if (L.nsplit == 1) {
-    if (A.lse && h == 0) A.lse[row * A.heads + head] = l_run > 0.f ? logf(l_run) : -INFINITY;
-  } else if (h == 0) {
-    float* pm = part_ml + (((long)row * L.nsplit + split) * A.heads + head) * 2;
-    pm[0] = l_run > 0.f ? 0.f : -INFINITY;
-    pm[1] = l_run;
   }
 }
 
@@ -1152,39 +1276,56 @@ __global__ __launch_bounds__(128) void mqa_combine_kernel(MqaArgs A, MqaLaunch L
 
 static MqaLaunch plan_mqa(const MqaArgs& A) {
   MqaLaunch L;
+  L.pre = 0;
   const long rows = (long)A.batch * A.n_q;
   const int total_max = (A.dense ? A.n_max : A.topk) + A.window;
   const int tiles_max = (total_max + kTile - 1) / kTile;
-  // 32-head MFMA paths need the unit RMSNorm weight and a scale that keeps every
-  // exp2(logit) normal without a running maximum.  Few queries (decode): 32-head
-  // workgroups, splitting heads and items; many queries: 128-head workgroups.
+  // The 32- and 128-head MFMA paths need the unit RMSNorm weight and a scale that
+  // keeps every exp2(logit) normal without a running maximum.
   const bool fixed = A.gamma == nullptr && A.scale * kLog2e * kD * 1.01f <= 100.f;
   L.kind = 0;
-  if (fixed && A.heads % 32 == 0 && rows <= 32) L.kind = 2;
-  else if (fixed && A.heads % 128 == 0) L.kind = 1;
-  if (L.kind != 0) {
-    // Split count from a cost model measured on MI355X: per 32-row tile a workgroup
-    // works through, rounds of <= 256 workgroups (one per CU), the fp32 partials each
-    // (query, head group, split) writes and the merge reads, and the merge launch.
-    const bool hg = L.kind == 2;
-    L.nw = hg ? kHgWaves : kFdWaves;
-    L.n_hg = A.heads / (hg ? 32 : 128);
-    const double t_tile = hg ? 2.6 : 1.5, t_part = hg ? 0.033 : 0.06, t_merge = 5.0;
+  if (fixed) {
+    // Kernel and split count from a cost model fitted to MI355X timings (microseconds):
+    // rounds of <= 256 workgroups (one per CU), each a fixed start-up cost plus its
+    // 32-row tiles; with splits, the fp32 partials are written and read back once
+    // (about 4 MB per microsecond each way) and the merge is one more launch.
     double best = 1e30;
-    int best_s = 1;
-    for (int sp = 1; sp <= kMaxSplit && sp <= tiles_max; ++sp) {
-      const int tps = (tiles_max + sp - 1) / sp;
-      const int s_eff = (tiles_max + tps - 1) / tps;
-      if (!A.dense && tps * kTile > kSlotsLds) continue;   // index slots must fit in LDS
-      const double wgs = (double)rows * L.n_hg * s_eff;
-      const int rounds = (int)((wgs + 255) / 256);
-      const double cost = rounds * tps * t_tile + (s_eff > 1 ? t_merge + t_part * rows * L.n_hg * s_eff : 0.0);
-      if (cost < best - 1e-9) { best = cost; best_s = s_eff; }
+    for (int variant = 0; variant < 3; ++variant) {
+      // 0: 32-head workgroups (32 query rows at most); 1, 2: 8-wave 128-head
+      // workgroups with row norms from the gathered tiles / from the pre-pass
+      const bool hg = variant == 0;
+      const bool pre = variant == 2;
+      if (hg && (A.heads % 32 != 0 || rows > 32)) continue;
+      if (!hg && A.heads % 128 != 0) continue;
+      const int wg_heads = hg ? 32 : 128;
+      const int n_hg = A.heads / wg_heads;
+      // (the 8-wave kernel gathers only ~1.5 tiles ahead: on rows scattered over HBM,
+      // as in sparse decode, it waits on memory)
+      const double t_tile = hg ? 2.5 : (pre ? 2.4 : (A.dense ? 3.0 : 5.0));
+      // the pre-pass reads every cached row once (~5 TB/s)
+      const double t_norms = pre ? 3.0 + (double)A.batch * ((double)A.kv_cap + A.raw_cap) * (kD * 2) / 5.0e6 : 0.0;
+      for (int sp = 1; sp <= kMaxSplit && sp <= tiles_max; ++sp) {
+        const int tps = (tiles_max + sp - 1) / sp;
+        const int s_eff = (tiles_max + tps - 1) / tps;
+        if (!A.dense && tps * kTile > kSlotsLds) continue;   // index slots must fit in LDS
+        const double wgs = (double)rows * n_hg * s_eff;
+        const double rounds = std::ceil(wgs / 256.0);
+        const double part_mb = s_eff > 1 ? wgs * wg_heads * kD * 4.0 / 1.0e6 : 0.0;
+        // start-up: first gathers, and the workgroup's partial (256 KB for 128 heads)
+        // leaving through one CU
+        const double t_start = hg ? 9.0 : (s_eff > 1 ? 13.0 : 4.0);
+        const double cost = t_norms + rounds * (t_start + tps * t_tile) + (s_eff > 1 ? 4.0 + part_mb / 2.0 : 0.0);
+        if (cost < best - 1e-9) {
+          best = cost;
+          L.kind = hg ? 2 : 3;
+          L.pre = pre ? 1 : 0;
+          L.n_hg = n_hg;
+          L.nw = hg ? kHgWaves : kW8Waves;
+          L.ips = tps * kTile;
+          L.nsplit = s_eff;
+        }
+      }
     }
-    const int tps = (tiles_max + best_s - 1) / best_s;
-    L.ips = tps * kTile;
-    L.nsplit = (tiles_max + tps - 1) / tps;
-    if (!A.dense && L.ips > kSlotsLds) L.kind = 0;
   }
   if (L.kind == 0) {
     L.nw = (A.heads % 64 == 0) ? 4 : ((A.heads % 32 == 0) ? 2 : 1);
@@ -1228,7 +1369,7 @@ static size_t partial_bytes(const MqaArgs& A, const MqaLaunch& L) {
 
 // Row norms of the full-dim kernel: [batch, kv_cap] then [batch, raw_cap] fp32.
 static size_t norm_bytes(const MqaArgs& A, const MqaLaunch& L) {
-  if (L.kind != 1) return 0;
+  if (!(L.kind == 3 && L.pre)) return 0;
   return r256((size_t)A.batch * A.kv_cap * sizeof(float)) + r256((size_t)A.batch * A.raw_cap * sizeof(float));
 }
 
@@ -1291,10 +1432,14 @@ hipError_t launch_mqa(const MqaArgs& A, void* ws, size_t ws_bytes, hipStream_t s
   if (lds > (size_t)kMaxDynLds) return hipErrorInvalidValue;
   const long groups = ((long)L.units + 7) / 8;
   dim3 grid((unsigned)(groups * 8 * L.n_hg));
+  if (L.kind == 3) grid = dim3((unsigned)((((long)L.units * L.n_hg + 7) / 8) * 8));
   {
-    LaunchTimer timer(L.kind == 2 ? "mqa_bf16_hg" : (L.kind == 1 ? "mqa_bf16_h32" : "mqa_bf16_h16"), s);
-    if (L.kind == 2) mqa_hg_kernel<<<grid, kHgWaves * 64, lds, s>>>(A, L, part_o, part_ml);
-    else if (L.kind == 1) mqa_fd_kernel<<<grid, kFdWaves * 64, lds, s>>>(A, L, part_o, part_ml, inv_kv, inv_raw);
+    LaunchTimer timer(L.kind == 3 ? "mqa_bf16_w8" : (L.kind == 2 ? "mqa_bf16_hg" : "mqa_bf16_h16"), s);
+    if (L.kind == 3 && L.pre)
+      mqa_w8_kernel<true><<<grid, kW8Waves * 64, lds, s>>>(A, L, part_o, part_ml, inv_kv, inv_raw);
+    else if (L.kind == 3)
+      mqa_w8_kernel<false><<<grid, kW8Waves * 64, lds, s>>>(A, L, part_o, part_ml, nullptr, nullptr);
+    else if (L.kind == 2) mqa_hg_kernel<<<grid, kHgWaves * 64, lds, s>>>(A, L, part_o, part_ml);
     else if (L.nw == 4) mqa_bf16_kernel<4><<<grid, 4 * 64, lds, s>>>(A, L, part_o, part_ml);
     else if (L.nw == 2) mqa_bf16_kernel<2><<<grid, 2 * 64, lds, s>>>(A, L, part_o, part_ml);
     else mqa_bf16_kernel<1><<<grid, 64, lds, s>>>(A, L, part_o, part_ml);
