@@ -169,8 +169,101 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_mfma(IndexArgs A,
   }
 }
 
+// ------------------------------------------- bf16, few queries: keys staged in LDS
+// For decode-sized query counts the scores are a stream over the index keys.  A
+// workgroup owns 256 consecutive entries: its waves bring the 64 KB of keys (and the
+// query's 64 x 128 q) into LDS with direct-to-LDS loads, each instruction 1 KB of
+// contiguous rows, so HBM sees whole lines in order.  Inside a 256-byte row the 16-byte
+// chunk c lands in slot c ^ (row % 16): the MFMA operand reads (32 rows, one chunk
+// each) then hit 16 distinct bank groups.  80 KB of LDS: two workgroups per CU.
+constexpr int kIdxLdsEntries = 256;
+
+__device__ __attribute__((aligned(16))) uint8_t g_zero_key[kIdxDim * 2];
+
+__device__ __forceinline__ void dma16(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)l, 16, 0, 0);
+}
+
+template <int HB>
+__global__ __launch_bounds__(kIdxWaves * 64) void index_scores_lds(IndexArgs A, float* scores) {
+  constexpr int H = HB * 32;
+  constexpr int RB = kIdxDim * 2;                                   // 256-byte rows
+  constexpr int TPW = kIdxLdsEntries / (32 * kIdxWaves);            // tiles per wave
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds[kIdxLdsEntries * RB];
+  __shared__ __attribute__((aligned(16))) uint8_t q_lds[H * RB];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = lane >> 5, col = lane & 31;
+  const int b = blockIdx.z;
+  const int qi = blockIdx.y;
+  const long row = (long)b * A.n_q + qi;
+  const int e0 = blockIdx.x * kIdxLdsEntries;
+  const int ne = min(A.n_entries[b], A.n_max);
+
+  // ---- loads: lane l of a 1 KB instruction fills row 4 j + l / 16, slot l % 16
+  const int r_in = lane >> 4, slot = lane & 15;
+  {
+    const uint8_t* kb = (const uint8_t*)A.k + (long)b * A.k_cap * RB;
+#pragma unroll
+    for (int j = 0; j < 8 * TPW; ++j) {
+      const int r = 32 * TPW * wave + 4 * j + r_in;
+      const int e = e0 + r;
+      const uint8_t* src = e < ne ? kb + (long)e * RB + 16 * (slot ^ (r & 15)) : g_zero_key;
+      dma16(src, k_lds + (32 * TPW * wave + 4 * j) * RB);
+    }
+    const uint8_t* qg = (const uint8_t*)A.q + row * H * RB;
+#pragma unroll
+    for (int j = 0; j < H / 16; ++j) {   // H / 4 instructions over the 4 waves
+      const int hd = (H / 4) * wave + 4 * j + r_in;
+      dma16(qg + (long)hd * RB + 16 * (slot ^ (hd & 15)), q_lds + ((H / 4) * wave + 4 * j) * RB);
+    }
+  }
+  // head weights of this lane's accumulator rows: head 32 hb + 8 (r / 4) + 4 half + r % 4
+  f32x4_t wl[HB][4];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) wl[hb][g] = *(const f32x4_t*)(A.w + row * H + 32 * hb + 8 * g + 4 * half);
+  const int V = visible_entries(A.q_pos[row], ne, A.m);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // this wave's loads are in LDS
+  __syncthreads();
+
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int r = 32 * (TPW * wave + t) + col;   // this lane's entry (B column)
+    const int e = e0 + r;
+    float part = 0.f;
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      const int hd = 32 * hb + col;              // this lane's head (A row)
+      f32x16_t acc = {};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const int c = 2 * ks + half;
+        const uint4 a4 = *(const uint4*)(q_lds + hd * RB + 16 * (c ^ (hd & 15)));
+        const uint4 b4 = *(const uint4*)(k_lds + r * RB + 16 * (c ^ (r & 15)));
+        acc = mfma32x32x16(as_bf16x8(a4), as_bf16x8(b4), acc);
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) part = fmaf(wl[hb][g][k], fmaxf(acc[4 * g + k], 0.f), part);
+    }
+    part += __shfl_xor(part, 32, 64);
+    if (half == 0 && e < A.n_max) scores[row * A.n_max + e] = (e < V) ? part : -INFINITY;
+  }
+}
+
 template <int HB, bool FP4>
 static void launch_mfma_hb(const IndexArgs& A, float* scores, hipStream_t s) {
+  if (!FP4 && A.n_q < 64) {   // few queries: one query per workgroup, keys through LDS
+    dim3 grid((A.n_max + kIdxLdsEntries - 1) / kIdxLdsEntries, A.n_q, A.batch);
+    LaunchTimer timer("index_scores_bf16", s);
+    index_scores_lds<HB><<<grid, kIdxWaves * 64, 0, s>>>(A, scores);
+    return;
+  }
   constexpr int TPW = 2;
   const int chunk = kIdxWaves * TPW * 32;
   const int q_tile = A.n_q >= 64 ? 16 : 1;
