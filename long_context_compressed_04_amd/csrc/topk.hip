@@ -26,6 +26,8 @@
 // selects among the candidates.  If the sample's threshold passes fewer than k keys
 // or more than kCandCap, that row is selected straight from its scores in global
 // memory (exact, slower).
+#include <type_traits>
+
 #include "csa_device.hpp"
 #include "csa_kernels.hpp"
 #include "launch_timer.hpp"
@@ -68,24 +70,56 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+// Cross-lane steps on DPP (data-parallel primitives: a VALU operand read from another
+// lane of the same 16-lane row, a few cycles) rather than LDS permutes.
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowRor1 = 0x121, kDppRowRor2 = 0x122, kDppRowRor4 = 0x124, kDppRowRor8 = 0x128;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+// v of lane src(CTRL) for lanes in ROW_MASK rows, 0 elsewhere and for lanes with no source
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp0(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, true);
+}
+
+// Inclusive prefix sum over the 64 lanes: within rows by shifts 1, 2, 4, 8, then row
+// totals carried across rows (lane 15 into rows 1 and 3, lane 31 into rows 2 and 3).
 __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = (uint32_t)__shfl_up((int)v, o, 64);
-    if (lane >= o) v += y;
-  }
+  v += dpp0<kDppRowShr1>(v);
+  v += dpp0<kDppRowShr2>(v);
+  v += dpp0<kDppRowShr4>(v);
+  v += dpp0<kDppRowShr8>(v);
+  v += dpp0<kDppRowBcast15, 0xA>(v);
+  v += dpp0<kDppRowBcast31, 0xC>(v);
   return v;
 }
 
-// Block-wide min and max of one key pair per thread (barriers inside).
+// Minimum and maximum over the 64 lanes (uniform results): within rows by rotations,
+// then over the four row results.
+__device__ __forceinline__ void wave_minmax(uint32_t& mn, uint32_t& mx) {
+  auto ror = [](uint32_t v, auto CTRL) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, decltype(CTRL)::value, 0xF, 0xF, false);
+  };
+  mn = min(mn, ror(mn, std::integral_constant<int, kDppRowRor1>{}));
+  mx = max(mx, ror(mx, std::integral_constant<int, kDppRowRor1>{}));
+  mn = min(mn, ror(mn, std::integral_constant<int, kDppRowRor2>{}));
+  mx = max(mx, ror(mx, std::integral_constant<int, kDppRowRor2>{}));
+  mn = min(mn, ror(mn, std::integral_constant<int, kDppRowRor4>{}));
+  mx = max(mx, ror(mx, std::integral_constant<int, kDppRowRor4>{}));
+  mn = min(mn, ror(mn, std::integral_constant<int, kDppRowRor8>{}));
+  mx = max(mx, ror(mx, std::integral_constant<int, kDppRowRor8>{}));
+  uint32_t a = mn, c = mx;
+  mn = min(min((uint32_t)__builtin_amdgcn_readlane((int)a, 0), (uint32_t)__builtin_amdgcn_readlane((int)a, 16)),
+           min((uint32_t)__builtin_amdgcn_readlane((int)a, 32), (uint32_t)__builtin_amdgcn_readlane((int)a, 48)));
+  mx = max(max((uint32_t)__builtin_amdgcn_readlane((int)c, 0), (uint32_t)__builtin_amdgcn_readlane((int)c, 16)),
+           max((uint32_t)__builtin_amdgcn_readlane((int)c, 32), (uint32_t)__builtin_amdgcn_readlane((int)c, 48)));
+}
+
+// Block-wide min and max of one key pair per thread (uniform results; one barrier:
+// sh.red is next written only after later barriers).
 __device__ __forceinline__ void block_minmax(uint32_t& kmin, uint32_t& kmax, SelShared& sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
-  }
+  wave_minmax(kmin, kmax);
   if (lane == 0) {
     sh.red[wave] = kmin;
     sh.red[kTW + wave] = kmax;
@@ -93,14 +127,7 @@ __device__ __forceinline__ void block_minmax(uint32_t& kmin, uint32_t& kmax, Sel
   __syncthreads();
   kmin = lane < kTW ? sh.red[lane] : 0xffffffffu;
   kmax = lane < kTW ? sh.red[kTW + lane] : 0u;
-#pragma unroll
-  for (int o = kTW / 2; o >= 1; o >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
-  }
-  kmin = (uint32_t)__builtin_amdgcn_readfirstlane((int)kmin);
-  kmax = (uint32_t)__builtin_amdgcn_readfirstlane((int)kmax);
-  __syncthreads();
+  wave_minmax(kmin, kmax);
 }
 
 // One radix pass's threshold digit.  Wave 0 scans the 2048-bin histogram from the
@@ -402,16 +429,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t float_rsrc(const float* p, int
   return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, n_valid * 4, 0x00020000);
 }
 
-// One row of V <= KPT * 1024 scores, held in registers.
+// One row of V <= KPT * 1024 scores, held in registers (key[] loaded by load_row).
 template <int KPT>
-__device__ __forceinline__ void select_reg_row(const float* src, int V, int k, int32_t* oi, float* os,
-                                               SelShared& sh) {
-  const __amdgpu_buffer_rsrc_t rs = float_rsrc(src, V);
-  uint32_t key[KPT];
+__device__ __forceinline__ void load_row(const float* src, int n, uint32_t (&key)[KPT]) {
+  const __amdgpu_buffer_rsrc_t rs = float_rsrc(src, n);
 #pragma unroll
   for (int j = 0; j < KPT; ++j)
     key[j] = order_key(
         __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (int)threadIdx.x * 4, j * kTopkThreads * 4, 0)));
+}
+
+template <int KPT>
+__device__ __forceinline__ void select_reg_row(uint32_t (&key)[KPT], int V, int k, int32_t* oi, float* os,
+                                               SelShared& sh) {
   uint32_t prefix, mask, need;
   reg_threshold<KPT>(key, V, (uint32_t)k, sh, prefix, mask, need);
   auto idx_of = [](int j) { return kTopkThreads * j + (int)threadIdx.x; };
@@ -424,16 +454,20 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(IndexArgs A, co
                                                                  float* out_score) {
   __shared__ SelShared sh;
   const long row = blockIdx.x;
+  const float* src = scores + row * A.n_max;
+  // the row's scores are requested before the visible count arrives (positions past
+  // it are never counted)
+  uint32_t key[KPT];
+  load_row<KPT>(src, A.n_max, key);
   const int V = row_visible(A, row);
   const int k = A.topk;
-  const float* src = scores + row * A.n_max;
   int32_t* oi = out_idx + row * k;
   float* os = out_score ? out_score + row * k : nullptr;
   if (V <= k) {
     take_all(src, V, k, oi, os);
     return;
   }
-  select_reg_row<KPT>(src, V, k, oi, os, sh);
+  select_reg_row<KPT>(key, V, k, oi, os, sh);
 }
 
 // ---- long rows, launch 1: the threshold from a fixed sample of the row
@@ -528,7 +562,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_candidates_kernel(IndexArgs
     return;
   }
   if (V <= kRegKeys) {
-    select_reg_row<kMaxKpt>(src, V, k, oi, os, sh);
+    uint32_t key[kMaxKpt];
+    load_row<kMaxKpt>(src, V, key);
+    select_reg_row<kMaxKpt>(key, V, k, oi, os, sh);
     return;
   }
   // chunk offsets (exclusive scan of the per-chunk counts, one wave)
