@@ -256,12 +256,122 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_lds(IndexArgs A, 
   }
 }
 
+// ------------------------------------------ bf16, many queries (prefill)
+// A workgroup owns 256 consecutive entries (keys in registers, B operands, loaded
+// once) and kIdxPfQueries consecutive queries.  The next query's q (64 x 128, rows
+// swizzled as above) and head weights are loaded into the other half of a double
+// buffer by direct-to-LDS loads while this query's scores are formed: one barrier per
+// query.  Each q fragment read from LDS feeds the MFMAs of both key tiles.
+constexpr int kIdxPfQueries = 64;
+
+__device__ __forceinline__ void dma4(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)l, 4, 0, 0);
+}
+
+template <int HB>
+__global__ __launch_bounds__(kIdxWaves * 64) void index_scores_pf(IndexArgs A, float* scores) {
+  constexpr int H = HB * 32;
+  constexpr int RB = kIdxDim * 2;
+  constexpr int TPW = 2;
+  constexpr int QI = H / 16;   // q loads per wave per query (1 KB = 4 heads each)
+  __shared__ __attribute__((aligned(16))) uint8_t q_lds[2][H * RB];
+  __shared__ __attribute__((aligned(16))) float w_lds[2][H];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = lane >> 5, col = lane & 31;
+  const int b = blockIdx.z;
+  const int wave0 = blockIdx.x * (kIdxWaves * TPW * 32) + wave * TPW * 32;
+  const int ne = min(A.n_entries[b], A.n_max);
+  const int q_begin = blockIdx.y * kIdxPfQueries;
+  const int q_end = min(A.n_q, q_begin + kIdxPfQueries);
+  const int r_in = lane >> 4, slot = lane & 15;
+
+  // q of query qi (and, from wave 0, its head weights) into buffer bi
+  auto load_q = [&](int qi, int bi) {
+    const long row = (long)b * A.n_q + qi;
+    const uint8_t* qg = (const uint8_t*)A.q + row * H * RB;
+#pragma unroll
+    for (int j = 0; j < QI; ++j) {
+      const int hd = (H / 4) * wave + 4 * j + r_in;
+      dma16(qg + (long)hd * RB + 16 * (slot ^ (hd & 15)), q_lds[bi] + ((H / 4) * wave + 4 * j) * RB);
+    }
+    if (wave == 0) {
+#pragma unroll
+      for (int j = 0; j < H; j += 64)
+        if (j + lane < H) dma4(A.w + row * H + j + lane, w_lds[bi] + j);
+    }
+  };
+  if (q_begin < q_end) load_q(q_begin, 0);
+
+  // ---- keys for this wave's TPW tiles (registers, B operands)
+  uint4 kb[TPW][8];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int e = wave0 + t * 32 + col;
+    const bool ok = e < ne;
+    const uint16_t* kr = (const uint16_t*)A.k + ((long)b * A.k_cap + (ok ? e : 0)) * kIdxDim;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) kb[t][ks] = ok ? *(const uint4*)(kr + 16 * ks + 8 * half) : make_uint4(0, 0, 0, 0);
+  }
+
+  for (int qi = q_begin; qi < q_end; ++qi) {
+    const int bi = (qi - q_begin) & 1;
+    const long row = (long)b * A.n_q + qi;
+    const int V = visible_entries(A.q_pos[row], ne, A.m);
+    // this wave's loads of query qi have landed (the keys, issued later, may not have:
+    // the wait covers them too on the first query)
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();   // every wave's, and every wave is past query qi - 1
+    if (qi + 1 < q_end) load_q(qi + 1, bi ^ 1);
+    const uint8_t* qb = q_lds[bi];
+    float part[TPW] = {};
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      const int hd = 32 * hb + col;
+      f32x16_t acc[TPW];
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) acc[t] = f32x16_t{};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const int c = 2 * ks + half;
+        const uint4 a4 = *(const uint4*)(qb + hd * RB + 16 * (c ^ (hd & 15)));
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) acc[t] = mfma32x32x16(as_bf16x8(a4), as_bf16x8(kb[t][ks]), acc[t]);
+      }
+      // head 32 hb + 8 (r / 4) + 4 half + r % 4 of accumulator row r
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4_t wv = *(const f32x4_t*)&w_lds[bi][32 * hb + 8 * g + 4 * half];
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) part[t] = fmaf(wv[k], fmaxf(acc[t][4 * g + k], 0.f), part[t]);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const float p = part[t] + __shfl_xor(part[t], 32, 64);
+      const int e = wave0 + t * 32 + col;
+      if (half == 0 && e < A.n_max) scores[row * A.n_max + e] = (e < V) ? p : -INFINITY;
+    }
+  }
+}
+
 template <int HB, bool FP4>
 static void launch_mfma_hb(const IndexArgs& A, float* scores, hipStream_t s) {
   if (!FP4 && A.n_q < 64) {   // few queries: one query per workgroup, keys through LDS
     dim3 grid((A.n_max + kIdxLdsEntries - 1) / kIdxLdsEntries, A.n_q, A.batch);
     LaunchTimer timer("index_scores_bf16", s);
     index_scores_lds<HB><<<grid, kIdxWaves * 64, 0, s>>>(A, scores);
+    return;
+  }
+  if (!FP4) {   // many queries: keys in registers, q double-buffered in LDS
+    dim3 grid((A.n_max + kIdxLdsEntries - 1) / kIdxLdsEntries, (A.n_q + kIdxPfQueries - 1) / kIdxPfQueries,
+              A.batch);
+    LaunchTimer timer("index_scores_bf16", s);
+    index_scores_pf<HB><<<grid, kIdxWaves * 64, 0, s>>>(A, scores);
     return;
   }
   constexpr int TPW = 2;

@@ -103,6 +103,9 @@ def _oracle_scores(qv, kv, w, n_entries, q_pos, m, b, i):
     ("bf16", 2, 2, 32, 128, 333, 4, 16),
     ("bf16", 1, 2, 128, 128, 257, 4, 300),        # V < k for some rows
     ("mxfp4", 2, 1, 64, 128, 2500, 4, 128),
+    ("bf16", 1, 70, 64, 128, 700, 4, 64),         # many queries: two query tiles, the second ragged
+    ("bf16", 2, 66, 128, 128, 300, 4, 32),
+    ("mxfp4", 1, 65, 64, 128, 600, 4, 64),
 ])
 def test_index_scores_and_topk(dtype, B, n_q, HI, dI, N, m, k):
     q, kk, w, n_entries, q_pos = _index_case(dtype, B, n_q, HI, dI, N, N + 40, m, seed=HI + N)
