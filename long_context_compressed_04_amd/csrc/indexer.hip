@@ -316,6 +316,18 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_pf(IndexArgs A, f
     for (int ks = 0; ks < 8; ++ks) kb[t][ks] = ok ? *(const uint4*)(kr + 16 * ks + 8 * half) : make_uint4(0, 0, 0, 0);
   }
 
+  // A query's scores are stored one step later, after the next q loads are issued, so
+  // that the wait for those loads (which counts stores too) finds the stores done.
+  float held[TPW];
+  long held_row = -1;
+  int held_V = 0;
+  auto store_held = [&]() {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int e = wave0 + t * 32 + col;
+      if (half == 0 && e < A.n_max) scores[held_row * A.n_max + e] = (e < held_V) ? held[t] : -INFINITY;
+    }
+  };
   for (int qi = q_begin; qi < q_end; ++qi) {
     const int bi = (qi - q_begin) & 1;
     const long row = (long)b * A.n_q + qi;
@@ -325,6 +337,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_pf(IndexArgs A, f
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();   // every wave's, and every wave is past query qi - 1
     if (qi + 1 < q_end) load_q(qi + 1, bi ^ 1);
+    if (held_row >= 0) store_held();
     const uint8_t* qb = q_lds[bi];
     float part[TPW] = {};
 #pragma unroll
@@ -351,12 +364,11 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_pf(IndexArgs A, f
       }
     }
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      const float p = part[t] + __shfl_xor(part[t], 32, 64);
-      const int e = wave0 + t * 32 + col;
-      if (half == 0 && e < A.n_max) scores[row * A.n_max + e] = (e < V) ? p : -INFINITY;
-    }
+    for (int t = 0; t < TPW; ++t) held[t] = part[t] + __shfl_xor(part[t], 32, 64);
+    held_row = row;
+    held_V = V;
   }
+  if (held_row >= 0) store_held();
 }
 
 template <int HB, bool FP4>
