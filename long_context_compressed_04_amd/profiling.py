@@ -28,7 +28,7 @@ CSRC = os.path.join(PKG, "csrc")
 
 # library launch-timer name -> (regex on the demangled kernel name, source file)
 KERNELS = {
-    "index_scores_bf16": (r"index_scores_mfma<\d+, false", "indexer.hip"),
+    "index_scores_bf16": (r"index_scores_(mfma<\d+, false|lds<|pf<)", "indexer.hip"),
     "index_scores_mxfp4": (r"index_scores_mfma<\d+, true", "indexer.hip"),
     "index_scores_f32": (r"index_scores_f32", "indexer.hip"),
     "topk": (r"topk_", "topk.hip"),
