@@ -227,7 +227,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_lds(IndexArgs A, 
 #pragma unroll
     for (int g = 0; g < 4; ++g) wl[hb][g] = *(const f32x4_t*)(A.w + row * H + 32 * hb + 8 * g + 4 * half);
   const int V = visible_entries(A.q_pos[row], ne, A.m);
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // this wave's loads are in LDS
+  wait_vmcnt<0>();   // this wave's loads are in LDS
   __syncthreads();
 
 #pragma unroll
@@ -334,7 +334,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_pf(IndexArgs A, f
     const int V = visible_entries(A.q_pos[row], ne, A.m);
     // this wave's loads of query qi have landed (the keys, issued later, may not have:
     // the wait covers them too on the first query)
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    wait_vmcnt<0>();
     __syncthreads();   // every wave's, and every wave is past query qi - 1
     if (qi + 1 < q_end) load_q(qi + 1, bi ^ 1);
     if (held_row >= 0) store_held();

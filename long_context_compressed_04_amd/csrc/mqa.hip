@@ -695,8 +695,8 @@ void mqa_hg_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml) {
     constexpr int BUF = decltype(BUFC)::value;
     uint8_t* const tile = BUF == 0 ? tb0 : (BUF == 1 ? tb1 : tb2);
     // this wave's rows of tile ti have landed (tile ti+1's may still be in flight)
-    if (ti + 1 < n_tiles) __builtin_amdgcn_s_waitcnt(0x0F70 | kHgRpw);
-    else __builtin_amdgcn_s_waitcnt(0x0F70);
+    if (ti + 1 < n_tiles) wait_vmcnt<kHgRpw>();
+    else wait_vmcnt<0>();
     // ---- 1/rms of the rows this wave staged (written for the other waves)
     {
       float part[kHgRpw];
@@ -1113,10 +1113,10 @@ void mqa_w8_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml, const 
     // this wave's loads of tile ti + 1 are done (those of tile ti + 2 may be in flight);
     // after the barrier every wave's are, and every wave's P of tile ti is in LDS
     if (ti + 2 < n_tiles) {
-      if (PRE && wave == 0) __builtin_amdgcn_s_waitcnt(0x0F70 | (kW8Rpw + 1));
-      else __builtin_amdgcn_s_waitcnt(0x0F70 | kW8Rpw);
+      if (PRE && wave == 0) wait_vmcnt<kW8Rpw + 1>();
+      else wait_vmcnt<kW8Rpw>();
     } else {
-      __builtin_amdgcn_s_waitcnt(0x0F70);
+      wait_vmcnt<0>();
     }
     lds_barrier();
     // ---- O^T[128 dq .. + 128 dims x 64 heads] += V^T . P^T
@@ -1148,10 +1148,10 @@ void mqa_w8_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml, const 
   };
   // tile 0 in LDS (tile 1 may be in flight)
   if (n_tiles > 1) {
-    if (PRE && wave == 0) __builtin_amdgcn_s_waitcnt(0x0F70 | (kW8Rpw + 1));
-    else __builtin_amdgcn_s_waitcnt(0x0F70 | kW8Rpw);
+    if (PRE && wave == 0) wait_vmcnt<kW8Rpw + 1>();
+    else wait_vmcnt<kW8Rpw>();
   } else {
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    wait_vmcnt<0>();
   }
   lds_barrier();
   auto run = [&](auto DHC) {
