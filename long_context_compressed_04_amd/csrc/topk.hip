@@ -39,7 +39,7 @@ constexpr int kTW = kTopkThreads / 64;
 constexpr int kRegKeys = 16384;       // direct path: the whole row in registers (16 keys per thread)
 constexpr int kMaxKpt = kRegKeys / kTopkThreads;
 constexpr int kCandCap = 16384;       // long rows: candidates kept for the exact selection
-constexpr int kSample = 8192;         // long rows: keys in the threshold sample
+constexpr int kSample = 4096;         // long rows: keys in the threshold sample
 constexpr int kChunk = 4096;          // long rows: keys per filter workgroup
 constexpr int kFilterThreads = 256;
 constexpr int kMaxChunks = 2048;
@@ -544,13 +544,41 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(IndexArgs A
   if (threadIdx.x == 0) L.counts[row * L.chunks + c] = total;
 }
 
+// Exact selection among the M candidates of a long row (KPT * 1024 >= M): candidate c
+// sits in the chunk whose offset range holds it; its position in the row comes along.
+template <int KPT>
+__device__ __forceinline__ void select_candidates(const uint32_t* gk, const int32_t* gi, const uint32_t* coff,
+                                                  int nch, int M, int k, int32_t* cand_idx, int32_t* oi,
+                                                  float* os, SelShared& sh) {
+  uint32_t key[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int c = kTopkThreads * j + (int)threadIdx.x;
+    key[j] = 0u;
+    if (c < M) {
+      int lo = 0, hi = nch - 1;   // chunk holding candidate c: last chunk whose offset is <= c
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (coff[mid] <= (uint32_t)c) lo = mid;
+        else hi = mid - 1;
+      }
+      const long src_pos = (long)lo * kChunk + (c - (int)coff[lo]);
+      key[j] = gk[src_pos];
+      cand_idx[c] = gi[src_pos];
+    }
+  }
+  uint32_t prefix, mask, need;
+  reg_threshold<KPT>(key, M, (uint32_t)k, sh, prefix, mask, need);   // (its barriers publish cand_idx)
+  auto idx_of = [&](int j) { return cand_idx[kTopkThreads * j + threadIdx.x]; };
+  reg_compact<KPT>(key, M, prefix, mask, need, k, idx_of, oi, os, sh);
+}
+
 // ---- long rows, launch 3: exact selection among the candidates (or the whole row)
 __global__ __launch_bounds__(kTopkThreads) void topk_candidates_kernel(IndexArgs A, const float* scores, LongWs L,
                                                                        int32_t* out_idx, float* out_score) {
   __shared__ SelShared sh;
   __shared__ uint32_t coff[kMaxChunks + 1];
   __shared__ int32_t cand_idx[kCandCap];
-  constexpr int KPT = kCandCap / kTopkThreads;
   const long row = blockIdx.x;
   const int V = row_visible(A, row);
   const int k = A.topk;
@@ -590,27 +618,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_candidates_kernel(IndexArgs
   }
   const uint32_t* gk = L.ckey + row * A.n_max;
   const int32_t* gi = L.cidx + row * A.n_max;
-  uint32_t key[KPT];
-#pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const int c = kTopkThreads * j + (int)threadIdx.x;
-    key[j] = 0u;
-    if (c < M) {
-      int lo = 0, hi = nch - 1;   // chunk holding candidate c: last chunk whose offset is <= c
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (coff[mid] <= (uint32_t)c) lo = mid;
-        else hi = mid - 1;
-      }
-      const long src_pos = (long)lo * kChunk + (c - (int)coff[lo]);
-      key[j] = gk[src_pos];
-      cand_idx[c] = gi[src_pos];
-    }
-  }
-  uint32_t prefix, mask, need;
-  reg_threshold<KPT>(key, M, (uint32_t)k, sh, prefix, mask, need);   // (its barriers publish cand_idx)
-  auto idx_of = [&](int j) { return cand_idx[kTopkThreads * j + threadIdx.x]; };
-  reg_compact<KPT>(key, M, prefix, mask, need, k, idx_of, oi, os, sh);
+  // as few registers per thread as the candidate count allows
+  if (M <= 4 * kTopkThreads) select_candidates<4>(gk, gi, coff, nch, M, k, cand_idx, oi, os, sh);
+  else if (M <= 8 * kTopkThreads) select_candidates<8>(gk, gi, coff, nch, M, k, cand_idx, oi, os, sh);
+  else select_candidates<kCandCap / kTopkThreads>(gk, gi, coff, nch, M, k, cand_idx, oi, os, sh);
 }
 
 static int long_chunks(const IndexArgs& A) { return (A.n_max + kChunk - 1) / kChunk; }
