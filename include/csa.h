@@ -180,6 +180,34 @@ csa_status csa_index_topk(const csa_index_desc* desc, const void* q_idx, const u
                           float* out_score, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------
+ * csa_index_topk_rescored -- the MXFP4 selector as a prefilter, then an exact
+ * rescoring (the pages' FP4 QK selector: forum post on the DeepSeek V4 paper;
+ * techniques map, "FP4 precision for the attention indexer"; the pages give no
+ * rescoring step: this is a labelled variant that trades one small gather for
+ * selection recall).  Per query:
+ *   1. the `cand` best visible entries by the MXFP4 score (as csa_index_topk with
+ *      topk = cand; q_idx / k_idx and their scales as there);
+ *   2. each candidate's score recomputed with the bf16 indexer from q_bf16 and
+ *      k_bf16, bf16 copies of the same queries and keys (same formula, fp32
+ *      accumulation);
+ *   3. the desc->topk best rescored candidates (ties to the lower entry index),
+ *      written in ascending index order, -1 padded when fewer than topk are
+ *      visible; out_score (nullable) receives their rescored scores.
+ *   desc     dtype CSA_MXFP4, idx_dim 128, idx_heads in {32, 64, 96, 128}
+ *   cand     desc->topk <= cand <= 8192
+ *   q_bf16   [batch, n_q, idx_heads, 128] bf16, 16-byte aligned
+ *   k_bf16   [batch, k_cap, 128] bf16, 16-byte aligned
+ * The workspace (csa_index_rescored_workspace_size) holds the MXFP4 score rows, the
+ * candidate lists and their rescored scores.
+ * ---------------------------------------------------------------------------- */
+size_t csa_index_rescored_workspace_size(const csa_index_desc* desc, int32_t cand);
+csa_status csa_index_topk_rescored(const csa_index_desc* desc, int32_t cand, const void* q_idx,
+                                   const uint8_t* q_scale, const void* q_bf16, const float* w,
+                                   const void* k_idx, const uint8_t* k_scale, const void* k_bf16,
+                                   const int32_t* n_entries, const int32_t* q_pos, int32_t* out_idx,
+                                   float* out_score, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------
  * Core multi-query attention ("DeepSeek-V4-Pro" techniques map, "Grouped-query
  * attention", "Sliding-window attention", "QK normalization"; anthology record,
  * Key takeaways: RMSNorm on every query head and on the compressed KV head).

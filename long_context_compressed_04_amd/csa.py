@@ -84,6 +84,10 @@ def lib():
         L.csa_index_scores.restype = S
         L.csa_index_topk.argtypes = [ctypes.POINTER(IndexDesc)] + [V] * 9 + [V, Z, V]
         L.csa_index_topk.restype = S
+        L.csa_index_rescored_workspace_size.argtypes = [ctypes.POINTER(IndexDesc), ctypes.c_int32]
+        L.csa_index_rescored_workspace_size.restype = Z
+        L.csa_index_topk_rescored.argtypes = [ctypes.POINTER(IndexDesc), ctypes.c_int32] + [V] * 11 + [V, Z, V]
+        L.csa_index_topk_rescored.restype = S
         L.csa_mqa_workspace_size.argtypes = [ctypes.POINTER(MqaDesc), ctypes.c_int32]
         L.csa_mqa_workspace_size.restype = Z
         L.csa_sparse_mqa.argtypes = [ctypes.POINTER(MqaDesc)] + [V] * 9 + [V, Z, V]
@@ -201,6 +205,23 @@ def index_topk(q_idx, w, k_idx, n_entries, q_pos, *, m, topk, n_max=None, q_scal
     ws, nb = _workspace(lib().csa_index_workspace_size(ctypes.byref(d)), dev, workspace)
     _check(lib().csa_index_topk(ctypes.byref(d), _p(q_idx), _p(q_scale), _p(w), _p(k_idx), _p(k_scale),
                                 _p(n_entries), _p(q_pos), _p(out_idx), _p(out_score), _p(ws), nb, _stream(q_idx)))
+    return out_idx, out_score
+
+
+def index_topk_rescored(q_idx, q_scale, q_bf16, w, k_idx, k_scale, k_bf16, n_entries, q_pos, *, m, topk, cand,
+                        n_max=None, workspace=None, out_idx=None, out_score=None):
+    """MXFP4 prefilter of `cand` entries, bf16 rescoring, top-k of the rescored
+    candidates: returns (idx int32 [B, n_q, topk], rescored score fp32 [B, n_q, topk])."""
+    d = _index_desc(q_idx, k_idx, m, topk, n_max, MXFP4)
+    dev = q_idx.device
+    if out_idx is None:
+        out_idx = torch.empty((d.batch, d.n_q, topk), dtype=torch.int32, device=dev)
+    if out_score is None:
+        out_score = torch.empty((d.batch, d.n_q, topk), dtype=torch.float32, device=dev)
+    ws, nb = _workspace(lib().csa_index_rescored_workspace_size(ctypes.byref(d), cand), dev, workspace)
+    _check(lib().csa_index_topk_rescored(ctypes.byref(d), cand, _p(q_idx), _p(q_scale), _p(q_bf16), _p(w),
+                                         _p(k_idx), _p(k_scale), _p(k_bf16), _p(n_entries), _p(q_pos),
+                                         _p(out_idx), _p(out_score), _p(ws), nb, _stream(q_idx)))
     return out_idx, out_score
 
 

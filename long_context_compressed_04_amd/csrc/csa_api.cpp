@@ -216,6 +216,68 @@ csa_status csa_index_topk(const csa_index_desc* d, const void* q, const uint8_t*
                     "csa_index_topk (select)");
 }
 
+// --------------------------------------------------------- MXFP4 + rescoring
+static size_t rescore_ws(const csa_index_desc* d, int32_t cand) {
+  csa_index_desc dc = *d;
+  dc.topk = cand;
+  const size_t rows = (size_t)d->batch * d->n_q;
+  return index_ws(&dc) + 2 * round256(rows * (size_t)cand * sizeof(int32_t));
+}
+
+size_t csa_index_rescored_workspace_size(const csa_index_desc* d, int32_t cand) {
+  return (d && cand >= 1) ? rescore_ws(d, cand) : 0;
+}
+
+csa_status csa_index_topk_rescored(const csa_index_desc* d, int32_t cand, const void* q, const uint8_t* qs,
+                                   const void* q16, const float* w, const void* k, const uint8_t* ks,
+                                   const void* k16, const int32_t* ne, const int32_t* qpos, int32_t* out_idx,
+                                   float* out_score, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "csa_index_topk_rescored";
+  csa_status st = check_index(fn, d, q, qs, w, k, ks, ne, qpos);
+  if (st != CSA_OK) return st;
+  if (d->dtype != CSA_MXFP4) return fail(CSA_ERR_DTYPE, "%s: the prefilter must be CSA_MXFP4", fn);
+  if (cand < d->topk || cand > 8192) return fail(CSA_ERR_SHAPE, "%s: need topk <= cand <= 8192", fn);
+  if (!out_idx || !q16 || !k16) return fail(CSA_ERR_NULL, "%s: out_idx, q_bf16 and k_bf16 are required", fn);
+  if (!aligned16(q16) || !aligned16(k16)) return fail(CSA_ERR_ALIGN, "%s: q_bf16 and k_bf16 must be 16-byte aligned", fn);
+  const size_t need = rescore_ws(d, cand);
+  if (!ws || ws_bytes < need)
+    return fail(CSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws ? ws_bytes : 0);
+  csa_index_desc dc = *d;
+  dc.topk = cand;
+  const size_t rows = (size_t)d->batch * d->n_q;
+  const size_t iws = index_ws(&dc), sws = scores_ws(&dc);
+  int32_t* cands = (int32_t*)((char*)ws + iws);
+  float* rescored = (float*)((char*)ws + iws + round256(rows * (size_t)cand * sizeof(int32_t)));
+  hipStream_t s = (hipStream_t)stream;
+  // 1. MXFP4 scores, the cand best (ascending, -1 padded)
+  csa::IndexArgs A = index_args(&dc, q, qs, w, k, ks, ne, qpos);
+  float* scores = (float*)ws;
+  st = hip_status(csa::launch_index_scores(A, scores, s), "csa_index_topk_rescored (prefilter scores)");
+  if (st != CSA_OK) return st;
+  st = hip_status(csa::launch_topk_rows(A, scores, cands, nullptr, (char*)ws + sws, iws - sws, s),
+                  "csa_index_topk_rescored (prefilter select)");
+  if (st != CSA_OK) return st;
+  // 2. bf16 scores of the candidates: slot e of a row is key cands[e]
+  csa::IndexArgs B = A;
+  B.dtype = CSA_BF16;
+  B.q = q16;
+  B.q_scale = nullptr;
+  B.k = k16;
+  B.k_scale = nullptr;
+  B.n_max = cand;
+  B.sel = cands;
+  st = hip_status(csa::launch_index_scores(B, rescored, s), "csa_index_topk_rescored (rescore)");
+  if (st != CSA_OK) return st;
+  // 3. the topk best candidates; a row holds min(cand, V) valid candidates, which is
+  //    the visible count with n_max = cand
+  csa::IndexArgs C = B;
+  C.topk = d->topk;
+  C.sel = nullptr;
+  C.map = cands;
+  return hip_status(csa::launch_topk_rows(C, rescored, out_idx, out_score, nullptr, 0, s),
+                    "csa_index_topk_rescored (select)");
+}
+
 size_t csa_mqa_workspace_size(const csa_mqa_desc* d, int32_t dense) {
   if (!d) return 0;
   csa::MqaArgs A = mqa_args(d, dense);

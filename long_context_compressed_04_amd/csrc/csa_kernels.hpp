@@ -24,6 +24,11 @@ struct IndexArgs {
   const void* q; const uint8_t* q_scale; const float* w;
   const void* k; const uint8_t* k_scale;
   const int32_t* n_entries; const int32_t* q_pos;
+  // Rescoring (bf16, few-query kernel): score slot e of row r is key row
+  // sel[r * n_max + e] (-1: masked) instead of key row e.
+  const int32_t* sel = nullptr;
+  // Top-k: the selected slot p of row r is written as map[r * n_max + p].
+  const int32_t* map = nullptr;
 };
 // Score rows [batch*n_q, n_max] (-inf past the visible count).
 hipError_t launch_index_scores(const IndexArgs& A, float* scores, hipStream_t s);

@@ -201,6 +201,14 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_lds(IndexArgs A, 
   const long row = (long)b * A.n_q + qi;
   const int e0 = blockIdx.x * kIdxLdsEntries;
   const int ne = min(A.n_entries[b], A.n_max);
+  // slot e -> key row: e itself below the visible count, or (rescoring) the listed
+  // row; -1 = masked
+  const int32_t* sel = A.sel ? A.sel + row * A.n_max : nullptr;
+  auto key_row = [&](int e) -> int {
+    if (e >= A.n_max) return -1;
+    if (sel) return sel[e];
+    return e < ne ? e : -1;
+  };
 
   // ---- loads: lane l of a 1 KB instruction fills row 4 j + l / 16, slot l % 16
   const int r_in = lane >> 4, slot = lane & 15;
@@ -209,8 +217,8 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_lds(IndexArgs A, 
 #pragma unroll
     for (int j = 0; j < 8 * TPW; ++j) {
       const int r = 32 * TPW * wave + 4 * j + r_in;
-      const int e = e0 + r;
-      const uint8_t* src = e < ne ? kb + (long)e * RB + 16 * (slot ^ (r & 15)) : g_zero_key;
+      const int kr = key_row(e0 + r);
+      const uint8_t* src = kr >= 0 ? kb + (long)kr * RB + 16 * (slot ^ (r & 15)) : g_zero_key;
       dma16(src, k_lds + (32 * TPW * wave + 4 * j) * RB);
     }
     const uint8_t* qg = (const uint8_t*)A.q + row * H * RB;
@@ -252,7 +260,8 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_lds(IndexArgs A, 
         for (int k = 0; k < 4; ++k) part = fmaf(wl[hb][g][k], fmaxf(acc[4 * g + k], 0.f), part);
     }
     part += __shfl_xor(part, 32, 64);
-    if (half == 0 && e < A.n_max) scores[row * A.n_max + e] = (e < V) ? part : -INFINITY;
+    const bool valid = sel ? key_row(e) >= 0 : e < V;
+    if (half == 0 && e < A.n_max) scores[row * A.n_max + e] = valid ? part : -INFINITY;
   }
 }
 
@@ -373,9 +382,9 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_pf(IndexArgs A, f
 
 template <int HB, bool FP4>
 static void launch_mfma_hb(const IndexArgs& A, float* scores, hipStream_t s) {
-  if (!FP4 && A.n_q < 64) {   // few queries: one query per workgroup, keys through LDS
+  if (!FP4 && (A.n_q < 64 || A.sel)) {   // few queries or rescoring: keys through LDS
     dim3 grid((A.n_max + kIdxLdsEntries - 1) / kIdxLdsEntries, A.n_q, A.batch);
-    LaunchTimer timer("index_scores_bf16", s);
+    LaunchTimer timer(A.sel ? "index_rescore_bf16" : "index_scores_bf16", s);
     index_scores_lds<HB><<<grid, kIdxWaves * 64, 0, s>>>(A, scores);
     return;
   }

@@ -415,10 +415,11 @@ __device__ __forceinline__ int row_visible(const IndexArgs& A, long row) {
   return visible_entries(A.q_pos[row], ne, A.m);
 }
 
-// V <= k: every visible entry in order, then -1.
-__device__ __forceinline__ void take_all(const float* src, int V, int k, int32_t* oi, float* os) {
+// V <= k: every visible entry in order (through map, when given), then -1.
+__device__ __forceinline__ void take_all(const float* src, int V, int k, int32_t* oi, float* os,
+                                         const int32_t* map = nullptr) {
   for (int i = threadIdx.x; i < k; i += blockDim.x) {
-    oi[i] = i < V ? i : -1;
+    oi[i] = i < V ? (map ? map[i] : i) : -1;
     if (os) os[i] = i < V ? src[i] : -INFINITY;
   }
 }
@@ -441,10 +442,13 @@ __device__ __forceinline__ void load_row(const float* src, int n, uint32_t (&key
 
 template <int KPT>
 __device__ __forceinline__ void select_reg_row(uint32_t (&key)[KPT], int V, int k, int32_t* oi, float* os,
-                                               SelShared& sh) {
+                                               SelShared& sh, const int32_t* map = nullptr) {
   uint32_t prefix, mask, need;
   reg_threshold<KPT>(key, V, (uint32_t)k, sh, prefix, mask, need);
-  auto idx_of = [](int j) { return kTopkThreads * j + (int)threadIdx.x; };
+  auto idx_of = [map](int j) {
+    const int p = kTopkThreads * j + (int)threadIdx.x;
+    return map ? map[p] : p;
+  };
   reg_compact<KPT>(key, V, prefix, mask, need, k, idx_of, oi, os, sh);
 }
 
@@ -463,11 +467,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(IndexArgs A, co
   const int k = A.topk;
   int32_t* oi = out_idx + row * k;
   float* os = out_score ? out_score + row * k : nullptr;
+  const int32_t* map = A.map ? A.map + row * A.n_max : nullptr;
   if (V <= k) {
-    take_all(src, V, k, oi, os);
+    take_all(src, V, k, oi, os, map);
     return;
   }
-  select_reg_row<KPT>(key, V, k, oi, os, sh);
+  select_reg_row<KPT>(key, V, k, oi, os, sh, map);
 }
 
 // ---- long rows, launch 1: the threshold from a fixed sample of the row
@@ -489,8 +494,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_sample_kernel(IndexArgs A, 
   uint32_t key[KPT];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) key[j] = order_key(src[(long)(kTopkThreads * j + threadIdx.x) * V / kSample]);
-  // rank in the sample expected to leave ~3k keys of the row at or above it
-  long r = ((long)3 * A.topk * kSample + V - 1) / V;
+  // rank in the sample expected to leave ~3k keys of the row at or above it, at most
+  // three quarters of the candidate capacity (a larger k keeps a smaller margin)
+  const long want = min((long)3 * A.topk, (long)kCandCap * 3 / 4);
+  long r = (want * kSample + V - 1) / V;
   r = r < 1 ? 1 : (r > kSample ? kSample : r);
   uint32_t prefix, mask, need;
   reg_threshold<KPT>(key, kSample, (uint32_t)r, sh, prefix, mask, need);

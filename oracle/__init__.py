@@ -129,6 +129,27 @@ def topk(scores, n_visible, k):
     return out
 
 
+def index_topk_rescored(q4, w, k4, q16, k16, n_visible, cand, k):
+    """MXFP4 prefilter + bf16 rescoring, a labelled variant of the FP4 QK selector
+    (forum post on the DeepSeek V4 paper; techniques map, "FP4 precision for the
+    attention indexer"; the pages give no rescoring step).  Over the first n_visible
+    entries: the `cand` best by the indexer score of the dequantised MXFP4 values
+    (q4 [H_I, d_I], k4 [n, d_I]); those candidates rescored with the bf16 values
+    (q16, k16); the k best rescored candidates, score descending then entry index
+    ascending.  Returns (idx [k] ascending, -1 padded; candidates ascending; their
+    rescored scores)."""
+    V = int(n_visible)
+    s4 = index_scores(q4, w, np.asarray(k4)[:V]) if V > 0 else np.zeros(0)
+    c = np.sort(topk(s4, V, cand))
+    c = c[c >= 0]
+    s16 = index_scores(q16, w, np.asarray(k16)[c]) if len(c) else np.zeros(0)
+    p = topk(s16, len(c), k)          # positions in c: a lower position is a lower entry
+    sel = np.sort(c[p[p >= 0]])
+    out = np.full(k, -1, dtype=np.int32)
+    out[:len(sel)] = sel
+    return out, c, s16
+
+
 def sparse_mqa(q, kv, idx, kv_raw, raw_base, t, window, scale, eps, gamma=None):
     """MQA of one query over kv[idx] (-1 skipped) plus the sliding window, one softmax.
     q [H, d]; kv [N, d]; kv_raw [W, d].  Returns (out [H, d], lse [H])."""

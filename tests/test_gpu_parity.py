@@ -136,6 +136,36 @@ def test_index_scores_and_topk(dtype, B, n_q, HI, dI, N, m, k):
             np.testing.assert_array_equal(idx[b, i], np.sort(exact[:min(k, V)]).tolist() + [-1] * (k - min(k, V)))
 
 
+@pytest.mark.parametrize("B,n_q,HI,N,k,cand", [
+    (2, 1, 64, 3000, 64, 256),
+    (1, 2, 64, 700, 100, 400),
+    (1, 1, 128, 300, 64, 4096),       # fewer visible entries than candidates
+    (1, 1, 64, 40, 64, 128),          # fewer visible entries than k
+])
+def test_index_topk_rescored(B, n_q, HI, N, k, cand):
+    """MXFP4 prefilter of `cand` entries, bf16 rescoring, top-k: the GPU set against the
+    oracle's, with the prefilter on the dequantised MXFP4 values."""
+    q, kk, w, n_entries, q_pos = _index_case("bf16", B, n_q, HI, 128, N, N + 40, 4, seed=HI + N + cand)
+    qc, qsc = csa.mxfp4_quantize(dev(q))
+    kc, ksc = csa.mxfp4_quantize(dev(kk))
+    q16, k16 = W.store(q, "bf16"), W.store(kk, "bf16")
+    idx, sc = csa.index_topk_rescored(qc, qsc, dev(q16), dev(w), kc, ksc, dev(k16), _i32(n_entries), _i32(q_pos),
+                                      m=4, topk=k, cand=cand, n_max=N)
+    idx, sc = idx.cpu().numpy(), host(sc)
+    for b in range(B):
+        k4 = oracle.mxfp4_dequantize(*oracle.mxfp4_quantize(kk[b]))
+        for i in range(n_q):
+            V = oracle.visible(q_pos[b, i], n_entries[b], 4)
+            q4 = oracle.mxfp4_dequantize(*oracle.mxfp4_quantize(q[b, i]))
+            want, cands, s16 = oracle.index_topk_rescored(q4, w[b, i], k4, W.value(q16[b, i]), W.value(k16[b]), V,
+                                                          cand, k)
+            full = np.full(V, -np.inf)
+            full[cands] = s16
+            check_topk_row(idx[b, i], full, V, k, "rescored b%d q%d" % (b, i))
+            sel = idx[b, i][idx[b, i] >= 0]
+            assert_f32_close(sc[b, i, :len(sel)], full[sel], "rescored scores")
+
+
 def test_topk_ties_and_degenerate_rows():
     """All-zero weights (every score 0), duplicated keys (exact ties), V == k, V == 0."""
     B, HI, dI, N, m = 4, 64, 128, 600, 4

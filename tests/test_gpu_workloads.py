@@ -111,6 +111,30 @@ def test_csa_decode_1m_fp4_full():
     assert_bf16_close(out, want, "out")
 
 
+def test_csa_decode_1m_fp4_rescored_recall():
+    """The labelled variant: MXFP4 prefilter of 8 x 1024 candidates, rescored with bf16
+    copies of q^I and K^I, top-1024.  The set must match the oracle's variant (tie rule)
+    and reach the recall target against the fp32 indexer."""
+    c = W.cfg4()
+    qc, qs = csa.mxfp4_quantize(dev(c["qI"][:, None]))
+    kc, ks = csa.mxfp4_quantize(dev(c["kI"]))
+    q16, k16 = W.store(c["qI"][:, None], "bf16"), W.store(c["kI"], "bf16")
+    idx, _ = csa.index_topk_rescored(qc, qs, dev(q16), dev(c["w"][:, None]), kc, ks, dev(k16), i32(c["n_entries"]),
+                                     i32(c["q_pos"][:, None]), m=4, topk=1024, cand=8192)
+    idx = idx.cpu().numpy()[0, 0]
+    q4 = oracle.mxfp4_dequantize(*oracle.mxfp4_quantize(c["qI"][0]))
+    k4 = oracle.mxfp4_dequantize(*oracle.mxfp4_quantize(c["kI"][0]))
+    want, cands, s16 = oracle.index_topk_rescored(q4, c["w"][0], k4, W.value(q16[0, 0]), W.value(k16[0]), 262144,
+                                                  8192, 1024)
+    full = np.full(262144, -np.inf)
+    full[cands] = s16
+    check_topk_row(idx, full, 262144, 1024, "rescored set vs oracle")
+    ref = oracle.topk(oracle.index_scores(c["qI"][0], c["w"][0], c["kI"][0]), 262144, 1024)
+    r = recall(idx, ref)
+    print("MXFP4 prefilter (8192) + bf16 rescoring top-1024 recall vs fp32 indexer: %.4f" % r)
+    assert r >= 0.995
+
+
 def test_csa_prefill_4k_on_60k_sampled():
     """4,096 new queries on 61,440 prior tokens: compression of the new blocks, per-query
     indexer + top-1024, MQA over top-k + window; oracle on a fixed sample of queries."""

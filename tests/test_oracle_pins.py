@@ -325,3 +325,47 @@ def test_mxfp4_error_bound_and_monotone():
     xs[-1] = max(xs[-1], 4.0)
     d = oracle.mxfp4_dequantize(*oracle.mxfp4_quantize(xs[None]))[0]
     assert np.all(np.diff(d) >= 0)
+
+
+# ------------------------------------------------- MXFP4 prefilter + bf16 rescoring
+def _rescore_case(seed, V, H=4, d=32):
+    rng = np.random.default_rng(seed)
+    q, K = rng.standard_normal((H, d)), rng.standard_normal((V, d))
+    w = rng.random(H)
+    q4 = oracle.mxfp4_dequantize(*oracle.mxfp4_quantize(q))
+    k4 = oracle.mxfp4_dequantize(*oracle.mxfp4_quantize(K))
+    return q, K, w, q4, k4
+
+
+def test_rescored_with_every_entry_a_candidate_is_the_plain_selection():
+    """cand >= V: every visible entry is rescored, so the result is the plain top-k of
+    the rescoring scores."""
+    q, K, w, q4, k4 = _rescore_case(31, 50)
+    got, cands, _ = oracle.index_topk_rescored(q4, w, k4, q, K, 50, 64, 7)
+    np.testing.assert_array_equal(cands, np.arange(50))
+    want = np.sort(oracle.topk(oracle.index_scores(q, w, K), 50, 7))
+    np.testing.assert_array_equal(got, want)
+
+
+def test_rescored_with_k_candidates_is_the_prefilter_selection():
+    """cand == k: the rescoring only reorders the prefilter's set."""
+    q, K, w, q4, k4 = _rescore_case(32, 60)
+    got, _, _ = oracle.index_topk_rescored(q4, w, k4, q, K, 60, 9, 9)
+    np.testing.assert_array_equal(got, np.sort(oracle.topk(oracle.index_scores(q4, w, k4), 60, 9)))
+
+
+@pytest.mark.parametrize("V,cand,k", [(40, 12, 5), (30, 8, 8), (6, 12, 9)])
+def test_rescored_brute_force(V, cand, k):
+    """Explicit sorts by (score desc, index asc) of explicitly summed scores."""
+    q, K, w, q4, k4 = _rescore_case(V + cand, V)
+
+    def score(qq, kk):
+        return sum(w[h] * max(0.0, float(np.dot(qq[h], kk))) for h in range(len(w)))
+
+    first = sorted(range(V), key=lambda i: (-score(q4, k4[i]), i))[:cand]
+    second = sorted(first, key=lambda i: (-score(q, K[i]), i))[:k]
+    want = sorted(second) + [-1] * (k - len(second))
+    got, cands, s16 = oracle.index_topk_rescored(q4, w, k4, q, K, V, cand, k)
+    np.testing.assert_array_equal(got, want)
+    np.testing.assert_array_equal(cands, sorted(first))
+    np.testing.assert_allclose(s16, [score(q, K[i]) for i in sorted(first)], rtol=1e-12)
