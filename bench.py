@@ -11,6 +11,9 @@ the window (RMSNorm folded in).  Other workloads (--workload):
                      (the per-step query quantisation included), top-1024, MQA
   csa_prefill_4k     4,096 new queries on 61,440 prior tokens: compression of the new
                      blocks (KV and index keys), indexer + top-1024 per query, MQA
+  csa_decode_1m_fp4_rescored
+                     csa_decode_1m_fp4 with the labelled selector variant: MXFP4
+                     prefilter of 8,192 candidates, bf16 rescoring, top-1024
 
 Inputs are seeded synthetic data resident in HBM before timing starts.  Decode
 steps cycle through replicas of every cache so that the 256 MB Infinity Cache
@@ -38,7 +41,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "mxfp4": 10100.0}
-WORKLOADS = ["csa_decode_64k", "hca_decode_1m", "csa_decode_1m_fp4", "csa_prefill_4k"]
+WORKLOADS = ["csa_decode_64k", "hca_decode_1m", "csa_decode_1m_fp4", "csa_prefill_4k", "csa_decode_1m_fp4_rescored"]
 CALIB_BYTES = 256 << 20
 
 
@@ -288,6 +291,85 @@ class CsaDecode1mFp4(Step):
                           "top-1024, MQA over 1,152 rows x 128 heads), fp64, single thread, %.1f s" % (n, secs)}
 
 
+class CsaDecode1mFp4Rescored(CsaDecode1mFp4):
+    """The labelled selector variant on the 1M FP4 workload: the MXFP4 scores pick 8,192
+    candidates, bf16 copies of q^I and K^I rescore them, the top-1024 rescored
+    candidates feed the MQA (three library calls per step)."""
+    name = "csa_decode_1m_fp4_rescored"
+    metric = ("CSA decode tokens/s at 1M context, MXFP4 prefilter + bf16 rescoring selector "
+              "(one layer, 1 sequence)")
+    cand = 8192
+
+    def __init__(self, dev, R):
+        super().__init__(dev, R)
+        torch = _torch()
+        from long_context_compressed_04_amd import workloads as W
+        c = self.c
+        q16 = to_dev(W.store(c["qI"][:, None], "bf16"), dev)
+        k16 = to_dev(W.store(c["kI"], "bf16"), dev)
+        for j, r in enumerate(self.reps):
+            r["q16"] = q16 if j == 0 else q16.clone()
+            r["k16"] = k16 if j == 0 else k16.clone()
+        self.w_dev = to_dev(c["w"][:, None], dev)
+        self.rb, self.qp, self.ne = (i32(c["raw_base"], dev), i32(c["q_pos"][:, None], dev),
+                                     i32(c["n_entries"], dev))
+        import ctypes
+        r0 = self.reps[0]
+        d = self.csa._index_desc(r0["qc"], r0["kc"], 4, self.k, None, self.csa.MXFP4)
+        self.ws_i = torch.zeros(self.csa.lib().csa_index_rescored_workspace_size(ctypes.byref(d), self.cand),
+                                dtype=torch.uint8, device=dev)
+        dm = self.csa._mqa_desc(r0["q"], r0["kv"], r0["kv_raw"], topk=self.k, window=self.w)
+        self.ws_m = torch.zeros(max(1, self.csa.lib().csa_mqa_workspace_size(ctypes.byref(dm), 0)),
+                                dtype=torch.uint8, device=dev)
+        self.idx = torch.empty((1, 1, self.k), dtype=torch.int32, device=dev)
+        self.isc = torch.empty((1, 1, self.k), dtype=torch.float32, device=dev)
+        self.out = torch.empty_like(r0["q"])
+        self.lse = torch.empty(r0["q"].shape[:3], dtype=torch.float32, device=dev)
+        self.config.update(workload=self.name, selector="mxfp4 prefilter + bf16 rescoring", candidates=self.cand)
+        self.step_bytes += self.cand * 4 + self.cand * self.dI * 2
+
+    def launch(self, i):
+        r = self.reps[i % self.replicas]
+        csa = self.csa
+        csa.mxfp4_quantize(r["qI"], r["qc"], r["qs"])
+        csa.index_topk_rescored(r["qc"], r["qs"], r["q16"], self.w_dev, r["kc"], r["ks"], r["k16"], self.ne, self.qp,
+                                m=self.m, topk=self.k, cand=self.cand, workspace=self.ws_i, out_idx=self.idx,
+                                out_score=self.isc)
+        csa.sparse_mqa(r["q"], r["kv"], self.idx, r["kv_raw"], self.rb, self.qp, window=self.w, workspace=self.ws_m,
+                       out=self.out, lse=self.lse)
+
+    def algorithmic(self, kernel):
+        if kernel == "index_rescore_bf16":
+            return "hbm", self.cand * (4 + self.dI * 2) + self.HI * self.dI * 2 + self.cand * 4
+        if kernel == "topk":   # the prefilter's and the final selection's reads and writes
+            return "hbm", self.N * 4 + self.cand * 4 + self.cand * 4 + self.k * 4
+        return super().algorithmic(kernel)
+
+    def cpu_baseline(self):
+        import oracle
+        from long_context_compressed_04_amd import workloads as W
+        c = self.c
+        q, kv, raw = W.value(c["q"][0]), W.value(c["kv"][0]), W.value(c["kv_raw"][0])
+        kc, ksc = oracle.mxfp4_quantize(c["kI"][0])
+        k_deq = oracle.mxfp4_dequantize(kc, ksc)      # at cache write, not per step
+        k16 = W.value(W.store(c["kI"][0], "bf16"))
+        q16 = W.value(W.store(c["qI"][0], "bf16"))
+        n, t0 = 0, time.perf_counter()
+        while True:
+            q_deq = oracle.mxfp4_dequantize(*oracle.mxfp4_quantize(c["qI"][0]))
+            idx, _, _ = oracle.index_topk_rescored(q_deq, c["w"][0], k_deq, q16, k16, self.N, self.cand, self.k)
+            oracle.sparse_mqa(q, kv, idx, raw, int(c["raw_base"][0]), int(c["q_pos"][0]), self.w, c["scale"],
+                              c["eps"])
+            n += 1
+            secs = time.perf_counter() - t0
+            if secs >= 10.0:
+                break
+        return {"value": round(n / secs, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                "sample": "%d whole decode steps (query quantisation, MXFP4 scores over 262,144 keys, top-8192, "
+                          "bf16 rescoring, top-1024, MQA over 1,152 rows x 128 heads), fp64, single thread, %.1f s"
+                          % (n, secs)}
+
+
 class CsaPrefill4k(Step):
     name = "csa_prefill_4k"
     metric = "CSA prefill tokens/s (4,096 new queries on 61,440 prior tokens, one layer)"
@@ -397,7 +479,7 @@ class CsaPrefill4k(Step):
 
 def make(name, dev, R):
     return {"csa_decode_64k": CsaDecode64k, "hca_decode_1m": HcaDecode1m, "csa_decode_1m_fp4": CsaDecode1mFp4,
-            "csa_prefill_4k": CsaPrefill4k}[name](dev, R)
+            "csa_prefill_4k": CsaPrefill4k, "csa_decode_1m_fp4_rescored": CsaDecode1mFp4Rescored}[name](dev, R)
 
 
 # ------------------------------------------------------------------------------------
