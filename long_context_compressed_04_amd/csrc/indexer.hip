@@ -267,11 +267,13 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_lds(IndexArgs A, 
 
 // ------------------------------------------ bf16, many queries (prefill)
 // A workgroup owns 256 consecutive entries (keys in registers, B operands, loaded
-// once) and kIdxPfQueries consecutive queries.  The next query's q (64 x 128, rows
-// swizzled as above) and head weights are loaded into the other half of a double
-// buffer by direct-to-LDS loads while this query's scores are formed: one barrier per
-// query.  Each q fragment read from LDS feeds the MFMAs of both key tiles.
+// once) and kIdxPfQueries consecutive queries, taken kIdxPfPair at a time.  The next
+// pair's q (64 x 128 each, rows swizzled as above) and head weights are loaded into
+// the other half of a double buffer by direct-to-LDS loads while this pair's scores
+// are formed: one barrier per pair.  Each q fragment read from LDS feeds the MFMAs of
+// both key tiles.
 constexpr int kIdxPfQueries = 64;
+constexpr int kIdxPfPair = 2;
 
 __device__ __forceinline__ void dma4(const void* g, void* l) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
@@ -283,9 +285,10 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_pf(IndexArgs A, f
   constexpr int H = HB * 32;
   constexpr int RB = kIdxDim * 2;
   constexpr int TPW = 2;
+  constexpr int P = kIdxPfPair;
   constexpr int QI = H / 16;   // q loads per wave per query (1 KB = 4 heads each)
-  __shared__ __attribute__((aligned(16))) uint8_t q_lds[2][H * RB];
-  __shared__ __attribute__((aligned(16))) float w_lds[2][H];
+  __shared__ __attribute__((aligned(16))) uint8_t q_lds[2][P][H * RB];
+  __shared__ __attribute__((aligned(16))) float w_lds[2][P][H];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -297,19 +300,24 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_pf(IndexArgs A, f
   const int q_end = min(A.n_q, q_begin + kIdxPfQueries);
   const int r_in = lane >> 4, slot = lane & 15;
 
-  // q of query qi (and, from wave 0, its head weights) into buffer bi
-  auto load_q = [&](int qi, int bi) {
-    const long row = (long)b * A.n_q + qi;
-    const uint8_t* qg = (const uint8_t*)A.q + row * H * RB;
+  // q of the queries q0 .. q0 + P - 1 that exist (and, from wave 0, their head
+  // weights) into buffer bi
+  auto load_q = [&](int q0, int bi) {
 #pragma unroll
-    for (int j = 0; j < QI; ++j) {
-      const int hd = (H / 4) * wave + 4 * j + r_in;
-      dma16(qg + (long)hd * RB + 16 * (slot ^ (hd & 15)), q_lds[bi] + ((H / 4) * wave + 4 * j) * RB);
-    }
-    if (wave == 0) {
+    for (int u = 0; u < P; ++u) {
+      if (q0 + u >= q_end) break;
+      const long row = (long)b * A.n_q + q0 + u;
+      const uint8_t* qg = (const uint8_t*)A.q + row * H * RB;
 #pragma unroll
-      for (int j = 0; j < H; j += 64)
-        if (j + lane < H) dma4(A.w + row * H + j + lane, w_lds[bi] + j);
+      for (int j = 0; j < QI; ++j) {
+        const int hd = (H / 4) * wave + 4 * j + r_in;
+        dma16(qg + (long)hd * RB + 16 * (slot ^ (hd & 15)), q_lds[bi][u] + ((H / 4) * wave + 4 * j) * RB);
+      }
+      if (wave == 0) {
+#pragma unroll
+        for (int j = 0; j < H; j += 64)
+          if (j + lane < H) dma4(A.w + row * H + j + lane, w_lds[bi][u] + j);
+      }
     }
   };
   if (q_begin < q_end) load_q(q_begin, 0);
@@ -325,59 +333,70 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_pf(IndexArgs A, f
     for (int ks = 0; ks < 8; ++ks) kb[t][ks] = ok ? *(const uint4*)(kr + 16 * ks + 8 * half) : make_uint4(0, 0, 0, 0);
   }
 
-  // A query's scores are stored one step later, after the next q loads are issued, so
+  // A pair's scores are stored one step later, after the next q loads are issued, so
   // that the wait for those loads (which counts stores too) finds the stores done.
-  float held[TPW];
-  long held_row = -1;
-  int held_V = 0;
+  float held[P][TPW];
+  long held_row[P];
+  int held_V[P];
+  int n_held = 0;
   auto store_held = [&]() {
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      const int e = wave0 + t * 32 + col;
-      if (half == 0 && e < A.n_max) scores[held_row * A.n_max + e] = (e < held_V) ? held[t] : -INFINITY;
+    for (int u = 0; u < P; ++u) {
+      if (u >= n_held) break;
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const int e = wave0 + t * 32 + col;
+        if (half == 0 && e < A.n_max) scores[held_row[u] * A.n_max + e] = (e < held_V[u]) ? held[u][t] : -INFINITY;
+      }
     }
   };
-  for (int qi = q_begin; qi < q_end; ++qi) {
-    const int bi = (qi - q_begin) & 1;
-    const long row = (long)b * A.n_q + qi;
-    const int V = visible_entries(A.q_pos[row], ne, A.m);
-    // this wave's loads of query qi have landed (the keys, issued later, may not have:
-    // the wait covers them too on the first query)
+  for (int q0 = q_begin; q0 < q_end; q0 += P) {
+    const int bi = ((q0 - q_begin) / P) & 1;
+    // this wave's loads of the pair have landed (the keys, issued later, may not have:
+    // the wait covers them too on the first pair)
     wait_vmcnt<0>();
-    __syncthreads();   // every wave's, and every wave is past query qi - 1
-    if (qi + 1 < q_end) load_q(qi + 1, bi ^ 1);
-    if (held_row >= 0) store_held();
-    const uint8_t* qb = q_lds[bi];
-    float part[TPW] = {};
+    __syncthreads();   // every wave's, and every wave is past the previous pair
+    if (q0 + P < q_end) load_q(q0 + P, bi ^ 1);
+    store_held();
+    n_held = 0;
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
-      const int hd = 32 * hb + col;
-      f32x16_t acc[TPW];
+    for (int u = 0; u < P; ++u) {
+      if (q0 + u >= q_end) break;
+      const long row = (long)b * A.n_q + q0 + u;
+      const int V = visible_entries(A.q_pos[row], ne, A.m);
+      const uint8_t* qb = q_lds[bi][u];
+      float part[TPW] = {};
 #pragma unroll
-      for (int t = 0; t < TPW; ++t) acc[t] = f32x16_t{};
+      for (int hb = 0; hb < HB; ++hb) {
+        const int hd = 32 * hb + col;
+        f32x16_t acc[TPW];
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const int c = 2 * ks + half;
-        const uint4 a4 = *(const uint4*)(qb + hd * RB + 16 * (c ^ (hd & 15)));
+        for (int t = 0; t < TPW; ++t) acc[t] = f32x16_t{};
 #pragma unroll
-        for (int t = 0; t < TPW; ++t) acc[t] = mfma32x32x16(as_bf16x8(a4), as_bf16x8(kb[t][ks]), acc[t]);
+        for (int ks = 0; ks < 8; ++ks) {
+          const int c = 2 * ks + half;
+          const uint4 a4 = *(const uint4*)(qb + hd * RB + 16 * (c ^ (hd & 15)));
+#pragma unroll
+          for (int t = 0; t < TPW; ++t) acc[t] = mfma32x32x16(as_bf16x8(a4), as_bf16x8(kb[t][ks]), acc[t]);
+        }
+        // head 32 hb + 8 (r / 4) + 4 half + r % 4 of accumulator row r
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4_t wv = *(const f32x4_t*)&w_lds[bi][u][32 * hb + 8 * g + 4 * half];
+#pragma unroll
+          for (int t = 0; t < TPW; ++t)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) part[t] = fmaf(wv[k], fmaxf(acc[t][4 * g + k], 0.f), part[t]);
+        }
       }
-      // head 32 hb + 8 (r / 4) + 4 half + r % 4 of accumulator row r
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4_t wv = *(const f32x4_t*)&w_lds[bi][32 * hb + 8 * g + 4 * half];
-#pragma unroll
-        for (int t = 0; t < TPW; ++t)
-#pragma unroll
-          for (int k = 0; k < 4; ++k) part[t] = fmaf(wv[k], fmaxf(acc[t][4 * g + k], 0.f), part[t]);
-      }
+      for (int t = 0; t < TPW; ++t) held[u][t] = part[t] + __shfl_xor(part[t], 32, 64);
+      held_row[u] = row;
+      held_V[u] = V;
+      n_held = u + 1;
     }
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) held[t] = part[t] + __shfl_xor(part[t], 32, 64);
-    held_row = row;
-    held_V = V;
   }
-  if (held_row >= 0) store_held();
+  store_held();
 }
 
 template <int HB, bool FP4>
