@@ -185,7 +185,8 @@ __device__ __forceinline__ void dma16(const void* g, void* l) {
                                    (__attribute__((address_space(3))) void*)l, 16, 0, 0);
 }
 
-template <int HB>
+// SEL: slot e of a row scores key row A.sel[row * n_max + e] (-1: masked) instead of e.
+template <int HB, bool SEL>
 __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_lds(IndexArgs A, float* scores) {
   constexpr int H = HB * 32;
   constexpr int RB = kIdxDim * 2;                                   // 256-byte rows
@@ -201,23 +202,26 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_lds(IndexArgs A, 
   const long row = (long)b * A.n_q + qi;
   const int e0 = blockIdx.x * kIdxLdsEntries;
   const int ne = min(A.n_entries[b], A.n_max);
-  // slot e -> key row: e itself below the visible count, or (rescoring) the listed
-  // row; -1 = masked
-  const int32_t* sel = A.sel ? A.sel + row * A.n_max : nullptr;
+  const int32_t* sel = SEL ? A.sel + row * A.n_max : nullptr;
+  // slot e -> key row: e itself below the visible count, or the listed row; -1 = masked
   auto key_row = [&](int e) -> int {
     if (e >= A.n_max) return -1;
-    if (sel) return sel[e];
+    if (SEL) return sel[e];
     return e < ne ? e : -1;
   };
 
   // ---- loads: lane l of a 1 KB instruction fills row 4 j + l / 16, slot l % 16
   const int r_in = lane >> 4, slot = lane & 15;
   {
+    // the listed rows are all read before the first key load is issued (one wait)
+    int krow[8 * TPW];
+#pragma unroll
+    for (int j = 0; j < 8 * TPW; ++j) krow[j] = key_row(e0 + 32 * TPW * wave + 4 * j + r_in);
     const uint8_t* kb = (const uint8_t*)A.k + (long)b * A.k_cap * RB;
 #pragma unroll
     for (int j = 0; j < 8 * TPW; ++j) {
       const int r = 32 * TPW * wave + 4 * j + r_in;
-      const int kr = key_row(e0 + r);
+      const int kr = krow[j];
       const uint8_t* src = kr >= 0 ? kb + (long)kr * RB + 16 * (slot ^ (r & 15)) : g_zero_key;
       dma16(src, k_lds + (32 * TPW * wave + 4 * j) * RB);
     }
@@ -260,7 +264,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_lds(IndexArgs A, 
         for (int k = 0; k < 4; ++k) part = fmaf(wl[hb][g][k], fmaxf(acc[4 * g + k], 0.f), part);
     }
     part += __shfl_xor(part, 32, 64);
-    const bool valid = sel ? key_row(e) >= 0 : e < V;
+    const bool valid = SEL ? key_row(e) >= 0 : e < V;
     if (half == 0 && e < A.n_max) scores[row * A.n_max + e] = valid ? part : -INFINITY;
   }
 }
@@ -404,7 +408,8 @@ static void launch_mfma_hb(const IndexArgs& A, float* scores, hipStream_t s) {
   if (!FP4 && (A.n_q < 64 || A.sel)) {   // few queries or rescoring: keys through LDS
     dim3 grid((A.n_max + kIdxLdsEntries - 1) / kIdxLdsEntries, A.n_q, A.batch);
     LaunchTimer timer(A.sel ? "index_rescore_bf16" : "index_scores_bf16", s);
-    index_scores_lds<HB><<<grid, kIdxWaves * 64, 0, s>>>(A, scores);
+    if (A.sel) index_scores_lds<HB, true><<<grid, kIdxWaves * 64, 0, s>>>(A, scores);
+    else index_scores_lds<HB, false><<<grid, kIdxWaves * 64, 0, s>>>(A, scores);
     return;
   }
   if (!FP4) {   // many queries: keys in registers, q double-buffered in LDS
