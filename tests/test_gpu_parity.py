@@ -243,6 +243,7 @@ def _mqa_case(dtype, B, n_q, H, d, N, k, window, seed):
     ("bf16", 1, 40, 128, 512, 700, 300, 128),      # many queries, 128-head workgroups
     ("bf16", 3, 2, 96, 512, 1500, 700, 128),       # few queries, 32-head workgroups, 3 head groups
     ("bf16", 1, 1, 128, 512, 300, 40, 0),          # no window, one tile
+    ("bf16", 1, 34, 256, 512, 300, 64, 64),        # 8-wave kernel, two 128-head groups per query
 ])
 def test_sparse_mqa(dtype, B, n_q, H, d, N, k, window):
     q, kv, kv_raw, rng = _mqa_case(dtype, B, n_q, H, d, N, k, window, seed=H + N + k)
