@@ -1234,38 +1234,53 @@ constexpr int kMaxSplit = 128;
 
 __global__ __launch_bounds__(128) void mqa_combine_kernel(MqaArgs A, MqaLaunch L, const float* part_o,
                                                           const float* part_ml) {
+  constexpr int kPre = 16;   // splits whose partials are requested before the weights exist
   const int head = blockIdx.x;
   const long row = blockIdx.y;
   const int S = L.nsplit;
-  __shared__ float ms[kMaxSplit], ls[kMaxSplit], wts[kMaxSplit];
+  __shared__ float wts[kMaxSplit];
   __shared__ float s_M, s_L;
-  for (int s = threadIdx.x; s < S; s += blockDim.x) {
-    const float* pm = part_ml + ((row * S + s) * A.heads + head) * 2;
-    ms[s] = pm[0];
-    ls[s] = pm[1];
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, ms[s]);
-    float Ls = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const float w = (ms[s] == -INFINITY) ? 0.f : exp2f(ms[s] - M);
-      wts[s] = w;
-      Ls += ls[s] * w;
+  const int d0 = threadIdx.x * 4;
+  const float* po = part_o + ((row * S) * A.heads + head) * kD + d0;
+  const long sstride = (long)A.heads * kD;
+  // the first splits' partials are in flight while the weights are formed
+  f32x4_t pre[kPre];
+#pragma unroll
+  for (int s = 0; s < kPre; ++s) pre[s] = s < S ? *(const f32x4_t*)(po + s * sstride) : f32x4_t{};
+  if (threadIdx.x < 64) {   // one wave: w_s = 2^(m_s - M), L = sum_s l_s w_s
+    const int lane = threadIdx.x;
+    float m2[2], l2[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int sp = lane + 64 * j;
+      const float* pm = part_ml + ((row * S + sp) * A.heads + head) * 2;
+      m2[j] = sp < S ? pm[0] : -INFINITY;
+      l2[j] = sp < S ? pm[1] : 0.f;
     }
-    s_M = M;
-    s_L = Ls;
+    const float M = wave_max(fmaxf(m2[0], m2[1]));
+    float ls = 0.f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int sp = lane + 64 * j;
+      const float w = (m2[j] == -INFINITY) ? 0.f : exp2f(m2[j] - M);
+      if (sp < S) wts[sp] = w;
+      ls += l2[j] * w;
+    }
+    ls = wave_sum(ls);
+    if (lane == 0) {
+      s_M = M;
+      s_L = ls;
+    }
   }
   __syncthreads();
   const float Lsum = s_L;
   const float inv_l = Lsum > 0.f ? 1.f / Lsum : 0.f;
-  const int d0 = threadIdx.x * 4;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  const float* po = part_o + ((row * S) * A.heads + head) * kD + d0;
-  const long sstride = (long)A.heads * kD;
+#pragma unroll
+  for (int s = 0; s < kPre; ++s)
+    if (s < S) acc += pre[s] * wts[s];
 #pragma unroll 8
-  for (int s = 0; s < S; ++s) acc += *(const f32x4_t*)(po + s * sstride) * wts[s];
+  for (int s = kPre; s < S; ++s) acc += *(const f32x4_t*)(po + s * sstride) * wts[s];
   float v[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) v[r] = acc[r] * inv_l * (A.gamma ? A.gamma[d0 + r] : 1.f);
