@@ -20,12 +20,12 @@
 //    threshold and which equal it; one wave scans the cells in position order; each
 //    thread then writes its selected keys to their output slots (keys above before
 //    it plus the equal keys before it, capped at the number still needed).
-// Rows longer than kRegKeys take three launches: a sample of kSample keys gives a
-// threshold expected to pass about 3k keys; many workgroups filter the row against
-// it into per-chunk candidate lists (index order kept); one workgroup per row
-// selects among the candidates.  If the sample's threshold passes fewer than k keys
-// or more than kCandCap, that row is selected straight from its scores in global
-// memory (exact, slower).
+// Rows longer than kRegKeys take two launches.  Many workgroups each derive the same
+// threshold from a fixed sample of kSample keys (expected to pass about 3k keys) and
+// filter their chunks of the row against it into per-chunk candidate lists (index
+// order kept); then one workgroup per row selects among the candidates.  If the
+// threshold passes fewer than k keys or more than kCandCap, that row is selected
+// straight from its scores in global memory (exact, slower).
 #include <type_traits>
 
 #include "csa_device.hpp"
@@ -475,49 +475,51 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(IndexArgs A, co
   select_reg_row<KPT>(key, V, k, oi, os, sh, map);
 }
 
-// ---- long rows, launch 1: the threshold from a fixed sample of the row
+// ---- long rows, launch 1: the threshold from a fixed sample of the row, then the
+// keys at or above it, per chunk of kChunk keys, in index order
 struct LongWs {
-  uint32_t* tau;      // [rows]
   uint32_t* counts;   // [rows, chunks]
   uint32_t* ckey;     // [rows, n_max]
   int32_t* cidx;      // [rows, n_max]
   int chunks;
 };
 
-__global__ __launch_bounds__(kTopkThreads) void topk_sample_kernel(IndexArgs A, const float* scores, LongWs L) {
-  __shared__ SelShared sh;
+constexpr int kFilterGroups = kTopkThreads / kFilterThreads;   // chunks per workgroup
+
+// The threshold key: its rank in a fixed, evenly spaced sample of the row is chosen to
+// leave ~3k keys of the row at or above it (at most three quarters of the candidate
+// capacity; a larger k keeps a smaller margin).  key >= tau <=> (key & mask) >= prefix.
+__device__ __forceinline__ uint32_t sample_threshold(const IndexArgs& A, const float* src, int V, SelShared& sh) {
   constexpr int KPT = kSample / kTopkThreads;
-  const long row = blockIdx.x;
-  const int V = row_visible(A, row);
-  if (V <= kRegKeys || V <= A.topk) return;
-  const float* src = scores + row * A.n_max;
   uint32_t key[KPT];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) key[j] = order_key(src[(long)(kTopkThreads * j + threadIdx.x) * V / kSample]);
-  // rank in the sample expected to leave ~3k keys of the row at or above it, at most
-  // three quarters of the candidate capacity (a larger k keeps a smaller margin)
   const long want = min((long)3 * A.topk, (long)kCandCap * 3 / 4);
   long r = (want * kSample + V - 1) / V;
   r = r < 1 ? 1 : (r > kSample ? kSample : r);
   uint32_t prefix, mask, need;
   reg_threshold<KPT>(key, kSample, (uint32_t)r, sh, prefix, mask, need);
-  if (threadIdx.x == 0) L.tau[row] = prefix;   // key >= prefix  <=>  (key & mask) >= prefix
+  return prefix;
 }
 
-// ---- long rows, launch 2: keys at or above the threshold, per chunk, index order
-__global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(IndexArgs A, const float* scores, LongWs L) {
-  __shared__ uint32_t wtot[kFilterThreads / 64];
+// Every workgroup of a row forms the same threshold (the sample and its selection are
+// deterministic), then each group of kFilterThreads threads filters one chunk.
+__global__ __launch_bounds__(kTopkThreads) void topk_filter_kernel(IndexArgs A, const float* scores, LongWs L) {
+  __shared__ SelShared sh;
+  __shared__ uint32_t wtot[kTopkThreads / 64];
   const long row = blockIdx.y;
-  const int c = blockIdx.x;
   const int V = row_visible(A, row);
   if (V <= kRegKeys || V <= A.topk) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int c0 = c * kChunk;
-  const uint32_t tau = L.tau[row];
   const float* src = scores + row * A.n_max;
-  constexpr int kIt = kChunk / kFilterThreads;            // 16 keys per lane
-  constexpr int kPerWave = kChunk / (kFilterThreads / 64);
-  const int w0 = c0 + wave * kPerWave;
+  const uint32_t tau = sample_threshold(A, src, V, sh);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int kGw = kFilterThreads / 64;                  // waves per group
+  const int grp = wave / kGw, gw = wave % kGw;
+  const int c = blockIdx.x * kFilterGroups + grp;
+  const int c0 = c * kChunk;
+  constexpr int kIt = kChunk / kFilterThreads;              // 16 keys per lane
+  constexpr int kPerWave = kChunk / kGw;
+  const int w0 = c0 + gw * kPerWave;
   uint32_t key[kIt];
   uint32_t cnt = 0;
 #pragma unroll
@@ -530,10 +532,11 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(IndexArgs A
   __syncthreads();
   uint32_t pos = 0, total = 0;
 #pragma unroll
-  for (int w = 0; w < kFilterThreads / 64; ++w) {
-    pos += w < wave ? wtot[w] : 0u;
-    total += wtot[w];
+  for (int w = 0; w < kGw; ++w) {
+    pos += w < gw ? wtot[grp * kGw + w] : 0u;
+    total += wtot[grp * kGw + w];
   }
+  if (c >= L.chunks) return;   // (after the last barrier)
   uint32_t* ck = L.ckey + row * A.n_max + c0;
   int32_t* ci = L.cidx + row * A.n_max + c0;
 #pragma unroll
@@ -548,7 +551,7 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(IndexArgs A
     }
     pos += __popcll(bs);
   }
-  if (threadIdx.x == 0) L.counts[row * L.chunks + c] = total;
+  if (threadIdx.x == (unsigned)(grp * kFilterThreads)) L.counts[row * L.chunks + c] = total;
 }
 
 // Exact selection among the M candidates of a long row (KPT * 1024 >= M): candidate c
@@ -580,7 +583,7 @@ __device__ __forceinline__ void select_candidates(const uint32_t* gk, const int3
   reg_compact<KPT>(key, M, prefix, mask, need, k, idx_of, oi, os, sh);
 }
 
-// ---- long rows, launch 3: exact selection among the candidates (or the whole row)
+// ---- long rows, launch 2: exact selection among the candidates (or the whole row)
 __global__ __launch_bounds__(kTopkThreads) void topk_candidates_kernel(IndexArgs A, const float* scores, LongWs L,
                                                                        int32_t* out_idx, float* out_score) {
   __shared__ SelShared sh;
@@ -638,7 +641,7 @@ size_t topk_workspace_bytes(const IndexArgs& A) {
   const size_t rows = (size_t)A.batch * A.n_q;
   const size_t chunks = (size_t)long_chunks(A);
   auto r256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  return r256(rows * 4) + r256(rows * chunks * 4) + 2 * r256(rows * (size_t)A.n_max * 4);
+  return r256(rows * chunks * 4) + 2 * r256(rows * (size_t)A.n_max * 4);
 }
 
 hipError_t launch_topk_rows(const IndexArgs& A, const float* scores, int32_t* out_idx, float* out_score, void* ws,
@@ -658,16 +661,14 @@ hipError_t launch_topk_rows(const IndexArgs& A, const float* scores, int32_t* ou
   auto r256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
   char* p = (char*)ws;
   LongWs L;
-  L.tau = (uint32_t*)p;
-  p += r256((size_t)rows * 4);
   L.counts = (uint32_t*)p;
   p += r256((size_t)rows * chunks * 4);
   L.ckey = (uint32_t*)p;
   p += r256((size_t)rows * A.n_max * 4);
   L.cidx = (int32_t*)p;
   L.chunks = chunks;
-  topk_sample_kernel<<<grid, kTopkThreads, 0, s>>>(A, scores, L);
-  topk_filter_kernel<<<dim3((unsigned)chunks, (unsigned)rows), kFilterThreads, 0, s>>>(A, scores, L);
+  const unsigned fgroups = (unsigned)((chunks + kFilterGroups - 1) / kFilterGroups);
+  topk_filter_kernel<<<dim3(fgroups, (unsigned)rows), kTopkThreads, 0, s>>>(A, scores, L);
   topk_candidates_kernel<<<grid, kTopkThreads, 0, s>>>(A, scores, L, out_idx, out_score);
   return hipGetLastError();
 }
