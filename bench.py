@@ -240,10 +240,9 @@ class CsaDecode1mFp4(Step):
         w = to_dev(c["w"][:, None], dev)
         reps = [base] + [{key: t.clone() for key, t in base.items()} for _ in range(R - 1)]
         self.reps = reps
-        for r in reps:
-            r["qc"], r["qs"] = csa.mxfp4_quantize(r["qI"])
-        self.decs = [csa.Decoder(r["q"], r["kv"], r["kv_raw"], rb, qp, r["qc"], w, r["kc"], ne, m=self.m,
-                                 topk=self.k, window=self.w, q_scale=r["qs"], k_scale=r["ks"]) for r in reps]
+        # the fp32 indexer queries are quantised inside each step's indexer launch
+        self.decs = [csa.Decoder(r["q"], r["kv"], r["kv_raw"], rb, qp, r["qI"], w, r["kc"], ne, m=self.m,
+                                 topk=self.k, window=self.w, k_scale=r["ks"]) for r in reps]
         self.config = {"workload": self.name, "batch": 1, "context": 1 << 20, "compress_ratio": self.m,
                        "entries": self.N, "heads": self.H, "head_dim": self.d, "idx_heads": self.HI,
                        "idx_dim": self.dI, "idx_dtype": "mxfp4", "topk": self.k, "window": self.w,
@@ -254,8 +253,6 @@ class CsaDecode1mFp4(Step):
         self.step_flops = 2.0 * N * HI * dI + 4.0 * H * d * (k + w)
 
     def launch(self, i):
-        r = self.reps[i % self.replicas]
-        self.csa.mxfp4_quantize(r["qI"], r["qc"], r["qs"])
         self.decs[i % self.replicas]()
 
     def algorithmic(self, kernel):
@@ -264,8 +261,6 @@ class CsaDecode1mFp4(Step):
             return "hbm", self.key_bytes + HI * (dI // 2 + dI // 32) + HI * 4 + N * 4
         if kernel == "topk":
             return "hbm", N * 4 + k * 4
-        if kernel == "mxfp4_quantize":
-            return "hbm", HI * dI * 2 + HI * (dI // 2 + dI // 32)
         if kernel.startswith("mqa_bf16"):
             return "hbm", (k + w) * d * 2 + 2 * H * d * 2 + k * 4
         return None
@@ -315,7 +310,7 @@ class CsaDecode1mFp4Rescored(CsaDecode1mFp4):
                                      i32(c["n_entries"], dev))
         import ctypes
         r0 = self.reps[0]
-        d = self.csa._index_desc(r0["qc"], r0["kc"], 4, self.k, None, self.csa.MXFP4)
+        d = self.csa._index_desc(r0["qI"], r0["kc"], 4, self.k, None, *self.csa._index_dtype(r0["qI"], r0["kc"]))
         self.ws_i = torch.zeros(self.csa.lib().csa_index_rescored_workspace_size(ctypes.byref(d), self.cand),
                                 dtype=torch.uint8, device=dev)
         dm = self.csa._mqa_desc(r0["q"], r0["kv"], r0["kv_raw"], topk=self.k, window=self.w)
@@ -331,8 +326,7 @@ class CsaDecode1mFp4Rescored(CsaDecode1mFp4):
     def launch(self, i):
         r = self.reps[i % self.replicas]
         csa = self.csa
-        csa.mxfp4_quantize(r["qI"], r["qc"], r["qs"])
-        csa.index_topk_rescored(r["qc"], r["qs"], r["q16"], self.w_dev, r["kc"], r["ks"], r["k16"], self.ne, self.qp,
+        csa.index_topk_rescored(r["qI"], None, r["q16"], self.w_dev, r["kc"], r["ks"], r["k16"], self.ne, self.qp,
                                 m=self.m, topk=self.k, cand=self.cand, workspace=self.ws_i, out_idx=self.idx,
                                 out_score=self.isc)
         csa.sparse_mqa(r["q"], r["kv"], self.idx, r["kv_raw"], self.rb, self.qp, window=self.w, workspace=self.ws_m,

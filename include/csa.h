@@ -164,6 +164,9 @@ typedef struct {
   int32_t n_max;      /* upper bound of n_entries[b] over the batch */
   int32_t k_cap;      /* rows per sequence in k_idx */
   int32_t dtype;      /* CSA_F32, CSA_BF16 or CSA_MXFP4 (q_idx and k_idx) */
+  int32_t q_quantize; /* CSA_MXFP4 only: 0 = q_idx / q_scale hold MXFP4 codes and scales;
+                         1 = q_idx holds fp32 values [.., idx_dim], quantised inside the
+                         call exactly as csa_mxfp4_quantize would (q_scale unused) */
 } csa_index_desc;
 
 size_t csa_index_workspace_size(const csa_index_desc* desc);

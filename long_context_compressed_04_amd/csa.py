@@ -33,7 +33,7 @@ class CompressDesc(ctypes.Structure):
 
 class IndexDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
-        "batch", "n_q", "idx_heads", "idx_dim", "m", "topk", "n_max", "k_cap", "dtype")]
+        "batch", "n_q", "idx_heads", "idx_dim", "m", "topk", "n_max", "k_cap", "dtype", "q_quantize")]
 
 
 class MqaDesc(ctypes.Structure):
@@ -175,17 +175,26 @@ def mxfp4_quantize(x, codes=None, scales=None):
     return codes, scales
 
 
-def _index_desc(q_idx, k_idx, m, topk, n_max, dtype):
+def _index_dtype(q_idx, k_idx):
+    """(dtype, q_quantize): MXFP4 keys with fp32 queries quantise the queries inside
+    the call; otherwise q_idx and k_idx share one dtype."""
+    if _dtype_code(k_idx) == MXFP4 and q_idx.dtype != torch.uint8:
+        if q_idx.dtype != torch.float32:
+            raise ValueError("queries quantised inside the call must be float32")
+        return MXFP4, 1
+    return _dtype_code(q_idx), 0
+
+
+def _index_desc(q_idx, k_idx, m, topk, n_max, dtype, q_quantize=0):
     B, n_q, HI = q_idx.shape[:3]
-    dI = q_idx.shape[3] * (2 if dtype == MXFP4 else 1)
+    dI = q_idx.shape[3] * (2 if dtype == MXFP4 and not q_quantize else 1)
     k_cap = k_idx.shape[1]
-    return IndexDesc(B, n_q, HI, dI, m, topk, k_cap if n_max is None else n_max, k_cap, dtype)
+    return IndexDesc(B, n_q, HI, dI, m, topk, k_cap if n_max is None else n_max, k_cap, dtype, q_quantize)
 
 
 def index_scores(q_idx, w, k_idx, n_entries, q_pos, *, m, n_max=None, q_scale=None, k_scale=None):
     """Indexer score rows [B, n_q, n_max] fp32 (-inf where not visible)."""
-    dt = _dtype_code(q_idx)
-    d = _index_desc(q_idx, k_idx, m, 1, n_max, dt)
+    d = _index_desc(q_idx, k_idx, m, 1, n_max, *_index_dtype(q_idx, k_idx))
     scores = torch.empty((d.batch, d.n_q, d.n_max), dtype=torch.float32, device=q_idx.device)
     _check(lib().csa_index_scores(ctypes.byref(d), _p(q_idx), _p(q_scale), _p(w), _p(k_idx), _p(k_scale),
                                   _p(n_entries), _p(q_pos), _p(scores), _stream(q_idx)))
@@ -195,8 +204,7 @@ def index_scores(q_idx, w, k_idx, n_entries, q_pos, *, m, n_max=None, q_scale=No
 def index_topk(q_idx, w, k_idx, n_entries, q_pos, *, m, topk, n_max=None, q_scale=None, k_scale=None,
                workspace=None, out_idx=None, out_score=None):
     """Indexer + causal top-k: returns (idx int32 [B, n_q, topk], score fp32 [B, n_q, topk])."""
-    dt = _dtype_code(q_idx)
-    d = _index_desc(q_idx, k_idx, m, topk, n_max, dt)
+    d = _index_desc(q_idx, k_idx, m, topk, n_max, *_index_dtype(q_idx, k_idx))
     dev = q_idx.device
     if out_idx is None:
         out_idx = torch.empty((d.batch, d.n_q, topk), dtype=torch.int32, device=dev)
@@ -212,7 +220,7 @@ def index_topk_rescored(q_idx, q_scale, q_bf16, w, k_idx, k_scale, k_bf16, n_ent
                         n_max=None, workspace=None, out_idx=None, out_score=None):
     """MXFP4 prefilter of `cand` entries, bf16 rescoring, top-k of the rescored
     candidates: returns (idx int32 [B, n_q, topk], rescored score fp32 [B, n_q, topk])."""
-    d = _index_desc(q_idx, k_idx, m, topk, n_max, MXFP4)
+    d = _index_desc(q_idx, k_idx, m, topk, n_max, *_index_dtype(q_idx, k_idx))
     dev = q_idx.device
     if out_idx is None:
         out_idx = torch.empty((d.batch, d.n_q, topk), dtype=torch.int32, device=dev)
@@ -263,10 +271,9 @@ class Decoder:
     def __init__(self, q, kv, kv_raw, raw_base, q_pos, q_idx, w, k_idx, n_entries, *, m, topk, window,
                  n_max=None, q_scale=None, k_scale=None, scale=0.0, eps=1e-6, rms_weight=None, out=None,
                  out_idx=None, out_score=None, lse=None):
-        dt = _dtype_code(q_idx)
         self.tensors = [q, kv, kv_raw, raw_base, q_pos, q_idx, w, k_idx, n_entries, q_scale, k_scale, rms_weight]
         a = DecodeArgs()
-        a.index = _index_desc(q_idx, k_idx, m, topk, n_max, dt)
+        a.index = _index_desc(q_idx, k_idx, m, topk, n_max, *_index_dtype(q_idx, k_idx))
         a.attn = _mqa_desc(q, kv, kv_raw, topk=topk, window=window, scale=scale, eps=eps)
         dev = q.device
         self.out = torch.empty_like(q) if out is None else out

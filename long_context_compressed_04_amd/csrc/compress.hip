@@ -125,26 +125,6 @@ hipError_t launch_compress(const CompressArgs& A, hipStream_t s) {
 // MXFP4 (OCP MX v1.0) quantisation: one thread per block of 32 values.
 // E = floor(log2 amax) - 2 (clamped to [-127, 127]; -127 for an all-zero block);
 // codes = nearest e2m1 value of x * 2^-E with ties to the even code, saturating.
-__device__ __forceinline__ int floor_log2_f32(float a) {
-  uint32_t u = __float_as_uint(a);
-  int e = (int)((u >> 23) & 0xff);
-  if (e != 0) return e - 127;
-  uint32_t mant = u & 0x7fffffu;                 // subnormal: position of leading one
-  return -149 + (31 - __clz((int)mant));
-}
-
-__device__ __forceinline__ uint32_t e2m1_magnitude_code(float v) {
-  // thresholds at the midpoints of {0, .5, 1, 1.5, 2, 3, 4, 6}; exact midpoints go to
-  // the even code (0, 2, 2, 4, 4, 6, 6)
-  if (v <= 0.25f) return 0;
-  if (v < 0.75f) return 1;
-  if (v <= 1.25f) return 2;
-  if (v < 1.75f) return 3;
-  if (v <= 2.5f) return 4;
-  if (v < 3.5f) return 5;
-  if (v <= 5.0f) return 6;
-  return 7;
-}
 
 template <bool IN_BF16>
 __global__ __launch_bounds__(256) void mxfp4_quantize_kernel(const void* x, int64_t n_blocks, uint8_t* codes,
@@ -172,20 +152,9 @@ __global__ __launch_bounds__(256) void mxfp4_quantize_kernel(const void* x, int6
       v[4 * i] = q.x; v[4 * i + 1] = q.y; v[4 * i + 2] = q.z; v[4 * i + 3] = q.w;
     }
   }
-  float amax = 0.f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  int E = (amax == 0.f) ? -127 : floor_log2_f32(amax) - 2;
-  E = E < -127 ? -127 : (E > 127 ? 127 : E);
-  uint32_t packed[4] = {0, 0, 0, 0};
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    float sv = ldexpf(fabsf(v[i]), -E);
-    uint32_t code = e2m1_magnitude_code(sv) | ((__float_as_uint(v[i]) >> 31) << 3);
-    packed[i / 8] |= code << (4 * (i % 8));
-  }
-  *(uint4*)(codes + blk * 16) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-  scales[blk] = (uint8_t)(E + 127);
+  uint8_t scale;
+  *(uint4*)(codes + blk * 16) = mxfp4_block(v, scale);
+  scales[blk] = scale;
 }
 
 hipError_t launch_mxfp4_quantize(int in_bf16, const void* x, int64_t n_blocks, uint8_t* codes, uint8_t* scales,

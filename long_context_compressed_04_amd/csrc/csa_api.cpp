@@ -75,9 +75,12 @@ csa_status check_index(const char* fn, const csa_index_desc* d, const void* q, c
       return fail(CSA_ERR_UNSUPPORTED, "%s: bf16/MXFP4 indexer needs idx_dim == 128 and idx_heads in {32,64,96,128}", fn);
     if (!aligned16(q) || !aligned16(k)) return fail(CSA_ERR_ALIGN, "%s: q_idx and k_idx must be 16-byte aligned", fn);
     if (d->dtype == CSA_MXFP4) {
-      if (!qs || !kscale) return fail(CSA_ERR_NULL, "%s: MXFP4 needs q_scale and k_scale", fn);
-      if (((uintptr_t)qs & 3u) || ((uintptr_t)kscale & 3u))
+      if (d->q_quantize != 0 && d->q_quantize != 1) return fail(CSA_ERR_SHAPE, "%s: q_quantize must be 0 or 1", fn);
+      if ((!qs && !d->q_quantize) || !kscale) return fail(CSA_ERR_NULL, "%s: MXFP4 needs q_scale and k_scale", fn);
+      if ((qs && !d->q_quantize && ((uintptr_t)qs & 3u)) || ((uintptr_t)kscale & 3u))
         return fail(CSA_ERR_ALIGN, "%s: q_scale and k_scale must be 4-byte aligned", fn);
+    } else if (d->q_quantize) {
+      return fail(CSA_ERR_DTYPE, "%s: q_quantize applies to CSA_MXFP4 only", fn);
     }
   } else {
     return fail(CSA_ERR_DTYPE, "%s: dtype must be CSA_F32, CSA_BF16 or CSA_MXFP4", fn);
@@ -91,6 +94,7 @@ csa::IndexArgs index_args(const csa_index_desc* d, const void* q, const uint8_t*
   A.batch = d->batch; A.n_q = d->n_q; A.heads = d->idx_heads; A.dim = d->idx_dim; A.m = d->m; A.topk = d->topk;
   A.n_max = d->n_max; A.k_cap = d->k_cap; A.dtype = d->dtype;
   A.q = q; A.q_scale = qs; A.w = w; A.k = k; A.k_scale = ks; A.n_entries = ne; A.q_pos = qpos;
+  A.q_quantize = d->dtype == CSA_MXFP4 ? d->q_quantize : 0;
   return A;
 }
 
@@ -264,6 +268,7 @@ csa_status csa_index_topk_rescored(const csa_index_desc* d, int32_t cand, const 
   B.q_scale = nullptr;
   B.k = k16;
   B.k_scale = nullptr;
+  B.q_quantize = 0;
   B.n_max = cand;
   B.sel = cands;
   st = hip_status(csa::launch_index_scores(B, rescored, s), "csa_index_topk_rescored (rescore)");

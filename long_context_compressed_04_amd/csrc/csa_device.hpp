@@ -101,4 +101,41 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* t
   return res;
 }
 
+
+// ---- MXFP4 (OCP MX v1.0): one block of 32 values -> 16 code bytes (element 2i in
+// the low nibble of byte i) and its e8m0 scale byte.  Shared exponent
+// E = floor(log2(max|x|)) - 2 clamped to [-127, 127] (-127 for an all-zero block);
+// element code = nearest e2m1 value of |x| / 2^E (ties to the even code, saturating
+// at 6) with the sign of x.
+__device__ __forceinline__ int floor_log2_f32(float a) {
+  uint32_t u = __float_as_uint(a);
+  int e = (int)((u >> 23) & 0xff);
+  if (e != 0) return e - 127;
+  uint32_t mant = u & 0x7fffffu;                 // subnormal: position of leading one
+  return -149 + (31 - __clz((int)mant));
+}
+
+// The division and rounding are gfx950's scaled FP4 conversion (two values per
+// instruction, byte `sel` of the word): it divides by the scale and reads only the
+// scale's exponent field, so 2^E is built from E + 127 directly (all zero bits for
+// E = -127).
+__device__ __forceinline__ uint4 mxfp4_block(const float (&v)[32], uint8_t& scale) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  int E = (amax == 0.f) ? -127 : floor_log2_f32(amax) - 2;
+  E = E < -127 ? -127 : (E > 127 ? 127 : E);
+  const float sc = __uint_as_float((uint32_t)(E + 127) << 23);
+  uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    w[p] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[p], v[8 * p], v[8 * p + 1], sc, 0);
+    w[p] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[p], v[8 * p + 2], v[8 * p + 3], sc, 1);
+    w[p] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[p], v[8 * p + 4], v[8 * p + 5], sc, 2);
+    w[p] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[p], v[8 * p + 6], v[8 * p + 7], sc, 3);
+  }
+  scale = (uint8_t)(E + 127);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 }  // namespace csa

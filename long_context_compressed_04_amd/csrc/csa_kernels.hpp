@@ -29,6 +29,8 @@ struct IndexArgs {
   const int32_t* sel = nullptr;
   // Top-k: the selected slot p of row r is written as map[r * n_max + p].
   const int32_t* map = nullptr;
+  // MXFP4: q holds fp32 values, quantised in the indexer as the standalone quantiser does
+  int q_quantize = 0;
 };
 // Score rows [batch*n_q, n_max] (-inf past the visible count).
 hipError_t launch_index_scores(const IndexArgs& A, float* scores, hipStream_t s);

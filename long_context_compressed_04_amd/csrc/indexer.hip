@@ -104,7 +104,23 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_mfma(IndexArgs A,
     const long row = (long)b * A.n_q + qi;
     // ---- stage q (and its scales) and w for this query in LDS
     __syncthreads();
-    if (FP4) {
+    if (FP4 && A.q_quantize) {
+      // fp32 q, quantised here block by block (as the standalone quantiser): block i
+      // is head i / 4, dims 32 (i % 4) ..; its codes land where the staged codes would
+      const float* qg = (const float*)A.q + row * H * kIdxDim;
+      for (int i = threadIdx.x; i < H * 4; i += blockDim.x) {
+        const int h = i >> 2, p = i & 3;
+        float v[32];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float4 f = *(const float4*)(qg + h * kIdxDim + 32 * p + 4 * j);
+          v[4 * j] = f.x; v[4 * j + 1] = f.y; v[4 * j + 2] = f.z; v[4 * j + 3] = f.w;
+        }
+        uint8_t sc;
+        *(uint4*)(q_lds + h * QROW + 16 * p) = mxfp4_block(v, sc);
+        ((uint8_t*)qs_lds)[4 * h + p] = sc;
+      }
+    } else if (FP4) {
       const uint8_t* qg = (const uint8_t*)A.q + row * H * (kIdxDim / 2);
       for (int i = threadIdx.x; i < H * 4; i += blockDim.x) {   // 16 B pieces: 4 per head
         int h = i >> 2, p = i & 3;

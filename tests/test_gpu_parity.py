@@ -166,6 +166,28 @@ def test_index_topk_rescored(B, n_q, HI, N, k, cand):
             assert_f32_close(sc[b, i, :len(sel)], full[sel], "rescored scores")
 
 
+@pytest.mark.parametrize("B,n_q,HI,N", [(2, 1, 64, 2500), (1, 65, 64, 600), (1, 2, 128, 700)])
+def test_mxfp4_queries_quantised_inside_the_call(B, n_q, HI, N):
+    """fp32 queries quantised inside the indexer give the same scores and sets, bit for
+    bit, as quantising them first with csa_mxfp4_quantize."""
+    q, kk, w, n_entries, q_pos = _index_case("bf16", B, n_q, HI, 128, N, N + 40, 4, seed=HI + N + 7)
+    qc, qsc = csa.mxfp4_quantize(dev(q))
+    kc, ksc = csa.mxfp4_quantize(dev(kk))
+    ne_d, qp_d, w_d = _i32(n_entries), _i32(q_pos), dev(w)
+    two = host(csa.index_scores(qc, w_d, kc, ne_d, qp_d, m=4, n_max=N, q_scale=qsc, k_scale=ksc))
+    one = host(csa.index_scores(dev(q), w_d, kc, ne_d, qp_d, m=4, n_max=N, k_scale=ksc))
+    np.testing.assert_array_equal(one, two)
+    i2, _ = csa.index_topk(qc, w_d, kc, ne_d, qp_d, m=4, topk=64, n_max=N, q_scale=qsc, k_scale=ksc)
+    i1, _ = csa.index_topk(dev(q), w_d, kc, ne_d, qp_d, m=4, topk=64, n_max=N, k_scale=ksc)
+    np.testing.assert_array_equal(i1.cpu().numpy(), i2.cpu().numpy())
+    q16, k16 = dev(W.store(q, "bf16")), dev(W.store(kk, "bf16"))
+    r2, s2 = csa.index_topk_rescored(qc, qsc, q16, w_d, kc, ksc, k16, ne_d, qp_d, m=4, topk=64, cand=256, n_max=N)
+    r1, s1 = csa.index_topk_rescored(dev(q), None, q16, w_d, kc, ksc, k16, ne_d, qp_d, m=4, topk=64, cand=256,
+                                     n_max=N)
+    np.testing.assert_array_equal(r1.cpu().numpy(), r2.cpu().numpy())
+    np.testing.assert_array_equal(host(s1), host(s2))
+
+
 def test_topk_ties_and_degenerate_rows():
     """All-zero weights (every score 0), duplicated keys (exact ties), V == k, V == 0."""
     B, HI, dI, N, m = 4, 64, 128, 600, 4
