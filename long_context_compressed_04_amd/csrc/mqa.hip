@@ -16,8 +16,8 @@
 // bf16 kernels (head_dim 512), chosen by the host:
 //  - mqa_w8_kernel (unit RMSNorm weight): 8 waves = the 128 heads of a (query,
 //    split) unit, two waves per SIMD; prefill, dense HCA decode;
-//  - mqa_hg_kernel (few queries, unit weight): 4 waves = one group of 32 heads of a
-//    (query, split) unit, 128 dims per wave, partial logits summed through LDS;
+//  - mqa_sd_kernel (few queries, unit weight): 6 waves = one group of 32 heads of a
+//    (query, split) unit, split into logit and value roles on a software pipeline;
 //    sparse decode;
 //  - mqa_bf16_kernel (any RMSNorm weight): NW waves x 16 heads with an online
 //    (running maximum) softmax.
@@ -175,7 +175,8 @@ constexpr int kRowB = kD * 2 + 16;      // LDS row stride in bytes (padded)
 struct MqaLaunch {
   int nsplit, ips, n_hg, units, nw;   // nw: waves per workgroup
   int slots;                          // index slots of a split copied to LDS
-  int kind;   // 0: 16-head waves, 2: 32-head workgroups, 3: 128-head 8-wave workgroups
+  int kind;   // 0: 16-head waves, 3: 128-head 8-wave workgroups, 4: split-role 32-head
+              // workgroups
   int pre;    // kind 3: row 1/rms from the per-cache pre-pass
 };
 
@@ -566,6 +567,13 @@ __device__ __forceinline__ uint32_t issue_rows(Resolve resolve, int item0, int l
   return ok;
 }
 
+// acc + (both bf16 halves of w) squared, by the bf16 dot-product instruction
+__device__ __forceinline__ float dot2_bf16(uint32_t w, float acc) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = __builtin_bit_cast(bf16x2_t, w);
+  return __builtin_amdgcn_fdot2_f32_bf16(v, v, acc, false);
+}
+
 struct RowSrc {
   const uint8_t* kv;
   const uint8_t* raw;
@@ -574,30 +582,41 @@ struct RowSrc {
 };
 
 // ---------------------------------------------------------------------------------
-// Head-group kernel for few queries (decode): a workgroup = 4 waves = one group of
-// 32 heads of one (query, split) unit, wave w owning dims 128 w .. 128 w + 127.  The
-// four head groups of a unit run on one XCD, so three of the four gathers of a row
-// hit that XCD's L2.  Per 32-row tile each wave forms S^T over its 128 dims, the
-// four partial S^T meet in LDS (one barrier), and each wave accumulates O^T for its
-// own dims.  Splitting heads as well as items keeps the fp32 partials of a
-// decode-sized batch 4x smaller than splitting items alone.
-constexpr int kHgWaves = 4;
-constexpr int kHgRpw = kTile / kHgWaves;   // rows each wave stages per tile
+// Split-role decode kernel: one workgroup = one group of 32 heads of a (query,
+// split) unit, six waves in two roles on a software pipeline over 32-row tiles
+// (step s: tile s weighed while tile s-1 is accumulated and tile s+2 is gathered):
+//  - logit waves 0, 1: rows 16 w .. 16 w + 15 of tile s against all 32 heads and all
+//    512 dims, S^T on v_mfma_f32_16x16x32_bf16 (A = K rows, B = normalised q held in
+//    registers), the rows' sums of squares from the same A fragments by bf16 dot
+//    products, then the softmax weights of their 16 rows x 32 heads into LDS: no
+//    partial logits cross waves and no weight is formed twice;
+//  - value waves 2..5: O^T for dims 128 (w - 2) .. of tile s-1 on
+//    v_mfma_f32_32x32x16_bf16 (A = V^T by transposing LDS reads, B = the weights
+//    of the previous step); waves 2, 3 gather (direct-to-LDS) the even tiles and
+//    waves 4, 5 the odd ones, tile s+2 at step s, and wait for it at the end of step
+//    s+1, so each wave's wait is for all of its loads (a count the compiler can
+//    follow: it sees a rolled gather loop as one load).
+// One barrier per step; four tile buffers: two tiles in flight, one being weighed,
+// one being accumulated.  The weights are stored per head in the order the B operand
+// of the 32x32x16 product consumes its k index (rows 4 kg .. 4 kg + 3 and
+// 8 + 4 kg .. of each 16-row step in lane half kg), so each value wave reads one
+// 16-byte fragment per step and head.
+constexpr int kSdQk = 2, kSdPv = 4, kSdWaves = kSdQk + kSdPv;
+constexpr int kSdRpw = kTile / 2;       // rows each gathering value wave loads per tile
+constexpr int kPRow = 2 * kTile + 16;   // bytes per head row of a weight buffer (padded)
 
-__global__ __launch_bounds__(kHgWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void mqa_hg_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml) {
+__global__ __launch_bounds__(kSdWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void mqa_sd_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml) {
   __shared__ __attribute__((aligned(16))) uint8_t tb0[kTile * kRowB2];
   __shared__ __attribute__((aligned(16))) uint8_t tb1[kTile * kRowB2];
   __shared__ __attribute__((aligned(16))) uint8_t tb2[kTile * kRowB2];
-  __shared__ float irms[kNB][kTile];
-  __shared__ float xbuf[2][kHgWaves][kXS][64];   // by tile parity: one barrier per tile
+  __shared__ __attribute__((aligned(16))) uint8_t tb3[kTile * kRowB2];
+  __shared__ __attribute__((aligned(16))) uint8_t wts[2][32 * kPRow];
   __shared__ int32_t slot[kSlotsLds];
-  __shared__ float qss[kHgWaves][64];
+  __shared__ float lsum[kSdQk][32];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int h = lane >> 5, c32 = lane & 31;
-
   const int f = blockIdx.x;
   const int xcd = f & 7, r8 = f >> 3;
   const int hg = r8 % L.n_hg, ug = r8 / L.n_hg;
@@ -606,9 +625,17 @@ void mqa_hg_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml) {
   const long row = unit / L.nsplit;
   const int split = unit % L.nsplit;
   const int b = (int)(row / A.n_q);
-  const int head = hg * 32 + c32;
 
-  // ---- the items of this (query, split): index slots first, then the query
+  // raw q rows of the heads this wave normalises (heads wave + 6 j), 16 bytes a lane;
+  // loaded before the slots, so waiting for the slots has waited for them too
+  constexpr int kQn = (32 + kSdWaves - 1) / kSdWaves;
+  uint4 qraw[kQn];
+#pragma unroll
+  for (int j = 0; j < kQn; ++j) {
+    const int hq = wave + kSdWaves * j;
+    if (hq < 32) qraw[j] = *(const uint4*)((const uint16_t*)A.q + (row * A.heads + hg * 32 + hq) * kD + 8 * lane);
+  }
+  // ---- the items of this (query, split): index slots to LDS
   RowSrc R;
   {
     ItemSource src;
@@ -621,17 +648,13 @@ void mqa_hg_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml) {
     R.gidx = src.idx;
     R.use_slots = !A.dense;
     if (R.use_slots)
-      for (int i = threadIdx.x; i < L.ips; i += kHgWaves * 64) {
+      for (int i = threadIdx.x; i < L.ips; i += kSdWaves * 64) {
         const int it = R.it0 + i;
         slot[i] = (it < min(R.it1, R.n_first)) ? src.idx[it] : -1;
       }
   }
-  // this wave's dims of the query row: 128 w + 16 ks + 8 h + [0, 8)
-  const uint16_t* qrow = (const uint16_t*)A.q + (row * A.heads + head) * kD + 128 * wave;
-  uint4 qraw[8];
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) qraw[ks] = *(const uint4*)(qrow + 16 * ks + 8 * h);
-  lds_barrier();   // the slots are in LDS (each store waited for its load)
+  wait_vmcnt<0>();   // q has arrived: nothing later waits for it behind the gathers
+  lds_barrier();     // the slots are in LDS
 
   auto resolve = [&](int item) -> const uint8_t* {
     if (item >= R.it1) return nullptr;
@@ -643,151 +666,176 @@ void mqa_hg_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml) {
     return (r >= 0 && r < R.raw_cap) ? R.raw + (long)r * (kD * 2) : nullptr;
   };
   const int n_tiles = (R.it1 - R.it0 + kTile - 1) / kTile;
-  uint32_t okm[kNB] = {0, 0, 0};
-  auto buf_ptr = [&](int bi) -> uint8_t* { return bi == 0 ? tb0 : (bi == 1 ? tb1 : tb2); };
-  auto issue = [&](int ti, uint8_t* dst) -> uint32_t {
-    return issue_rows<kHgRpw, kHgWaves>(resolve, R.it0 + ti * kTile + wave, lane, dst + wave * kRowB2);
+  const bool value_wave = wave >= kSdQk;
+  const int pw = wave - kSdQk;
+  const int grp = pw >> 1;   // gathers tiles t with t % 2 == grp
+  auto issue = [&](int t, uint8_t* dst) {
+    issue_rows<kSdRpw, 2>(resolve, R.it0 + t * kTile + (pw & 1), lane, dst + (pw & 1) * kRowB2);
   };
-  // the first two tiles' gathers go out before the query is normalised
-  if (n_tiles > 0) okm[0] = issue(0, tb0);
-  if (n_tiles > 1) okm[1] = issue(1, tb1);
-
-  // ---- u = q / rms(q): the four waves swap their partial sums of squares
-  bf16x8_t qf[8];
-  {
-    float ss = 0.f;
+  if (value_wave) {
+    if (grp == 0 && n_tiles > 0) issue(0, tb0);
+    if (grp == 1 && n_tiles > 1) issue(1, tb1);
+  }
+  // ---- u = q / rms(q), staged in tile buffer 3 (free until tile 3 is gathered)
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const uint32_t w4[4] = {qraw[ks].x, qraw[ks].y, qraw[ks].z, qraw[ks].w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float lo = __uint_as_float(w4[k] << 16), hi = __uint_as_float(w4[k] & 0xffff0000u);
-        ss = fmaf(lo, lo, fmaf(hi, hi, ss));
-      }
-    }
-    ss += __shfl_xor(ss, 32, 64);
-    qss[wave][lane] = ss;
-    lds_barrier();
-    ss = qss[0][lane] + qss[1][lane] + qss[2][lane] + qss[3][lane];
-    const float qinv = 1.f / sqrtf(ss * (1.f / kD) + A.eps);
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const uint32_t w4[4] = {qraw[ks].x, qraw[ks].y, qraw[ks].z, qraw[ks].w};
+  for (int j = 0; j < kQn; ++j) {
+    const int hq = wave + kSdWaves * j;
+    if (hq < 32) {
+      const uint4 v = qraw[j];
+      float ss = sumsq_bf16x8(v, 0.f);
+      ss = wave_sum(ss);
+      const float qinv = 1.f / sqrtf(ss * (1.f / kD) + A.eps);
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
       uint32_t o4[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k)
         o4[k] = pack_bf16x2(__uint_as_float(w4[k] << 16) * qinv, __uint_as_float(w4[k] & 0xffff0000u) * qinv);
-      qf[ks] = as_bf16x8(make_uint4(o4[0], o4[1], o4[2], o4[3]));
+      *(uint4*)(tb3 + hq * kRowB2 + 16 * lane) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
     }
   }
+  if (value_wave && grp == 0) wait_vmcnt<0>();
+  lds_barrier();   // q staged, tile 0 landed
+
   const float sl2 = A.scale * kLog2e;
   const float eps = A.eps;
-  float l_run = 0.f;
+  if (!value_wave) {
+    // ================================================================ logit waves
+    const int qw = wave;
+    const int g = lane >> 4, c16 = lane & 15;
+    bf16x8_t q0[16], q1[16];   // B fragments: heads c16 and 16 + c16, dims 32 ks + 8 g ..
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) {
+      q0[ks] = as_bf16x8(*(const uint4*)(tb3 + c16 * kRowB2 + 64 * ks + 16 * g));
+      q1[ks] = as_bf16x8(*(const uint4*)(tb3 + (16 + c16) * kRowB2 + 64 * ks + 16 * g));
+    }
+    float l0 = 0.f, l1 = 0.f;
+    // weight position of rows 4 g .. 4 g + 3 of this wave's 16-row step
+    const int ppos = 16 * qw + 4 * ((g >> 1) | ((g & 1) << 1));
+    auto step = [&](auto BUFC, int s) {
+      constexpr int BUF = decltype(BUFC)::value;
+      if (s < n_tiles) {
+        const uint8_t* tile = BUF == 0 ? tb0 : (BUF == 1 ? tb1 : (BUF == 2 ? tb2 : tb3));
+        const uint8_t* ka = tile + (16 * qw + c16) * kRowB2 + 16 * g;
+        f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+        float ss = 0.f;
+        constexpr int PF = 4;
+        uint4 a[PF];
+#pragma unroll
+        for (int j = 0; j < PF; ++j) a[j] = *(const uint4*)(ka + 64 * j);
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) {
+          const uint4 c = a[ks % PF];
+          if (ks + PF < 16) a[ks % PF] = *(const uint4*)(ka + 64 * (ks + PF));
+          s0 = mfma16x16x32(as_bf16x8(c), q0[ks], s0);
+          s1 = mfma16x16x32(as_bf16x8(c), q1[ks], s1);
+          ss = dot2_bf16(c.x, ss);
+          ss = dot2_bf16(c.y, ss);
+          ss = dot2_bf16(c.z, ss);
+          ss = dot2_bf16(c.w, ss);
+        }
+        ss += __shfl_xor(ss, 16, 64);
+        ss += __shfl_xor(ss, 32, 64);   // sum of squares of row c16
+        const bool ok = resolve(R.it0 + s * kTile + 16 * qw + c16) != nullptr;
+        const float irow = ok ? 1.f / sqrtf(ss * (1.f / kD) + eps) : 0.f;
+        uint8_t* const P = wts[s & 1];
+        float p0[4], p1[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float ir = __shfl(irow, 4 * g + r, 64);   // row 4 g + r
+          const float e0 = __builtin_amdgcn_exp2f(s0[r] * sl2 * ir);
+          const float e1 = __builtin_amdgcn_exp2f(s1[r] * sl2 * ir);
+          const float w0 = ir > 0.f ? e0 : 0.f, w1 = ir > 0.f ? e1 : 0.f;
+          l0 += w0;
+          l1 += w1;
+          p0[r] = w0 * ir;
+          p1[r] = w1 * ir;
+        }
+        *(uint2*)(P + c16 * kPRow + 2 * ppos) = make_uint2(pack_bf16x2(p0[0], p0[1]), pack_bf16x2(p0[2], p0[3]));
+        *(uint2*)(P + (16 + c16) * kPRow + 2 * ppos) =
+            make_uint2(pack_bf16x2(p1[0], p1[1]), pack_bf16x2(p1[2], p1[3]));
+      }
+      lds_barrier();
+    };
+    for (int s = 0; s <= n_tiles; s += 4) {
+      step(std::integral_constant<int, 0>{}, s);
+      if (s + 1 <= n_tiles) step(std::integral_constant<int, 1>{}, s + 1);
+      if (s + 2 <= n_tiles) step(std::integral_constant<int, 2>{}, s + 2);
+      if (s + 3 <= n_tiles) step(std::integral_constant<int, 3>{}, s + 3);
+    }
+    l0 += __shfl_xor(l0, 16, 64);
+    l0 += __shfl_xor(l0, 32, 64);
+    l1 += __shfl_xor(l1, 16, 64);
+    l1 += __shfl_xor(l1, 32, 64);
+    if (g == 0) {
+      lsum[qw][c16] = l0;
+      lsum[qw][16 + c16] = l1;
+    }
+    lds_barrier();   // the head sums are in LDS
+    if (wave == 0 && lane < 32) {
+      const float l = lsum[0][lane] + lsum[1][lane];
+      const int head = hg * 32 + lane;
+      if (L.nsplit == 1) {
+        if (A.lse) A.lse[row * A.heads + head] = l > 0.f ? logf(l) : -INFINITY;
+      } else {
+        float* pm = part_ml + (((long)row * L.nsplit + split) * A.heads + head) * 2;
+        pm[0] = l > 0.f ? 0.f : -INFINITY;
+        pm[1] = l;
+      }
+    }
+    return;
+  }
+  // ================================================================== value waves
+  const int h = lane >> 5, c32 = lane & 31;
+  const int G = lane >> 4, sl = lane & 15;
+  const int vb_off = (4 * h + (sl >> 2)) * kRowB2 + 256 * pw + (16 * (G & 1) + 4 * (sl & 3)) * 2;
   f32x16_t o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = f32x16_t{};
-
-  const int G = lane >> 4, sl = lane & 15;
-  const int vb_off = (4 * h + (sl >> 2)) * kRowB2 + 256 * wave + (16 * (G & 1) + 4 * (sl & 3)) * 2;
-  const int ka_off = c32 * kRowB2 + 256 * wave + 16 * h;
-
-  auto step = [&](auto BUFC, int ti) {
-    constexpr int BUF = decltype(BUFC)::value;
-    uint8_t* const tile = BUF == 0 ? tb0 : (BUF == 1 ? tb1 : tb2);
-    // this wave's rows of tile ti have landed (tile ti+1's may still be in flight)
-    if (ti + 1 < n_tiles) wait_vmcnt<kHgRpw>();
-    else wait_vmcnt<0>();
-    // ---- 1/rms of the rows this wave staged (written for the other waves)
-    {
-      float part[kHgRpw];
+  auto step = [&](auto BUFC, auto GRPC, int s) {
+    constexpr int K = decltype(BUFC)::value;   // s % 4
+    constexpr bool GATHER = (K & 1) == decltype(GRPC)::value;   // this group gathers tile s+2
+    constexpr int BI = (K + 2) % 4, BV = (K + 3) % 4;
+    uint8_t* const tin = BI == 0 ? tb0 : (BI == 1 ? tb1 : (BI == 2 ? tb2 : tb3));
+    const uint8_t* const tv = BV == 0 ? tb0 : (BV == 1 ? tb1 : (BV == 2 ? tb2 : tb3));
+    if (GATHER && s + 2 < n_tiles) issue(s + 2, tin);
+    if (s >= 1) {
+      const uint8_t* P = wts[(s - 1) & 1] + c32 * kPRow + 16 * h;
+      const bf16x8_t pb0 = as_bf16x8(*(const uint4*)P);
+      const bf16x8_t pb1 = as_bf16x8(*(const uint4*)(P + 32));
+      const uint8_t* vb = tv + vb_off;
+      i16x4_t v0[8], v1[8];
+      auto vaddr = [&](int k) { return vb + (16 * (k & 1)) * kRowB2 + 64 * (k >> 1); };   // k = 2 db + step
 #pragma unroll
-      for (int rr = 0; rr < kHgRpw; ++rr) {
-        const uint4 v = *(const uint4*)(tile + (wave + kHgWaves * rr) * kRowB2 + 16 * lane);
-        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-        float ss = 0.f;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float lo = __uint_as_float(w4[k] << 16), hi = __uint_as_float(w4[k] & 0xffff0000u);
-          ss = fmaf(lo, lo, fmaf(hi, hi, ss));
-        }
-        part[rr] = ss;
+      for (int k = 0; k < 8; ++k) {
+        v0[k] = lds_read_tr16(vaddr(k));
+        v1[k] = lds_read_tr16(vaddr(k) + 8 * kRowB2);
       }
-      row_totals<kHgRpw>(part, lane, irms[BUF], wave, kHgWaves, okm[BUF], eps);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        typedef short i16x8_t __attribute__((ext_vector_type(8)));
+        const i16x8_t vv = {v0[k][0], v0[k][1], v0[k][2], v0[k][3], v1[k][0], v1[k][1], v1[k][2], v1[k][3]};
+        o[k >> 1] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, vv), (k & 1) ? pb1 : pb0, o[k >> 1]);
+      }
     }
-    // ---- partial S^T over this wave's 128 dims: 8 k-steps of 16
-    f32x16_t s;
-    {
-      const uint8_t* ka = tile + ka_off;
-      uint4 a[8];
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) a[ks] = *(const uint4*)(ka + 32 * ks);
-      f32x16_t s2[2] = {f32x16_t{}, f32x16_t{}};
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) s2[ks & 1] = mfma32x32x16(as_bf16x8(a[ks]), qf[ks], s2[ks & 1]);
-      s = s2[0] + s2[1];
-    }
-    float (*const xb)[kXS][64] = xbuf[ti & 1];
-#pragma unroll
-    for (int r = 0; r < kXS; ++r) xb[wave][r][lane] = s[r];
-    // every wave is past the previous tile (its buffer is free) and this tile's
-    // partial S^T and row norms are in LDS
+    // the other group's step: tile s+1, gathered by this group at step s-1, has landed
+    if (!GATHER) wait_vmcnt<0>();
     lds_barrier();
-    if (ti + 2 < n_tiles) okm[(BUF + 2) % kNB] = issue(ti + 2, buf_ptr((BUF + 2) % kNB));
-    float ir[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) ir[r] = irms[BUF][8 * (r / 4) + 4 * h + (r % 4)];
-#pragma unroll
-    for (int w = 0; w < kHgWaves; ++w) {
-      if (w == wave) continue;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] += xb[w][r][lane];
-    }
-    // ---- softmax weights (exponents within [-100, 100]; a masked row has weight 0)
-    float psum = 0.f;
-    uint32_t pk[8];
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      float p2[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const float e = __builtin_amdgcn_exp2f(s[r + u] * sl2 * ir[r + u]);
-        const float p = ir[r + u] > 0.f ? e : 0.f;
-        psum += p;
-        p2[u] = p * ir[r + u];
-      }
-      pk[r / 2] = pack_bf16x2(p2[0], p2[1]);
-    }
-    l_run += psum;
-    const bf16x8_t pb0 = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
-    const bf16x8_t pb1 = as_bf16x8(make_uint4(pk[4], pk[5], pk[6], pk[7]));
-    // ---- O^T += V^T . P^T over this wave's 4 dim blocks
-    const uint8_t* vb = tile + vb_off;
-    i16x4_t v0[8], v1[8];
-    auto vaddr = [&](int k) { return vb + (16 * (k & 1)) * kRowB2 + 64 * (k >> 1); };   // k = 2*db + t
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      v0[k] = lds_read_tr16(vaddr(k));
-      v1[k] = lds_read_tr16(vaddr(k) + 8 * kRowB2);
-    }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      typedef short i16x8_t __attribute__((ext_vector_type(8)));
-      const i16x8_t vv = {v0[k][0], v0[k][1], v0[k][2], v0[k][3], v1[k][0], v1[k][1], v1[k][2], v1[k][3]};
-      o[k >> 1] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, vv), (k & 1) ? pb1 : pb0, o[k >> 1]);
+  };
+  auto run = [&](auto GRPC) {
+    for (int s = 0; s <= n_tiles; s += 4) {
+      step(std::integral_constant<int, 0>{}, GRPC, s);
+      if (s + 1 <= n_tiles) step(std::integral_constant<int, 1>{}, GRPC, s + 1);
+      if (s + 2 <= n_tiles) step(std::integral_constant<int, 2>{}, GRPC, s + 2);
+      if (s + 3 <= n_tiles) step(std::integral_constant<int, 3>{}, GRPC, s + 3);
     }
   };
-  for (int ti = 0; ti < n_tiles; ti += kNB) {
-    step(std::integral_constant<int, 0>{}, ti);
-    if (ti + 1 < n_tiles) step(std::integral_constant<int, 1>{}, ti + 1);
-    if (ti + 2 < n_tiles) step(std::integral_constant<int, 2>{}, ti + 2);
-  }
-
-  l_run += __shfl_xor(l_run, 32, 64);
-  // o[db][r] holds dim 128 w + 32 db + 8 (r/4) + 4 h + r%4 of this lane's head.  The
-  // 32 x 128 block goes through LDS (the tile buffers are free once every wave is
-  // past its last tile) so that each store instruction writes two whole head rows.
-  lds_barrier();
-  float* stage = (float*)((wave < 2 ? tb0 : tb1) + (wave & 1) * (32 * kStageRow * 4));
+  if (grp == 0) run(std::integral_constant<int, 0>{});
+  else run(std::integral_constant<int, 1>{});
+  lds_barrier();   // the head sums are in LDS
+  // o[db][r] holds dim 128 pw + 32 db + 8 (r/4) + 4 h + r%4 of head c32.  The
+  // 32 x 128 block goes through LDS (every tile buffer is free after the last step)
+  // so that each store instruction writes two whole head rows.
+  float* stage = (float*)(pw == 0 ? tb0 : (pw == 1 ? tb1 : (pw == 2 ? tb2 : tb3)));
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -797,27 +845,21 @@ void mqa_hg_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml) {
   __builtin_amdgcn_s_waitcnt(0xC07F);   // this wave's LDS writes are done (wave-private region)
   const int hl = lane >> 5, d4 = lane & 31;
   if (L.nsplit == 1) {
-    const float inv_l = l_run > 0.f ? 1.f / l_run : 0.f;   // l is per head: lane c32's head
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const int hh = 2 * k + hl;
-      const float il = __shfl(inv_l, hh, 64);
+      const float l = lsum[0][hh] + lsum[1][hh];
+      const float il = l > 0.f ? 1.f / l : 0.f;
       const f32x4_t v = *(const f32x4_t*)(stage + hh * kStageRow + 4 * d4);
-      uint16_t* orow = (uint16_t*)A.out + (row * A.heads + hg * 32 + hh) * kD + 128 * wave + 4 * d4;
+      uint16_t* orow = (uint16_t*)A.out + (row * A.heads + hg * 32 + hh) * kD + 128 * pw + 4 * d4;
       *(uint2*)orow = make_uint2(pack_bf16x2(v[0] * il, v[1] * il), pack_bf16x2(v[2] * il, v[3] * il));
     }
-    if (A.lse && h == 0 && wave == 0) A.lse[row * A.heads + head] = l_run > 0.f ? logf(l_run) : -INFINITY;
   } else {
-    float* po = part_o + (((long)row * L.nsplit + split) * A.heads + hg * 32) * kD + 128 * wave + 4 * d4;
+    float* po = part_o + (((long)row * L.nsplit + split) * A.heads + hg * 32) * kD + 128 * pw + 4 * d4;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const int hh = 2 * k + hl;
       *(f32x4_t*)(po + (long)hh * kD) = *(const f32x4_t*)(stage + hh * kStageRow + 4 * d4);
-    }
-    if (h == 0 && wave == 0) {
-      float* pm = part_ml + (((long)row * L.nsplit + split) * A.heads + head) * 2;
-      pm[0] = l_run > 0.f ? 0.f : -INFINITY;
-      pm[1] = l_run;
     }
   }
 }
@@ -1306,8 +1348,8 @@ static MqaLaunch plan_mqa(const MqaArgs& A) {
     // (about 4 MB per microsecond each way) and the merge is one more launch.
     double best = 1e30;
     for (int variant = 0; variant < 3; ++variant) {
-      // 0: 32-head workgroups (32 query rows at most); 1, 2: 8-wave 128-head
-      // workgroups with row norms from the gathered tiles / from the pre-pass
+      // 0: split-role 32-head workgroups (32 query rows at most); 1, 2: 8-wave
+      // 128-head workgroups with row norms from the gathered tiles / from the pre-pass
       const bool hg = variant == 0;
       const bool pre = variant == 2;
       if (hg && (A.heads % 32 != 0 || rows > 32)) continue;
@@ -1316,7 +1358,10 @@ static MqaLaunch plan_mqa(const MqaArgs& A) {
       const int n_hg = A.heads / wg_heads;
       // (the 8-wave kernel gathers only ~1.5 tiles ahead: on rows scattered over HBM,
       // as in sparse decode, it waits on memory)
-      const double t_tile = hg ? 2.5 : (pre ? 2.4 : (A.dense ? 3.0 : 5.0));
+      // (the split-role kernel is bound by how fast its two gathering waves issue
+      // rows: about 1.5 us a tile once every CU gathers; its start-up waits on the
+      // index slots, then on the first two tiles)
+      const double t_tile = hg ? 1.5 : (pre ? 2.4 : (A.dense ? 3.0 : 5.0));
       // the pre-pass reads every cached row once (~5 TB/s)
       const double t_norms = pre ? 3.0 + (double)A.batch * ((double)A.kv_cap + A.raw_cap) * (kD * 2) / 5.0e6 : 0.0;
       for (int sp = 1; sp <= kMaxSplit && sp <= tiles_max; ++sp) {
@@ -1328,14 +1373,14 @@ static MqaLaunch plan_mqa(const MqaArgs& A) {
         const double part_mb = s_eff > 1 ? wgs * wg_heads * kD * 4.0 / 1.0e6 : 0.0;
         // start-up: first gathers, and the workgroup's partial (256 KB for 128 heads)
         // leaving through one CU
-        const double t_start = hg ? 9.0 : (s_eff > 1 ? 13.0 : 4.0);
+        const double t_start = hg ? 15.0 : (s_eff > 1 ? 13.0 : 4.0);
         const double cost = t_norms + rounds * (t_start + tps * t_tile) + (s_eff > 1 ? 4.0 + part_mb / 2.0 : 0.0);
         if (cost < best - 1e-9) {
           best = cost;
-          L.kind = hg ? 2 : 3;
+          L.kind = hg ? 4 : 3;
           L.pre = pre ? 1 : 0;
           L.n_hg = n_hg;
-          L.nw = hg ? kHgWaves : kW8Waves;
+          L.nw = hg ? kSdWaves : kW8Waves;
           L.ips = tps * kTile;
           L.nsplit = s_eff;
         }
@@ -1449,12 +1494,12 @@ hipError_t launch_mqa(const MqaArgs& A, void* ws, size_t ws_bytes, hipStream_t s
   dim3 grid((unsigned)(groups * 8 * L.n_hg));
   if (L.kind == 3) grid = dim3((unsigned)((((long)L.units * L.n_hg + 7) / 8) * 8));
   {
-    LaunchTimer timer(L.kind == 3 ? "mqa_bf16_w8" : (L.kind == 2 ? "mqa_bf16_hg" : "mqa_bf16_h16"), s);
+    LaunchTimer timer(L.kind == 3 ? "mqa_bf16_w8" : (L.kind == 4 ? "mqa_bf16_sd" : "mqa_bf16_h16"), s);
     if (L.kind == 3 && L.pre)
       mqa_w8_kernel<true><<<grid, kW8Waves * 64, lds, s>>>(A, L, part_o, part_ml, inv_kv, inv_raw);
     else if (L.kind == 3)
       mqa_w8_kernel<false><<<grid, kW8Waves * 64, lds, s>>>(A, L, part_o, part_ml, nullptr, nullptr);
-    else if (L.kind == 2) mqa_hg_kernel<<<grid, kHgWaves * 64, lds, s>>>(A, L, part_o, part_ml);
+    else if (L.kind == 4) mqa_sd_kernel<<<grid, kSdWaves * 64, lds, s>>>(A, L, part_o, part_ml);
     else if (L.nw == 4) mqa_bf16_kernel<4><<<grid, 4 * 64, lds, s>>>(A, L, part_o, part_ml);
     else if (L.nw == 2) mqa_bf16_kernel<2><<<grid, 2 * 64, lds, s>>>(A, L, part_o, part_ml);
     else mqa_bf16_kernel<1><<<grid, 64, lds, s>>>(A, L, part_o, part_ml);

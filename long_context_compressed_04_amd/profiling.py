@@ -33,7 +33,7 @@ KERNELS = {
     "index_scores_f32": (r"index_scores_f32", "indexer.hip"),
     "topk": (r"topk_", "topk.hip"),
     "mqa_bf16_w8": (r"mqa_w8_kernel", "mqa.hip"),
-    "mqa_bf16_hg": (r"mqa_hg_kernel", "mqa.hip"),
+    "mqa_bf16_sd": (r"mqa_sd_kernel", "mqa.hip"),
     "mqa_bf16_h16": (r"mqa_bf16_kernel<", "mqa.hip"),
     "mqa_f32": (r"mqa_f32_kernel", "mqa.hip"),
     "mqa_combine": (r"mqa_combine_kernel", "mqa.hip"),
