@@ -98,8 +98,9 @@ csa::IndexArgs index_args(const csa_index_desc* d, const void* q, const uint8_t*
   return A;
 }
 
+// Score rows, with 16 bytes of slack: the top-k kernels read rows 16 bytes at a time.
 size_t scores_ws(const csa_index_desc* d) {
-  return round256(sizeof(float) * (size_t)d->batch * d->n_q * (size_t)d->n_max);
+  return round256(sizeof(float) * (size_t)d->batch * d->n_q * (size_t)d->n_max + 16);
 }
 size_t index_ws(const csa_index_desc* d) {
   csa::IndexArgs A{};
@@ -225,7 +226,8 @@ static size_t rescore_ws(const csa_index_desc* d, int32_t cand) {
   csa_index_desc dc = *d;
   dc.topk = cand;
   const size_t rows = (size_t)d->batch * d->n_q;
-  return index_ws(&dc) + 2 * round256(rows * (size_t)cand * sizeof(int32_t));
+  return index_ws(&dc) + round256(rows * (size_t)cand * sizeof(int32_t)) +
+         round256(rows * (size_t)cand * sizeof(float) + 16);   // (rescored rows: 16 bytes of slack)
 }
 
 size_t csa_index_rescored_workspace_size(const csa_index_desc* d, int32_t cand) {

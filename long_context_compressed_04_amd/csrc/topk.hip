@@ -9,17 +9,19 @@
 // The selected set is exact: "score descending, ties to the lower index", written
 // in ascending index order and -1 padded.  Scores map to order-preserving uint32
 // keys.  One 1024-thread workgroup selects one row:
-//  - the keys stay in registers (thread t holds positions 1024 j + t, loaded
-//    coalesced with raw buffer loads that return 0 past the row);
+//  - the keys stay in registers (thread t holds the KPT consecutive positions
+//    KPT t .. KPT t + KPT - 1, loaded 16 bytes at a time with raw buffer loads that
+//    return 0 past the row);
 //  - threshold: below the bits every key shares, an 11-bit radix digit is counted
 //    in a 2048-bin LDS histogram (padded so that one wave reads it without bank
 //    conflicts) and one wave finds the bin of the k-th largest key with two
 //    cross-lane scans.  A bin of at most 64 keys is then resolved exactly by one
 //    wave, bit by bit with ballots; larger bins take further 11-bit passes;
-//  - compaction: two ballots per (round, wave) cell record which keys lie above the
-//    threshold and which equal it; one wave scans the cells in position order; each
-//    thread then writes its selected keys to their output slots (keys above before
-//    it plus the equal keys before it, capped at the number still needed).
+//  - compaction: each thread counts its keys above the threshold and equal to it;
+//    exclusive scans over the threads (which are in position order) give each key
+//    its output slot (keys above before it plus the equal keys before it, capped at
+//    the number still needed); the selection is assembled in LDS and written out
+//    with coalesced stores.
 // Rows longer than kRegKeys take two launches.  Many workgroups each derive the same
 // threshold from a fixed sample of kSample keys (expected to pass about 3k keys) and
 // filter their chunks of the row against it into per-chunk candidate lists (index
@@ -46,16 +48,15 @@ constexpr int kMaxChunks = 2048;
 constexpr int kBins = 2048;           // 11-bit radix digit
 constexpr int kHistWords = kBins + kBins / 32;
 constexpr int kBucketMax = 64;
+constexpr int kMaxTopk = 8192;        // largest k: the C ABI's 4096, or a rescoring prefilter's candidates
 
 struct SelShared {
   uint32_t hist[kHistWords];          // bin b at b + b / 32
   uint32_t red[2 * kTW];
   uint32_t wcnt[2 * kTW];
-  uint64_t gmask[kMaxKpt * kTW];      // per (round, wave) cell: keys above the threshold
-  uint64_t emask[kMaxKpt * kTW];      // ... and keys equal to it
-  uint32_t gbase[kMaxKpt * kTW];      // ... and how many of each come before the cell
-  uint32_t ebase[kMaxKpt * kTW];
   uint32_t bkey[kBucketMax];
+  int32_t oidx[kMaxTopk];             // the selection in output order, written out coalesced
+  uint32_t okey[kMaxTopk];
   uint32_t bcount;
   uint32_t s_prefix, s_need, s_cnt;
 };
@@ -190,9 +191,10 @@ __device__ __forceinline__ void radix_passes(HistKeys hist_keys, Bucket bucket, 
   }
 }
 
-// ---- keys held in registers: key[j] is position 1024 j + t; positions >= n are
+// ---- keys held in registers: key[j] is position KPT t + j; positions >= n are
 // never counted
-__device__ __forceinline__ bool valid_pos(int j, int n) { return kTopkThreads * j + (int)threadIdx.x < n; }
+template <int KPT>
+__device__ __forceinline__ bool valid_pos(int j, int n) { return KPT * (int)threadIdx.x + j < n; }
 
 // Finds (prefix, mask, need): the k largest of the n keys are every key with
 // (key & mask) > prefix plus the first `need` keys (in position order) with
@@ -204,7 +206,7 @@ __device__ __forceinline__ void reg_threshold(const uint32_t (&key)[KPT], int n,
   uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
-    if (valid_pos(j, n)) {
+    if (valid_pos<KPT>(j, n)) {
       kmin = min(kmin, key[j]);
       kmax = max(kmax, key[j]);
     }
@@ -217,7 +219,7 @@ __device__ __forceinline__ void reg_threshold(const uint32_t (&key)[KPT], int n,
   auto hist = [&](uint32_t msk, uint32_t pre, int shift, uint32_t dmask) {
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-      if (valid_pos(j, n) && (key[j] & msk) == pre) atomicAdd(&sh.hist[hslot((key[j] >> shift) & dmask)], 1u);
+      if (valid_pos<KPT>(j, n) && (key[j] & msk) == pre) atomicAdd(&sh.hist[hslot((key[j] >> shift) & dmask)], 1u);
     }
   };
   // a bucket of <= 64 keys: gather it, and let one wave find the need-th largest
@@ -226,7 +228,7 @@ __device__ __forceinline__ void reg_threshold(const uint32_t (&key)[KPT], int n,
   auto bucket = [&](uint32_t pre, uint32_t msk, uint32_t nd, uint32_t cnt) {
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-      const bool in = valid_pos(j, n) && (key[j] & msk) == pre;
+      const bool in = valid_pos<KPT>(j, n) && (key[j] & msk) == pre;
       const uint64_t bm = __ballot(in);
       if (bm) {   // uniform: one slot reservation per wave and round
         uint32_t base = 0;
@@ -271,73 +273,51 @@ __device__ __forceinline__ void reg_threshold(const uint32_t (&key)[KPT], int n,
 
 // Writes the selection in position order: out_idx[p] = idx_of(j) for this thread's
 // key[j] when it is the p-th selected position, out_score[p] its score.  Exactly k
-// slots are written.
+// slots are written: first to LDS at their output slots, then copied out in order.
 template <int KPT, class IdxOf>
 __device__ __forceinline__ void reg_compact(const uint32_t (&key)[KPT], int n, uint32_t prefix, uint32_t mask,
                                             uint32_t need, int k, IdxOf idx_of, int32_t* oi, float* os,
                                             SelShared& sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // ballots per round; lane j of the wave keeps round j's two masks
-  uint32_t glo = 0, ghi = 0, elo = 0, ehi = 0;
+  static_assert(KPT <= 16, "two class bits per key in one word");
+  // class of key j in bits 2j (above the threshold) and 2j+1 (equal to it)
+  uint32_t cls = 0;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
-    const bool v = valid_pos(j, n);
+    const bool v = valid_pos<KPT>(j, n);
     const uint32_t kp = key[j] & mask;
-    const uint64_t g = __ballot(v && kp > prefix);
-    const uint64_t e = __ballot(v && kp == prefix);
-    if (lane == j) {
-      glo = (uint32_t)g;
-      ghi = (uint32_t)(g >> 32);
-      elo = (uint32_t)e;
-      ehi = (uint32_t)(e >> 32);
-    }
+    cls |= ((v && kp > prefix) ? 1u : 0u) << (2 * j);
+    cls |= ((v && kp == prefix) ? 2u : 0u) << (2 * j);
   }
-  if (lane < KPT) {
-    sh.gmask[lane * kTW + wave] = ((uint64_t)ghi << 32) | glo;
-    sh.emask[lane * kTW + wave] = ((uint64_t)ehi << 32) | elo;
+  const uint32_t ng = (uint32_t)__popc(cls & 0x55555555u), ne = (uint32_t)__popc(cls & 0xAAAAAAAAu);
+  // exclusive scans in position order: within the wave, then over the waves before
+  const uint32_t ig = wave_inclusive_sum(ng), ie = wave_inclusive_sum(ne);
+  if (lane == 63) {
+    sh.wcnt[wave] = ig;
+    sh.wcnt[kTW + wave] = ie;
   }
   __syncthreads();
-  // cells c = round * kTW + wave are in position order: one wave scans them (lane l
-  // takes C consecutive cells) into per-cell bases
-  if (wave == 0) {
-    constexpr int C = KPT * kTW / 64;
-    uint32_t cg[C], ce[C], sg = 0, se = 0;
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-      cg[c] = (uint32_t)__popcll(sh.gmask[lane * C + c]);
-      ce[c] = (uint32_t)__popcll(sh.emask[lane * C + c]);
-      sg += cg[c];
-      se += ce[c];
-    }
-    uint32_t gb = wave_inclusive_sum(sg) - sg;
-    uint32_t eb = wave_inclusive_sum(se) - se;
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-      sh.gbase[lane * C + c] = gb;
-      sh.ebase[lane * C + c] = eb;
-      gb += cg[c];
-      eb += ce[c];
-    }
-  }
-  __syncthreads();
-  const uint32_t bgl = lane < KPT ? sh.gbase[lane * kTW + wave] : 0u;
-  const uint32_t bel = lane < KPT ? sh.ebase[lane * kTW + wave] : 0u;
+  const uint32_t wg = lane < wave ? sh.wcnt[lane] : 0u;
+  const uint32_t we = lane < wave ? sh.wcnt[kTW + lane] : 0u;
+  uint32_t gb = (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_sum(wg), 63) + ig - ng;
+  uint32_t eb = (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_sum(we), 63) + ie - ne;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
-    const uint64_t G = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)ghi, j) << 32) |
-                       (uint32_t)__builtin_amdgcn_readlane((int)glo, j);
-    const uint64_t E = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)ehi, j) << 32) |
-                       (uint32_t)__builtin_amdgcn_readlane((int)elo, j);
-    const uint32_t gb = (uint32_t)__builtin_amdgcn_readlane((int)bgl, j);
-    const uint32_t eb = (uint32_t)__builtin_amdgcn_readlane((int)bel, j);
-    const uint64_t bit = 1ull << lane;
-    const uint32_t eq_before = eb + lanes_below(E);
-    const bool sel = (G & bit) || ((E & bit) && eq_before < need);
-    const uint32_t p = gb + lanes_below(G) + min(eq_before, need);
+    const uint32_t c = (cls >> (2 * j)) & 3u;
+    const bool g = c == 1u, e = c == 2u;
+    const bool sel = g || (e && eb < need);
+    const uint32_t p = gb + min(eb, need);
     if (sel && p < (uint32_t)k) {
-      oi[p] = idx_of(j);
-      if (os) os[p] = key_to_float(key[j]);
+      sh.oidx[p] = idx_of(j);
+      sh.okey[p] = key[j];
     }
+    gb += g ? 1u : 0u;
+    eb += e ? 1u : 0u;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < k; i += kTopkThreads) {
+    oi[i] = sh.oidx[i];
+    if (os) os[i] = key_to_float(sh.okey[i]);
   }
 }
 
@@ -430,14 +410,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t float_rsrc(const float* p, int
   return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, n_valid * 4, 0x00020000);
 }
 
-// One row of V <= KPT * 1024 scores, held in registers (key[] loaded by load_row).
+// One row of V <= KPT * 1024 scores, held in registers (key[] loaded by load_row),
+// 16 bytes per load.  The range covers n rounded up to four positions: score rows
+// live in the library's workspace, which keeps 16 bytes of slack after them, and the
+// positions past n are never counted.
 template <int KPT>
 __device__ __forceinline__ void load_row(const float* src, int n, uint32_t (&key)[KPT]) {
-  const __amdgpu_buffer_rsrc_t rs = float_rsrc(src, n);
+  const __amdgpu_buffer_rsrc_t rs = float_rsrc(src, (n + 3) & ~3);
+  static_assert(KPT % 4 == 0, "keys are loaded four at a time");
 #pragma unroll
-  for (int j = 0; j < KPT; ++j)
-    key[j] = order_key(
-        __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (int)threadIdx.x * 4, j * kTopkThreads * 4, 0)));
+  for (int q = 0; q < KPT / 4; ++q) {
+    typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, ((int)threadIdx.x * KPT + 4 * q) * 4, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) key[4 * q + i] = order_key(__uint_as_float(v[i]));
+  }
 }
 
 template <int KPT>
@@ -446,7 +433,7 @@ __device__ __forceinline__ void select_reg_row(uint32_t (&key)[KPT], int V, int 
   uint32_t prefix, mask, need;
   reg_threshold<KPT>(key, V, (uint32_t)k, sh, prefix, mask, need);
   auto idx_of = [map](int j) {
-    const int p = kTopkThreads * j + (int)threadIdx.x;
+    const int p = KPT * (int)threadIdx.x + j;
     return map ? map[p] : p;
   };
   reg_compact<KPT>(key, V, prefix, mask, need, k, idx_of, oi, os, sh);
@@ -563,7 +550,7 @@ __device__ __forceinline__ void select_candidates(const uint32_t* gk, const int3
   uint32_t key[KPT];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
-    const int c = kTopkThreads * j + (int)threadIdx.x;
+    const int c = KPT * (int)threadIdx.x + j;
     key[j] = 0u;
     if (c < M) {
       int lo = 0, hi = nch - 1;   // chunk holding candidate c: last chunk whose offset is <= c
@@ -579,7 +566,7 @@ __device__ __forceinline__ void select_candidates(const uint32_t* gk, const int3
   }
   uint32_t prefix, mask, need;
   reg_threshold<KPT>(key, M, (uint32_t)k, sh, prefix, mask, need);   // (its barriers publish cand_idx)
-  auto idx_of = [&](int j) { return cand_idx[kTopkThreads * j + threadIdx.x]; };
+  auto idx_of = [&](int j) { return cand_idx[KPT * threadIdx.x + j]; };
   reg_compact<KPT>(key, M, prefix, mask, need, k, idx_of, oi, os, sh);
 }
 
@@ -648,6 +635,7 @@ hipError_t launch_topk_rows(const IndexArgs& A, const float* scores, int32_t* ou
                             size_t ws_bytes, hipStream_t s) {
   const long rows = (long)A.batch * A.n_q;
   if (rows <= 0) return hipSuccess;
+  if (A.topk < 1 || A.topk > kMaxTopk) return hipErrorInvalidValue;
   LaunchTimer timer("topk", s);
   const dim3 grid((unsigned)rows);
   if (A.n_max <= kRegKeys) {

@@ -141,6 +141,7 @@ def test_index_scores_and_topk(dtype, B, n_q, HI, dI, N, m, k):
     (1, 2, 64, 700, 100, 400),
     (1, 1, 128, 300, 64, 4096),       # fewer visible entries than candidates
     (1, 1, 64, 40, 64, 128),          # fewer visible entries than k
+    (1, 1, 64, 12000, 64, 8192),      # the largest prefilter, on one workgroup's row
 ])
 def test_index_topk_rescored(B, n_q, HI, N, k, cand):
     """MXFP4 prefilter of `cand` entries, bf16 rescoring, top-k: the GPU set against the
