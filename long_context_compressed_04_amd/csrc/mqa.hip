@@ -16,9 +16,9 @@
 // bf16 kernels (head_dim 512), chosen by the host:
 //  - mqa_w8_kernel (unit RMSNorm weight): 8 waves = the 128 heads of a (query,
 //    split) unit, two waves per SIMD; prefill, dense HCA decode;
-//  - mqa_sd_kernel (few queries, unit weight): 6 waves = one group of 32 heads of a
-//    (query, split) unit, split into logit and value roles on a software pipeline;
-//    sparse decode;
+//  - mqa_sd_kernel (few queries, unit weight): 16 waves = one group of 32 heads of a
+//    (query, split) unit, split into logit, value and gather roles on a software
+//    pipeline; sparse and dense decode;
 //  - mqa_bf16_kernel (any RMSNorm weight): NW waves x 16 heads with an online
 //    (running maximum) softmax.
 // All stage 32-row item tiles in LDS (row-major, padded) and form S^T = K . u^T and
@@ -583,29 +583,31 @@ struct RowSrc {
 
 // ---------------------------------------------------------------------------------
 // Split-role decode kernel: one workgroup = one group of 32 heads of a (query,
-// split) unit, six waves in two roles on a software pipeline over 32-row tiles
+// split) unit, sixteen waves in three roles on a software pipeline over 32-row tiles
 // (step s: tile s weighed while tile s-1 is accumulated and tile s+2 is gathered):
-//  - logit waves 0, 1: rows 16 w .. 16 w + 15 of tile s against all 32 heads and all
-//    512 dims, S^T on v_mfma_f32_16x16x32_bf16 (A = K rows, B = normalised q held in
-//    registers), the rows' sums of squares from the same A fragments by bf16 dot
-//    products, then the softmax weights of their 16 rows x 32 heads into LDS: no
-//    partial logits cross waves and no weight is formed twice;
-//  - value waves 2..5: O^T for dims 128 (w - 2) .. of tile s-1 on
-//    v_mfma_f32_32x32x16_bf16 (A = V^T by transposing LDS reads, B = the weights
-//    of the previous step); waves 2, 3 gather (direct-to-LDS) the even tiles and
-//    waves 4, 5 the odd ones, tile s+2 at step s, and wait for it at the end of step
-//    s+1, so each wave's wait is for all of its loads (a count the compiler can
-//    follow: it sees a rolled gather loop as one load).
+//  - logit waves 0..3: wave w takes rows 16 (w >> 1) .. + 15 of tile s against heads
+//    16 (w & 1) .. + 15 over all 512 dims, S^T on v_mfma_f32_16x16x32_bf16 (A = K
+//    rows, B = normalised q held in registers), the rows' sums of squares from the
+//    same A fragments by bf16 dot products, then the softmax weights into LDS: no
+//    partial logits cross waves;
+//  - value waves 4..7: O^T for dims 128 (w - 4) .. of tile s-1 on
+//    v_mfma_f32_32x32x16_bf16 (A = V^T by transposing LDS reads, B = the weights of
+//    the previous step);
+//  - gather waves 8..15: the rows of tile s+2, four each, by direct-to-LDS loads.
+//    A wave issues a row only every hundred-odd cycles, so the gather rate of a CU
+//    grows with the number of waves issuing; these waves read no tile buffer, so
+//    waiting for all but their last four loads needs no help from the compiler.
 // One barrier per step; four tile buffers: two tiles in flight, one being weighed,
 // one being accumulated.  The weights are stored per head in the order the B operand
 // of the 32x32x16 product consumes its k index (rows 4 kg .. 4 kg + 3 and
 // 8 + 4 kg .. of each 16-row step in lane half kg), so each value wave reads one
 // 16-byte fragment per step and head.
-constexpr int kSdQk = 2, kSdPv = 4, kSdWaves = kSdQk + kSdPv;
-constexpr int kSdRpw = kTile / 2;       // rows each gathering value wave loads per tile
+constexpr int kSdQk = 4, kSdPv = 4, kSdGa = 8;
+constexpr int kSdWaves = kSdQk + kSdPv + kSdGa;
+constexpr int kSdRpw = kTile / kSdGa;   // rows each gather wave loads per tile
 constexpr int kPRow = 2 * kTile + 16;   // bytes per head row of a weight buffer (padded)
 
-__global__ __launch_bounds__(kSdWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kSdWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void mqa_sd_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml) {
   __shared__ __attribute__((aligned(16))) uint8_t tb0[kTile * kRowB2];
   __shared__ __attribute__((aligned(16))) uint8_t tb1[kTile * kRowB2];
@@ -613,7 +615,7 @@ void mqa_sd_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml) {
   __shared__ __attribute__((aligned(16))) uint8_t tb3[kTile * kRowB2];
   __shared__ __attribute__((aligned(16))) uint8_t wts[2][32 * kPRow];
   __shared__ int32_t slot[kSlotsLds];
-  __shared__ float lsum[kSdQk][32];
+  __shared__ float lsum[2][32];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -626,15 +628,13 @@ void mqa_sd_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml) {
   const int split = unit % L.nsplit;
   const int b = (int)(row / A.n_q);
 
-  // raw q rows of the heads this wave normalises (heads wave + 6 j), 16 bytes a lane;
+  // raw q rows of the heads this wave normalises (heads wave + 16 j), 16 bytes a lane;
   // loaded before the slots, so waiting for the slots has waited for them too
-  constexpr int kQn = (32 + kSdWaves - 1) / kSdWaves;
+  constexpr int kQn = 32 / kSdWaves;
   uint4 qraw[kQn];
 #pragma unroll
-  for (int j = 0; j < kQn; ++j) {
-    const int hq = wave + kSdWaves * j;
-    if (hq < 32) qraw[j] = *(const uint4*)((const uint16_t*)A.q + (row * A.heads + hg * 32 + hq) * kD + 8 * lane);
-  }
+  for (int j = 0; j < kQn; ++j)
+    qraw[j] = *(const uint4*)((const uint16_t*)A.q + (row * A.heads + hg * 32 + wave + kSdWaves * j) * kD + 8 * lane);
   // ---- the items of this (query, split): index slots to LDS
   RowSrc R;
   {
@@ -666,57 +666,53 @@ void mqa_sd_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml) {
     return (r >= 0 && r < R.raw_cap) ? R.raw + (long)r * (kD * 2) : nullptr;
   };
   const int n_tiles = (R.it1 - R.it0 + kTile - 1) / kTile;
-  const bool value_wave = wave >= kSdQk;
-  const int pw = wave - kSdQk;
-  const int grp = pw >> 1;   // gathers tiles t with t % 2 == grp
+  const int gw = wave - kSdQk - kSdPv;   // gather-wave index (>= 0 for gather waves)
   auto issue = [&](int t, uint8_t* dst) {
-    issue_rows<kSdRpw, 2>(resolve, R.it0 + t * kTile + (pw & 1), lane, dst + (pw & 1) * kRowB2);
+    issue_rows<kSdRpw, kSdGa>(resolve, R.it0 + t * kTile + gw, lane, dst + gw * kRowB2);
   };
-  if (value_wave) {
-    if (grp == 0 && n_tiles > 0) issue(0, tb0);
-    if (grp == 1 && n_tiles > 1) issue(1, tb1);
+  if (gw >= 0) {
+    if (n_tiles > 0) issue(0, tb0);
+    if (n_tiles > 1) issue(1, tb1);
   }
   // ---- u = q / rms(q), staged in tile buffer 3 (free until tile 3 is gathered)
 #pragma unroll
   for (int j = 0; j < kQn; ++j) {
     const int hq = wave + kSdWaves * j;
-    if (hq < 32) {
-      const uint4 v = qraw[j];
-      float ss = sumsq_bf16x8(v, 0.f);
-      ss = wave_sum(ss);
-      const float qinv = 1.f / sqrtf(ss * (1.f / kD) + A.eps);
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-      uint32_t o4[4];
+    const uint4 v = qraw[j];
+    const float ss = wave_sum(sumsq_bf16x8(v, 0.f));
+    const float qinv = 1.f / sqrtf(ss * (1.f / kD) + A.eps);
+    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o4[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        o4[k] = pack_bf16x2(__uint_as_float(w4[k] << 16) * qinv, __uint_as_float(w4[k] & 0xffff0000u) * qinv);
-      *(uint4*)(tb3 + hq * kRowB2 + 16 * lane) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
-    }
+    for (int k = 0; k < 4; ++k)
+      o4[k] = pack_bf16x2(__uint_as_float(w4[k] << 16) * qinv, __uint_as_float(w4[k] & 0xffff0000u) * qinv);
+    *(uint4*)(tb3 + hq * kRowB2 + 16 * lane) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
   }
-  if (value_wave && grp == 0) wait_vmcnt<0>();
+  if (gw >= 0) {
+    if (n_tiles > 1) wait_vmcnt<kSdRpw>();
+    else wait_vmcnt<0>();
+  }
   lds_barrier();   // q staged, tile 0 landed
 
   const float sl2 = A.scale * kLog2e;
   const float eps = A.eps;
-  if (!value_wave) {
+  if (wave < kSdQk) {
     // ================================================================ logit waves
-    const int qw = wave;
+    const int hb = wave & 1, rb = wave >> 1;
     const int g = lane >> 4, c16 = lane & 15;
-    bf16x8_t q0[16], q1[16];   // B fragments: heads c16 and 16 + c16, dims 32 ks + 8 g ..
+    bf16x8_t qf[16];   // B fragments: head 16 hb + c16, dims 32 ks + 8 g ..
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      q0[ks] = as_bf16x8(*(const uint4*)(tb3 + c16 * kRowB2 + 64 * ks + 16 * g));
-      q1[ks] = as_bf16x8(*(const uint4*)(tb3 + (16 + c16) * kRowB2 + 64 * ks + 16 * g));
-    }
-    float l0 = 0.f, l1 = 0.f;
+    for (int ks = 0; ks < 16; ++ks)
+      qf[ks] = as_bf16x8(*(const uint4*)(tb3 + (16 * hb + c16) * kRowB2 + 64 * ks + 16 * g));
+    float lh = 0.f;
     // weight position of rows 4 g .. 4 g + 3 of this wave's 16-row step
-    const int ppos = 16 * qw + 4 * ((g >> 1) | ((g & 1) << 1));
+    const int ppos = 16 * rb + 4 * ((g >> 1) | ((g & 1) << 1));
     auto step = [&](auto BUFC, int s) {
       constexpr int BUF = decltype(BUFC)::value;
       if (s < n_tiles) {
         const uint8_t* tile = BUF == 0 ? tb0 : (BUF == 1 ? tb1 : (BUF == 2 ? tb2 : tb3));
-        const uint8_t* ka = tile + (16 * qw + c16) * kRowB2 + 16 * g;
-        f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+        const uint8_t* ka = tile + (16 * rb + c16) * kRowB2 + 16 * g;
+        f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
         float ss = 0.f;
         constexpr int PF = 4;
         uint4 a[PF];
@@ -726,33 +722,28 @@ void mqa_sd_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml) {
         for (int ks = 0; ks < 16; ++ks) {
           const uint4 c = a[ks % PF];
           if (ks + PF < 16) a[ks % PF] = *(const uint4*)(ka + 64 * (ks + PF));
-          s0 = mfma16x16x32(as_bf16x8(c), q0[ks], s0);
-          s1 = mfma16x16x32(as_bf16x8(c), q1[ks], s1);
+          sacc[ks & 1] = mfma16x16x32(as_bf16x8(c), qf[ks], sacc[ks & 1]);
           ss = dot2_bf16(c.x, ss);
           ss = dot2_bf16(c.y, ss);
           ss = dot2_bf16(c.z, ss);
           ss = dot2_bf16(c.w, ss);
         }
+        const f32x4_t sv = sacc[0] + sacc[1];
         ss += __shfl_xor(ss, 16, 64);
         ss += __shfl_xor(ss, 32, 64);   // sum of squares of row c16
-        const bool ok = resolve(R.it0 + s * kTile + 16 * qw + c16) != nullptr;
+        const bool ok = resolve(R.it0 + s * kTile + 16 * rb + c16) != nullptr;
         const float irow = ok ? 1.f / sqrtf(ss * (1.f / kD) + eps) : 0.f;
-        uint8_t* const P = wts[s & 1];
-        float p0[4], p1[4];
+        float p[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float ir = __shfl(irow, 4 * g + r, 64);   // row 4 g + r
-          const float e0 = __builtin_amdgcn_exp2f(s0[r] * sl2 * ir);
-          const float e1 = __builtin_amdgcn_exp2f(s1[r] * sl2 * ir);
-          const float w0 = ir > 0.f ? e0 : 0.f, w1 = ir > 0.f ? e1 : 0.f;
-          l0 += w0;
-          l1 += w1;
-          p0[r] = w0 * ir;
-          p1[r] = w1 * ir;
+          const float e = __builtin_amdgcn_exp2f(sv[r] * sl2 * ir);
+          const float w = ir > 0.f ? e : 0.f;
+          lh += w;
+          p[r] = w * ir;
         }
-        *(uint2*)(P + c16 * kPRow + 2 * ppos) = make_uint2(pack_bf16x2(p0[0], p0[1]), pack_bf16x2(p0[2], p0[3]));
-        *(uint2*)(P + (16 + c16) * kPRow + 2 * ppos) =
-            make_uint2(pack_bf16x2(p1[0], p1[1]), pack_bf16x2(p1[2], p1[3]));
+        *(uint2*)(wts[s & 1] + (16 * hb + c16) * kPRow + 2 * ppos) =
+            make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
       }
       lds_barrier();
     };
@@ -762,14 +753,9 @@ void mqa_sd_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml) {
       if (s + 2 <= n_tiles) step(std::integral_constant<int, 2>{}, s + 2);
       if (s + 3 <= n_tiles) step(std::integral_constant<int, 3>{}, s + 3);
     }
-    l0 += __shfl_xor(l0, 16, 64);
-    l0 += __shfl_xor(l0, 32, 64);
-    l1 += __shfl_xor(l1, 16, 64);
-    l1 += __shfl_xor(l1, 32, 64);
-    if (g == 0) {
-      lsum[qw][c16] = l0;
-      lsum[qw][16 + c16] = l1;
-    }
+    lh += __shfl_xor(lh, 16, 64);
+    lh += __shfl_xor(lh, 32, 64);
+    if (g == 0) lsum[rb][16 * hb + c16] = lh;
     lds_barrier();   // the head sums are in LDS
     if (wave == 0 && lane < 32) {
       const float l = lsum[0][lane] + lsum[1][lane];
@@ -784,20 +770,33 @@ void mqa_sd_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml) {
     }
     return;
   }
+  if (gw >= 0) {
+    // ================================================================= gather waves
+    for (int s = 0; s <= n_tiles; ++s) {
+      const int t = s + 2;
+      if (t < n_tiles) {
+        const int bi = t & 3;
+        issue(t, bi == 0 ? tb0 : (bi == 1 ? tb1 : (bi == 2 ? tb2 : tb3)));
+        wait_vmcnt<kSdRpw>();   // tile s+1 has landed; tile s+2 may still be in flight
+      } else {
+        wait_vmcnt<0>();
+      }
+      lds_barrier();
+    }
+    lds_barrier();   // the head sums are in LDS
+    return;
+  }
   // ================================================================== value waves
+  const int pw = wave - kSdQk;
   const int h = lane >> 5, c32 = lane & 31;
   const int G = lane >> 4, sl = lane & 15;
   const int vb_off = (4 * h + (sl >> 2)) * kRowB2 + 256 * pw + (16 * (G & 1) + 4 * (sl & 3)) * 2;
   f32x16_t o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = f32x16_t{};
-  auto step = [&](auto BUFC, auto GRPC, int s) {
-    constexpr int K = decltype(BUFC)::value;   // s % 4
-    constexpr bool GATHER = (K & 1) == decltype(GRPC)::value;   // this group gathers tile s+2
-    constexpr int BI = (K + 2) % 4, BV = (K + 3) % 4;
-    uint8_t* const tin = BI == 0 ? tb0 : (BI == 1 ? tb1 : (BI == 2 ? tb2 : tb3));
+  auto step = [&](auto BUFC, int s) {
+    constexpr int BV = (decltype(BUFC)::value + 3) % 4;   // tile s-1's buffer
     const uint8_t* const tv = BV == 0 ? tb0 : (BV == 1 ? tb1 : (BV == 2 ? tb2 : tb3));
-    if (GATHER && s + 2 < n_tiles) issue(s + 2, tin);
     if (s >= 1) {
       const uint8_t* P = wts[(s - 1) & 1] + c32 * kPRow + 16 * h;
       const bf16x8_t pb0 = as_bf16x8(*(const uint4*)P);
@@ -817,20 +816,14 @@ void mqa_sd_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml) {
         o[k >> 1] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, vv), (k & 1) ? pb1 : pb0, o[k >> 1]);
       }
     }
-    // the other group's step: tile s+1, gathered by this group at step s-1, has landed
-    if (!GATHER) wait_vmcnt<0>();
     lds_barrier();
   };
-  auto run = [&](auto GRPC) {
-    for (int s = 0; s <= n_tiles; s += 4) {
-      step(std::integral_constant<int, 0>{}, GRPC, s);
-      if (s + 1 <= n_tiles) step(std::integral_constant<int, 1>{}, GRPC, s + 1);
-      if (s + 2 <= n_tiles) step(std::integral_constant<int, 2>{}, GRPC, s + 2);
-      if (s + 3 <= n_tiles) step(std::integral_constant<int, 3>{}, GRPC, s + 3);
-    }
-  };
-  if (grp == 0) run(std::integral_constant<int, 0>{});
-  else run(std::integral_constant<int, 1>{});
+  for (int s = 0; s <= n_tiles; s += 4) {
+    step(std::integral_constant<int, 0>{}, s);
+    if (s + 1 <= n_tiles) step(std::integral_constant<int, 1>{}, s + 1);
+    if (s + 2 <= n_tiles) step(std::integral_constant<int, 2>{}, s + 2);
+    if (s + 3 <= n_tiles) step(std::integral_constant<int, 3>{}, s + 3);
+  }
   lds_barrier();   // the head sums are in LDS
   // o[db][r] holds dim 128 pw + 32 db + 8 (r/4) + 4 h + r%4 of head c32.  The
   // 32 x 128 block goes through LDS (every tile buffer is free after the last step)
@@ -1358,10 +1351,10 @@ static MqaLaunch plan_mqa(const MqaArgs& A) {
       const int n_hg = A.heads / wg_heads;
       // (the 8-wave kernel gathers only ~1.5 tiles ahead: on rows scattered over HBM,
       // as in sparse decode, it waits on memory)
-      // (the split-role kernel is bound by how fast its two gathering waves issue
-      // rows: about 1.5 us a tile once every CU gathers; its start-up waits on the
-      // index slots, then on the first two tiles)
-      const double t_tile = hg ? 1.5 : (pre ? 2.4 : (A.dense ? 3.0 : 5.0));
+      // (the split-role kernel is bound by the gather rate when every CU gathers:
+      // about 0.9 us a tile; its start-up waits on the index slots, then on the
+      // first two tiles, and its partial leaves at the end)
+      const double t_tile = hg ? 0.9 : (pre ? 2.4 : (A.dense ? 3.0 : 5.0));
       // the pre-pass reads every cached row once (~5 TB/s)
       const double t_norms = pre ? 3.0 + (double)A.batch * ((double)A.kv_cap + A.raw_cap) * (kD * 2) / 5.0e6 : 0.0;
       for (int sp = 1; sp <= kMaxSplit && sp <= tiles_max; ++sp) {
@@ -1373,7 +1366,7 @@ static MqaLaunch plan_mqa(const MqaArgs& A) {
         const double part_mb = s_eff > 1 ? wgs * wg_heads * kD * 4.0 / 1.0e6 : 0.0;
         // start-up: first gathers, and the workgroup's partial (256 KB for 128 heads)
         // leaving through one CU
-        const double t_start = hg ? 15.0 : (s_eff > 1 ? 13.0 : 4.0);
+        const double t_start = hg ? 13.0 : (s_eff > 1 ? 13.0 : 4.0);
         const double cost = t_norms + rounds * (t_start + tps * t_tile) + (s_eff > 1 ? 4.0 + part_mb / 2.0 : 0.0);
         if (cost < best - 1e-9) {
           best = cost;
