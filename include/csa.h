@@ -249,6 +249,16 @@ typedef struct {
   float scale;
   float eps;
   int32_t dtype;      /* CSA_F32 or CSA_BF16 */
+  int32_t split_items; /* 0: the library picks the kernel and where a query's items
+                          are split for speed, which may change with the batch;
+                          > 0 (a multiple of 32, <= 2048, at most 128 splits of the
+                          largest set): batch-invariant decoding, the set is split at
+                          multiples of split_items and the splits are merged in a
+                          fixed order by a fixed kernel, so each query's output is the
+                          same, bit for bit, whatever batch it is computed in
+                          ("DeepSeek-V4-Pro" techniques map, inference kernels:
+                          batch-invariant attention decoding, separate split-K outputs
+                          with a deterministic reduction) */
 } csa_mqa_desc;
 
 size_t csa_mqa_workspace_size(const csa_mqa_desc* desc, int32_t dense);

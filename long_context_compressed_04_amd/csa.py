@@ -39,7 +39,8 @@ class IndexDesc(ctypes.Structure):
 class MqaDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "n_q", "heads", "head_dim", "topk", "m", "n_max", "window", "kv_cap", "raw_cap")] + [
-        ("scale", ctypes.c_float), ("eps", ctypes.c_float), ("dtype", ctypes.c_int32)]
+        ("scale", ctypes.c_float), ("eps", ctypes.c_float), ("dtype", ctypes.c_int32),
+        ("split_items", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -233,16 +234,17 @@ def index_topk_rescored(q_idx, q_scale, q_bf16, w, k_idx, k_scale, k_bf16, n_ent
     return out_idx, out_score
 
 
-def _mqa_desc(q, kv, kv_raw, *, topk=0, m=1, n_max=0, window=128, scale=0.0, eps=1e-6):
+def _mqa_desc(q, kv, kv_raw, *, topk=0, m=1, n_max=0, window=128, scale=0.0, eps=1e-6, split_items=0):
     B, n_q, H, D = q.shape
     return MqaDesc(B, n_q, H, D, topk, m, n_max, window, kv.shape[1], kv_raw.shape[1], float(scale), float(eps),
-                   _dtype_code(q))
+                   _dtype_code(q), split_items)
 
 
 def sparse_mqa(q, kv, idx, kv_raw, raw_base, q_pos, *, window, scale=0.0, eps=1e-6, rms_weight=None,
-               workspace=None, out=None, lse=None):
-    """CSA attention over idx (-1 skipped) plus the sliding window.  Returns (out, lse)."""
-    d = _mqa_desc(q, kv, kv_raw, topk=idx.shape[-1], window=window, scale=scale, eps=eps)
+               split_items=0, workspace=None, out=None, lse=None):
+    """CSA attention over idx (-1 skipped) plus the sliding window.  Returns (out, lse).
+    split_items > 0 selects batch-invariant splitting (see csa_mqa_desc)."""
+    d = _mqa_desc(q, kv, kv_raw, topk=idx.shape[-1], window=window, scale=scale, eps=eps, split_items=split_items)
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if lse is None else lse
     ws, nb = _workspace(lib().csa_mqa_workspace_size(ctypes.byref(d), 0), q.device, workspace)
@@ -252,10 +254,11 @@ def sparse_mqa(q, kv, idx, kv_raw, raw_base, q_pos, *, window, scale=0.0, eps=1e
 
 
 def hca_dense_mqa(q, kv, n_entries, kv_raw, raw_base, q_pos, *, m, window, n_max=None, scale=0.0, eps=1e-6,
-                  rms_weight=None, workspace=None, out=None, lse=None):
-    """HCA attention over every visible compressed entry plus the window.  Returns (out, lse)."""
+                  rms_weight=None, split_items=0, workspace=None, out=None, lse=None):
+    """HCA attention over every visible compressed entry plus the window.  Returns (out, lse).
+    split_items > 0 selects batch-invariant splitting (see csa_mqa_desc)."""
     d = _mqa_desc(q, kv, kv_raw, m=m, n_max=kv.shape[1] if n_max is None else n_max, window=window, scale=scale,
-                  eps=eps)
+                  eps=eps, split_items=split_items)
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if lse is None else lse
     ws, nb = _workspace(lib().csa_mqa_workspace_size(ctypes.byref(d), 1), q.device, workspace)
@@ -269,12 +272,12 @@ class Decoder:
     so that repeated calls only re-enqueue the kernels."""
 
     def __init__(self, q, kv, kv_raw, raw_base, q_pos, q_idx, w, k_idx, n_entries, *, m, topk, window,
-                 n_max=None, q_scale=None, k_scale=None, scale=0.0, eps=1e-6, rms_weight=None, out=None,
-                 out_idx=None, out_score=None, lse=None):
+                 n_max=None, q_scale=None, k_scale=None, scale=0.0, eps=1e-6, rms_weight=None, split_items=0,
+                 out=None, out_idx=None, out_score=None, lse=None):
         self.tensors = [q, kv, kv_raw, raw_base, q_pos, q_idx, w, k_idx, n_entries, q_scale, k_scale, rms_weight]
         a = DecodeArgs()
         a.index = _index_desc(q_idx, k_idx, m, topk, n_max, *_index_dtype(q_idx, k_idx))
-        a.attn = _mqa_desc(q, kv, kv_raw, topk=topk, window=window, scale=scale, eps=eps)
+        a.attn = _mqa_desc(q, kv, kv_raw, topk=topk, window=window, scale=scale, eps=eps, split_items=split_items)
         dev = q.device
         self.out = torch.empty_like(q) if out is None else out
         self.out_idx = torch.empty((q.shape[0], q.shape[1], topk), dtype=torch.int32, device=dev) \

@@ -124,6 +124,13 @@ csa_status check_mqa(const char* fn, const csa_mqa_desc* d, int dense, const voi
     return fail(CSA_ERR_SHAPE, "%s: need 0 <= topk <= 65536", fn);
   }
   if (!(d->eps >= 0.f) || !std::isfinite(d->scale)) return fail(CSA_ERR_SHAPE, "%s: eps must be >= 0, scale finite", fn);
+  if (d->split_items != 0) {
+    const long total = (long)(dense ? d->n_max : d->topk) + d->window;
+    if (d->split_items < 0 || d->split_items % 32 != 0 || d->split_items > 2048 ||
+        (total + d->split_items - 1) / d->split_items > 128)
+      return fail(CSA_ERR_SHAPE, "%s: split_items must be 0, or a multiple of 32 <= 2048 giving at most 128 splits",
+                  fn);
+  }
   if (d->dtype == CSA_F32) {
     if (d->head_dim < 1 || d->head_dim > 512) return fail(CSA_ERR_SHAPE, "%s: fp32 path needs 1 <= head_dim <= 512", fn);
   } else if (d->dtype == CSA_BF16) {
@@ -144,6 +151,7 @@ csa::MqaArgs mqa_args(const csa_mqa_desc* d, int dense) {
   A.dense = dense; A.bf16 = d->dtype == CSA_BF16;
   A.scale = d->scale > 0.f ? d->scale : 1.f / std::sqrt((float)d->head_dim);
   A.eps = d->eps;
+  A.split_items = d->split_items;
   return A;
 }
 

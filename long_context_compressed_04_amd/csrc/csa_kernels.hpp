@@ -46,6 +46,7 @@ struct MqaArgs {
   const void* q; const void* kv; const int32_t* idx; const int32_t* n_entries;
   const void* kv_raw; const int32_t* raw_base; const int32_t* q_pos; const float* gamma;
   void* out; float* lse;
+  int split_items = 0;   // > 0: batch-invariant split boundaries (multiples of it)
 };
 // Workspace bytes the MQA path needs for these sizes (split partials).
 size_t mqa_workspace_bytes(const MqaArgs& A);

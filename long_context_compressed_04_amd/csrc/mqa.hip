@@ -1333,6 +1333,27 @@ static MqaLaunch plan_mqa(const MqaArgs& A) {
   // The 32- and 128-head MFMA paths need the unit RMSNorm weight and a scale that
   // keeps every exp2(logit) normal without a running maximum.
   const bool fixed = A.gamma == nullptr && A.scale * kLog2e * kD * 1.01f <= 100.f;
+  if (A.split_items > 0) {
+    // Batch-invariant: the kernel and the split boundaries (multiples of split_items
+    // from a query's first item) follow from the configuration alone, never from the
+    // batch, and the merge runs in split order; a query's arithmetic is then the
+    // same in any batch.
+    if (fixed && A.heads % 32 == 0) {
+      L.kind = 4;
+      L.n_hg = A.heads / 32;
+      L.nw = kSdWaves;
+    } else {
+      L.kind = 0;
+      L.nw = (A.heads % 64 == 0) ? 4 : ((A.heads % 32 == 0) ? 2 : 1);
+      L.n_hg = A.heads / (L.nw * 16);
+    }
+    L.ips = A.split_items;
+    L.nsplit = (total_max + L.ips - 1) / L.ips;
+    if (L.nsplit < 1) L.nsplit = 1;
+    L.units = (int)(rows * L.nsplit);
+    L.slots = (!A.dense && L.ips <= 8192) ? 1 : 0;
+    return L;
+  }
   L.kind = 0;
   if (fixed) {
     // Kernel and split count from a cost model fitted to MI355X timings (microseconds):

@@ -99,6 +99,9 @@ def test_mqa_validation():
     assert sp(D(eps=-1.0)) == 2
     assert de(D(n_max=2000)) == 2                           # n_max > kv_cap
     assert de(D(m=0, n_max=10)) == 2
+    assert sp(D(split_items=48)) == 2                       # not a multiple of 32
+    assert sp(D(split_items=4096)) == 2                     # more than 2048
+    assert sp(D(topk=8192, split_items=32)) == 2            # more than 128 splits
 
 
 def test_decode_validation():

@@ -294,6 +294,56 @@ def test_sparse_mqa(dtype, B, n_q, H, d, N, k, window):
                     np.testing.assert_allclose(lse[b, i], wl, atol=2e-2)
 
 
+@pytest.mark.parametrize("dense,H,n_q,with_gamma,split_items", [
+    (False, 128, 1, False, 256),    # split-role kernel, three splits
+    (False, 128, 1, True, 256),     # online-softmax kernel (RMSNorm weight given)
+    (True, 128, 1, False, 256),     # dense, seven splits
+    (False, 64, 3, False, 640),     # several queries, one split
+])
+def test_batch_invariant_mqa(dense, H, n_q, with_gamma, split_items):
+    """split_items > 0: each sequence's output, computed in a batch of four, equals bit
+    for bit its output computed alone; and it matches the oracle."""
+    B, d, N, k, window, m = 4, 512, 1500, 512, 128, 4
+    q, kv, kv_raw, rng = _mqa_case("bf16", B, n_q, H, d, N, k, window, seed=17 + H + n_q)
+    gamma = (0.5 + rng.random(d)).astype(np.float32) if with_gamma else None
+    if dense:
+        n_entries = np.array([N - 3 * b for b in range(B)], dtype=np.int32)
+        q_pos = np.array([[m * N - 1 - 40 * b - i for i in range(n_q)] for b in range(B)], dtype=np.int32)
+        raw_base = np.array([max(0, q_pos[b].min() - window + 1) for b in range(B)], dtype=np.int32)
+    else:
+        idx = np.stack([np.stack([np.sort(rng.choice(N, size=k, replace=False)) for _ in range(n_q)])
+                        for _ in range(B)]).astype(np.int32)
+        idx[:, :, -5:] = -1
+        raw_base = np.array([1000 + 10 * b for b in range(B)], dtype=np.int32)
+        q_pos = np.array([[raw_base[b] + window + 2 + i for i in range(n_q)] for b in range(B)], dtype=np.int32)
+
+    def run(sl):
+        g = None if gamma is None else dev(gamma)
+        if dense:
+            return csa.hca_dense_mqa(dev(q[sl]), dev(kv[sl]), _i32(n_entries[sl]), dev(kv_raw[sl]), _i32(raw_base[sl]),
+                                     _i32(q_pos[sl]), m=m, window=window, n_max=N, rms_weight=g,
+                                     split_items=split_items)
+        return csa.sparse_mqa(dev(q[sl]), dev(kv[sl]), _i32(idx[sl]), dev(kv_raw[sl]), _i32(raw_base[sl]),
+                              _i32(q_pos[sl]), window=window, rms_weight=g, split_items=split_items)
+
+    out, lse = run(slice(0, B))
+    for b in range(B):
+        o1, l1 = run(slice(b, b + 1))
+        assert torch.equal(out[b], o1[0]), "sequence %d: output depends on the batch" % b
+        assert torch.equal(lse[b], l1[0]), "sequence %d: lse depends on the batch" % b
+    out, lse = host(out), host(lse)
+    for b in (0, B - 1):
+        for i in range(n_q):
+            if dense:
+                want, wl = oracle.dense_mqa(W.value(q[b, i]), W.value(kv[b]), n_entries[b], m, W.value(kv_raw[b]),
+                                            raw_base[b], q_pos[b, i], window, 1 / np.sqrt(d), 1e-6, gamma)
+            else:
+                want, wl = oracle.sparse_mqa(W.value(q[b, i]), W.value(kv[b]), idx[b, i], W.value(kv_raw[b]),
+                                             raw_base[b], q_pos[b, i], window, 1 / np.sqrt(d), 1e-6, gamma)
+            assert_bf16_close(out[b, i], want, "batch-invariant out")
+            np.testing.assert_allclose(lse[b, i], wl, atol=2e-2)
+
+
 @pytest.mark.parametrize("dtype,B,n_q,H,d,N,m,window,t_off", [
     ("f32", 1, 1, 8, 64, 300, 128, 128, 0),
     ("f32", 2, 2, 4, 32, 50, 4, 9, -30),           # causal: V < N
