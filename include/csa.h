@@ -223,6 +223,11 @@ csa_status csa_index_topk_rescored(const csa_index_desc* desc, int32_t cand, con
  * over the whole set with logits scale * q_hat . k_hat (scale <= 0 selects
  * 1/sqrt(head_dim)); out = sum softmax * k_hat.  An empty set gives out = 0 and
  * lse = -inf.
+ * Attention sink ("DeepSeek-V4-Pro" techniques map, "Learnable attention sink": one
+ * learnable logit per head joins the softmax denominator): sink [heads] fp32, or
+ * NULL for none.  With a sink s_h the softmax runs over the set plus one extra logit
+ * s_h whose value vector is zero, so out = sum exp(l_j) k_hat_j / (sum exp(l_j) +
+ * exp(s_h)) and lse includes exp(s_h).  |s_h| <= 80.
  *
  *   q      [batch, n_q, heads, head_dim] dtype
  *   kv     [batch, kv_cap, head_dim]     dtype (compressed entries)
@@ -265,13 +270,13 @@ size_t csa_mqa_workspace_size(const csa_mqa_desc* desc, int32_t dense);
 
 csa_status csa_sparse_mqa(const csa_mqa_desc* desc, const void* q, const void* kv,
                           const int32_t* idx, const void* kv_raw, const int32_t* raw_base,
-                          const int32_t* q_pos, const float* rms_weight, void* out, float* lse,
-                          void* ws, size_t ws_bytes, void* stream);
+                          const int32_t* q_pos, const float* rms_weight, const float* sink,
+                          void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 csa_status hca_dense_mqa(const csa_mqa_desc* desc, const void* q, const void* kv,
                          const int32_t* n_entries, const void* kv_raw, const int32_t* raw_base,
-                         const int32_t* q_pos, const float* rms_weight, void* out, float* lse,
-                         void* ws, size_t ws_bytes, void* stream);
+                         const int32_t* q_pos, const float* rms_weight, const float* sink,
+                         void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------
  * csa_decode -- one fused CSA step for n_q queries per sequence, stream-ordered:
@@ -302,6 +307,7 @@ typedef struct {
   const int32_t* raw_base;
   const int32_t* q_pos;
   const float* rms_weight;
+  const float* sink;                /* nullable: per-head sink logits (as csa_sparse_mqa) */
   const void* q_idx;
   const uint8_t* q_idx_scale;
   const float* w;

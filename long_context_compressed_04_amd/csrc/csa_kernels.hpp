@@ -47,6 +47,7 @@ struct MqaArgs {
   const void* kv_raw; const int32_t* raw_base; const int32_t* q_pos; const float* gamma;
   void* out; float* lse;
   int split_items = 0;   // > 0: batch-invariant split boundaries (multiples of it)
+  const float* sink = nullptr;   // [heads] sink logits (natural log), or none
 };
 // Workspace bytes the MQA path needs for these sizes (split partials).
 size_t mqa_workspace_bytes(const MqaArgs& A);

@@ -83,6 +83,24 @@ __device__ __forceinline__ void query_items(const MqaArgs& A, int b, long row, i
   total = src.n_first + n_win;
 }
 
+// The end of a softmax: a head's weights were formed as 2^(l2_j - m2) (log2 units;
+// m2 = 0 on the paths without a running maximum) and sum to l.  Returns the factor
+// that turns the weighted sum of rows into the output, and the natural-log
+// denominator.  A sink logit s joins the denominator only: with s2 = s log2(e) and
+// M = max(m2, s2) the denominator is l 2^(m2 - M) + 2^(s2 - M) (in units of 2^M).
+struct SoftmaxEnd {
+  float mul, lse;
+};
+__device__ __forceinline__ SoftmaxEnd softmax_end(float m2, float l, const float* sink, int head) {
+  const bool none = !(l > 0.f);
+  if (!sink) return {none ? 0.f : 1.f / l, none ? -INFINITY : m2 * kLn2 + logf(l)};
+  const float s2 = sink[head] * kLog2e;
+  const float M = none ? s2 : fmaxf(m2, s2);
+  const float scale = none ? 0.f : exp2f(m2 - M);
+  const float den = l * scale + exp2f(s2 - M);
+  return {scale / den, M * kLn2 + logf(den)};
+}
+
 // ---------------------------------------------------------------- fp32 (VALU)
 // One workgroup (4 waves) per (sequence, query, head).  Each wave walks every 4th
 // item with the head dimension spread over its lanes; online softmax per wave, then
@@ -158,13 +176,14 @@ __global__ __launch_bounds__(kF32Waves * 64) void mqa_f32_kernel(MqaArgs A) {
     fw[w] = (sm[w] == -INFINITY) ? 0.f : expf(sm[w] - M);
     L += sl[w] * fw[w];
   }
+  const SoftmaxEnd fin = softmax_end(M * kLog2e, L, A.sink, h);   // (M is in natural-log units)
   float* orow = (float*)A.out + (row * A.heads + h) * D;
   for (int d = threadIdx.x; d < D; d += blockDim.x) {
     float o = 0.f;
     for (int w = 0; w < kF32Waves; ++w) o += so[w][d] * fw[w];
-    orow[d] = (L > 0.f) ? o / L * (A.gamma ? A.gamma[d] : 1.f) : 0.f;
+    orow[d] = o * fin.mul * (A.gamma ? A.gamma[d] : 1.f);
   }
-  if (A.lse && threadIdx.x == 0) A.lse[row * A.heads + h] = (L > 0.f) ? M + logf(L) : -INFINITY;
+  if (A.lse && threadIdx.x == 0) A.lse[row * A.heads + h] = fin.lse;
 }
 
 // ---------------------------------------------------------------- bf16 (MFMA)
@@ -480,7 +499,8 @@ __global__ __launch_bounds__(NW * 64) void mqa_bf16_kernel(MqaArgs A, MqaLaunch 
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
   if (L.nsplit == 1) {
-    const float inv_l = l_run > 0.f ? 1.f / l_run : 0.f;
+    const SoftmaxEnd fin = softmax_end(m_run, l_run, A.sink, head);
+    const float inv_l = fin.mul;
     uint16_t* orow = (uint16_t*)A.out + (row * A.heads + head) * kD;
 #pragma unroll
     for (int db = 0; db < 32; ++db) {
@@ -490,7 +510,7 @@ __global__ __launch_bounds__(NW * 64) void mqa_bf16_kernel(MqaArgs A, MqaLaunch 
       for (int r = 0; r < 4; ++r) v[r] = o[db][r] * inv_l * gam[d0 + r];
       *(uint2*)(orow + d0) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
     }
-    if (A.lse && g == 0) A.lse[row * A.heads + head] = l_run > 0.f ? m_run * kLn2 + logf(l_run) : -INFINITY;
+    if (A.lse && g == 0) A.lse[row * A.heads + head] = fin.lse;
   } else {
     float* po = part_o + (((long)row * L.nsplit + split) * A.heads + head) * kD;
 #pragma unroll
@@ -761,7 +781,7 @@ void mqa_sd_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml) {
       const float l = lsum[0][lane] + lsum[1][lane];
       const int head = hg * 32 + lane;
       if (L.nsplit == 1) {
-        if (A.lse) A.lse[row * A.heads + head] = l > 0.f ? logf(l) : -INFINITY;
+        if (A.lse) A.lse[row * A.heads + head] = softmax_end(0.f, l, A.sink, head).lse;
       } else {
         float* pm = part_ml + (((long)row * L.nsplit + split) * A.heads + head) * 2;
         pm[0] = l > 0.f ? 0.f : -INFINITY;
@@ -841,8 +861,7 @@ void mqa_sd_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml) {
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const int hh = 2 * k + hl;
-      const float l = lsum[0][hh] + lsum[1][hh];
-      const float il = l > 0.f ? 1.f / l : 0.f;
+      const float il = softmax_end(0.f, lsum[0][hh] + lsum[1][hh], A.sink, hg * 32 + hh).mul;
       const f32x4_t v = *(const f32x4_t*)(stage + hh * kStageRow + 4 * d4);
       uint16_t* orow = (uint16_t*)A.out + (row * A.heads + hg * 32 + hh) * kD + 128 * pw + 4 * d4;
       *(uint2*)orow = make_uint2(pack_bf16x2(v[0] * il, v[1] * il), pack_bf16x2(v[2] * il, v[3] * il));
@@ -1210,7 +1229,7 @@ void mqa_w8_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml, const 
   for (int j = 0; j < 2; ++j) {
     const int hbj = 2 * hp + j;
     l_tot[j] = red[hbj][c32] + red[hbj + 4][c32];
-    inv_l[j] = l_tot[j] > 0.f ? 1.f / l_tot[j] : 0.f;
+    inv_l[j] = softmax_end(0.f, l_tot[j], A.sink, hg * 128 + 64 * hp + 32 * j + c32).mul;
   }
   // ---- O^T -> rows of 64 dims through a wave-private LDS region, four chunks
   // (head block j of the pair, dim half of the quarter)
@@ -1254,7 +1273,7 @@ void mqa_w8_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml, const 
     for (int j = 0; j < 2; ++j) {
       const int head = hg * 128 + 64 * hp + 32 * j + c32;
       if (L.nsplit == 1) {
-        if (A.lse) A.lse[row * A.heads + head] = l_tot[j] > 0.f ? logf(l_tot[j]) : -INFINITY;
+        if (A.lse) A.lse[row * A.heads + head] = softmax_end(0.f, l_tot[j], A.sink, head).lse;
       } else {
         float* pm = part_ml + (((long)row * L.nsplit + split) * A.heads + head) * 2;
         pm[0] = l_tot[j] > 0.f ? 0.f : -INFINITY;
@@ -1309,7 +1328,8 @@ __global__ __launch_bounds__(128) void mqa_combine_kernel(MqaArgs A, MqaLaunch L
   }
   __syncthreads();
   const float Lsum = s_L;
-  const float inv_l = Lsum > 0.f ? 1.f / Lsum : 0.f;
+  const SoftmaxEnd fin = softmax_end(s_M, Lsum, A.sink, head);
+  const float inv_l = fin.mul;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < kPre; ++s)
@@ -1321,7 +1341,7 @@ __global__ __launch_bounds__(128) void mqa_combine_kernel(MqaArgs A, MqaLaunch L
   for (int r = 0; r < 4; ++r) v[r] = acc[r] * inv_l * (A.gamma ? A.gamma[d0 + r] : 1.f);
   uint16_t* orow = (uint16_t*)A.out + (row * A.heads + head) * kD;
   *(uint2*)(orow + d0) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-  if (A.lse && threadIdx.x == 0) A.lse[row * A.heads + head] = Lsum > 0.f ? s_M * kLn2 + logf(Lsum) : -INFINITY;
+  if (A.lse && threadIdx.x == 0) A.lse[row * A.heads + head] = fin.lse;
 }
 
 static MqaLaunch plan_mqa(const MqaArgs& A) {

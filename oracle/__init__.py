@@ -54,9 +54,9 @@ def _get():
         lib.oracle_index_scores.restype = None
         lib.oracle_topk.argtypes = [_D, L, I, _I32]
         lib.oracle_topk.restype = None
-        lib.oracle_sparse_mqa.argtypes = [_D, _D, L, _I32, I, _D, L, L, L, I, I, I, D, D, _D, _D, _D]
+        lib.oracle_sparse_mqa.argtypes = [_D, _D, L, _I32, I, _D, L, L, L, I, I, I, D, D, _D, _D, _D, _D]
         lib.oracle_sparse_mqa.restype = I
-        lib.oracle_dense_mqa.argtypes = [_D, _D, L, I, _D, L, L, L, I, I, I, D, D, _D, _D, _D]
+        lib.oracle_dense_mqa.argtypes = [_D, _D, L, I, _D, L, L, L, I, I, I, D, D, _D, _D, _D, _D]
         lib.oracle_dense_mqa.restype = I
         lib.oracle_mxfp4_quantize.argtypes = [_D, L, _U8, _U8]
         lib.oracle_mxfp4_quantize.restype = None
@@ -150,8 +150,9 @@ def index_topk_rescored(q4, w, k4, q16, k16, n_visible, cand, k):
     return out, c, s16
 
 
-def sparse_mqa(q, kv, idx, kv_raw, raw_base, t, window, scale, eps, gamma=None):
-    """MQA of one query over kv[idx] (-1 skipped) plus the sliding window, one softmax.
+def sparse_mqa(q, kv, idx, kv_raw, raw_base, t, window, scale, eps, gamma=None, sink=None):
+    """MQA of one query over kv[idx] (-1 skipped) plus the sliding window, one softmax
+    (with the per-head sink logits in its denominator when sink [H] is given).
     q [H, d]; kv [N, d]; kv_raw [W, d].  Returns (out [H, d], lse [H])."""
     q, kv, kv_raw = _f64(q), _f64(kv), _f64(kv_raw)
     H, d = q.shape
@@ -159,24 +160,27 @@ def sparse_mqa(q, kv, idx, kv_raw, raw_base, t, window, scale, eps, gamma=None):
     out = np.empty((H, d), dtype=np.float64)
     lse = np.empty(H, dtype=np.float64)
     g = None if gamma is None else _f64(gamma)
+    sk = None if sink is None else _f64(sink)
     rc = _get().oracle_sparse_mqa(_p(q), _p(kv), kv.shape[0], _p(idx, _I32), idx.size, _p(kv_raw),
                                   kv_raw.shape[0], int(raw_base), int(t), int(window), H, d, float(scale),
-                                  float(eps), _p(g), _p(out), _p(lse))
+                                  float(eps), _p(g), _p(sk), _p(out), _p(lse))
     if rc != 0:
         raise ValueError("oracle_sparse_mqa: index or window row out of range")
     return out, lse
 
 
-def dense_mqa(q, kv, n_entries, m, kv_raw, raw_base, t, window, scale, eps, gamma=None):
-    """HCA: MQA over every visible compressed entry plus the window, one softmax."""
+def dense_mqa(q, kv, n_entries, m, kv_raw, raw_base, t, window, scale, eps, gamma=None, sink=None):
+    """HCA: MQA over every visible compressed entry plus the window, one softmax
+    (with the per-head sink logits in its denominator when sink [H] is given)."""
     q, kv, kv_raw = _f64(q), _f64(kv), _f64(kv_raw)
     H, d = q.shape
     out = np.empty((H, d), dtype=np.float64)
     lse = np.empty(H, dtype=np.float64)
     g = None if gamma is None else _f64(gamma)
+    sk = None if sink is None else _f64(sink)
     rc = _get().oracle_dense_mqa(_p(q), _p(kv), int(n_entries), int(m), _p(kv_raw), kv_raw.shape[0],
                                  int(raw_base), int(t), int(window), H, d, float(scale), float(eps),
-                                 _p(g), _p(out), _p(lse))
+                                 _p(g), _p(sk), _p(out), _p(lse))
     if rc != 0:
         raise ValueError("oracle_dense_mqa: window row out of range")
     return out, lse

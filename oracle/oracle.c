@@ -179,9 +179,14 @@ void oracle_topk(const double* scores, long n_visible, int k, int32_t* out) {
  * set (top-k entries and sliding-window tokens together).
  *   q [H, d] raw; rows [S, d] raw; RMSNorm applied here to both sides.
  *   out [H, d]; lse [H] (natural log of the softmax denominator incl. max).
+ * [P4] "Learnable attention sink": a per-head sink logit is concatenated to
+ * the logits before the softmax and its column dropped after, i.e. it adds
+ * exp(sink[h]) to the denominator and nothing to the numerator.  sink [H] or
+ * NULL.
  * ------------------------------------------------------------------------ */
 static void attend(const double* q, const double* const* rows, long S, int H, int d,
-                   double scale, double eps, const double* gamma, double* out, double* lse) {
+                   double scale, double eps, const double* gamma, const double* sink, double* out,
+                   double* lse) {
   double* qn = (double*)malloc(sizeof(double) * d);
   double* kn = (double*)malloc(sizeof(double) * (S > 0 ? S : 1) * d);
   double* logit = (double*)malloc(sizeof(double) * (S > 0 ? S : 1));
@@ -195,14 +200,16 @@ static void attend(const double* q, const double* const* rows, long S, int H, in
       logit[j] = scale * dot;
       if (logit[j] > mx) mx = logit[j];
     }
+    if (sink && sink[h] > mx) mx = sink[h];
     double den = 0.0;
     for (long j = 0; j < S; ++j) den += exp(logit[j] - mx);
+    if (sink) den += exp(sink[h] - mx);
     for (int i = 0; i < d; ++i) {
       double acc = 0.0;
       for (long j = 0; j < S; ++j) acc += (exp(logit[j] - mx) / den) * kn[j * d + i];
       out[(long)h * d + i] = (S > 0) ? acc : 0.0;
     }
-    if (lse) lse[h] = (S > 0) ? mx + log(den) : -INFINITY;
+    if (lse) lse[h] = (S > 0 || sink) ? mx + log(den) : -INFINITY;
   }
   free(qn); free(kn); free(logit);
 }
@@ -233,7 +240,8 @@ static long window_rows(const double* kv_raw, long n_raw, long raw_base, long t,
  * ------------------------------------------------------------------------ */
 int oracle_sparse_mqa(const double* q, const double* kv, long n_entries, const int32_t* idx, int k,
                       const double* kv_raw, long n_raw, long raw_base, long t, int window, int H, int d,
-                      double scale, double eps, const double* gamma, double* out, double* lse) {
+                      double scale, double eps, const double* gamma, const double* sink, double* out,
+                      double* lse) {
   const double** rows = (const double**)malloc(sizeof(double*) * (size_t)(k + window + 1));
   long S = 0;
   for (int i = 0; i < k; ++i) {
@@ -244,7 +252,7 @@ int oracle_sparse_mqa(const double* q, const double* kv, long n_entries, const i
   long w = window_rows(kv_raw, n_raw, raw_base, t, window, d, rows, S);
   if (w < 0) { free(rows); return ORC_EINVAL; }
   S += w;
-  attend(q, rows, S, H, d, scale, eps, gamma, out, lse);
+  attend(q, rows, S, H, d, scale, eps, gamma, sink, out, lse);
   free(rows);
   return ORC_OK;
 }
@@ -257,7 +265,7 @@ int oracle_sparse_mqa(const double* q, const double* kv, long n_entries, const i
  * ------------------------------------------------------------------------ */
 int oracle_dense_mqa(const double* q, const double* kv, long n_entries, int m, const double* kv_raw,
                      long n_raw, long raw_base, long t, int window, int H, int d, double scale,
-                     double eps, const double* gamma, double* out, double* lse) {
+                     double eps, const double* gamma, const double* sink, double* out, double* lse) {
   long V = oracle_visible(t, n_entries, m);
   const double** rows = (const double**)malloc(sizeof(double*) * (size_t)(V + window + 1));
   long S = 0;
@@ -265,7 +273,7 @@ int oracle_dense_mqa(const double* q, const double* kv, long n_entries, int m, c
   long w = window_rows(kv_raw, n_raw, raw_base, t, window, d, rows, S);
   if (w < 0) { free(rows); return ORC_EINVAL; }
   S += w;
-  attend(q, rows, S, H, d, scale, eps, gamma, out, lse);
+  attend(q, rows, S, H, d, scale, eps, gamma, sink, out, lse);
   free(rows);
   return ORC_OK;
 }

@@ -84,9 +84,9 @@ def test_mqa_validation():
     ok = dict(batch=1, n_q=1, heads=128, head_dim=512, topk=64, m=4, n_max=0, window=128, kv_cap=1024,
               raw_cap=128, scale=0.0, eps=1e-6, dtype=1)
     D = lambda **kw: csa.MqaDesc(**{**ok, **kw})
-    sp = lambda d, q=FAKE, out=FAKE: L.csa_sparse_mqa(ctypes.byref(d), q, FAKE, FAKE, FAKE, FAKE, FAKE, None, out,
-                                                      None, FAKE, 1 << 30, None)
-    de = lambda d: L.hca_dense_mqa(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE,
+    sp = lambda d, q=FAKE, out=FAKE: L.csa_sparse_mqa(ctypes.byref(d), q, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+                                                      out, None, FAKE, 1 << 30, None)
+    de = lambda d: L.hca_dense_mqa(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None, FAKE,
                                    1 << 30, None)
     assert sp(D(), q=None) == 1
     assert sp(D(head_dim=256)) == 6

@@ -294,6 +294,52 @@ def test_sparse_mqa(dtype, B, n_q, H, d, N, k, window):
                     np.testing.assert_allclose(lse[b, i], wl, atol=2e-2)
 
 
+@pytest.mark.parametrize("dtype,dense,n_q,H,d,N,k,with_gamma,split_items", [
+    ("f32", False, 1, 8, 64, 300, 64, False, 0),       # fp32 kernel
+    ("bf16", False, 1, 128, 512, 1500, 512, False, 0),  # split-role kernel, merged splits
+    ("bf16", False, 1, 128, 512, 1500, 512, False, 1024),   # split-role kernel, one split
+    ("bf16", False, 1, 64, 512, 900, 256, True, 0),     # online-softmax kernel
+    ("bf16", True, 40, 128, 512, 600, 0, False, 0),     # many queries: 128-head workgroups
+])
+def test_mqa_sink(dtype, dense, n_q, H, d, N, k, with_gamma, split_items):
+    """Per-head sink logits in the softmax denominator, against the oracle."""
+    B, window, m = 2 if not dense else 1, 128, 4
+    q, kv, kv_raw, rng = _mqa_case(dtype, B, n_q, H, d, N, k, window, seed=31 + H + N)
+    sink = rng.normal(0.0, 2.0, H).astype(np.float32)
+    sink[0], sink[-1] = -60.0, 8.0                      # no effect / dominant
+    gamma = (0.5 + rng.random(d)).astype(np.float32) if with_gamma else None
+    g = None if gamma is None else dev(gamma)
+    if dense:
+        n_entries = np.array([N - 3 * b for b in range(B)], dtype=np.int32)
+        q_pos = np.array([[m * N - 1 - 20 - i for i in range(n_q)] for b in range(B)], dtype=np.int32)
+        raw_base = np.array([max(0, q_pos[b].min() - window + 1) for b in range(B)], dtype=np.int32)
+        out, lse = csa.hca_dense_mqa(dev(q), dev(kv), _i32(n_entries), dev(kv_raw), _i32(raw_base), _i32(q_pos),
+                                     m=m, window=window, rms_weight=g, sink=dev(sink), split_items=split_items)
+    else:
+        idx = np.stack([np.stack([np.sort(rng.choice(N, size=k, replace=False)) for _ in range(n_q)])
+                        for _ in range(B)]).astype(np.int32)
+        idx[:, :, -3:] = -1
+        raw_base = np.array([1000 + 10 * b for b in range(B)], dtype=np.int32)
+        q_pos = np.array([[raw_base[b] + window + 2 + i for i in range(n_q)] for b in range(B)], dtype=np.int32)
+        out, lse = csa.sparse_mqa(dev(q), dev(kv), _i32(idx), dev(kv_raw), _i32(raw_base), _i32(q_pos),
+                                  window=window, rms_weight=g, sink=dev(sink), split_items=split_items)
+    out, lse = host(out), host(lse)
+    for b in range(B):
+        for i in range(0, n_q, max(1, n_q // 4)):
+            if dense:
+                want, wl = oracle.dense_mqa(W.value(q[b, i]), W.value(kv[b]), n_entries[b], m, W.value(kv_raw[b]),
+                                            raw_base[b], q_pos[b, i], window, 1 / np.sqrt(d), 1e-6, gamma, sink)
+            else:
+                want, wl = oracle.sparse_mqa(W.value(q[b, i]), W.value(kv[b]), idx[b, i], W.value(kv_raw[b]),
+                                             raw_base[b], q_pos[b, i], window, 1 / np.sqrt(d), 1e-6, gamma, sink)
+            if dtype == "f32":
+                assert_f32_close(out[b, i], want, "sink out")
+                assert_f32_close(lse[b, i], wl, "sink lse")
+            else:
+                assert_bf16_close(out[b, i], want, "sink out")
+                np.testing.assert_allclose(lse[b, i], wl, atol=2e-2)
+
+
 @pytest.mark.parametrize("dense,H,n_q,with_gamma,split_items", [
     (False, 128, 1, False, 256),    # split-role kernel, three splits
     (False, 128, 1, True, 256),     # online-softmax kernel (RMSNorm weight given)

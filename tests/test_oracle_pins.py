@@ -279,6 +279,34 @@ def test_window_only_before_first_block_and_short_window():
     np.testing.assert_allclose(out, want, atol=1e-12)
 
 
+def test_sink_joins_the_denominator_only():
+    """A sink logit s_h adds exp(s_h) to head h's softmax denominator and nothing to
+    its numerator: lse_sink = logaddexp(lse, s); out_sink = out * exp(lse - lse_sink);
+    s = -inf changes nothing (techniques map, "Learnable attention sink")."""
+    rng = np.random.default_rng(21)
+    d, H = 16, 3
+    kv = rng.standard_normal((40, d))
+    kv_raw = rng.standard_normal((8, d))
+    q = rng.standard_normal((H, d))
+    idx = np.array([3, 17, -1, 25, 9])
+    args = (q, kv, idx, kv_raw, 100, 105, 4, 0.3, 1e-6)
+    out, lse = oracle.sparse_mqa(*args)
+    sink = np.array([0.5, -2.0, 4.0])
+    o_s, l_s = oracle.sparse_mqa(*args, sink=sink)
+    np.testing.assert_allclose(l_s, np.logaddexp(lse, sink), rtol=1e-13)
+    np.testing.assert_allclose(o_s, out * np.exp(lse - l_s)[:, None], rtol=1e-12, atol=1e-14)
+    o_n, l_n = oracle.sparse_mqa(*args, sink=np.full(H, -np.inf))
+    np.testing.assert_allclose(o_n, out, rtol=1e-14)
+    np.testing.assert_allclose(l_n, lse, rtol=1e-14)
+    # dense, and an empty set: out = 0, lse = the sink
+    o_d, l_d = oracle.dense_mqa(q, kv, 40, 4, kv_raw, 100, 105, 4, 0.3, 1e-6, sink=sink)
+    o_d0, l_d0 = oracle.dense_mqa(q, kv, 40, 4, kv_raw, 100, 105, 4, 0.3, 1e-6)
+    np.testing.assert_allclose(l_d, np.logaddexp(l_d0, sink), rtol=1e-13)
+    o_e, l_e = oracle.sparse_mqa(q, kv, np.array([-1, -1]), kv_raw, 100, 105, 0, 0.3, 1e-6, sink=sink)
+    assert np.all(o_e == 0.0)
+    np.testing.assert_allclose(l_e, sink, rtol=1e-15)
+
+
 def test_window_row_outside_raw_buffer_is_an_error():
     with pytest.raises(ValueError):
         oracle.sparse_mqa(np.ones((1, 4)), np.ones((2, 4)), [0], np.ones((3, 4)), 10, 20, 4, 1.0, 1e-6)
