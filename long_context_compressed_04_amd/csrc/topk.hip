@@ -163,14 +163,16 @@ __device__ __forceinline__ void pick_digit(SelShared& sh, uint32_t prefix, int s
 }
 
 // 11-bit radix passes narrowing (prefix, mask, need) until the remaining bucket is
-// taken whole or the bits run out (hi = number of undecided low bits).
+// taken whole, the bits run out (hi = number of undecided low bits) or max_passes
+// passes are done.
 // `hist_keys(mask, prefix, shift, dmask)` adds every key matching the prefix to the
 // histogram under its digit.  `bucket(prefix, mask, need, cnt)` may resolve a small
 // bucket itself and return true.
 template <class HistKeys, class Bucket>
 __device__ __forceinline__ void radix_passes(HistKeys hist_keys, Bucket bucket, SelShared& sh, int hi,
-                                             uint32_t& prefix, uint32_t& mask, uint32_t& need) {
-  while (hi > 0) {
+                                             uint32_t& prefix, uint32_t& mask, uint32_t& need,
+                                             int max_passes = 8) {
+  for (int pass = 0; hi > 0 && pass < max_passes; ++pass) {
     const int width = hi < 11 ? hi : 11;
     const int shift = hi - width;
     const uint32_t dmask = (1u << width) - 1u;
@@ -186,7 +188,7 @@ __device__ __forceinline__ void radix_passes(HistKeys hist_keys, Bucket bucket, 
     const uint32_t cnt = sh.s_cnt;
     mask |= dmask << shift;
     hi = shift;
-    if (cnt == need || hi == 0) break;   // uniform across the block
+    if (cnt == need || hi == 0 || pass + 1 == max_passes) break;   // uniform across the block
     if (cnt <= (uint32_t)kBucketMax && bucket(prefix, mask, need, cnt)) break;
   }
 }
@@ -198,8 +200,11 @@ __device__ __forceinline__ bool valid_pos(int j, int n) { return KPT * (int)thre
 
 // Finds (prefix, mask, need): the k largest of the n keys are every key with
 // (key & mask) > prefix plus the first `need` keys (in position order) with
-// (key & mask) == prefix.  Requires 1 <= k <= n.
-template <int KPT>
+// (key & mask) == prefix.  Requires 1 <= k <= n.  ONE_PASS: stop after the first
+// digit (prefix then has zeros below it: the k-th largest key lies in
+// [prefix, prefix + 2^shift) and every key >= prefix is among the k largest or in
+// that bin).
+template <int KPT, bool ONE_PASS = false>
 __device__ __forceinline__ void reg_threshold(const uint32_t (&key)[KPT], int n, uint32_t k, SelShared& sh,
                                               uint32_t& prefix, uint32_t& mask, uint32_t& need) {
   const int lane = threadIdx.x & 63;
@@ -263,7 +268,7 @@ __device__ __forceinline__ void reg_threshold(const uint32_t (&key)[KPT], int n,
     resolved = true;
     return true;
   };
-  radix_passes(hist, bucket, sh, hi, prefix, mask, need);
+  radix_passes(hist, bucket, sh, hi, prefix, mask, need, ONE_PASS ? 1 : 8);
   if (resolved) {   // uniform: the exact threshold key and the count of its ties to take
     prefix = sh.s_prefix;
     need = sh.s_need;
@@ -473,19 +478,25 @@ struct LongWs {
 
 constexpr int kFilterGroups = kTopkThreads / kFilterThreads;   // chunks per workgroup
 
-// The threshold key: its rank in a fixed, evenly spaced sample of the row is chosen to
-// leave ~3k keys of the row at or above it (at most three quarters of the candidate
-// capacity; a larger k keeps a smaller margin).  key >= tau <=> (key & mask) >= prefix.
+// The threshold key: the lower edge of the first-digit bin that holds the key of rank
+// r in a fixed sample of the row, r chosen to leave ~3k keys of the row at or above
+// it (at most three quarters of the candidate capacity; a larger k keeps a smaller
+// margin).  One radix pass: the bin adds a few samples' worth of keys beyond rank r.
+// The sample is 64 runs of 64 consecutive keys, evenly spaced (V > kRegKeys).
 __device__ __forceinline__ uint32_t sample_threshold(const IndexArgs& A, const float* src, int V, SelShared& sh) {
   constexpr int KPT = kSample / kTopkThreads;
+  constexpr int kRun = 64, kRuns = kSample / kRun;
   uint32_t key[KPT];
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) key[j] = order_key(src[(long)(kTopkThreads * j + threadIdx.x) * V / kSample]);
+  for (int j = 0; j < KPT; ++j) {
+    const int i = KPT * (int)threadIdx.x + j;   // sample i: key i % 64 of run i / 64
+    key[j] = order_key(src[(long)(i / kRun) * (V / kRuns) + i % kRun]);
+  }
   const long want = min((long)3 * A.topk, (long)kCandCap * 3 / 4);
   long r = (want * kSample + V - 1) / V;
   r = r < 1 ? 1 : (r > kSample ? kSample : r);
   uint32_t prefix, mask, need;
-  reg_threshold<KPT>(key, kSample, (uint32_t)r, sh, prefix, mask, need);
+  reg_threshold<KPT, true>(key, kSample, (uint32_t)r, sh, prefix, mask, need);
   return prefix;
 }
 
