@@ -49,14 +49,20 @@ constexpr int kBins = 2048;           // 11-bit radix digit
 constexpr int kHistWords = kBins + kBins / 32;
 constexpr int kBucketMax = 64;
 constexpr int kMaxTopk = 8192;        // largest k: the C ABI's 4096, or a rescoring prefilter's candidates
+static_assert(2 * kMaxTopk >= kCandCap, "the output arrays stage a long row's candidates");
 
 struct SelShared {
   uint32_t hist[kHistWords];          // bin b at b + b / 32
   uint32_t red[2 * kTW];
   uint32_t wcnt[2 * kTW];
   uint32_t bkey[kBucketMax];
-  int32_t oidx[kMaxTopk];             // the selection in output order, written out coalesced
-  uint32_t okey[kMaxTopk];
+  union {
+    struct {
+      int32_t oidx[kMaxTopk];         // the selection in output order, written out coalesced
+      uint32_t okey[kMaxTopk];
+    };
+    uint32_t stage[2 * kMaxTopk];     // (long rows: the candidate keys, before the selection)
+  };
   uint32_t bcount;
   uint32_t s_prefix, s_need, s_cnt;
 };
@@ -552,31 +558,34 @@ __global__ __launch_bounds__(kTopkThreads) void topk_filter_kernel(IndexArgs A, 
   if (threadIdx.x == (unsigned)(grp * kFilterThreads)) L.counts[row * L.chunks + c] = total;
 }
 
-// Exact selection among the M candidates of a long row (KPT * 1024 >= M): candidate c
-// sits in the chunk whose offset range holds it; its position in the row comes along.
+// Exact selection among the M candidates of a long row (KPT * 1024 >= M <= kCandCap).
+// Chunk c's candidates (stored from c * kChunk in the row's lists) are copied, 16
+// threads per chunk with coalesced reads, to candidate positions coff[c] .. in LDS
+// (keys to the staging area, row positions to cand_idx); thread t then takes
+// candidates KPT t .. KPT t + KPT - 1.
 template <int KPT>
 __device__ __forceinline__ void select_candidates(const uint32_t* gk, const int32_t* gi, const uint32_t* coff,
                                                   int nch, int M, int k, int32_t* cand_idx, int32_t* oi,
                                                   float* os, SelShared& sh) {
+  constexpr int kT = 16;
+  for (int c = (int)threadIdx.x / kT; c < nch; c += kTopkThreads / kT) {
+    const int base = (int)coff[c], n = (int)coff[c + 1] - base;
+    const long src = (long)c * kChunk;
+    for (int i = (int)threadIdx.x % kT; i < n; i += kT) {
+      sh.stage[base + i] = gk[src + i];
+      cand_idx[base + i] = gi[src + i];
+    }
+  }
+  __syncthreads();
   uint32_t key[KPT];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const int c = KPT * (int)threadIdx.x + j;
-    key[j] = 0u;
-    if (c < M) {
-      int lo = 0, hi = nch - 1;   // chunk holding candidate c: last chunk whose offset is <= c
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (coff[mid] <= (uint32_t)c) lo = mid;
-        else hi = mid - 1;
-      }
-      const long src_pos = (long)lo * kChunk + (c - (int)coff[lo]);
-      key[j] = gk[src_pos];
-      cand_idx[c] = gi[src_pos];
-    }
+    key[j] = c < M ? sh.stage[c] : 0u;
   }
+  // (the staging area is next written by the compaction, after the threshold's barriers)
   uint32_t prefix, mask, need;
-  reg_threshold<KPT>(key, M, (uint32_t)k, sh, prefix, mask, need);   // (its barriers publish cand_idx)
+  reg_threshold<KPT>(key, M, (uint32_t)k, sh, prefix, mask, need);
   auto idx_of = [&](int j) { return cand_idx[KPT * threadIdx.x + j]; };
   reg_compact<KPT>(key, M, prefix, mask, need, k, idx_of, oi, os, sh);
 }
