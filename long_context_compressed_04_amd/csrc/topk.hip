@@ -515,7 +515,6 @@ __global__ __launch_bounds__(kTopkThreads) void topk_filter_kernel(IndexArgs A, 
   const int V = row_visible(A, row);
   if (V <= kRegKeys || V <= A.topk) return;
   const float* src = scores + row * A.n_max;
-  const uint32_t tau = sample_threshold(A, src, V, sh);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int kGw = kFilterThreads / 64;                  // waves per group
   const int grp = wave / kGw, gw = wave % kGw;
@@ -524,12 +523,20 @@ __global__ __launch_bounds__(kTopkThreads) void topk_filter_kernel(IndexArgs A, 
   constexpr int kIt = kChunk / kFilterThreads;              // 16 keys per lane
   constexpr int kPerWave = kChunk / kGw;
   const int w0 = c0 + gw * kPerWave;
+  // this chunk's scores are requested first: they arrive while the threshold forms
+  float sc[kIt];
+#pragma unroll
+  for (int r = 0; r < kIt; ++r) {
+    const int i = w0 + r * 64 + lane;
+    sc[r] = i < V ? src[i] : 0.f;
+  }
+  const uint32_t tau = sample_threshold(A, src, V, sh);
   uint32_t key[kIt];
   uint32_t cnt = 0;
 #pragma unroll
   for (int r = 0; r < kIt; ++r) {
     const int i = w0 + r * 64 + lane;
-    key[r] = i < V ? order_key(src[i]) : 0u;
+    key[r] = i < V ? order_key(sc[r]) : 0u;
     cnt += __popcll(__ballot(i < V && key[r] >= tau));
   }
   if (lane == 0) wtot[wave] = cnt;
