@@ -566,19 +566,33 @@ __global__ __launch_bounds__(kTopkThreads) void topk_filter_kernel(IndexArgs A, 
 }
 
 // Exact selection among the M candidates of a long row (KPT * 1024 >= M <= kCandCap).
-// Chunk c's candidates (stored from c * kChunk in the row's lists) are copied, 16
+// Chunk c's candidates (stored from c * kChunk in the row's lists) are copied, kCopyT
 // threads per chunk with coalesced reads, to candidate positions coff[c] .. in LDS
 // (keys to the staging area, row positions to cand_idx); thread t then takes
-// candidates KPT t .. KPT t + KPT - 1.
+// candidates KPT t .. KPT t + KPT - 1.  The first kSpec per thread of the first
+// kTopkThreads / kCopyT chunks were read before the counts were known (spk, spi).
+constexpr int kCopyT = 16, kSpec = 8;
 template <int KPT>
-__device__ __forceinline__ void select_candidates(const uint32_t* gk, const int32_t* gi, const uint32_t* coff,
+__device__ __forceinline__ void select_candidates(const uint32_t (&spk)[kSpec], const int32_t (&spi)[kSpec],
+                                                  const uint32_t* gk, const int32_t* gi, const uint32_t* coff,
                                                   int nch, int M, int k, int32_t* cand_idx, int32_t* oi,
                                                   float* os, SelShared& sh) {
-  constexpr int kT = 16;
-  for (int c = (int)threadIdx.x / kT; c < nch; c += kTopkThreads / kT) {
+  const int c_sp = (int)threadIdx.x / kCopyT;
+  for (int c = c_sp; c < nch; c += kTopkThreads / kCopyT) {
     const int base = (int)coff[c], n = (int)coff[c + 1] - base;
     const long src = (long)c * kChunk;
-    for (int i = (int)threadIdx.x % kT; i < n; i += kT) {
+    int i = (int)threadIdx.x % kCopyT;
+    if (c == c_sp) {
+#pragma unroll
+      for (int j = 0; j < kSpec; ++j) {
+        if (i + kCopyT * j < n) {
+          sh.stage[base + i + kCopyT * j] = spk[j];
+          cand_idx[base + i + kCopyT * j] = spi[j];
+        }
+      }
+      i += kCopyT * kSpec;
+    }
+    for (; i < n; i += kCopyT) {
       sh.stage[base + i] = gk[src + i];
       cand_idx[base + i] = gi[src + i];
     }
@@ -619,8 +633,24 @@ __global__ __launch_bounds__(kTopkThreads) void topk_candidates_kernel(IndexArgs
     select_reg_row<kMaxKpt>(key, V, k, oi, os, sh);
     return;
   }
-  // chunk offsets (exclusive scan of the per-chunk counts, one wave)
   const int nch = (V + kChunk - 1) / kChunk;
+  const uint32_t* gk = L.ckey + row * A.n_max;
+  const int32_t* gi = L.cidx + row * A.n_max;
+  // the first candidates of the first chunks are requested before the counts arrive
+  // (reads inside the row's lists; those past a chunk's count are not used)
+  uint32_t spk[kSpec];
+  int32_t spi[kSpec];
+  {
+    const int c = (int)threadIdx.x / kCopyT, i = (int)threadIdx.x % kCopyT;
+#pragma unroll
+    for (int j = 0; j < kSpec; ++j) {
+      const long p = (long)c * kChunk + i + kCopyT * j;
+      const bool in = c < nch && p < A.n_max;
+      spk[j] = in ? gk[p] : 0u;
+      spi[j] = in ? gi[p] : -1;
+    }
+  }
+  // chunk offsets (exclusive scan of the per-chunk counts, one wave)
   const int lane = threadIdx.x & 63;
   if (threadIdx.x < 64) {
     uint32_t run = 0;
@@ -640,12 +670,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_candidates_kernel(IndexArgs
     global_select(key_at, V, k, oi, os, sh);
     return;
   }
-  const uint32_t* gk = L.ckey + row * A.n_max;
-  const int32_t* gi = L.cidx + row * A.n_max;
   // as few registers per thread as the candidate count allows
-  if (M <= 4 * kTopkThreads) select_candidates<4>(gk, gi, coff, nch, M, k, cand_idx, oi, os, sh);
-  else if (M <= 8 * kTopkThreads) select_candidates<8>(gk, gi, coff, nch, M, k, cand_idx, oi, os, sh);
-  else select_candidates<kCandCap / kTopkThreads>(gk, gi, coff, nch, M, k, cand_idx, oi, os, sh);
+  if (M <= 4 * kTopkThreads) select_candidates<4>(spk, spi, gk, gi, coff, nch, M, k, cand_idx, oi, os, sh);
+  else if (M <= 8 * kTopkThreads) select_candidates<8>(spk, spi, gk, gi, coff, nch, M, k, cand_idx, oi, os, sh);
+  else select_candidates<kCandCap / kTopkThreads>(spk, spi, gk, gi, coff, nch, M, k, cand_idx, oi, os, sh);
 }
 
 static int long_chunks(const IndexArgs& A) { return (A.n_max + kChunk - 1) / kChunk; }
