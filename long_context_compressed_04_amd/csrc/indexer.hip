@@ -435,11 +435,20 @@ static void launch_mfma_hb(const IndexArgs& A, float* scores, hipStream_t s) {
     index_scores_pf<HB><<<grid, kIdxWaves * 64, 0, s>>>(A, scores);
     return;
   }
+  const int q_tile = A.n_q >= 64 ? 16 : 1;
+  LaunchTimer timer(FP4 ? "index_scores_mxfp4" : "index_scores_bf16", s);
+  if (FP4 && A.q_quantize) {
+    // every workgroup reads and quantises all of q (32 KB of fp32 for 64 heads): more
+    // entries per workgroup, fewer copies of q read
+    constexpr int TPW = 8;
+    const int chunk = kIdxWaves * TPW * 32;
+    dim3 grid((A.n_max + chunk - 1) / chunk, (A.n_q + q_tile - 1) / q_tile, A.batch);
+    index_scores_mfma<HB, FP4, TPW><<<grid, kIdxWaves * 64, 0, s>>>(A, scores, q_tile);
+    return;
+  }
   constexpr int TPW = 2;
   const int chunk = kIdxWaves * TPW * 32;
-  const int q_tile = A.n_q >= 64 ? 16 : 1;
   dim3 grid((A.n_max + chunk - 1) / chunk, (A.n_q + q_tile - 1) / q_tile, A.batch);
-  LaunchTimer timer(FP4 ? "index_scores_mxfp4" : "index_scores_bf16", s);
   index_scores_mfma<HB, FP4, TPW><<<grid, kIdxWaves * 64, 0, s>>>(A, scores, q_tile);
 }
 
