@@ -67,8 +67,10 @@ typedef enum {
 typedef enum {
   CSA_F32 = 0,   /* IEEE binary32 */
   CSA_BF16 = 1,  /* bfloat16 stored as uint16 bit patterns */
-  CSA_MXFP4 = 2  /* OCP MX v1.0 MXFP4: 4-bit e2m1 codes, two per byte (even element in
+  CSA_MXFP4 = 2, /* OCP MX v1.0 MXFP4: 4-bit e2m1 codes, two per byte (even element in
                     the low nibble), plus one e8m0 scale byte per 32 elements */
+  CSA_FP8 = 3    /* OCP FP8 E4M3 ("E4M3FN"): one byte per element, bias 7, max 448, no
+                    scale (the KV cache variant: csa_mqa_desc.kv_dtype) */
 } csa_dtype;
 
 /* Returns CSA_ABI_VERSION. */
@@ -130,6 +132,17 @@ csa_status csa_compress(const csa_compress_desc* desc, const void* a, const void
  * ---------------------------------------------------------------------------- */
 csa_status csa_mxfp4_quantize(int32_t dtype, const void* x, int64_t n_blocks, uint8_t* codes,
                               uint8_t* scales, void* stream);
+
+/* ------------------------------------------------------------------------------
+ * csa_fp8_quantize -- FP8 E4M3 encoding of n values ("DeepSeek-V4-Pro" techniques
+ * map, inference quantization: FP8 KV-cache quantization), for a compressed KV
+ * cache and window rows kept in FP8 (csa_mqa_desc.kv_dtype = CSA_FP8).  Per
+ * element, no scale: x is clamped to [-448, 448] and rounded to the nearest E4M3
+ * value, ties to the even code; the sign bit copies the sign of x.
+ *   x      [n]  dtype CSA_F32 or CSA_BF16, 16-byte aligned
+ *   codes  [n]  bytes, 8-byte aligned;   n a multiple of 8
+ * ---------------------------------------------------------------------------- */
+csa_status csa_fp8_quantize(int32_t dtype, const void* x, int64_t n, uint8_t* codes, void* stream);
 
 /* ------------------------------------------------------------------------------
  * Lightning indexer and top-k ("DeepSeek v4" summary, "Compressed Sparse
@@ -264,6 +277,13 @@ typedef struct {
                           ("DeepSeek-V4-Pro" techniques map, inference kernels:
                           batch-invariant attention decoding, separate split-K outputs
                           with a deterministic reduction) */
+  int32_t kv_dtype;   /* 0: kv and kv_raw hold `dtype` rows.  CSA_FP8: they hold FP8
+                         E4M3 rows of head_dim bytes (csa_fp8_quantize; no scale),
+                         read as their exact bf16 values ("DeepSeek-V4-Pro"
+                         techniques map, FP8 KV cache).  Requires dtype CSA_BF16,
+                         head_dim 512, heads a multiple of 32, rms_weight NULL and
+                         a scale <= 68/512 (0 selects 1/sqrt(512)); kv and kv_raw
+                         16-byte aligned.  Otherwise CSA_ERR_UNSUPPORTED */
 } csa_mqa_desc;
 
 size_t csa_mqa_workspace_size(const csa_mqa_desc* desc, int32_t dense);

@@ -16,7 +16,7 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa.so")
 _lib = None
 
-F32, BF16, MXFP4 = 0, 1, 2
+F32, BF16, MXFP4, FP8 = 0, 1, 2, 3
 
 
 class CsaError(RuntimeError):
@@ -40,7 +40,7 @@ class MqaDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "n_q", "heads", "head_dim", "topk", "m", "n_max", "window", "kv_cap", "raw_cap")] + [
         ("scale", ctypes.c_float), ("eps", ctypes.c_float), ("dtype", ctypes.c_int32),
-        ("split_items", ctypes.c_int32)]
+        ("split_items", ctypes.c_int32), ("kv_dtype", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -79,6 +79,8 @@ def lib():
         L.csa_compress.restype = S
         L.csa_mxfp4_quantize.argtypes = [ctypes.c_int32, V, ctypes.c_int64, V, V, V]
         L.csa_mxfp4_quantize.restype = S
+        L.csa_fp8_quantize.argtypes = [ctypes.c_int32, V, ctypes.c_int64, V, V]
+        L.csa_fp8_quantize.restype = S
         L.csa_index_workspace_size.argtypes = [ctypes.POINTER(IndexDesc)]
         L.csa_index_workspace_size.restype = Z
         L.csa_index_scores.argtypes = [ctypes.POINTER(IndexDesc)] + [V] * 9
@@ -176,6 +178,17 @@ def mxfp4_quantize(x, codes=None, scales=None):
     return codes, scales
 
 
+def fp8_quantize(x, codes=None):
+    """FP8 E4M3 codes (uint8, same shape as x): clamp to +-448, nearest value, ties to
+    the even code.  x float32 or bfloat16 with a multiple of 8 elements."""
+    if codes is None:
+        codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if codes.numel() != x.numel():
+        raise ValueError("codes do not match x")
+    _check(lib().csa_fp8_quantize(_dtype_code(x), _p(x), x.numel(), _p(codes), _stream(x)))
+    return codes
+
+
 def _index_dtype(q_idx, k_idx):
     """(dtype, q_quantize): MXFP4 keys with fp32 queries quantise the queries inside
     the call; otherwise q_idx and k_idx share one dtype."""
@@ -236,15 +249,20 @@ def index_topk_rescored(q_idx, q_scale, q_bf16, w, k_idx, k_scale, k_bf16, n_ent
 
 def _mqa_desc(q, kv, kv_raw, *, topk=0, m=1, n_max=0, window=128, scale=0.0, eps=1e-6, split_items=0):
     B, n_q, H, D = q.shape
+    # uint8 caches hold FP8 E4M3 rows (fp8_quantize)
+    kv_dtype = FP8 if kv.dtype == torch.uint8 else 0
+    if (kv_raw.dtype == torch.uint8) != (kv_dtype == FP8):
+        raise ValueError("kv and kv_raw must both be FP8 (uint8) or both of q's dtype")
     return MqaDesc(B, n_q, H, D, topk, m, n_max, window, kv.shape[1], kv_raw.shape[1], float(scale), float(eps),
-                   _dtype_code(q), split_items)
+                   _dtype_code(q), split_items, kv_dtype)
 
 
 def sparse_mqa(q, kv, idx, kv_raw, raw_base, q_pos, *, window, scale=0.0, eps=1e-6, rms_weight=None, sink=None,
                split_items=0, workspace=None, out=None, lse=None):
     """CSA attention over idx (-1 skipped) plus the sliding window.  Returns (out, lse).
     sink: per-head sink logits [heads] fp32 or None; split_items > 0 selects
-    batch-invariant splitting (see csa_mqa_desc)."""
+    batch-invariant splitting (see csa_mqa_desc).  kv and kv_raw as uint8: FP8 E4M3
+    rows (bf16 q, no rms_weight)."""
     d = _mqa_desc(q, kv, kv_raw, topk=idx.shape[-1], window=window, scale=scale, eps=eps, split_items=split_items)
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if lse is None else lse
@@ -258,7 +276,8 @@ def hca_dense_mqa(q, kv, n_entries, kv_raw, raw_base, q_pos, *, m, window, n_max
                   rms_weight=None, sink=None, split_items=0, workspace=None, out=None, lse=None):
     """HCA attention over every visible compressed entry plus the window.  Returns (out, lse).
     sink: per-head sink logits [heads] fp32 or None; split_items > 0 selects
-    batch-invariant splitting (see csa_mqa_desc)."""
+    batch-invariant splitting (see csa_mqa_desc).  kv and kv_raw as uint8: FP8 E4M3
+    rows (bf16 q, no rms_weight)."""
     d = _mqa_desc(q, kv, kv_raw, m=m, n_max=kv.shape[1] if n_max is None else n_max, window=window, scale=scale,
                   eps=eps, split_items=split_items)
     out = torch.empty_like(q) if out is None else out

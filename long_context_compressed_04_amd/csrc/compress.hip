@@ -157,6 +157,49 @@ __global__ __launch_bounds__(256) void mxfp4_quantize_kernel(const void* x, int6
   scales[blk] = scale;
 }
 
+// FP8 E4M3 quantisation: one thread per 8 values.  gfx950's conversion rounds to the
+// nearest E4M3 value (ties to even) but turns values beyond the range into NaN, so
+// they are clamped to +-448 first.
+template <bool IN_BF16>
+__global__ __launch_bounds__(256) void fp8_quantize_kernel(const void* x, int64_t n8, uint8_t* codes) {
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= n8) return;
+  float v[8];
+  if (IN_BF16) {
+    const uint4 q = *((const uint4*)x + g);
+    const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[2 * k] = __uint_as_float(w4[k] << 16);
+      v[2 * k + 1] = __uint_as_float(w4[k] & 0xffff0000u);
+    }
+  } else {
+    const float4 a = *((const float4*)x + 2 * g), b = *((const float4*)x + 2 * g + 1);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  uint32_t w[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float c[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) c[k] = fminf(fmaxf(v[4 * h + k], -448.f), 448.f);
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], r, true);
+    w[h] = (uint32_t)r;
+  }
+  *((uint2*)codes + g) = make_uint2(w[0], w[1]);
+}
+
+hipError_t launch_fp8_quantize(int in_bf16, const void* x, int64_t n, uint8_t* codes, hipStream_t s) {
+  const int64_t n8 = n / 8;
+  if (n8 <= 0) return hipSuccess;
+  dim3 grid((unsigned)((n8 + 255) / 256)), block(256);
+  LaunchTimer timer("fp8_quantize", s);
+  if (in_bf16) fp8_quantize_kernel<true><<<grid, block, 0, s>>>(x, n8, codes);
+  else fp8_quantize_kernel<false><<<grid, block, 0, s>>>(x, n8, codes);
+  return hipGetLastError();
+}
+
 hipError_t launch_mxfp4_quantize(int in_bf16, const void* x, int64_t n_blocks, uint8_t* codes, uint8_t* scales,
                                  hipStream_t s) {
   if (n_blocks <= 0) return hipSuccess;

@@ -141,6 +141,13 @@ csa_status check_mqa(const char* fn, const csa_mqa_desc* d, int dense, const voi
   } else {
     return fail(CSA_ERR_DTYPE, "%s: dtype must be CSA_F32 or CSA_BF16", fn);
   }
+  if (d->kv_dtype != 0) {
+    if (d->kv_dtype != CSA_FP8) return fail(CSA_ERR_DTYPE, "%s: kv_dtype must be 0 or CSA_FP8", fn);
+    const float sc = d->scale > 0.f ? d->scale : 1.f / std::sqrt((float)d->head_dim);
+    if (d->dtype != CSA_BF16 || d->heads % 32 != 0 || sc * 512.f > 68.f)
+      return fail(CSA_ERR_UNSUPPORTED, "%s: an FP8 cache needs dtype CSA_BF16, heads a multiple of 32 and scale <= 68/512",
+                  fn);
+  }
   return CSA_OK;
 }
 
@@ -152,6 +159,7 @@ csa::MqaArgs mqa_args(const csa_mqa_desc* d, int dense) {
   A.scale = d->scale > 0.f ? d->scale : 1.f / std::sqrt((float)d->head_dim);
   A.eps = d->eps;
   A.split_items = d->split_items;
+  A.kv_f8 = d->kv_dtype == CSA_FP8;
   return A;
 }
 
@@ -187,6 +195,16 @@ csa_status csa_compress(const csa_compress_desc* d, const void* a, const void* b
   A.in_bf16 = d->in_dtype == CSA_BF16; A.out_bf16 = d->out_dtype == CSA_BF16;
   A.a = a; A.b = b; A.za = za; A.zb = zb; A.bias_a = bias_a; A.bias_b = bias_b; A.out = out;
   return hip_status(csa::launch_compress(A, (hipStream_t)stream), "csa_compress");
+}
+
+csa_status csa_fp8_quantize(int32_t dtype, const void* x, int64_t n, uint8_t* codes, void* stream) {
+  if (!x || !codes) return fail(CSA_ERR_NULL, "csa_fp8_quantize: x and codes are required");
+  if (dtype != CSA_F32 && dtype != CSA_BF16) return fail(CSA_ERR_DTYPE, "csa_fp8_quantize: dtype must be CSA_F32 or CSA_BF16");
+  if (n < 0 || n % 8 != 0) return fail(CSA_ERR_SHAPE, "csa_fp8_quantize: n must be a non-negative multiple of 8");
+  if (!aligned16(x) || ((uintptr_t)codes & 7u))
+    return fail(CSA_ERR_ALIGN, "csa_fp8_quantize: x must be 16-byte and codes 8-byte aligned");
+  return hip_status(csa::launch_fp8_quantize(dtype == CSA_BF16, x, n, codes, (hipStream_t)stream),
+                    "csa_fp8_quantize");
 }
 
 csa_status csa_mxfp4_quantize(int32_t dtype, const void* x, int64_t n_blocks, uint8_t* codes, uint8_t* scales,
@@ -309,6 +327,7 @@ static csa_status run_mqa(const char* fn, const csa_mqa_desc* d, int dense, cons
     return fail(CSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws ? ws_bytes : 0);
   A.q = q; A.kv = kv; A.idx = idx; A.n_entries = ne; A.kv_raw = kv_raw; A.raw_base = raw_base; A.q_pos = qpos;
   A.gamma = g; A.sink = sink; A.out = out; A.lse = lse;
+  if (A.kv_f8 && g) return fail(CSA_ERR_UNSUPPORTED, "%s: an FP8 cache needs rms_weight NULL", fn);
   return hip_status(csa::launch_mqa(A, ws, ws_bytes, s), fn);
 }
 
@@ -340,6 +359,8 @@ static csa_status check_decode(const csa_decode_args* a) {
   if (st != CSA_OK) return st;
   st = check_mqa("csa_decode", &a->attn, 0, a->q, a->kv, a->out_idx, a->kv_raw, a->raw_base, a->q_pos, a->out);
   if (st != CSA_OK) return st;
+  if (a->attn.kv_dtype != 0 && a->kv_job)
+    return fail(CSA_ERR_UNSUPPORTED, "csa_decode: no kv_job with an FP8 cache (compress, then csa_fp8_quantize)");
   const csa_compress_job* jobs[2] = {a->kv_job, a->key_job};
   for (const csa_compress_job* j : jobs) {
     if (!j) continue;

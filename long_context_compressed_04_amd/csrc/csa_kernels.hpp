@@ -17,6 +17,7 @@ hipError_t launch_compress(const CompressArgs& A, hipStream_t s);
 
 hipError_t launch_mxfp4_quantize(int in_bf16, const void* x, int64_t n_blocks, uint8_t* codes,
                                  uint8_t* scales, hipStream_t s);
+hipError_t launch_fp8_quantize(int in_bf16, const void* x, int64_t n, uint8_t* codes, hipStream_t s);
 
 // dtype: 0 = fp32, 1 = bf16, 2 = mxfp4
 struct IndexArgs {
@@ -47,6 +48,7 @@ struct MqaArgs {
   const void* kv_raw; const int32_t* raw_base; const int32_t* q_pos; const float* gamma;
   void* out; float* lse;
   int split_items = 0;   // > 0: batch-invariant split boundaries (multiples of it)
+  int kv_f8 = 0;         // kv and kv_raw hold FP8 E4M3 rows (bf16 path, 32-head groups)
   const float* sink = nullptr;   // [heads] sink logits (natural log), or none
 };
 // Workspace bytes the MQA path needs for these sizes (split partials).

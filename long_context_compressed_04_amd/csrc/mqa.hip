@@ -627,8 +627,29 @@ constexpr int kSdWaves = kSdQk + kSdPv + kSdGa;
 constexpr int kSdRpw = kTile / kSdGa;   // rows each gather wave loads per tile
 constexpr int kPRow = 2 * kTile + 16;   // bytes per head row of a weight buffer (padded)
 
+// 16 FP8 E4M3 values -> bf16, stored as 32 bytes (exact: E4M3 has 3 mantissa bits).
+__device__ __forceinline__ void fp8x16_to_bf16(uint4 v, uint8_t* dst) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], false);   // bytes 0, 1
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], true);    // bytes 2, 3
+    o[2 * k] = (__float_as_uint(lo[0]) >> 16) | (__float_as_uint(lo[1]) & 0xffff0000u);
+    o[2 * k + 1] = (__float_as_uint(hi[0]) >> 16) | (__float_as_uint(hi[1]) & 0xffff0000u);
+  }
+  *(uint4*)dst = make_uint4(o[0], o[1], o[2], o[3]);
+  *(uint4*)(dst + 16) = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
+// F8: the cache (kv and the window rows) holds FP8 E4M3 rows of 512 bytes.  The gather
+// waves load them into registers instead, 1 KB (two rows) per instruction and wave,
+// three tiles ahead (tile s+3 requested at step s), and at step s write tile s+1 to
+// its tile buffer as bf16; the logit and value waves are the same as without F8.
+template <bool F8>
 __global__ __launch_bounds__(kSdWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void mqa_sd_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml) {
+  constexpr int kRowG = F8 ? kD : 2 * kD;   // bytes per cache row
   __shared__ __attribute__((aligned(16))) uint8_t tb0[kTile * kRowB2];
   __shared__ __attribute__((aligned(16))) uint8_t tb1[kTile * kRowB2];
   __shared__ __attribute__((aligned(16))) uint8_t tb2[kTile * kRowB2];
@@ -660,7 +681,7 @@ void mqa_sd_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml) {
   {
     ItemSource src;
     int total;
-    query_items(A, b, row, 2, src, total);
+    query_items(A, b, row, F8 ? 1 : 2, src, total);   // bytes per element of the cache
     R.kv = src.kv; R.raw = src.raw; R.n_first = src.n_first; R.kv_rows = src.kv_rows; R.win_lo = src.win_lo;
     R.raw_base = src.raw_base; R.raw_cap = src.raw_cap; R.dense = A.dense;
     R.it0 = split * L.ips;
@@ -680,35 +701,87 @@ void mqa_sd_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml) {
     if (item >= R.it1) return nullptr;
     if (item < R.n_first) {
       const int e = R.dense ? item : slot[item - R.it0];
-      return (e >= 0 && e < R.kv_rows) ? R.kv + (long)e * (kD * 2) : nullptr;
+      return (e >= 0 && e < R.kv_rows) ? R.kv + (long)e * kRowG : nullptr;
     }
     const int r = R.win_lo + (item - R.n_first) - R.raw_base;
-    return (r >= 0 && r < R.raw_cap) ? R.raw + (long)r * (kD * 2) : nullptr;
+    return (r >= 0 && r < R.raw_cap) ? R.raw + (long)r * kRowG : nullptr;
   };
   const int n_tiles = (R.it1 - R.it0 + kTile - 1) / kTile;
   const int gw = wave - kSdQk - kSdPv;   // gather-wave index (>= 0 for gather waves)
   auto issue = [&](int t, uint8_t* dst) {
     issue_rows<kSdRpw, kSdGa>(resolve, R.it0 + t * kTile + gw, lane, dst + gw * kRowB2);
   };
-  if (gw >= 0) {
+  // F8: gather wave gw takes rows 2 gw, 2 gw + 1 (registers r[0]) and 16 + 2 gw,
+  // 17 + 2 gw (r[1]) of a tile, lanes 32 .. 63 the second row of each pair.  Tiles past
+  // the last are read from the zero row, so every step makes the same requests.
+  auto load8 = [&](int t, uint4 (&r)[2]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint8_t* p = resolve(R.it0 + t * kTile + 2 * gw + 16 * j + (lane >> 5));
+      r[j] = *(const uint4*)((p ? p : g_zero_row) + 16 * (lane & 31));
+    }
+  };
+  auto store8 = [&](const uint4 (&r)[2], uint8_t* tile) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      fp8x16_to_bf16(r[j], tile + (2 * gw + 16 * j + (lane >> 5)) * kRowB2 + 32 * (lane & 31));
+  };
+  // ---- u = q / rms(q), staged in tile buffer 3 (free until tile 3 is gathered)
+  auto stage_q = [&]() {
+#pragma unroll
+    for (int j = 0; j < kQn; ++j) {
+      const int hq = wave + kSdWaves * j;
+      const uint4 v = qraw[j];
+      const float ss = wave_sum(sumsq_bf16x8(v, 0.f));
+      const float qinv = 1.f / sqrtf(ss * (1.f / kD) + A.eps);
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+      uint32_t o4[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        o4[k] = pack_bf16x2(__uint_as_float(w4[k] << 16) * qinv, __uint_as_float(w4[k] & 0xffff0000u) * qinv);
+      *(uint4*)(tb3 + hq * kRowB2 + 16 * lane) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
+    }
+  };
+  if constexpr (F8) {
+    if (gw >= 0) {
+      // ============================================================ FP8 gather waves
+      // (their whole path, so that the registers in flight never meet another
+      // role's code)
+      uint4 rf8[3][2];   // tiles in flight, tile t in rf8[t % 3]
+      load8(0, rf8[0]);
+      load8(1, rf8[1]);
+      load8(2, rf8[2]);
+      stage_q();
+      store8(rf8[0], tb0);
+      lds_barrier();   // q staged, tile 0 in its buffer
+      // step s: request tile s+3, write tile s+1 to buffer (s+1) % 4 (tile s-3 was
+      // accumulated at step s-2)
+      auto gstep = [&](auto KC, int s) {
+        constexpr int K = decltype(KC)::value;   // s % 3
+        load8(s + 3, rf8[K]);
+        const int bi = (s + 1) & 3;
+        store8(rf8[(K + 1) % 3], bi == 0 ? tb0 : (bi == 1 ? tb1 : (bi == 2 ? tb2 : tb3)));
+        lds_barrier();
+      };
+      // (the loop repeats only after all three steps, so the registers in flight are
+      // the same at every entry)
+      for (int s = 0;; s += 3) {
+        gstep(std::integral_constant<int, 0>{}, s);
+        if (s + 1 > n_tiles) break;
+        gstep(std::integral_constant<int, 1>{}, s + 1);
+        if (s + 2 > n_tiles) break;
+        gstep(std::integral_constant<int, 2>{}, s + 2);
+        if (s + 3 > n_tiles) break;
+      }
+      lds_barrier();   // the head sums are in LDS
+      return;
+    }
+  } else if (gw >= 0) {
     if (n_tiles > 0) issue(0, tb0);
     if (n_tiles > 1) issue(1, tb1);
   }
-  // ---- u = q / rms(q), staged in tile buffer 3 (free until tile 3 is gathered)
-#pragma unroll
-  for (int j = 0; j < kQn; ++j) {
-    const int hq = wave + kSdWaves * j;
-    const uint4 v = qraw[j];
-    const float ss = wave_sum(sumsq_bf16x8(v, 0.f));
-    const float qinv = 1.f / sqrtf(ss * (1.f / kD) + A.eps);
-    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-    uint32_t o4[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      o4[k] = pack_bf16x2(__uint_as_float(w4[k] << 16) * qinv, __uint_as_float(w4[k] & 0xffff0000u) * qinv);
-    *(uint4*)(tb3 + hq * kRowB2 + 16 * lane) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
-  }
-  if (gw >= 0) {
+  stage_q();
+  if (!F8 && gw >= 0) {
     if (n_tiles > 1) wait_vmcnt<kSdRpw>();
     else wait_vmcnt<0>();
   }
@@ -1358,7 +1431,7 @@ static MqaLaunch plan_mqa(const MqaArgs& A) {
     // from a query's first item) follow from the configuration alone, never from the
     // batch, and the merge runs in split order; a query's arithmetic is then the
     // same in any batch.
-    if (fixed && A.heads % 32 == 0) {
+    if (A.kv_f8 || (fixed && A.heads % 32 == 0)) {   // (an FP8 cache implies both)
       L.kind = 4;
       L.n_hg = A.heads / 32;
       L.nw = kSdWaves;
@@ -1386,8 +1459,9 @@ static MqaLaunch plan_mqa(const MqaArgs& A) {
       // 128-head workgroups with row norms from the gathered tiles / from the pre-pass
       const bool hg = variant == 0;
       const bool pre = variant == 2;
-      if (hg && (A.heads % 32 != 0 || rows > 32)) continue;
-      if (!hg && A.heads % 128 != 0) continue;
+      // (an FP8 cache is read by the split-role kernel only)
+      if (hg && (A.heads % 32 != 0 || (rows > 32 && !A.kv_f8))) continue;
+      if (!hg && (A.heads % 128 != 0 || A.kv_f8)) continue;
       const int wg_heads = hg ? 32 : 128;
       const int n_hg = A.heads / wg_heads;
       // (the 8-wave kernel gathers only ~1.5 tiles ahead: on rows scattered over HBM,
@@ -1524,16 +1598,20 @@ hipError_t launch_mqa(const MqaArgs& A, void* ws, size_t ws_bytes, hipStream_t s
   }();
   if (attr != hipSuccess) return attr;
   if (lds > (size_t)kMaxDynLds) return hipErrorInvalidValue;
+  if (A.kv_f8 && L.kind != 4) return hipErrorInvalidValue;   // only that kernel reads FP8 rows
   const long groups = ((long)L.units + 7) / 8;
   dim3 grid((unsigned)(groups * 8 * L.n_hg));
   if (L.kind == 3) grid = dim3((unsigned)((((long)L.units * L.n_hg + 7) / 8) * 8));
   {
-    LaunchTimer timer(L.kind == 3 ? "mqa_bf16_w8" : (L.kind == 4 ? "mqa_bf16_sd" : "mqa_bf16_h16"), s);
+    LaunchTimer timer(L.kind == 3 ? "mqa_bf16_w8"
+                                  : (L.kind == 4 ? (A.kv_f8 ? "mqa_f8_sd" : "mqa_bf16_sd") : "mqa_bf16_h16"),
+                      s);
     if (L.kind == 3 && L.pre)
       mqa_w8_kernel<true><<<grid, kW8Waves * 64, lds, s>>>(A, L, part_o, part_ml, inv_kv, inv_raw);
     else if (L.kind == 3)
       mqa_w8_kernel<false><<<grid, kW8Waves * 64, lds, s>>>(A, L, part_o, part_ml, nullptr, nullptr);
-    else if (L.kind == 4) mqa_sd_kernel<<<grid, kSdWaves * 64, lds, s>>>(A, L, part_o, part_ml);
+    else if (L.kind == 4 && A.kv_f8) mqa_sd_kernel<true><<<grid, kSdWaves * 64, lds, s>>>(A, L, part_o, part_ml);
+    else if (L.kind == 4) mqa_sd_kernel<false><<<grid, kSdWaves * 64, lds, s>>>(A, L, part_o, part_ml);
     else if (L.nw == 4) mqa_bf16_kernel<4><<<grid, 4 * 64, lds, s>>>(A, L, part_o, part_ml);
     else if (L.nw == 2) mqa_bf16_kernel<2><<<grid, 2 * 64, lds, s>>>(A, L, part_o, part_ml);
     else mqa_bf16_kernel<1><<<grid, 64, lds, s>>>(A, L, part_o, part_ml);

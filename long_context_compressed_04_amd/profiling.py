@@ -33,13 +33,15 @@ KERNELS = {
     "index_scores_f32": (r"index_scores_f32", "indexer.hip"),
     "topk": (r"topk_", "topk.hip"),
     "mqa_bf16_w8": (r"mqa_w8_kernel", "mqa.hip"),
-    "mqa_bf16_sd": (r"mqa_sd_kernel", "mqa.hip"),
+    "mqa_bf16_sd": (r"mqa_sd_kernel<false>", "mqa.hip"),
+    "mqa_f8_sd": (r"mqa_sd_kernel<true>", "mqa.hip"),
     "mqa_bf16_h16": (r"mqa_bf16_kernel<", "mqa.hip"),
     "mqa_f32": (r"mqa_f32_kernel", "mqa.hip"),
     "mqa_combine": (r"mqa_combine_kernel", "mqa.hip"),
     "mqa_row_norms": (r"row_inv_rms_kernel", "mqa.hip"),
     "compress": (r"compress_kernel<", "compress.hip"),
     "mxfp4_quantize": (r"mxfp4_quantize_kernel", "compress.hip"),
+    "fp8_quantize": (r"fp8_quantize_kernel", "compress.hip"),
 }
 # the calibration copy (a torch elementwise negation of an fp32 buffer)
 CALIB_PATTERN = r"neg_kernel"

@@ -62,6 +62,10 @@ def _get():
         lib.oracle_mxfp4_quantize.restype = None
         lib.oracle_mxfp4_dequantize.argtypes = [_U8, _U8, L, _D]
         lib.oracle_mxfp4_dequantize.restype = None
+        lib.oracle_fp8_quantize.argtypes = [_D, L, _U8]
+        lib.oracle_fp8_quantize.restype = None
+        lib.oracle_fp8_dequantize.argtypes = [_U8, L, _D]
+        lib.oracle_fp8_dequantize.restype = None
         _lib = lib
     return _lib
 
@@ -217,3 +221,20 @@ def csa_decode_query(q, kv, n_entries, m, qI, w, kI, k, kv_raw, raw_base, t, win
     idx = topk(scores, V, k)
     out, lse = sparse_mqa(q, kv, idx, kv_raw, raw_base, t, window, scale, eps, gamma)
     return {"scores": scores, "idx": idx, "out": out, "lse": lse, "visible": V}
+
+
+def fp8_quantize(x):
+    """FP8 E4M3 codes (uint8, same shape) of x: clamp to +-448, nearest finite value,
+    ties to the even code, sign kept (OCP 8-bit floating point; techniques map,
+    "FP8 KV-cache quantization")."""
+    x = _f64(x)
+    codes = np.empty(x.shape, dtype=np.uint8)
+    _get().oracle_fp8_quantize(_p(x), x.size, _p(codes, _U8))
+    return codes
+
+
+def fp8_dequantize(codes):
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    x = np.empty(codes.shape, dtype=np.float64)
+    _get().oracle_fp8_dequantize(_p(codes, _U8), codes.size, _p(x))
+    return x

@@ -338,3 +338,35 @@ void oracle_mxfp4_dequantize(const uint8_t* codes, const uint8_t* scales, long n
     }
   }
 }
+
+/* ------------------------------------------------------------------------ */
+/* FP8 E4M3 (OCP 8-bit floating point, "E4M3FN"): sign, 4 exponent bits with
+ * bias 7, 3 mantissa bits; exponent field 0 is subnormal (m * 2^-9); the code
+ * S.1111.111 is NaN and there is no infinity, so the largest finite value is
+ * 1.75 * 2^8 = 448.  [Techniques, Inference quantization]: the compressed KV
+ * cache is kept in FP8.  Reading: per element, no scale; x is clamped to
+ * [-448, 448] and rounded to the nearest finite value, ties to the even code;
+ * the sign bit copies the sign of x (-0 kept).
+ * ------------------------------------------------------------------------ */
+static double e4m3_value(int mag) { /* mag = code & 0x7f, 0..126 */
+  int e = mag >> 3, m = mag & 7;
+  return (e == 0) ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
+}
+void oracle_fp8_quantize(const double* x, long n, uint8_t* codes) {
+  for (long i = 0; i < n; ++i) {
+    double a = fabs(x[i]);
+    if (a > 448.0) a = 448.0;
+    int best = 0; /* nearest of the 127 finite magnitudes; ties to the even code */
+    for (int mag = 1; mag < 127; ++mag) {
+      double d = fabs(e4m3_value(mag) - a), db = fabs(e4m3_value(best) - a);
+      if (d < db || (d == db && (mag & 1) == 0)) best = mag;
+    }
+    codes[i] = (uint8_t)(best | (signbit(x[i]) ? 0x80 : 0));
+  }
+}
+void oracle_fp8_dequantize(const uint8_t* codes, long n, double* x) {
+  for (long i = 0; i < n; ++i) {
+    double v = e4m3_value(codes[i] & 0x7f);
+    x[i] = (codes[i] & 0x80) ? -v : v;
+  }
+}

@@ -102,6 +102,12 @@ def test_mqa_validation():
     assert sp(D(split_items=48)) == 2                       # not a multiple of 32
     assert sp(D(split_items=4096)) == 2                     # more than 2048
     assert sp(D(topk=8192, split_items=32)) == 2            # more than 128 splits
+    assert sp(D(kv_dtype=2)) == 3                           # the cache is FP8 or q's dtype
+    assert sp(D(kv_dtype=3, heads=48)) == 6                 # FP8 cache: 32-head groups
+    assert sp(D(kv_dtype=3, dtype=0)) == 6                  # FP8 cache: bf16 queries
+    assert sp(D(kv_dtype=3, scale=0.2)) == 6                # FP8 cache: bounded logits
+    assert L.csa_sparse_mqa(ctypes.byref(D(kv_dtype=3)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None,
+                            FAKE, 1 << 30, None) == 6       # FP8 cache: no RMSNorm weight
 
 
 def test_decode_validation():
@@ -121,6 +127,10 @@ def test_quantize_validation():
     assert L.csa_mxfp4_quantize(1, FAKE_MISALIGNED, 4, FAKE, FAKE, None) == 4
     assert L.csa_mxfp4_quantize(2, FAKE, 4, FAKE, FAKE, None) == 3
     assert L.csa_mxfp4_quantize(0, FAKE, -1, FAKE, FAKE, None) == 2
+    assert L.csa_fp8_quantize(0, None, 8, FAKE, None) == 1
+    assert L.csa_fp8_quantize(3, FAKE, 8, FAKE, None) == 3
+    assert L.csa_fp8_quantize(0, FAKE, 12, FAKE, None) == 2            # not a multiple of 8
+    assert L.csa_fp8_quantize(1, FAKE, 8, FAKE + 4, None) == 4         # codes not 8-byte aligned
 
 
 def test_binding_refuses_host_tensors():

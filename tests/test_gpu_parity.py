@@ -77,6 +77,20 @@ def test_mxfp4_quantize_bit_exact(dtype):
     np.testing.assert_array_equal(codes.cpu().numpy(), oc)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fp8_quantize_bit_exact(dtype):
+    rng = np.random.default_rng(8)
+    x = (rng.standard_normal((61, 512)) * np.exp(rng.uniform(-9, 6, (61, 1)))).astype(np.float32)
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    grid = np.sort(np.unique(oracle.fp8_dequantize(codes)))
+    mids = ((grid[1:] + grid[:-1]) / 2).astype(np.float32)     # exact ties
+    x[0, :len(mids)] = mids[:512]
+    x[1, :8] = [460.0, 500.0, -1e6, 1e-30, -0.0, 448.0, 2.0 ** -10, 3 * 2.0 ** -10]
+    xs = W.store(x, dtype)
+    got = csa.fp8_quantize(dev(xs)).cpu().numpy()
+    np.testing.assert_array_equal(got, oracle.fp8_quantize(W.value(xs)))
+
+
 # ----------------------------------------------------------------- indexer
 def _index_case(dtype, B, n_q, HI, dI, N, cap, m, seed, t_list=None):
     rng = np.random.default_rng(seed)
@@ -415,6 +429,59 @@ def test_dense_mqa(dtype, B, n_q, H, d, N, m, window, t_off):
                 assert_f32_close(lse[b, i], wl, "dense lse")
             else:
                 assert_bf16_close(out[b, i], want, "dense out")
+                np.testing.assert_allclose(lse[b, i], wl, atol=2e-2)
+
+
+@pytest.mark.parametrize("dense,B,n_q,H,N,k,window,split_items,with_sink", [
+    (False, 2, 1, 128, 2000, 1024, 128, 0, False),     # many splits
+    (False, 1, 3, 64, 500, 100, 128, 0, True),         # two head groups, sink
+    (True, 2, 1, 128, 1500, 0, 128, 0, False),         # dense
+    (False, 1, 40, 32, 400, 64, 128, 0, False),        # many queries (one split each)
+    (False, 3, 2, 96, 1500, 700, 128, 256, False),     # batch-invariant splits
+    (False, 1, 1, 128, 300, 40, 0, 0, False),          # no window, two tiles
+    (False, 1, 1, 32, 100, 8, 0, 0, False),            # every slot invalid: empty set
+])
+def test_fp8_cache_mqa(dense, B, n_q, H, N, k, window, split_items, with_sink):
+    """kv and the window rows as FP8 E4M3 codes: the kernels read their exact values,
+    so the result is the oracle's attention over the dequantised rows."""
+    d, m = 512, 4
+    q, _, _, rng = _mqa_case("bf16", B, n_q, H, d, 1, 0, window, seed=71 + H + N)
+    raw_cap = window + n_q + 5
+    kv_c = oracle.fp8_quantize(rng.standard_normal((B, N, d)) * 1.5).reshape(B, N, d)
+    raw_c = oracle.fp8_quantize(rng.standard_normal((B, raw_cap, d)) * 1.5).reshape(B, raw_cap, d)
+    kv_v, raw_v = oracle.fp8_dequantize(kv_c), oracle.fp8_dequantize(raw_c)
+    sink = rng.normal(0.0, 2.0, H).astype(np.float32) if with_sink else None
+    kvt, rawt = torch.from_numpy(kv_c).cuda(), torch.from_numpy(raw_c).cuda()
+    sk = None if sink is None else dev(sink)
+    if dense:
+        n_entries = np.array([N - 3 * b for b in range(B)], dtype=np.int32)
+        q_pos = np.array([[m * N - 1 - 20 - i for i in range(n_q)] for b in range(B)], dtype=np.int32)
+        raw_base = np.array([max(0, q_pos[b].min() - window + 1) for b in range(B)], dtype=np.int32)
+        out, lse = csa.hca_dense_mqa(dev(q), kvt, _i32(n_entries), rawt, _i32(raw_base), _i32(q_pos), m=m,
+                                     window=window, sink=sk, split_items=split_items)
+    else:
+        idx = np.stack([np.stack([np.sort(rng.choice(N, size=k, replace=False)) for _ in range(n_q)])
+                        for _ in range(B)]).astype(np.int32)
+        idx[:, :, -3:] = -1
+        if k <= 8:
+            idx[:] = -1
+        raw_base = np.array([1000 + 10 * b for b in range(B)], dtype=np.int32)
+        q_pos = np.array([[raw_base[b] + window + 2 + i for i in range(n_q)] for b in range(B)], dtype=np.int32)
+        out, lse = csa.sparse_mqa(dev(q), kvt, _i32(idx), rawt, _i32(raw_base), _i32(q_pos), window=window,
+                                  sink=sk, split_items=split_items)
+    out, lse = host(out), host(lse)
+    for b in range(B):
+        for i in range(0, n_q, max(1, n_q // 4)):
+            if dense:
+                want, wl = oracle.dense_mqa(W.value(q[b, i]), kv_v[b], n_entries[b], m, raw_v[b], raw_base[b],
+                                            q_pos[b, i], window, 1 / np.sqrt(d), 1e-6, None, sink)
+            else:
+                want, wl = oracle.sparse_mqa(W.value(q[b, i]), kv_v[b], idx[b, i], raw_v[b], raw_base[b],
+                                             q_pos[b, i], window, 1 / np.sqrt(d), 1e-6, None, sink)
+            assert_bf16_close(out[b, i], want, "fp8-cache out")
+            if np.all(np.isneginf(wl)):
+                assert np.all(out[b, i] == 0) and np.all(np.isneginf(lse[b, i]))
+            else:
                 np.testing.assert_allclose(lse[b, i], wl, atol=2e-2)
 
 

@@ -397,3 +397,36 @@ def test_rescored_brute_force(V, cand, k):
     np.testing.assert_array_equal(got, want)
     np.testing.assert_array_equal(cands, sorted(first))
     np.testing.assert_allclose(s16, [score(q, K[i]) for i in sorted(first)], rtol=1e-12)
+
+
+# ------------------------------------------------------------------------- FP8
+def test_fp8_e4m3_hand_values():
+    """E4M3 (bias 7, 3 mantissa bits, no infinity, max 448): values worked by hand from
+    the format definition, including subnormals, both tie directions, saturation."""
+    cases = [(0.0, 0x00), (-0.0, 0x80), (2.0 ** -9, 0x01), (7 * 2.0 ** -9, 0x07), (2.0 ** -6, 0x08),
+             (1.0, 0x38), (1.125, 0x39), (1.875, 0x3F), (2.0, 0x40), (240.0, 0x77), (448.0, 0x7E),
+             (-3.0, 0xC4),                       # 1.5 * 2^1: e = 8, m = 4
+             (1.0625, 0x38),                     # tie between 1.0 (m 0) and 1.125 (m 1): even
+             (1.1875, 0x3A),                     # tie between 1.125 (m 1) and 1.25 (m 2): even
+             (2.0 ** -10, 0x00),                 # tie between 0 and the smallest subnormal
+             (3 * 2.0 ** -10, 0x02),             # tie between codes 1 and 2
+             (460.0, 0x7E), (1e6, 0x7E), (-1e6, 0xFE)]   # saturation
+    x = np.array([c[0] for c in cases])
+    np.testing.assert_array_equal(oracle.fp8_quantize(x), np.array([c[1] for c in cases], dtype=np.uint8))
+    np.testing.assert_array_equal(oracle.fp8_dequantize(np.array([0x01, 0x7E, 0xC4, 0x3A], dtype=np.uint8)),
+                                  [2.0 ** -9, 448.0, -3.0, 1.25])
+
+
+def test_fp8_round_trip_and_error_bound():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)   # every finite code
+    np.testing.assert_array_equal(oracle.fp8_quantize(oracle.fp8_dequantize(codes)), codes)
+    vals = np.sort(oracle.fp8_dequantize(codes[codes < 0x80]))
+    assert np.all(np.diff(vals) > 0) and vals[-1] == 448.0
+    rng = np.random.default_rng(22)
+    x = rng.standard_normal(20000) * np.exp(rng.uniform(-8, 5, 20000))
+    q = oracle.fp8_dequantize(oracle.fp8_quantize(x))
+    a = np.minimum(np.abs(x), 448.0)
+    # half a quantum: 2^(floor(log2 a) - 4) in the normal range, 2^-10 below 2^-6
+    half = np.where(a >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(a, 2.0 ** -6))) - 4), 2.0 ** -10)
+    assert np.all(np.abs(np.abs(q) - a) <= half * (1 + 1e-12))
+    assert np.all(np.sign(q[q != 0]) == np.sign(x[q != 0]))
