@@ -66,6 +66,8 @@ def _get():
         lib.oracle_fp8_quantize.restype = None
         lib.oracle_fp8_dequantize.argtypes = [_U8, L, _D]
         lib.oracle_fp8_dequantize.restype = None
+        lib.oracle_rope_conjugate.argtypes = [_D, I, I, _D]
+        lib.oracle_rope_conjugate.restype = None
         _lib = lib
     return _lib
 
@@ -238,3 +240,15 @@ def fp8_dequantize(codes):
     x = np.empty(codes.shape, dtype=np.float64)
     _get().oracle_fp8_dequantize(_p(codes, _U8), codes.size, _p(x))
     return x
+
+
+def rope_conjugate(out, cs):
+    """Rope-conjugate rotation of an attention output (techniques map, "Gated attention
+    output" and "Partial RoPE"): the trailing 64 dims of each head, rotated by the
+    query's cos and the negated sin.  out [H, d]; cs [128] = cos[64], sin[64].
+    Returns a new array."""
+    y = np.array(out, dtype=np.float64, order="C")
+    H, d = y.shape
+    c = _f64(cs).reshape(128)
+    _get().oracle_rope_conjugate(_p(y), H, d, _p(c))
+    return y

@@ -370,3 +370,27 @@ void oracle_fp8_dequantize(const uint8_t* codes, long n, double* x) {
     x[i] = (codes[i] & 0x80) ? -v : v;
   }
 }
+
+/* ------------------------------------------------------------------------ */
+/* Rope-conjugate rotation of the attention output ([P4] techniques map,
+ * "Gated attention output": the output passes through the conjugate of the
+ * rotary rotation before the output projection; "Partial RoPE": only the
+ * trailing 64 dims of each 512-dim head are rotated, by
+ * x*cos + rotate_half(x)*sin with rotate_half([a, b]) = [-b, a] over the two
+ * 32-dim halves).  The conjugate rotation uses the query's cos and sin with the
+ * sine negated.  cs [128] = cos[64] then sin[64]; out [H, d] is rotated in
+ * place over dims d-64 .. d-1 of every head.
+ * ------------------------------------------------------------------------ */
+void oracle_rope_conjugate(double* out, int H, int d, const double* cs) {
+  const double* c = cs;
+  const double* s = cs + 64;
+  double y[64];
+  for (int h = 0; h < H; ++h) {
+    double* x = out + (long)h * d + (d - 64);
+    for (int i = 0; i < 64; ++i) {
+      double rot_half = (i < 32) ? -x[i + 32] : x[i - 32];
+      y[i] = x[i] * c[i] - rot_half * s[i];
+    }
+    for (int i = 0; i < 64; ++i) x[i] = y[i];
+  }
+}

@@ -430,3 +430,60 @@ def test_fp8_round_trip_and_error_bound():
     half = np.where(a >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(a, 2.0 ** -6))) - 4), 2.0 ** -10)
     assert np.all(np.abs(np.abs(q) - a) <= half * (1 + 1e-12))
     assert np.all(np.sign(q[q != 0]) == np.sign(x[q != 0]))
+
+
+# --------------------------------------------------------- rope-conjugate output
+def _rope_cs(theta):
+    """cos and sin per rope dim: the 32 pair angles repeated over both halves."""
+    th = np.concatenate([theta, theta])
+    return np.concatenate([np.cos(th), np.sin(th)])
+
+
+def _rotate_complex(x, theta):
+    """RoPE of the trailing 64 dims written as complex multiplication: the pair
+    (x_i, x_{i+32}) is x_i + 1j x_{i+32}, multiplied by exp(1j theta_i)."""
+    y = np.array(x, dtype=np.float64)
+    z = (y[..., -64:-32] + 1j * y[..., -32:]) * np.exp(1j * theta)
+    y[..., -64:-32], y[..., -32:] = z.real, z.imag
+    return y
+
+
+def test_rope_conjugate_undoes_the_rotation():
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((3, 512))
+    theta = rng.uniform(-40, 40, 32)
+    y = oracle.rope_conjugate(_rotate_complex(x, theta), _rope_cs(theta))
+    np.testing.assert_allclose(y, x, atol=1e-12)
+    # it is the rotation by -theta, and the 448 leading dims pass through unchanged
+    np.testing.assert_allclose(oracle.rope_conjugate(x, _rope_cs(theta)), _rotate_complex(x, -theta), atol=1e-12)
+    np.testing.assert_array_equal(oracle.rope_conjugate(x, _rope_cs(theta))[:, :448], x[:, :448])
+
+
+def test_rope_conjugate_quarter_turn_by_hand():
+    """theta = pi/2 (cos 0, sin 1): (a, b) pairs map to (b, -a)."""
+    x = np.arange(2 * 96, dtype=np.float64).reshape(2, 96) + 1
+    cs = np.concatenate([np.zeros(64), np.ones(64)])
+    y = oracle.rope_conjugate(x, cs)
+    np.testing.assert_array_equal(y[:, :32], x[:, :32])
+    np.testing.assert_array_equal(y[:, 32:64], x[:, 64:96])
+    np.testing.assert_array_equal(y[:, 64:96], -x[:, 32:64])
+
+
+def test_rope_conjugate_of_attention_over_rotated_inputs():
+    """q and every attended row rotated by one common angle (one position): the logits and
+    the RMS norms do not change, so the conjugated output is the attention output over
+    the unrotated inputs."""
+    rng = np.random.default_rng(42)
+    H, d, N, k, window = 4, 128, 40, 12, 6
+    q = rng.standard_normal((H, d))
+    kv = rng.standard_normal((N, d))
+    raw = rng.standard_normal((window + 2, d))
+    idx = np.sort(rng.choice(N, size=k, replace=False)).astype(np.int32)
+    theta = rng.uniform(-3, 3, 32)
+    base, t = 100, 100 + window
+    o0, l0 = oracle.sparse_mqa(q, kv, idx, raw, base, t, window, 1 / np.sqrt(d), 1e-6)
+    o1, l1 = oracle.sparse_mqa(_rotate_complex(q, theta), _rotate_complex(kv, theta), idx,
+                               _rotate_complex(raw, theta), base, t, window, 1 / np.sqrt(d), 1e-6)
+    np.testing.assert_allclose(l1, l0, atol=1e-12)
+    assert np.abs(o1 - o0).max() > 1e-3                     # the rotation is visible in the output
+    np.testing.assert_allclose(oracle.rope_conjugate(o1, _rope_cs(theta)), o0, atol=1e-12)
