@@ -241,6 +241,13 @@ csa_status csa_index_topk_rescored(const csa_index_desc* desc, int32_t cand, con
  * NULL for none.  With a sink s_h the softmax runs over the set plus one extra logit
  * s_h whose value vector is zero, so out = sum exp(l_j) k_hat_j / (sum exp(l_j) +
  * exp(s_h)) and lse includes exp(s_h).  |s_h| <= 80.
+ * Rope-conjugate output ("DeepSeek-V4-Pro" techniques map, "Gated attention output" and
+ * "Partial RoPE": the output is rotated back before the output projection; RoPE
+ * covers the trailing 64 dims of a head, x*cos + rotate_half(x)*sin with
+ * rotate_half([a, b]) = [-b, a] over the two 32-dim halves): rope [batch, n_q, 128]
+ * fp32 = the query's cos[64] then sin[64], or NULL for none.  With rope, dims
+ * head_dim-64 .. head_dim-1 of every output head become x*cos - rotate_half(x)*sin
+ * (head_dim >= 64); lse is unchanged.
  *
  *   q      [batch, n_q, heads, head_dim] dtype
  *   kv     [batch, kv_cap, head_dim]     dtype (compressed entries)
@@ -291,12 +298,14 @@ size_t csa_mqa_workspace_size(const csa_mqa_desc* desc, int32_t dense);
 csa_status csa_sparse_mqa(const csa_mqa_desc* desc, const void* q, const void* kv,
                           const int32_t* idx, const void* kv_raw, const int32_t* raw_base,
                           const int32_t* q_pos, const float* rms_weight, const float* sink,
-                          void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+                          const float* rope, void* out, float* lse, void* ws, size_t ws_bytes,
+                          void* stream);
 
 csa_status hca_dense_mqa(const csa_mqa_desc* desc, const void* q, const void* kv,
                          const int32_t* n_entries, const void* kv_raw, const int32_t* raw_base,
                          const int32_t* q_pos, const float* rms_weight, const float* sink,
-                         void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+                         const float* rope, void* out, float* lse, void* ws, size_t ws_bytes,
+                         void* stream);
 
 /* ------------------------------------------------------------------------------
  * csa_decode -- one fused CSA step for n_q queries per sequence, stream-ordered:
@@ -328,6 +337,7 @@ typedef struct {
   const int32_t* q_pos;
   const float* rms_weight;
   const float* sink;                /* nullable: per-head sink logits (as csa_sparse_mqa) */
+  const float* rope;                /* nullable: cos/sin of the query positions (as csa_sparse_mqa) */
   const void* q_idx;
   const uint8_t* q_idx_scale;
   const float* w;

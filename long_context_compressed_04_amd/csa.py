@@ -54,7 +54,7 @@ class CompressJob(ctypes.Structure):
 class DecodeArgs(ctypes.Structure):
     _fields_ = [("index", IndexDesc), ("attn", MqaDesc), ("kv_job", ctypes.POINTER(CompressJob)),
                 ("key_job", ctypes.POINTER(CompressJob))] + [(n, _P) for n in (
-                    "q", "kv", "kv_raw", "raw_base", "q_pos", "rms_weight", "sink", "q_idx", "q_idx_scale", "w", "k_idx",
+                    "q", "kv", "kv_raw", "raw_base", "q_pos", "rms_weight", "sink", "rope", "q_idx", "q_idx_scale", "w", "k_idx",
                     "k_idx_scale", "n_entries", "out_idx", "out_score", "out", "lse")]
 
 
@@ -93,9 +93,9 @@ def lib():
         L.csa_index_topk_rescored.restype = S
         L.csa_mqa_workspace_size.argtypes = [ctypes.POINTER(MqaDesc), ctypes.c_int32]
         L.csa_mqa_workspace_size.restype = Z
-        L.csa_sparse_mqa.argtypes = [ctypes.POINTER(MqaDesc)] + [V] * 10 + [V, Z, V]
+        L.csa_sparse_mqa.argtypes = [ctypes.POINTER(MqaDesc)] + [V] * 11 + [V, Z, V]
         L.csa_sparse_mqa.restype = S
-        L.hca_dense_mqa.argtypes = [ctypes.POINTER(MqaDesc)] + [V] * 10 + [V, Z, V]
+        L.hca_dense_mqa.argtypes = [ctypes.POINTER(MqaDesc)] + [V] * 11 + [V, Z, V]
         L.hca_dense_mqa.restype = S
         L.csa_decode_workspace_size.argtypes = [ctypes.POINTER(DecodeArgs)]
         L.csa_decode_workspace_size.restype = Z
@@ -258,33 +258,34 @@ def _mqa_desc(q, kv, kv_raw, *, topk=0, m=1, n_max=0, window=128, scale=0.0, eps
 
 
 def sparse_mqa(q, kv, idx, kv_raw, raw_base, q_pos, *, window, scale=0.0, eps=1e-6, rms_weight=None, sink=None,
-               split_items=0, workspace=None, out=None, lse=None):
+               rope=None, split_items=0, workspace=None, out=None, lse=None):
     """CSA attention over idx (-1 skipped) plus the sliding window.  Returns (out, lse).
     sink: per-head sink logits [heads] fp32 or None; split_items > 0 selects
     batch-invariant splitting (see csa_mqa_desc).  kv and kv_raw as uint8: FP8 E4M3
-    rows (bf16 q, no rms_weight)."""
+    rows (bf16 q, no rms_weight).  rope: [B, n_q, 128] fp32 cos and sin of each query
+    (rope-conjugate rotation of the output's trailing 64 dims), or None."""
     d = _mqa_desc(q, kv, kv_raw, topk=idx.shape[-1], window=window, scale=scale, eps=eps, split_items=split_items)
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if lse is None else lse
     ws, nb = _workspace(lib().csa_mqa_workspace_size(ctypes.byref(d), 0), q.device, workspace)
     _check(lib().csa_sparse_mqa(ctypes.byref(d), _p(q), _p(kv), _p(idx), _p(kv_raw), _p(raw_base), _p(q_pos),
-                                _p(rms_weight), _p(sink), _p(out), _p(lse), _p(ws), nb, _stream(q)))
+                                _p(rms_weight), _p(sink), _p(rope), _p(out), _p(lse), _p(ws), nb, _stream(q)))
     return out, lse
 
 
 def hca_dense_mqa(q, kv, n_entries, kv_raw, raw_base, q_pos, *, m, window, n_max=None, scale=0.0, eps=1e-6,
-                  rms_weight=None, sink=None, split_items=0, workspace=None, out=None, lse=None):
+                  rms_weight=None, sink=None, rope=None, split_items=0, workspace=None, out=None, lse=None):
     """HCA attention over every visible compressed entry plus the window.  Returns (out, lse).
     sink: per-head sink logits [heads] fp32 or None; split_items > 0 selects
     batch-invariant splitting (see csa_mqa_desc).  kv and kv_raw as uint8: FP8 E4M3
-    rows (bf16 q, no rms_weight)."""
+    rows (bf16 q, no rms_weight).  rope: as sparse_mqa."""
     d = _mqa_desc(q, kv, kv_raw, m=m, n_max=kv.shape[1] if n_max is None else n_max, window=window, scale=scale,
                   eps=eps, split_items=split_items)
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if lse is None else lse
     ws, nb = _workspace(lib().csa_mqa_workspace_size(ctypes.byref(d), 1), q.device, workspace)
     _check(lib().hca_dense_mqa(ctypes.byref(d), _p(q), _p(kv), _p(n_entries), _p(kv_raw), _p(raw_base), _p(q_pos),
-                               _p(rms_weight), _p(sink), _p(out), _p(lse), _p(ws), nb, _stream(q)))
+                               _p(rms_weight), _p(sink), _p(rope), _p(out), _p(lse), _p(ws), nb, _stream(q)))
     return out, lse
 
 
@@ -294,9 +295,9 @@ class Decoder:
 
     def __init__(self, q, kv, kv_raw, raw_base, q_pos, q_idx, w, k_idx, n_entries, *, m, topk, window,
                  n_max=None, q_scale=None, k_scale=None, scale=0.0, eps=1e-6, rms_weight=None, sink=None,
-                 split_items=0, out=None, out_idx=None, out_score=None, lse=None):
+                 rope=None, split_items=0, out=None, out_idx=None, out_score=None, lse=None):
         self.tensors = [q, kv, kv_raw, raw_base, q_pos, q_idx, w, k_idx, n_entries, q_scale, k_scale, rms_weight,
-                        sink]
+                        sink, rope]
         a = DecodeArgs()
         a.index = _index_desc(q_idx, k_idx, m, topk, n_max, *_index_dtype(q_idx, k_idx))
         a.attn = _mqa_desc(q, kv, kv_raw, topk=topk, window=window, scale=scale, eps=eps, split_items=split_items)
@@ -307,7 +308,7 @@ class Decoder:
         self.out_score = out_score
         self.lse = lse
         for name, t in (("q", q), ("kv", kv), ("kv_raw", kv_raw), ("raw_base", raw_base), ("q_pos", q_pos),
-                        ("rms_weight", rms_weight), ("sink", sink), ("q_idx", q_idx), ("q_idx_scale", q_scale),
+                        ("rms_weight", rms_weight), ("sink", sink), ("rope", rope), ("q_idx", q_idx), ("q_idx_scale", q_scale),
                         ("w", w),
                         ("k_idx", k_idx), ("k_idx_scale", k_scale), ("n_entries", n_entries),
                         ("out_idx", self.out_idx), ("out_score", out_score), ("out", self.out), ("lse", lse)):

@@ -319,33 +319,39 @@ size_t csa_mqa_workspace_size(const csa_mqa_desc* d, int32_t dense) {
 
 static csa_status run_mqa(const char* fn, const csa_mqa_desc* d, int dense, const void* q, const void* kv,
                           const int32_t* idx, const int32_t* ne, const void* kv_raw, const int32_t* raw_base,
-                          const int32_t* qpos, const float* g, const float* sink, void* out, float* lse, void* ws,
+                          const int32_t* qpos, const float* g, const float* sink, const float* rope, void* out,
+                          float* lse, void* ws,
                           size_t ws_bytes, hipStream_t s) {
   csa::MqaArgs A = mqa_args(d, dense);
   const size_t need = round256(csa::mqa_workspace_bytes(A));
   if (need && (!ws || ws_bytes < need))
     return fail(CSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws ? ws_bytes : 0);
   A.q = q; A.kv = kv; A.idx = idx; A.n_entries = ne; A.kv_raw = kv_raw; A.raw_base = raw_base; A.q_pos = qpos;
-  A.gamma = g; A.sink = sink; A.out = out; A.lse = lse;
+  A.gamma = g; A.sink = sink; A.rope = rope; A.out = out; A.lse = lse;
+  if (rope && d->head_dim < 64) return fail(CSA_ERR_SHAPE, "%s: rope needs head_dim >= 64", fn);
   if (A.kv_f8 && g) return fail(CSA_ERR_UNSUPPORTED, "%s: an FP8 cache needs rms_weight NULL", fn);
   return hip_status(csa::launch_mqa(A, ws, ws_bytes, s), fn);
 }
 
 csa_status csa_sparse_mqa(const csa_mqa_desc* d, const void* q, const void* kv, const int32_t* idx, const void* kv_raw,
-                          const int32_t* raw_base, const int32_t* qpos, const float* g, const float* sink, void* out,
+                          const int32_t* raw_base, const int32_t* qpos, const float* g, const float* sink,
+                          const float* rope, void* out,
                           float* lse, void* ws, size_t ws_bytes, void* stream) {
   csa_status st = check_mqa("csa_sparse_mqa", d, 0, q, kv, idx, kv_raw, raw_base, qpos, out);
   if (st != CSA_OK) return st;
-  return run_mqa("csa_sparse_mqa", d, 0, q, kv, idx, nullptr, kv_raw, raw_base, qpos, g, sink, out, lse, ws, ws_bytes,
+  return run_mqa("csa_sparse_mqa", d, 0, q, kv, idx, nullptr, kv_raw, raw_base, qpos, g, sink, rope, out, lse, ws,
+                 ws_bytes,
                  (hipStream_t)stream);
 }
 
 csa_status hca_dense_mqa(const csa_mqa_desc* d, const void* q, const void* kv, const int32_t* ne, const void* kv_raw,
-                         const int32_t* raw_base, const int32_t* qpos, const float* g, const float* sink, void* out,
+                         const int32_t* raw_base, const int32_t* qpos, const float* g, const float* sink,
+                         const float* rope, void* out,
                          float* lse, void* ws, size_t ws_bytes, void* stream) {
   csa_status st = check_mqa("hca_dense_mqa", d, 1, q, kv, ne, kv_raw, raw_base, qpos, out);
   if (st != CSA_OK) return st;
-  return run_mqa("hca_dense_mqa", d, 1, q, kv, nullptr, ne, kv_raw, raw_base, qpos, g, sink, out, lse, ws, ws_bytes,
+  return run_mqa("hca_dense_mqa", d, 1, q, kv, nullptr, ne, kv_raw, raw_base, qpos, g, sink, rope, out, lse, ws,
+                 ws_bytes,
                  (hipStream_t)stream);
 }
 
@@ -394,7 +400,7 @@ csa_status csa_decode(const csa_decode_args* a, void* ws, size_t ws_bytes, void*
                       a->out_idx, a->out_score, ws, iws, stream);
   if (st != CSA_OK) return st;
   return run_mqa("csa_decode", &a->attn, 0, a->q, a->kv, a->out_idx, nullptr, a->kv_raw, a->raw_base, a->q_pos,
-                 a->rms_weight, a->sink, a->out, a->lse, (uint8_t*)ws + iws, ws_bytes - iws, s);
+                 a->rms_weight, a->sink, a->rope, a->out, a->lse, (uint8_t*)ws + iws, ws_bytes - iws, s);
 }
 
 }  // extern "C"

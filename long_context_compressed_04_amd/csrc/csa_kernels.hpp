@@ -50,6 +50,7 @@ struct MqaArgs {
   int split_items = 0;   // > 0: batch-invariant split boundaries (multiples of it)
   int kv_f8 = 0;         // kv and kv_raw hold FP8 E4M3 rows (bf16 path, 32-head groups)
   const float* sink = nullptr;   // [heads] sink logits (natural log), or none
+  const float* rope = nullptr;   // [rows, 128] cos[64], sin[64] of each query: rope-conjugate output
 };
 // Workspace bytes the MQA path needs for these sizes (split partials).
 size_t mqa_workspace_bytes(const MqaArgs& A);

@@ -101,6 +101,14 @@ __device__ __forceinline__ SoftmaxEnd softmax_end(float m2, float l, const float
   return {scale / den, M * kLn2 + logf(den)};
 }
 
+// Rope-conjugate rotation of dim i (0..63) of a head's rotated slice (the trailing 64
+// dims), from its value x and the value xp of its partner dim (i + 32 or i - 32):
+// x cos_i - rotate_half(x)_i sin_i, with rotate_half(x)_i = -x_{i+32} (i < 32) or
+// x_{i-32} (i >= 32).  cs = cos[64] then sin[64] of the query.
+__device__ __forceinline__ float rope_conj(float x, float xp, int i, const float* cs) {
+  return fmaf(x, cs[i], (i < 32 ? xp : -xp) * cs[64 + i]);
+}
+
 // ---------------------------------------------------------------- fp32 (VALU)
 // One workgroup (4 waves) per (sequence, query, head).  Each wave walks every 4th
 // item with the head dimension spread over its lanes; online softmax per wave, then
@@ -178,10 +186,17 @@ __global__ __launch_bounds__(kF32Waves * 64) void mqa_f32_kernel(MqaArgs A) {
   }
   const SoftmaxEnd fin = softmax_end(M * kLog2e, L, A.sink, h);   // (M is in natural-log units)
   float* orow = (float*)A.out + (row * A.heads + h) * D;
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+  auto val = [&](int d) {
     float o = 0.f;
     for (int w = 0; w < kF32Waves; ++w) o += so[w][d] * fw[w];
-    orow[d] = o * fin.mul * (A.gamma ? A.gamma[d] : 1.f);
+    return o * fin.mul * (A.gamma ? A.gamma[d] : 1.f);
+  };
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    const int i = d - (D - 64);   // position in the rotated slice
+    if (A.rope && i >= 0)
+      orow[d] = rope_conj(val(d), val(i < 32 ? d + 32 : d - 32), i, A.rope + row * 128);
+    else
+      orow[d] = val(d);
   }
   if (A.lse && threadIdx.x == 0) A.lse[row * A.heads + h] = fin.lse;
 }
@@ -508,6 +523,12 @@ __global__ __launch_bounds__(NW * 64) void mqa_bf16_kernel(MqaArgs A, MqaLaunch 
       float v[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) v[r] = o[db][r] * inv_l * gam[d0 + r];
+      if (db >= 28 && A.rope) {   // dims 448 ..: the partner of dim d is d +- 32, block db ^ 2
+        const int dp = 16 * (db ^ 2) + 4 * g;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          v[r] = rope_conj(v[r], o[db ^ 2][r] * inv_l * gam[dp + r], d0 + r - (kD - 64), A.rope + row * 128);
+      }
       *(uint2*)(orow + d0) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
     }
     if (A.lse && g == 0) A.lse[row * A.heads + head] = fin.lse;
@@ -930,12 +951,18 @@ void mqa_sd_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml) {
           f32x4_t{o[db][4 * j], o[db][4 * j + 1], o[db][4 * j + 2], o[db][4 * j + 3]};
   __builtin_amdgcn_s_waitcnt(0xC07F);   // this wave's LDS writes are done (wave-private region)
   const int hl = lane >> 5, d4 = lane & 31;
+  const bool rot = A.rope && pw == 3 && d4 >= 16;   // this lane's dims are in the rotated slice
   if (L.nsplit == 1) {
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const int hh = 2 * k + hl;
       const float il = softmax_end(0.f, lsum[0][hh] + lsum[1][hh], A.sink, hg * 32 + hh).mul;
-      const f32x4_t v = *(const f32x4_t*)(stage + hh * kStageRow + 4 * d4);
+      f32x4_t v = *(const f32x4_t*)(stage + hh * kStageRow + 4 * d4);
+      if (rot) {   // dims 448 ..: the partner of dim d (d +- 32) is 8 lanes away in the stage
+        const f32x4_t vp = *(const f32x4_t*)(stage + hh * kStageRow + 4 * (d4 ^ 8));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = rope_conj(v[r], vp[r], 4 * (d4 - 16) + r, A.rope + row * 128);
+      }
       uint16_t* orow = (uint16_t*)A.out + (row * A.heads + hg * 32 + hh) * kD + 128 * pw + 4 * d4;
       *(uint2*)orow = make_uint2(pack_bf16x2(v[0] * il, v[1] * il), pack_bf16x2(v[2] * il, v[3] * il));
     }
@@ -1322,12 +1349,18 @@ void mqa_w8_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml, const 
       __builtin_amdgcn_s_waitcnt(0xC07F);
       const int dim0 = 128 * dq + 64 * half + 4 * (lane & 15);
       const int head0 = hg * 128 + 64 * hp + 32 * j;
+      const bool rot = A.rope && dq == 3 && half == 1;
       if (L.nsplit == 1) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           const int hh = 4 * k + (lane >> 4);
           const float il = __shfl(inv_l[j], hh, 64);
-          const f32x4_t v = *(const f32x4_t*)(stage + hh * kW8Stage + 4 * (lane & 15));
+          f32x4_t v = *(const f32x4_t*)(stage + hh * kW8Stage + 4 * (lane & 15));
+          if (rot) {   // the chunk is the rotated slice; the partner of dim d (d +- 32) is 8 lanes away
+            const f32x4_t vp = *(const f32x4_t*)(stage + hh * kW8Stage + 4 * ((lane & 15) ^ 8));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = rope_conj(v[r], vp[r], 4 * (lane & 15) + r, A.rope + row * 128);
+          }
           uint16_t* orow = (uint16_t*)A.out + (row * A.heads + head0 + hh) * kD + dim0;
           *(uint2*)orow = make_uint2(pack_bf16x2(v[0] * il, v[1] * il), pack_bf16x2(v[2] * il, v[3] * il));
         }
@@ -1412,6 +1445,14 @@ __global__ __launch_bounds__(128) void mqa_combine_kernel(MqaArgs A, MqaLaunch L
   float v[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) v[r] = acc[r] * inv_l * (A.gamma ? A.gamma[d0 + r] : 1.f);
+  if (A.rope) {   // dims 448 ..: the partner of dim d (d +- 32) is 8 threads away
+    float vp[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) vp[r] = __shfl_xor(v[r], 8, 64);
+    if (d0 >= kD - 64)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = rope_conj(v[r], vp[r], d0 + r - (kD - 64), A.rope + row * 128);
+  }
   uint16_t* orow = (uint16_t*)A.out + (row * A.heads + head) * kD;
   *(uint2*)(orow + d0) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
   if (A.lse && threadIdx.x == 0) A.lse[row * A.heads + head] = fin.lse;

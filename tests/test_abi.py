@@ -84,10 +84,10 @@ def test_mqa_validation():
     ok = dict(batch=1, n_q=1, heads=128, head_dim=512, topk=64, m=4, n_max=0, window=128, kv_cap=1024,
               raw_cap=128, scale=0.0, eps=1e-6, dtype=1)
     D = lambda **kw: csa.MqaDesc(**{**ok, **kw})
-    sp = lambda d, q=FAKE, out=FAKE: L.csa_sparse_mqa(ctypes.byref(d), q, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
-                                                      out, None, FAKE, 1 << 30, None)
-    de = lambda d: L.hca_dense_mqa(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None, FAKE,
-                                   1 << 30, None)
+    sp = lambda d, q=FAKE, out=FAKE, rope=None: L.csa_sparse_mqa(ctypes.byref(d), q, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                                                 None, None, rope, out, None, FAKE, 1 << 30, None)
+    de = lambda d: L.hca_dense_mqa(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, None,
+                                   FAKE, 1 << 30, None)
     assert sp(D(), q=None) == 1
     assert sp(D(head_dim=256)) == 6
     assert sp(D(heads=40)) == 6
@@ -106,8 +106,9 @@ def test_mqa_validation():
     assert sp(D(kv_dtype=3, heads=48)) == 6                 # FP8 cache: 32-head groups
     assert sp(D(kv_dtype=3, dtype=0)) == 6                  # FP8 cache: bf16 queries
     assert sp(D(kv_dtype=3, scale=0.2)) == 6                # FP8 cache: bounded logits
-    assert L.csa_sparse_mqa(ctypes.byref(D(kv_dtype=3)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None,
-                            FAKE, 1 << 30, None) == 6       # FP8 cache: no RMSNorm weight
+    assert L.csa_sparse_mqa(ctypes.byref(D(kv_dtype=3)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE,
+                            None, FAKE, 1 << 30, None) == 6   # FP8 cache: no RMSNorm weight
+    assert sp(D(dtype=0, head_dim=32), rope=FAKE) == 2      # the rotated slice is 64 dims
 
 
 def test_decode_validation():

@@ -485,6 +485,63 @@ def test_fp8_cache_mqa(dense, B, n_q, H, N, k, window, split_items, with_sink):
                 np.testing.assert_allclose(lse[b, i], wl, atol=2e-2)
 
 
+@pytest.mark.parametrize("dtype,dense,B,n_q,H,d,N,k,with_gamma,fp8,split_items", [
+    ("f32", False, 1, 2, 8, 64, 300, 64, False, False, 0),          # fp32 kernel
+    ("bf16", False, 2, 1, 128, 512, 2000, 1024, False, False, 0),   # split-role kernel, merged splits
+    ("bf16", False, 1, 4, 128, 512, 400, 256, False, False, 1024),  # split-role kernel, one split
+    ("bf16", False, 1, 3, 64, 512, 900, 256, True, False, 0),       # 16-head waves (gamma), merged
+    ("bf16", False, 1, 256, 16, 512, 300, 64, True, False, 0),      # 16-head waves, one split
+    ("bf16", True, 1, 40, 128, 512, 600, 0, False, False, 0),       # 128-head workgroups, merged
+    ("bf16", True, 1, 300, 128, 512, 200, 0, False, False, 0),      # 128-head workgroups, one split
+    ("bf16", True, 2, 1, 128, 512, 1500, 0, False, True, 0),        # FP8 cache, dense
+])
+def test_mqa_rope_conjugate_output(dtype, dense, B, n_q, H, d, N, k, with_gamma, fp8, split_items):
+    """The trailing 64 dims of every output head rotated back with each query's cos and
+    sin, against the oracle's rotation of its attention output."""
+    window, m = 128, 4
+    q, kv, kv_raw, rng = _mqa_case(dtype, B, n_q, H, d, N, k, window, seed=57 + H + N)
+    kv_v, raw_v = W.value(kv), W.value(kv_raw)
+    kvt, rawt = dev(kv), dev(kv_raw)
+    if fp8:
+        kc, rc = oracle.fp8_quantize(kv_v), oracle.fp8_quantize(raw_v)
+        kv_v, raw_v = oracle.fp8_dequantize(kc), oracle.fp8_dequantize(rc)
+        kvt, rawt = torch.from_numpy(kc).cuda(), torch.from_numpy(rc).cuda()
+    # independent cos and sin values per dim, so that a dim mixed up with another shows
+    cs = rng.uniform(-1, 1, (B, n_q, 128)).astype(np.float32)
+    gamma = (0.5 + rng.random(d)).astype(np.float32) if with_gamma else None
+    g = None if gamma is None else dev(gamma)
+    if dense:
+        n_entries = np.array([N - 3 * b for b in range(B)], dtype=np.int32)
+        q_pos = np.array([[m * N - 1 - 20 - i for i in range(n_q)] for b in range(B)], dtype=np.int32)
+        raw_base = np.array([max(0, q_pos[b].min() - window + 1) for b in range(B)], dtype=np.int32)
+        out, lse = csa.hca_dense_mqa(dev(q), kvt, _i32(n_entries), rawt, _i32(raw_base), _i32(q_pos), m=m,
+                                     window=window, rms_weight=g, rope=dev(cs), split_items=split_items)
+    else:
+        idx = np.stack([np.stack([np.sort(rng.choice(N, size=k, replace=False)) for _ in range(n_q)])
+                        for _ in range(B)]).astype(np.int32)
+        idx[:, :, -3:] = -1
+        raw_base = np.array([1000 + 10 * b for b in range(B)], dtype=np.int32)
+        q_pos = np.array([[raw_base[b] + window + 2 + i for i in range(n_q)] for b in range(B)], dtype=np.int32)
+        out, lse = csa.sparse_mqa(dev(q), kvt, _i32(idx), rawt, _i32(raw_base), _i32(q_pos), window=window,
+                                  rms_weight=g, rope=dev(cs), split_items=split_items)
+    out, lse = host(out), host(lse)
+    for b in range(B):
+        for i in range(0, n_q, max(1, n_q // 4)):
+            if dense:
+                want, wl = oracle.dense_mqa(W.value(q[b, i]), kv_v[b], n_entries[b], m, raw_v[b], raw_base[b],
+                                            q_pos[b, i], window, 1 / np.sqrt(d), 1e-6, gamma)
+            else:
+                want, wl = oracle.sparse_mqa(W.value(q[b, i]), kv_v[b], idx[b, i], raw_v[b], raw_base[b],
+                                             q_pos[b, i], window, 1 / np.sqrt(d), 1e-6, gamma)
+            want = oracle.rope_conjugate(want, cs[b, i])
+            if dtype == "f32":
+                assert_f32_close(out[b, i], want, "rope out")
+                assert_f32_close(lse[b, i], wl, "rope lse")
+            else:
+                assert_bf16_close(out[b, i], want, "rope out")
+                np.testing.assert_allclose(lse[b, i], wl, atol=2e-2)
+
+
 def test_sparse_topk_covering_everything_equals_dense():
     """k >= N: CSA over all entries equals HCA on the same cache (GPU vs GPU and oracle)."""
     B, H, d, N, m, window = 1, 64, 512, 200, 4, 128
