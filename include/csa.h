@@ -60,7 +60,7 @@ typedef enum {
   CSA_ERR_DTYPE = 3,       /* unsupported dtype or dtype combination */
   CSA_ERR_ALIGN = 4,       /* a pointer is not aligned as the kernel requires */
   CSA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than *_workspace_size */
-  CSA_ERR_UNSUPPORTED = 6, /* valid request this build does not implement */
+  CSA_ERR_UNSUPPORTED = 6, /* valid request the library does not implement */
   CSA_ERR_HIP = 7          /* the HIP runtime reported an error */
 } csa_status;
 
