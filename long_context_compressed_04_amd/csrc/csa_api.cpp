@@ -320,8 +320,7 @@ size_t csa_mqa_workspace_size(const csa_mqa_desc* d, int32_t dense) {
 static csa_status run_mqa(const char* fn, const csa_mqa_desc* d, int dense, const void* q, const void* kv,
                           const int32_t* idx, const int32_t* ne, const void* kv_raw, const int32_t* raw_base,
                           const int32_t* qpos, const float* g, const float* sink, const float* rope, void* out,
-                          float* lse, void* ws,
-                          size_t ws_bytes, hipStream_t s) {
+                          float* lse, void* ws, size_t ws_bytes, hipStream_t s) {
   csa::MqaArgs A = mqa_args(d, dense);
   const size_t need = round256(csa::mqa_workspace_bytes(A));
   if (need && (!ws || ws_bytes < need))
@@ -335,24 +334,20 @@ static csa_status run_mqa(const char* fn, const csa_mqa_desc* d, int dense, cons
 
 csa_status csa_sparse_mqa(const csa_mqa_desc* d, const void* q, const void* kv, const int32_t* idx, const void* kv_raw,
                           const int32_t* raw_base, const int32_t* qpos, const float* g, const float* sink,
-                          const float* rope, void* out,
-                          float* lse, void* ws, size_t ws_bytes, void* stream) {
+                          const float* rope, void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
   csa_status st = check_mqa("csa_sparse_mqa", d, 0, q, kv, idx, kv_raw, raw_base, qpos, out);
   if (st != CSA_OK) return st;
   return run_mqa("csa_sparse_mqa", d, 0, q, kv, idx, nullptr, kv_raw, raw_base, qpos, g, sink, rope, out, lse, ws,
-                 ws_bytes,
-                 (hipStream_t)stream);
+                 ws_bytes, (hipStream_t)stream);
 }
 
 csa_status hca_dense_mqa(const csa_mqa_desc* d, const void* q, const void* kv, const int32_t* ne, const void* kv_raw,
                          const int32_t* raw_base, const int32_t* qpos, const float* g, const float* sink,
-                         const float* rope, void* out,
-                         float* lse, void* ws, size_t ws_bytes, void* stream) {
+                         const float* rope, void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
   csa_status st = check_mqa("hca_dense_mqa", d, 1, q, kv, ne, kv_raw, raw_base, qpos, out);
   if (st != CSA_OK) return st;
   return run_mqa("hca_dense_mqa", d, 1, q, kv, nullptr, ne, kv_raw, raw_base, qpos, g, sink, rope, out, lse, ws,
-                 ws_bytes,
-                 (hipStream_t)stream);
+                 ws_bytes, (hipStream_t)stream);
 }
 
 static csa_status check_decode(const csa_decode_args* a) {
