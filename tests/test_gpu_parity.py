@@ -594,6 +594,40 @@ def test_decode_bf16_small(B, T, k):
         assert_bf16_close(out[b], want, "decode out")
 
 
+@pytest.mark.parametrize("B,T,k,idx_dtype", [(2, 12000, 256, "bf16"), (2, 80000, 1024, "bf16"),
+                                               (1, 80000, 1024, "mxfp4")])
+def test_decode_graph_replay(B, T, k, idx_dtype):
+    """csa_decode captured in a HIP graph: every replay, with eager work and
+    synchronisations between them, equals the eager call bit for bit (rows above 16,384
+    entries take the two-launch top-k with its workspace counters)."""
+    c = W.csa_decode(5, B=B, T=T, H=64, k=k, idx_dtype=idx_dtype)
+    if idx_dtype == "mxfp4":
+        kd, ksc = csa.mxfp4_quantize(dev(c["kI"]))
+        qd = dev(c["qI"][:, None])                 # fp32 queries, quantised inside the call
+    else:
+        qd, kd, ksc = dev(c["qI"][:, None]), dev(c["kI"]), None
+    dec = csa.Decoder(dev(c["q"][:, None]), dev(c["kv"]), dev(c["kv_raw"]), _i32(c["raw_base"]),
+                      _i32(c["q_pos"][:, None]), qd, dev(c["w"][:, None]), kd, _i32(c["n_entries"]), m=4, topk=k,
+                      window=128, k_scale=ksc)
+    out, idx = dec()
+    torch.cuda.synchronize()
+    ref_out, ref_idx = out.clone(), idx.clone()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=side):
+        dec()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        dec.out.zero_()
+        dec.out_idx.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dec.out_idx, ref_idx), "replay %d: indices differ from the eager call" % rep
+        assert torch.equal(dec.out, ref_out), "replay %d: output differs from the eager call" % rep
+
+
 def test_decode_fp32_workload_end_to_end():
     """The fp32 single-layer decode: compression of 2048 tokens -> 512 entries on the GPU,
     then indexer, top-64, window-128 sparse MQA, all against the oracle at 1e-5."""
