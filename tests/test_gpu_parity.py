@@ -628,6 +628,32 @@ def test_decode_graph_replay(B, T, k, idx_dtype):
         assert torch.equal(dec.out, ref_out), "replay %d: output differs from the eager call" % rep
 
 
+def test_decode_with_fp8_cache_sink_and_rope():
+    """csa_decode with every attention option at once: FP8 cache and window rows, per-head
+    sinks, the rope-conjugate output and batch-invariant splits, against the oracle over the
+    dequantised rows and the GPU's selection (whose top-k is checked on its own)."""
+    B, T, k, H = 2, 12000, 256, 64
+    c = W.csa_decode(9, B=B, T=T, H=H, k=k)
+    rng = np.random.default_rng(90)
+    kv_c, raw_c = oracle.fp8_quantize(W.value(c["kv"])), oracle.fp8_quantize(W.value(c["kv_raw"]))
+    kv_v, raw_v = oracle.fp8_dequantize(kv_c), oracle.fp8_dequantize(raw_c)
+    sink = rng.normal(0.0, 2.0, H).astype(np.float32)
+    cs = rng.uniform(-1, 1, (B, 1, 128)).astype(np.float32)
+    dec = csa.Decoder(dev(c["q"][:, None]), torch.from_numpy(kv_c).cuda(), torch.from_numpy(raw_c).cuda(),
+                      _i32(c["raw_base"]), _i32(c["q_pos"][:, None]), dev(c["qI"][:, None]), dev(c["w"][:, None]),
+                      dev(c["kI"]), _i32(c["n_entries"]), m=4, topk=k, window=128, sink=dev(sink), rope=dev(cs),
+                      split_items=128)
+    out, idx = dec()
+    out, idx = host(out)[:, 0], idx.cpu().numpy()[:, 0]
+    for b in range(B):
+        t = int(c["q_pos"][b])
+        scores = oracle.index_scores(W.value(c["qI"][b]), c["w"][b], W.value(c["kI"][b]))
+        check_topk_row(idx[b], scores, oracle.visible(t, c["N"], 4), k, "decode topk")
+        want, _ = oracle.sparse_mqa(W.value(c["q"][b]), kv_v[b], idx[b], raw_v[b], c["raw_base"][b], t, 128,
+                                    c["scale"], c["eps"], None, sink)
+        assert_bf16_close(out[b], oracle.rope_conjugate(want, cs[b, 0]), "decode out")
+
+
 def test_decode_fp32_workload_end_to_end():
     """The fp32 single-layer decode: compression of 2048 tokens -> 512 entries on the GPU,
     then indexer, top-64, window-128 sparse MQA, all against the oracle at 1e-5."""
