@@ -250,10 +250,11 @@ csa_status csa_index_topk_rescored(const csa_index_desc* desc, int32_t cand, con
  * (head_dim >= 64); lse is unchanged.
  *
  *   q      [batch, n_q, heads, head_dim] dtype
- *   kv     [batch, kv_cap, head_dim]     dtype (compressed entries)
+ *   kv     [batch, kv_cap, head_dim]     dtype, or E4M3 bytes with kv_dtype = CSA_FP8
+ *                                        (compressed entries)
  *   idx    [batch, n_q, topk] int32 (sparse only)
  *   n_entries [batch] int32 (dense only, <= n_max)
- *   kv_raw [batch, raw_cap, head_dim] dtype;  raw_base [batch] int32
+ *   kv_raw [batch, raw_cap, head_dim] as kv;  raw_base [batch] int32
  *   q_pos  [batch, n_q] int32
  *   out    [batch, n_q, heads, head_dim] dtype
  *   lse    [batch, n_q, heads] fp32 natural-log softmax denominator, or NULL
