@@ -33,6 +33,20 @@ def oracle_attend_selected(q, kv_store, idx, kv_raw, raw_base, t, window, scale,
     return oracle.sparse_mqa(q, sub, idx_sub, W.value(kv_raw), raw_base, t, window, scale, eps)
 
 
+def fp8_codes(x):
+    """E4M3 codes of x (nearest finite value, saturating): an input generator for FP8 caches,
+    vectorised; the oracle reads the codes back with its own dequantiser."""
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    vals = oracle.fp8_dequantize(codes)
+    order = np.lexsort((codes, vals))                 # ascending value; -0 before +0
+    grid, gc = vals[order], codes[order]
+    x = np.clip(np.asarray(x, dtype=np.float64), -448.0, 448.0)
+    hi = np.clip(np.searchsorted(grid, x), 1, len(grid) - 1)
+    lo = hi - 1
+    pick = np.where(np.abs(grid[hi] - x) < np.abs(x - grid[lo]), hi, lo)
+    return gc[pick].reshape(np.shape(x))
+
+
 def test_fp32_decode_2k_full():
     """2,048 tokens, m = 4, 8 heads x 64, indexer 4 x 32, top-64, window 128 (fp32, 1e-5)."""
     c = W.cfg1()
@@ -179,3 +193,25 @@ def test_csa_prefill_4k_on_60k_sampled():
         want, _ = oracle.sparse_mqa(W.value(c["q"][i]), sub, idx_sub, W.value(c["kv_raw"]), c["raw_base"], t, 128,
                                     c["scale"], c["eps"])
         assert_bf16_close(host(out[0, i]), want, "query %d out" % i)
+
+
+def test_csa_decode_64k_full_fp8_cache():
+    """The 64K decode workload with its compressed entries and window rows stored as FP8
+    E4M3: the fused call selects as with bf16 and attends over the codes' exact values."""
+    c = W.cfg2()
+    kv8 = fp8_codes(W.value(c["kv"]))
+    raw8 = fp8_codes(W.value(c["kv_raw"]))
+    dec = csa.Decoder(dev(c["q"][:, None]), torch.from_numpy(kv8).cuda(), torch.from_numpy(raw8).cuda(),
+                      i32(c["raw_base"]), i32(c["q_pos"][:, None]), dev(c["qI"][:, None]), dev(c["w"][:, None]),
+                      dev(c["kI"]), i32(c["n_entries"]), m=4, topk=1024, window=128)
+    out, idx = dec()
+    out, idx = host(out)[:, 0], idx.cpu().numpy()[:, 0]
+    for b in range(8):
+        scores = oracle.index_scores(W.value(c["qI"][b]), c["w"][b], W.value(c["kI"][b]))
+        check_topk_row(idx[b], scores, 16384, 1024, "seq %d" % b)
+        sel = idx[b][idx[b] >= 0]
+        idx_sub = np.where(idx[b] >= 0, np.cumsum(idx[b] >= 0) - 1, -1).astype(np.int32)
+        want, _ = oracle.sparse_mqa(W.value(c["q"][b]), oracle.fp8_dequantize(kv8[b][sel]), idx_sub,
+                                    oracle.fp8_dequantize(raw8[b]), int(c["raw_base"][b]), int(c["q_pos"][b]), 128,
+                                    c["scale"], c["eps"])
+        assert_bf16_close(out[b], want, "seq %d out" % b)
