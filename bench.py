@@ -41,7 +41,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "mxfp4": 10100.0}
-WORKLOADS = ["csa_decode_64k", "hca_decode_1m", "csa_decode_1m_fp4", "csa_prefill_4k", "csa_decode_1m_fp4_rescored"]
+WORKLOADS = ["csa_decode_64k", "hca_decode_1m", "csa_decode_1m_fp4", "csa_prefill_4k", "csa_decode_1m_fp4_rescored",
+             "csa_decode_64k_fp8"]
 CALIB_BYTES = 256 << 20
 
 
@@ -97,6 +98,7 @@ def i32(x, dev):
 class CsaDecode64k(Step):
     name = "csa_decode_64k"
     metric = "CSA decode tokens/s at 64K context (one layer, 8 sequences)"
+    fp8 = False   # the compressed entries and window rows as FP8 E4M3 codes
 
     def __init__(self, dev, R):
         from long_context_compressed_04_amd import csa
@@ -108,6 +110,11 @@ class CsaDecode64k(Step):
         self.replicas = R
         c = W.csa_decode(0, B=self.B, T=self.T, m=self.m, H=self.H, d=self.d, HI=self.HI, dI=self.dI, k=self.k,
                          window=self.w)
+        if self.fp8:   # codes drawn after the other tensors (the bf16 workload's draws are unchanged)
+            rng = W.rng_for(1)
+            c["kv"] = W.fp8_cache_codes(rng, c["kv"].shape)
+            c["kv_raw"] = W.fp8_cache_codes(rng, c["kv_raw"].shape)
+        self.c = c
         base = dict(q=to_dev(c["q"][:, None], dev), kv=to_dev(c["kv"], dev), kv_raw=to_dev(c["kv_raw"], dev),
                     qI=to_dev(c["qI"][:, None], dev), w=to_dev(c["w"][:, None], dev), kI=to_dev(c["kI"], dev))
         rb, qp, ne = i32(c["raw_base"], dev), i32(c["q_pos"][:, None], dev), i32(c["n_entries"], dev)
@@ -117,9 +124,12 @@ class CsaDecode64k(Step):
         self.config = {"workload": self.name, "batch": self.B, "context": self.T, "compress_ratio": self.m,
                        "entries": self.N, "heads": self.H, "head_dim": self.d, "idx_heads": self.HI,
                        "idx_dim": self.dI, "topk": self.k, "window": self.w, "cache_replicas": R}
+        if self.fp8:
+            self.config["cache_dtype"] = "fp8_e4m3"
         B, N, k, w, d, H, HI, dI = self.B, self.N, self.k, self.w, self.d, self.H, self.HI, self.dI
-        self.step_bytes = B * N * dI * 2 + B * (k + w) * d * 2 + 2 * B * H * d * 2 + B * HI * dI * 2 + B * HI * 4 \
-            + B * k * 4
+        self.row_bytes = d * (1 if self.fp8 else 2)
+        self.step_bytes = B * N * dI * 2 + B * (k + w) * self.row_bytes + 2 * B * H * d * 2 + B * HI * dI * 2 \
+            + B * HI * 4 + B * k * 4
         self.step_flops = 2.0 * B * N * HI * dI + 4.0 * B * H * d * (k + w)
 
     def launch(self, i):
@@ -131,17 +141,17 @@ class CsaDecode64k(Step):
             return "hbm", B * N * dI * 2 + B * HI * dI * 2 + B * HI * 4 + B * N * 4
         if kernel == "topk":
             return "hbm", B * N * 4 + B * k * 4
-        if kernel.startswith("mqa_bf16"):
-            return "hbm", B * (k + w) * d * 2 + 2 * B * H * d * 2 + B * k * 4
+        if kernel.startswith("mqa_bf16") or kernel.startswith("mqa_f8"):
+            return "hbm", B * (k + w) * self.row_bytes + 2 * B * H * d * 2 + B * k * 4
         return None
 
     def cpu_baseline(self):
         import oracle
         from long_context_compressed_04_amd import workloads as W
-        c = W.csa_decode(0, B=self.B, T=self.T, m=self.m, H=self.H, d=self.d, HI=self.HI, dI=self.dI, k=self.k,
-                         window=self.w)
-        vals = [(W.value(c["q"][b]), W.value(c["kv"][b]), W.value(c["qI"][b]), c["w"][b], W.value(c["kI"][b]),
-                 W.value(c["kv_raw"][b]), int(c["raw_base"][b]), int(c["q_pos"][b])) for b in range(self.B)]
+        c = self.c
+        rows = (lambda x: oracle.fp8_dequantize(x)) if self.fp8 else W.value
+        vals = [(W.value(c["q"][b]), rows(c["kv"][b]), W.value(c["qI"][b]), c["w"][b], W.value(c["kI"][b]),
+                 rows(c["kv_raw"][b]), int(c["raw_base"][b]), int(c["q_pos"][b])) for b in range(self.B)]
         n, t0 = 0, time.perf_counter()
         while True:     # sequences in turn until at least 10 s of work
             q, kv, qI, w, kI, raw, rb, t = vals[n % len(vals)]
@@ -153,7 +163,16 @@ class CsaDecode64k(Step):
                 break
         return {"value": round(n / secs, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
                 "sample": "%d whole decode steps of one sequence each (indexer over 16,384 keys, top-1024, MQA over "
-                          "1,152 rows x 128 heads), fp64, single thread, %.1f s" % (n, secs)}
+                          "1,152 rows x 128 heads%s), fp64, single thread, %.1f s"
+                          % (n, ", FP8 rows dequantised" if self.fp8 else "", secs)}
+
+
+class CsaDecode64kFp8(CsaDecode64k):
+    name = "csa_decode_64k_fp8"
+    metric = "CSA decode tokens/s at 64K context with an FP8 E4M3 KV cache (one layer, 8 sequences)"
+    fp8 = True
+    data = ("synthetic (seeded FP8 E4M3 cache codes of unit-scale values; N(0,1) queries and index keys; U[0,1) "
+            "indexer head weights)")
 
 
 class HcaDecode1m(Step):
@@ -472,7 +491,8 @@ class CsaPrefill4k(Step):
 
 
 def make(name, dev, R):
-    return {"csa_decode_64k": CsaDecode64k, "hca_decode_1m": HcaDecode1m, "csa_decode_1m_fp4": CsaDecode1mFp4,
+    return {"csa_decode_64k": CsaDecode64k, "csa_decode_64k_fp8": CsaDecode64kFp8, "hca_decode_1m": HcaDecode1m,
+            "csa_decode_1m_fp4": CsaDecode1mFp4,
             "csa_prefill_4k": CsaPrefill4k, "csa_decode_1m_fp4_rescored": CsaDecode1mFp4Rescored}[name](dev, R)
 
 
@@ -594,7 +614,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) caches, token streams and queries; U[0,1) indexer head weights)",
+        "data": getattr(wl, "data", "synthetic (seeded N(0,1) caches, token streams and queries; U[0,1) indexer "
+                                    "head weights)"),
         "config": dict(wl.config, graph=graph is not None),
         "step_bytes": wl.step_bytes,
         "step_flops": wl.step_flops,

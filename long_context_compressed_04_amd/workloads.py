@@ -56,6 +56,19 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
+def fp8_cache_codes(rng, shape) -> np.ndarray:
+    """FP8 E4M3 cache rows drawn directly as codes (uint8), no rounding: a uniform sign,
+    an exponent field whose weights follow where |N(0,1)| values fall (field e covers
+    [2^(e-7), 2^(e-6)), e = 7 is [1, 2)), and a uniform 3-bit mantissa.  Unit-scale data
+    like the bf16 caches; every code is finite."""
+    w = np.array([0.012, 0.024, 0.048, 0.095, 0.18, 0.30, 0.27, 0.045, 0.0001])   # fields 1 .. 9
+    n = int(np.prod(shape))
+    sign = rng.integers(0, 2, n, dtype=np.uint8)
+    field = (rng.choice(len(w), size=n, p=w / w.sum()) + 1).astype(np.uint8)
+    mant = rng.integers(0, 8, n, dtype=np.uint8)
+    return ((sign << 7) | (field << 3) | mant).astype(np.uint8).reshape(shape)
+
+
 def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
     return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
