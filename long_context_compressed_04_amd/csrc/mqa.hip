@@ -26,6 +26,13 @@
 // the product, 1/rms of each row scales its logit and its softmax weight, and g
 // multiplies the output.  Splits write fp32 partials (unnormalised O, maximum, sum)
 // that a second kernel combines in fixed split order (deterministic).
+//
+// Options on every path: per-head sink logits in the softmax denominator (techniques
+// map, "Learnable attention sink"), and the rope-conjugate rotation of the output's
+// trailing 64 dims with the query's cos and sin ("Gated attention output", "Partial
+// RoPE"), both applied where the output is finished.  The split-role kernel also reads
+// FP8 E4M3 caches ("FP8 KV-cache quantization"), converting each row to bf16 on its way
+// into LDS.
 #include <cmath>
 #include <type_traits>
 
