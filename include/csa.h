@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 1
+#define CSA_ABI_VERSION 2
 
 typedef enum {
   CSA_OK = 0,
@@ -100,6 +100,13 @@ const char* csa_last_error(void);
  * Entries [entry_begin, entry_end) are produced.  Requires the rows they need to be
  * present: m*entry_begin - (entry_begin > 0 ? m : 0) >= tok_base and
  * m*entry_end <= tok_base + n_rows; entry_end <= out_cap; 1 <= m <= 256.
+ * A bias_b of -inf everywhere masks the lagging stream: every entry then pools the
+ * m tokens of its own block only (non-overlapping, single-stream pooling).
+ * norm = 1: each entry is RMS-normalised in fp32 before it is stored,
+ * entry * g / sqrt(mean(entry^2) + norm_eps) with g = norm_weight [channels] fp32
+ * (NULL = ones); channels <= 4096.  (DeepSeek-V4's compressors normalise every
+ * pooled entry, the indexer's keys included; the attention calls of this library
+ * normalise the KV rows they read themselves, so the KV cache needs no norm here.)
  * ---------------------------------------------------------------------------- */
 typedef struct {
   int32_t batch;
@@ -113,11 +120,13 @@ typedef struct {
   int32_t out_cap;
   int32_t in_dtype;      /* CSA_F32 or CSA_BF16 */
   int32_t out_dtype;     /* CSA_F32 or CSA_BF16 */
+  int32_t norm;          /* 0: entries as pooled; 1: RMS-normalised (see above) */
+  float norm_eps;        /* norm = 1: epsilon, >= 0 */
 } csa_compress_desc;
 
 csa_status csa_compress(const csa_compress_desc* desc, const void* a, const void* b,
                         const float* za, const float* zb, const float* bias_a,
-                        const float* bias_b, void* out, void* stream);
+                        const float* bias_b, const float* norm_weight, void* out, void* stream);
 
 /* ------------------------------------------------------------------------------
  * csa_mxfp4_quantize -- OCP MX v1.0 MXFP4 encoding of n_blocks blocks of 32
@@ -243,11 +252,13 @@ csa_status csa_index_topk_rescored(const csa_index_desc* desc, int32_t cand, con
  * exp(s_h)) and lse includes exp(s_h).  |s_h| <= 80.
  * Rope-conjugate output ("DeepSeek-V4-Pro" techniques map, "Gated attention output" and
  * "Partial RoPE": the output is rotated back before the output projection; RoPE
- * covers the trailing 64 dims of a head, x*cos + rotate_half(x)*sin with
- * rotate_half([a, b]) = [-b, a] over the two 32-dim halves): rope [batch, n_q, 128]
- * fp32 = the query's cos[64] then sin[64], or NULL for none.  With rope, dims
- * head_dim-64 .. head_dim-1 of every output head become x*cos - rotate_half(x)*sin
- * (head_dim >= 64); lse is unchanged.
+ * covers the trailing 64 dims of a head, x*cos + rotate_half(x)*sin).  V4's rotary
+ * turns interleaved pairs: within the rotated slice, rotate_half(x)_{2j} = -x_{2j+1}
+ * and rotate_half(x)_{2j+1} = x_{2j}.  rope [batch, n_q, 128] fp32 = the query's
+ * cos[64] then sin[64], one value per rotated dim (V4's per-pair angle repeated on
+ * both dims of its pair), or NULL for none.  With rope, dims head_dim-64 ..
+ * head_dim-1 of every output head become x*cos - rotate_half(x)*sin (head_dim >= 64);
+ * lse is unchanged.
  *
  *   q      [batch, n_q, heads, head_dim] dtype
  *   kv     [batch, kv_cap, head_dim]     dtype, or E4M3 bytes with kv_dtype = CSA_FP8
@@ -314,6 +325,10 @@ csa_status hca_dense_mqa(const csa_mqa_desc* desc, const void* q, const void* kv
  * csa_compress), then the indexer and top-k (as csa_index_topk, writing out_idx),
  * then sparse MQA over the selected entries plus the window (as csa_sparse_mqa).
  * index.batch/n_q must equal attn.batch/n_q and index.topk == attn.topk.
+ * A job writes its entries [entry_begin, entry_end) before the indexer reads the
+ * keys, so n_entries[b] must already count them (entry_end when the step's block
+ * has just completed: t + 1 = m * entry_end).  The jobs' out pointers are normally
+ * the kv and k_idx caches of this call; one entry range serves the whole batch.
  * ---------------------------------------------------------------------------- */
 typedef struct {
   csa_compress_desc desc;
@@ -323,6 +338,7 @@ typedef struct {
   const float* zb;
   const float* bias_a;
   const float* bias_b;
+  const float* norm_weight;
   void* out;
 } csa_compress_job;
 

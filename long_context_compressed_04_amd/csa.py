@@ -28,7 +28,7 @@ class CsaError(RuntimeError):
 class CompressDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "channels", "m", "zc", "n_rows", "tok_base", "entry_begin", "entry_end", "out_cap",
-        "in_dtype", "out_dtype")]
+        "in_dtype", "out_dtype", "norm")] + [("norm_eps", ctypes.c_float)]
 
 
 class IndexDesc(ctypes.Structure):
@@ -48,7 +48,7 @@ _P = ctypes.c_void_p
 
 class CompressJob(ctypes.Structure):
     _fields_ = [("desc", CompressDesc), ("a", _P), ("b", _P), ("za", _P), ("zb", _P), ("bias_a", _P),
-                ("bias_b", _P), ("out", _P)]
+                ("bias_b", _P), ("norm_weight", _P), ("out", _P)]
 
 
 class DecodeArgs(ctypes.Structure):
@@ -75,7 +75,7 @@ def lib():
         L.csa_status_string.restype = ctypes.c_char_p
         L.csa_status_string.argtypes = [ctypes.c_int]
         L.csa_last_error.restype = ctypes.c_char_p
-        L.csa_compress.argtypes = [ctypes.POINTER(CompressDesc)] + [V] * 8
+        L.csa_compress.argtypes = [ctypes.POINTER(CompressDesc)] + [V] * 9
         L.csa_compress.restype = S
         L.csa_mxfp4_quantize.argtypes = [ctypes.c_int32, V, ctypes.c_int64, V, V, V]
         L.csa_mxfp4_quantize.restype = S
@@ -149,19 +149,36 @@ def _workspace(nbytes, device, ws):
 
 
 # ----------------------------------------------------------------------------------
-def compress(a, b, za, zb, m, out, *, tok_base=0, entry_begin=0, entry_end=None, bias_a=None, bias_b=None):
-    """Pool token rows into compressed entries (csa_compress).  a, b: [B, rows, c]
-    fp32/bf16; za, zb: [B, rows] or [B, rows, c] fp32; out: [B, cap, c] fp32/bf16,
-    entry j written to row j."""
+def _compress_desc(a, za, m, out, tok_base, entry_begin, entry_end, norm_eps):
     B, rows, c = a.shape
     zc = 1 if za.dim() == 2 else za.shape[-1]
     if entry_end is None:
         entry_end = (tok_base + rows) // m
-    d = CompressDesc(B, c, m, zc, rows, tok_base, entry_begin, entry_end, out.shape[1], _dtype_code(a),
-                     _dtype_code(out))
-    _check(lib().csa_compress(ctypes.byref(d), _p(a), _p(b), _p(za), _p(zb), _p(bias_a), _p(bias_b), _p(out),
-                              _stream(a)))
+    norm = 0 if norm_eps is None else 1
+    return CompressDesc(B, c, m, zc, rows, tok_base, entry_begin, entry_end, out.shape[1], _dtype_code(a),
+                        _dtype_code(out), norm, 0.0 if norm_eps is None else float(norm_eps))
+
+
+def compress(a, b, za, zb, m, out, *, tok_base=0, entry_begin=0, entry_end=None, bias_a=None, bias_b=None,
+             norm_eps=None, norm_weight=None):
+    """Pool token rows into compressed entries (csa_compress).  a, b: [B, rows, c]
+    fp32/bf16; za, zb: [B, rows] or [B, rows, c] fp32; out: [B, cap, c] fp32/bf16,
+    entry j written to row j.  norm_eps given: each entry RMS-normalised (times
+    norm_weight [c] fp32, or ones) before it is stored."""
+    d = _compress_desc(a, za, m, out, tok_base, entry_begin, entry_end, norm_eps)
+    _check(lib().csa_compress(ctypes.byref(d), _p(a), _p(b), _p(za), _p(zb), _p(bias_a), _p(bias_b),
+                              _p(norm_weight), _p(out), _stream(a)))
     return out
+
+
+def compress_job(a, b, za, zb, m, out, *, tok_base=0, entry_begin=0, entry_end=None, bias_a=None, bias_b=None,
+                 norm_eps=None, norm_weight=None):
+    """A compression for Decoder's kv_job / key_job: the same arguments as compress(),
+    run inside each decode call before the indexer."""
+    d = _compress_desc(a, za, m, out, tok_base, entry_begin, entry_end, norm_eps)
+    job = CompressJob(d, _p(a), _p(b), _p(za), _p(zb), _p(bias_a), _p(bias_b), _p(norm_weight), _p(out))
+    job._keep = [a, b, za, zb, out, bias_a, bias_b, norm_weight]
+    return job
 
 
 def mxfp4_quantize(x, codes=None, scales=None):
@@ -295,10 +312,16 @@ class Decoder:
 
     def __init__(self, q, kv, kv_raw, raw_base, q_pos, q_idx, w, k_idx, n_entries, *, m, topk, window,
                  n_max=None, q_scale=None, k_scale=None, scale=0.0, eps=1e-6, rms_weight=None, sink=None,
-                 rope=None, split_items=0, out=None, out_idx=None, out_score=None, lse=None):
+                 rope=None, split_items=0, out=None, out_idx=None, out_score=None, lse=None, kv_job=None,
+                 key_job=None):
+        """kv_job / key_job: compress_job() results, run at the start of every call (the
+        entries a step's completed block adds to the KV cache and to the index keys)."""
         self.tensors = [q, kv, kv_raw, raw_base, q_pos, q_idx, w, k_idx, n_entries, q_scale, k_scale, rms_weight,
                         sink, rope]
+        self.jobs = (kv_job, key_job)
         a = DecodeArgs()
+        a.kv_job = ctypes.pointer(kv_job) if kv_job is not None else None
+        a.key_job = ctypes.pointer(key_job) if key_job is not None else None
         a.index = _index_desc(q_idx, k_idx, m, topk, n_max, *_index_dtype(q_idx, k_idx))
         a.attn = _mqa_desc(q, kv, kv_raw, topk=topk, window=window, scale=scale, eps=eps, split_items=split_items)
         dev = q.device

@@ -11,6 +11,9 @@
 // workgroup per (entry, sequence); the 2m softmax weights are computed once into
 // LDS (shared logits) or per channel (per-channel logits), then every thread
 // streams channels with coalesced row reads.  fp32 arithmetic throughout.
+// Optionally the pooled entry is RMS-normalised before it is stored (DeepSeek-V4's
+// compressors normalise each pooled entry, index keys included): the fp32 entry is
+// kept in LDS until the block has its sum of squares.
 #include "csa_device.hpp"
 #include "csa_kernels.hpp"
 #include "launch_timer.hpp"
@@ -27,6 +30,7 @@ __global__ __launch_bounds__(kCompressThreads) void compress_kernel(CompressArgs
   const int m = A.m, c = A.channels, zc = A.zc;
   __shared__ float wts[2 * kMaxM];
   __shared__ float red[kCompressThreads / 64];
+  __shared__ float pooled[kCompressNormMaxChannels];   // (A.norm only)
 
   const long a0 = (long)m * j - A.tok_base;      // first A row (relative)
   const long b0 = (long)m * (j - 1) - A.tok_base; // first B row (relative)
@@ -37,6 +41,16 @@ __global__ __launch_bounds__(kCompressThreads) void compress_kernel(CompressArgs
     long e = (rows_off + row) * c + ch;
     if (IN_BF16) return bf16_to_f32(((const uint16_t*)base)[e]);
     return ((const float*)base)[e];
+  };
+  auto store = [&](int ch, float v) {
+    long o = ((long)b * A.out_cap + j) * c + ch;
+    if (OUT_BF16) ((uint16_t*)A.out)[o] = f32_to_bf16(v);
+    else ((float*)A.out)[o] = v;
+  };
+  // the pooled value of channel ch: stored, or kept for the normalisation
+  auto emit = [&](int ch, float v) {
+    if (A.norm) pooled[ch] = v;
+    else store(ch, v);
   };
 
   if (zc == 1) {
@@ -76,9 +90,7 @@ __global__ __launch_bounds__(kCompressThreads) void compress_kernel(CompressArgs
       for (int r = 0; r < m; ++r) acc += (wts[r] * inv) * in_val(A.a, a0 + r, ch);
       if (has_b)
         for (int r = 0; r < m; ++r) acc += (wts[m + r] * inv) * in_val(A.b, b0 + r, ch);
-      long o = ((long)b * A.out_cap + j) * c + ch;
-      if (OUT_BF16) ((uint16_t*)A.out)[o] = f32_to_bf16(acc);
-      else ((float*)A.out)[o] = acc;
+      emit(ch, acc);
     }
   } else {
     // Per-channel logits: each thread owns channels and runs its own softmax.
@@ -101,11 +113,21 @@ __global__ __launch_bounds__(kCompressThreads) void compress_kernel(CompressArgs
           den += e;
           acc += e * in_val(A.b, b0 + r, ch);
         }
-      acc = acc / den;
-      long o = ((long)b * A.out_cap + j) * c + ch;
-      if (OUT_BF16) ((uint16_t*)A.out)[o] = f32_to_bf16(acc);
-      else ((float*)A.out)[o] = acc;
+      emit(ch, acc / den);
     }
+  }
+  if (A.norm) {   // uniform: x * g / sqrt(mean(x^2) + eps) over the entry's channels
+    __syncthreads();
+    float ss = 0.f;
+    for (int ch = threadIdx.x; ch < c; ch += blockDim.x) ss = fmaf(pooled[ch], pooled[ch], ss);
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    float tot = 0.f;
+    for (int i = 0; i < kCompressThreads / 64; ++i) tot += red[i];
+    const float inv = 1.f / sqrtf(tot / c + A.norm_eps);
+    for (int ch = threadIdx.x; ch < c; ch += blockDim.x)
+      store(ch, pooled[ch] * inv * (A.norm_weight ? A.norm_weight[ch] : 1.f));
   }
 }
 
@@ -113,12 +135,10 @@ hipError_t launch_compress(const CompressArgs& A, hipStream_t s) {
   int n = A.entry_end - A.entry_begin;
   if (n <= 0 || A.batch <= 0) return hipSuccess;
   dim3 grid(n, A.batch), block(kCompressThreads);
-  LaunchTimer timer("compress", s);
-  if (A.in_bf16 && A.out_bf16) compress_kernel<true, true><<<grid, block, 0, s>>>(A);
-  else if (A.in_bf16) compress_kernel<true, false><<<grid, block, 0, s>>>(A);
-  else if (A.out_bf16) compress_kernel<false, true><<<grid, block, 0, s>>>(A);
-  else compress_kernel<false, false><<<grid, block, 0, s>>>(A);
-  return hipGetLastError();
+  if (A.in_bf16 && A.out_bf16) return launch("compress", compress_kernel<true, true>, grid, block, 0, s, A);
+  if (A.in_bf16) return launch("compress", compress_kernel<true, false>, grid, block, 0, s, A);
+  if (A.out_bf16) return launch("compress", compress_kernel<false, true>, grid, block, 0, s, A);
+  return launch("compress", compress_kernel<false, false>, grid, block, 0, s, A);
 }
 
 // ---------------------------------------------------------------------------------
@@ -194,20 +214,16 @@ hipError_t launch_fp8_quantize(int in_bf16, const void* x, int64_t n, uint8_t* c
   const int64_t n8 = n / 8;
   if (n8 <= 0) return hipSuccess;
   dim3 grid((unsigned)((n8 + 255) / 256)), block(256);
-  LaunchTimer timer("fp8_quantize", s);
-  if (in_bf16) fp8_quantize_kernel<true><<<grid, block, 0, s>>>(x, n8, codes);
-  else fp8_quantize_kernel<false><<<grid, block, 0, s>>>(x, n8, codes);
-  return hipGetLastError();
+  if (in_bf16) return launch("fp8_quantize", fp8_quantize_kernel<true>, grid, block, 0, s, x, n8, codes);
+  return launch("fp8_quantize", fp8_quantize_kernel<false>, grid, block, 0, s, x, n8, codes);
 }
 
 hipError_t launch_mxfp4_quantize(int in_bf16, const void* x, int64_t n_blocks, uint8_t* codes, uint8_t* scales,
                                  hipStream_t s) {
   if (n_blocks <= 0) return hipSuccess;
   dim3 grid((unsigned)((n_blocks + 255) / 256)), block(256);
-  LaunchTimer timer("mxfp4_quantize", s);
-  if (in_bf16) mxfp4_quantize_kernel<true><<<grid, block, 0, s>>>(x, n_blocks, codes, scales);
-  else mxfp4_quantize_kernel<false><<<grid, block, 0, s>>>(x, n_blocks, codes, scales);
-  return hipGetLastError();
+  if (in_bf16) return launch("mxfp4_quantize", mxfp4_quantize_kernel<true>, grid, block, 0, s, x, n_blocks, codes, scales);
+  return launch("mxfp4_quantize", mxfp4_quantize_kernel<false>, grid, block, 0, s, x, n_blocks, codes, scales);
 }
 
 }  // namespace csa

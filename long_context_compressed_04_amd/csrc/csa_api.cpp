@@ -46,6 +46,10 @@ csa_status check_compress(const csa_compress_desc* d, const void* a, const void*
     return fail(CSA_ERR_DTYPE, "csa_compress: in_dtype/out_dtype must be CSA_F32 or CSA_BF16");
   if (d->batch < 0 || d->channels < 1 || d->m < 1 || d->m > 256 || d->n_rows < 0 || d->out_cap < 0)
     return fail(CSA_ERR_SHAPE, "csa_compress: need batch >= 0, channels >= 1, 1 <= m <= 256");
+  if (d->norm != 0 && d->norm != 1) return fail(CSA_ERR_SHAPE, "csa_compress: norm must be 0 or 1");
+  if (d->norm && (d->channels > csa::kCompressNormMaxChannels || !(d->norm_eps >= 0.f) || !std::isfinite(d->norm_eps)))
+    return fail(CSA_ERR_SHAPE, "csa_compress: norm needs channels <= %d and a finite norm_eps >= 0",
+                csa::kCompressNormMaxChannels);
   if (!(d->zc == 1 || d->zc == d->channels)) return fail(CSA_ERR_SHAPE, "csa_compress: zc must be 1 or channels");
   if (d->entry_begin < 0 || d->entry_end < d->entry_begin || d->entry_end > d->out_cap)
     return fail(CSA_ERR_SHAPE, "csa_compress: need 0 <= entry_begin <= entry_end <= out_cap");
@@ -186,7 +190,7 @@ const char* csa_status_string(int s) {
 const char* csa_last_error(void) { return g_last_error.c_str(); }
 
 csa_status csa_compress(const csa_compress_desc* d, const void* a, const void* b, const float* za, const float* zb,
-                        const float* bias_a, const float* bias_b, void* out, void* stream) {
+                        const float* bias_a, const float* bias_b, const float* norm_weight, void* out, void* stream) {
   csa_status st = check_compress(d, a, b, za, zb, out);
   if (st != CSA_OK) return st;
   csa::CompressArgs A;
@@ -194,6 +198,7 @@ csa_status csa_compress(const csa_compress_desc* d, const void* a, const void* b
   A.tok_base = d->tok_base; A.entry_begin = d->entry_begin; A.entry_end = d->entry_end; A.out_cap = d->out_cap;
   A.in_bf16 = d->in_dtype == CSA_BF16; A.out_bf16 = d->out_dtype == CSA_BF16;
   A.a = a; A.b = b; A.za = za; A.zb = zb; A.bias_a = bias_a; A.bias_b = bias_b; A.out = out;
+  A.norm = d->norm; A.norm_eps = d->norm_eps; A.norm_weight = norm_weight;
   return hip_status(csa::launch_compress(A, (hipStream_t)stream), "csa_compress");
 }
 
@@ -388,7 +393,7 @@ csa_status csa_decode(const csa_decode_args* a, void* ws, size_t ws_bytes, void*
   const csa_compress_job* jobs[2] = {a->kv_job, a->key_job};
   for (const csa_compress_job* j : jobs) {
     if (!j) continue;
-    st = csa_compress(&j->desc, j->a, j->b, j->za, j->zb, j->bias_a, j->bias_b, j->out, stream);
+    st = csa_compress(&j->desc, j->a, j->b, j->za, j->zb, j->bias_a, j->bias_b, j->norm_weight, j->out, stream);
     if (st != CSA_OK) return st;
   }
   st = csa_index_topk(&a->index, a->q_idx, a->q_idx_scale, a->w, a->k_idx, a->k_idx_scale, a->n_entries, a->q_pos,

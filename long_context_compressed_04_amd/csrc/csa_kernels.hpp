@@ -12,7 +12,11 @@ struct CompressArgs {
   int in_bf16, out_bf16;
   const void* a; const void* b; const float* za; const float* zb;
   const float* bias_a; const float* bias_b; void* out;
+  int norm = 0;                       // RMSNorm of each produced entry
+  float norm_eps = 0.f;
+  const float* norm_weight = nullptr; // [channels] or ones
 };
+constexpr int kCompressNormMaxChannels = 4096;
 hipError_t launch_compress(const CompressArgs& A, hipStream_t s);
 
 hipError_t launch_mxfp4_quantize(int in_bf16, const void* x, int64_t n_blocks, uint8_t* codes,

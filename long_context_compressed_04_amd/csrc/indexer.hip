@@ -420,36 +420,31 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_pf(IndexArgs A, f
 }
 
 template <int HB, bool FP4>
-static void launch_mfma_hb(const IndexArgs& A, float* scores, hipStream_t s) {
+static hipError_t launch_mfma_hb(const IndexArgs& A, float* scores, hipStream_t s) {
+  const dim3 block(kIdxWaves * 64);
   if (!FP4 && (A.n_q < 64 || A.sel)) {   // few queries or rescoring: keys through LDS
     dim3 grid((A.n_max + kIdxLdsEntries - 1) / kIdxLdsEntries, A.n_q, A.batch);
-    LaunchTimer timer(A.sel ? "index_rescore_bf16" : "index_scores_bf16", s);
-    if (A.sel) index_scores_lds<HB, true><<<grid, kIdxWaves * 64, 0, s>>>(A, scores);
-    else index_scores_lds<HB, false><<<grid, kIdxWaves * 64, 0, s>>>(A, scores);
-    return;
+    if (A.sel) return launch("index_rescore_bf16", index_scores_lds<HB, true>, grid, block, 0, s, A, scores);
+    return launch("index_scores_bf16", index_scores_lds<HB, false>, grid, block, 0, s, A, scores);
   }
   if (!FP4) {   // many queries: keys in registers, q double-buffered in LDS
     dim3 grid((A.n_max + kIdxLdsEntries - 1) / kIdxLdsEntries, (A.n_q + kIdxPfQueries - 1) / kIdxPfQueries,
               A.batch);
-    LaunchTimer timer("index_scores_bf16", s);
-    index_scores_pf<HB><<<grid, kIdxWaves * 64, 0, s>>>(A, scores);
-    return;
+    return launch("index_scores_bf16", index_scores_pf<HB>, grid, block, 0, s, A, scores);
   }
   const int q_tile = A.n_q >= 64 ? 16 : 1;
-  LaunchTimer timer(FP4 ? "index_scores_mxfp4" : "index_scores_bf16", s);
-  if (FP4 && A.q_quantize) {
+  if (A.q_quantize) {
     // every workgroup reads and quantises all of q (32 KB of fp32 for 64 heads): more
     // entries per workgroup, fewer copies of q read
     constexpr int TPW = 8;
     const int chunk = kIdxWaves * TPW * 32;
     dim3 grid((A.n_max + chunk - 1) / chunk, (A.n_q + q_tile - 1) / q_tile, A.batch);
-    index_scores_mfma<HB, FP4, TPW><<<grid, kIdxWaves * 64, 0, s>>>(A, scores, q_tile);
-    return;
+    return launch("index_scores_mxfp4", index_scores_mfma<HB, FP4, TPW>, grid, block, 0, s, A, scores, q_tile);
   }
   constexpr int TPW = 2;
   const int chunk = kIdxWaves * TPW * 32;
   dim3 grid((A.n_max + chunk - 1) / chunk, (A.n_q + q_tile - 1) / q_tile, A.batch);
-  index_scores_mfma<HB, FP4, TPW><<<grid, kIdxWaves * 64, 0, s>>>(A, scores, q_tile);
+  return launch("index_scores_mxfp4", index_scores_mfma<HB, FP4, TPW>, grid, block, 0, s, A, scores, q_tile);
 }
 
 hipError_t launch_index_scores(const IndexArgs& A, float* scores, hipStream_t s) {
@@ -457,19 +452,16 @@ hipError_t launch_index_scores(const IndexArgs& A, float* scores, hipStream_t s)
   if (A.dtype == 0) {
     dim3 grid((A.n_max + kIdxF32Threads - 1) / kIdxF32Threads, A.n_q, A.batch);
     size_t lds = sizeof(float) * ((size_t)A.heads * A.dim + A.heads);
-    LaunchTimer timer("index_scores_f32", s);
-    index_scores_f32<<<grid, kIdxF32Threads, lds, s>>>(A, scores);
-    return hipGetLastError();
+    return launch("index_scores_f32", index_scores_f32, grid, dim3(kIdxF32Threads), lds, s, A, scores);
   }
   const bool fp4 = A.dtype == 2;
   switch (A.heads / 32) {
-    case 1: fp4 ? launch_mfma_hb<1, true>(A, scores, s) : launch_mfma_hb<1, false>(A, scores, s); break;
-    case 2: fp4 ? launch_mfma_hb<2, true>(A, scores, s) : launch_mfma_hb<2, false>(A, scores, s); break;
-    case 3: fp4 ? launch_mfma_hb<3, true>(A, scores, s) : launch_mfma_hb<3, false>(A, scores, s); break;
-    case 4: fp4 ? launch_mfma_hb<4, true>(A, scores, s) : launch_mfma_hb<4, false>(A, scores, s); break;
+    case 1: return fp4 ? launch_mfma_hb<1, true>(A, scores, s) : launch_mfma_hb<1, false>(A, scores, s);
+    case 2: return fp4 ? launch_mfma_hb<2, true>(A, scores, s) : launch_mfma_hb<2, false>(A, scores, s);
+    case 3: return fp4 ? launch_mfma_hb<3, true>(A, scores, s) : launch_mfma_hb<3, false>(A, scores, s);
+    case 4: return fp4 ? launch_mfma_hb<4, true>(A, scores, s) : launch_mfma_hb<4, false>(A, scores, s);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace csa

@@ -1,6 +1,7 @@
-// Per-launch timing: HIP event pairs around each kernel, aggregated per kernel name
-// on collection.  Events are pooled and reused; nothing is recorded while timing is
-// off or while the launch stream is being captured into a graph.
+// Per-launch timing: a HIP event pair per kernel dispatch (stamped by the runtime with
+// the dispatch's start and end), aggregated per kernel name on collection.  Events
+// are pooled and reused; nothing is recorded while timing is off or while the launch
+// stream is being captured into a graph.
 #include "launch_timer.hpp"
 
 #include <atomic>
@@ -40,25 +41,30 @@ hipEvent_t take_event() {
 
 bool timing_enabled() { return g_on.load(std::memory_order_relaxed); }
 
-int timing_begin(hipStream_t s) {
+int timing_begin(hipStream_t s, hipEvent_t* start, hipEvent_t* stop) {
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return -1;
   std::lock_guard<std::mutex> lk(g_mu);
   Record r;
   r.start = take_event();
   r.stop = take_event();
-  if (!r.start || !r.stop) return -1;
-  if (hipEventRecord(r.start, s) != hipSuccess) return -1;
+  if (!r.start || !r.stop) {
+    if (r.start) g_pool.push_back(r.start);
+    if (r.stop) g_pool.push_back(r.stop);
+    return -1;
+  }
+  *start = r.start;
+  *stop = r.stop;
   g_recs.push_back(r);
   return (int)g_recs.size() - 1;
 }
 
-void timing_end(int slot, const char* kernel, hipStream_t s) {
+void timing_end(int slot, const char* kernel, bool launched) {
   std::lock_guard<std::mutex> lk(g_mu);
   if (slot < 0 || slot >= (int)g_recs.size()) return;
   Record& r = g_recs[slot];
   r.kernel = kernel;
-  r.done = hipEventRecord(r.stop, s) == hipSuccess;
+  r.done = launched;
 }
 
 }  // namespace csa

@@ -109,11 +109,11 @@ __device__ __forceinline__ SoftmaxEnd softmax_end(float m2, float l, const float
 }
 
 // Rope-conjugate rotation of dim i (0..63) of a head's rotated slice (the trailing 64
-// dims), from its value x and the value xp of its partner dim (i + 32 or i - 32):
-// x cos_i - rotate_half(x)_i sin_i, with rotate_half(x)_i = -x_{i+32} (i < 32) or
-// x_{i-32} (i >= 32).  cs = cos[64] then sin[64] of the query.
+// dims), from its value x and the value xp of its partner dim i ^ 1 (V4's rotary turns
+// interleaved pairs): x cos_i - rotate_half(x)_i sin_i, with rotate_half(x)_i =
+// -x_{i+1} (i even) or x_{i-1} (i odd).  cs = cos[64] then sin[64] of the query.
 __device__ __forceinline__ float rope_conj(float x, float xp, int i, const float* cs) {
-  return fmaf(x, cs[i], (i < 32 ? xp : -xp) * cs[64 + i]);
+  return fmaf(x, cs[i], ((i & 1) ? -xp : xp) * cs[64 + i]);
 }
 
 // ---------------------------------------------------------------- fp32 (VALU)
@@ -201,7 +201,7 @@ __global__ __launch_bounds__(kF32Waves * 64) void mqa_f32_kernel(MqaArgs A) {
   for (int d = threadIdx.x; d < D; d += blockDim.x) {
     const int i = d - (D - 64);   // position in the rotated slice
     if (A.rope && i >= 0)
-      orow[d] = rope_conj(val(d), val(i < 32 ? d + 32 : d - 32), i, A.rope + row * 128);
+      orow[d] = rope_conj(val(d), val(d ^ 1), i, A.rope + row * 128);
     else
       orow[d] = val(d);
   }
@@ -530,11 +530,10 @@ __global__ __launch_bounds__(NW * 64) void mqa_bf16_kernel(MqaArgs A, MqaLaunch 
       float v[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) v[r] = o[db][r] * inv_l * gam[d0 + r];
-      if (db >= 28 && A.rope) {   // dims 448 ..: the partner of dim d is d +- 32, block db ^ 2
-        const int dp = 16 * (db ^ 2) + 4 * g;
+      if (db >= 28 && A.rope) {   // dims 448 ..: the partner of dim d0 + r is d0 + (r ^ 1), in this lane
+        const float x[4] = {v[0], v[1], v[2], v[3]};
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          v[r] = rope_conj(v[r], o[db ^ 2][r] * inv_l * gam[dp + r], d0 + r - (kD - 64), A.rope + row * 128);
+        for (int r = 0; r < 4; ++r) v[r] = rope_conj(x[r], x[r ^ 1], d0 + r - (kD - 64), A.rope + row * 128);
       }
       *(uint2*)(orow + d0) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
     }
@@ -965,10 +964,10 @@ void mqa_sd_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml) {
       const int hh = 2 * k + hl;
       const float il = softmax_end(0.f, lsum[0][hh] + lsum[1][hh], A.sink, hg * 32 + hh).mul;
       f32x4_t v = *(const f32x4_t*)(stage + hh * kStageRow + 4 * d4);
-      if (rot) {   // dims 448 ..: the partner of dim d (d +- 32) is 8 lanes away in the stage
-        const f32x4_t vp = *(const f32x4_t*)(stage + hh * kStageRow + 4 * (d4 ^ 8));
+      if (rot) {   // dims 448 ..: the partner of dim d is d ^ 1, in the same four
+        const f32x4_t x = v;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = rope_conj(v[r], vp[r], 4 * (d4 - 16) + r, A.rope + row * 128);
+        for (int r = 0; r < 4; ++r) v[r] = rope_conj(x[r], x[r ^ 1], 4 * (d4 - 16) + r, A.rope + row * 128);
       }
       uint16_t* orow = (uint16_t*)A.out + (row * A.heads + hg * 32 + hh) * kD + 128 * pw + 4 * d4;
       *(uint2*)orow = make_uint2(pack_bf16x2(v[0] * il, v[1] * il), pack_bf16x2(v[2] * il, v[3] * il));
@@ -1363,10 +1362,10 @@ void mqa_w8_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml, const 
           const int hh = 4 * k + (lane >> 4);
           const float il = __shfl(inv_l[j], hh, 64);
           f32x4_t v = *(const f32x4_t*)(stage + hh * kW8Stage + 4 * (lane & 15));
-          if (rot) {   // the chunk is the rotated slice; the partner of dim d (d +- 32) is 8 lanes away
-            const f32x4_t vp = *(const f32x4_t*)(stage + hh * kW8Stage + 4 * ((lane & 15) ^ 8));
+          if (rot) {   // the chunk is the rotated slice; the partner of dim d is d ^ 1, in the same four
+            const f32x4_t x = v;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] = rope_conj(v[r], vp[r], 4 * (lane & 15) + r, A.rope + row * 128);
+            for (int r = 0; r < 4; ++r) v[r] = rope_conj(x[r], x[r ^ 1], 4 * (lane & 15) + r, A.rope + row * 128);
           }
           uint16_t* orow = (uint16_t*)A.out + (row * A.heads + head0 + hh) * kD + dim0;
           *(uint2*)orow = make_uint2(pack_bf16x2(v[0] * il, v[1] * il), pack_bf16x2(v[2] * il, v[3] * il));
@@ -1452,13 +1451,10 @@ __global__ __launch_bounds__(128) void mqa_combine_kernel(MqaArgs A, MqaLaunch L
   float v[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) v[r] = acc[r] * inv_l * (A.gamma ? A.gamma[d0 + r] : 1.f);
-  if (A.rope) {   // dims 448 ..: the partner of dim d (d +- 32) is 8 threads away
-    float vp[4];
+  if (A.rope && d0 >= kD - 64) {   // dims 448 ..: the partner of dim d0 + r is d0 + (r ^ 1)
+    const float x[4] = {v[0], v[1], v[2], v[3]};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) vp[r] = __shfl_xor(v[r], 8, 64);
-    if (d0 >= kD - 64)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = rope_conj(v[r], vp[r], d0 + r - (kD - 64), A.rope + row * 128);
+    for (int r = 0; r < 4; ++r) v[r] = rope_conj(x[r], x[r ^ 1], d0 + r - (kD - 64), A.rope + row * 128);
   }
   uint16_t* orow = (uint16_t*)A.out + (row * A.heads + head) * kD;
   *(uint2*)(orow + d0) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
@@ -1608,9 +1604,7 @@ hipError_t launch_mqa(const MqaArgs& A, void* ws, size_t ws_bytes, hipStream_t s
   if (A.batch <= 0 || A.n_q <= 0) return hipSuccess;
   if (!A.bf16) {
     dim3 grid(A.heads, A.n_q, A.batch);
-    LaunchTimer timer("mqa_f32", s);
-    mqa_f32_kernel<<<grid, kF32Waves * 64, 0, s>>>(A);
-    return hipGetLastError();
+    return launch("mqa_f32", mqa_f32_kernel, grid, dim3(kF32Waves * 64), 0, s, A);
   }
   MqaLaunch L = plan_mqa(A);
   float* part_o = nullptr;
@@ -1628,9 +1622,8 @@ hipError_t launch_mqa(const MqaArgs& A, void* ws, size_t ws_bytes, hipStream_t s
     inv_kv = (float*)((char*)ws + pb);
     inv_raw = (float*)((char*)ws + pb + r256((size_t)A.batch * A.kv_cap * sizeof(float)));
     const long n_rows = (long)A.batch * ((long)A.kv_cap + A.raw_cap);
-    LaunchTimer timer("mqa_row_norms", s);
-    row_inv_rms_kernel<<<dim3((unsigned)((n_rows + 3) / 4)), 256, 0, s>>>(A, inv_kv, inv_raw);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch("mqa_row_norms", row_inv_rms_kernel, dim3((unsigned)((n_rows + 3) / 4)), dim3(256), 0, s,
+                          A, inv_kv, inv_raw);
     if (e != hipSuccess) return e;
   }
   const size_t lds = mqa_lds_bytes(L);
@@ -1650,26 +1643,27 @@ hipError_t launch_mqa(const MqaArgs& A, void* ws, size_t ws_bytes, hipStream_t s
   const long groups = ((long)L.units + 7) / 8;
   dim3 grid((unsigned)(groups * 8 * L.n_hg));
   if (L.kind == 3) grid = dim3((unsigned)((((long)L.units * L.n_hg + 7) / 8) * 8));
-  {
-    LaunchTimer timer(L.kind == 3 ? "mqa_bf16_w8"
-                                  : (L.kind == 4 ? (A.kv_f8 ? "mqa_f8_sd" : "mqa_bf16_sd") : "mqa_bf16_h16"),
-                      s);
-    if (L.kind == 3 && L.pre)
-      mqa_w8_kernel<true><<<grid, kW8Waves * 64, lds, s>>>(A, L, part_o, part_ml, inv_kv, inv_raw);
-    else if (L.kind == 3)
-      mqa_w8_kernel<false><<<grid, kW8Waves * 64, lds, s>>>(A, L, part_o, part_ml, nullptr, nullptr);
-    else if (L.kind == 4 && A.kv_f8) mqa_sd_kernel<true><<<grid, kSdWaves * 64, lds, s>>>(A, L, part_o, part_ml);
-    else if (L.kind == 4) mqa_sd_kernel<false><<<grid, kSdWaves * 64, lds, s>>>(A, L, part_o, part_ml);
-    else if (L.nw == 4) mqa_bf16_kernel<4><<<grid, 4 * 64, lds, s>>>(A, L, part_o, part_ml);
-    else if (L.nw == 2) mqa_bf16_kernel<2><<<grid, 2 * 64, lds, s>>>(A, L, part_o, part_ml);
-    else mqa_bf16_kernel<1><<<grid, 64, lds, s>>>(A, L, part_o, part_ml);
-  }
-  hipError_t e = hipGetLastError();
+  hipError_t e;
+  if (L.kind == 3 && L.pre)
+    e = launch("mqa_bf16_w8", mqa_w8_kernel<true>, grid, dim3(kW8Waves * 64), lds, s, A, L, part_o, part_ml, inv_kv,
+               inv_raw);
+  else if (L.kind == 3)
+    e = launch("mqa_bf16_w8", mqa_w8_kernel<false>, grid, dim3(kW8Waves * 64), lds, s, A, L, part_o, part_ml,
+               (const float*)nullptr, (const float*)nullptr);
+  else if (L.kind == 4 && A.kv_f8)
+    e = launch("mqa_f8_sd", mqa_sd_kernel<true>, grid, dim3(kSdWaves * 64), lds, s, A, L, part_o, part_ml);
+  else if (L.kind == 4)
+    e = launch("mqa_bf16_sd", mqa_sd_kernel<false>, grid, dim3(kSdWaves * 64), lds, s, A, L, part_o, part_ml);
+  else if (L.nw == 4)
+    e = launch("mqa_bf16_h16", mqa_bf16_kernel<4>, grid, dim3(4 * 64), lds, s, A, L, part_o, part_ml);
+  else if (L.nw == 2)
+    e = launch("mqa_bf16_h16", mqa_bf16_kernel<2>, grid, dim3(2 * 64), lds, s, A, L, part_o, part_ml);
+  else
+    e = launch("mqa_bf16_h16", mqa_bf16_kernel<1>, grid, dim3(64), lds, s, A, L, part_o, part_ml);
   if (e != hipSuccess || L.nsplit == 1) return e;
   dim3 cgrid(A.heads, (unsigned)((long)A.batch * A.n_q));
-  LaunchTimer timer("mqa_combine", s);
-  mqa_combine_kernel<<<cgrid, kD / 4, 0, s>>>(A, L, part_o, part_ml);
-  return hipGetLastError();
+  return launch("mqa_combine", mqa_combine_kernel, cgrid, dim3(kD / 4), 0, s, A, L, (const float*)part_o,
+                (const float*)part_ml);
 }
 
 }  // namespace csa

@@ -691,13 +691,11 @@ hipError_t launch_topk_rows(const IndexArgs& A, const float* scores, int32_t* ou
   const long rows = (long)A.batch * A.n_q;
   if (rows <= 0) return hipSuccess;
   if (A.topk < 1 || A.topk > kMaxTopk) return hipErrorInvalidValue;
-  LaunchTimer timer("topk", s);
-  const dim3 grid((unsigned)rows);
+  const dim3 grid((unsigned)rows), block(kTopkThreads);
   if (A.n_max <= kRegKeys) {
-    if (A.n_max <= 4096) topk_rows_kernel<4><<<grid, kTopkThreads, 0, s>>>(A, scores, out_idx, out_score);
-    else if (A.n_max <= 8192) topk_rows_kernel<8><<<grid, kTopkThreads, 0, s>>>(A, scores, out_idx, out_score);
-    else topk_rows_kernel<16><<<grid, kTopkThreads, 0, s>>>(A, scores, out_idx, out_score);
-    return hipGetLastError();
+    if (A.n_max <= 4096) return launch("topk", topk_rows_kernel<4>, grid, block, 0, s, A, scores, out_idx, out_score);
+    if (A.n_max <= 8192) return launch("topk", topk_rows_kernel<8>, grid, block, 0, s, A, scores, out_idx, out_score);
+    return launch("topk", topk_rows_kernel<16>, grid, block, 0, s, A, scores, out_idx, out_score);
   }
   const int chunks = long_chunks(A);
   if (chunks > kMaxChunks || ws_bytes < topk_workspace_bytes(A) || !ws) return hipErrorInvalidValue;
@@ -711,9 +709,9 @@ hipError_t launch_topk_rows(const IndexArgs& A, const float* scores, int32_t* ou
   L.cidx = (int32_t*)p;
   L.chunks = chunks;
   const unsigned fgroups = (unsigned)((chunks + kFilterGroups - 1) / kFilterGroups);
-  topk_filter_kernel<<<dim3(fgroups, (unsigned)rows), kTopkThreads, 0, s>>>(A, scores, L);
-  topk_candidates_kernel<<<grid, kTopkThreads, 0, s>>>(A, scores, L, out_idx, out_score);
-  return hipGetLastError();
+  hipError_t e = launch("topk", topk_filter_kernel, dim3(fgroups, (unsigned)rows), block, 0, s, A, scores, L);
+  if (e != hipSuccess) return e;
+  return launch("topk", topk_candidates_kernel, grid, block, 0, s, A, scores, L, out_idx, out_score);
 }
 
 }  // namespace csa

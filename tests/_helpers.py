@@ -2,7 +2,13 @@
 
 Tolerances (stated for the attention hot path):
   * fp32 outputs: norm-wise relative, max|gpu - oracle| <= 1e-5 * max|oracle|.
-  * bf16 outputs: max|gpu - oracle| <= 2e-2 on unit-scale data.
+  * bf16 outputs: max|gpu - oracle| <= 2e-2 (the stated bar for unit-scale data),
+    and, because softmax outputs over thousands of rows are far below unit scale,
+    also relative to the oracle's own scale: max|gpu - oracle| <= 2e-2 * max|oracle|
+    and ||gpu - oracle||_2 <= 1e-2 * ||oracle||_2.  A CPU model of the kernels'
+    bf16 roundings at the 1M-token HCA shape gives 0.4% and 0.24% on those two
+    measures; dropping the window or the KV RMSNorm gives 4-6% and 3.6-4.6%
+    (tests/test_tolerance_controls.py holds such negative controls).
   * top-k index sets: identical, except that an entry may be swapped for another
     whose oracle score lies within 1e-6 * |k-th oracle score| of the k-th score.
   * integer / byte outputs (MXFP4 codes, indices on identical scores): bit-exact.
@@ -14,6 +20,9 @@ from long_context_compressed_04_amd import workloads as W
 
 F32_RTOL = 1e-5
 BF16_ATOL = 2e-2
+BF16_SCALED = 2e-2
+BF16_REL_L2 = 1e-2
+BF16_LSE_ATOL = 5e-3   # natural-log softmax denominators of bf16 paths (q/rms(q) is rounded to bf16)
 TIE_RTOL = 1e-6
 
 
@@ -42,12 +51,25 @@ def assert_f32_close(g, o, what=""):
     return err / max(ref, 1e-300)
 
 
+def bf16_errors(g, o):
+    """(max abs error, max abs error / max|oracle|, relative L2 error)."""
+    g, o = np.asarray(g, dtype=np.float64), np.asarray(o, dtype=np.float64)
+    err = float(np.max(np.abs(g - o))) if g.size else 0.0
+    scale = float(np.max(np.abs(o))) if o.size else 0.0
+    norm = float(np.linalg.norm(o))
+    rel_max = err / scale if scale > 0 else (0.0 if err == 0 else np.inf)
+    rel_l2 = float(np.linalg.norm(g - o)) / norm if norm > 0 else (0.0 if err == 0 else np.inf)
+    return err, rel_max, rel_l2
+
+
 def assert_bf16_close(g, o, what=""):
     g, o = np.asarray(g, dtype=np.float64), np.asarray(o, dtype=np.float64)
     assert g.shape == o.shape, (what, g.shape, o.shape)
     assert np.all(np.isfinite(g)), what + ": non-finite GPU values"
-    err = np.max(np.abs(g - o)) if g.size else 0.0
+    err, rel_max, rel_l2 = bf16_errors(g, o)
     assert err <= BF16_ATOL, "%s: max abs err %.3g > %.1g" % (what, err, BF16_ATOL)
+    assert rel_max <= BF16_SCALED, "%s: max err %.3g = %.3g of max|oracle| > %.1g" % (what, err, rel_max, BF16_SCALED)
+    assert rel_l2 <= BF16_REL_L2, "%s: relative L2 error %.3g > %.1g" % (what, rel_l2, BF16_REL_L2)
     return err
 
 

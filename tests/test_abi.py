@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) >= 12
     for n in names:
         assert hasattr(L, n), "libcsa.so does not export %s" % n
-    assert L.csa_abi_version() == 1
+    assert L.csa_abi_version() == 2
 
 
 def test_status_strings():
@@ -37,8 +37,8 @@ def test_status_strings():
 
 
 def _compress(desc, a=FAKE, b=FAKE, za=FAKE, zb=FAKE, out=FAKE):
-    return csa.lib().csa_compress(ctypes.byref(desc) if desc is not None else None, a, b, za, zb, None, None, out,
-                                  None)
+    return csa.lib().csa_compress(ctypes.byref(desc) if desc is not None else None, a, b, za, zb, None, None, None,
+                                  out, None)
 
 
 def test_compress_validation():
@@ -55,6 +55,10 @@ def test_compress_validation():
     assert _compress(D(tok_base=8, entry_begin=2)) == 2     # entry 2 needs B rows from token 4
     assert _compress(D(in_dtype=2)) == 3
     assert b"csa_compress" in csa.lib().csa_last_error()
+    assert _compress(D(norm=2)) == 2
+    assert _compress(D(norm=1, norm_eps=-1.0)) == 2
+    assert _compress(D(norm=1, norm_eps=float("nan"))) == 2
+    assert _compress(D(norm=1, channels=4097)) == 2         # the normalised entry is held in LDS
 
 
 def test_index_validation():

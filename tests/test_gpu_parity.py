@@ -60,6 +60,46 @@ def test_compress(dtype, m, c, zc, rows, tok_base, e0, e1):
         assert np.all(got[b, :e0] == 0) and np.all(got[b, e1:] == 0), "wrote outside [e0, e1)"
 
 
+@pytest.mark.parametrize("dtype,m,c,zc,rows,e1,with_weight,masked_b", [
+    ("f32", 4, 64, 64, 40, 10, False, False),     # V4's index-key form: per-channel gates, normalised
+    ("bf16", 4, 128, 128, 44, 11, True, False),   # bf16 in and out, weighted norm
+    ("bf16", 4, 512, 1, 36, 9, True, False),      # shared logits, KV width
+    ("f32", 8, 48, 48, 50, 6, False, True),       # V4's HCA form: one stream, non-overlapping
+    ("bf16", 128, 64, 1, 384, 3, True, True),     # HCA ratio, single stream
+])
+def test_compress_norm_and_single_stream(dtype, m, c, zc, rows, e1, with_weight, masked_b):
+    """The RMS-normalised entries (csa_compress norm = 1, eps 1e-6, weight or ones) against
+    oracle_rmsnorm of oracle_compress; a bias_b of -inf masks the lagging stream."""
+    rng = np.random.default_rng(300 + m + c)
+    B = 2
+    A = W.store(rng.standard_normal((B, rows, c)).astype(np.float32) * 3.0, dtype)
+    Bs = W.store(rng.standard_normal((B, rows, c)).astype(np.float32), dtype)
+    zshape = (B, rows) if zc == 1 else (B, rows, c)
+    za = rng.standard_normal(zshape).astype(np.float32)
+    zb = rng.standard_normal(zshape).astype(np.float32)
+    bias_a = rng.standard_normal((m, zc)).astype(np.float32) * 0.5
+    bias_b = np.full((m, zc), -np.inf, np.float32) if masked_b else \
+        rng.standard_normal((m, zc)).astype(np.float32) * 0.5
+    gw = (0.5 + rng.random(c)).astype(np.float32) if with_weight else None
+    out = torch.zeros((B, e1 + 2, c), dtype=torch.float32 if dtype == "f32" else torch.bfloat16, device="cuda")
+    csa.compress(dev(A), dev(Bs), dev(za), dev(zb), m, out, entry_end=e1, bias_a=dev(bias_a), bias_b=dev(bias_b),
+                 norm_eps=1e-6, norm_weight=None if gw is None else dev(gw))
+    got = host(out)
+    for b in range(B):
+        pooled = oracle.compress(W.value(A[b]), W.value(Bs[b]), za[b], zb[b], m, bias_a=bias_a, bias_b=bias_b,
+                                 entry_end=e1)
+        want = oracle.rmsnorm(pooled, 1e-6, gw)
+        if masked_b:   # the single-stream reading: the A block's own pooling
+            solo = oracle.compress(W.value(A[b]), W.value(A[b]), za[b], za[b], m, bias_a=bias_a,
+                                   bias_b=np.full((m, zc), -np.inf), entry_end=e1)
+            np.testing.assert_allclose(pooled, solo, rtol=0, atol=1e-12)
+        if dtype == "f32":
+            assert_f32_close(got[b, :e1], want, "normalised compress")
+        else:
+            assert_bf16_close(got[b, :e1], want, "normalised compress")
+        assert np.all(got[b, e1:] == 0)
+
+
 # ---------------------------------------------------------------------- MXFP4
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_mxfp4_quantize_bit_exact(dtype):
@@ -683,3 +723,87 @@ def test_determinism():
     o2, i2 = _run_decode(c, 512, 128, 4)
     np.testing.assert_array_equal(i1, i2)
     np.testing.assert_array_equal(o1, o2)
+
+
+# ------------------------------------------------- fused decode at a block boundary
+def _bf16_round(x):
+    """Round-to-nearest-even of float64 values to bf16 (through fp32), as stored values."""
+    return W.value(W.store(np.asarray(x, dtype=np.float32), "bf16"))
+
+
+@pytest.mark.parametrize("dtype,B,H,d,HI,dI,n_prev,k,m", [
+    ("f32", 1, 8, 64, 4, 32, 511, 64, 4),          # the 2K fp32 shape: the block of tokens 2044..2047
+    ("bf16", 2, 128, 512, 64, 128, 4095, 1024, 4),  # 64K shape, two sequences at 16K tokens
+])
+def test_decode_compresses_the_completed_block(dtype, B, H, d, HI, dI, n_prev, k, m):
+    """A decode step at t with t + 1 = m * (n_prev + 1): csa_decode's kv_job and key_job
+    write entry n_prev (the block just completed) into the KV cache and the index keys,
+    then the indexer (n_entries counting the new entry), top-k and MQA run over it.
+    Checked against the oracle chain compress -> index -> top-k -> MQA, with the
+    oracle's own compressed rows (rounded as the cache stores them).  The new entry is
+    made to rank first, so a step that skipped the job could not pass."""
+    rng = np.random.default_rng(900 + d)
+    window, t = 128, m * (n_prev + 1) - 1
+    cap = n_prev + 8
+    tok0 = m * (n_prev - 1)                  # token rows [tok0, tok0 + 2m): the entry's two blocks
+    st = "f32" if dtype == "f32" else "bf16"
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    kv = W.store(rng.standard_normal((B, cap, d)).astype(np.float32), st)
+    kI = W.store(rng.standard_normal((B, cap, dI)).astype(np.float32), st)
+    q = W.store(rng.standard_normal((B, H, d)).astype(np.float32), st)
+    qI = W.store(rng.standard_normal((B, HI, dI)).astype(np.float32), st)
+    w = rng.random((B, HI)).astype(np.float32)
+    # index-key token rows aligned with the queries' head-weighted mean: the new key scores highest
+    lead = np.einsum("bh,bhi->bi", w, W.value(qI)).astype(np.float32)
+    lead /= np.linalg.norm(lead, axis=1, keepdims=True)
+    AI = W.store(rng.standard_normal((B, 2 * m, dI)).astype(np.float32) * 0.3 + 8.0 * lead[:, None], st)
+    BI = W.store(rng.standard_normal((B, 2 * m, dI)).astype(np.float32) * 0.3 + 8.0 * lead[:, None], st)
+    A = W.store(rng.standard_normal((B, 2 * m, d)).astype(np.float32), st)
+    Bs = W.store(rng.standard_normal((B, 2 * m, d)).astype(np.float32), st)
+    z = rng.standard_normal((B, 2 * m)).astype(np.float32)
+    zI = rng.standard_normal((B, 2 * m)).astype(np.float32)
+    kv_raw = W.store(rng.standard_normal((B, window, d)).astype(np.float32), st)
+    raw_base = np.full(B, t - window + 1, np.int32)
+    kvt, kIt = dev(kv), dev(kI)
+    kvt[:, n_prev:] = 0          # the entry is absent before the step
+    kIt[:, n_prev:] = 0
+    jobs = [csa.compress_job(dev(A), dev(Bs), dev(z), dev(z), m, kvt, tok_base=tok0, entry_begin=n_prev,
+                             entry_end=n_prev + 1),
+            csa.compress_job(dev(AI), dev(BI), dev(zI), dev(zI), m, kIt, tok_base=tok0, entry_begin=n_prev,
+                             entry_end=n_prev + 1)]
+    dec = csa.Decoder(dev(q[:, None]), kvt, dev(kv_raw), _i32(raw_base), _i32(np.full((B, 1), t)),
+                      dev(qI[:, None]), dev(w[:, None]), kIt, _i32(np.full(B, n_prev + 1)), m=m, topk=k,
+                      window=window, kv_job=jobs[0], key_job=jobs[1], lse=torch.empty((B, 1, H), device="cuda"))
+    out, idx = dec()
+    got_kv, got_kI = host(kvt), host(kIt)
+    out, lse, idx = host(out)[:, 0], host(dec.lse)[:, 0], idx.cpu().numpy()[:, 0]
+    for b in range(B):
+        new_kv = oracle.compress(W.value(A[b]), W.value(Bs[b]), z[b], z[b], m, tok_base=tok0, entry_begin=n_prev,
+                                 entry_end=n_prev + 1)
+        new_kI = oracle.compress(W.value(AI[b]), W.value(BI[b]), zI[b], zI[b], m, tok_base=tok0,
+                                 entry_begin=n_prev, entry_end=n_prev + 1)
+        if dtype == "f32":
+            assert_f32_close(got_kv[b, n_prev], new_kv[0], "new KV entry")
+            assert_f32_close(got_kI[b, n_prev], new_kI[0], "new index key")
+            kv_o = np.concatenate([W.value(kv[b, :n_prev]), new_kv])
+            kI_o = np.concatenate([W.value(kI[b, :n_prev]), new_kI])
+        else:   # stored as bf16: the oracle's value rounded, within one bf16 unit of the GPU's
+            kv_o = np.concatenate([W.value(kv[b, :n_prev]), _bf16_round(new_kv)])
+            kI_o = np.concatenate([W.value(kI[b, :n_prev]), _bf16_round(new_kI)])
+            for g, o in ((got_kv[b, n_prev], kv_o[n_prev]), (got_kI[b, n_prev], kI_o[n_prev])):
+                assert np.all(np.abs(g - o) <= np.abs(o) * 2.0 ** -7 + 1e-30), "new entry beyond one bf16 unit"
+        assert np.all(got_kv[b, n_prev + 1:] == 0) and np.all(got_kI[b, n_prev + 1:] == 0)
+        scores = oracle.index_scores(W.value(qI[b]), w[b], kI_o)
+        V = oracle.visible(t, n_prev + 1, m)
+        assert V == n_prev + 1
+        assert int(np.argmax(scores)) == n_prev, "the new entry must rank first"
+        check_topk_row(idx[b], scores, V, k, "seq %d" % b)
+        assert n_prev in idx[b]
+        want, wl = oracle.sparse_mqa(W.value(q[b]), kv_o, idx[b], W.value(kv_raw[b]), int(raw_base[b]), t, window,
+                                     1 / np.sqrt(d), 1e-6)
+        if dtype == "f32":
+            assert_f32_close(out[b], want, "out")
+            assert_f32_close(lse[b], wl, "lse")
+        else:
+            assert_bf16_close(out[b], want, "out")
+            np.testing.assert_allclose(lse[b], wl, rtol=0, atol=2e-3)

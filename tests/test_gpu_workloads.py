@@ -9,7 +9,8 @@ import oracle
 from long_context_compressed_04_amd import csa
 from long_context_compressed_04_amd import workloads as W
 
-from _helpers import assert_bf16_close, assert_f32_close, check_topk_row, dev, host, recall
+from _helpers import (BF16_LSE_ATOL, assert_bf16_close, assert_f32_close, bf16_errors, check_topk_row, dev, host,
+                      recall)
 
 pytestmark = pytest.mark.gpu
 
@@ -25,12 +26,29 @@ def i32(x):
     return torch.as_tensor(np.asarray(x, dtype=np.int32)).cuda()
 
 
-def oracle_attend_selected(q, kv_store, idx, kv_raw, raw_base, t, window, scale, eps):
-    """oracle.sparse_mqa on the rows idx selects (passing only those rows)."""
+def oracle_attend_selected(q, kv_store, idx, kv_raw, raw_base, t, window, scale, eps, values=None):
+    """oracle.sparse_mqa on the rows idx selects (passing only those rows); `values`
+    maps storage rows to their values (default: the stored bf16 / fp32 values)."""
+    values = W.value if values is None else values
     sel = idx[idx >= 0]
-    sub = W.value(kv_store[sel])
+    sub = values(kv_store[sel])
     idx_sub = np.where(idx >= 0, np.cumsum(idx >= 0) - 1, -1).astype(np.int32)
-    return oracle.sparse_mqa(q, sub, idx_sub, W.value(kv_raw), raw_base, t, window, scale, eps)
+    return oracle.sparse_mqa(q, sub, idx_sub, values(kv_raw), raw_base, t, window, scale, eps)
+
+
+def check_bf16_out(got, want, got_lse, want_lse, what):
+    """The bf16 output rule plus the natural-log denominators; prints the margins."""
+    err, rel_max, rel_l2 = bf16_errors(got, want)
+    lse_err = float(np.max(np.abs(got_lse - want_lse)))
+    print("%s: max err %.3g (bar 2e-2), %.3g of max|o| = %.3g, rel L2 %.3g, lse err %.3g"
+          % (what, err, rel_max, float(np.max(np.abs(want))), rel_l2, lse_err))
+    assert_bf16_close(got, want, what)
+    assert lse_err <= BF16_LSE_ATOL, "%s: lse err %.3g > %.1g" % (what, lse_err, BF16_LSE_ATOL)
+
+
+def _bf16_round(x):
+    """float64 values rounded (through fp32, to nearest even) to bf16 storage values."""
+    return W.value(W.store(np.asarray(x, dtype=np.float32), "bf16"))
 
 
 def fp8_codes(x):
@@ -71,16 +89,17 @@ def test_csa_decode_64k_full():
     c = W.cfg2()
     dec = csa.Decoder(dev(c["q"][:, None]), dev(c["kv"]), dev(c["kv_raw"]), i32(c["raw_base"]),
                       i32(c["q_pos"][:, None]), dev(c["qI"][:, None]), dev(c["w"][:, None]), dev(c["kI"]),
-                      i32(c["n_entries"]), m=4, topk=1024, window=128)
+                      i32(c["n_entries"]), m=4, topk=1024, window=128,
+                      lse=torch.empty((8, 1, 128), dtype=torch.float32, device="cuda"))
     out, idx = dec()
-    out, idx = host(out)[:, 0], idx.cpu().numpy()[:, 0]
+    out, lse, idx = host(out)[:, 0], host(dec.lse)[:, 0], idx.cpu().numpy()[:, 0]
     swaps = 0
     for b in range(8):
         scores = oracle.index_scores(W.value(c["qI"][b]), c["w"][b], W.value(c["kI"][b]))
         swaps += check_topk_row(idx[b], scores, 16384, 1024, "seq %d" % b)
-        want, _ = oracle_attend_selected(W.value(c["q"][b]), c["kv"][b], idx[b], c["kv_raw"][b],
-                                         int(c["raw_base"][b]), int(c["q_pos"][b]), 128, c["scale"], c["eps"])
-        assert_bf16_close(out[b], want, "seq %d out" % b)
+        want, wl = oracle_attend_selected(W.value(c["q"][b]), c["kv"][b], idx[b], c["kv_raw"][b],
+                                          int(c["raw_base"][b]), int(c["q_pos"][b]), 128, c["scale"], c["eps"])
+        check_bf16_out(out[b], want, lse[b], wl, "seq %d out" % b)
     print("tie swaps:", swaps)
 
 
@@ -89,11 +108,11 @@ def test_hca_decode_1m_full():
     c = W.cfg3()
     out, lse = csa.hca_dense_mqa(dev(c["q"][:, None]), dev(c["kv"]), i32(c["n_entries"]), dev(c["kv_raw"]),
                                  i32(c["raw_base"]), i32(c["q_pos"][:, None]), m=128, window=128)
-    out = host(out)[:, 0]
+    out, lse = host(out)[:, 0], host(lse)[:, 0]
     for b in range(4):
-        want, _ = oracle.dense_mqa(W.value(c["q"][b]), W.value(c["kv"][b]), 8192, 128, W.value(c["kv_raw"][b]),
-                                   int(c["raw_base"][b]), int(c["q_pos"][b]), 128, c["scale"], c["eps"])
-        assert_bf16_close(out[b], want, "seq %d" % b)
+        want, wl = oracle.dense_mqa(W.value(c["q"][b]), W.value(c["kv"][b]), 8192, 128, W.value(c["kv_raw"][b]),
+                                    int(c["raw_base"][b]), int(c["q_pos"][b]), 128, c["scale"], c["eps"])
+        check_bf16_out(out[b], want, lse[b], wl, "seq %d" % b)
 
 
 def test_csa_decode_1m_fp4_full():
@@ -108,9 +127,9 @@ def test_csa_decode_1m_fp4_full():
     np.testing.assert_array_equal(kc.cpu().numpy()[0], oc)
     dec = csa.Decoder(dev(c["q"][:, None]), dev(c["kv"]), dev(c["kv_raw"]), i32(c["raw_base"]),
                       i32(c["q_pos"][:, None]), qc, dev(c["w"][:, None]), kc, i32(c["n_entries"]), m=4, topk=1024,
-                      window=128, q_scale=qs, k_scale=ks)
+                      window=128, q_scale=qs, k_scale=ks, lse=torch.empty((1, 1, 128), device="cuda"))
     out, idx = dec()
-    out, idx = host(out)[0, 0], idx.cpu().numpy()[0, 0]
+    out, lse, idx = host(out)[0, 0], host(dec.lse)[0, 0], idx.cpu().numpy()[0, 0]
     q_deq = oracle.mxfp4_dequantize(*oracle.mxfp4_quantize(c["qI"][0]))
     k_deq = oracle.mxfp4_dequantize(oc, os_)
     s_q = oracle.index_scores(q_deq, c["w"][0], k_deq)
@@ -120,9 +139,9 @@ def test_csa_decode_1m_fp4_full():
     r = recall(idx, ref)
     print("MXFP4 top-1024 recall vs fp32 indexer: %.4f" % r)
     assert r > 0.5
-    want, _ = oracle_attend_selected(W.value(c["q"][0]), c["kv"][0], idx, c["kv_raw"][0], int(c["raw_base"][0]),
-                                     int(c["q_pos"][0]), 128, c["scale"], c["eps"])
-    assert_bf16_close(out, want, "out")
+    want, wl = oracle_attend_selected(W.value(c["q"][0]), c["kv"][0], idx, c["kv_raw"][0], int(c["raw_base"][0]),
+                                      int(c["q_pos"][0]), 128, c["scale"], c["eps"])
+    check_bf16_out(out, want, lse, wl, "out")
 
 
 def test_csa_decode_1m_fp4_rescored_recall():
@@ -168,31 +187,33 @@ def test_csa_prefill_4k_on_60k_sampled():
     new_kI = oracle.compress(W.value(c["AI"]), W.value(c["BI"]), c["zI"], c["zI"], 4, tok_base=tb, entry_begin=P,
                              entry_end=N)
     kv_h, kI_h = host(kv)[0], host(kI)[0]
-    assert_bf16_close(kv_h[P:], new_kv, "compressed entries")
-    assert_bf16_close(kI_h[P:], new_kI, "compressed index keys")
+    # the caches the oracle works on: the prior entries as given, the new ones from its
+    # own compression, rounded as the cache stores them (bf16, nearest even); the GPU's
+    # stored entries must lie within one bf16 unit of those
+    kv_o = np.concatenate([W.value(c["kv_prior"]), _bf16_round(new_kv)])
+    kI_o = np.concatenate([W.value(c["kI_prior"]), _bf16_round(new_kI)])
+    for g, o, what in ((kv_h, kv_o, "compressed entries"), (kI_h, kI_o, "compressed index keys")):
+        assert np.all(np.abs(g[P:] - o[P:]) <= np.abs(o[P:]) * 2.0 ** -7), what + ": beyond one bf16 unit"
+        print("%s: %d of %d values differ from the oracle's by one bf16 unit" % (what, int(np.sum(g[P:] != o[P:])),
+                                                                                  g[P:].size))
     Q = c["n_new"]
     q_pos = i32(c["q_pos"][None])
     n_entries = i32([N])
     idx, _ = csa.index_topk(dev(c["qI"][None]), dev(c["w"][None]), kI, n_entries, q_pos, m=4, topk=1024)
-    out, _ = csa.sparse_mqa(dev(c["q"][None]), kv, idx, dev(c["kv_raw"][None]), i32([c["raw_base"]]), q_pos,
-                            window=128)
+    out, lse = csa.sparse_mqa(dev(c["q"][None]), kv, idx, dev(c["kv_raw"][None]), i32([c["raw_base"]]), q_pos,
+                              window=128)
     torch.cuda.synchronize()
     idx = idx.cpu().numpy()[0]
-    sample = sorted(set([0, 1, 2, Q - 2, Q - 1] + list(range(97, Q, 331))))
-    # the oracle works on the bf16 caches as the GPU holds them (its own compression
-    # of the new blocks matched above to bf16 rounding)
-    keys_v = kI_h
+    out_h, lse_h = host(out)[0], host(lse)[0]
+    sample = sorted(set([0, 1, 2, 3, 511, 512, 1023, 1024, Q - 3, Q - 2, Q - 1] + list(range(97, Q, 113))))
     for i in sample:
         t = int(c["q_pos"][i])
         V = oracle.visible(t, N, 4)
-        scores = oracle.index_scores(W.value(c["qI"][i]), c["w"][i], keys_v[:V])
+        scores = oracle.index_scores(W.value(c["qI"][i]), c["w"][i], kI_o[:V])
         check_topk_row(idx[i], scores, V, 1024, "query %d" % i)
-        sel = idx[i][idx[i] >= 0]
-        sub = kv_h[sel]
-        idx_sub = np.arange(len(sel), dtype=np.int32)
-        want, _ = oracle.sparse_mqa(W.value(c["q"][i]), sub, idx_sub, W.value(c["kv_raw"]), c["raw_base"], t, 128,
-                                    c["scale"], c["eps"])
-        assert_bf16_close(host(out[0, i]), want, "query %d out" % i)
+        want, wl = oracle.sparse_mqa(W.value(c["q"][i]), kv_o, idx[i], W.value(c["kv_raw"]), c["raw_base"], t, 128,
+                                     c["scale"], c["eps"])
+        check_bf16_out(out_h[i], want, lse_h[i], wl, "query %d out" % i)
 
 
 def test_csa_decode_64k_full_fp8_cache():
@@ -203,15 +224,64 @@ def test_csa_decode_64k_full_fp8_cache():
     raw8 = fp8_codes(W.value(c["kv_raw"]))
     dec = csa.Decoder(dev(c["q"][:, None]), torch.from_numpy(kv8).cuda(), torch.from_numpy(raw8).cuda(),
                       i32(c["raw_base"]), i32(c["q_pos"][:, None]), dev(c["qI"][:, None]), dev(c["w"][:, None]),
-                      dev(c["kI"]), i32(c["n_entries"]), m=4, topk=1024, window=128)
+                      dev(c["kI"]), i32(c["n_entries"]), m=4, topk=1024, window=128,
+                      lse=torch.empty((8, 1, 128), device="cuda"))
     out, idx = dec()
-    out, idx = host(out)[:, 0], idx.cpu().numpy()[:, 0]
+    out, lse, idx = host(out)[:, 0], host(dec.lse)[:, 0], idx.cpu().numpy()[:, 0]
     for b in range(8):
         scores = oracle.index_scores(W.value(c["qI"][b]), c["w"][b], W.value(c["kI"][b]))
         check_topk_row(idx[b], scores, 16384, 1024, "seq %d" % b)
         sel = idx[b][idx[b] >= 0]
         idx_sub = np.where(idx[b] >= 0, np.cumsum(idx[b] >= 0) - 1, -1).astype(np.int32)
-        want, _ = oracle.sparse_mqa(W.value(c["q"][b]), oracle.fp8_dequantize(kv8[b][sel]), idx_sub,
-                                    oracle.fp8_dequantize(raw8[b]), int(c["raw_base"][b]), int(c["q_pos"][b]), 128,
-                                    c["scale"], c["eps"])
-        assert_bf16_close(out[b], want, "seq %d out" % b)
+        want, wl = oracle.sparse_mqa(W.value(c["q"][b]), oracle.fp8_dequantize(kv8[b][sel]), idx_sub,
+                                     oracle.fp8_dequantize(raw8[b]), int(c["raw_base"][b]), int(c["q_pos"][b]), 128,
+                                     c["scale"], c["eps"])
+        check_bf16_out(out[b], want, lse[b], wl, "seq %d out" % b)
+
+
+# --------------------------------------------- structured full-size edge cases
+def _structure(c, rng, key):
+    """Per-row scale factors in [1/4, 4] (log-uniform) on every cache row, so that the
+    RMSNorm of the attended rows changes the result; in the first sequence every query
+    head equals one window row (the window dominates its softmax), in the second every
+    head equals one compressed entry."""
+    kv, raw = W.value(c[key]), W.value(c["kv_raw"])
+    kv = kv * np.exp(rng.uniform(np.log(0.25), np.log(4.0), kv.shape[:2]))[..., None]
+    raw = raw * np.exp(rng.uniform(np.log(0.25), np.log(4.0), raw.shape[:2]))[..., None]
+    q = W.value(c["q"]).copy()
+    q[0] = raw[0, 100 + np.arange(q.shape[1]) % 20]
+    q[1] = kv[1, 37 + 5 * np.arange(q.shape[1])]
+    return W.store(q.astype(np.float32), "bf16"), W.store(kv.astype(np.float32), "bf16"), \
+        W.store(raw.astype(np.float32), "bf16")
+
+
+def test_hca_decode_1m_structured():
+    """The 1M-token HCA workload with scaled rows and queries equal to a window row or
+    to a compressed entry: out and lse against the oracle for every sequence."""
+    c = W.cfg3()
+    q, kv, raw = _structure(c, np.random.default_rng(77), "kv")
+    out, lse = csa.hca_dense_mqa(dev(q[:, None]), dev(kv), i32(c["n_entries"]), dev(raw), i32(c["raw_base"]),
+                                 i32(c["q_pos"][:, None]), m=128, window=128)
+    out, lse = host(out)[:, 0], host(lse)[:, 0]
+    for b in range(4):
+        want, wl = oracle.dense_mqa(W.value(q[b]), W.value(kv[b]), 8192, 128, W.value(raw[b]), int(c["raw_base"][b]),
+                                    int(c["q_pos"][b]), 128, c["scale"], c["eps"])
+        check_bf16_out(out[b], want, lse[b], wl, "structured seq %d" % b)
+
+
+def test_csa_decode_64k_structured():
+    """The 64K CSA workload (fused call) with scaled rows and queries equal to a window
+    row or to a compressed entry."""
+    c = W.cfg2()
+    q, kv, raw = _structure(c, np.random.default_rng(78), "kv")
+    dec = csa.Decoder(dev(q[:, None]), dev(kv), dev(raw), i32(c["raw_base"]), i32(c["q_pos"][:, None]),
+                      dev(c["qI"][:, None]), dev(c["w"][:, None]), dev(c["kI"]), i32(c["n_entries"]), m=4,
+                      topk=1024, window=128, lse=torch.empty((8, 1, 128), device="cuda"))
+    out, idx = dec()
+    out, lse, idx = host(out)[:, 0], host(dec.lse)[:, 0], idx.cpu().numpy()[:, 0]
+    for b in range(8):
+        scores = oracle.index_scores(W.value(c["qI"][b]), c["w"][b], W.value(c["kI"][b]))
+        check_topk_row(idx[b], scores, 16384, 1024, "seq %d" % b)
+        want, wl = oracle_attend_selected(W.value(q[b]), kv[b], idx[b], raw[b], int(c["raw_base"][b]),
+                                          int(c["q_pos"][b]), 128, c["scale"], c["eps"])
+        check_bf16_out(out[b], want, lse[b], wl, "structured seq %d" % b)

@@ -434,17 +434,17 @@ def test_fp8_round_trip_and_error_bound():
 
 # --------------------------------------------------------- rope-conjugate output
 def _rope_cs(theta):
-    """cos and sin per rope dim: the 32 pair angles repeated over both halves."""
-    th = np.concatenate([theta, theta])
+    """cos and sin per rope dim: each of the 32 pair angles on both dims of its pair."""
+    th = np.repeat(theta, 2)
     return np.concatenate([np.cos(th), np.sin(th)])
 
 
 def _rotate_complex(x, theta):
-    """RoPE of the trailing 64 dims written as complex multiplication: the pair
-    (x_i, x_{i+32}) is x_i + 1j x_{i+32}, multiplied by exp(1j theta_i)."""
+    """RoPE of the trailing 64 dims written as complex multiplication: the interleaved
+    pair (x_{2j}, x_{2j+1}) is x_{2j} + 1j x_{2j+1}, multiplied by exp(1j theta_j)."""
     y = np.array(x, dtype=np.float64)
-    z = (y[..., -64:-32] + 1j * y[..., -32:]) * np.exp(1j * theta)
-    y[..., -64:-32], y[..., -32:] = z.real, z.imag
+    z = (y[..., -64::2] + 1j * y[..., -63::2]) * np.exp(1j * theta)
+    y[..., -64::2], y[..., -63::2] = z.real, z.imag
     return y
 
 
@@ -460,13 +460,18 @@ def test_rope_conjugate_undoes_the_rotation():
 
 
 def test_rope_conjugate_quarter_turn_by_hand():
-    """theta = pi/2 (cos 0, sin 1): (a, b) pairs map to (b, -a)."""
+    """theta = pi/2 (cos 0, sin 1): the conjugate turns each interleaved pair (a, b)
+    into (b, -a); a perturbation of one rotated dim moves that dim's pair only."""
     x = np.arange(2 * 96, dtype=np.float64).reshape(2, 96) + 1
     cs = np.concatenate([np.zeros(64), np.ones(64)])
     y = oracle.rope_conjugate(x, cs)
     np.testing.assert_array_equal(y[:, :32], x[:, :32])
-    np.testing.assert_array_equal(y[:, 32:64], x[:, 64:96])
-    np.testing.assert_array_equal(y[:, 64:96], -x[:, 32:64])
+    np.testing.assert_array_equal(y[:, 32::2], x[:, 33::2])
+    np.testing.assert_array_equal(y[:, 33::2], -x[:, 32::2])
+    x2 = x.copy()
+    x2[:, 32] += 1.0
+    moved = np.nonzero(np.any(oracle.rope_conjugate(x2, cs) != y, axis=0))[0]
+    np.testing.assert_array_equal(moved, [33])
 
 
 def test_rope_conjugate_of_attention_over_rotated_inputs():
