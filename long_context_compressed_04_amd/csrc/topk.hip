@@ -33,6 +33,7 @@
 #include "csa_device.hpp"
 #include "csa_kernels.hpp"
 #include "launch_timer.hpp"
+#include "select_device.hpp"
 
 namespace csa {
 
@@ -68,38 +69,6 @@ struct SelShared {
 };
 
 __device__ __forceinline__ int hslot(int b) { return b + (b >> 5); }
-
-__device__ __forceinline__ float key_to_float(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
-}
-
-__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-}
-
-// Cross-lane steps on DPP (data-parallel primitives: a VALU operand read from another
-// lane of the same 16-lane row, a few cycles) rather than LDS permutes.
-constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
-constexpr int kDppRowRor1 = 0x121, kDppRowRor2 = 0x122, kDppRowRor4 = 0x124, kDppRowRor8 = 0x128;
-constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
-
-// v of lane src(CTRL) for lanes in ROW_MASK rows, 0 elsewhere and for lanes with no source
-template <int CTRL, int ROW_MASK = 0xF>
-__device__ __forceinline__ uint32_t dpp0(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, true);
-}
-
-// Inclusive prefix sum over the 64 lanes: within rows by shifts 1, 2, 4, 8, then row
-// totals carried across rows (lane 15 into rows 1 and 3, lane 31 into rows 2 and 3).
-__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
-  v += dpp0<kDppRowShr1>(v);
-  v += dpp0<kDppRowShr2>(v);
-  v += dpp0<kDppRowShr4>(v);
-  v += dpp0<kDppRowShr8>(v);
-  v += dpp0<kDppRowBcast15, 0xA>(v);
-  v += dpp0<kDppRowBcast31, 0xC>(v);
-  return v;
-}
 
 // Minimum and maximum over the 64 lanes (uniform results): within rows by rotations,
 // then over the four row results.
@@ -204,6 +173,128 @@ __device__ __forceinline__ void radix_passes(HistKeys hist_keys, Bucket bucket, 
 template <int KPT>
 __device__ __forceinline__ bool valid_pos(int j, int n) { return KPT * (int)threadIdx.x + j < n; }
 
+// A bucket of cnt <= 64 keys (those with in(j)) holding the need-th largest key of the
+// selection: gathered into LDS, then one wave finds that key exactly, bit by bit from
+// the highest bit of `undecided` down, with ballots; ties with it are taken in
+// position order later.  Leaves the key in sh.s_prefix and the number of keys equal
+// to it still to take in sh.s_need.  Contains barriers: call from every thread.
+template <int KPT, class In>
+__device__ __forceinline__ void resolve_bucket(const uint32_t (&key)[KPT], int n, In in, uint32_t need, uint32_t cnt,
+                                               uint32_t undecided, SelShared& sh) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const bool hit = valid_pos<KPT>(j, n) && in(j);
+    const uint64_t bm = __ballot(hit);
+    if (bm) {   // uniform: one slot reservation per wave and round
+      uint32_t base = 0;
+      if (lane == (int)__builtin_ctzll(bm)) base = atomicAdd(&sh.bcount, (uint32_t)__popcll(bm));
+      base = (uint32_t)__builtin_amdgcn_readlane((int)base, (int)__builtin_ctzll(bm));
+      if (hit) sh.bkey[base + lanes_below(bm)] = key[j];
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const uint32_t kl = (uint32_t)lane < cnt ? sh.bkey[lane] : 0u;
+    bool cand = (uint32_t)lane < cnt;
+    uint32_t rem = need;
+    for (int bit = undecided ? 31 - __clz((int)undecided) : -1; bit >= 0; --bit) {
+      const uint64_t ones = __ballot(cand && ((kl >> bit) & 1u));
+      const uint32_t c1 = (uint32_t)__popcll(ones);
+      const bool take_ones = rem <= c1;
+      if (!take_ones) rem -= c1;
+      cand = cand && (((kl >> bit) & 1u) == (take_ones ? 1u : 0u));
+    }
+    const uint64_t left = __ballot(cand);
+    if (lane == (int)__builtin_ctzll(left)) {
+      sh.s_prefix = kl;
+      sh.s_need = rem;
+    }
+  }
+  __syncthreads();
+}
+
+// Single-histogram selection for rows held in registers.  kBins equal-width bins span
+// the row's smallest to largest score (a monotone map: every key in a higher bin is
+// larger).  On scores with a smooth distribution the bin of the k-th largest holds a
+// handful of keys; they are gathered, and one wave ranks them exactly.  Returns false
+// (with nothing written and the LDS reusable) when that bin holds more than
+// kBucketMax keys or the value range cannot be binned; the caller then runs the radix
+// passes.  On success: every key > T and the first `need` keys == T (position order)
+// are the k largest.  The caller zeroes sh.hist and sh.bcount before its first
+// barrier.  Requires 1 <= k <= n.  Contains barriers: call from every thread.
+template <int KPT>
+__device__ __forceinline__ bool threshold_one_pass(const uint32_t (&key)[KPT], int n, uint32_t k, SelShared& sh,
+                                                   uint32_t& T, uint32_t& need) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    if (valid_pos<KPT>(j, n)) {
+      kmin = min(kmin, key[j]);
+      kmax = max(kmax, key[j]);
+    }
+  }
+  wave_minmax(kmin, kmax);
+  if (lane == 0) {
+    sh.red[wave] = kmin;
+    sh.red[kTW + wave] = kmax;
+  }
+  __syncthreads();
+  kmin = 0xffffffffu;
+  kmax = 0u;
+#pragma unroll
+  for (int w = 0; w < kTW; ++w) {
+    kmin = min(kmin, sh.red[w]);
+    kmax = max(kmax, sh.red[kTW + w]);
+  }
+  if (kmin == kmax) {   // every key equal: the first k in position order
+    T = kmin;
+    need = k;
+    return true;
+  }
+  const float lo = key_to_float(kmin), hi = key_to_float(kmax);
+  const float scale = (float)kBins / (hi - lo);
+  if (!(scale > 0.f) || !(scale < INFINITY) || !(lo > -INFINITY) || !(hi < INFINITY)) {
+    __syncthreads();   // (uniform) every wave has read sh.red before the fallback writes it
+    return false;
+  }
+  int bins[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    bins[j] = valid_pos<KPT>(j, n) ? (int)fminf((key_to_float(key[j]) - lo) * scale, (float)(kBins - 1)) : -1;
+    if (bins[j] >= 0) atomicAdd(&sh.hist[hslot(bins[j])], 1u);
+  }
+  __syncthreads();
+  pick_digit(sh, 0u, 0, k);
+  __syncthreads();
+  const int b = (int)sh.s_prefix;
+  const uint32_t nd = sh.s_need, cnt = sh.s_cnt;
+  if (cnt > (uint32_t)kBucketMax) return false;   // uniform
+  // the bin's keys (a few per thread at most)
+#pragma unroll
+  for (int j = 0; j < KPT; ++j)
+    if (bins[j] == b) sh.bkey[atomicAdd(&sh.bcount, 1u)] = key[j];
+  __syncthreads();
+  if (threadIdx.x < 64) {   // rank each bucket key among the others: the nd-th largest is T
+    const uint32_t mine = (uint32_t)lane < cnt ? sh.bkey[lane] : 0u;
+    uint32_t gt = 0, eq = 0;
+    for (int j = 0; j < (int)cnt; ++j) {   // (cnt is uniform: the other keys by lane broadcast)
+      const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)mine, j);
+      gt += o > mine ? 1u : 0u;
+      eq += o == mine ? 1u : 0u;
+    }
+    if ((uint32_t)lane < cnt && gt < nd && nd <= gt + eq) {   // the lanes holding T (same values)
+      sh.s_prefix = mine;
+      sh.s_need = nd - gt;
+    }
+  }
+  __syncthreads();
+  T = sh.s_prefix;
+  need = sh.s_need;
+  return true;
+}
+
 // Finds (prefix, mask, need): the k largest of the n keys are every key with
 // (key & mask) > prefix plus the first `need` keys (in position order) with
 // (key & mask) == prefix.  Requires 1 <= k <= n.  ONE_PASS: stop after the first
@@ -233,44 +324,11 @@ __device__ __forceinline__ void reg_threshold(const uint32_t (&key)[KPT], int n,
       if (valid_pos<KPT>(j, n) && (key[j] & msk) == pre) atomicAdd(&sh.hist[hslot((key[j] >> shift) & dmask)], 1u);
     }
   };
-  // a bucket of <= 64 keys: gather it, and let one wave find the need-th largest
-  // key exactly, bit by bit; ties with it are taken in position order later
+  // a bucket of <= 64 keys: resolved exactly by one wave
   bool resolved = false;
   auto bucket = [&](uint32_t pre, uint32_t msk, uint32_t nd, uint32_t cnt) {
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const bool in = valid_pos<KPT>(j, n) && (key[j] & msk) == pre;
-      const uint64_t bm = __ballot(in);
-      if (bm) {   // uniform: one slot reservation per wave and round
-        uint32_t base = 0;
-        if (lane == (int)__builtin_ctzll(bm)) base = atomicAdd(&sh.bcount, (uint32_t)__popcll(bm));
-        base = (uint32_t)__builtin_amdgcn_readlane((int)base, (int)__builtin_ctzll(bm));
-        if (in) {
-          const uint32_t p = base + lanes_below(bm);
-          sh.bkey[p] = key[j];
-        }
-      }
-    }
-    __syncthreads();
-    if (threadIdx.x < 64) {
-      // bitwise MSB-first selection over the undecided low bits, with ballots
-      const uint32_t kl = (uint32_t)lane < cnt ? sh.bkey[lane] : 0u;
-      bool cand = (uint32_t)lane < cnt;
-      uint32_t rem = nd;
-      for (int bit = 31 - __clz((int)~msk); bit >= 0; --bit) {
-        const uint64_t ones = __ballot(cand && ((kl >> bit) & 1u));
-        const uint32_t c1 = (uint32_t)__popcll(ones);
-        const bool take_ones = rem <= c1;
-        if (!take_ones) rem -= c1;
-        cand = cand && (((kl >> bit) & 1u) == (take_ones ? 1u : 0u));
-      }
-      const uint64_t left = __ballot(cand);
-      if (lane == (int)__builtin_ctzll(left)) {
-        sh.s_prefix = kl;
-        sh.s_need = rem;
-      }
-    }
-    __syncthreads();
+    auto in = [&](int j) { return (key[j] & msk) == pre; };
+    resolve_bucket<KPT>(key, n, in, nd, cnt, ~msk, sh);
     resolved = true;
     return true;
   };
@@ -438,16 +496,24 @@ __device__ __forceinline__ void load_row(const float* src, int n, uint32_t (&key
   }
 }
 
+// The caller zeroes sh.hist and sh.bcount before its first barrier (threshold_one_pass).
 template <int KPT>
 __device__ __forceinline__ void select_reg_row(uint32_t (&key)[KPT], int V, int k, int32_t* oi, float* os,
                                                SelShared& sh, const int32_t* map = nullptr) {
-  uint32_t prefix, mask, need;
-  reg_threshold<KPT>(key, V, (uint32_t)k, sh, prefix, mask, need);
   auto idx_of = [map](int j) {
     const int p = KPT * (int)threadIdx.x + j;
     return map ? map[p] : p;
   };
+  uint32_t prefix, mask = 0xffffffffu, need;
+  if (!threshold_one_pass<KPT>(key, V, (uint32_t)k, sh, prefix, need))
+    reg_threshold<KPT>(key, V, (uint32_t)k, sh, prefix, mask, need);
   reg_compact<KPT>(key, V, prefix, mask, need, k, idx_of, oi, os, sh);
+}
+
+// Zeroes the histogram and the bucket counter (before the caller's first barrier).
+__device__ __forceinline__ void clear_select_lds(SelShared& sh) {
+  for (int i = threadIdx.x; i < kHistWords; i += kTopkThreads) sh.hist[i] = 0u;
+  if (threadIdx.x == 0) sh.bcount = 0u;
 }
 
 // ---- rows of up to KPT * 1024 entries: one workgroup per row
@@ -461,6 +527,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(IndexArgs A, co
   // it are never counted)
   uint32_t key[KPT];
   load_row<KPT>(src, A.n_max, key);
+  clear_select_lds(sh);
   const int V = row_visible(A, row);
   const int k = A.topk;
   int32_t* oi = out_idx + row * k;
@@ -605,9 +672,11 @@ __device__ __forceinline__ void select_candidates(const uint32_t (&spk)[kSpec], 
     key[j] = c < M ? sh.stage[c] : 0u;
   }
   // (the staging area is next written by the compaction, after the threshold's barriers)
-  uint32_t prefix, mask, need;
-  reg_threshold<KPT>(key, M, (uint32_t)k, sh, prefix, mask, need);
   auto idx_of = [&](int j) { return cand_idx[KPT * threadIdx.x + j]; };
+  clear_select_lds(sh);   // (the staging barrier above precedes the next one)
+  uint32_t prefix, mask = 0xffffffffu, need;
+  if (!threshold_one_pass<KPT>(key, M, (uint32_t)k, sh, prefix, need))
+    reg_threshold<KPT>(key, M, (uint32_t)k, sh, prefix, mask, need);
   reg_compact<KPT>(key, M, prefix, mask, need, k, idx_of, oi, os, sh);
 }
 
@@ -630,6 +699,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_candidates_kernel(IndexArgs
   if (V <= kRegKeys) {
     uint32_t key[kMaxKpt];
     load_row<kMaxKpt>(src, V, key);
+    clear_select_lds(sh);
     select_reg_row<kMaxKpt>(key, V, k, oi, os, sh);
     return;
   }

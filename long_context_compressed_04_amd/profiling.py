@@ -28,7 +28,8 @@ CSRC = os.path.join(PKG, "csrc")
 
 # library launch-timer name -> (regex on the demangled kernel name, source file)
 KERNELS = {
-    "index_scores_bf16": (r"index_scores_(mfma<\d+, false|lds<|pf<)", "indexer.hip"),
+    "index_scores_bf16": (r"index_scores_(mfma<\d+, false|lds<\d+, false|pf<)", "indexer.hip"),
+    "index_rescore_bf16": (r"index_scores_lds<\d+, true", "indexer.hip"),
     "index_scores_mxfp4": (r"index_scores_mfma<\d+, true", "indexer.hip"),
     "index_scores_f32": (r"index_scores_f32", "indexer.hip"),
     "topk": (r"topk_", "topk.hip"),
@@ -45,12 +46,13 @@ KERNELS = {
 }
 # the calibration copy (a torch elementwise negation of an fp32 buffer)
 CALIB_PATTERN = r"neg_kernel"
-COMMON_SOURCES = ["csa_device.hpp", "csa_kernels.hpp"]
+COMMON_SOURCES = ["csa_device.hpp", "csa_kernels.hpp", "select_device.hpp"]
 
 
 def source_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for f in [KERNELS[kernel][1]] + COMMON_SOURCES:
+    src = KERNELS[kernel][1]
+    for f in ([src] if isinstance(src, str) else list(src)) + COMMON_SOURCES:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

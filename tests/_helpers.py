@@ -2,8 +2,11 @@
 
 Tolerances (stated for the attention hot path):
   * fp32 outputs: norm-wise relative, max|gpu - oracle| <= 1e-5 * max|oracle|.
-  * bf16 outputs: max|gpu - oracle| <= 2e-2 (the stated bar for unit-scale data),
-    and, because softmax outputs over thousands of rows are far below unit scale,
+  * bf16 outputs: max|gpu - oracle| <= 2e-2 (the stated bar for unit-scale data;
+    for data whose largest value exceeds 1, e.g. an attention output dominated by
+    one normalised row, the bar scales with max|oracle|, since bf16 itself rounds a
+    value of 4 by up to 2^-7), and, because softmax outputs over thousands of rows
+    are far below unit scale,
     also relative to the oracle's own scale: max|gpu - oracle| <= 2e-2 * max|oracle|
     and ||gpu - oracle||_2 <= 1e-2 * ||oracle||_2.  A CPU model of the kernels'
     bf16 roundings at the 1M-token HCA shape gives 0.4% and 0.24% on those two
@@ -67,10 +70,22 @@ def assert_bf16_close(g, o, what=""):
     assert g.shape == o.shape, (what, g.shape, o.shape)
     assert np.all(np.isfinite(g)), what + ": non-finite GPU values"
     err, rel_max, rel_l2 = bf16_errors(g, o)
-    assert err <= BF16_ATOL, "%s: max abs err %.3g > %.1g" % (what, err, BF16_ATOL)
+    bar = BF16_ATOL * max(1.0, float(np.max(np.abs(o))) if o.size else 1.0)
+    assert err <= bar, "%s: max abs err %.3g > %.3g" % (what, err, bar)
     assert rel_max <= BF16_SCALED, "%s: max err %.3g = %.3g of max|oracle| > %.1g" % (what, err, rel_max, BF16_SCALED)
     assert rel_l2 <= BF16_REL_L2, "%s: relative L2 error %.3g > %.1g" % (what, rel_l2, BF16_REL_L2)
     return err
+
+
+def assert_stored_bf16(g, o, what="", floor=4e-6):
+    """A bf16 value the GPU computed in fp32 and stored (g) against the oracle's value
+    rounded to bf16 (o): within one bf16 unit of o, plus an absolute floor for fp32
+    rounding where the sum cancels (a pooled value near zero from terms near one)."""
+    g, o = np.asarray(g, dtype=np.float64), np.asarray(o, dtype=np.float64)
+    bad = np.abs(g - o) > np.abs(o) * 2.0 ** -7 + floor
+    assert not np.any(bad), "%s: %d values beyond one bf16 unit, e.g. gpu %r oracle %r" % (
+        what, int(bad.sum()), g[bad][:3].tolist(), o[bad][:3].tolist())
+    return int(np.sum(g != o))
 
 
 def check_topk_row(gpu_row, scores, V, k, what=""):

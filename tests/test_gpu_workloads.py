@@ -9,8 +9,8 @@ import oracle
 from long_context_compressed_04_amd import csa
 from long_context_compressed_04_amd import workloads as W
 
-from _helpers import (BF16_LSE_ATOL, assert_bf16_close, assert_f32_close, bf16_errors, check_topk_row, dev, host,
-                      recall)
+from _helpers import (BF16_LSE_ATOL, assert_bf16_close, assert_f32_close, assert_stored_bf16, bf16_errors,
+                      check_topk_row, dev, host, recall)
 
 pytestmark = pytest.mark.gpu
 
@@ -36,14 +36,34 @@ def oracle_attend_selected(q, kv_store, idx, kv_raw, raw_base, t, window, scale,
     return oracle.sparse_mqa(q, sub, idx_sub, values(kv_raw), raw_base, t, window, scale, eps)
 
 
-def check_bf16_out(got, want, got_lse, want_lse, what):
-    """The bf16 output rule plus the natural-log denominators; prints the margins."""
+def lse_bf16_query(q, rows, scale, eps):
+    """Per-head lse of attention over `rows` (fp64) with the query operand the bf16
+    kernels feed to the matrix cores: q / rms(q) rounded to bf16 and used as is (not
+    normalised again).  Where one row dominates a head (the query equals that row) this
+    rounding moves the dominant logit by scale * sum_i k_i^2 d_i (d_i the relative
+    rounding of each element), ~0.01 at 512 dims; the output is normalised by the same
+    denominator and barely moves."""
+    qh = q / np.sqrt(np.mean(q * q, axis=-1, keepdims=True) + eps)
+    qh = W.value(W.store(qh.astype(np.float32), "bf16"))
+    kn = rows / np.sqrt(np.mean(rows * rows, axis=-1, keepdims=True) + eps)
+    logit = scale * qh @ kn.T
+    mx = logit.max(axis=1, keepdims=True)
+    return (mx + np.log(np.exp(logit - mx).sum(axis=1, keepdims=True)))[:, 0]
+
+
+def check_bf16_out(got, want, got_lse, want_lse, what, lse_rounded=None):
+    """The bf16 output rule plus the natural-log denominators; prints the margins.
+    lse_rounded: lse_bf16_query of the same attention; when given, each head's lse
+    bound is 1.5 x the change that rounding alone makes, plus 2e-3, else 5e-3."""
     err, rel_max, rel_l2 = bf16_errors(got, want)
-    lse_err = float(np.max(np.abs(got_lse - want_lse)))
-    print("%s: max err %.3g (bar 2e-2), %.3g of max|o| = %.3g, rel L2 %.3g, lse err %.3g"
-          % (what, err, rel_max, float(np.max(np.abs(want))), rel_l2, lse_err))
+    lse_err = np.abs(got_lse - want_lse)
+    tol = (1.5 * np.abs(lse_rounded - want_lse) + 2e-3) if lse_rounded is not None else \
+        np.full(lse_err.shape, BF16_LSE_ATOL)
+    print("%s: max err %.3g (bar 2e-2), %.3g of max|o| = %.3g, rel L2 %.3g, lse err %.3g (largest bound %.3g)"
+          % (what, err, rel_max, float(np.max(np.abs(want))), rel_l2, float(lse_err.max()), float(tol.max())))
     assert_bf16_close(got, want, what)
-    assert lse_err <= BF16_LSE_ATOL, "%s: lse err %.3g > %.1g" % (what, lse_err, BF16_LSE_ATOL)
+    bad = lse_err > tol
+    assert not np.any(bad), "%s: lse err %.3g > %.3g" % (what, float(lse_err[bad].max()), float(tol[bad].max()))
 
 
 def _bf16_round(x):
@@ -193,9 +213,8 @@ def test_csa_prefill_4k_on_60k_sampled():
     kv_o = np.concatenate([W.value(c["kv_prior"]), _bf16_round(new_kv)])
     kI_o = np.concatenate([W.value(c["kI_prior"]), _bf16_round(new_kI)])
     for g, o, what in ((kv_h, kv_o, "compressed entries"), (kI_h, kI_o, "compressed index keys")):
-        assert np.all(np.abs(g[P:] - o[P:]) <= np.abs(o[P:]) * 2.0 ** -7), what + ": beyond one bf16 unit"
-        print("%s: %d of %d values differ from the oracle's by one bf16 unit" % (what, int(np.sum(g[P:] != o[P:])),
-                                                                                  g[P:].size))
+        n_diff = assert_stored_bf16(g[P:], o[P:], what)
+        print("%s: %d of %d values differ from the oracle's rounded value" % (what, n_diff, g[P:].size))
     Q = c["n_new"]
     q_pos = i32(c["q_pos"][None])
     n_entries = i32([N])
@@ -264,9 +283,12 @@ def test_hca_decode_1m_structured():
                                  i32(c["q_pos"][:, None]), m=128, window=128)
     out, lse = host(out)[:, 0], host(lse)[:, 0]
     for b in range(4):
-        want, wl = oracle.dense_mqa(W.value(q[b]), W.value(kv[b]), 8192, 128, W.value(raw[b]), int(c["raw_base"][b]),
-                                    int(c["q_pos"][b]), 128, c["scale"], c["eps"])
-        check_bf16_out(out[b], want, lse[b], wl, "structured seq %d" % b)
+        t, rb = int(c["q_pos"][b]), int(c["raw_base"][b])
+        want, wl = oracle.dense_mqa(W.value(q[b]), W.value(kv[b]), 8192, 128, W.value(raw[b]), rb, t, 128,
+                                    c["scale"], c["eps"])
+        rows = np.concatenate([W.value(kv[b, :8192]), W.value(raw[b, t - 127 - rb:t + 1 - rb])])
+        wl_r = lse_bf16_query(W.value(q[b]), rows, c["scale"], c["eps"])
+        check_bf16_out(out[b], want, lse[b], wl, "structured seq %d" % b, wl_r)
 
 
 def test_csa_decode_64k_structured():
@@ -282,6 +304,8 @@ def test_csa_decode_64k_structured():
     for b in range(8):
         scores = oracle.index_scores(W.value(c["qI"][b]), c["w"][b], W.value(c["kI"][b]))
         check_topk_row(idx[b], scores, 16384, 1024, "seq %d" % b)
-        want, wl = oracle_attend_selected(W.value(q[b]), kv[b], idx[b], raw[b], int(c["raw_base"][b]),
-                                          int(c["q_pos"][b]), 128, c["scale"], c["eps"])
-        check_bf16_out(out[b], want, lse[b], wl, "structured seq %d" % b)
+        t, rb = int(c["q_pos"][b]), int(c["raw_base"][b])
+        want, wl = oracle_attend_selected(W.value(q[b]), kv[b], idx[b], raw[b], rb, t, 128, c["scale"], c["eps"])
+        rows = np.concatenate([W.value(kv[b][idx[b][idx[b] >= 0]]), W.value(raw[b, t - 127 - rb:t + 1 - rb])])
+        wl_r = lse_bf16_query(W.value(q[b]), rows, c["scale"], c["eps"])
+        check_bf16_out(out[b], want, lse[b], wl, "structured seq %d" % b, wl_r)

@@ -52,6 +52,7 @@ def test_library_kernel_names():
     assert k("void csa::fp8_quantize_kernel<true>(void const*, long, unsigned char*)") == "fp8_quantize"
     assert k("void csa::index_scores_mfma<2, true, 8>(csa::IndexArgs, float*, int)") == "index_scores_mxfp4"
     assert k("void csa::index_scores_lds<2, false>(csa::IndexArgs, float*)") == "index_scores_bf16"
+    assert k("void csa::index_scores_lds<2, true>(csa::IndexArgs, float*)") == "index_rescore_bf16"
     assert k("void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel>") is None
 
 
