@@ -371,6 +371,23 @@ size_t csa_decode_workspace_size(const csa_decode_args* args);
 csa_status csa_decode(const csa_decode_args* args, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------
+ * csa_decode_noalloc -- csa_decode for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The workspace is the library's own device-resident scratch array of
+ * CSA_NOALLOC_SCRATCH_BYTES (32 MiB) on each GPU, held from the first call on that
+ * GPU until the process ends; nothing is allocated or freed by the call.  Arguments
+ * and outputs as csa_decode (the caller still passes every input and output).
+ * Returns CSA_ERR_WORKSPACE, enqueueing nothing, when csa_decode_workspace_size(args)
+ * exceeds the scratch size (csa_decode with a workspace of the caller's serves
+ * larger steps).  Every call on one GPU uses that GPU's one array, which keeps the
+ * previous call's contents (harmless: the step writes every workspace byte it reads
+ * before reading it, and keeps no counters there): calls that overlap in time on one
+ * GPU (other streams or threads) race and give undefined results; serialise them.
+ * ---------------------------------------------------------------------------- */
+#define CSA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+csa_status csa_decode_noalloc(const csa_decode_args* args, void* stream);
+
+/* ------------------------------------------------------------------------------
  * Launch timing (diagnostics; not part of the method).  csa_timing_enable(1)
  * makes the library bracket every later kernel launch with a pair of HIP events
  * recorded on the launch stream (launches on a stream that is being captured into

@@ -101,6 +101,8 @@ def lib():
         L.csa_decode_workspace_size.restype = Z
         L.csa_decode.argtypes = [ctypes.POINTER(DecodeArgs), V, Z, V]
         L.csa_decode.restype = S
+        L.csa_decode_noalloc.argtypes = [ctypes.POINTER(DecodeArgs), V]
+        L.csa_decode_noalloc.restype = S
         L.csa_timing_enable.argtypes = [ctypes.c_int32]
         L.csa_timing_enable.restype = S
         L.csa_timing_collect.argtypes = [ctypes.POINTER(KernelTime), ctypes.c_int32]
@@ -342,6 +344,12 @@ class Decoder:
 
     def __call__(self):
         _check(lib().csa_decode(ctypes.byref(self.args), _p(self.ws), self.nb, _stream(self.stream_of)))
+        return self.out, self.out_idx
+
+    def call_noalloc(self):
+        """The same step through csa_decode_noalloc: the library's own scratch array as
+        the workspace (this object's workspace is not used)."""
+        _check(lib().csa_decode_noalloc(ctypes.byref(self.args), _stream(self.stream_of)))
         return self.out, self.out_idx
 
 

@@ -169,6 +169,20 @@ csa::MqaArgs mqa_args(const csa_mqa_desc* d, int dense) {
 
 }  // namespace
 
+namespace csa {
+
+int api_fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+}  // namespace csa
+
 extern "C" {
 
 int csa_abi_version(void) { return CSA_ABI_VERSION; }

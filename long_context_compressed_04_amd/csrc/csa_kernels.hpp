@@ -60,4 +60,8 @@ struct MqaArgs {
 size_t mqa_workspace_bytes(const MqaArgs& A);
 hipError_t launch_mqa(const MqaArgs& A, void* ws, size_t ws_bytes, hipStream_t s);
 
+// Host-side helper of the C ABI for its other translation units: records the detail
+// of a failure for csa_last_error() and returns `status`.
+int api_fail(int status, const char* fmt, ...);
+
 }  // namespace csa
