@@ -75,15 +75,16 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_mfma(IndexArgs A,
   const int b = blockIdx.z;
   const int chunk0 = blockIdx.x * (kIdxWaves * TPW * 32);
   const int wave0 = chunk0 + wave * TPW * 32;
-  const int ne = min(A.n_entries[b], A.n_max);
 
-  // ---- keys for this wave's TPW tiles (registers, B operands)
+  // ---- keys for this wave's TPW tiles (registers, B operands).  Rows up to n_max lie
+  // inside the cache (n_max <= k_cap): they are loaded without waiting for the entry
+  // count, and the scores past the visible count are masked below.
   uint4 kb[TPW][KS];
   uint32_t ksc[TPW];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     const int e = wave0 + t * 32 + col;
-    const bool ok = e < ne;
+    const bool ok = e < A.n_max;
     if (FP4) {
       const uint8_t* kr = (const uint8_t*)A.k + ((long)b * A.k_cap + (ok ? e : 0)) * (kIdxDim / 2);
 #pragma unroll
@@ -98,6 +99,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_mfma(IndexArgs A,
     }
   }
 
+  const int ne = min(A.n_entries[b], A.n_max);
   const int q_begin = blockIdx.y * q_tile;
   const int q_end = min(A.n_q, q_begin + q_tile);
   for (int qi = q_begin; qi < q_end; ++qi) {
@@ -202,12 +204,19 @@ __device__ __forceinline__ void dma16(const void* g, void* l) {
 }
 
 // SEL: slot e of a row scores key row A.sel[row * n_max + e] (-1: masked) instead of e.
+// Each wave owns two 32-entry tiles.  Without SEL the key loads do not wait for
+// the entry count: rows up to n_max lie inside the cache (n_max <= k_cap), and the
+// scores past the visible count are replaced by -inf whatever the rows hold.
 template <int HB, bool SEL>
 __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_lds(IndexArgs A, float* scores) {
   constexpr int H = HB * 32;
   constexpr int RB = kIdxDim * 2;                                   // 256-byte rows
   constexpr int TPW = kIdxLdsEntries / (32 * kIdxWaves);            // tiles per wave
-  __shared__ __attribute__((aligned(16))) uint8_t k_lds[kIdxLdsEntries * RB];
+  static_assert(TPW == 2, "two key tiles per wave");
+  constexpr bool QREG = HB <= 2;   // q fragments held in registers (32 HB of them)
+  // tile t of wave w: rows 32 w .. 32 w + 31 of kt[t], entries e0 + 32 (2 w + t) ..
+  __shared__ __attribute__((aligned(16))) uint8_t kt0[32 * kIdxWaves * RB];
+  __shared__ __attribute__((aligned(16))) uint8_t kt1[32 * kIdxWaves * RB];
   __shared__ __attribute__((aligned(16))) uint8_t q_lds[H * RB];
 
   const int lane = threadIdx.x & 63;
@@ -217,72 +226,92 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_lds(IndexArgs A, 
   const int qi = blockIdx.y;
   const long row = (long)b * A.n_q + qi;
   const int e0 = blockIdx.x * kIdxLdsEntries;
-  const int ne = min(A.n_entries[b], A.n_max);
   const int32_t* sel = SEL ? A.sel + row * A.n_max : nullptr;
-  // slot e -> key row: e itself below the visible count, or the listed row; -1 = masked
+  // slot e -> key row to load: -1 = the zero row
   auto key_row = [&](int e) -> int {
     if (e >= A.n_max) return -1;
     if (SEL) return sel[e];
-    return e < ne ? e : -1;
+    return e;
   };
 
-  // ---- loads: lane l of a 1 KB instruction fills row 4 j + l / 16, slot l % 16
-  const int r_in = lane >> 4, slot = lane & 15;
-  {
-    // the listed rows are all read before the first key load is issued (one wait)
-    int krow[8 * TPW];
-#pragma unroll
-    for (int j = 0; j < 8 * TPW; ++j) krow[j] = key_row(e0 + 32 * TPW * wave + 4 * j + r_in);
-    const uint8_t* kb = (const uint8_t*)A.k + (long)b * A.k_cap * RB;
-#pragma unroll
-    for (int j = 0; j < 8 * TPW; ++j) {
-      const int r = 32 * TPW * wave + 4 * j + r_in;
-      const int kr = krow[j];
-      const uint8_t* src = kr >= 0 ? kb + (long)kr * RB + 16 * (slot ^ (r & 15)) : g_zero_key;
-      dma16(src, k_lds + (32 * TPW * wave + 4 * j) * RB);
-    }
-    const uint8_t* qg = (const uint8_t*)A.q + row * H * RB;
-#pragma unroll
-    for (int j = 0; j < H / 16; ++j) {   // H / 4 instructions over the 4 waves
-      const int hd = (H / 4) * wave + 4 * j + r_in;
-      dma16(qg + (long)hd * RB + 16 * (slot ^ (hd & 15)), q_lds + ((H / 4) * wave + 4 * j) * RB);
-    }
-  }
+  // ---- loads: the visible count, head weights, q, the keys
+  const int ne = min(A.n_entries[b], A.n_max);
+  const int V = visible_entries(A.q_pos[row], ne, A.m);
   // head weights of this lane's accumulator rows: head 32 hb + 8 (r / 4) + 4 half + r % 4
   f32x4_t wl[HB][4];
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
     for (int g = 0; g < 4; ++g) wl[hb][g] = *(const f32x4_t*)(A.w + row * H + 32 * hb + 8 * g + 4 * half);
-  const int V = visible_entries(A.q_pos[row], ne, A.m);
-  wait_vmcnt<0>();   // this wave's loads are in LDS
-  __syncthreads();
-
+  // lane l of a 1 KB instruction fills row 4 j + l / 16, slot l % 16 (chunk slot ^ (row % 16))
+  const int r_in = lane >> 4, slot = lane & 15;
+  const uint8_t* qg = (const uint8_t*)A.q + row * H * RB;
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const int r = 32 * (TPW * wave + t) + col;   // this lane's entry (B column)
-    const int e = e0 + r;
+  for (int j = 0; j < H / 16; ++j) {   // H / 4 instructions over the 4 waves
+    const int hd = (H / 4) * wave + 4 * j + r_in;
+    dma16(qg + (long)hd * RB + 16 * (slot ^ (hd & 15)), q_lds + ((H / 4) * wave + 4 * j) * RB);
+  }
+  int krow[TPW][8];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) krow[t][j] = key_row(e0 + 32 * (TPW * wave + t) + 4 * j + r_in);
+  const uint8_t* kb = (const uint8_t*)A.k + (long)b * A.k_cap * RB;
+  auto issue_tile = [&](uint8_t* kt, int t) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = 4 * j + r_in;   // row within the tile (row % 16 as in the array)
+      const int kr = krow[t][j];
+      const uint8_t* src = kr >= 0 ? kb + (long)kr * RB + 16 * (slot ^ (r & 15)) : g_zero_key;
+      dma16(src, kt + (32 * wave + 4 * j) * RB);
+    }
+  };
+  issue_tile(kt0, 0);
+  issue_tile(kt1, 1);
+  // (one wait for every load: the compiler cannot tell the LDS arrays the direct loads
+  // fill apart, and waits for all of them before the first LDS read anyway)
+  wait_vmcnt<0>();
+  __syncthreads();   // every wave's share of q
+
+  // q fragments (A operands): head 32 hb + col, 16-byte chunk 2 ks + half
+  auto q_frag = [&](int hb, int ks) {
+    const int hd = 32 * hb + col, c = 2 * ks + half;
+    return *(const uint4*)(q_lds + hd * RB + 16 * (c ^ (hd & 15)));
+  };
+  uint4 qf[QREG ? HB : 1][8];
+  if (QREG) {
+#pragma unroll
+    for (int hb = 0; hb < (QREG ? HB : 1); ++hb)
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) qf[hb][ks] = q_frag(hb, ks);
+  }
+  auto tile = [&](const uint8_t* kt, int t) {
+    const int r = 32 * wave + col;               // this lane's entry row (B column) in the array
+    const int e = e0 + 32 * (TPW * wave + t) + col;
+    f32x16_t acc[HB];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) acc[hb] = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const int c = 2 * ks + half;
+      const uint4 b4 = *(const uint4*)(kt + r * RB + 16 * (c ^ (r & 15)));
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb)
+        acc[hb] = mfma32x32x16(as_bf16x8(QREG ? qf[QREG ? hb : 0][ks] : q_frag(hb, ks)), as_bf16x8(b4), acc[hb]);
+    }
     float part = 0.f;
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
-      const int hd = 32 * hb + col;              // this lane's head (A row)
-      f32x16_t acc = {};
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const int c = 2 * ks + half;
-        const uint4 a4 = *(const uint4*)(q_lds + hd * RB + 16 * (c ^ (hd & 15)));
-        const uint4 b4 = *(const uint4*)(k_lds + r * RB + 16 * (c ^ (r & 15)));
-        acc = mfma32x32x16(as_bf16x8(a4), as_bf16x8(b4), acc);
-      }
+    for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
       for (int g = 0; g < 4; ++g)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) part = fmaf(wl[hb][g][k], fmaxf(acc[4 * g + k], 0.f), part);
-    }
+        for (int k = 0; k < 4; ++k) part = fmaf(wl[hb][g][k], fmaxf(acc[hb][4 * g + k], 0.f), part);
     part += __shfl_xor(part, 32, 64);
     const bool valid = SEL ? key_row(e) >= 0 : e < V;
     if (half == 0 && e < A.n_max) scores[row * A.n_max + e] = valid ? part : -INFINITY;
-  }
+  };
+  tile(kt0, 0);
+  tile(kt1, 1);
 }
 
 // ------------------------------------------ bf16, many queries (prefill)
@@ -342,12 +371,13 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_pf(IndexArgs A, f
   };
   if (q_begin < q_end) load_q(q_begin, 0);
 
-  // ---- keys for this wave's TPW tiles (registers, B operands)
+  // ---- keys for this wave's TPW tiles (registers, B operands); rows up to n_max lie
+  // inside the cache, so the loads do not wait for the entry count
   uint4 kb[TPW][8];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     const int e = wave0 + t * 32 + col;
-    const bool ok = e < ne;
+    const bool ok = e < A.n_max;
     const uint16_t* kr = (const uint16_t*)A.k + ((long)b * A.k_cap + (ok ? e : 0)) * kIdxDim;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) kb[t][ks] = ok ? *(const uint4*)(kr + 16 * ks + 8 * half) : make_uint4(0, 0, 0, 0);
@@ -386,27 +416,31 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_pf(IndexArgs A, f
       const int V = visible_entries(A.q_pos[row], ne, A.m);
       const uint8_t* qb = q_lds[bi][u];
       float part[TPW] = {};
+      // causal skip: every entry of this wave's tiles at or past V(t) (uniform per wave;
+      // the store writes -inf for them)
+      if (wave0 < V) {
 #pragma unroll
-      for (int hb = 0; hb < HB; ++hb) {
-        const int hd = 32 * hb + col;
-        f32x16_t acc[TPW];
+        for (int hb = 0; hb < HB; ++hb) {
+          const int hd = 32 * hb + col;
+          f32x16_t acc[TPW];
 #pragma unroll
-        for (int t = 0; t < TPW; ++t) acc[t] = f32x16_t{};
+          for (int t = 0; t < TPW; ++t) acc[t] = f32x16_t{};
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          const int c = 2 * ks + half;
-          const uint4 a4 = *(const uint4*)(qb + hd * RB + 16 * (c ^ (hd & 15)));
+          for (int ks = 0; ks < 8; ++ks) {
+            const int c = 2 * ks + half;
+            const uint4 a4 = *(const uint4*)(qb + hd * RB + 16 * (c ^ (hd & 15)));
 #pragma unroll
-          for (int t = 0; t < TPW; ++t) acc[t] = mfma32x32x16(as_bf16x8(a4), as_bf16x8(kb[t][ks]), acc[t]);
-        }
-        // head 32 hb + 8 (r / 4) + 4 half + r % 4 of accumulator row r
+            for (int t = 0; t < TPW; ++t) acc[t] = mfma32x32x16(as_bf16x8(a4), as_bf16x8(kb[t][ks]), acc[t]);
+          }
+          // head 32 hb + 8 (r / 4) + 4 half + r % 4 of accumulator row r
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4_t wv = *(const f32x4_t*)&w_lds[bi][u][32 * hb + 8 * g + 4 * half];
+          for (int g = 0; g < 4; ++g) {
+            const f32x4_t wv = *(const f32x4_t*)&w_lds[bi][u][32 * hb + 8 * g + 4 * half];
 #pragma unroll
-          for (int t = 0; t < TPW; ++t)
+            for (int t = 0; t < TPW; ++t)
 #pragma unroll
-            for (int k = 0; k < 4; ++k) part[t] = fmaf(wv[k], fmaxf(acc[t][4 * g + k], 0.f), part[t]);
+              for (int k = 0; k < 4; ++k) part[t] = fmaf(wv[k], fmaxf(acc[t][4 * g + k], 0.f), part[t]);
+          }
         }
       }
 #pragma unroll
