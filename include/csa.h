@@ -394,9 +394,10 @@ csa_status csa_decode_noalloc(const csa_decode_args* args, void* stream);
  * a graph are not timed); csa_timing_enable(0) stops it.  This is the one piece of
  * state the library keeps across calls: the events, created on first use and
  * reused.  csa_timing_collect waits for every recorded launch to finish, writes
- * up to `cap` per-kernel aggregates (in order of first launch) to `out` and forgets
- * the records; it returns the number of entries written, or with out == NULL the
- * number of distinct kernels without writing anything.  Thread-safe.
+ * up to `cap` per-kernel aggregates (in order of first launch; kernels beyond `cap`
+ * are dropped) to `out` and forgets the records; it returns the number of entries
+ * written.  With out == NULL it only returns the number of distinct kernels
+ * launched so far: it neither waits nor forgets anything.  Thread-safe.
  * ---------------------------------------------------------------------------- */
 typedef struct {
   char name[40];      /* kernel name, NUL-terminated */

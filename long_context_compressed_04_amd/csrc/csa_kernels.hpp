@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "csa_limits.hpp"
+
 namespace csa {
 
 struct CompressArgs {
@@ -16,7 +18,6 @@ struct CompressArgs {
   float norm_eps = 0.f;
   const float* norm_weight = nullptr; // [channels] or ones
 };
-constexpr int kCompressNormMaxChannels = 4096;
 hipError_t launch_compress(const CompressArgs& A, hipStream_t s);
 
 hipError_t launch_mxfp4_quantize(int in_bf16, const void* x, int64_t n_blocks, uint8_t* codes,
@@ -59,9 +60,5 @@ struct MqaArgs {
 // Workspace bytes the MQA path needs for these sizes (split partials).
 size_t mqa_workspace_bytes(const MqaArgs& A);
 hipError_t launch_mqa(const MqaArgs& A, void* ws, size_t ws_bytes, hipStream_t s);
-
-// Host-side helper of the C ABI for its other translation units: records the detail
-// of a failure for csa_last_error() and returns `status`.
-int api_fail(int status, const char* fmt, ...);
 
 }  // namespace csa

@@ -79,6 +79,16 @@ csa_status csa_timing_enable(int32_t on) {
 int32_t csa_timing_collect(csa_kernel_time* out, int32_t cap) {
   using namespace csa;
   std::lock_guard<std::mutex> lk(g_mu);
+  if (!out) {   // count the distinct kernels launched so far; records are kept
+    std::vector<std::string> names;
+    for (const Record& r : g_recs) {
+      if (!r.done || !r.kernel) continue;
+      bool seen = false;
+      for (const std::string& n : names) seen = seen || n == r.kernel;
+      if (!seen) names.push_back(r.kernel);
+    }
+    return (int32_t)names.size();
+  }
   struct Agg { int32_t n = 0; double total = 0, mn = 1e30, mx = 0; };
   std::map<std::string, Agg> agg;
   std::vector<std::string> order;
@@ -105,7 +115,7 @@ int32_t csa_timing_collect(csa_kernel_time* out, int32_t cap) {
   g_recs.clear();
   int32_t n = 0;
   for (const std::string& name : order) {
-    if (n >= cap || !out) break;
+    if (n >= cap) break;
     const Agg& a = agg[name];
     csa_kernel_time& t = out[n++];
     size_t i = 0;
@@ -116,7 +126,7 @@ int32_t csa_timing_collect(csa_kernel_time* out, int32_t cap) {
     t.min_us = a.mn;
     t.max_us = a.mx;
   }
-  return out ? n : (int32_t)order.size();
+  return n;
 }
 
 }  // extern "C"

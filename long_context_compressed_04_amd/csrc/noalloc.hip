@@ -13,6 +13,7 @@
 
 #include "csa.h"
 #include "csa_kernels.hpp"
+#include "validate.hpp"
 
 namespace {
 
@@ -27,16 +28,16 @@ void* g_scratch_ptr[kMaxDevices] = {};
 csa_status scratch_ptr(void** out) {
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return (csa_status)csa::api_fail(CSA_ERR_HIP, "csa_decode_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return csa::fail(CSA_ERR_HIP, "csa_decode_noalloc: hipGetDevice: %s", hipGetErrorString(e));
   if (dev < 0 || dev >= kMaxDevices)
-    return (csa_status)csa::api_fail(CSA_ERR_UNSUPPORTED, "csa_decode_noalloc: device %d beyond the %d the library tracks", dev,
+    return csa::fail(CSA_ERR_UNSUPPORTED, "csa_decode_noalloc: device %d beyond the %d the library tracks", dev,
                          kMaxDevices);
   std::lock_guard<std::mutex> lk(g_mu);
   if (!g_scratch_ptr[dev]) {
     void* p = nullptr;
     e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
     if (e != hipSuccess || !p)
-      return (csa_status)csa::api_fail(CSA_ERR_HIP, "csa_decode_noalloc: hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+      return csa::fail(CSA_ERR_HIP, "csa_decode_noalloc: hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
     g_scratch_ptr[dev] = p;
   }
   *out = g_scratch_ptr[dev];
@@ -46,10 +47,10 @@ csa_status scratch_ptr(void** out) {
 }  // namespace
 
 extern "C" csa_status csa_decode_noalloc(const csa_decode_args* a, void* stream) {
-  if (!a) return (csa_status)csa::api_fail(CSA_ERR_NULL, "csa_decode_noalloc: args is NULL");
+  if (!a) return csa::fail(CSA_ERR_NULL, "csa_decode_noalloc: args is NULL");
   const size_t need = csa_decode_workspace_size(a);
   if (need > kScratchBytes)
-    return (csa_status)csa::api_fail(CSA_ERR_WORKSPACE,
+    return csa::fail(CSA_ERR_WORKSPACE,
                          "csa_decode_noalloc: this step needs %zu bytes of workspace; the scratch array holds %zu "
                          "(use csa_decode with a workspace of your own)",
                          need, kScratchBytes);

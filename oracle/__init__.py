@@ -21,6 +21,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
+_HDR = os.path.join(_HERE, "oracle.h")
 _LIB = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
@@ -31,7 +32,8 @@ _U8 = ctypes.POINTER(ctypes.c_uint8)
 
 def build(force: bool = False) -> str:
     """Compile oracle.c with gcc (strict IEEE: no fast-math) into liboracle.so."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+    newest = max(os.path.getmtime(_SRC), os.path.getmtime(_HDR))
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < newest:
         tmp = _LIB + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fno-fast-math",
                                "-ffp-contract=off", "-o", tmp, _SRC, "-lm"])

@@ -34,6 +34,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include "oracle.h"
+
 #define ORC_OK 0
 #define ORC_EINVAL 1
 

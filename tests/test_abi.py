@@ -59,6 +59,8 @@ def test_compress_validation():
     assert _compress(D(norm=1, norm_eps=-1.0)) == 2
     assert _compress(D(norm=1, norm_eps=float("nan"))) == 2
     assert _compress(D(norm=1, channels=4097)) == 2         # the normalised entry is held in LDS
+    assert _compress(D(tok_base=2**31 - 1)) == 2            # rows near INT_MAX: rejected, no overflow
+    assert _compress(D(out_cap=2**30, entry_begin=2**29, entry_end=2**30, tok_base=2**31 - 8, n_rows=8)) == 2
 
 
 def test_index_validation():
@@ -74,6 +76,9 @@ def test_index_validation():
     assert call(D(idx_dim=64)) == 6                         # bf16 path needs 128
     assert call(D(idx_heads=48)) == 6
     assert call(D(), q=FAKE_MISALIGNED) == 4
+    # the head weights are read 16 bytes at a time on the bf16 / MXFP4 paths
+    assert L.csa_index_topk(ctypes.byref(D()), FAKE, None, FAKE_MISALIGNED, FAKE, None, FAKE, FAKE, FAKE, None, FAKE,
+                            1 << 30, None) == 4
     assert call(D(dtype=2)) == 1                            # MXFP4 without scales
     assert call(D(dtype=7)) == 3
     assert call(D(dtype=0, idx_heads=128, idx_dim=256)) == 2

@@ -63,6 +63,30 @@ def test_compress(dtype, m, c, zc, rows, tok_base, e0, e1):
         assert np.all(got[b, :e0] == 0) and np.all(got[b, e1:] == 0), "wrote outside [e0, e1)"
 
 
+@pytest.mark.gpu
+def test_launch_timing_counts_then_collects():
+    """csa_timing_collect(NULL) only counts the kernels launched so far; a collection with
+    a buffer then returns them all and forgets them."""
+    L = csa.lib()
+    rng = np.random.default_rng(7)
+    A = dev(rng.standard_normal((1, 16, 64)).astype(np.float32))
+    z = dev(rng.standard_normal((1, 16)).astype(np.float32))
+    out = torch.zeros((1, 4, 64), dtype=torch.float32, device="cuda")
+    csa.timing_collect()                       # start from no records
+    csa.timing_enable(True)
+    try:
+        for _ in range(3):
+            csa.compress(A, A, z, z, 4, out, entry_begin=0, entry_end=4)
+        torch.cuda.synchronize()
+        assert L.csa_timing_collect(None, 0) == 1
+        assert L.csa_timing_collect(None, 0) == 1   # counting keeps the records
+        got = csa.timing_collect()
+        assert list(got) == ["compress"] and got["compress"]["launches"] == 3
+        assert L.csa_timing_collect(None, 0) == 0
+    finally:
+        csa.timing_enable(False)
+
+
 @pytest.mark.parametrize("dtype,m,c,zc,rows,e1,with_weight,masked_b", [
     ("f32", 4, 64, 64, 40, 10, False, False),     # V4's index-key form: per-channel gates, normalised
     ("bf16", 4, 128, 128, 44, 11, True, False),   # bf16 in and out, weighted norm
