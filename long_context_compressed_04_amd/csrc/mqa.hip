@@ -24,8 +24,9 @@
 // All stage 32-row item tiles in LDS (row-major, padded) and form S^T = K . u^T and
 // O^T += V^T . P^T on MFMA.  RMSNorm is folded: q is normalised (times g^2) before
 // the product, 1/rms of each row scales its logit and its softmax weight, and g
-// multiplies the output.  Splits write fp32 partials (unnormalised O, maximum, sum)
-// that a second kernel combines in fixed split order (deterministic).
+// multiplies the output.  Splits write partials (their own softmax average in fp16,
+// maximum and sum in fp32) that a second kernel combines in fixed split order
+// (deterministic).
 //
 // Options on every path: per-head sink logits in the softmax denominator (techniques
 // map, "Learnable attention sink"), and the rope-conjugate rotation of the output's
@@ -114,6 +115,20 @@ __device__ __forceinline__ SoftmaxEnd softmax_end(float m2, float l, const float
 // -x_{i+1} (i even) or x_{i-1} (i odd).  cs = cos[64] then sin[64] of the query.
 __device__ __forceinline__ float rope_conj(float x, float xp, int i, const float* cs) {
   return fmaf(x, cs[i], ((i & 1) ? -xp : xp) * cs[64 + i]);
+}
+
+// Split partials.  A split stores its own softmax average O_s / l_s (fp16, 4 dims per
+// call; 0 for a split with nothing to attend) beside (m_s, l_s) in fp32; the merge
+// weights split s by l_s 2^(m_s - M).  The average is a convex combination of
+// RMS-normalised rows (|value| <= sqrt(512)), so fp16 holds it with a relative error
+// of 2^-11, below the bf16 rounding of the output (2^-9).
+__device__ __forceinline__ uint2 partial4(f32x4_t v, float il) {
+  auto h = [](float x) { return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x); };
+  return make_uint2(h(v[0] * il) | (h(v[1] * il) << 16), h(v[2] * il) | (h(v[3] * il) << 16));
+}
+__device__ __forceinline__ f32x4_t partial4_value(uint2 u) {
+  auto f = [](uint32_t b) { return (float)__builtin_bit_cast(_Float16, (uint16_t)b); };
+  return f32x4_t{f(u.x & 0xffffu), f(u.x >> 16), f(u.y & 0xffffu), f(u.y >> 16)};
 }
 
 // ---------------------------------------------------------------- fp32 (VALU)
@@ -422,7 +437,7 @@ __device__ __forceinline__ void mqa_tiles(const TileCtx& C, const bf16x8_t (&qf)
 }
 
 template <int NW>
-__global__ __launch_bounds__(NW * 64) void mqa_bf16_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml) {
+__global__ __launch_bounds__(NW * 64) void mqa_bf16_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   float* const gam = (float*)(lds + 2 * kTile * kRowB + 2 * kTile * sizeof(float));   // [kD]
   int32_t* const slot_idx = (int32_t*)(gam + kD);                                   // [L.ips] (sparse)
@@ -539,9 +554,10 @@ __global__ __launch_bounds__(NW * 64) void mqa_bf16_kernel(MqaArgs A, MqaLaunch 
     }
     if (A.lse && g == 0) A.lse[row * A.heads + head] = fin.lse;
   } else {
-    float* po = part_o + (((long)row * L.nsplit + split) * A.heads + head) * kD;
+    uint16_t* po = part_o + (((long)row * L.nsplit + split) * A.heads + head) * kD;
+    const float il = l_run > 0.f ? 1.f / l_run : 0.f;
 #pragma unroll
-    for (int db = 0; db < 32; ++db) *(f32x4_t*)(po + 16 * db + 4 * g) = o[db];
+    for (int db = 0; db < 32; ++db) *(uint2*)(po + 16 * db + 4 * g) = partial4(o[db], il);
     if (g == 0) {
       float* pm = part_ml + (((long)row * L.nsplit + split) * A.heads + head) * 2;
       pm[0] = l_run > 0.f ? m_run : -INFINITY;
@@ -675,7 +691,7 @@ __device__ __forceinline__ void fp8x16_to_bf16(uint4 v, uint8_t* dst) {
 // its tile buffer as bf16; the logit and value waves are the same as without F8.
 template <bool F8>
 __global__ __launch_bounds__(kSdWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
-void mqa_sd_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml) {
+void mqa_sd_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml) {
   constexpr int kRowG = F8 ? kD : 2 * kD;   // bytes per cache row
   __shared__ __attribute__((aligned(16))) uint8_t tb0[kTile * kRowB2];
   __shared__ __attribute__((aligned(16))) uint8_t tb1[kTile * kRowB2];
@@ -973,11 +989,12 @@ void mqa_sd_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml) {
       *(uint2*)orow = make_uint2(pack_bf16x2(v[0] * il, v[1] * il), pack_bf16x2(v[2] * il, v[3] * il));
     }
   } else {
-    float* po = part_o + (((long)row * L.nsplit + split) * A.heads + hg * 32) * kD + 128 * pw + 4 * d4;
+    uint16_t* po = part_o + (((long)row * L.nsplit + split) * A.heads + hg * 32) * kD + 128 * pw + 4 * d4;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const int hh = 2 * k + hl;
-      *(f32x4_t*)(po + (long)hh * kD) = *(const f32x4_t*)(stage + hh * kStageRow + 4 * d4);
+      const float l = lsum[0][hh] + lsum[1][hh];
+      *(uint2*)(po + (long)hh * kD) = partial4(*(const f32x4_t*)(stage + hh * kStageRow + 4 * d4), l > 0.f ? 1.f / l : 0.f);
     }
   }
 }
@@ -1046,7 +1063,7 @@ __device__ __forceinline__ float rows_total4(const float (&p)[4], int lane) {
 
 template <bool PRE>
 __global__ __launch_bounds__(kW8Waves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void mqa_w8_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml, const float* inv_kv,
+void mqa_w8_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml, const float* inv_kv,
                    const float* inv_raw) {
   __shared__ __attribute__((aligned(16))) uint8_t tb0[kTile * kRowB2];
   __shared__ __attribute__((aligned(16))) uint8_t tb1[kTile * kRowB2];
@@ -1335,7 +1352,8 @@ void mqa_w8_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml, const 
   for (int j = 0; j < 2; ++j) {
     const int hbj = 2 * hp + j;
     l_tot[j] = red[hbj][c32] + red[hbj + 4][c32];
-    inv_l[j] = softmax_end(0.f, l_tot[j], A.sink, hg * 128 + 64 * hp + 32 * j + c32).mul;
+    inv_l[j] = L.nsplit == 1 ? softmax_end(0.f, l_tot[j], A.sink, hg * 128 + 64 * hp + 32 * j + c32).mul
+                             : (l_tot[j] > 0.f ? 1.f / l_tot[j] : 0.f);   // a split's own average
   }
   // ---- O^T -> rows of 64 dims through a wave-private LDS region, four chunks
   // (head block j of the pair, dim half of the quarter)
@@ -1371,11 +1389,12 @@ void mqa_w8_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml, const 
           *(uint2*)orow = make_uint2(pack_bf16x2(v[0] * il, v[1] * il), pack_bf16x2(v[2] * il, v[3] * il));
         }
       } else {
-        float* po = part_o + (((long)row * L.nsplit + split) * A.heads + head0) * kD + dim0;
+        uint16_t* po = part_o + (((long)row * L.nsplit + split) * A.heads + head0) * kD + dim0;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           const int hh = 4 * k + (lane >> 4);
-          *(f32x4_t*)(po + (long)hh * kD) = *(const f32x4_t*)(stage + hh * kW8Stage + 4 * (lane & 15));
+          const float il = __shfl(inv_l[j], hh, 64);
+          *(uint2*)(po + (long)hh * kD) = partial4(*(const f32x4_t*)(stage + hh * kW8Stage + 4 * (lane & 15)), il);
         }
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);   // reads done before the next chunk overwrites
@@ -1395,10 +1414,11 @@ void mqa_w8_kernel(MqaArgs A, MqaLaunch L, float* part_o, float* part_ml, const 
   }
 }
 
-// Fixed-order merge of split partials: out = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
+// Fixed-order merge of split partials (each the split's average A_s = O_s / l_s):
+// out = sum_s A_s l_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
 constexpr int kMaxSplit = 128;
 
-__global__ __launch_bounds__(128) void mqa_combine_kernel(MqaArgs A, MqaLaunch L, const float* part_o,
+__global__ __launch_bounds__(128) void mqa_combine_kernel(MqaArgs A, MqaLaunch L, const uint16_t* part_o,
                                                           const float* part_ml) {
   constexpr int kPre = 16;   // splits whose partials are requested before the weights exist
   const int head = blockIdx.x;
@@ -1407,13 +1427,14 @@ __global__ __launch_bounds__(128) void mqa_combine_kernel(MqaArgs A, MqaLaunch L
   __shared__ float wts[kMaxSplit];
   __shared__ float s_M, s_L;
   const int d0 = threadIdx.x * 4;
-  const float* po = part_o + ((row * S) * A.heads + head) * kD + d0;
+  const uint16_t* po = part_o + ((row * S) * A.heads + head) * kD + d0;
   const long sstride = (long)A.heads * kD;
-  // the first splits' partials are in flight while the weights are formed
-  f32x4_t pre[kPre];
+  // the first splits' partials are in flight while the weights are formed (kept as
+  // loaded: converting them here would wait for each load in turn)
+  uint2 pre[kPre];
 #pragma unroll
-  for (int s = 0; s < kPre; ++s) pre[s] = s < S ? *(const f32x4_t*)(po + s * sstride) : f32x4_t{};
-  if (threadIdx.x < 64) {   // one wave: w_s = 2^(m_s - M), L = sum_s l_s w_s
+  for (int s = 0; s < kPre; ++s) pre[s] = *(const uint2*)(po + min(s, S - 1) * sstride);   // (no branch)
+  if (threadIdx.x < 64) {   // one wave: w_s = l_s 2^(m_s - M), L = sum_s w_s
     const int lane = threadIdx.x;
     float m2[2], l2[2];
 #pragma unroll
@@ -1428,9 +1449,9 @@ __global__ __launch_bounds__(128) void mqa_combine_kernel(MqaArgs A, MqaLaunch L
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int sp = lane + 64 * j;
-      const float w = (m2[j] == -INFINITY) ? 0.f : exp2f(m2[j] - M);
+      const float w = (m2[j] == -INFINITY) ? 0.f : l2[j] * exp2f(m2[j] - M);
       if (sp < S) wts[sp] = w;
-      ls += l2[j] * w;
+      ls += w;
     }
     ls = wave_sum(ls);
     if (lane == 0) {
@@ -1445,9 +1466,9 @@ __global__ __launch_bounds__(128) void mqa_combine_kernel(MqaArgs A, MqaLaunch L
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < kPre; ++s)
-    if (s < S) acc += pre[s] * wts[s];
+    if (s < S) acc += partial4_value(pre[s]) * wts[s];
 #pragma unroll 8
-  for (int s = kPre; s < S; ++s) acc += *(const f32x4_t*)(po + s * sstride) * wts[s];
+  for (int s = kPre; s < S; ++s) acc += partial4_value(*(const uint2*)(po + s * sstride)) * wts[s];
   float v[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) v[r] = acc[r] * inv_l * (A.gamma ? A.gamma[d0 + r] : 1.f);
@@ -1495,7 +1516,7 @@ static MqaLaunch plan_mqa(const MqaArgs& A) {
   if (fixed) {
     // Kernel and split count from a cost model fitted to MI355X timings (microseconds):
     // rounds of <= 256 workgroups (one per CU), each a fixed start-up cost plus its
-    // 32-row tiles; with splits, the fp32 partials are written and read back once
+    // 32-row tiles; with splits, the fp16 partials are written and read back once
     // (about 4 MB per microsecond each way) and the merge is one more launch.
     double best = 1e30;
     for (int variant = 0; variant < 3; ++variant) {
@@ -1522,8 +1543,8 @@ static MqaLaunch plan_mqa(const MqaArgs& A) {
         if (!A.dense && tps * kTile > kSlotsLds) continue;   // index slots must fit in LDS
         const double wgs = (double)rows * n_hg * s_eff;
         const double rounds = std::ceil(wgs / 256.0);
-        const double part_mb = s_eff > 1 ? wgs * wg_heads * kD * 4.0 / 1.0e6 : 0.0;
-        // start-up: first gathers, and the workgroup's partial (256 KB for 128 heads)
+        const double part_mb = s_eff > 1 ? wgs * wg_heads * kD * 2.0 / 1.0e6 : 0.0;
+        // start-up: first gathers, and the workgroup's partial (128 KB for 128 heads)
         // leaving through one CU
         const double t_start = hg ? 13.0 : (s_eff > 1 ? 13.0 : 4.0);
         const double cost = t_norms + rounds * (t_start + tps * t_tile) + (s_eff > 1 ? 4.0 + part_mb / 2.0 : 0.0);
@@ -1576,7 +1597,7 @@ static size_t r256(size_t x) { return (x + 255) & ~(size_t)255; }
 static size_t partial_bytes(const MqaArgs& A, const MqaLaunch& L) {
   if (L.nsplit == 1) return 0;
   const size_t parts = (size_t)A.batch * A.n_q * L.nsplit * A.heads;
-  return r256(parts * kD * sizeof(float) + parts * 2 * sizeof(float));
+  return r256(parts * kD * sizeof(uint16_t) + parts * 2 * sizeof(float));   // fp16 averages, fp32 (m, l)
 }
 
 // Row norms of the full-dim kernel: [batch, kv_cap] then [batch, raw_cap] fp32.
@@ -1607,14 +1628,14 @@ hipError_t launch_mqa(const MqaArgs& A, void* ws, size_t ws_bytes, hipStream_t s
     return launch("mqa_f32", mqa_f32_kernel, grid, dim3(kF32Waves * 64), 0, s, A);
   }
   MqaLaunch L = plan_mqa(A);
-  float* part_o = nullptr;
+  uint16_t* part_o = nullptr;
   float* part_ml = nullptr;
   const size_t pb = partial_bytes(A, L), nb = norm_bytes(A, L);
   if (pb + nb > 0 && (ws_bytes < pb + nb || !ws)) return hipErrorInvalidValue;
   if (L.nsplit > 1) {
     const size_t parts = (size_t)A.batch * A.n_q * L.nsplit * A.heads;
-    part_o = (float*)ws;
-    part_ml = part_o + parts * kD;
+    part_o = (uint16_t*)ws;
+    part_ml = (float*)(part_o + parts * kD);
   }
   float* inv_kv = nullptr;
   float* inv_raw = nullptr;
@@ -1662,7 +1683,7 @@ hipError_t launch_mqa(const MqaArgs& A, void* ws, size_t ws_bytes, hipStream_t s
     e = launch("mqa_bf16_h16", mqa_bf16_kernel<1>, grid, dim3(64), lds, s, A, L, part_o, part_ml);
   if (e != hipSuccess || L.nsplit == 1) return e;
   dim3 cgrid(A.heads, (unsigned)((long)A.batch * A.n_q));
-  return launch("mqa_combine", mqa_combine_kernel, cgrid, dim3(kD / 4), 0, s, A, L, (const float*)part_o,
+  return launch("mqa_combine", mqa_combine_kernel, cgrid, dim3(kD / 4), 0, s, A, L, (const uint16_t*)part_o,
                 (const float*)part_ml);
 }
 

@@ -5,6 +5,10 @@ summaries kept as text next to the code.
         kernel-trace summary (calls, average / min / max duration per kernel) of a
         `rocprofv3 --kernel-trace --stats` run, with the command that produced it.
 
+    python -m long_context_compressed_04_amd.profiling counters --db RUN.db --cmd "..." --out FILE
+        per-kernel averages of the counters (and derived metrics such as MfmaUtil) of a
+        `rocprofv3 --pmc ...` run.
+
     python -m long_context_compressed_04_amd.profiling traffic --fetch F.db --write W.db \\
             --workload NAME --calib-bytes N --cmd-fetch "..." --cmd-write "..." --out FILE.json
         L2-to-fabric bytes per launch of each library kernel, from one `--pmc FETCH_SIZE`
@@ -133,6 +137,26 @@ def traffic(fetch_db, write_db, calib_bytes, workload, cmd_fetch, cmd_write):
     return res
 
 
+def counters(db: str, cmd: str) -> str:
+    """Per library kernel: the average per dispatch of every counter (and derived metric)
+    in a `rocprofv3 --pmc ...` run, as rocprofv3 reduced it over the GPU's instances."""
+    con = sqlite3.connect(db)
+    names = [r[0] for r in con.execute("select distinct counter_name from counters_collection order by counter_name")]
+    con.close()
+    per = {c: _counter_per_dispatch(db, c) for c in names}
+    lines = ["# rocprofv3 counter summary (average per dispatch)", "# command: " + cmd, "#",
+             "# %-20s %10s  %s" % ("library kernel", "dispatches", "  ".join("%18s" % c for c in names))]
+    kernels = sorted({library_kernel(k) or "-" for c in names for k in per[c]})
+    for lk in kernels:
+        vals, n = [], 0
+        for c in names:
+            v = [x for k, xs in per[c].items() if (library_kernel(k) or "-") == lk for x in xs]
+            n = max(n, len(v))
+            vals.append(sum(v) / len(v) if v else float("nan"))
+        lines.append("  %-20s %10d  %s" % (lk, n, "  ".join("%18.6g" % v for v in vals)))
+    return "\n".join(lines) + "\n"
+
+
 def main(argv=None):
     p = argparse.ArgumentParser()
     sub = p.add_subparsers(dest="what", required=True)
@@ -140,6 +164,10 @@ def main(argv=None):
     s.add_argument("--db", required=True)
     s.add_argument("--cmd", required=True)
     s.add_argument("--out", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("--db", required=True)
+    c.add_argument("--cmd", required=True)
+    c.add_argument("--out", required=True)
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -149,8 +177,8 @@ def main(argv=None):
     t.add_argument("--cmd-write", required=True)
     t.add_argument("--out", required=True)
     a = p.parse_args(argv)
-    if a.what == "stats":
-        text = stats(a.db, a.cmd)
+    if a.what in ("stats", "counters"):
+        text = (stats if a.what == "stats" else counters)(a.db, a.cmd)
         with open(a.out, "w") as f:
             f.write(text)
         sys.stdout.write(text)
