@@ -496,14 +496,27 @@ __device__ __forceinline__ void load_row(const float* src, int n, uint32_t (&key
   }
 }
 
+// The position map of a row (rescoring: slot p of the row is candidate map[p]),
+// loaded like the keys: entry j of this thread is position KPT t + j.  The range is n
+// rounded up to four positions: the map rows are followed by other workspace regions.
+template <int KPT>
+__device__ __forceinline__ void load_map(const int32_t* map, int n, int32_t (&mv)[KPT]) {
+  const __amdgpu_buffer_rsrc_t rs = float_rsrc((const float*)map, (n + 3) & ~3);
+#pragma unroll
+  for (int q = 0; q < KPT / 4; ++q) {
+    typedef int i32x4_t __attribute__((ext_vector_type(4)));
+    const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, ((int)threadIdx.x * KPT + 4 * q) * 4, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mv[4 * q + i] = v[i];
+  }
+}
+
 // The caller zeroes sh.hist and sh.bcount before its first barrier (threshold_one_pass).
+// mv: the row's position map in registers (load_map), when has_map.
 template <int KPT>
 __device__ __forceinline__ void select_reg_row(uint32_t (&key)[KPT], int V, int k, int32_t* oi, float* os,
-                                               SelShared& sh, const int32_t* map = nullptr) {
-  auto idx_of = [map](int j) {
-    const int p = KPT * (int)threadIdx.x + j;
-    return map ? map[p] : p;
-  };
+                                               SelShared& sh, bool has_map, const int32_t (&mv)[KPT]) {
+  auto idx_of = [&](int j) { return has_map ? mv[j] : KPT * (int)threadIdx.x + j; };
   uint32_t prefix, mask = 0xffffffffu, need;
   if (!threshold_one_pass<KPT>(key, V, (uint32_t)k, sh, prefix, need))
     reg_threshold<KPT>(key, V, (uint32_t)k, sh, prefix, mask, need);
@@ -527,17 +540,19 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(IndexArgs A, co
   // it are never counted)
   uint32_t key[KPT];
   load_row<KPT>(src, A.n_max, key);
+  const int32_t* map = A.map ? A.map + row * A.n_max : nullptr;
+  int32_t mv[KPT] = {};
+  if (map) load_map<KPT>(map, A.n_max, mv);   // (in flight with the keys: no load inside the compaction)
   clear_select_lds(sh);
   const int V = row_visible(A, row);
   const int k = A.topk;
   int32_t* oi = out_idx + row * k;
   float* os = out_score ? out_score + row * k : nullptr;
-  const int32_t* map = A.map ? A.map + row * A.n_max : nullptr;
   if (V <= k) {
     take_all(src, V, k, oi, os, map);
     return;
   }
-  select_reg_row<KPT>(key, V, k, oi, os, sh, map);
+  select_reg_row<KPT>(key, V, k, oi, os, sh, map != nullptr, mv);
 }
 
 // ---- long rows, launch 1: the threshold from a fixed sample of the row, then the
@@ -700,7 +715,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_candidates_kernel(IndexArgs
     uint32_t key[kMaxKpt];
     load_row<kMaxKpt>(src, V, key);
     clear_select_lds(sh);
-    select_reg_row<kMaxKpt>(key, V, k, oi, os, sh);
+    const int32_t none[kMaxKpt] = {};
+    select_reg_row<kMaxKpt>(key, V, k, oi, os, sh, false, none);
     return;
   }
   const int nch = (V + kChunk - 1) / kChunk;
