@@ -58,10 +58,7 @@ struct SelShared {
   uint32_t wcnt[2 * kTW];
   uint32_t bkey[kBucketMax];
   union {
-    struct {
-      int32_t oidx[kMaxTopk];         // the selection in output order, written out coalesced
-      uint32_t okey[kMaxTopk];
-    };
+    int32_t opos[kMaxTopk];           // the selection's positions in output order
     uint32_t stage[2 * kMaxTopk];     // (long rows: the candidate keys, before the selection)
   };
   uint32_t bcount;
@@ -340,25 +337,28 @@ __device__ __forceinline__ void reg_threshold(const uint32_t (&key)[KPT], int n,
   }
 }
 
-// Writes the selection in position order: out_idx[p] = idx_of(j) for this thread's
-// key[j] when it is the p-th selected position, out_score[p] its score.  Exactly k
-// slots are written: first to LDS at their output slots, then copied out in order.
-template <int KPT, class IdxOf>
+// Writes the selection in position order: out_idx[p] = idx_at(pos) and out_score[p] =
+// score_at(pos) for the p-th selected position pos.  Thread t's selected keys (every key
+// above the threshold, and the first `need` keys equal to it overall) take consecutive
+// output slots from base(t) = (keys above before t) + min(keys equal before t, need).
+// Only their positions are scattered to LDS, by a loop over the set bits of the thread's
+// selection mask (about one selected key in sixteen); exactly k slots are then written
+// out in order.
+template <int KPT, class IdxAt, class ScoreAt>
 __device__ __forceinline__ void reg_compact(const uint32_t (&key)[KPT], int n, uint32_t prefix, uint32_t mask,
-                                            uint32_t need, int k, IdxOf idx_of, int32_t* oi, float* os,
-                                            SelShared& sh) {
+                                            uint32_t need, int k, IdxAt idx_at, ScoreAt score_at, int32_t* oi,
+                                            float* os, SelShared& sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  static_assert(KPT <= 16, "two class bits per key in one word");
-  // class of key j in bits 2j (above the threshold) and 2j+1 (equal to it)
-  uint32_t cls = 0;
+  static_assert(KPT <= 16, "one selection bit per key in 16 bits");
+  uint32_t gm = 0, em = 0;   // bit j: key j above / equal to the threshold
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const bool v = valid_pos<KPT>(j, n);
     const uint32_t kp = key[j] & mask;
-    cls |= ((v && kp > prefix) ? 1u : 0u) << (2 * j);
-    cls |= ((v && kp == prefix) ? 2u : 0u) << (2 * j);
+    gm |= ((v && kp > prefix) ? 1u : 0u) << j;
+    em |= ((v && kp == prefix) ? 1u : 0u) << j;
   }
-  const uint32_t ng = (uint32_t)__popc(cls & 0x55555555u), ne = (uint32_t)__popc(cls & 0xAAAAAAAAu);
+  const uint32_t ng = (uint32_t)__popc(gm), ne = (uint32_t)__popc(em);
   // exclusive scans in position order: within the wave, then over the waves before
   const uint32_t ig = wave_inclusive_sum(ng), ie = wave_inclusive_sum(ne);
   if (lane == 63) {
@@ -368,25 +368,29 @@ __device__ __forceinline__ void reg_compact(const uint32_t (&key)[KPT], int n, u
   __syncthreads();
   const uint32_t wg = lane < wave ? sh.wcnt[lane] : 0u;
   const uint32_t we = lane < wave ? sh.wcnt[kTW + lane] : 0u;
-  uint32_t gb = (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_sum(wg), 63) + ig - ng;
-  uint32_t eb = (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_sum(we), 63) + ie - ne;
-#pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const uint32_t c = (cls >> (2 * j)) & 3u;
-    const bool g = c == 1u, e = c == 2u;
-    const bool sel = g || (e && eb < need);
-    const uint32_t p = gb + min(eb, need);
-    if (sel && p < (uint32_t)k) {
-      sh.oidx[p] = idx_of(j);
-      sh.okey[p] = key[j];
-    }
-    gb += g ? 1u : 0u;
-    eb += e ? 1u : 0u;
+  const uint32_t gb = (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_sum(wg), 63) + ig - ng;
+  const uint32_t eb = (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_sum(we), 63) + ie - ne;
+  // the equal keys this thread takes: the lowest min(need - eb, ne) set bits of em
+  uint32_t et = 0;
+  if (eb < need) {
+    const uint32_t take = min(need - eb, ne);
+    et = em;
+    for (uint32_t d = ne; d > take; --d) et &= ~(1u << (31 - __clz((int)et)));   // drop the highest
+  }
+  uint32_t sel = gm | et;
+  uint32_t p = gb + min(eb, need);
+  const int pos0 = KPT * (int)threadIdx.x;
+  while (sel) {
+    const int j = __builtin_ctz(sel);
+    if (p < (uint32_t)k) sh.opos[p] = pos0 + j;
+    ++p;
+    sel &= sel - 1u;
   }
   __syncthreads();
   for (int i = threadIdx.x; i < k; i += kTopkThreads) {
-    oi[i] = sh.oidx[i];
-    if (os) os[i] = key_to_float(sh.okey[i]);
+    const int pos = sh.opos[i];
+    oi[i] = idx_at(pos);
+    if (os) os[i] = score_at(pos);
   }
 }
 
@@ -496,31 +500,18 @@ __device__ __forceinline__ void load_row(const float* src, int n, uint32_t (&key
   }
 }
 
-// The position map of a row (rescoring: slot p of the row is candidate map[p]),
-// loaded like the keys: entry j of this thread is position KPT t + j.  The range is n
-// rounded up to four positions: the map rows are followed by other workspace regions.
-template <int KPT>
-__device__ __forceinline__ void load_map(const int32_t* map, int n, int32_t (&mv)[KPT]) {
-  const __amdgpu_buffer_rsrc_t rs = float_rsrc((const float*)map, (n + 3) & ~3);
-#pragma unroll
-  for (int q = 0; q < KPT / 4; ++q) {
-    typedef int i32x4_t __attribute__((ext_vector_type(4)));
-    const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, ((int)threadIdx.x * KPT + 4 * q) * 4, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) mv[4 * q + i] = v[i];
-  }
-}
-
 // The caller zeroes sh.hist and sh.bcount before its first barrier (threshold_one_pass).
-// mv: the row's position map in registers (load_map), when has_map.
+// src: the row's scores (read back for the selected positions); map: the row's position
+// map (rescoring: slot p of the row is candidate map[p]) or none.
 template <int KPT>
 __device__ __forceinline__ void select_reg_row(uint32_t (&key)[KPT], int V, int k, int32_t* oi, float* os,
-                                               SelShared& sh, bool has_map, const int32_t (&mv)[KPT]) {
-  auto idx_of = [&](int j) { return has_map ? mv[j] : KPT * (int)threadIdx.x + j; };
+                                               SelShared& sh, const float* src, const int32_t* map) {
+  auto idx_at = [map](int pos) { return map ? map[pos] : pos; };
+  auto score_at = [src](int pos) { return src[pos]; };
   uint32_t prefix, mask = 0xffffffffu, need;
   if (!threshold_one_pass<KPT>(key, V, (uint32_t)k, sh, prefix, need))
     reg_threshold<KPT>(key, V, (uint32_t)k, sh, prefix, mask, need);
-  reg_compact<KPT>(key, V, prefix, mask, need, k, idx_of, oi, os, sh);
+  reg_compact<KPT>(key, V, prefix, mask, need, k, idx_at, score_at, oi, os, sh);
 }
 
 // Zeroes the histogram and the bucket counter (before the caller's first barrier).
@@ -541,8 +532,6 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(IndexArgs A, co
   uint32_t key[KPT];
   load_row<KPT>(src, A.n_max, key);
   const int32_t* map = A.map ? A.map + row * A.n_max : nullptr;
-  int32_t mv[KPT] = {};
-  if (map) load_map<KPT>(map, A.n_max, mv);   // (in flight with the keys: no load inside the compaction)
   clear_select_lds(sh);
   const int V = row_visible(A, row);
   const int k = A.topk;
@@ -552,7 +541,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(IndexArgs A, co
     take_all(src, V, k, oi, os, map);
     return;
   }
-  select_reg_row<KPT>(key, V, k, oi, os, sh, map != nullptr, mv);
+  select_reg_row<KPT>(key, V, k, oi, os, sh, src, map);
 }
 
 // ---- long rows, launch 1: the threshold from a fixed sample of the row, then the
@@ -657,8 +646,8 @@ constexpr int kCopyT = 16, kSpec = 8;
 template <int KPT>
 __device__ __forceinline__ void select_candidates(const uint32_t (&spk)[kSpec], const int32_t (&spi)[kSpec],
                                                   const uint32_t* gk, const int32_t* gi, const uint32_t* coff,
-                                                  int nch, int M, int k, int32_t* cand_idx, int32_t* oi,
-                                                  float* os, SelShared& sh) {
+                                                  int nch, int M, int k, int32_t* cand_idx,
+                                                  const float* row_scores, int32_t* oi, float* os, SelShared& sh) {
   const int c_sp = (int)threadIdx.x / kCopyT;
   for (int c = c_sp; c < nch; c += kTopkThreads / kCopyT) {
     const int base = (int)coff[c], n = (int)coff[c + 1] - base;
@@ -686,13 +675,15 @@ __device__ __forceinline__ void select_candidates(const uint32_t (&spk)[kSpec], 
     const int c = KPT * (int)threadIdx.x + j;
     key[j] = c < M ? sh.stage[c] : 0u;
   }
-  // (the staging area is next written by the compaction, after the threshold's barriers)
-  auto idx_of = [&](int j) { return cand_idx[KPT * threadIdx.x + j]; };
+  // (the staging area is next written by the compaction, after the threshold's barriers:
+  // the selected scores are read back from the row)
+  auto idx_at = [&](int c) { return cand_idx[c]; };
+  auto score_at = [&](int c) { return row_scores[cand_idx[c]]; };
   clear_select_lds(sh);   // (the staging barrier above precedes the next one)
   uint32_t prefix, mask = 0xffffffffu, need;
   if (!threshold_one_pass<KPT>(key, M, (uint32_t)k, sh, prefix, need))
     reg_threshold<KPT>(key, M, (uint32_t)k, sh, prefix, mask, need);
-  reg_compact<KPT>(key, M, prefix, mask, need, k, idx_of, oi, os, sh);
+  reg_compact<KPT>(key, M, prefix, mask, need, k, idx_at, score_at, oi, os, sh);
 }
 
 // ---- long rows, launch 2: exact selection among the candidates (or the whole row)
@@ -715,8 +706,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_candidates_kernel(IndexArgs
     uint32_t key[kMaxKpt];
     load_row<kMaxKpt>(src, V, key);
     clear_select_lds(sh);
-    const int32_t none[kMaxKpt] = {};
-    select_reg_row<kMaxKpt>(key, V, k, oi, os, sh, false, none);
+    select_reg_row<kMaxKpt>(key, V, k, oi, os, sh, src, nullptr);
     return;
   }
   const int nch = (V + kChunk - 1) / kChunk;
@@ -757,9 +747,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_candidates_kernel(IndexArgs
     return;
   }
   // as few registers per thread as the candidate count allows
-  if (M <= 4 * kTopkThreads) select_candidates<4>(spk, spi, gk, gi, coff, nch, M, k, cand_idx, oi, os, sh);
-  else if (M <= 8 * kTopkThreads) select_candidates<8>(spk, spi, gk, gi, coff, nch, M, k, cand_idx, oi, os, sh);
-  else select_candidates<kCandCap / kTopkThreads>(spk, spi, gk, gi, coff, nch, M, k, cand_idx, oi, os, sh);
+  if (M <= 4 * kTopkThreads) select_candidates<4>(spk, spi, gk, gi, coff, nch, M, k, cand_idx, src, oi, os, sh);
+  else if (M <= 8 * kTopkThreads) select_candidates<8>(spk, spi, gk, gi, coff, nch, M, k, cand_idx, src, oi, os, sh);
+  else select_candidates<kCandCap / kTopkThreads>(spk, spi, gk, gi, coff, nch, M, k, cand_idx, src, oi, os, sh);
 }
 
 static int long_chunks(const IndexArgs& A) { return (A.n_max + kChunk - 1) / kChunk; }
