@@ -221,8 +221,8 @@ __device__ __forceinline__ void resolve_bucket(const uint32_t (&key)[KPT], int n
 // are the k largest.  The caller zeroes sh.hist and sh.bcount before its first
 // barrier.  Requires 1 <= k <= n.  Contains barriers: call from every thread.
 template <int KPT>
-__device__ __forceinline__ bool threshold_one_pass(const uint32_t (&key)[KPT], int n, uint32_t k, SelShared& sh,
-                                                   uint32_t& T, uint32_t& need) {
+__device__ __forceinline__ bool threshold_one_pass(const uint32_t (&key)[KPT], const float (&x)[KPT], int n,
+                                                   uint32_t k, SelShared& sh, uint32_t& T, uint32_t& need) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
@@ -256,11 +256,22 @@ __device__ __forceinline__ bool threshold_one_pass(const uint32_t (&key)[KPT], i
     __syncthreads();   // (uniform) every wave has read sh.red before the fallback writes it
     return false;
   }
+  // bin = min((x - lo) * scale, 2047) as one fma: still non-decreasing in x.  A wave whose
+  // positions are all below n (every wave but at most one) skips the checks.
+  const float c0 = -lo * scale;
   int bins[KPT];
+  if (KPT * (64 * wave + 64) <= n) {
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    bins[j] = valid_pos<KPT>(j, n) ? (int)fminf((key_to_float(key[j]) - lo) * scale, (float)(kBins - 1)) : -1;
-    if (bins[j] >= 0) atomicAdd(&sh.hist[hslot(bins[j])], 1u);
+    for (int j = 0; j < KPT; ++j) {
+      bins[j] = (int)fminf(fmaf(x[j], scale, c0), (float)(kBins - 1));
+      atomicAdd(&sh.hist[hslot(bins[j])], 1u);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      bins[j] = valid_pos<KPT>(j, n) ? (int)fminf(fmaf(x[j], scale, c0), (float)(kBins - 1)) : -1;
+      if (bins[j] >= 0) atomicAdd(&sh.hist[hslot(bins[j])], 1u);
+    }
   }
   __syncthreads();
   pick_digit(sh, 0u, 0, k);
@@ -488,7 +499,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t float_rsrc(const float* p, int
 // live in the library's workspace, which keeps 16 bytes of slack after them, and the
 // positions past n are never counted.
 template <int KPT>
-__device__ __forceinline__ void load_row(const float* src, int n, uint32_t (&key)[KPT]) {
+__device__ __forceinline__ void load_row(const float* src, int n, uint32_t (&key)[KPT], float (&x)[KPT]) {
   const __amdgpu_buffer_rsrc_t rs = float_rsrc(src, (n + 3) & ~3);
   static_assert(KPT % 4 == 0, "keys are loaded four at a time");
 #pragma unroll
@@ -496,7 +507,10 @@ __device__ __forceinline__ void load_row(const float* src, int n, uint32_t (&key
     typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
     const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, ((int)threadIdx.x * KPT + 4 * q) * 4, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) key[4 * q + i] = order_key(__uint_as_float(v[i]));
+    for (int i = 0; i < 4; ++i) {
+      x[4 * q + i] = __uint_as_float(v[i]);
+      key[4 * q + i] = order_key(x[4 * q + i]);
+    }
   }
 }
 
@@ -504,12 +518,12 @@ __device__ __forceinline__ void load_row(const float* src, int n, uint32_t (&key
 // src: the row's scores (read back for the selected positions); map: the row's position
 // map (rescoring: slot p of the row is candidate map[p]) or none.
 template <int KPT>
-__device__ __forceinline__ void select_reg_row(uint32_t (&key)[KPT], int V, int k, int32_t* oi, float* os,
-                                               SelShared& sh, const float* src, const int32_t* map) {
+__device__ __forceinline__ void select_reg_row(uint32_t (&key)[KPT], const float (&x)[KPT], int V, int k, int32_t* oi,
+                                               float* os, SelShared& sh, const float* src, const int32_t* map) {
   auto idx_at = [map](int pos) { return map ? map[pos] : pos; };
   auto score_at = [src](int pos) { return src[pos]; };
   uint32_t prefix, mask = 0xffffffffu, need;
-  if (!threshold_one_pass<KPT>(key, V, (uint32_t)k, sh, prefix, need))
+  if (!threshold_one_pass<KPT>(key, x, V, (uint32_t)k, sh, prefix, need))
     reg_threshold<KPT>(key, V, (uint32_t)k, sh, prefix, mask, need);
   reg_compact<KPT>(key, V, prefix, mask, need, k, idx_at, score_at, oi, os, sh);
 }
@@ -530,7 +544,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(IndexArgs A, co
   // the row's scores are requested before the visible count arrives (positions past
   // it are never counted)
   uint32_t key[KPT];
-  load_row<KPT>(src, A.n_max, key);
+  float x[KPT];
+  load_row<KPT>(src, A.n_max, key, x);
   const int32_t* map = A.map ? A.map + row * A.n_max : nullptr;
   clear_select_lds(sh);
   const int V = row_visible(A, row);
@@ -541,7 +556,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(IndexArgs A, co
     take_all(src, V, k, oi, os, map);
     return;
   }
-  select_reg_row<KPT>(key, V, k, oi, os, sh, src, map);
+  select_reg_row<KPT>(key, x, V, k, oi, os, sh, src, map);
 }
 
 // ---- long rows, launch 1: the threshold from a fixed sample of the row, then the
@@ -681,7 +696,10 @@ __device__ __forceinline__ void select_candidates(const uint32_t (&spk)[kSpec], 
   auto score_at = [&](int c) { return row_scores[cand_idx[c]]; };
   clear_select_lds(sh);   // (the staging barrier above precedes the next one)
   uint32_t prefix, mask = 0xffffffffu, need;
-  if (!threshold_one_pass<KPT>(key, M, (uint32_t)k, sh, prefix, need))
+  float x[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) x[j] = key_to_float(key[j]);
+  if (!threshold_one_pass<KPT>(key, x, M, (uint32_t)k, sh, prefix, need))
     reg_threshold<KPT>(key, M, (uint32_t)k, sh, prefix, mask, need);
   reg_compact<KPT>(key, M, prefix, mask, need, k, idx_at, score_at, oi, os, sh);
 }
@@ -704,9 +722,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_candidates_kernel(IndexArgs
   }
   if (V <= kRegKeys) {
     uint32_t key[kMaxKpt];
-    load_row<kMaxKpt>(src, V, key);
+    float x[kMaxKpt];
+    load_row<kMaxKpt>(src, V, key, x);
     clear_select_lds(sh);
-    select_reg_row<kMaxKpt>(key, V, k, oi, os, sh, src, nullptr);
+    select_reg_row<kMaxKpt>(key, x, V, k, oi, os, sh, src, nullptr);
     return;
   }
   const int nch = (V + kChunk - 1) / kChunk;
