@@ -36,4 +36,13 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
   return v;
 }
 
+// Sum over the 16 lanes of each row (every lane of the row gets it): rotations 1, 2, 4, 8.
+__device__ __forceinline__ uint32_t row_sum16(uint32_t v) {
+  v += dpp0<kDppRowRor1>(v);
+  v += dpp0<kDppRowRor2>(v);
+  v += dpp0<kDppRowRor4>(v);
+  v += dpp0<kDppRowRor8>(v);
+  return v;
+}
+
 }  // namespace csa

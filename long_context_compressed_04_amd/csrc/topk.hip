@@ -56,7 +56,7 @@ struct SelShared {
   uint32_t hist[kHistWords];          // bin b at b + b / 32
   uint32_t red[2 * kTW];
   uint32_t wcnt[2 * kTW];
-  uint32_t bkey[kBucketMax];
+  alignas(16) uint32_t bkey[kBucketMax];
   union {
     int32_t opos[kMaxTopk];           // the selection's positions in output order
     uint32_t stage[2 * kMaxTopk];     // (long rows: the candidate keys, before the selection)
@@ -284,15 +284,22 @@ __device__ __forceinline__ bool threshold_one_pass(const uint32_t (&key)[KPT], c
   for (int j = 0; j < KPT; ++j)
     if (bins[j] == b) sh.bkey[atomicAdd(&sh.bcount, 1u)] = key[j];
   __syncthreads();
-  if (threadIdx.x < 64) {   // rank each bucket key among the others: the nd-th largest is T
-    const uint32_t mine = (uint32_t)lane < cnt ? sh.bkey[lane] : 0u;
+  {   // rank each bucket key among the others, 16 threads per key (4 comparisons each,
+      // summed over their DPP row): the nd-th largest is T
+    const uint32_t i = threadIdx.x >> 4, part = threadIdx.x & 15;
+    const uint32_t mine = i < cnt ? sh.bkey[i] : 0u;
+    const uint4 o4 = *(const uint4*)&sh.bkey[4 * part];
+    const uint32_t o[4] = {o4.x, o4.y, o4.z, o4.w};
     uint32_t gt = 0, eq = 0;
-    for (int j = 0; j < (int)cnt; ++j) {   // (cnt is uniform: the other keys by lane broadcast)
-      const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)mine, j);
-      gt += o > mine ? 1u : 0u;
-      eq += o == mine ? 1u : 0u;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool in = 4 * part + r < cnt;
+      gt += (in && o[r] > mine) ? 1u : 0u;
+      eq += (in && o[r] == mine) ? 1u : 0u;
     }
-    if ((uint32_t)lane < cnt && gt < nd && nd <= gt + eq) {   // the lanes holding T (same values)
+    gt = row_sum16(gt);
+    eq = row_sum16(eq);
+    if (part == 0 && i < cnt && gt < nd && nd <= gt + eq) {   // the keys equal to T (same values)
       sh.s_prefix = mine;
       sh.s_need = nd - gt;
     }
