@@ -224,12 +224,22 @@ template <int KPT>
 __device__ __forceinline__ bool threshold_one_pass(const uint32_t (&key)[KPT], const float (&x)[KPT], int n,
                                                    uint32_t k, SelShared& sh, uint32_t& T, uint32_t& need) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // a wave whose positions all lie below n (every wave but at most one) skips the checks
+  const bool wave_full = KPT * (64 * wave + 64) <= n;
   uint32_t kmin = 0xffffffffu, kmax = 0u;
+  if (wave_full) {
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    if (valid_pos<KPT>(j, n)) {
+    for (int j = 0; j < KPT; ++j) {
       kmin = min(kmin, key[j]);
       kmax = max(kmax, key[j]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      if (valid_pos<KPT>(j, n)) {
+        kmin = min(kmin, key[j]);
+        kmax = max(kmax, key[j]);
+      }
     }
   }
   wave_minmax(kmin, kmax);
@@ -256,11 +266,10 @@ __device__ __forceinline__ bool threshold_one_pass(const uint32_t (&key)[KPT], c
     __syncthreads();   // (uniform) every wave has read sh.red before the fallback writes it
     return false;
   }
-  // bin = min((x - lo) * scale, 2047) as one fma: still non-decreasing in x.  A wave whose
-  // positions are all below n (every wave but at most one) skips the checks.
+  // bin = min((x - lo) * scale, 2047) as one fma: still non-decreasing in x
   const float c0 = -lo * scale;
   int bins[KPT];
-  if (KPT * (64 * wave + 64) <= n) {
+  if (wave_full) {
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       bins[j] = (int)fminf(fmaf(x[j], scale, c0), (float)(kBins - 1));
@@ -369,12 +378,20 @@ __device__ __forceinline__ void reg_compact(const uint32_t (&key)[KPT], int n, u
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   static_assert(KPT <= 16, "one selection bit per key in 16 bits");
   uint32_t gm = 0, em = 0;   // bit j: key j above / equal to the threshold
+  if (KPT * (64 * wave + 64) <= n && mask == 0xffffffffu) {   // (uniform) no range check, no mask
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const bool v = valid_pos<KPT>(j, n);
-    const uint32_t kp = key[j] & mask;
-    gm |= ((v && kp > prefix) ? 1u : 0u) << j;
-    em |= ((v && kp == prefix) ? 1u : 0u) << j;
+    for (int j = 0; j < KPT; ++j) {
+      gm |= (key[j] > prefix ? 1u : 0u) << j;
+      em |= (key[j] == prefix ? 1u : 0u) << j;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const bool v = valid_pos<KPT>(j, n);
+      const uint32_t kp = key[j] & mask;
+      gm |= ((v && kp > prefix) ? 1u : 0u) << j;
+      em |= ((v && kp == prefix) ? 1u : 0u) << j;
+    }
   }
   const uint32_t ng = (uint32_t)__popc(gm), ne = (uint32_t)__popc(em);
   // exclusive scans in position order: within the wave, then over the waves before
