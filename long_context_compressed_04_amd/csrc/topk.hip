@@ -58,7 +58,10 @@ struct SelShared {
   uint32_t wcnt[2 * kTW];
   alignas(16) uint32_t bkey[kBucketMax];
   union {
-    int32_t opos[kMaxTopk];           // the selection's positions in output order
+    struct {
+      int32_t opos[kMaxTopk];         // the selection's positions in output order
+      uint32_t okey[kMaxTopk];        // and their keys (when the scores are wanted)
+    };
     uint32_t stage[2 * kMaxTopk];     // (long rows: the candidate keys, before the selection)
   };
   uint32_t bcount;
@@ -364,17 +367,18 @@ __device__ __forceinline__ void reg_threshold(const uint32_t (&key)[KPT], int n,
   }
 }
 
-// Writes the selection in position order: out_idx[p] = idx_at(pos) and out_score[p] =
-// score_at(pos) for the p-th selected position pos.  Thread t's selected keys (every key
-// above the threshold, and the first `need` keys equal to it overall) take consecutive
-// output slots from base(t) = (keys above before t) + min(keys equal before t, need).
-// Only their positions are scattered to LDS, by a loop over the set bits of the thread's
-// selection mask (about one selected key in sixteen); exactly k slots are then written
-// out in order.
-template <int KPT, class IdxAt, class ScoreAt>
+// Writes the selection in position order: out_idx[p] = idx_at(pos) for the p-th
+// selected position pos, and out_score[p] its score.  Thread t's selected keys (every
+// key above the threshold, and the first `need` keys equal to it overall) take
+// consecutive output slots from base(t) = (keys above before t) + min(keys equal before
+// t, need).  Without scores only their positions are scattered to LDS, by a loop over the
+// set bits of the thread's selection mask (about one selected key in sixteen); with
+// scores a loop over the KPT keys writes each selected key too.  Exactly k slots are
+// then written out in order.
+template <int KPT, class IdxAt>
 __device__ __forceinline__ void reg_compact(const uint32_t (&key)[KPT], int n, uint32_t prefix, uint32_t mask,
-                                            uint32_t need, int k, IdxAt idx_at, ScoreAt score_at, int32_t* oi,
-                                            float* os, SelShared& sh) {
+                                            uint32_t need, int k, IdxAt idx_at, int32_t* oi, float* os,
+                                            SelShared& sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   static_assert(KPT <= 16, "one selection bit per key in 16 bits");
   uint32_t gm = 0, em = 0;   // bit j: key j above / equal to the threshold
@@ -415,17 +419,29 @@ __device__ __forceinline__ void reg_compact(const uint32_t (&key)[KPT], int n, u
   uint32_t sel = gm | et;
   uint32_t p = gb + min(eb, need);
   const int pos0 = KPT * (int)threadIdx.x;
-  while (sel) {
-    const int j = __builtin_ctz(sel);
-    if (p < (uint32_t)k) sh.opos[p] = pos0 + j;
-    ++p;
-    sel &= sel - 1u;
+  if (os) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      if ((sel >> j) & 1u) {
+        if (p < (uint32_t)k) {
+          sh.opos[p] = pos0 + j;
+          sh.okey[p] = key[j];
+        }
+        ++p;
+      }
+    }
+  } else {
+    while (sel) {
+      const int j = __builtin_ctz(sel);
+      if (p < (uint32_t)k) sh.opos[p] = pos0 + j;
+      ++p;
+      sel &= sel - 1u;
+    }
   }
   __syncthreads();
   for (int i = threadIdx.x; i < k; i += kTopkThreads) {
-    const int pos = sh.opos[i];
-    oi[i] = idx_at(pos);
-    if (os) os[i] = score_at(pos);
+    oi[i] = idx_at(sh.opos[i]);
+    if (os) os[i] = key_to_float(sh.okey[i]);
   }
 }
 
@@ -539,17 +555,16 @@ __device__ __forceinline__ void load_row(const float* src, int n, uint32_t (&key
 }
 
 // The caller zeroes sh.hist and sh.bcount before its first barrier (threshold_one_pass).
-// src: the row's scores (read back for the selected positions); map: the row's position
-// map (rescoring: slot p of the row is candidate map[p]) or none.
+// x: the keys' scores; map: the row's position map (rescoring: slot p of the row is
+// candidate map[p]) or none.
 template <int KPT>
 __device__ __forceinline__ void select_reg_row(uint32_t (&key)[KPT], const float (&x)[KPT], int V, int k, int32_t* oi,
-                                               float* os, SelShared& sh, const float* src, const int32_t* map) {
+                                               float* os, SelShared& sh, const int32_t* map) {
   auto idx_at = [map](int pos) { return map ? map[pos] : pos; };
-  auto score_at = [src](int pos) { return src[pos]; };
   uint32_t prefix, mask = 0xffffffffu, need;
   if (!threshold_one_pass<KPT>(key, x, V, (uint32_t)k, sh, prefix, need))
     reg_threshold<KPT>(key, V, (uint32_t)k, sh, prefix, mask, need);
-  reg_compact<KPT>(key, V, prefix, mask, need, k, idx_at, score_at, oi, os, sh);
+  reg_compact<KPT>(key, V, prefix, mask, need, k, idx_at, oi, os, sh);
 }
 
 // Zeroes the histogram and the bucket counter (before the caller's first barrier).
@@ -559,9 +574,11 @@ __device__ __forceinline__ void clear_select_lds(SelShared& sh) {
 }
 
 // ---- rows of up to KPT * 1024 entries: one workgroup per row
+// (two workgroups per CU, so that one's loads and barriers overlap the other's work on
+// many rows: at most 64 registers per lane)
 template <int KPT>
-__global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(IndexArgs A, const float* scores, int32_t* out_idx,
-                                                                 float* out_score) {
+__global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void topk_rows_kernel(IndexArgs A, const float* scores, int32_t* out_idx, float* out_score) {
   __shared__ SelShared sh;
   const long row = blockIdx.x;
   const float* src = scores + row * A.n_max;
@@ -580,7 +597,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(IndexArgs A, co
     take_all(src, V, k, oi, os, map);
     return;
   }
-  select_reg_row<KPT>(key, x, V, k, oi, os, sh, src, map);
+  select_reg_row<KPT>(key, x, V, k, oi, os, sh, map);
 }
 
 // ---- long rows, launch 1: the threshold from a fixed sample of the row, then the
@@ -685,8 +702,8 @@ constexpr int kCopyT = 16, kSpec = 8;
 template <int KPT>
 __device__ __forceinline__ void select_candidates(const uint32_t (&spk)[kSpec], const int32_t (&spi)[kSpec],
                                                   const uint32_t* gk, const int32_t* gi, const uint32_t* coff,
-                                                  int nch, int M, int k, int32_t* cand_idx,
-                                                  const float* row_scores, int32_t* oi, float* os, SelShared& sh) {
+                                                  int nch, int M, int k, int32_t* cand_idx, int32_t* oi,
+                                                  float* os, SelShared& sh) {
   const int c_sp = (int)threadIdx.x / kCopyT;
   for (int c = c_sp; c < nch; c += kTopkThreads / kCopyT) {
     const int base = (int)coff[c], n = (int)coff[c + 1] - base;
@@ -714,10 +731,8 @@ __device__ __forceinline__ void select_candidates(const uint32_t (&spk)[kSpec], 
     const int c = KPT * (int)threadIdx.x + j;
     key[j] = c < M ? sh.stage[c] : 0u;
   }
-  // (the staging area is next written by the compaction, after the threshold's barriers:
-  // the selected scores are read back from the row)
+  // (the staging area is next written by the compaction, after the threshold's barriers)
   auto idx_at = [&](int c) { return cand_idx[c]; };
-  auto score_at = [&](int c) { return row_scores[cand_idx[c]]; };
   clear_select_lds(sh);   // (the staging barrier above precedes the next one)
   uint32_t prefix, mask = 0xffffffffu, need;
   float x[KPT];
@@ -725,7 +740,7 @@ __device__ __forceinline__ void select_candidates(const uint32_t (&spk)[kSpec], 
   for (int j = 0; j < KPT; ++j) x[j] = key_to_float(key[j]);
   if (!threshold_one_pass<KPT>(key, x, M, (uint32_t)k, sh, prefix, need))
     reg_threshold<KPT>(key, M, (uint32_t)k, sh, prefix, mask, need);
-  reg_compact<KPT>(key, M, prefix, mask, need, k, idx_at, score_at, oi, os, sh);
+  reg_compact<KPT>(key, M, prefix, mask, need, k, idx_at, oi, os, sh);
 }
 
 // ---- long rows, launch 2: exact selection among the candidates (or the whole row)
@@ -749,7 +764,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_candidates_kernel(IndexArgs
     float x[kMaxKpt];
     load_row<kMaxKpt>(src, V, key, x);
     clear_select_lds(sh);
-    select_reg_row<kMaxKpt>(key, x, V, k, oi, os, sh, src, nullptr);
+    select_reg_row<kMaxKpt>(key, x, V, k, oi, os, sh, nullptr);
     return;
   }
   const int nch = (V + kChunk - 1) / kChunk;
@@ -790,9 +805,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_candidates_kernel(IndexArgs
     return;
   }
   // as few registers per thread as the candidate count allows
-  if (M <= 4 * kTopkThreads) select_candidates<4>(spk, spi, gk, gi, coff, nch, M, k, cand_idx, src, oi, os, sh);
-  else if (M <= 8 * kTopkThreads) select_candidates<8>(spk, spi, gk, gi, coff, nch, M, k, cand_idx, src, oi, os, sh);
-  else select_candidates<kCandCap / kTopkThreads>(spk, spi, gk, gi, coff, nch, M, k, cand_idx, src, oi, os, sh);
+  if (M <= 4 * kTopkThreads) select_candidates<4>(spk, spi, gk, gi, coff, nch, M, k, cand_idx, oi, os, sh);
+  else if (M <= 8 * kTopkThreads) select_candidates<8>(spk, spi, gk, gi, coff, nch, M, k, cand_idx, oi, os, sh);
+  else select_candidates<kCandCap / kTopkThreads>(spk, spi, gk, gi, coff, nch, M, k, cand_idx, oi, os, sh);
 }
 
 static int long_chunks(const IndexArgs& A) { return (A.n_max + kChunk - 1) / kChunk; }
