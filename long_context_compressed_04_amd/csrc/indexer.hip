@@ -348,6 +348,10 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_pf(IndexArgs A, f
   const int q_begin = blockIdx.y * kIdxPfQueries;
   const int q_end = min(A.n_q, q_begin + kIdxPfQueries);
   const int r_in = lane >> 4, slot = lane & 15;
+  // the positions of the workgroup's queries, one per lane, read once (a query's V(t) is
+  // then a lane broadcast, not a load the causal skip would wait for)
+  static_assert(kIdxPfQueries <= 64, "one query position per lane");
+  const int qp_lane = q_begin + lane < q_end ? A.q_pos[(long)b * A.n_q + q_begin + lane] : 0;
 
   // q of the queries q0 .. q0 + P - 1 that exist (and, from wave 0, their head
   // weights) into buffer bi
@@ -413,7 +417,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_pf(IndexArgs A, f
     for (int u = 0; u < P; ++u) {
       if (q0 + u >= q_end) break;
       const long row = (long)b * A.n_q + q0 + u;
-      const int V = visible_entries(A.q_pos[row], ne, A.m);
+      const int V = visible_entries(__builtin_amdgcn_readlane(qp_lane, q0 + u - q_begin), ne, A.m);
       const uint8_t* qb = q_lds[bi][u];
       float part[TPW] = {};
       // causal skip: every entry of this wave's tiles at or past V(t) (uniform per wave;
