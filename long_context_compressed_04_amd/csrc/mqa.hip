@@ -244,6 +244,27 @@ __device__ __forceinline__ i16x4_t lds_read_tr16(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)p);
 }
 
+// v plus v of lane ^ 16 (lane ^ 32): the permlane swaps exchange 16-lane rows (32-lane
+// halves) of two registers on the VALU, with no trip through LDS.  Given v twice,
+// the two results hold v of the lane and of its partner, in either order.
+__device__ __forceinline__ float add_xor16(float v) {
+  const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+__device__ __forceinline__ float add_xor32(float v) {
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+
+// Sum over the 16 lanes of each row (every lane gets it): DPP row rotations 1, 2, 4, 8.
+__device__ __forceinline__ float row_sum16f(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xF, 0xF, true));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xF, 0xF, true));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, true));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, true));
+  return v;
+}
+
 __device__ __forceinline__ void load_row_to_lds(const uint8_t* g, uint8_t* l) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
                                    (__attribute__((address_space(3))) void*)l, 16, 0, 0);
@@ -649,10 +670,12 @@ struct RowSrc {
 // split) unit, sixteen waves in three roles on a software pipeline over 32-row tiles
 // (step s: tile s weighed while tile s-1 is accumulated and tile s+2 is gathered):
 //  - logit waves 0..3: wave w takes rows 16 (w >> 1) .. + 15 of tile s against heads
-//    16 (w & 1) .. + 15 over all 512 dims, S^T on v_mfma_f32_16x16x32_bf16 (A = K
-//    rows, B = normalised q held in registers), the rows' sums of squares from the
-//    same A fragments by bf16 dot products, then the softmax weights into LDS: no
-//    partial logits cross waves;
+//    16 (w & 1) .. + 15 over all 512 dims, S on v_mfma_f32_16x16x32_bf16 (A =
+//    normalised q held in registers, B = K rows), so that a lane's four logits all
+//    belong to one row; the rows' sums of squares come from the same K fragments by
+//    bf16 dot products (four independent sums, reduced across the lanes of the row by
+//    permlane swaps), then the softmax weights go into LDS: no partial logits cross
+//    waves and no per-row value crosses lanes of different rows;
 //  - value waves 4..7: O^T for dims 128 (w - 4) .. of tile s-1 on
 //    v_mfma_f32_32x32x16_bf16 (A = V^T by transposing LDS reads, B = the weights of
 //    the previous step);
@@ -661,14 +684,13 @@ struct RowSrc {
 //    grows with the number of waves issuing; these waves read no tile buffer, so
 //    waiting for all but their last four loads needs no help from the compiler.
 // One barrier per step; four tile buffers: two tiles in flight, one being weighed,
-// one being accumulated.  The weights are stored per head in the order the B operand
-// of the 32x32x16 product consumes its k index (rows 4 kg .. 4 kg + 3 and
-// 8 + 4 kg .. of each 16-row step in lane half kg), so each value wave reads one
-// 16-byte fragment per step and head.
+// one being accumulated.  The weights are stored row-major (tile row, head), and the
+// value waves read them with the same transposing reads as the rows, so both
+// operands of the 32x32x16 product take their k index in the same order.
 constexpr int kSdQk = 4, kSdPv = 4, kSdGa = 8;
 constexpr int kSdWaves = kSdQk + kSdPv + kSdGa;
 constexpr int kSdRpw = kTile / kSdGa;   // rows each gather wave loads per tile
-constexpr int kPRow = 2 * kTile + 16;   // bytes per head row of a weight buffer (padded)
+constexpr int kWRow = 2 * 32 + 8;       // bytes per tile row of a weight buffer (32 heads, padded)
 
 // 16 FP8 E4M3 values -> bf16, stored as 32 bytes (exact: E4M3 has 3 mantissa bits).
 __device__ __forceinline__ void fp8x16_to_bf16(uint4 v, uint8_t* dst) {
@@ -697,9 +719,9 @@ void mqa_sd_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml) {
   __shared__ __attribute__((aligned(16))) uint8_t tb1[kTile * kRowB2];
   __shared__ __attribute__((aligned(16))) uint8_t tb2[kTile * kRowB2];
   __shared__ __attribute__((aligned(16))) uint8_t tb3[kTile * kRowB2];
-  __shared__ __attribute__((aligned(16))) uint8_t wts[2][32 * kPRow];
+  __shared__ __attribute__((aligned(16))) uint8_t wts[2][kTile * kWRow];
   __shared__ int32_t slot[kSlotsLds];
-  __shared__ float lsum[2][32];
+  __shared__ __attribute__((aligned(16))) float lsum[2][32];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -836,20 +858,20 @@ void mqa_sd_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml) {
     // ================================================================ logit waves
     const int hb = wave & 1, rb = wave >> 1;
     const int g = lane >> 4, c16 = lane & 15;
-    bf16x8_t qf[16];   // B fragments: head 16 hb + c16, dims 32 ks + 8 g ..
+    bf16x8_t qf[16];   // A fragments: head 16 hb + c16, dims 32 ks + 8 g ..
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks)
       qf[ks] = as_bf16x8(*(const uint4*)(tb3 + (16 * hb + c16) * kRowB2 + 64 * ks + 16 * g));
-    float lh = 0.f;
-    // weight position of rows 4 g .. 4 g + 3 of this wave's 16-row step
-    const int ppos = 16 * rb + 4 * ((g >> 1) | ((g & 1) << 1));
+    float lh[4] = {0.f, 0.f, 0.f, 0.f};   // heads 16 hb + 4 g + r, over this lane's rows
     auto step = [&](auto BUFC, int s) {
       constexpr int BUF = decltype(BUFC)::value;
       if (s < n_tiles) {
         const uint8_t* tile = BUF == 0 ? tb0 : (BUF == 1 ? tb1 : (BUF == 2 ? tb2 : tb3));
         const uint8_t* ka = tile + (16 * rb + c16) * kRowB2 + 16 * g;
+        // row 16 rb + c16 of the tile: masked or not (its slot is read before the product)
+        const bool ok = resolve(R.it0 + s * kTile + 16 * rb + c16) != nullptr;
         f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-        float ss = 0.f;
+        float ss4[4] = {0.f, 0.f, 0.f, 0.f};
         constexpr int PF = 4;
         uint4 a[PF];
 #pragma unroll
@@ -858,27 +880,26 @@ void mqa_sd_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml) {
         for (int ks = 0; ks < 16; ++ks) {
           const uint4 c = a[ks % PF];
           if (ks + PF < 16) a[ks % PF] = *(const uint4*)(ka + 64 * (ks + PF));
-          sacc[ks & 1] = mfma16x16x32(as_bf16x8(c), qf[ks], sacc[ks & 1]);
-          ss = dot2_bf16(c.x, ss);
-          ss = dot2_bf16(c.y, ss);
-          ss = dot2_bf16(c.z, ss);
-          ss = dot2_bf16(c.w, ss);
+          sacc[ks & 1] = mfma16x16x32(qf[ks], as_bf16x8(c), sacc[ks & 1]);
+          ss4[0] = dot2_bf16(c.x, ss4[0]);
+          ss4[1] = dot2_bf16(c.y, ss4[1]);
+          ss4[2] = dot2_bf16(c.z, ss4[2]);
+          ss4[3] = dot2_bf16(c.w, ss4[3]);
         }
+        // sv[r]: head 16 hb + 4 g + r against row 16 rb + c16
         const f32x4_t sv = sacc[0] + sacc[1];
-        ss += __shfl_xor(ss, 16, 64);
-        ss += __shfl_xor(ss, 32, 64);   // sum of squares of row c16
-        const bool ok = resolve(R.it0 + s * kTile + 16 * rb + c16) != nullptr;
+        const float ss = add_xor32(add_xor16((ss4[0] + ss4[1]) + (ss4[2] + ss4[3])));   // row c16's sum of squares
         const float irow = ok ? 1.f / sqrtf(ss * (1.f / kD) + eps) : 0.f;
+        const float li = sl2 * irow;
         float p[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float ir = __shfl(irow, 4 * g + r, 64);   // row 4 g + r
-          const float e = __builtin_amdgcn_exp2f(sv[r] * sl2 * ir);
-          const float w = ir > 0.f ? e : 0.f;
-          lh += w;
-          p[r] = w * ir;
+          const float e = __builtin_amdgcn_exp2f(sv[r] * li);
+          const float w = ok ? e : 0.f;
+          lh[r] += w;
+          p[r] = w * irow;
         }
-        *(uint2*)(wts[s & 1] + (16 * hb + c16) * kPRow + 2 * ppos) =
+        *(uint2*)(wts[s & 1] + (16 * rb + c16) * kWRow + 2 * (16 * hb + 4 * g)) =
             make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
       }
       lds_barrier();
@@ -889,9 +910,9 @@ void mqa_sd_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml) {
       if (s + 2 <= n_tiles) step(std::integral_constant<int, 2>{}, s + 2);
       if (s + 3 <= n_tiles) step(std::integral_constant<int, 3>{}, s + 3);
     }
-    lh += __shfl_xor(lh, 16, 64);
-    lh += __shfl_xor(lh, 32, 64);
-    if (g == 0) lsum[rb][16 * hb + c16] = lh;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) lh[r] = row_sum16f(lh[r]);   // over the wave's 16 rows
+    if (c16 == 0) *(f32x4_t*)&lsum[rb][16 * hb + 4 * g] = f32x4_t{lh[0], lh[1], lh[2], lh[3]};
     lds_barrier();   // the head sums are in LDS
     if (wave == 0 && lane < 32) {
       const float l = lsum[0][lane] + lsum[1][lane];
@@ -927,6 +948,7 @@ void mqa_sd_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml) {
   const int h = lane >> 5, c32 = lane & 31;
   const int G = lane >> 4, sl = lane & 15;
   const int vb_off = (4 * h + (sl >> 2)) * kRowB2 + 256 * pw + (16 * (G & 1) + 4 * (sl & 3)) * 2;
+  const int pb_off = (4 * h + (sl >> 2)) * kWRow + (16 * (G & 1) + 4 * (sl & 3)) * 2;
   f32x16_t o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = f32x16_t{};
@@ -934,9 +956,17 @@ void mqa_sd_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml) {
     constexpr int BV = (decltype(BUFC)::value + 3) % 4;   // tile s-1's buffer
     const uint8_t* const tv = BV == 0 ? tb0 : (BV == 1 ? tb1 : (BV == 2 ? tb2 : tb3));
     if (s >= 1) {
-      const uint8_t* P = wts[(s - 1) & 1] + c32 * kPRow + 16 * h;
-      const bf16x8_t pb0 = as_bf16x8(*(const uint4*)P);
-      const bf16x8_t pb1 = as_bf16x8(*(const uint4*)(P + 32));
+      // P^T fragments by the same transposing reads as V^T: k = rows 4 h .. and 8 + 4 h ..
+      // of each 16-row step, n = head c32
+      const uint8_t* P = wts[(s - 1) & 1] + pb_off;
+      typedef short i16x8_t __attribute__((ext_vector_type(8)));
+      i16x4_t pr[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pr[j] = lds_read_tr16(P + 8 * j * kWRow);
+      const bf16x8_t pb0 = __builtin_bit_cast(bf16x8_t, i16x8_t{pr[0][0], pr[0][1], pr[0][2], pr[0][3],
+                                                                 pr[1][0], pr[1][1], pr[1][2], pr[1][3]});
+      const bf16x8_t pb1 = __builtin_bit_cast(bf16x8_t, i16x8_t{pr[2][0], pr[2][1], pr[2][2], pr[2][3],
+                                                                 pr[3][0], pr[3][1], pr[3][2], pr[3][3]});
       const uint8_t* vb = tv + vb_off;
       i16x4_t v0[8], v1[8];
       auto vaddr = [&](int k) { return vb + (16 * (k & 1)) * kRowB2 + 64 * (k >> 1); };   // k = 2 db + step
