@@ -244,6 +244,11 @@ __device__ __forceinline__ i16x4_t lds_read_tr16(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)p);
 }
 
+// 1/sqrt(x) for a row's mean square (plus eps) in the per-tile paths: the hardware
+// reciprocal square root (one instruction, ~1 ulp) instead of a rounded square root and
+// a division (a dozen instructions on the step's critical path).
+__device__ __forceinline__ float inv_rms(float x) { return __builtin_amdgcn_rsqf(x); }
+
 // v plus v of lane ^ 16 (lane ^ 32): the permlane swaps exchange 16-lane rows (32-lane
 // halves) of two registers on the VALU, with no trip through LDS.  Given v twice,
 // the two results hold v of the lane and of its partner, in either order.
@@ -304,12 +309,12 @@ __device__ __forceinline__ void row_totals(const float (&part)[RPW], int lane, f
   if constexpr (RPW == 8) {
     const float s = rows_total8(part, lane);
     const int rr = 4 * ((lane >> 5) & 1) + 2 * ((lane >> 4) & 1) + ((lane >> 3) & 1);
-    if ((lane & 7) == 0) irms[wave + nw * rr] = ((okmask >> rr) & 1u) ? 1.f / sqrtf(s * (1.f / 512) + eps) : 0.f;
+    if ((lane & 7) == 0) irms[wave + nw * rr] = ((okmask >> rr) & 1u) ? inv_rms(s * (1.f / 512) + eps) : 0.f;
   } else {
 #pragma unroll
     for (int rr = 0; rr < RPW; ++rr) {
       const float s = wave_sum(part[rr]);
-      if (lane == 0) irms[wave + nw * rr] = ((okmask >> rr) & 1u) ? 1.f / sqrtf(s * (1.f / 512) + eps) : 0.f;
+      if (lane == 0) irms[wave + nw * rr] = ((okmask >> rr) & 1u) ? inv_rms(s * (1.f / 512) + eps) : 0.f;
     }
   }
 }
@@ -889,7 +894,7 @@ void mqa_sd_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml) {
         // sv[r]: head 16 hb + 4 g + r against row 16 rb + c16
         const f32x4_t sv = sacc[0] + sacc[1];
         const float ss = add_xor32(add_xor16((ss4[0] + ss4[1]) + (ss4[2] + ss4[3])));   // row c16's sum of squares
-        const float irow = ok ? 1.f / sqrtf(ss * (1.f / kD) + eps) : 0.f;
+        const float irow = ok ? inv_rms(ss * (1.f / kD) + eps) : 0.f;
         const float li = sl2 * irow;
         float p[4];
 #pragma unroll
@@ -1259,7 +1264,7 @@ void mqa_w8_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml, con
       const float s = rows_total4(part, lane);
       const int rr = 2 * ((lane >> 5) & 1) + ((lane >> 4) & 1);
       if ((lane & 15) == 0)
-        irms[BUF][wave + kW8Waves * rr] = ((okm[BUF] >> rr) & 1u) ? 1.f / sqrtf(s * (1.f / kD) + A.eps) : 0.f;
+        irms[BUF][wave + kW8Waves * rr] = ((okm[BUF] >> rr) & 1u) ? inv_rms(s * (1.f / kD) + A.eps) : 0.f;
       __builtin_amdgcn_sched_barrier(0);
     }
     // ---- partial S^T over this wave's 256 dims: 16 k-steps
