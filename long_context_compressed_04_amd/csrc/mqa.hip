@@ -1459,8 +1459,6 @@ __global__ __launch_bounds__(128) void mqa_combine_kernel(MqaArgs A, MqaLaunch L
   const int head = blockIdx.x;
   const long row = blockIdx.y;
   const int S = L.nsplit;
-  __shared__ float wts[kMaxSplit];
-  __shared__ float s_M, s_L;
   const int d0 = threadIdx.x * 4;
   const uint16_t* po = part_o + ((row * S) * A.heads + head) * kD + d0;
   const long sstride = (long)A.heads * kD;
@@ -1469,41 +1467,35 @@ __global__ __launch_bounds__(128) void mqa_combine_kernel(MqaArgs A, MqaLaunch L
   uint2 pre[kPre];
 #pragma unroll
   for (int s = 0; s < kPre; ++s) pre[s] = *(const uint2*)(po + min(s, S - 1) * sstride);   // (no branch)
-  if (threadIdx.x < 64) {   // one wave: w_s = l_s 2^(m_s - M), L = sum_s w_s
-    const int lane = threadIdx.x;
-    float m2[2], l2[2];
+  // (m_s, l_s) are the same for every thread of the workgroup: each thread forms the
+  // weights w_s = l_s 2^(m_s - M) and their sum itself, from uniform loads, with no
+  // cross-lane step or barrier on the way to the first multiply
+  const float* pm = part_ml + ((row * S) * A.heads + head) * 2;
+  const long mstride = (long)A.heads * 2;
+  float2 ml[kPre];   // requested together (no branch), so their latencies overlap
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int sp = lane + 64 * j;
-      const float* pm = part_ml + ((row * S + sp) * A.heads + head) * 2;
-      m2[j] = sp < S ? pm[0] : -INFINITY;
-      l2[j] = sp < S ? pm[1] : 0.f;
-    }
-    const float M = wave_max(fmaxf(m2[0], m2[1]));
-    float ls = 0.f;
+  for (int s = 0; s < kPre; ++s) ml[s] = *(const float2*)(pm + min(s, S - 1) * mstride);
+  float M = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int sp = lane + 64 * j;
-      const float w = (m2[j] == -INFINITY) ? 0.f : l2[j] * exp2f(m2[j] - M);
-      if (sp < S) wts[sp] = w;
-      ls += w;
-    }
-    ls = wave_sum(ls);
-    if (lane == 0) {
-      s_M = M;
-      s_L = ls;
-    }
-  }
-  __syncthreads();
-  const float Lsum = s_L;
-  const SoftmaxEnd fin = softmax_end(s_M, Lsum, A.sink, head);
-  const float inv_l = fin.mul;
+  for (int s = 0; s < kPre; ++s) M = fmaxf(M, ml[s].x);   // (repeats of the last split change nothing)
+  for (int s = kPre; s < S; ++s) M = fmaxf(M, pm[s * mstride]);
+  auto weight = [&](float m, float l) { return m == -INFINITY ? 0.f : l * exp2f(m - M); };
+  float Lsum = 0.f;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < kPre; ++s)
-    if (s < S) acc += partial4_value(pre[s]) * wts[s];
-#pragma unroll 8
-  for (int s = kPre; s < S; ++s) acc += partial4_value(*(const uint2*)(po + s * sstride)) * wts[s];
+    if (s < S) {
+      const float w = weight(ml[s].x, ml[s].y);
+      Lsum += w;
+      acc += partial4_value(pre[s]) * w;
+    }
+  for (int s = kPre; s < S; ++s) {
+    const float w = weight(pm[s * mstride], pm[s * mstride + 1]);
+    Lsum += w;
+    acc += partial4_value(*(const uint2*)(po + s * sstride)) * w;
+  }
+  const SoftmaxEnd fin = softmax_end(M, Lsum, A.sink, head);
+  const float inv_l = fin.mul;
   float v[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) v[r] = acc[r] * inv_l * (A.gamma ? A.gamma[d0 + r] : 1.f);
