@@ -43,16 +43,49 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+// ---- cross-lane steps on the VALU (no trip through LDS, unlike a shuffle)
+// v of lane l ^ 1, l ^ 2 (DPP quad permutations), 7 - l within 8 lanes (half mirror),
+// 15 - l within 16 (mirror): every lane has a source, and summing over these pairs
+// gives every lane of a group the same bits.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+// the value of lane ^ 16 (^ 32) beside the lane's own: a permlane swap of v with
+// itself exchanges odd and even 16-lane rows (the two 32-lane halves); the pair it
+// returns holds both values, in an order that depends on the lane
+__device__ __forceinline__ float add_xor16(float v) {
+  const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
 }
+__device__ __forceinline__ float add_xor32(float v) {
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+// sum (max) over each 16-lane row; every lane of the row gets the same value
+__device__ __forceinline__ float row_sum16f(float v) {
+  v += dpp_f32<kDppXor1>(v);
+  v += dpp_f32<kDppXor2>(v);
+  v += dpp_f32<kDppHalfMirror>(v);
+  return v + dpp_f32<kDppMirror>(v);
+}
+__device__ __forceinline__ float row_max16f(float v) {
+  v = fmaxf(v, dpp_f32<kDppXor1>(v));
+  v = fmaxf(v, dpp_f32<kDppXor2>(v));
+  v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+  return fmaxf(v, dpp_f32<kDppMirror>(v));
+}
+__device__ __forceinline__ float wave_sum(float v) { return add_xor32(add_xor16(row_sum16f(v))); }
+__device__ __forceinline__ float wave_max(float v) { return max_xor32(max_xor16(row_max16f(v))); }
 
 // Number of compressed entries visible to the query at absolute position t:
 // only complete blocks, V(t) = min(N, floor((t+1)/m)).

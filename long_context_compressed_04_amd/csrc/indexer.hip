@@ -174,7 +174,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_mfma(IndexArgs A,
 #pragma unroll
         for (int r = 0; r < 16; ++r) part = fmaf(wl[hb][r], fmaxf(acc[r], 0.f), part);
       }
-      part += __shfl_xor(part, 32, 64);
+      part = add_xor32(part);
       const int e = tile0 + col;
       if (half == 0 && e < A.n_max) scores[row * A.n_max + e] = (e < V) ? part : -INFINITY;
     }
@@ -306,7 +306,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_lds(IndexArgs A, 
       for (int g = 0; g < 4; ++g)
 #pragma unroll
         for (int k = 0; k < 4; ++k) part = fmaf(wl[hb][g][k], fmaxf(acc[hb][4 * g + k], 0.f), part);
-    part += __shfl_xor(part, 32, 64);
+    part = add_xor32(part);
     const bool valid = SEL ? key_row(e) >= 0 : e < V;
     if (half == 0 && e < A.n_max) scores[row * A.n_max + e] = valid ? part : -INFINITY;
   };
@@ -448,7 +448,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_pf(IndexArgs A, f
         }
       }
 #pragma unroll
-      for (int t = 0; t < TPW; ++t) held[u][t] = part[t] + __shfl_xor(part[t], 32, 64);
+      for (int t = 0; t < TPW; ++t) held[u][t] = add_xor32(part[t]);
       held_row[u] = row;
       held_V[u] = V;
       n_held = u + 1;

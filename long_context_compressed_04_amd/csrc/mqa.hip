@@ -249,27 +249,6 @@ __device__ __forceinline__ i16x4_t lds_read_tr16(const uint8_t* p) {
 // a division (a dozen instructions on the step's critical path).
 __device__ __forceinline__ float inv_rms(float x) { return __builtin_amdgcn_rsqf(x); }
 
-// v plus v of lane ^ 16 (lane ^ 32): the permlane swaps exchange 16-lane rows (32-lane
-// halves) of two registers on the VALU, with no trip through LDS.  Given v twice,
-// the two results hold v of the lane and of its partner, in either order.
-__device__ __forceinline__ float add_xor16(float v) {
-  const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
-}
-__device__ __forceinline__ float add_xor32(float v) {
-  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
-}
-
-// Sum over the 16 lanes of each row (every lane gets it): DPP row rotations 1, 2, 4, 8.
-__device__ __forceinline__ float row_sum16f(float v) {
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xF, 0xF, true));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xF, 0xF, true));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, true));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, true));
-  return v;
-}
-
 __device__ __forceinline__ void load_row_to_lds(const uint8_t* g, uint8_t* l) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
                                    (__attribute__((address_space(3))) void*)l, 16, 0, 0);
@@ -279,28 +258,25 @@ __device__ __forceinline__ void load_row_to_lds(const uint8_t* g, uint8_t* l) {
 // share of row rr.  A row-splitting butterfly: each exchange step halves the rows a
 // lane keeps; the lane then holds the total of row row_of_lane(lane).
 __device__ __forceinline__ float rows_total8(const float (&p)[8], int lane) {
-  bool up = (lane & 32) != 0;
-  float a[4];
+  // a permlane swap of two registers hands each half of the lanes the other half's copy
+  // of the registers it keeps: lanes 0..31 keep rows 0..3, lanes 32..63 rows 4..7
+  float a[4], c[2];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float send = up ? p[j] : p[4 + j];
-    const float keep = up ? p[4 + j] : p[j];
-    a[j] = keep + __shfl_xor(send, 32, 64);
+    const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[j]), __float_as_uint(p[4 + j]), false, false);
+    a[j] = __uint_as_float(t[0]) + __uint_as_float(t[1]);
   }
-  up = (lane & 16) != 0;
-  float c[2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const float send = up ? a[j] : a[2 + j];
-    const float keep = up ? a[2 + j] : a[j];
-    c[j] = keep + __shfl_xor(send, 16, 64);
+  for (int j = 0; j < 2; ++j) {   // even 16-lane rows keep a[j], odd ones a[2 + j]
+    const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(a[j]), __float_as_uint(a[2 + j]), false, false);
+    c[j] = __uint_as_float(t[0]) + __uint_as_float(t[1]);
   }
-  up = (lane & 8) != 0;
-  float s = (up ? c[1] : c[0]) + __shfl_xor(up ? c[0] : c[1], 8, 64);
-  s += __shfl_xor(s, 4, 64);
-  s += __shfl_xor(s, 2, 64);
-  s += __shfl_xor(s, 1, 64);
-  return s;
+  const bool up = (lane & 8) != 0;   // lanes 8..15 of a row keep c[1]; lane ^ 8 is 15 - lane's mirror pair
+  // (mirror pairs lane i with 15 - i: the other 8-lane half, as lane ^ 8 would)
+  float v = (up ? c[1] : c[0]) + dpp_f32<kDppMirror>(up ? c[0] : c[1]);
+  v += dpp_f32<kDppXor1>(v);
+  v += dpp_f32<kDppXor2>(v);
+  return v + dpp_f32<kDppHalfMirror>(v);
 }
 
 template <int RPW>
@@ -410,8 +386,7 @@ __device__ __forceinline__ void mqa_tiles(const TileCtx& C, const bf16x8_t (&qf)
       float tmax = lg[0];
 #pragma unroll
       for (int r = 1; r < 8; ++r) tmax = fmaxf(tmax, lg[r]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      tmax = max_xor32(max_xor16(tmax));
       const float m_new = fixed ? m_run : fmaxf(m_run, tmax);
       const bool none = m_new == -INFINITY;   // nothing valid yet for this head
       const float corr = none ? 1.f : exp2f(m_run - m_new);
@@ -428,7 +403,7 @@ __device__ __forceinline__ void mqa_tiles(const TileCtx& C, const bf16x8_t (&qf)
     } else {
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
-        const float p = exp2f(lg[r] - m_run);   // masked: exp2(-inf) = 0
+        const float p = __builtin_amdgcn_exp2f(lg[r] - m_run);   // masked: exp2(-inf) = 0
         psum += p;
         pw[r] = p * ir[r];                        // weight on the raw row (1/rms folded)
       }
@@ -522,8 +497,7 @@ __global__ __launch_bounds__(NW * 64) void mqa_bf16_kernel(MqaArgs A, MqaLaunch 
         ss = fmaf(lo, lo, fmaf(hi, hi, ss));
       }
     }
-    ss += __shfl_xor(ss, 16, 64);
-    ss += __shfl_xor(ss, 32, 64);
+    ss = add_xor32(add_xor16(ss));
     const float qinv = 1.f / sqrtf(ss * (1.f / kD) + A.eps);
     float uu = 0.f;
 #pragma unroll
@@ -541,8 +515,7 @@ __global__ __launch_bounds__(NW * 64) void mqa_bf16_kernel(MqaArgs A, MqaLaunch 
       }
       qf[ks] = as_bf16x8(make_uint4(o4[0], o4[1], o4[2], o4[3]));
     }
-    uu += __shfl_xor(uu, 16, 64);
-    uu += __shfl_xor(uu, 32, 64);
+    uu = add_xor32(add_xor16(uu));
     m_fix = A.scale * kLog2e * sqrtf((float)kD * uu) * 1.0001f + 1e-6f;   // log2 units
   }
   // A fixed maximum needs no rescaling: exp2(l - M) >= 2^(-2M) stays a normal
@@ -559,8 +532,7 @@ __global__ __launch_bounds__(NW * 64) void mqa_bf16_kernel(MqaArgs A, MqaLaunch 
   else mqa_tiles<NW, true>(C, qf, fixed, m_run, l_run, o);
 
   // ---- finish: total sum per head across the 4 lane groups
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
+  l_run = add_xor32(add_xor16(l_run));
   if (L.nsplit == 1) {
     const SoftmaxEnd fin = softmax_end(m_run, l_run, A.sink, head);
     const float inv_l = fin.mul;
@@ -1079,21 +1051,15 @@ constexpr int kW8Stage = 64 + 4;           // fp32 words per head row of the out
 // row rr): a row-splitting butterfly; the lane ends with the total of row
 // 2 * bit5(lane) + bit4(lane).
 __device__ __forceinline__ float rows_total4(const float (&p)[4], int lane) {
-  bool up = (lane & 32) != 0;
   float a[2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const float send = up ? p[j] : p[2 + j];
-    const float keep = up ? p[2 + j] : p[j];
-    a[j] = keep + __shfl_xor(send, 32, 64);
+  for (int j = 0; j < 2; ++j) {   // lanes 0..31 keep rows 0, 1; lanes 32..63 rows 2, 3
+    const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[j]), __float_as_uint(p[2 + j]), false, false);
+    a[j] = __uint_as_float(t[0]) + __uint_as_float(t[1]);
   }
-  up = (lane & 16) != 0;
-  float s = (up ? a[1] : a[0]) + __shfl_xor(up ? a[0] : a[1], 16, 64);
-  s += __shfl_xor(s, 8, 64);
-  s += __shfl_xor(s, 4, 64);
-  s += __shfl_xor(s, 2, 64);
-  s += __shfl_xor(s, 1, 64);
-  return s;
+  // even 16-lane rows keep a[0], odd ones a[1]
+  const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(a[0]), __float_as_uint(a[1]), false, false);
+  return row_sum16f(__uint_as_float(t[0]) + __uint_as_float(t[1]));
 }
 
 template <bool PRE>
@@ -1219,7 +1185,7 @@ void mqa_w8_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml, con
     float ss = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) ss = sumsq_bf16x8(qraw[ks], ss);
-    ss += __shfl_xor(ss, 32, 64);
+    ss = add_xor32(ss);
     red[wave][lane] = ss;
     lds_barrier();
     const float qinv = 1.f / sqrtf((ss + red[wave ^ 4][lane]) * (1.f / kD) + A.eps);
@@ -1378,7 +1344,7 @@ void mqa_w8_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml, con
 
   // ---- softmax denominators: head 32 hb + c32 summed over the two lane halves here,
   // then over the pair (hb, 0), (hb, 1) through LDS
-  l_run += __shfl_xor(l_run, 32, 64);
+  l_run = add_xor32(l_run);
   lds_barrier();   // every wave is past its last tile: the tile buffers and red are free
   red[wave][lane] = l_run;
   lds_barrier();

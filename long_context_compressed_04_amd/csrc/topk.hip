@@ -125,7 +125,7 @@ __device__ __forceinline__ void pick_digit(SelShared& sh, uint32_t prefix, int s
     const uint32_t inc = wave_inclusive_sum(s);
     const uint64_t hit = __ballot(inc - s < need && need <= inc);
     const int L = hit ? (int)__builtin_ctzll(hit) : 0;
-    const uint32_t aboveL = (uint32_t)__shfl((int)(inc - s), L, 64);
+    const uint32_t aboveL = (uint32_t)__builtin_amdgcn_readlane((int)(inc - s), L);   // (L is uniform)
     const int b = kBins - 1 - 32 * L - lane;
     const uint32_t c = lane < 32 ? sh.hist[hslot(b)] : 0u;
     const uint32_t inc2 = aboveL + wave_inclusive_sum(c);
@@ -793,7 +793,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_candidates_kernel(IndexArgs
       const uint32_t v = c < nch ? L.counts[row * L.chunks + c] : 0u;
       const uint32_t inc = wave_inclusive_sum(v);
       if (c < nch) coff[c] = run + inc - v;
-      run += (uint32_t)__shfl((int)inc, 63, 64);
+      run += (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
     }
     if (lane == 0) coff[nch] = run;
   }
