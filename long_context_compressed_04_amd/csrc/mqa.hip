@@ -1112,6 +1112,8 @@ void mqa_w8_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml, con
   }
   const float* inv_kv_b = PRE ? inv_kv + (long)b * A.kv_cap : nullptr;
   const float* inv_raw_b = PRE ? inv_raw + (long)b * A.raw_cap : nullptr;
+  // inv_raw lies in the same workspace as inv_kv, after it
+  const int raw_norm_off = PRE ? __builtin_amdgcn_readfirstlane((int)(inv_raw_b - inv_kv_b)) : 0;
   // this lane's query head (QK role) and its dims 256 dh + 16 ks + 8 h + [0, 8)
   const uint16_t* qrow = (const uint16_t*)A.q + (row * A.heads + hg * 128 + 32 * hb + c32) * kD + 256 * dh + 8 * h;
   uint4 qraw[16];
@@ -1120,21 +1122,33 @@ void mqa_w8_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml, con
   lds_barrier();   // the slots are in LDS
 
   const int n_tiles = (R.it1 - R.it0 + kTile - 1) / kTile;
-  // tile row item -> source row (nullptr: masked) and, with PRE, its 1/rms (the zero
-  // float for a masked row, whose weight is then 0)
-  auto resolve = [&](int item, const float*& ip) -> const uint8_t* {
-    ip = &g_zero_f32;
-    if (item >= R.it1) return nullptr;
-    if (item < R.n_first) {
-      const int e = R.dense ? item : slot[item - R.it0];
-      if (e < 0 || e >= R.kv_rows) return nullptr;
-      if (PRE) ip = inv_kv_b + e;
-      return R.kv + (long)e * (kD * 2);
-    }
-    const int r = R.win_lo + (item - R.n_first) - R.raw_base;
-    if (r < 0 || r >= R.raw_cap) return nullptr;
-    if (PRE) ip = inv_raw_b + r;
-    return R.raw + (long)r * (kD * 2);
+  // Gathering a tile takes the index slots of its rows, read from LDS one step ahead
+  // (slots_of, at the start of a step, where the read's latency hides behind the
+  // products), then turns them into row addresses without branches (resolve).
+  struct Slots {
+    int row;   // slot of this lane's row wave + 8 (lane % 4)
+    int nrm;   // PRE, wave 0: slot of row c32
+  };
+  auto slot_at = [&](int item) -> int {   // (an in-bounds read; ignored where no slot applies)
+    return R.use_slots ? slot[min(max(item - R.it0, 0), kSlotsLds - 1)] : 0;
+  };
+  auto slots_of = [&](int ti) -> Slots {
+    const int item0 = R.it0 + ti * kTile;
+    Slots sv;
+    sv.row = slot_at(item0 + wave + kW8Waves * (lane & (kW8Rpw - 1)));
+    sv.nrm = (PRE && wave == 0) ? slot_at(item0 + c32) : 0;
+    return sv;
+  };
+  // tile row item (its slot sv) -> source row (nullptr: masked) and, with PRE, its
+  // 1/rms (the zero float for a masked row, whose weight is then 0)
+  auto resolve = [&](int item, int sv, const float*& ip) -> const uint8_t* {
+    const bool first = item < R.n_first;
+    const int e = first ? (R.dense ? item : sv) : R.win_lo + (item - R.n_first) - R.raw_base;
+    const bool ok = item < R.it1 && e >= 0 && e < (first ? R.kv_rows : R.raw_cap);
+    // (one base, a 32-bit element offset per lane: no 64-bit pointer per lane lives
+    // across the loop)
+    if (PRE) ip = ok ? inv_kv_b + (first ? e : raw_norm_off + e) : &g_zero_f32;
+    return ok ? (first ? R.kv : R.raw) + (long)e * (kD * 2) : nullptr;
   };
   // Gathering tile ti: lane rr of every wave resolves the wave's row wave + 8 rr (a
   // masked row reads the zero row), with PRE wave 0's lane l also the 1/rms of row l.
@@ -1143,13 +1157,13 @@ void mqa_w8_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml, con
     const float* ip;   // PRE: 1/rms address of row c32
     uint32_t ok;       // rows that exist
   };
-  auto resolve_tile = [&](int ti) -> Gather {
+  auto resolve_tile = [&](int ti, const Slots& sv) -> Gather {
     Gather g;
     const int item0 = R.it0 + ti * kTile;
     g.ip = &g_zero_f32;
-    if (PRE && wave == 0) resolve(item0 + c32, g.ip);
+    if (PRE && wave == 0) resolve(item0 + c32, sv.nrm, g.ip);
     const float* unused;
-    const uint8_t* pl = resolve(item0 + wave + kW8Waves * (lane & (kW8Rpw - 1)), unused);
+    const uint8_t* pl = resolve(item0 + wave + kW8Waves * (lane & (kW8Rpw - 1)), sv.row, unused);
     g.ok = (uint32_t)__ballot(pl != nullptr) & ((1u << kW8Rpw) - 1u);
     const uint64_t pv = (uint64_t)(pl ? pl : g_zero_row);
     g.lo = (uint32_t)pv;
@@ -1167,8 +1181,8 @@ void mqa_w8_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml, con
                        (uint32_t)__builtin_amdgcn_readlane((int)g.lo, rr);
     load_row_to_lds((const uint8_t*)p + 16 * lane, dst + (wave + kW8Waves * rr) * kRowB2);
   };
-  auto issue = [&](int ti, uint8_t* dst, float* irms_dst) -> uint32_t {
-    const Gather g = resolve_tile(ti);
+  auto issue = [&](int ti, const Slots& sv, uint8_t* dst, float* irms_dst) -> uint32_t {
+    const Gather g = resolve_tile(ti, sv);
     load_norms(g, irms_dst);
 #pragma unroll 1
     for (int rr = 0; rr < kW8Rpw; ++rr) load_row(g, rr, dst);
@@ -1176,8 +1190,8 @@ void mqa_w8_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml, con
   };
   auto buf_ptr = [&](int bi) -> uint8_t* { return bi == 0 ? tb0 : (bi == 1 ? tb1 : tb2); };
   uint32_t okm[kNB] = {0, 0, 0};
-  if (n_tiles > 0) okm[0] = issue(0, tb0, irms[0]);
-  if (n_tiles > 1) okm[1] = issue(1, tb1, irms[1]);
+  if (n_tiles > 0) okm[0] = issue(0, slots_of(0), tb0, irms[0]);
+  if (n_tiles > 1) okm[1] = issue(1, slots_of(1), tb1, irms[1]);
 
   // ---- u = q / rms(q): the pair (hb, 0), (hb, 1) holds the two dim halves of a head
   bf16x8_t qf[16];
@@ -1218,6 +1232,8 @@ void mqa_w8_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml, con
     constexpr int BUF = decltype(BUFC)::value;
     constexpr int DH = decltype(DHC)::value;
     uint8_t* const tile = BUF == 0 ? tb0 : (BUF == 1 ? tb1 : tb2);
+    // the slots of tile ti + 2, for its gather after the first barrier
+    const Slots sv2 = slots_of(ti + 2);
     // tile ti is in LDS (waited before the previous barrier)
     if (!PRE) {
       // 1/rms of the 4 rows this wave loaded (read before the barrier: they are its own)
@@ -1255,9 +1271,20 @@ void mqa_w8_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml, con
       xs[wave][0][lane] = f32x4_t{s[g], s[g + 1], s[g + 2], s[g + 3]};
       xs[wave][1][lane] = f32x4_t{s[g + 4], s[g + 5], s[g + 6], s[g + 7]};
     }
-    // every wave is past tile ti - 1 (its P V): its buffer takes tile ti + 2
     lds_barrier();
-    if (ti + 2 < n_tiles) okm[(BUF + 2) % kNB] = issue(ti + 2, buf_ptr((BUF + 2) % kNB), irms[(BUF + 2) % kNB]);
+    // tile ti + 2: its rows' addresses (wave-uniform: scalar registers until the P V
+    // phase issues the loads) and, with PRE, the load of its row norms
+    const bool gi = ti + 2 < n_tiles;
+    uint64_t growp[kW8Rpw] = {};
+    if (gi) {
+      const Gather gn = resolve_tile(ti + 2, sv2);
+      load_norms(gn, irms[(BUF + 2) % kNB]);
+      okm[(BUF + 2) % kNB] = gn.ok;
+#pragma unroll
+      for (int rr = 0; rr < kW8Rpw; ++rr)
+        growp[rr] = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)gn.hi, rr) << 32) |
+                    (uint32_t)__builtin_amdgcn_readlane((int)gn.lo, rr);
+    }
     // rows of k-step dh: s[8 dh + k] is row 16 dh + 8 (k / 4) + 4 h + k % 4
     {
       const f32x4_t x0 = xs[wave ^ 4][0][lane], x1 = xs[wave ^ 4][1][lane];
@@ -1288,17 +1315,17 @@ void mqa_w8_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml, con
       l_run += psum;
       pbuf[hb][DH][lane] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
     }
-    // this wave's loads of tile ti + 1 are done (those of tile ti + 2 may be in flight);
-    // after the barrier every wave's are, and every wave's P of tile ti is in LDS
-    if (ti + 2 < n_tiles) {
-      if (PRE && wave == 0) wait_vmcnt<kW8Rpw + 1>();
-      else wait_vmcnt<kW8Rpw>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    // this wave's loads of tile ti + 1 (the only ones in flight) are done; after the
+    // barrier every wave's are, and every wave's P of tile ti is in LDS
+    wait_vmcnt<0>();
     lds_barrier();
-    // ---- O^T[128 dq .. + 128 dims x 64 heads] += V^T . P^T
+    // ---- O^T[128 dq .. + 128 dims x 64 heads] += V^T . P^T, with the gather of tile
+    // ti + 2 into the buffer of tile ti - 1 (every wave is past it since the first
+    // barrier): one row after every second pair of products, so that a load that waits for room in the memory pipeline
+    // holds up this wave while the products already issued, and the other wave of the
+    // SIMD, keep the matrix unit busy
     {
+      uint8_t* const gdst = buf_ptr((BUF + 2) % kNB);
       const bf16x8_t p00 = as_bf16x8(pbuf[2 * hp][0][lane]), p01 = as_bf16x8(pbuf[2 * hp][1][lane]);
       const bf16x8_t p10 = as_bf16x8(pbuf[2 * hp + 1][0][lane]), p11 = as_bf16x8(pbuf[2 * hp + 1][1][lane]);
       const uint8_t* vb = tile + vb_base;
@@ -1320,10 +1347,13 @@ void mqa_w8_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml, con
         const bf16x8_t va = __builtin_bit_cast(bf16x8_t, i16x8_t{c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]});
         o[0][f >> 1] = mfma32x32x16(va, (f & 1) ? p01 : p00, o[0][f >> 1]);
         o[1][f >> 1] = mfma32x32x16(va, (f & 1) ? p11 : p10, o[1][f >> 1]);
+        if (gi && (f & 1))
+          load_row_to_lds((const uint8_t*)growp[f >> 1] + 16 * lane, gdst + (wave + kW8Waves * (f >> 1)) * kRowB2);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
+  static_assert(kW8Rpw == 4, "one gathered row per two of the eight P V k-steps");
   // tile 0 in LDS (tile 1 may be in flight)
   if (n_tiles > 1) {
     if (PRE && wave == 0) wait_vmcnt<kW8Rpw + 1>();
