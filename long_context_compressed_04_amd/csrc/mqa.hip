@@ -1009,23 +1009,27 @@ void mqa_sd_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml) {
 // ---------------------------------------------------------------------------------
 // Row 1/rms pre-pass for many queries (prefill): a compressed entry is normalised
 // once, not once per query that selects it.
-__device__ float g_zero_f32;   // 1/rms of a missing row: weight 0
 
-// One wave per row: 1/rms of every row of kv (all kv_cap rows of every sequence) and
-// kv_raw, written to inv_kv [batch, kv_cap] and inv_raw [batch, raw_cap].
-__global__ __launch_bounds__(256) void row_inv_rms_kernel(MqaArgs A, float* inv_kv, float* inv_raw) {
+// One wave per row: every row of kv (all kv_cap rows of every sequence) and kv_raw,
+// RMS-normalised (unit weight) and rounded to bf16, into kvn [batch, kv_cap, 512] and
+// rawn [batch, raw_cap, 512]: the keys and values the attention itself reads.
+__global__ __launch_bounds__(256) void row_normalize_kernel(MqaArgs A, uint16_t* kvn, uint16_t* rawn) {
   const long gw = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const long n_kv = (long)A.batch * A.kv_cap, n_raw = (long)A.batch * A.raw_cap;
   if (gw >= n_kv + n_raw) return;
   const uint8_t* rowp = gw < n_kv ? (const uint8_t*)A.kv + gw * (kD * 2)
                                   : (const uint8_t*)A.kv_raw + (gw - n_kv) * (kD * 2);
-  const float ss = wave_sum(sumsq_bf16x8(*(const uint4*)(rowp + 16 * lane), 0.f));
-  if (lane == 0) {
-    const float r = 1.f / sqrtf(ss * (1.f / kD) + A.eps);
-    if (gw < n_kv) inv_kv[gw] = r;
-    else inv_raw[gw - n_kv] = r;
-  }
+  uint16_t* dst = gw < n_kv ? kvn + gw * kD : rawn + (gw - n_kv) * kD;
+  const uint4 v = *(const uint4*)(rowp + 16 * lane);
+  const float ss = wave_sum(sumsq_bf16x8(v, 0.f));
+  const float r = 1.f / sqrtf(ss * (1.f / kD) + A.eps);
+  const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o4[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    o4[k] = pack_bf16x2(__uint_as_float(w4[k] << 16) * r, __uint_as_float(w4[k] & 0xffff0000u) * r);
+  *(uint4*)(dst + 8 * lane) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
 }
 
 // ---------------------------------------------------------------------------------
@@ -1040,9 +1044,10 @@ __global__ __launch_bounds__(256) void row_inv_rms_kernel(MqaArgs A, float* inv_
 //   PV: wave w = (head pair hp = w & 1, dim quarter dq = w >> 1) accumulates
 //       O^T[128 dims x 64 heads]; each V^T fragment (ds_read_b64_tr_b16, the slow
 //       LDS read) feeds two MFMAs.
-// Row 1/rms: from the per-cache pre-pass (PRE, many queries: each row normalised
-// once), or from the gathered tile itself, each wave summing the 4 rows it loaded
-// (few queries: a pre-pass would read the whole cache for a few hundred rows).
+// Row RMSNorm: PRE (many queries) reads a normalised bf16 copy of the cache made by a
+// pre-pass (each row normalised once; the tile's per-row factor is then 1, or 0 for a
+// masked row); otherwise each wave sums the squares of the 4 rows it loaded (few
+// queries: a pre-pass would read the whole cache for a few hundred rows).
 constexpr int kW8Waves = 8;
 constexpr int kW8Rpw = kTile / kW8Waves;   // rows each wave gathers per tile
 constexpr int kW8Stage = 64 + 4;           // fp32 words per head row of the output staging
@@ -1064,8 +1069,8 @@ __device__ __forceinline__ float rows_total4(const float (&p)[4], int lane) {
 
 template <bool PRE>
 __global__ __launch_bounds__(kW8Waves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void mqa_w8_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml, const float* inv_kv,
-                   const float* inv_raw) {
+void mqa_w8_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml, const uint16_t* kvn,
+                   const uint16_t* rawn) {
   __shared__ __attribute__((aligned(16))) uint8_t tb0[kTile * kRowB2];
   __shared__ __attribute__((aligned(16))) uint8_t tb1[kTile * kRowB2];
   __shared__ __attribute__((aligned(16))) uint8_t tb2[kTile * kRowB2];
@@ -1110,10 +1115,10 @@ void mqa_w8_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml, con
         slot[i] = (it < min(R.it1, R.n_first)) ? src.idx[it] : -1;
       }
   }
-  const float* inv_kv_b = PRE ? inv_kv + (long)b * A.kv_cap : nullptr;
-  const float* inv_raw_b = PRE ? inv_raw + (long)b * A.raw_cap : nullptr;
-  // inv_raw lies in the same workspace as inv_kv, after it
-  const int raw_norm_off = PRE ? __builtin_amdgcn_readfirstlane((int)(inv_raw_b - inv_kv_b)) : 0;
+  if (PRE) {   // rows from the normalised copy (same layout as kv and kv_raw)
+    R.kv = (const uint8_t*)(kvn + (long)b * A.kv_cap * kD);
+    R.raw = (const uint8_t*)(rawn + (long)b * A.raw_cap * kD);
+  }
   // this lane's query head (QK role) and its dims 256 dh + 16 ks + 8 h + [0, 8)
   const uint16_t* qrow = (const uint16_t*)A.q + (row * A.heads + hg * 128 + 32 * hb + c32) * kD + 256 * dh + 8 * h;
   uint4 qraw[16];
@@ -1127,7 +1132,6 @@ void mqa_w8_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml, con
   // products), then turns them into row addresses without branches (resolve).
   struct Slots {
     int row;   // slot of this lane's row wave + 8 (lane % 4)
-    int nrm;   // PRE, wave 0: slot of row c32
   };
   auto slot_at = [&](int item) -> int {   // (an in-bounds read; ignored where no slot applies)
     return R.use_slots ? slot[min(max(item - R.it0, 0), kSlotsLds - 1)] : 0;
@@ -1136,45 +1140,35 @@ void mqa_w8_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml, con
     const int item0 = R.it0 + ti * kTile;
     Slots sv;
     sv.row = slot_at(item0 + wave + kW8Waves * (lane & (kW8Rpw - 1)));
-    sv.nrm = (PRE && wave == 0) ? slot_at(item0 + c32) : 0;
     return sv;
   };
-  // tile row item (its slot sv) -> source row (nullptr: masked) and, with PRE, its
-  // 1/rms (the zero float for a masked row, whose weight is then 0)
-  auto resolve = [&](int item, int sv, const float*& ip) -> const uint8_t* {
+  // tile row item (its slot sv) -> source row (nullptr: masked)
+  auto resolve = [&](int item, int sv) -> const uint8_t* {
     const bool first = item < R.n_first;
     const int e = first ? (R.dense ? item : sv) : R.win_lo + (item - R.n_first) - R.raw_base;
     const bool ok = item < R.it1 && e >= 0 && e < (first ? R.kv_rows : R.raw_cap);
-    // (one base, a 32-bit element offset per lane: no 64-bit pointer per lane lives
-    // across the loop)
-    if (PRE) ip = ok ? inv_kv_b + (first ? e : raw_norm_off + e) : &g_zero_f32;
     return ok ? (first ? R.kv : R.raw) + (long)e * (kD * 2) : nullptr;
   };
   // Gathering tile ti: lane rr of every wave resolves the wave's row wave + 8 rr (a
-  // masked row reads the zero row), with PRE wave 0's lane l also the 1/rms of row l.
+  // masked row reads the zero row).
   struct Gather {
     uint32_t lo, hi;   // row address of lane rr
-    const float* ip;   // PRE: 1/rms address of row c32
     uint32_t ok;       // rows that exist
   };
   auto resolve_tile = [&](int ti, const Slots& sv) -> Gather {
     Gather g;
     const int item0 = R.it0 + ti * kTile;
-    g.ip = &g_zero_f32;
-    if (PRE && wave == 0) resolve(item0 + c32, sv.nrm, g.ip);
-    const float* unused;
-    const uint8_t* pl = resolve(item0 + wave + kW8Waves * (lane & (kW8Rpw - 1)), sv.row, unused);
+    const uint8_t* pl = resolve(item0 + wave + kW8Waves * (lane & (kW8Rpw - 1)), sv.row);
     g.ok = (uint32_t)__ballot(pl != nullptr) & ((1u << kW8Rpw) - 1u);
     const uint64_t pv = (uint64_t)(pl ? pl : g_zero_row);
     g.lo = (uint32_t)pv;
     g.hi = (uint32_t)(pv >> 32);
     return g;
   };
-  // the 1/rms of the tile's rows (PRE, wave 0, lanes 0..31: row = lane)
-  auto load_norms = [&](const Gather& g, float* irms_dst) {
-    if (PRE && wave == 0 && h == 0)
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g.ip,
-                                       (__attribute__((address_space(3))) void*)irms_dst, 4, 0, 0);
+  // PRE: the tile's per-row factors (1 for a row that exists, 0 for a masked one), the
+  // wave's four rows from lanes 0..3
+  auto row_mask = [&](uint32_t ok, float* irms_dst) {
+    if (PRE && lane < kW8Rpw) irms_dst[wave + kW8Waves * lane] = ((ok >> lane) & 1u) ? 1.f : 0.f;
   };
   auto load_row = [&](const Gather& g, int rr, uint8_t* dst) {
     const uint64_t p = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)g.hi, rr) << 32) |
@@ -1183,7 +1177,7 @@ void mqa_w8_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml, con
   };
   auto issue = [&](int ti, const Slots& sv, uint8_t* dst, float* irms_dst) -> uint32_t {
     const Gather g = resolve_tile(ti, sv);
-    load_norms(g, irms_dst);
+    row_mask(g.ok, irms_dst);
 #pragma unroll 1
     for (int rr = 0; rr < kW8Rpw; ++rr) load_row(g, rr, dst);
     return g.ok;
@@ -1278,7 +1272,7 @@ void mqa_w8_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml, con
     uint64_t growp[kW8Rpw] = {};
     if (gi) {
       const Gather gn = resolve_tile(ti + 2, sv2);
-      load_norms(gn, irms[(BUF + 2) % kNB]);
+      row_mask(gn.ok, irms[(BUF + 2) % kNB]);
       okm[(BUF + 2) % kNB] = gn.ok;
 #pragma unroll
       for (int rr = 0; rr < kW8Rpw; ++rr)
@@ -1558,8 +1552,8 @@ static MqaLaunch plan_mqa(const MqaArgs& A) {
       // about 0.9 us a tile; its start-up waits on the index slots, then on the
       // first two tiles, and its partial leaves at the end)
       const double t_tile = hg ? 0.9 : (pre ? 2.4 : (A.dense ? 3.0 : 5.0));
-      // the pre-pass reads every cached row once (~5 TB/s)
-      const double t_norms = pre ? 3.0 + (double)A.batch * ((double)A.kv_cap + A.raw_cap) * (kD * 2) / 5.0e6 : 0.0;
+      // the pre-pass reads every cached row once and writes its normalised copy (~5 TB/s)
+      const double t_norms = pre ? 3.0 + 2.0 * (double)A.batch * ((double)A.kv_cap + A.raw_cap) * (kD * 2) / 5.0e6 : 0.0;
       for (int sp = 1; sp <= kMaxSplit && sp <= tiles_max; ++sp) {
         const int tps = (tiles_max + sp - 1) / sp;
         const int s_eff = (tiles_max + tps - 1) / tps;
@@ -1623,10 +1617,11 @@ static size_t partial_bytes(const MqaArgs& A, const MqaLaunch& L) {
   return r256(parts * kD * sizeof(uint16_t) + parts * 2 * sizeof(float));   // fp16 averages, fp32 (m, l)
 }
 
-// Row norms of the full-dim kernel: [batch, kv_cap] then [batch, raw_cap] fp32.
+// The normalised copy of the full-dim kernel's rows: [batch, kv_cap, 512] then
+// [batch, raw_cap, 512] bf16.
 static size_t norm_bytes(const MqaArgs& A, const MqaLaunch& L) {
   if (!(L.kind == 3 && L.pre)) return 0;
-  return r256((size_t)A.batch * A.kv_cap * sizeof(float)) + r256((size_t)A.batch * A.raw_cap * sizeof(float));
+  return r256((size_t)A.batch * A.kv_cap * kD * 2) + r256((size_t)A.batch * A.raw_cap * kD * 2);
 }
 
 // The plan depends on whether a norm weight is given, which the size query does not
@@ -1660,14 +1655,14 @@ hipError_t launch_mqa(const MqaArgs& A, void* ws, size_t ws_bytes, hipStream_t s
     part_o = (uint16_t*)ws;
     part_ml = (float*)(part_o + parts * kD);
   }
-  float* inv_kv = nullptr;
-  float* inv_raw = nullptr;
+  uint16_t* kvn = nullptr;
+  uint16_t* rawn = nullptr;
   if (nb > 0) {
-    inv_kv = (float*)((char*)ws + pb);
-    inv_raw = (float*)((char*)ws + pb + r256((size_t)A.batch * A.kv_cap * sizeof(float)));
+    kvn = (uint16_t*)((char*)ws + pb);
+    rawn = (uint16_t*)((char*)ws + pb + r256((size_t)A.batch * A.kv_cap * kD * 2));
     const long n_rows = (long)A.batch * ((long)A.kv_cap + A.raw_cap);
-    hipError_t e = launch("mqa_row_norms", row_inv_rms_kernel, dim3((unsigned)((n_rows + 3) / 4)), dim3(256), 0, s,
-                          A, inv_kv, inv_raw);
+    hipError_t e = launch("mqa_row_norms", row_normalize_kernel, dim3((unsigned)((n_rows + 3) / 4)), dim3(256), 0,
+                          s, A, kvn, rawn);
     if (e != hipSuccess) return e;
   }
   const size_t lds = mqa_lds_bytes(L);
@@ -1689,11 +1684,11 @@ hipError_t launch_mqa(const MqaArgs& A, void* ws, size_t ws_bytes, hipStream_t s
   if (L.kind == 3) grid = dim3((unsigned)((((long)L.units * L.n_hg + 7) / 8) * 8));
   hipError_t e;
   if (L.kind == 3 && L.pre)
-    e = launch("mqa_bf16_w8", mqa_w8_kernel<true>, grid, dim3(kW8Waves * 64), lds, s, A, L, part_o, part_ml, inv_kv,
-               inv_raw);
+    e = launch("mqa_bf16_w8", mqa_w8_kernel<true>, grid, dim3(kW8Waves * 64), lds, s, A, L, part_o, part_ml,
+               (const uint16_t*)kvn, (const uint16_t*)rawn);
   else if (L.kind == 3)
     e = launch("mqa_bf16_w8", mqa_w8_kernel<false>, grid, dim3(kW8Waves * 64), lds, s, A, L, part_o, part_ml,
-               (const float*)nullptr, (const float*)nullptr);
+               (const uint16_t*)nullptr, (const uint16_t*)nullptr);
   else if (L.kind == 4 && A.kv_f8)
     e = launch("mqa_f8_sd", mqa_sd_kernel<true>, grid, dim3(kSdWaves * 64), lds, s, A, L, part_o, part_ml);
   else if (L.kind == 4)
