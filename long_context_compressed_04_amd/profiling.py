@@ -43,7 +43,7 @@ KERNELS = {
     "mqa_bf16_h16": (r"mqa_bf16_kernel<", "mqa.hip"),
     "mqa_f32": (r"mqa_f32_kernel", "mqa.hip"),
     "mqa_combine": (r"mqa_combine_kernel", "mqa.hip"),
-    "mqa_row_norms": (r"row_inv_rms_kernel", "mqa.hip"),
+    "mqa_row_norms": (r"row_normalize_kernel", "mqa.hip"),
     "compress": (r"compress_kernel<", "compress.hip"),
     "mxfp4_quantize": (r"mxfp4_quantize_kernel", "compress.hip"),
     "fp8_quantize": (r"fp8_quantize_kernel", "compress.hip"),
