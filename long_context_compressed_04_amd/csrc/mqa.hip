@@ -805,16 +805,17 @@ void mqa_sd_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml) {
         store8(rf8[(K + 1) % 3], bi == 0 ? tb0 : (bi == 1 ? tb1 : (bi == 2 ? tb2 : tb3)));
         lds_barrier();
       };
-      // (the loop repeats only after all three steps, so the registers in flight are
-      // the same at every entry)
-      for (int s = 0;; s += 3) {
+      // steps 0 .. n_tiles: whole groups of three in the loop (the registers in flight are
+      // the same at every entry), the remainder after it.  (A loop left from inside a
+      // group made the compiler wait for every load in flight at the loop head.)
+      int s = 0;
+      for (; s + 2 <= n_tiles; s += 3) {
         gstep(std::integral_constant<int, 0>{}, s);
-        if (s + 1 > n_tiles) break;
         gstep(std::integral_constant<int, 1>{}, s + 1);
-        if (s + 2 > n_tiles) break;
         gstep(std::integral_constant<int, 2>{}, s + 2);
-        if (s + 3 > n_tiles) break;
       }
+      if (s <= n_tiles) gstep(std::integral_constant<int, 0>{}, s);
+      if (s + 1 <= n_tiles) gstep(std::integral_constant<int, 1>{}, s + 1);
       lds_barrier();   // the head sums are in LDS
       return;
     }
