@@ -669,16 +669,16 @@ constexpr int kSdWaves = kSdQk + kSdPv + kSdGa;
 constexpr int kSdRpw = kTile / kSdGa;   // rows each gather wave loads per tile
 constexpr int kWRow = 2 * 32 + 8;       // bytes per tile row of a weight buffer (32 heads, padded)
 
-// 16 FP8 E4M3 values -> bf16, stored as 32 bytes (exact: E4M3 has 3 mantissa bits).
+// 16 FP8 E4M3 values -> bf16, stored as 32 bytes (exact: E4M3 has 3 mantissa bits and
+// a narrower exponent range than bf16).  gfx950's scaled conversion turns two codes
+// into a bf16 pair in one instruction (a scale of 1 leaves the values as they are).
 __device__ __forceinline__ void fp8x16_to_bf16(uint4 v, uint8_t* dst) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
   uint32_t o[8];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], false);   // bytes 0, 1
-    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], true);    // bytes 2, 3
-    o[2 * k] = (__float_as_uint(lo[0]) >> 16) | (__float_as_uint(lo[1]) & 0xffff0000u);
-    o[2 * k + 1] = (__float_as_uint(hi[0]) >> 16) | (__float_as_uint(hi[1]) & 0xffff0000u);
+    o[2 * k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[k], 1.f, false));   // bytes 0, 1
+    o[2 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[k], 1.f, true));   // 2, 3
   }
   *(uint4*)dst = make_uint4(o[0], o[1], o[2], o[3]);
   *(uint4*)(dst + 16) = make_uint4(o[4], o[5], o[6], o[7]);
