@@ -33,7 +33,8 @@
 // trailing 64 dims with the query's cos and sin ("Gated attention output", "Partial
 // RoPE"), both applied where the output is finished.  The split-role kernel also reads
 // FP8 E4M3 caches ("FP8 KV-cache quantization"), converting each row to bf16 on its way
-// into LDS.
+// into LDS; with many queries the 8-wave kernel's pre-pass converts them into its
+// normalised bf16 copy.
 #include <cmath>
 #include <type_traits>
 
@@ -1013,19 +1014,30 @@ void mqa_sd_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml) {
 
 // One wave per row: every row of kv (all kv_cap rows of every sequence) and kv_raw,
 // RMS-normalised (unit weight) and rounded to bf16, into kvn [batch, kv_cap, 512] and
-// rawn [batch, raw_cap, 512]: the keys and values the attention itself reads.
+// rawn [batch, raw_cap, 512]: the keys and values the attention itself reads.  F8: the
+// rows are FP8 E4M3 codes (512 bytes), taken at their exact values.
+template <bool F8>
 __global__ __launch_bounds__(256) void row_normalize_kernel(MqaArgs A, uint16_t* kvn, uint16_t* rawn) {
+  constexpr int kRowG = F8 ? kD : 2 * kD;   // bytes per cache row
   const long gw = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const long n_kv = (long)A.batch * A.kv_cap, n_raw = (long)A.batch * A.raw_cap;
   if (gw >= n_kv + n_raw) return;
-  const uint8_t* rowp = gw < n_kv ? (const uint8_t*)A.kv + gw * (kD * 2)
-                                  : (const uint8_t*)A.kv_raw + (gw - n_kv) * (kD * 2);
+  const uint8_t* rowp = gw < n_kv ? (const uint8_t*)A.kv + gw * kRowG : (const uint8_t*)A.kv_raw + (gw - n_kv) * kRowG;
   uint16_t* dst = gw < n_kv ? kvn + gw * kD : rawn + (gw - n_kv) * kD;
-  const uint4 v = *(const uint4*)(rowp + 16 * lane);
-  const float ss = wave_sum(sumsq_bf16x8(v, 0.f));
+  uint32_t w4[4];   // this lane's 8 values (dims 8 lane ..) as bf16 pairs
+  if (F8) {
+    const uint2 c = *(const uint2*)(rowp + 8 * lane);
+    w4[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.f, false));
+    w4[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.f, true));
+    w4[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.f, false));
+    w4[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.f, true));
+  } else {
+    const uint4 v = *(const uint4*)(rowp + 16 * lane);
+    w4[0] = v.x; w4[1] = v.y; w4[2] = v.z; w4[3] = v.w;
+  }
+  const float ss = wave_sum(sumsq_bf16x8(make_uint4(w4[0], w4[1], w4[2], w4[3]), 0.f));
   const float r = 1.f / sqrtf(ss * (1.f / kD) + A.eps);
-  const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
   uint32_t o4[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k)
@@ -1542,9 +1554,10 @@ static MqaLaunch plan_mqa(const MqaArgs& A) {
       // 128-head workgroups with row norms from the gathered tiles / from the pre-pass
       const bool hg = variant == 0;
       const bool pre = variant == 2;
-      // (an FP8 cache is read by the split-role kernel only)
+      // (an FP8 cache is read by the split-role kernel, and by the 8-wave kernel through
+      // the pre-pass's normalised bf16 copy)
       if (hg && (A.heads % 32 != 0 || (rows > 32 && !A.kv_f8))) continue;
-      if (!hg && (A.heads % 128 != 0 || A.kv_f8)) continue;
+      if (!hg && (A.heads % 128 != 0 || (A.kv_f8 && !pre))) continue;
       const int wg_heads = hg ? 32 : 128;
       const int n_hg = A.heads / wg_heads;
       // (the 8-wave kernel gathers only ~1.5 tiles ahead: on rows scattered over HBM,
@@ -1554,7 +1567,9 @@ static MqaLaunch plan_mqa(const MqaArgs& A) {
       // first two tiles, and its partial leaves at the end)
       const double t_tile = hg ? 0.9 : (pre ? 2.4 : (A.dense ? 3.0 : 5.0));
       // the pre-pass reads every cached row once and writes its normalised copy (~5 TB/s)
-      const double t_norms = pre ? 3.0 + 2.0 * (double)A.batch * ((double)A.kv_cap + A.raw_cap) * (kD * 2) / 5.0e6 : 0.0;
+      const double t_norms = pre ? 3.0 + (A.kv_f8 ? 1.5 : 2.0) * (double)A.batch * ((double)A.kv_cap + A.raw_cap) *
+                                             (kD * 2) / 5.0e6
+                                 : 0.0;
       for (int sp = 1; sp <= kMaxSplit && sp <= tiles_max; ++sp) {
         const int tps = (tiles_max + sp - 1) / sp;
         const int s_eff = (tiles_max + tps - 1) / tps;
@@ -1662,8 +1677,10 @@ hipError_t launch_mqa(const MqaArgs& A, void* ws, size_t ws_bytes, hipStream_t s
     kvn = (uint16_t*)((char*)ws + pb);
     rawn = (uint16_t*)((char*)ws + pb + r256((size_t)A.batch * A.kv_cap * kD * 2));
     const long n_rows = (long)A.batch * ((long)A.kv_cap + A.raw_cap);
-    hipError_t e = launch("mqa_row_norms", row_normalize_kernel, dim3((unsigned)((n_rows + 3) / 4)), dim3(256), 0,
-                          s, A, kvn, rawn);
+    hipError_t e = A.kv_f8 ? launch("mqa_row_norms", row_normalize_kernel<true>, dim3((unsigned)((n_rows + 3) / 4)),
+                                    dim3(256), 0, s, A, kvn, rawn)
+                           : launch("mqa_row_norms", row_normalize_kernel<false>, dim3((unsigned)((n_rows + 3) / 4)),
+                                    dim3(256), 0, s, A, kvn, rawn);
     if (e != hipSuccess) return e;
   }
   const size_t lds = mqa_lds_bytes(L);
@@ -1679,7 +1696,8 @@ hipError_t launch_mqa(const MqaArgs& A, void* ws, size_t ws_bytes, hipStream_t s
   }();
   if (attr != hipSuccess) return attr;
   if (lds > (size_t)kMaxDynLds) return hipErrorInvalidValue;
-  if (A.kv_f8 && L.kind != 4) return hipErrorInvalidValue;   // only that kernel reads FP8 rows
+  // FP8 rows are read by the split-role kernel, or normalised into bf16 by the pre-pass
+  if (A.kv_f8 && !(L.kind == 4 || (L.kind == 3 && L.pre))) return hipErrorInvalidValue;
   const long groups = ((long)L.units + 7) / 8;
   dim3 grid((unsigned)(groups * 8 * L.n_hg));
   if (L.kind == 3) grid = dim3((unsigned)((((long)L.units * L.n_hg + 7) / 8) * 8));

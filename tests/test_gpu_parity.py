@@ -598,6 +598,51 @@ def test_fp8_cache_mqa(dense, B, n_q, H, N, k, window, split_items, with_sink):
                 np.testing.assert_allclose(lse[b, i], wl, atol=2e-2)
 
 
+@pytest.mark.gpu
+@pytest.mark.parametrize("dense", [False, True])
+def test_fp8_cache_many_queries_through_normalised_copy(dense):
+    """An FP8 cache with many queries: the 8-wave kernel reads the pre-pass's normalised
+    bf16 copy of the rows (each code taken at its exact value), and the result is the
+    oracle's attention over the dequantised rows."""
+    B, n_q, H, d, N, k, window, m = 1, 256, 128, 512, 1200, 256, 128, 4
+    q, _, _, rng = _mqa_case("bf16", B, n_q, H, d, 1, 0, window, seed=93 + int(dense))
+    raw_cap = window + n_q + 5
+    kv_c = oracle.fp8_quantize(rng.standard_normal((B, N, d)) * 1.5).reshape(B, N, d)
+    raw_c = oracle.fp8_quantize(rng.standard_normal((B, raw_cap, d)) * 1.5).reshape(B, raw_cap, d)
+    kv_v, raw_v = oracle.fp8_dequantize(kv_c), oracle.fp8_dequantize(raw_c)
+    kvt, rawt = torch.from_numpy(kv_c).cuda(), torch.from_numpy(raw_c).cuda()
+    csa.timing_collect()
+    csa.timing_enable(True)
+    try:
+        if dense:
+            n_entries = np.array([N], dtype=np.int32)
+            q_pos = np.array([[m * N - 1 - n_q + i for i in range(n_q)]], dtype=np.int32)
+            raw_base = np.array([q_pos[0].min() - window + 1], dtype=np.int32)
+            out, lse = csa.hca_dense_mqa(dev(q), kvt, _i32(n_entries), rawt, _i32(raw_base), _i32(q_pos), m=m,
+                                         window=window)
+        else:
+            idx = np.stack([np.sort(rng.choice(N, size=k, replace=False)) for _ in range(n_q)])[None].astype(np.int32)
+            idx[:, :, -3:] = -1
+            raw_base = np.array([1000], dtype=np.int32)
+            q_pos = np.array([[raw_base[0] + window + 2 + i for i in range(n_q)]], dtype=np.int32)
+            out, lse = csa.sparse_mqa(dev(q), kvt, _i32(idx), rawt, _i32(raw_base), _i32(q_pos), window=window)
+        torch.cuda.synchronize()
+        launched = csa.timing_collect()
+    finally:
+        csa.timing_enable(False)
+    assert "mqa_bf16_w8" in launched and "mqa_row_norms" in launched, sorted(launched)
+    out, lse = host(out), host(lse)
+    for i in range(0, n_q, 37):
+        if dense:
+            want, wl = oracle.dense_mqa(W.value(q[0, i]), kv_v[0], N, m, raw_v[0], raw_base[0], q_pos[0, i], window,
+                                        1 / np.sqrt(d), 1e-6)
+        else:
+            want, wl = oracle.sparse_mqa(W.value(q[0, i]), kv_v[0], idx[0, i], raw_v[0], raw_base[0], q_pos[0, i],
+                                         window, 1 / np.sqrt(d), 1e-6)
+        assert_bf16_close(out[0, i], want, "fp8-cache out (normalised copy)")
+        np.testing.assert_allclose(lse[0, i], wl, atol=2e-2)
+
+
 @pytest.mark.parametrize("dtype,dense,B,n_q,H,d,N,k,with_gamma,fp8,split_items", [
     ("f32", False, 1, 2, 8, 64, 300, 64, False, False, 0),          # fp32 kernel
     ("bf16", False, 2, 1, 128, 512, 2000, 1024, False, False, 0),   # split-role kernel, merged splits
