@@ -1361,13 +1361,9 @@ void mqa_w8_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml, con
     }
   };
   static_assert(kW8Rpw == 4, "one gathered row per two of the eight P V k-steps");
-  // tile 0 in LDS (tile 1 may be in flight)
-  if (n_tiles > 1) {
-    if (PRE && wave == 0) wait_vmcnt<kW8Rpw + 1>();
-    else wait_vmcnt<kW8Rpw>();
-  } else {
-    wait_vmcnt<0>();
-  }
+  // tile 0 in LDS (tile 1's kW8Rpw row loads, the last this wave issued, may be in flight)
+  if (n_tiles > 1) wait_vmcnt<kW8Rpw>();
+  else wait_vmcnt<0>();
   lds_barrier();
   auto run = [&](auto DHC) {
     for (int ti = 0; ti < n_tiles; ti += kNB) {
