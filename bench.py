@@ -16,6 +16,8 @@ the window (RMSNorm folded in).  Other workloads (--workload):
                      prefilter of 8,192 candidates, bf16 rescoring, top-1024
   csa_decode_64k_fp8 csa_decode_64k with the compressed entries and window rows in
                      FP8 E4M3
+  csa_prefill_4k_fp8 csa_prefill_4k with an FP8 E4M3 cache: the new entries are
+                     compressed, then quantised into it
 
 Inputs are seeded synthetic data resident in HBM before timing starts.  Decode
 steps cycle through replicas of every cache so that the 256 MB Infinity Cache
@@ -51,7 +53,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "mxfp4": 10100.0}
 WORKLOADS = ["csa_decode_64k", "hca_decode_1m", "csa_decode_1m_fp4", "csa_prefill_4k", "csa_decode_1m_fp4_rescored",
-             "csa_decode_64k_fp8"]
+             "csa_decode_64k_fp8", "csa_prefill_4k_fp8"]
 CALIB_BYTES = 256 << 20
 CPU_SECONDS = 10.0        # oracle work per CPU measurement (single thread, then every core)
 CPU_PROCS_MAX = 16        # the host share of one GPU
@@ -523,9 +525,57 @@ class CsaPrefill4k(Step):
         return self.Q / (self.t_compress / procs + self.Q * query_s / procs)
 
 
+class CsaPrefill4kFp8(CsaPrefill4k):
+    """csa_prefill_4k with the compressed entries and the window rows held as FP8 E4M3
+    codes: the step compresses the new entries (bf16), quantises them into the cache,
+    and attends the FP8 rows (through the 8-wave kernel's normalising pre-pass)."""
+    name = "csa_prefill_4k_fp8"
+    metric = "CSA prefill tokens/s with an FP8 E4M3 KV cache (4,096 new queries on 61,440 prior tokens, one layer)"
+    dtype = "bf16+fp8_e4m3_kv"
+
+    def __init__(self, R):
+        super().__init__(R)
+        self.config["workload"] = self.name
+        self.config["cache_dtype"] = "fp8_e4m3"
+
+    def setup(self, dev):
+        super().setup(dev)
+        csa = self.csa
+        N, P = self.N, self.P
+        import ctypes
+        torch = _torch()
+        self.kv8 = csa.fp8_quantize(self.kv)            # the prior entries (new ones per step)
+        self.raw8 = csa.fp8_quantize(self.raw)
+        self.new_bf16 = self.kv[0, P:N]                  # where the step's compression lands
+        self.new_codes = self.kv8[0, P:N]
+        dm = csa._mqa_desc(self.q, self.kv8, self.raw8, topk=self.k, window=self.w)
+        self.mqa_ws = torch.zeros(max(1, csa.lib().csa_mqa_workspace_size(ctypes.byref(dm), 0)), dtype=torch.uint8,
+                                  device=dev)
+
+    def cpu_prepare(self):
+        import oracle
+        super().cpu_prepare()
+        # the attention reads the rows' FP8 codes at their exact values
+        self.kv_all = oracle.fp8_dequantize(oracle.fp8_quantize(self.kv_all)).reshape(self.kv_all.shape)
+        self.raw_v = oracle.fp8_dequantize(oracle.fp8_quantize(self.raw_v)).reshape(self.raw_v.shape)
+        self.cpu_sample += "; FP8 rows dequantised"
+
+    def launch(self, i):
+        csa = self.csa
+        csa.compress(self.A, self.Bs, self.z, self.z, self.m, self.kv, tok_base=self.tb, entry_begin=self.P,
+                     entry_end=self.N)
+        csa.fp8_quantize(self.new_bf16, self.new_codes)
+        csa.compress(self.AI, self.BI, self.zI, self.zI, self.m, self.kI, tok_base=self.tb, entry_begin=self.P,
+                     entry_end=self.N)
+        csa.index_topk(self.qI, self.wt, self.kI, self.ne, self.q_pos, m=self.m, topk=self.k,
+                       workspace=self.idx_ws, out_idx=self.idx, out_score=self.score)
+        csa.sparse_mqa(self.q, self.kv8, self.idx, self.raw8, self.rb, self.q_pos, window=self.w,
+                       workspace=self.mqa_ws, out=self.out, lse=self.lse)
+
+
 def make(name, R):
     return {"csa_decode_64k": CsaDecode64k, "csa_decode_64k_fp8": CsaDecode64kFp8, "hca_decode_1m": HcaDecode1m,
-            "csa_decode_1m_fp4": CsaDecode1mFp4,
+            "csa_decode_1m_fp4": CsaDecode1mFp4, "csa_prefill_4k_fp8": CsaPrefill4kFp8,
             "csa_prefill_4k": CsaPrefill4k, "csa_decode_1m_fp4_rescored": CsaDecode1mFp4Rescored}[name](R)
 
 
