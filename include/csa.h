@@ -305,6 +305,11 @@ typedef struct {
                          16-byte aligned.  Otherwise CSA_ERR_UNSUPPORTED */
 } csa_mqa_desc;
 
+/* Workspace of csa_sparse_mqa / hca_dense_mqa (dense = 1) for desc: the split partials
+ * (per query, split and head: the split's softmax average in fp16, its maximum and sum
+ * in fp32) and, for the 128-head kernel with many queries, an RMS-normalised bf16 copy
+ * of every kv and kv_raw row (1 KiB per cached row), written by the call itself.
+ * 0 when the call needs none. */
 size_t csa_mqa_workspace_size(const csa_mqa_desc* desc, int32_t dense);
 
 csa_status csa_sparse_mqa(const csa_mqa_desc* desc, const void* q, const void* kv,

@@ -600,6 +600,52 @@ def test_fp8_cache_mqa(dense, B, n_q, H, N, k, window, split_items, with_sink):
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("dense", [False, True])
+def test_many_queries_through_normalised_copy(dense):
+    """Many queries on the 128-head kernel: the call's pre-pass writes an RMS-normalised
+    bf16 copy of every row and the kernel attends it.  Rows scaled by per-row factors in
+    [1/4, 4] (so the normalisation changes the result) and invalid slots: out and lse
+    against the oracle."""
+    B, n_q, H, d, N, k, window, m = 1, 200, 128, 512, 900, 192, 128, 4
+    rng = np.random.default_rng(131 + int(dense))
+    q = W.store(rng.standard_normal((B, n_q, H, d)).astype(np.float32), "bf16")
+    raw_cap = window + n_q + 5
+    scale_rows = lambda x: x * np.exp(rng.uniform(np.log(0.25), np.log(4.0), x.shape[:2]))[..., None]
+    kv = W.store(scale_rows(rng.standard_normal((B, N, d))).astype(np.float32), "bf16")
+    raw = W.store(scale_rows(rng.standard_normal((B, raw_cap, d))).astype(np.float32), "bf16")
+    csa.timing_collect()
+    csa.timing_enable(True)
+    try:
+        if dense:
+            n_entries = np.array([N - 7], dtype=np.int32)
+            q_pos = np.array([[m * N - 40 - n_q + i for i in range(n_q)]], dtype=np.int32)
+            raw_base = np.array([q_pos[0].min() - window + 1], dtype=np.int32)
+            out, lse = csa.hca_dense_mqa(dev(q), dev(kv), _i32(n_entries), dev(raw), _i32(raw_base), _i32(q_pos),
+                                         m=m, window=window)
+        else:
+            idx = np.stack([np.sort(rng.choice(N, size=k, replace=False)) for _ in range(n_q)])[None].astype(np.int32)
+            idx[:, :, ::17] = -1
+            raw_base = np.array([500], dtype=np.int32)
+            q_pos = np.array([[raw_base[0] + window - 1 + i for i in range(n_q)]], dtype=np.int32)
+            out, lse = csa.sparse_mqa(dev(q), dev(kv), _i32(idx), dev(raw), _i32(raw_base), _i32(q_pos), window=window)
+        torch.cuda.synchronize()
+        launched = csa.timing_collect()
+    finally:
+        csa.timing_enable(False)
+    assert "mqa_bf16_w8" in launched and "mqa_row_norms" in launched, sorted(launched)
+    out, lse = host(out), host(lse)
+    for i in list(range(0, n_q, 41)) + [n_q - 1]:
+        if dense:
+            want, wl = oracle.dense_mqa(W.value(q[0, i]), W.value(kv[0]), int(n_entries[0]), m, W.value(raw[0]),
+                                        int(raw_base[0]), int(q_pos[0, i]), window, 1 / np.sqrt(d), 1e-6)
+        else:
+            want, wl = oracle.sparse_mqa(W.value(q[0, i]), W.value(kv[0]), idx[0, i], W.value(raw[0]), int(raw_base[0]),
+                                         int(q_pos[0, i]), window, 1 / np.sqrt(d), 1e-6)
+        assert_bf16_close(out[0, i], want, "normalised-copy out")
+        np.testing.assert_allclose(lse[0, i], wl, atol=2e-2)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dense", [False, True])
 def test_fp8_cache_many_queries_through_normalised_copy(dense):
     """An FP8 cache with many queries: the 8-wave kernel reads the pre-pass's normalised
     bf16 copy of the rows (each code taken at its exact value), and the result is the
