@@ -26,10 +26,18 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-u
          "-I", INCLUDE, "-I", CSRC]
 
 
+# Per-source options.  MFMA results go to ordinary VGPRs in the indexer and the MQA
+# kernels: an epilogue reads every accumulator once, and from AGPRs each read is one
+# more instruction (v_accvgpr_read), behind a wait for the matrix pipe before the
+# registers are reused.  Every kernel keeps its occupancy or gains; the decode and
+# prefill MQA kernels compile to the same code either way.
+SOURCE_FLAGS = {src: ["-mllvm", "-amdgpu-mfma-vgpr-form"] for src in ("indexer.hip", "mqa.hip")}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [HIPCC] + FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + FLAGS + SOURCE_FLAGS.get(src, []) + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s" % (src, res.stderr))

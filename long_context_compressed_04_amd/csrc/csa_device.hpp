@@ -29,6 +29,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // fp32 -> bf16, round to nearest even.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) { return (uint16_t)(pack_bf16x2(f, 0.f) & 0xffffu); }
 
+// max(x, 0) as one integer max on the bits: a float with the sign bit set is a
+// negative int32.  (fmaxf costs a second instruction, which quiets a signalling NaN
+// first; here a NaN with a clear sign bit passes through unchanged.)
+__device__ __forceinline__ float relu_f32(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // Order-preserving map fp32 -> uint32 (larger float <=> larger key).
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);

@@ -172,7 +172,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_mfma(IndexArgs A,
           }
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) part = fmaf(wl[hb][r], fmaxf(acc[r], 0.f), part);
+        for (int r = 0; r < 16; ++r) part = fmaf(wl[hb][r], relu_f32(acc[r]), part);
       }
       part = add_xor32(part);
       const int e = tile0 + col;
@@ -305,7 +305,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_lds(IndexArgs A, 
 #pragma unroll
       for (int g = 0; g < 4; ++g)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) part = fmaf(wl[hb][g][k], fmaxf(acc[hb][4 * g + k], 0.f), part);
+        for (int k = 0; k < 4; ++k) part = fmaf(wl[hb][g][k], relu_f32(acc[hb][4 * g + k]), part);
     part = add_xor32(part);
     const bool valid = SEL ? key_row(e) >= 0 : e < V;
     if (half == 0 && e < A.n_max) scores[row * A.n_max + e] = valid ? part : -INFINITY;
@@ -443,7 +443,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_pf(IndexArgs A, f
 #pragma unroll
             for (int t = 0; t < TPW; ++t)
 #pragma unroll
-              for (int k = 0; k < 4; ++k) part[t] = fmaf(wv[k], fmaxf(acc[t][4 * g + k], 0.f), part[t]);
+              for (int k = 0; k < 4; ++k) part[t] = fmaf(wv[k], relu_f32(acc[t][4 * g + k]), part[t]);
           }
         }
       }
