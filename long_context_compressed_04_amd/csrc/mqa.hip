@@ -100,14 +100,18 @@ __device__ __forceinline__ void query_items(const MqaArgs& A, int b, long row, i
 struct SoftmaxEnd {
   float mul, lse;
 };
+// 1 / x by the hardware reciprocal (v_rcp_f32, within 1 ulp) instead of the IEEE
+// division's dozen instructions: the denominators here are softmax sums, normal
+// floats, and the quotient is rounded to bf16 or fp16 afterwards.
+__device__ __forceinline__ float rcp_f32(float x) { return __builtin_amdgcn_rcpf(x); }
 __device__ __forceinline__ SoftmaxEnd softmax_end(float m2, float l, const float* sink, int head) {
   const bool none = !(l > 0.f);
-  if (!sink) return {none ? 0.f : 1.f / l, none ? -INFINITY : m2 * kLn2 + logf(l)};
+  if (!sink) return {none ? 0.f : rcp_f32(l), none ? -INFINITY : m2 * kLn2 + logf(l)};
   const float s2 = sink[head] * kLog2e;
   const float M = none ? s2 : fmaxf(m2, s2);
   const float scale = none ? 0.f : exp2f(m2 - M);
   const float den = l * scale + exp2f(s2 - M);
-  return {scale / den, M * kLn2 + logf(den)};
+  return {scale * rcp_f32(den), M * kLn2 + logf(den)};
 }
 
 // Rope-conjugate rotation of dim i (0..63) of a head's rotated slice (the trailing 64
@@ -554,7 +558,7 @@ __global__ __launch_bounds__(NW * 64) void mqa_bf16_kernel(MqaArgs A, MqaLaunch 
     if (A.lse && g == 0) A.lse[row * A.heads + head] = fin.lse;
   } else {
     uint16_t* po = part_o + (((long)row * L.nsplit + split) * A.heads + head) * kD;
-    const float il = l_run > 0.f ? 1.f / l_run : 0.f;
+    const float il = l_run > 0.f ? rcp_f32(l_run) : 0.f;
 #pragma unroll
     for (int db = 0; db < 32; ++db) *(uint2*)(po + 16 * db + 4 * g) = partial4(o[db], il);
     if (g == 0) {
@@ -1003,7 +1007,7 @@ void mqa_sd_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml) {
     for (int k = 0; k < 16; ++k) {
       const int hh = 2 * k + hl;
       const float l = lsum[0][hh] + lsum[1][hh];
-      *(uint2*)(po + (long)hh * kD) = partial4(*(const f32x4_t*)(stage + hh * kStageRow + 4 * d4), l > 0.f ? 1.f / l : 0.f);
+      *(uint2*)(po + (long)hh * kD) = partial4(*(const f32x4_t*)(stage + hh * kStageRow + 4 * d4), l > 0.f ? rcp_f32(l) : 0.f);
     }
   }
 }
@@ -1387,7 +1391,7 @@ void mqa_w8_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml, con
     const int hbj = 2 * hp + j;
     l_tot[j] = red[hbj][c32] + red[hbj + 4][c32];
     inv_l[j] = L.nsplit == 1 ? softmax_end(0.f, l_tot[j], A.sink, hg * 128 + 64 * hp + 32 * j + c32).mul
-                             : (l_tot[j] > 0.f ? 1.f / l_tot[j] : 0.f);   // a split's own average
+                             : (l_tot[j] > 0.f ? rcp_f32(l_tot[j]) : 0.f);   // a split's own average
   }
   // ---- O^T -> rows of 64 dims through a wave-private LDS region, four chunks
   // (head block j of the pair, dim half of the quarter)
