@@ -463,9 +463,12 @@ __global__ __launch_bounds__(NW * 64) void mqa_bf16_kernel(MqaArgs A, MqaLaunch 
   const int hg = r8 % L.n_hg, ug = r8 / L.n_hg;
   const int unit = ug * 8 + xcd;
   if (unit >= L.units) return;
-  const long row = unit / L.nsplit;
-  const int split = unit % L.nsplit;
-  const int b = (int)(row / A.n_q);
+  // (32-bit quotients: a 64-bit division is a hundred scalar instructions on the way to
+  // the first loads; units and rows are int counts)
+  const int row32 = unit / L.nsplit;
+  const long row = row32;
+  const int split = unit - row32 * L.nsplit;
+  const int b = row32 / A.n_q;
   const int head = hg * (NW * 16) + C.wave * 16 + C.c16;   // this lane's head (column)
 
   int total;
@@ -712,9 +715,12 @@ void mqa_sd_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml) {
   const int hg = r8 % L.n_hg, ug = r8 / L.n_hg;
   const int unit = ug * 8 + xcd;
   if (unit >= L.units) return;
-  const long row = unit / L.nsplit;
-  const int split = unit % L.nsplit;
-  const int b = (int)(row / A.n_q);
+  // (32-bit quotients: a 64-bit division is a hundred scalar instructions on the way to
+  // the first loads; units and rows are int counts)
+  const int row32 = unit / L.nsplit;
+  const long row = row32;
+  const int split = unit - row32 * L.nsplit;
+  const int b = row32 / A.n_q;
 
   // raw q rows of the heads this wave normalises (heads wave + 16 j), 16 bytes a lane;
   // loaded before the slots, so waiting for the slots has waited for them too
@@ -780,7 +786,7 @@ void mqa_sd_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml) {
       const int hq = wave + kSdWaves * j;
       const uint4 v = qraw[j];
       const float ss = wave_sum(sumsq_bf16x8(v, 0.f));
-      const float qinv = 1.f / sqrtf(ss * (1.f / kD) + A.eps);
+      const float qinv = inv_rms(ss * (1.f / kD) + A.eps);   // (u is rounded to bf16 next)
       const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
       uint32_t o4[4];
 #pragma unroll
@@ -1110,10 +1116,11 @@ void mqa_w8_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml, con
   const int unit = (blockIdx.x & 7) * upx + (blockIdx.x >> 3);
   if (unit >= total_units) return;
   const int hg = unit % L.n_hg;
-  const long rs = unit / L.n_hg;
-  const long row = rs / L.nsplit;
-  const int split = (int)(rs % L.nsplit);
-  const int b = (int)(row / A.n_q);
+  const int rs = unit / L.n_hg;   // (32-bit quotients, as in the split-role kernel)
+  const int row32 = rs / L.nsplit;
+  const long row = row32;
+  const int split = rs - row32 * L.nsplit;
+  const int b = row32 / A.n_q;
 
   RowSrc R;
   {

@@ -514,7 +514,7 @@ __device__ __forceinline__ void global_select(KeyAt key_at, int n, int k, int32_
 }
 
 __device__ __forceinline__ int row_visible(const IndexArgs& A, long row) {
-  const int b = (int)(row / A.n_q);
+  const int b = (int)row / A.n_q;   // (rows are an int count: no 64-bit division)
   const int ne = min(A.n_entries[b], A.n_max);
   return visible_entries(A.q_pos[row], ne, A.m);
 }
