@@ -615,18 +615,30 @@ constexpr int kFilterGroups = kTopkThreads / kFilterThreads;   // chunks per wor
 // r in a fixed sample of the row, r chosen to leave ~3k keys of the row at or above
 // it (at most three quarters of the candidate capacity; a larger k keeps a smaller
 // margin).  One radix pass: the bin adds a few samples' worth of keys beyond rank r.
-// The sample is 64 runs of 64 consecutive keys, evenly spaced (V > kRegKeys).
-__device__ __forceinline__ uint32_t sample_threshold(const IndexArgs& A, const float* src, int V, SelShared& sh) {
-  constexpr int KPT = kSample / kTopkThreads;
+// The sample is 64 runs of 64 consecutive keys, evenly spaced over the row's n_max
+// slots (n_max > kRegKeys): it does not wait for the visible count, since the
+// indexer leaves -inf at and past V (at the bottom of the order, below any rank the
+// sample is asked for while V is near n_max).  Any threshold gives the exact
+// selection: the candidate kernel falls back to the whole row when it passed fewer
+// than k keys or more than kCandCap.
+constexpr int kSampleKpt = kSample / kTopkThreads;
+// This thread's sample scores (requested before anything else the filter loads: a
+// wait for them is then a wait for them alone).
+__device__ __forceinline__ void sample_load(const IndexArgs& A, const float* src, float (&x)[kSampleKpt]) {
   constexpr int kRun = 64, kRuns = kSample / kRun;
+#pragma unroll
+  for (int j = 0; j < kSampleKpt; ++j) {
+    const int i = kSampleKpt * (int)threadIdx.x + j;   // sample i: key i % 64 of run i / 64
+    x[j] = src[(long)(i / kRun) * (A.n_max / kRuns) + i % kRun];
+  }
+}
+__device__ __forceinline__ uint32_t sample_threshold(const IndexArgs& A, const float (&x)[kSampleKpt], SelShared& sh) {
+  constexpr int KPT = kSampleKpt;
   uint32_t key[KPT];
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const int i = KPT * (int)threadIdx.x + j;   // sample i: key i % 64 of run i / 64
-    key[j] = order_key(src[(long)(i / kRun) * (V / kRuns) + i % kRun]);
-  }
-  const long want = min((long)3 * A.topk, (long)kCandCap * 3 / 4);
-  long r = (want * kSample + V - 1) / V;
+  for (int j = 0; j < KPT; ++j) key[j] = order_key(x[j]);
+  const int want = min(3 * A.topk, kCandCap * 3 / 4);
+  int r = (want * kSample + A.n_max - 1) / A.n_max;   // (< 2^31: want <= 12,288)
   r = r < 1 ? 1 : (r > kSample ? kSample : r);
   uint32_t prefix, mask, need;
   reg_threshold<KPT, true>(key, kSample, (uint32_t)r, sh, prefix, mask, need);
@@ -639,8 +651,6 @@ __global__ __launch_bounds__(kTopkThreads) void topk_filter_kernel(IndexArgs A, 
   __shared__ SelShared sh;
   __shared__ uint32_t wtot[kTopkThreads / 64];
   const long row = blockIdx.y;
-  const int V = row_visible(A, row);
-  if (V <= kRegKeys || V <= A.topk) return;
   const float* src = scores + row * A.n_max;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int kGw = kFilterThreads / 64;                  // waves per group
@@ -650,14 +660,20 @@ __global__ __launch_bounds__(kTopkThreads) void topk_filter_kernel(IndexArgs A, 
   constexpr int kIt = kChunk / kFilterThreads;              // 16 keys per lane
   constexpr int kPerWave = kChunk / kGw;
   const int w0 = c0 + gw * kPerWave;
-  // this chunk's scores are requested first: they arrive while the threshold forms
+  // the sample, this chunk's scores and the visible count are requested together
+  // (slots below n_max lie in the row; those at or past V are never taken)
+  float smp[kSampleKpt];
+  sample_load(A, src, smp);
+  // (raw buffer loads over the row's n_max slots, 0 past them: no branch, so the wait
+  // for the sample counts exactly the loads issued after it)
+  const __amdgpu_buffer_rsrc_t rs = float_rsrc(src, A.n_max);
   float sc[kIt];
 #pragma unroll
-  for (int r = 0; r < kIt; ++r) {
-    const int i = w0 + r * 64 + lane;
-    sc[r] = i < V ? src[i] : 0.f;
-  }
-  const uint32_t tau = sample_threshold(A, src, V, sh);
+  for (int r = 0; r < kIt; ++r)
+    sc[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (w0 + r * 64 + lane) * 4, 0, 0));
+  const int V = row_visible(A, row);
+  const uint32_t tau = sample_threshold(A, smp, sh);
+  if (V <= kRegKeys || V <= A.topk) return;   // (uniform, after the threshold's barriers)
   uint32_t key[kIt];
   uint32_t cnt = 0;
 #pragma unroll
@@ -750,11 +766,30 @@ __global__ __launch_bounds__(kTopkThreads) void topk_candidates_kernel(IndexArgs
   __shared__ uint32_t coff[kMaxChunks + 1];
   __shared__ int32_t cand_idx[kCandCap];
   const long row = blockIdx.x;
-  const int V = row_visible(A, row);
   const int k = A.topk;
   const float* src = scores + row * A.n_max;
   int32_t* oi = out_idx + row * k;
   float* os = out_score ? out_score + row * k : nullptr;
+  const uint32_t* gk = L.ckey + row * A.n_max;
+  const int32_t* gi = L.cidx + row * A.n_max;
+  // Requested together with the visible count: the first candidates of the first
+  // chunks and the first 64 chunk counts (reads inside the row's lists and counts;
+  // what lies past a chunk's count, or in chunks at or past V, is never used)
+  uint32_t spk[kSpec];
+  int32_t spi[kSpec];
+  {
+    const int c = (int)threadIdx.x / kCopyT, i = (int)threadIdx.x % kCopyT;
+#pragma unroll
+    for (int j = 0; j < kSpec; ++j) {
+      const long p = (long)c * kChunk + i + kCopyT * j;
+      const bool in = c < L.chunks && p < A.n_max;
+      spk[j] = in ? gk[p] : 0u;
+      spi[j] = in ? gi[p] : -1;
+    }
+  }
+  const int lane = threadIdx.x & 63;
+  const uint32_t cnt0 = (threadIdx.x < 64 && lane < L.chunks) ? L.counts[row * L.chunks + lane] : 0u;
+  const int V = row_visible(A, row);
   if (V <= k) {
     take_all(src, V, k, oi, os);
     return;
@@ -768,29 +803,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_candidates_kernel(IndexArgs
     return;
   }
   const int nch = (V + kChunk - 1) / kChunk;
-  const uint32_t* gk = L.ckey + row * A.n_max;
-  const int32_t* gi = L.cidx + row * A.n_max;
-  // the first candidates of the first chunks are requested before the counts arrive
-  // (reads inside the row's lists; those past a chunk's count are not used)
-  uint32_t spk[kSpec];
-  int32_t spi[kSpec];
-  {
-    const int c = (int)threadIdx.x / kCopyT, i = (int)threadIdx.x % kCopyT;
-#pragma unroll
-    for (int j = 0; j < kSpec; ++j) {
-      const long p = (long)c * kChunk + i + kCopyT * j;
-      const bool in = c < nch && p < A.n_max;
-      spk[j] = in ? gk[p] : 0u;
-      spi[j] = in ? gi[p] : -1;
-    }
-  }
   // chunk offsets (exclusive scan of the per-chunk counts, one wave)
-  const int lane = threadIdx.x & 63;
   if (threadIdx.x < 64) {
     uint32_t run = 0;
     for (int base = 0; base < nch; base += 64) {
       const int c = base + lane;
-      const uint32_t v = c < nch ? L.counts[row * L.chunks + c] : 0u;
+      const uint32_t v = c < nch ? (base == 0 ? cnt0 : L.counts[row * L.chunks + c]) : 0u;
       const uint32_t inc = wave_inclusive_sum(v);
       if (c < nch) coff[c] = run + inc - v;
       run += (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);

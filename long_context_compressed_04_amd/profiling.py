@@ -54,10 +54,13 @@ COMMON_SOURCES = ["csa_device.hpp", "csa_kernels.hpp", "select_device.hpp"]
 
 
 def source_hash(kernel: str) -> str:
+    """Hash of what decides the kernel's code: its source, the shared device headers,
+    and the build script (compiler options, some per source)."""
     h = hashlib.sha256()
     src = KERNELS[kernel][1]
-    for f in ([src] if isinstance(src, str) else list(src)) + COMMON_SOURCES:
-        with open(os.path.join(CSRC, f), "rb") as fh:
+    paths = [os.path.join(CSRC, f) for f in ([src] if isinstance(src, str) else list(src)) + COMMON_SOURCES]
+    for path in paths + [os.path.join(PKG, "build_lib.py")]:
+        with open(path, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
