@@ -1267,7 +1267,14 @@ void mqa_w8_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml, con
         irms[BUF][wave + kW8Waves * rr] = ((okm[BUF] >> rr) & 1u) ? inv_rms(s * (1.f / kD) + A.eps) : 0.f;
       __builtin_amdgcn_sched_barrier(0);
     }
-    // ---- partial S^T over this wave's 256 dims: 16 k-steps
+    // ---- partial S^T over this wave's 256 dims: 16 k-steps.  Behind the first product,
+    // tile ti + 2's row addresses are resolved (wave-uniform: scalar registers until the
+    // P V phase issues the loads) and, with PRE, its row mask written: that work needs
+    // only the slots read above, and its irms slot (tile ti - 1's) was last read before
+    // the previous step's second barrier, so the scalar and vector units do it while
+    // the matrix unit runs instead of after the exchange barrier.
+    const bool gi = ti + 2 < n_tiles;
+    uint64_t growp[kW8Rpw] = {};
     f32x16_t s = f32x16_t{};
     {
       const uint8_t* ka = tile + ka_base + 512 * DH;
@@ -1280,6 +1287,15 @@ void mqa_w8_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml, con
         const uint4 c = a[ks % PF];
         if (ks + PF < 16) a[ks % PF] = *(const uint4*)(ka + 32 * (ks + PF));
         s = mfma32x32x16(as_bf16x8(c), qf[ks], s);
+        if (ks == 0 && gi) {
+          const Gather gn = resolve_tile(ti + 2, sv2);
+          row_mask(gn.ok, irms[(BUF + 2) % kNB]);
+          okm[(BUF + 2) % kNB] = gn.ok;
+#pragma unroll
+          for (int rr = 0; rr < kW8Rpw; ++rr)
+            growp[rr] = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)gn.hi, rr) << 32) |
+                        (uint32_t)__builtin_amdgcn_readlane((int)gn.lo, rr);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -1290,19 +1306,6 @@ void mqa_w8_kernel(MqaArgs A, MqaLaunch L, uint16_t* part_o, float* part_ml, con
       xs[wave][1][lane] = f32x4_t{s[g + 4], s[g + 5], s[g + 6], s[g + 7]};
     }
     lds_barrier();
-    // tile ti + 2: its rows' addresses (wave-uniform: scalar registers until the P V
-    // phase issues the loads) and, with PRE, the load of its row norms
-    const bool gi = ti + 2 < n_tiles;
-    uint64_t growp[kW8Rpw] = {};
-    if (gi) {
-      const Gather gn = resolve_tile(ti + 2, sv2);
-      row_mask(gn.ok, irms[(BUF + 2) % kNB]);
-      okm[(BUF + 2) % kNB] = gn.ok;
-#pragma unroll
-      for (int rr = 0; rr < kW8Rpw; ++rr)
-        growp[rr] = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)gn.hi, rr) << 32) |
-                    (uint32_t)__builtin_amdgcn_readlane((int)gn.lo, rr);
-    }
     // rows of k-step dh: s[8 dh + k] is row 16 dh + 8 (k / 4) + 4 h + k % 4
     {
       const f32x4_t x0 = xs[wave ^ 4][0][lane], x1 = xs[wave ^ 4][1][lane];
