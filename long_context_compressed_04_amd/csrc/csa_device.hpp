@@ -35,9 +35,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) { return (uint16_t)(pac
 __device__ __forceinline__ float relu_f32(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 // Order-preserving map fp32 -> uint32 (larger float <=> larger key).
+// (u ^ mask, mask = all ones for a negative float and only the sign bit otherwise:
+// three VALU operations, where the select form takes four)
 __device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __float_as_uint(f);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
 // s_waitcnt for "at most N vector-memory operations of this wave still outstanding"
