@@ -174,7 +174,7 @@ csa_status csa_fp8_quantize(int32_t dtype, const void* x, int64_t n, uint8_t* co
  *   out_score [batch, n_q, topk] fp32 score of each selected entry (-inf for -1), or NULL
  * Supported: CSA_F32 any idx_dim <= 256 and idx_heads <= 128; CSA_BF16 and CSA_MXFP4
  * with idx_dim == 128 and idx_heads in {32, 64, 96, 128}.  1 <= topk <= 4096,
- * n_max <= k_cap.
+ * n_max <= k_cap; CSA_MXFP4 also n_max <= 16,777,216 (else CSA_ERR_SHAPE).
  * ---------------------------------------------------------------------------- */
 typedef struct {
   int32_t batch;

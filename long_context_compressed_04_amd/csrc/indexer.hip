@@ -18,6 +18,8 @@
 //    v_mfma_scale_f32_32x32x64_f8f6f4 (e2m1 operands, e8m0 scale per 32 k-values).
 //    Epilogue: ReLU, per-head weight, reduction over the 32 rows of each block
 //    (16 in-lane, then the partner lane l^32), one fp32 score per entry.
+#include <type_traits>
+
 #include "csa_device.hpp"
 #include "csa_kernels.hpp"
 #include "launch_timer.hpp"
@@ -61,7 +63,7 @@ constexpr int kIdxDim = 128;                 // indexer head dim on the MFMA pat
 constexpr int kQRowBf16 = kIdxDim * 2 + 16;  // LDS row stride (bytes), padded
 constexpr int kQRowFp4 = kIdxDim / 2 + 16;
 
-template <int HB, bool FP4, int TPW>
+template <int HB, bool FP4, int TPW, bool QQ>
 __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_mfma(IndexArgs A, float* scores, int q_tile) {
   constexpr int H = HB * 32;
   constexpr int KS = FP4 ? 2 : 8;           // k-steps over the 128 dims
@@ -76,21 +78,60 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_mfma(IndexArgs A,
   const int chunk0 = blockIdx.x * (kIdxWaves * TPW * 32);
   const int wave0 = chunk0 + wave * TPW * 32;
 
+  const int q_begin = blockIdx.y * q_tile;
+  const int q_end = min(A.n_q, q_begin + q_tile);
+  const long row0 = (long)b * A.n_q + q_begin;
+  const int ne_raw = A.n_entries[b];
+  // QQ (fp32 queries quantised here): the first query's q block of this thread (block i:
+  // head i / 4, dims 32 (i % 4) ..), its head weight and its position are requested
+  // before the keys.  Loads return in order: requested after the keys, waiting for them
+  // waited for every key, and the tiles' products all started after the last key landed.
+  static_assert(!QQ || FP4, "in-call quantisation belongs to the MXFP4 path");
+  float qv0[QQ ? 32 : 1];
+  float w0 = 0.f;
+  int qpos0 = 0;
+  if constexpr (QQ) {
+    const int i = min((int)threadIdx.x, H * 4 - 1);
+    const float* qg = (const float*)A.q + (row0 * H + (i >> 2)) * kIdxDim + 32 * (i & 3);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float4 f = *(const float4*)(qg + 4 * j);
+      qv0[4 * j] = f.x; qv0[4 * j + 1] = f.y; qv0[4 * j + 2] = f.z; qv0[4 * j + 3] = f.w;
+    }
+    w0 = A.w[row0 * H + min((int)threadIdx.x, H - 1)];
+    qpos0 = A.q_pos[row0];
+    __builtin_amdgcn_sched_barrier(0);   // (the scheduler would hoist the key loads above)
+  }
+
   // ---- keys for this wave's TPW tiles (registers, B operands).  Rows up to n_max lie
   // inside the cache (n_max <= k_cap): they are loaded without waiting for the entry
   // count, and the scores past the visible count are masked below.
   uint4 kb[TPW][KS];
   uint32_t ksc[TPW];
+  // FP4: raw buffer loads over the sequence's n_max rows (codes and scales read as 0 past
+  // them; such entries are never stored), with no branch, so each tile's products wait
+  // for that tile's loads alone
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const uint8_t*)A.k + (long)b * A.k_cap * (kIdxDim / 2)), (short)0, A.n_max * (kIdxDim / 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(A.k_scale + (long)b * A.k_cap * (kIdxDim / 32)), (short)0, A.n_max * (kIdxDim / 32), 0x00020000);
+  if (FP4) {   // the scale words first, then the codes tile by tile
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+      ksc[t] = __builtin_amdgcn_raw_buffer_load_b32(srs, (wave0 + t * 32 + col) * (kIdxDim / 32), 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     const int e = wave0 + t * 32 + col;
     const bool ok = e < A.n_max;
     if (FP4) {
-      const uint8_t* kr = (const uint8_t*)A.k + ((long)b * A.k_cap + (ok ? e : 0)) * (kIdxDim / 2);
+      typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        kb[t][ks] = ok ? *(const uint4*)(kr + 32 * ks + 16 * half) : make_uint4(0, 0, 0, 0);
-      ksc[t] = ok ? *(const uint32_t*)(A.k_scale + ((long)b * A.k_cap + e) * (kIdxDim / 32)) : 0x7f7f7f7fu;
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(krs, e * (kIdxDim / 2) + 32 * ks + 16 * half, 0, 0);
+        kb[t][ks] = make_uint4(v[0], v[1], v[2], v[3]);
+      }
     } else {
       const uint16_t* kr = (const uint16_t*)A.k + ((long)b * A.k_cap + (ok ? e : 0)) * kIdxDim;
 #pragma unroll
@@ -99,10 +140,11 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_mfma(IndexArgs A,
     }
   }
 
-  const int ne = min(A.n_entries[b], A.n_max);
-  const int q_begin = blockIdx.y * q_tile;
-  const int q_end = min(A.n_q, q_begin + q_tile);
-  for (int qi = q_begin; qi < q_end; ++qi) {
+  const int ne = min(ne_raw, A.n_max);
+  // one query: FIRST (a compile-time flag) marks the first query of a QQ workgroup,
+  // whose inputs were requested before the keys
+  auto process = [&](const int qi, auto FIRSTC) {
+    constexpr bool FIRST = decltype(FIRSTC)::value;
     const long row = (long)b * A.n_q + qi;
     // ---- stage q (and its scales) and w for this query in LDS
     __syncthreads();
@@ -110,17 +152,35 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_mfma(IndexArgs A,
       // fp32 q, quantised here block by block (as the standalone quantiser): block i
       // is head i / 4, dims 32 (i % 4) ..; its codes land where the staged codes would
       const float* qg = (const float*)A.q + row * H * kIdxDim;
-      for (int i = threadIdx.x; i < H * 4; i += blockDim.x) {
-        const int h = i >> 2, p = i & 3;
-        float v[32];
+      constexpr int kThreads = kIdxWaves * 64;
+      auto stage_block = [&](int i, const float (&v)[32]) {
+        uint8_t sc;
+        *(uint4*)(q_lds + (i >> 2) * QROW + 16 * (i & 3)) = mxfp4_block(v, sc);
+        ((uint8_t*)qs_lds)[i] = sc;   // (byte 4 h + p of the scale words: i itself)
+      };
+      auto load_block = [&](int i, float (&v)[32]) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float4 f = *(const float4*)(qg + h * kIdxDim + 32 * p + 4 * j);
+          const float4 f = *(const float4*)(qg + (i >> 2) * kIdxDim + 32 * (i & 3) + 4 * j);
           v[4 * j] = f.x; v[4 * j + 1] = f.y; v[4 * j + 2] = f.z; v[4 * j + 3] = f.w;
         }
-        uint8_t sc;
-        *(uint4*)(q_lds + h * QROW + 16 * p) = mxfp4_block(v, sc);
-        ((uint8_t*)qs_lds)[4 * h + p] = sc;
+      };
+      // (the first query's first block per thread was requested before the keys; the
+      // branch is uniform, so the wait before its use counts those loads alone)
+      int i0 = threadIdx.x;
+      if (FIRST) {
+        if (i0 < H * 4) {
+          float v[32];
+#pragma unroll
+          for (int j = 0; j < 32; ++j) v[j] = qv0[QQ ? j : 0];
+          stage_block(i0, v);
+        }
+        i0 += kThreads;
+      }
+      for (int i = i0; i < H * 4; i += kThreads) {
+        float v[32];
+        load_block(i, v);
+        stage_block(i, v);
       }
     } else if (FP4) {
       const uint8_t* qg = (const uint8_t*)A.q + row * H * (kIdxDim / 2);
@@ -137,10 +197,15 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_mfma(IndexArgs A,
         *(uint4*)(q_lds + h * QROW + 16 * p) = *(const uint4*)(qg + h * kIdxDim + 8 * p);
       }
     }
-    for (int h = threadIdx.x; h < H; h += blockDim.x) w_lds[h] = A.w[row * H + h];
+    static_assert(H <= kIdxWaves * 64, "one head weight per thread");
+    if (FIRST) {
+      if ((int)threadIdx.x < H) w_lds[threadIdx.x] = w0;
+    } else if ((int)threadIdx.x < H) {
+      w_lds[threadIdx.x] = A.w[row * H + threadIdx.x];
+    }
     __syncthreads();
 
-    const int V = visible_entries(A.q_pos[row], ne, A.m);
+    const int V = visible_entries((FIRST) ? qpos0 : A.q_pos[row], ne, A.m);
     // weights of the 16 heads this lane's accumulator rows hold, per head block
     float wl[HB][16];
 #pragma unroll
@@ -153,6 +218,10 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_mfma(IndexArgs A,
       const int tile0 = wave0 + t * 32;
       if (tile0 >= V) break;                 // whole tile masked (uniform per wave)
       float part = 0.f;
+      // (an empty asm on the tile's scale word keeps its byte extraction in the loop: the
+      // compiler would hoist it above the query loop and wait there for every key)
+      uint32_t kst = ksc[t];
+      if (FP4) asm volatile("" : "+v"(kst));
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
         const int head = hb * 32 + col;      // A-operand row of this lane
@@ -164,7 +233,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_mfma(IndexArgs A,
             i32x8_t av = {(int)a4.x, (int)a4.y, (int)a4.z, (int)a4.w, 0, 0, 0, 0};
             i32x8_t bv = {(int)kb[t][ks].x, (int)kb[t][ks].y, (int)kb[t][ks].z, (int)kb[t][ks].w, 0, 0, 0, 0};
             const int sa = (int)((qs_lds[head] >> (8 * (2 * ks + half))) & 0xff);
-            const int sb = (int)((ksc[t] >> (8 * (2 * ks + half))) & 0xff);
+            const int sb = (int)((kst >> (8 * (2 * ks + half))) & 0xff);
             acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 4, 4, 0, sa, 0, sb);
           } else {
             uint4 a4 = *(const uint4*)(q_lds + head * QROW + (16 * ks + 8 * half) * 2);
@@ -184,6 +253,11 @@ __global__ __launch_bounds__(kIdxWaves * 64) void index_scores_mfma(IndexArgs A,
       const int e = wave0 + t * 32 + col;
       if (wave0 + t * 32 >= V && half == 0 && e < A.n_max) scores[row * A.n_max + e] = -INFINITY;
     }
+  };
+  if constexpr (QQ) {
+    process(q_begin, std::true_type{});   // (QQ workgroups hold one query)
+  } else {
+    for (int qi = q_begin; qi < q_end; ++qi) process(qi, std::false_type{});
   }
 }
 
@@ -477,12 +551,16 @@ static hipError_t launch_mfma_hb(const IndexArgs& A, float* scores, hipStream_t 
     constexpr int TPW = 8;
     const int chunk = kIdxWaves * TPW * 32;
     dim3 grid((A.n_max + chunk - 1) / chunk, (A.n_q + q_tile - 1) / q_tile, A.batch);
-    return launch("index_scores_mxfp4", index_scores_mfma<HB, FP4, TPW>, grid, block, 0, s, A, scores, q_tile);
+    // one query per workgroup (decode): its q, head weights and position are requested
+    // ahead of the keys (QQ)
+    if (q_tile == 1)
+      return launch("index_scores_mxfp4", index_scores_mfma<HB, FP4, TPW, FP4>, grid, block, 0, s, A, scores, q_tile);
+    return launch("index_scores_mxfp4", index_scores_mfma<HB, FP4, TPW, false>, grid, block, 0, s, A, scores, q_tile);
   }
   constexpr int TPW = 2;
   const int chunk = kIdxWaves * TPW * 32;
   dim3 grid((A.n_max + chunk - 1) / chunk, (A.n_q + q_tile - 1) / q_tile, A.batch);
-  return launch("index_scores_mxfp4", index_scores_mfma<HB, FP4, TPW>, grid, block, 0, s, A, scores, q_tile);
+  return launch("index_scores_mxfp4", index_scores_mfma<HB, FP4, TPW, false>, grid, block, 0, s, A, scores, q_tile);
 }
 
 hipError_t launch_index_scores(const IndexArgs& A, float* scores, hipStream_t s) {

@@ -74,6 +74,8 @@ csa_status check_index(const char* fn, const csa_index_desc* d, const void* q, c
       return fail(CSA_ERR_ALIGN, "%s: q_idx, k_idx and w must be 16-byte aligned", fn);
     if (d->dtype == CSA_MXFP4) {
       if (d->q_quantize != 0 && d->q_quantize != 1) return fail(CSA_ERR_SHAPE, "%s: q_quantize must be 0 or 1", fn);
+      // (the kernel reads a sequence's keys through a buffer descriptor of n_max * 64 bytes)
+      if (d->n_max > (1 << 24)) return fail(CSA_ERR_SHAPE, "%s: MXFP4 needs n_max <= 16777216", fn);
       if ((!qs && !d->q_quantize) || !kscale) return fail(CSA_ERR_NULL, "%s: MXFP4 needs q_scale and k_scale", fn);
       if ((qs && !d->q_quantize && ((uintptr_t)qs & 3u)) || ((uintptr_t)kscale & 3u))
         return fail(CSA_ERR_ALIGN, "%s: q_scale and k_scale must be 4-byte aligned", fn);
