@@ -97,6 +97,10 @@ void fixed_cases() {
   x.dtype = CSA_MXFP4;
   expect(csa::check_index("t", &x, p, nullptr, f, p, nullptr, i32, i32), CSA_ERR_NULL, "index mxfp4 scales");
   expect(csa::check_index("t", &x, p, u8, f, p, u8, i32, i32), CSA_OK, "index mxfp4 ok");
+  x.n_max = 1 << 24; x.k_cap = 1 << 24;
+  expect(csa::check_index("t", &x, p, u8, f, p, u8, i32, i32), CSA_OK, "index mxfp4 largest n_max");
+  x.n_max = (1 << 24) + 1; x.k_cap = (1 << 24) + 1;
+  expect(csa::check_index("t", &x, p, u8, f, p, u8, i32, i32), CSA_ERR_SHAPE, "index mxfp4 n_max bound");
 
   csa_mqa_desc a = good_mqa();
   expect(csa::check_mqa("t", &a, 0, p, p, p, p, i32, i32, g_buf), CSA_OK, "mqa ok");
