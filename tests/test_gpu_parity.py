@@ -186,6 +186,7 @@ def _oracle_scores(qv, kv, w, n_entries, q_pos, m, b, i):
     ("mxfp4", 2, 1, 64, 128, 2500, 4, 128),
     ("bf16", 1, 70, 64, 128, 700, 4, 64),         # many queries: two query tiles, the second ragged
     ("bf16", 2, 66, 128, 128, 300, 4, 32),
+    ("bf16", 1, 67, 64, 128, 1100, 4, 64),        # many queries, the last pair a single query
     ("mxfp4", 1, 65, 64, 128, 600, 4, 64),
 ])
 def test_index_scores_and_topk(dtype, B, n_q, HI, dI, N, m, k):
