@@ -30,8 +30,16 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-u
 # kernels: an epilogue reads every accumulator once, and from AGPRs each read is one
 # more instruction (v_accvgpr_read), behind a wait for the matrix pipe before the
 # registers are reused.  Every kernel keeps its occupancy or gains; the decode and
-# prefill MQA kernels compile to the same code either way.
-SOURCE_FLAGS = {src: ["-mllvm", "-amdgpu-mfma-vgpr-form"] for src in ("indexer.hip", "mqa.hip")}
+# prefill MQA kernels compile to the same code either way.  The top-k and indexer
+# sources use LLVM's ILP-first machine scheduler (same-box A/B: csa_decode_64k step
+# 33.21 -> 33.07 us, csa_decode_1m_fp4 35.03 -> 34.76 us, prefill unchanged); on the
+# MQA source it adds spills, so that source keeps the default scheduler.
+_ILP = ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]
+SOURCE_FLAGS = {
+    "indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"] + _ILP,
+    "mqa.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "topk.hip": _ILP,
+}
 
 
 def _compile(src: str) -> str:
